@@ -1,0 +1,33 @@
+"""CPU float64 oracle for mixed-codec paged decode attention.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything here. The
+library's product path (``paged_kv_cache_182_amd``) never imports it, and this
+package shares no code with that path: codec decoding, the in-page layout
+reader, attention and the log-sum-exp fold are all written here from their
+definitions.
+
+What it computes (sources are the three pages' own sections):
+
+* Codec values (``codecs``): FP16/BF16 pages; FP8 e4m3 codes times an fp32
+  scale (FreeToken PR #499 update, item 1); INT8/INT4 with one scale per group
+  of 32 along head_dim (GGML Q8/Q4 pages in ARGUS "v0.5" and "Direct paged
+  attention").
+* Attention (``attention``): for each query head, softmax over every attended
+  token of the scaled q.k score, applied to V -- the exact result that ARGUS's
+  page-at-a-time online-softmax recurrence reaches ("Why decode is slow",
+  "Direct paged attention"). Tokens come from the block table in logical order
+  (FreeToken PR #499 "Design": logical -> physical translation), or only from
+  the selected pages in sparse mode (PR #499 "Why this works").
+* Fold (``attention.fold``): partial results combined through their
+  log-sum-exp into one result (PR #499 discussion, in-place host K/V design:
+  windows folded by log-sum-exp into an fp32 accumulator).
+* Byte accounting (``accounting``): bytes of codes + scales, pinned to the
+  memory figures ARGUS prints for its engine at 32K ("Direct paged attention").
+
+Pins live in ``tests/test_oracle_*.py``; see each function for what pins it.
+"""
+from .codecs import (decode_bf16, decode_fp16, decode_fp8_e4m3, decode_int4,  # noqa: F401
+                     decode_int8)
+from .attention import decode_attention, fold, gather_kv, partials  # noqa: F401
+from .accounting import kv_bytes_per_token  # noqa: F401

@@ -1,0 +1,72 @@
+"""Pins for the oracle's codec decoders (no GPU).
+
+Each decoder is written from the format definition; here it is compared, code
+by code, with an independent library conversion or with integer enumeration.
+"""
+import numpy as np
+import torch
+
+from oracle.codecs import (decode_bf16, decode_fp8_e4m3, decode_fp16, decode_int4,
+                           decode_int8)
+from synth.encode import encode_int_g32, pack_int4
+
+
+def _same(a, b):
+    a, b = np.asarray(a, float), np.asarray(b, float)
+    both_nan = np.isnan(a) & np.isnan(b)
+    return bool(np.all(both_nan | (a == b)))
+
+
+def test_fp16_all_codes_match_numpy():
+    codes = np.arange(1 << 16, dtype=np.uint16)
+    assert _same(decode_fp16(codes), codes.view(np.float16).astype(np.float64))
+
+
+def test_bf16_all_codes_match_torch():
+    codes = np.arange(1 << 16, dtype=np.int32).astype(np.int16)
+    ref = torch.from_numpy(codes).view(torch.bfloat16).to(torch.float64).numpy()
+    assert _same(decode_bf16(codes.view(np.uint16)), ref)
+
+
+def test_fp8_e4m3fn_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = decode_fp8_e4m3(codes)
+    assert _same(got, ref)
+    finite = got[np.isfinite(got)]
+    assert finite.max() == 448.0 and finite.min() == -448.0
+    assert np.min(np.abs(finite[finite != 0])) == 2.0 ** -9
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    assert np.isfinite(got).sum() == 254          # no infinities, two NaN codes
+
+
+def test_int8_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    assert np.array_equal(decode_int8(codes), codes.view(np.int8).astype(np.float64))
+
+
+def test_int4_all_bytes_brute_force():
+    codes = np.arange(256, dtype=np.uint8)
+    got = decode_int4(codes[None, :])[0]
+    for b in range(256):
+        lo, hi = b & 15, b >> 4
+        assert got[2 * b] == (lo - 16 if lo >= 8 else lo)
+        assert got[2 * b + 1] == (hi - 16 if hi >= 8 else hi)
+
+
+def test_int_group_roundtrip_error_bound():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((5, 64)).astype(np.float32) * 3
+    for qmax, decode in ((127, None), (7, None)):
+        codes, scales = encode_int_g32(x, qmax)
+        s = scales.astype(np.float64).repeat(32, axis=-1)
+        if qmax == 7:
+            vals = decode_int4(pack_int4(codes)) * s
+        else:
+            vals = decode_int8(codes.view(np.uint8)) * s
+        # Symmetric rounding: every element within half a step of its input,
+        # up to the fp16 rounding of the scale (the largest element may sit
+        # slightly past qmax*s and be clipped by at most qmax*|s - absmax/qmax|).
+        amax = np.abs(x.reshape(5, 2, 32)).max(-1).repeat(32, -1)
+        bound = s / 2 + np.abs(amax - qmax * s) + 1e-6
+        assert np.all(np.abs(vals - x) <= bound)
