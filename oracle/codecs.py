@@ -55,10 +55,16 @@ def decode_int8(codes: np.ndarray) -> np.ndarray:
 
 
 def decode_int4(packed: np.ndarray) -> np.ndarray:
-    """Bytes holding two two's-complement nibbles; element 2k is the low nibble
-    of byte k. Returns twice as many values as bytes, in element order."""
+    """Bytes holding two's-complement nibbles, eight per 32-bit little-endian
+    word: element r (0..7) of each word sits at nibble slot (r % 2)*4 + r//2,
+    slot s being bits 4s..4s+3. Returns two values per byte, in element order."""
     u = np.asarray(packed).astype(np.int64) & 0xFF
-    lo, hi = u & 0xF, (u >> 4) & 0xF
-    out = np.empty(u.shape[:-1] + (u.shape[-1] * 2,), dtype=np.int64)
-    out[..., 0::2], out[..., 1::2] = lo, hi
-    return np.where(out >= 8, out - 16, out).astype(np.float64)
+    *lead, nb = u.shape
+    assert nb % 4 == 0
+    b = u.reshape(*lead, nb // 4, 4)
+    word = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)
+    out = np.empty((*lead, nb // 4, 8), dtype=np.int64)
+    for r in range(8):
+        out[..., r] = (word >> (4 * ((r % 2) * 4 + r // 2))) & 0xF
+    out = np.where(out >= 8, out - 16, out)
+    return out.reshape(*lead, nb * 2).astype(np.float64)

@@ -9,7 +9,9 @@ Within one head's codes, element (t, i) sits at element index
 * V:  (t // 16)*16*D + ((t % 16)//4 * 16 + i % 16) * (D//16) * 4
       + (i // 16) * 4 + t % 4;
 
-and INT4 element e is nibble ``e % 2`` (0 = low) of byte ``e // 2``.
+and INT4 packs eight elements per 32-bit little-endian word: element e is in
+word e // 8 at nibble slot (r % 2)*4 + r // 2 with r = e % 8 (even elements
+in the low half-word, odd ones in the high half-word).
 Pinned in tests/test_oracle_layout.py by hand-placed single codes.
 """
 from __future__ import annotations

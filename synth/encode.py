@@ -13,7 +13,8 @@ e4m3 codes plus fp32 scales):
            (page, kv head, K|V) block, saturated to +-448 before the cast.
 * INT8  -- symmetric groups of 32 along head_dim: s = fp16(absmax / 127),
            c = clip(rint(x / s), -127, 127).
-* INT4  -- as INT8 with 7 in place of 127; two's-complement nibbles.
+* INT4  -- as INT8 with 7 in place of 127; two's-complement nibbles packed
+           eight to a 32-bit word (see ``pack_int4``).
 """
 from __future__ import annotations
 
@@ -52,7 +53,15 @@ def encode_int_g32(x: np.ndarray, qmax: int) -> tuple[np.ndarray, np.ndarray]:
 
 
 def pack_int4(codes: np.ndarray) -> np.ndarray:
-    """Pack int4 values (int8 in [-8, 7]) along the last axis: element 2k in the
-    low nibble of byte k, element 2k+1 in the high nibble."""
-    c = (np.asarray(codes).astype(np.int16) & 0xF).astype(np.uint8)
-    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+    """Pack int4 values (int8 in [-8, 7]) along the last axis, 8 per 32-bit
+    little-endian word: element r of each group of 8 goes to nibble slot
+    (r % 2) * 4 + r // 2 (bits 4*slot .. 4*slot+3), i.e. the even elements
+    fill the low half-word and the odd ones the high half-word, in order."""
+    c = (np.asarray(codes).astype(np.int64) & 0xF).astype(np.uint32)
+    *lead, n = c.shape
+    assert n % 8 == 0
+    g = c.reshape(*lead, n // 8, 8)
+    word = np.zeros((*lead, n // 8), dtype=np.uint32)
+    for r in range(8):
+        word |= g[..., r] << np.uint32(4 * ((r % 2) * 4 + r // 2))
+    return word.astype("<u4").view(np.uint8).reshape(*lead, n // 2)

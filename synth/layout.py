@@ -9,7 +9,8 @@ plane is ``codes[Hkv][...]`` followed, for INT8/INT4, by
 * V codes, per head: 16-token tiles; inside a tile the element order is
   (token quad qd, dim-in-block c, dim block n, token-in-quad j) with
   t = 16*tile + 4*qd + j and i = 16*n + c.
-* INT4 packs element 2k in the low nibble of byte k.
+* INT4 packs 8 elements per 32-bit word: even elements in the low half-word,
+  odd elements in the high half-word, each half in element order.
 """
 from __future__ import annotations
 

@@ -45,13 +45,17 @@ def test_int8_all_codes():
     assert np.array_equal(decode_int8(codes), codes.view(np.int8).astype(np.float64))
 
 
-def test_int4_all_bytes_brute_force():
-    codes = np.arange(256, dtype=np.uint8)
-    got = decode_int4(codes[None, :])[0]
-    for b in range(256):
-        lo, hi = b & 15, b >> 4
-        assert got[2 * b] == (lo - 16 if lo >= 8 else lo)
-        assert got[2 * b + 1] == (hi - 16 if hi >= 8 else hi)
+def test_int4_every_slot_and_value_brute_force():
+    # element r of a word -> nibble slot, worked out by hand from the rule
+    # "even elements in the low half-word, odd in the high half-word"
+    slot = {0: 0, 1: 4, 2: 1, 3: 5, 4: 2, 5: 6, 6: 3, 7: 7}
+    for r in range(8):
+        for v in range(16):
+            word = np.array([v << (4 * slot[r])], dtype="<u4").view(np.uint8)
+            got = decode_int4(word[None, :])[0]
+            expect = np.zeros(8)
+            expect[r] = v - 16 if v >= 8 else v
+            assert np.array_equal(got, expect)
 
 
 def test_int_group_roundtrip_error_bound():

@@ -48,8 +48,9 @@ def test_single_int4_code_and_scale():
     hkv, P, D = 1, 16, 32
     codes = P * D // 2
     pool = np.zeros(codes + P * (D // 32) * 2, dtype=np.uint8)
-    # K element (3, 5) -> element 101 -> byte 50, high nibble; value -3 -> 0xD
-    pool[50] = 0xD0
+    # K element (3, 5) -> element 101 -> word 12, r = 5 -> nibble slot 6
+    # (bits 24..27) -> byte 48 + 3 = 51, low nibble; value -3 -> 0xD
+    pool[51] = 0x0D
     # scale of token 3, group 0 -> fp16 at codes + 3*2
     pool[codes + 6:codes + 8] = np.frombuffer(np.float16(0.25).tobytes(), np.uint8)
     k = plane_values(pool, 0, INT4, hkv, P, D, 0, 1.0, False, P)
