@@ -1,0 +1,287 @@
+"""Decode-attention benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+
+A step is one pkv_decode_attention call over one batch of synthetic input:
+every stage of the path (selection/block-table gather, codec decode, scores,
+online softmax, P.V, partition partials, log-sum-exp fold). The headline
+workload is the 1M-token split-K FP8 decode (batch 1, 16 query / 2 KV heads,
+head_dim 128, 64-token pages, 512 partitions). The 32K batched INT8-K/INT4-V
+workload and the sparse 48-row FP8 selection are timed the same way and
+reported beside it.
+
+Inputs are resident in HBM before timing. Each step reads a different copy
+of the pool (or, for the sparse workload, a different placement of its
+pages), so that the working set of consecutive steps exceeds the 256 MB
+last-level cache and the bytes really come from HBM.
+
+The value is effective KV bytes (codes + scales of attended tokens) divided
+by the step time. roofline.achieved uses the split-K kernel alone, timed with
+HIP events around each launch on the stream it runs on.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "effective KV-read GB/s (% of HBM peak) + decode-attn steps/s at 32K and 1M ctx"
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def params_for(pkv, w):
+    codes = {int(c) for c in w.page_codec}
+    kcs, vcs = {c & 15 for c in codes}, {c >> 4 for c in codes}
+    return pkv.make_params(
+        rows=w.rows, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+        page_size=w.page_size, num_pages=w.num_pages, max_pages_per_row=w.max_pages, pool_bytes=w.pool.nbytes,
+        max_sel_pages=w.max_sel, partition_tokens=w.partition_tokens,
+        k_codec=kcs.pop() if len(kcs) == 1 else pkv.CODEC_MIXED,
+        v_codec=vcs.pop() if len(vcs) == 1 else pkv.CODEC_MIXED, softmax_scale=w.softmax_scale)
+
+
+def rotations(torch, dw, min_bytes):
+    """Argument tuples for rotation copies of the input whose total size is at least min_bytes."""
+    import numpy as np
+    w = dw.w
+    if not w.sparse:
+        n = max(2, -(-min_bytes // w.pool.nbytes))
+        pools = [dw.pool] + [dw.pool.clone() for _ in range(n - 1)]
+        return [dw.args(pool=p) for p in pools], f"{n} pool copies"
+    # sparse: copy the selected pages into other free physical slots, one fresh
+    # block table per rotation; the selected pages' bytes and scales are identical
+    eff = sum(valid for pages in w.attended_pages() for _, valid in pages)
+    per = eff * w.num_kv_heads * w.head_dim * 2
+    n = max(2, -(-min_bytes // per))
+    rng = np.random.default_rng(7)
+    used = {int(w.block_table[r, lp]) for r in range(w.rows) for lp in w.page_sel[r]}
+    free = np.setdiff1d(np.arange(w.num_pages), np.fromiter(used, dtype=np.int64))
+    rng.shuffle(free)
+    slot = int(w.page_v_off[0] - w.page_k_off[0]) * 2
+    assert all(int(w.page_v_off[p] - w.page_k_off[p]) * 2 == slot for p in range(4))
+    out = [dw.args()]
+    pos = 0
+    pool_view = dw.pool.view(-1, slot)
+    scale = dw.page_scale
+    for _ in range(n - 1):
+        bt = w.block_table.copy()
+        src, dst = [], []
+        for r in range(w.rows):
+            for lp in w.page_sel[r]:
+                src.append(int(w.block_table[r, lp]))
+                dst.append(int(free[pos]))
+                bt[r, lp] = free[pos]
+                pos += 1
+        s = torch.from_numpy(np.array(src)).cuda()
+        d = torch.from_numpy(np.array(dst)).cuda()
+        koff = torch.from_numpy(w.page_k_off.astype(np.int64)).cuda()
+        assert bool(torch.all(koff[s] % slot == 0)) and bool(torch.all(koff[d] % slot == 0))
+        pool_view[koff[d] // slot] = pool_view[koff[s] // slot]
+        scale[d] = scale[s]
+        bt_t = torch.from_numpy(bt).cuda()
+        out.append((dw.q, dw.pool, dw.page_k_off, dw.page_v_off, dw.page_codec, dw.page_scale,
+                    bt_t, dw.seq_lens, dw.page_sel, dw.sel_lens))
+    return out, f"{n} page placements"
+
+
+def time_workload(torch, pkv, w, steps, warmup, min_rot_bytes):
+    import numpy as np
+    from synth import effective_kv_bytes_formula
+    from synth.device import to_device
+    dw = to_device(w)
+    p = params_for(pkv, w)
+    nparts = pkv.num_partitions(p)
+    eff = effective_kv_bytes_formula(w)
+    rot, rot_desc = rotations(torch, dw, min_rot_bytes)
+    out = torch.empty((w.rows, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.rows, w.num_q_heads), dtype=torch.float32, device="cuda")
+    need = pkv.workspace_bytes(p)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        pkv.decode_attention(p, *rot[i % len(rot)], out=out, lse=lse, workspace=ws, err_count=err,
+                             stream=stream)
+
+    # correctness guard: every rotation gives the same bits
+    step(0)
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone())
+    for i in range(1, len(rot)):
+        step(i)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), "rotation copies disagree"
+    assert int(err.item()) == 0, "device-visible input errors"
+    assert bool(torch.isfinite(out).all()), "non-finite output"
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+
+    # warm number: same copy every step (served partly from the last-level cache)
+    t0.record(stream)
+    for i in range(steps):
+        step(0)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_warm = t0.elapsed_time(t1) / steps
+
+    # the split-K kernel alone, one event pair around each launch
+    if nparts > 1:
+        pacc = torch.empty((w.rows, w.num_q_heads, nparts, w.head_dim), dtype=torch.float32, device="cuda")
+        pml = torch.empty((w.rows, w.num_q_heads, nparts, 2), dtype=torch.float32, device="cuda")
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(warmup):
+            pkv.decode_partials(p, *rot[i % len(rot)], part_acc=pacc, part_ml=pml, stream=stream)
+        for i in range(steps):
+            ev[i][0].record(stream)
+            pkv.decode_partials(p, *rot[i % len(rot)], part_acc=pacc, part_ml=pml, stream=stream)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms_kernel = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        flat_acc = pacc.view(-1, nparts, w.head_dim)
+        flat_ml = pml.view(-1, nparts, 2)
+        for i in range(steps):
+            cev[i][0].record(stream)
+            pkv.lse_combine(flat_acc, flat_ml, out=out.view(-1, w.head_dim), lse=lse.view(-1), stream=stream)
+            cev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms_combine = float(np.mean([a.elapsed_time(b) for a, b in cev]))
+    else:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            step(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms_kernel = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        ms_combine = 0.0
+    res = {
+        "workload": w.name, "effective_kv_bytes": int(eff), "partitions": nparts,
+        "ms_per_step": ms_step, "steps_per_s": 1e3 / ms_step,
+        "effective_gbps": eff / ms_step / 1e6, "pct_hbm_peak": 100 * eff / ms_step / 1e6 / HBM_PEAK_GBPS,
+        "ms_per_step_warm": ms_warm, "effective_gbps_warm": eff / ms_warm / 1e6,
+        "ms_split_k_kernel": ms_kernel, "split_k_kernel_gbps": eff / ms_kernel / 1e6,
+        "ms_combine_kernel": ms_combine, "rotation": rot_desc,
+    }
+    log(f"{w.name}: {ms_step * 1e3:.1f} us/step cold ({res['effective_gbps']:.0f} GB/s, "
+        f"{res['pct_hbm_peak']:.1f}% of peak), warm {ms_warm * 1e3:.1f} us, split-K kernel "
+        f"{ms_kernel * 1e3:.1f} us ({res['split_k_kernel_gbps']:.0f} GB/s), combine {ms_combine * 1e3:.1f} us")
+    del rot, dw
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w_full):
+    """The oracle, as it is, on a bounded sample of the headline workload: all
+    8 query heads of one KV head over the whole 1M-token row."""
+    import numpy as np
+    from synth import effective_kv_bytes_formula
+    from oracle.attention import _softmax_attention, gather_kv
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    G = w_full.num_q_heads // w_full.num_kv_heads
+    t = time.perf_counter()
+    K, V = gather_kv(w_full, 0, 1)
+    _softmax_attention(K, V, w_full.q[0, G:2 * G].astype(np.float64), w_full.softmax_scale)
+    dt = time.perf_counter() - t
+    sample_bytes = effective_kv_bytes_formula(w_full) / w_full.num_kv_heads
+    return {"value": sample_bytes / dt / 1e9, "unit": "GB/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"{w_full.name}: KV head 1 (8 query heads) of the 1M-token row, "
+                      f"{sample_bytes / 2**20:.1f} MiB effective, {dt:.1f} s; float64 numpy, "
+                      f"page gather single-threaded, BLAS with {blas} threads",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--quick", action="store_true", help="headline workload only, no CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every row of the path fits one MI355X). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_182_amd as pkv
+    import synth
+    pkv.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    log(f"device {torch.cuda.get_device_name(0)}")
+
+    min_rot = 1 << 30
+    log("generating 1M-token split-K workload")
+    w5 = synth.config(5)
+    head = time_workload(torch, pkv, w5, args.steps, args.warmup, min_rot)
+    also = {}
+    if not args.quick:
+        for cid in (3, 4):
+            log(f"generating workload {cid}")
+            w = synth.config(cid)
+            also[w.name] = time_workload(torch, pkv, w, args.steps, args.warmup, min_rot)
+            del w
+    cpu = None
+    if not args.quick and not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        cpu = cpu_baseline(w5)
+        log(f"oracle: {cpu['value']:.3f} GB/s ({cpu['seconds']:.1f} s)")
+
+    achieved = head["split_k_kernel_gbps"]
+    line = {
+        "metric": METRIC, "value": round(head["effective_gbps"], 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": w5.name, "batch": 1, "layers": 1, "context_tokens": int(w5.seq_lens[0]),
+                   "q_heads": 16, "kv_heads": 2, "head_dim": 128, "page_tokens": 64,
+                   "kv_codec": "fp8_e4m3 + fp32 page scales", "partitions": head["partitions"],
+                   "cold": head["rotation"], "parallelism": "single GPU"},
+        "pct_hbm_peak": round(head["pct_hbm_peak"], 2),
+        "steps_per_s_1m": round(head["steps_per_s"], 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+        "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "seconds"},
+        "detail": {"headline": head, **also},
+    }
+    c3 = also.get(synth.NAMES[3])
+    if c3:
+        line["steps_per_s_32k"] = round(c3["steps_per_s"], 1)
+        line["effective_gbps_32k"] = round(c3["effective_gbps"], 1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

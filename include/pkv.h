@@ -1,0 +1,201 @@
+/*
+ * pkv.h -- C ABI of libpkv: single-query (decode) attention read straight
+ * from a paged KV cache whose pages use mixed codecs, on AMD MI355X (gfx950).
+ *
+ * What is computed. For every row b (an independent query: a sequence, or a
+ * (layer, sequence) pair) and query head hq, with KV head h = hq / G where
+ * G = num_q_heads / num_kv_heads (grouped-query attention; ARGUS page "Why
+ * decode is slow"):
+ *
+ *     s_t  = softmax_scale * sum_i q[b][hq][i] * K_t[h][i]
+ *     out  = sum_t exp(s_t - m) V_t[h] / sum_t exp(s_t - m),  m = max_t s_t
+ *     lse  = m + ln(sum_t exp(s_t - m))                         (natural log)
+ *
+ * over the attended tokens t: in dense mode tokens 0 .. seq_lens[b]-1, found
+ * through the row's block table (logical page -> physical page; FreeToken PR
+ * #499 "Design"); in sparse mode only the tokens t < seq_lens[b] of the
+ * logical pages listed in page_sel (PR #499 "What" and "Why this works").
+ * The kernel walks the pages with an exact online softmax (ARGUS "Direct
+ * paged attention"); long rows are split into partitions of
+ * partition_tokens whose (acc, max, sum) partials are folded by log-sum-exp
+ * into the output (PR #499 discussion, in-place host K/V design). An empty
+ * token set gives out = 0 and lse = -inf.
+ *
+ * Codecs (per physical page, separately for K and V; ARGUS page intro and
+ * "v0.5": FP16/BF16 and Q8/Q4 group pages; PR #499 update: FP8 e4m3 codes +
+ * fp32 scales):
+ *   PKV_FP16      IEEE binary16.
+ *   PKV_BF16      bfloat16. The kernel converts K/V values to fp16 exactly;
+ *                 values outside fp16 range (|x| > 65504 or 0 < |x| < 2^-24)
+ *                 are outside the supported domain.
+ *   PKV_FP8_E4M3  OCP E4M3FN codes times page_scale[page][h][K|V] (fp32).
+ *   PKV_INT8_G32  int8 codes times one fp16 scale per (token, 32 dims).
+ *   PKV_INT4_G32  int4 codes times one fp16 scale per (token, 32 dims).
+ *
+ * In-page layout (this library's definition). page_k_off[p] / page_v_off[p]
+ * are byte offsets from page_pool to the K and V planes of physical page p;
+ * both must be multiples of 16. A plane holds codes[Hkv][...] head after
+ * head (each head's block is page_size * head_dim values), then, for the
+ * INT codecs only, fp16 scales[Hkv][page_size][head_dim/32].
+ *   K codes, per head: element (t, i) at index t*D + i.
+ *   V codes, per head: element (t, i) at index
+ *       (t/16)*16*D + ((t%16)/4*16 + i%16) * (D/16)*4 + (i/16)*4 + t%4.
+ *   INT4: eight elements per 32-bit little-endian word, element r of the word
+ *   in nibble slot (r%2)*4 + r/2 (even elements in the low half-word).
+ *
+ * Threading and ownership. The caller owns every buffer (device memory
+ * unless stated otherwise). Calls enqueue work on `stream` (a hipStream_t;
+ * NULL is the default stream) and return without synchronizing; buffers must
+ * stay valid until that work completes. The library allocates nothing and
+ * keeps no state, so calls are re-entrant; calls that share an output or a
+ * workspace race unless ordered on one stream.
+ *
+ * Errors. Return values report host-visible problems only. Problems that are
+ * visible only on the device (a page id outside [0, num_pages), an unknown
+ * codec nibble, a codec other than the one the launch declares, a misaligned
+ * plane offset, a plane reaching past pool_bytes, a negative length, ceil(seq_len / page_size) above
+ * max_pages_per_row, a selection entry outside [0, max_pages_per_row), a
+ * sel_len outside [0, max_sel_pages]) skip the offending page or clamp the
+ * row and add one to *err_count per offending entry, so nothing is consumed
+ * silently (PR #499 "Design": drop counter against silent corruption).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+/* Page codecs; page_codec[p] = K codec | (V codec << 4). */
+enum {
+  PKV_FP16 = 0,
+  PKV_BF16 = 1,
+  PKV_FP8_E4M3 = 2,
+  PKV_INT8_G32 = 3,
+  PKV_INT4_G32 = 4,
+  PKV_CODEC_MIXED = -1 /* pkv_params.k_codec / v_codec: any codec per page */
+};
+
+/* Status codes. */
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1, /* null/misaligned pointer, inconsistent sizes    */
+  PKV_ERR_UNSUPPORTED = -2, /* valid request with no kernel (fail closed: the
+                               caller falls back; ARGUS "Why decode is slow")  */
+  PKV_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required      */
+  PKV_ERR_HIP = -4          /* a HIP launch failed                             */
+};
+
+/* Geometry and launch description of one call. Plain values, host memory. */
+typedef struct pkv_params {
+  int32_t num_rows;          /* B: independent queries (rows) in this call, >= 0        */
+  int32_t num_q_heads;       /* Hq                                                      */
+  int32_t num_kv_heads;      /* Hkv; Hq % Hkv == 0, G = Hq / Hkv <= 16                   */
+  int32_t head_dim;          /* D: 64 or 128                                            */
+  int32_t page_size;         /* P tokens per page: a positive multiple of 16            */
+  int32_t num_pages;         /* physical pages described by the page tables            */
+  int32_t max_pages_per_row; /* row stride of block_table (entries), >= 1               */
+  int32_t max_sel_pages;     /* 0: dense mode; > 0: sparse mode, row stride of page_sel */
+  int32_t partition_tokens;  /* split-K partition length in attended tokens: 0 = chosen
+                                by the library, else a positive multiple of page_size   */
+  int32_t k_codec;           /* codec of every K plane in this call, or PKV_CODEC_MIXED */
+  int32_t v_codec;           /* codec of every V plane in this call, or PKV_CODEC_MIXED */
+  float softmax_scale;       /* tau, finite (1/sqrt(head_dim) in the usual case)        */
+  uint64_t pool_bytes;       /* size of page_pool in bytes: a plane that does not fit
+                                inside it is a device-visible error                      */
+} pkv_params;
+
+/* PKV_ABI_VERSION of the loaded library. */
+int pkv_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* pkv_status_string(int status);
+
+/* Partitions each row is split into for these params (>= 1), or a negative
+ * status if the params are invalid. Sizes the workspace and the partials. */
+int pkv_num_partitions(const pkv_params* p);
+
+/* Bytes of device workspace pkv_decode_attention needs for these params:
+ * rows*Hq*partitions*(D + 2)*4 when partitions > 1, else 0. Returns 0 for
+ * invalid params as well (the decode call then reports the error). */
+size_t pkv_workspace_bytes(const pkv_params* p);
+
+/* Decode attention (all steps: table gather, codec decode, scores, online
+ * softmax, P.V, partition partials and their log-sum-exp fold).
+ *
+ *   q            fp16 [B][Hq][D], 16-byte aligned.
+ *   page_pool    byte arena holding every plane, 256-byte aligned.
+ *   page_k_off,
+ *   page_v_off   uint64 [num_pages] byte offsets of the K / V plane of each page.
+ *   page_codec   uint8 [num_pages], K codec in the low nibble, V in the high one.
+ *   page_scale   fp32 [num_pages][Hkv][2] (K, V) FP8 scales; read only for FP8
+ *                planes. May be NULL when neither codec is declared FP8; an
+ *                FP8 page met with NULL scales is then a device-visible error.
+ *   block_table  int32 [B][max_pages_per_row] physical page of each logical page.
+ *   seq_lens     int32 [B] tokens per row.
+ *   page_sel     sparse mode: int32 [B][max_sel_pages] logical pages to attend,
+ *                any order, no duplicates; NULL in dense mode.
+ *   sel_lens     sparse mode: int32 [B] valid entries of each page_sel row.
+ *   out          fp32 [B][Hq][D] (written).
+ *   lse          fp32 [B][Hq] natural-log log-sum-exp (written).
+ *   workspace    device scratch of pkv_workspace_bytes(p) bytes, 16-byte aligned,
+ *                NULL allowed when that is 0. Contents need no initialization.
+ *   err_count    device int32 counter incremented per device-visible problem,
+ *                or NULL.
+ *   stream       hipStream_t to enqueue on (NULL: default stream).
+ */
+int pkv_decode_attention(const pkv_params* p, const void* q, const uint8_t* page_pool,
+                         const uint64_t* page_k_off, const uint64_t* page_v_off,
+                         const uint8_t* page_codec, const float* page_scale,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         const int32_t* page_sel, const int32_t* sel_lens, float* out,
+                         float* lse, void* workspace, size_t workspace_bytes,
+                         int32_t* err_count, void* stream);
+
+/* The same work as pkv_decode_attention up to, but not including, the fold:
+ * writes the unnormalised partial result of every partition instead of out and
+ * lse (the form pkv_lse_combine folds; also the form a caller that splits a row
+ * across windows or devices exchanges; PR #499 discussion, in-place host K/V
+ * design). Arguments as for pkv_decode_attention, with
+ *
+ *   part_acc  fp32 [B][Hq][n][D]  sum over the partition of exp(s - m) v,
+ *   part_ml   fp32 [B][Hq][n][2]  (m natural-log max, l sum of exp(s - m)),
+ *
+ * n = pkv_num_partitions(p), both 16-byte aligned. An empty partition writes
+ * (0, -inf, 0). No workspace is used.
+ */
+int pkv_decode_partials(const pkv_params* p, const void* q, const uint8_t* page_pool,
+                        const uint64_t* page_k_off, const uint64_t* page_v_off,
+                        const uint8_t* page_codec, const float* page_scale,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        const int32_t* page_sel, const int32_t* sel_lens, float* part_acc,
+                        float* part_ml, int32_t* err_count, void* stream);
+
+/* Log-sum-exp fold of partial results (PR #499 discussion: windows folded by
+ * their log-sum-exp into an fp32 accumulator). For each of `rows` rows:
+ *
+ *   M = max_p m_p;  w_p = exp(m_p - M);  L = sum_p w_p l_p;
+ *   out = sum_p w_p acc_p / L;  lse = M + ln L,
+ *
+ * summing parts in ascending order (run-to-run deterministic). Parts with
+ * m_p = -inf or l_p = 0 are empty; a row whose parts are all empty gets
+ * out = 0 and lse = -inf.
+ *
+ *   part_acc  fp32 [rows][num_parts][head_dim], unnormalised sum exp(s - m_p) v.
+ *   part_ml   fp32 [rows][num_parts][2] = (m_p natural-log max, l_p sum).
+ *   out       fp32 [rows][head_dim];  lse  fp32 [rows].
+ * rows >= 0, num_parts >= 1, 1 <= head_dim <= 512; pointers 4-byte aligned.
+ */
+int pkv_lse_combine(int32_t rows, int32_t num_parts, int32_t head_dim, const float* part_acc,
+                    const float* part_ml, float* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,209 @@
+"""ctypes binding of libpkv (argument marshalling only).
+
+Every step of decode attention runs in the HIP kernels behind the C ABI in
+include/pkv.h; this module only checks tensor dtypes/devices, packs
+``pkv_params`` and passes raw device pointers and the current HIP stream.
+There is no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch  # loads the HIP runtime the library must share (import before libpkv)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+
+FP16, BF16, FP8_E4M3, INT8_G32, INT4_G32, CODEC_MIXED = 0, 1, 2, 3, 4, -1
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+EXPORTS = ("pkv_abi_version", "pkv_status_string", "pkv_num_partitions",
+           "pkv_workspace_bytes", "pkv_decode_attention", "pkv_decode_partials",
+           "pkv_lse_combine")
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("num_rows", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_pages_per_row", ctypes.c_int32), ("max_sel_pages", ctypes.c_int32),
+                ("partition_tokens", ctypes.c_int32), ("k_codec", ctypes.c_int32),
+                ("v_codec", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("pool_bytes", ctypes.c_uint64)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpkv.so once. Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_cache_182_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    pp = ctypes.POINTER(Params)
+    lib.pkv_abi_version.restype = ctypes.c_int
+    lib.pkv_abi_version.argtypes = []
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_num_partitions.restype = ctypes.c_int
+    lib.pkv_num_partitions.argtypes = [pp]
+    lib.pkv_workspace_bytes.restype = sz
+    lib.pkv_workspace_bytes.argtypes = [pp]
+    lib.pkv_decode_attention.restype = ctypes.c_int
+    lib.pkv_decode_attention.argtypes = [pp] + [vp] * 12 + [vp, sz, vp, vp]
+    lib.pkv_decode_partials.restype = ctypes.c_int
+    lib.pkv_decode_partials.argtypes = [pp] + [vp] * 12 + [vp, vp]
+    lib.pkv_lse_combine.restype = ctypes.c_int
+    lib.pkv_lse_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+    if lib.pkv_abi_version() != 1:
+        raise RuntimeError("libpkv ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().pkv_status_string(status).decode()
+
+
+def make_params(*, rows, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                max_pages_per_row, pool_bytes, max_sel_pages=0, partition_tokens=0,
+                k_codec=CODEC_MIXED, v_codec=CODEC_MIXED, softmax_scale=None) -> Params:
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(head_dim)
+    return Params(rows, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                  max_pages_per_row, max_sel_pages, partition_tokens, k_codec, v_codec,
+                  softmax_scale, pool_bytes)
+
+
+def num_partitions(p: Params) -> int:
+    n = load().pkv_num_partitions(ctypes.byref(p))
+    if n < 0:
+        raise PkvError(n, "pkv_num_partitions")
+    return n
+
+
+def workspace_bytes(p: Params) -> int:
+    return int(load().pkv_workspace_bytes(ctypes.byref(p)))
+
+
+def _ptr(t: Optional[torch.Tensor], dtype, name: str, device) -> int:
+    if t is None:
+        return 0
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected a tensor on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def decode_attention(p: Params, q, page_pool, page_k_off, page_v_off, page_codec, page_scale,
+                     block_table, seq_lens, page_sel=None, sel_lens=None, *, out=None, lse=None,
+                     workspace=None, err_count=None, stream=None):
+    """Enqueue pkv_decode_attention. Returns (out, lse); allocates them (and the
+    workspace) with torch when not given. Raises PkvError on a bad status."""
+    lib = load()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be a device tensor")
+    if out is None:
+        out = torch.empty((p.num_rows, p.num_q_heads, p.head_dim), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((p.num_rows, p.num_q_heads), dtype=torch.float32, device=dev)
+    need = workspace_bytes(p)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = 0 if workspace is None else _ptr(workspace, torch.uint8, "workspace", dev)
+    ws_len = 0 if workspace is None else workspace.numel()
+    st = lib.pkv_decode_attention(
+        ctypes.byref(p), _ptr(q, torch.float16, "q", dev),
+        _ptr(page_pool, torch.uint8, "page_pool", dev),
+        _ptr(page_k_off, torch.uint64, "page_k_off", dev),
+        _ptr(page_v_off, torch.uint64, "page_v_off", dev),
+        _ptr(page_codec, torch.uint8, "page_codec", dev),
+        _ptr(page_scale, torch.float32, "page_scale", dev),
+        _ptr(block_table, torch.int32, "block_table", dev),
+        _ptr(seq_lens, torch.int32, "seq_lens", dev),
+        _ptr(page_sel, torch.int32, "page_sel", dev),
+        _ptr(sel_lens, torch.int32, "sel_lens", dev),
+        _ptr(out, torch.float32, "out", dev), _ptr(lse, torch.float32, "lse", dev),
+        ws_ptr, ws_len, _ptr(err_count, torch.int32, "err_count", dev), _stream(stream))
+    if st != OK:
+        raise PkvError(st, "pkv_decode_attention")
+    return out, lse
+
+
+def decode_partials(p: Params, q, page_pool, page_k_off, page_v_off, page_codec, page_scale,
+                    block_table, seq_lens, page_sel=None, sel_lens=None, *, part_acc=None,
+                    part_ml=None, err_count=None, stream=None):
+    """Enqueue pkv_decode_partials. Returns (part_acc [B, Hq, n, D], part_ml [B, Hq, n, 2])."""
+    lib = load()
+    dev = q.device
+    n = num_partitions(p)
+    if part_acc is None:
+        part_acc = torch.empty((p.num_rows, p.num_q_heads, n, p.head_dim), dtype=torch.float32, device=dev)
+    if part_ml is None:
+        part_ml = torch.empty((p.num_rows, p.num_q_heads, n, 2), dtype=torch.float32, device=dev)
+    st = lib.pkv_decode_partials(
+        ctypes.byref(p), _ptr(q, torch.float16, "q", dev),
+        _ptr(page_pool, torch.uint8, "page_pool", dev),
+        _ptr(page_k_off, torch.uint64, "page_k_off", dev),
+        _ptr(page_v_off, torch.uint64, "page_v_off", dev),
+        _ptr(page_codec, torch.uint8, "page_codec", dev),
+        _ptr(page_scale, torch.float32, "page_scale", dev),
+        _ptr(block_table, torch.int32, "block_table", dev),
+        _ptr(seq_lens, torch.int32, "seq_lens", dev),
+        _ptr(page_sel, torch.int32, "page_sel", dev),
+        _ptr(sel_lens, torch.int32, "sel_lens", dev),
+        _ptr(part_acc, torch.float32, "part_acc", dev), _ptr(part_ml, torch.float32, "part_ml", dev),
+        _ptr(err_count, torch.int32, "err_count", dev), _stream(stream))
+    if st != OK:
+        raise PkvError(st, "pkv_decode_partials")
+    return part_acc, part_ml
+
+
+def lse_combine(part_acc, part_ml, out=None, lse=None, stream=None):
+    """Enqueue pkv_lse_combine. part_acc [rows, parts, D], part_ml [rows, parts, 2]."""
+    lib = load()
+    rows, parts, d = part_acc.shape
+    dev = part_acc.device
+    if out is None:
+        out = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+    st = lib.pkv_lse_combine(rows, parts, d, _ptr(part_acc, torch.float32, "part_acc", dev),
+                             _ptr(part_ml, torch.float32, "part_ml", dev),
+                             _ptr(out, torch.float32, "out", dev), _ptr(lse, torch.float32, "lse", dev),
+                             _stream(stream))
+    if st != OK:
+        raise PkvError(st, "pkv_lse_combine")
+    return out, lse
+
+
+def hip_runtime_copies() -> list[str]:
+    """Paths of libamdhip64 mapped into this process (there must be one)."""
+    seen = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                seen.add(line.split()[-1])
+    return sorted(seen)

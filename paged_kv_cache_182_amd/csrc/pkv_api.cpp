@@ -1,0 +1,213 @@
+// C ABI of libpkv: argument validation, partition sizing and launches.
+// The declarations and their documentation are in include/pkv.h.
+
+#include "../../include/pkv.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "pkv_internal.h"
+
+namespace {
+
+constexpr int kWorkgroupsWanted = 1024;  // about four workgroups per compute unit
+constexpr int kMinPartitionTokens = 256;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool valid_codec(int32_t c) { return c == PKV_CODEC_MIXED || (c >= PKV_FP16 && c <= PKV_INT4_G32); }
+
+// Checks the plain-value part of the params. Returns PKV_OK or an error.
+int check_params(const pkv_params* p) {
+  if (!p) return PKV_ERR_INVALID_ARG;
+  if (p->num_rows < 0 || p->num_q_heads <= 0 || p->num_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
+  if (p->num_q_heads % p->num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+  if (p->page_size <= 0 || p->page_size % 16 != 0) return PKV_ERR_INVALID_ARG;
+  if (p->num_pages < 0 || p->max_pages_per_row < 1 || p->max_sel_pages < 0) return PKV_ERR_INVALID_ARG;
+  if (p->partition_tokens < 0 || p->partition_tokens % p->page_size != 0) return PKV_ERR_INVALID_ARG;
+  if (!isfinite(p->softmax_scale)) return PKV_ERR_INVALID_ARG;
+  if (!valid_codec(p->k_codec) || !valid_codec(p->v_codec)) return PKV_ERR_INVALID_ARG;
+  if (p->head_dim != 64 && p->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (p->num_q_heads / p->num_kv_heads > 16) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+// Pages (dense) or selection entries (sparse) a row can reach at most.
+int64_t row_capacity(const pkv_params* p) {
+  return p->max_sel_pages > 0 ? p->max_sel_pages : p->max_pages_per_row;
+}
+
+// Pages per partition after resolving partition_tokens == 0.
+int64_t pages_per_partition(const pkv_params* p) {
+  const int64_t cap = row_capacity(p);
+  if (p->partition_tokens > 0) return p->partition_tokens / p->page_size;
+  const int64_t units = (int64_t)(p->num_rows > 0 ? p->num_rows : 1) * p->num_kv_heads;
+  int64_t parts = (kWorkgroupsWanted + units - 1) / units;
+  if (parts < 1) parts = 1;
+  int64_t ppp = (cap + parts - 1) / parts;
+  const int64_t min_pages = (kMinPartitionTokens + p->page_size - 1) / p->page_size;
+  if (ppp < min_pages) ppp = min_pages;
+  if (ppp > cap) ppp = cap;
+  return ppp < 1 ? 1 : ppp;
+}
+
+int64_t partitions(const pkv_params* p) {
+  const int64_t ppp = pages_per_partition(p);
+  return (row_capacity(p) + ppp - 1) / ppp;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pkv_num_partitions(const pkv_params* p) {
+  const int st = check_params(p);
+  if (st != PKV_OK) return st;
+  const int64_t n = partitions(p);
+  return n > 0x7fffffff ? PKV_ERR_UNSUPPORTED : (int)n;
+}
+
+size_t pkv_workspace_bytes(const pkv_params* p) {
+  if (check_params(p) != PKV_OK) return 0;
+  const int64_t n = partitions(p);
+  if (n <= 1) return 0;
+  return (size_t)p->num_rows * p->num_q_heads * n * (p->head_dim + 2) * sizeof(float);
+}
+
+namespace {
+
+// Validates the pointers and fills the launch description (not the outputs).
+int prepare(const pkv_params* p, const void* q, const uint8_t* page_pool,
+            const uint64_t* page_k_off, const uint64_t* page_v_off, const uint8_t* page_codec,
+            const float* page_scale, const int32_t* block_table, const int32_t* seq_lens,
+            const int32_t* page_sel, const int32_t* sel_lens, int32_t* err_count,
+            pkv::DecodeArgs* a) {
+  if (!q || !page_pool || !page_k_off || !page_v_off || !page_codec || !block_table || !seq_lens)
+    return PKV_ERR_INVALID_ARG;
+  const bool sparse = p->max_sel_pages > 0;
+  if (sparse != (page_sel != nullptr) || sparse != (sel_lens != nullptr)) return PKV_ERR_INVALID_ARG;
+  if ((p->k_codec == PKV_FP8_E4M3 || p->v_codec == PKV_FP8_E4M3) && !page_scale)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(page_pool, 256) || !aligned(page_k_off, 8) ||
+      !aligned(page_v_off, 8) || !aligned(block_table, 4) || !aligned(seq_lens, 4) ||
+      (page_scale && !aligned(page_scale, 4)) || (page_sel && !aligned(page_sel, 4)) ||
+      (sel_lens && !aligned(sel_lens, 4)) || (err_count && !aligned(err_count, 4)))
+    return PKV_ERR_INVALID_ARG;
+  const int64_t nparts = partitions(p);
+  if (nparts > 65535 || (int64_t)p->num_rows > 65535 || p->num_kv_heads > 65535)
+    return PKV_ERR_UNSUPPORTED;  // grid dimension limits
+
+  a->q = static_cast<const uint16_t*>(q);
+  a->pool = page_pool;
+  a->koff = page_k_off;
+  a->voff = page_v_off;
+  a->codec = page_codec;
+  a->scale = page_scale;
+  a->bt = block_table;
+  a->seq_lens = seq_lens;
+  a->sel = page_sel;
+  a->sel_lens = sel_lens;
+  a->out = nullptr;
+  a->lse = nullptr;
+  a->part_acc = nullptr;
+  a->part_ml = nullptr;
+  a->err = err_count;
+  a->rows = p->num_rows;
+  a->hq = p->num_q_heads;
+  a->hkv = p->num_kv_heads;
+  a->group = p->num_q_heads / p->num_kv_heads;
+  a->page = p->page_size;
+  a->num_pages = p->num_pages;
+  a->max_pages = p->max_pages_per_row;
+  a->max_sel = p->max_sel_pages;
+  a->pages_per_part = (int32_t)pages_per_partition(p);
+  a->nparts = (int32_t)nparts;
+  a->sparse = sparse ? 1 : 0;
+  a->final_out = 0;
+  a->scale_log2 = p->softmax_scale * 1.44269504088896340736f;
+  a->pool_bytes = p->pool_bytes;
+  return PKV_OK;
+}
+
+int launch_status(int st) { return st == 0 ? PKV_OK : (st == -2 ? PKV_ERR_UNSUPPORTED : PKV_ERR_HIP); }
+
+}  // namespace
+
+int pkv_decode_attention(const pkv_params* p, const void* q, const uint8_t* page_pool,
+                         const uint64_t* page_k_off, const uint64_t* page_v_off,
+                         const uint8_t* page_codec, const float* page_scale,
+                         const int32_t* block_table, const int32_t* seq_lens,
+                         const int32_t* page_sel, const int32_t* sel_lens, float* out,
+                         float* lse, void* workspace, size_t workspace_bytes,
+                         int32_t* err_count, void* stream) {
+  int st = check_params(p);
+  if (st != PKV_OK) return st;
+  if (p->num_rows == 0) return PKV_OK;
+  if (!out || !lse || !aligned(out, 4) || !aligned(lse, 4)) return PKV_ERR_INVALID_ARG;
+  pkv::DecodeArgs a;
+  st = prepare(p, q, page_pool, page_k_off, page_v_off, page_codec, page_scale, block_table,
+               seq_lens, page_sel, sel_lens, err_count, &a);
+  if (st != PKV_OK) return st;
+  if (a.nparts > 1) {
+    const size_t need = pkv_workspace_bytes(p);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return PKV_ERR_WORKSPACE;
+    a.part_acc = static_cast<float*>(workspace);
+    a.part_ml = a.part_acc + (size_t)p->num_rows * p->num_q_heads * a.nparts * p->head_dim;
+  } else {
+    a.out = out;
+    a.lse = lse;
+    a.final_out = 1;
+  }
+  st = launch_status(pkv::launch_decode(a, p->head_dim, p->k_codec, p->v_codec, stream));
+  if (st != PKV_OK || a.nparts == 1) return st;
+  return launch_status(pkv::launch_combine(p->num_rows * p->num_q_heads, a.nparts, p->head_dim,
+                                           a.part_acc, a.part_ml, out, lse, stream));
+}
+
+int pkv_decode_partials(const pkv_params* p, const void* q, const uint8_t* page_pool,
+                        const uint64_t* page_k_off, const uint64_t* page_v_off,
+                        const uint8_t* page_codec, const float* page_scale,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        const int32_t* page_sel, const int32_t* sel_lens, float* part_acc,
+                        float* part_ml, int32_t* err_count, void* stream) {
+  int st = check_params(p);
+  if (st != PKV_OK) return st;
+  if (p->num_rows == 0) return PKV_OK;
+  if (!part_acc || !part_ml || !aligned(part_acc, 16) || !aligned(part_ml, 16))
+    return PKV_ERR_INVALID_ARG;
+  pkv::DecodeArgs a;
+  st = prepare(p, q, page_pool, page_k_off, page_v_off, page_codec, page_scale, block_table,
+               seq_lens, page_sel, sel_lens, err_count, &a);
+  if (st != PKV_OK) return st;
+  a.part_acc = part_acc;
+  a.part_ml = part_ml;
+  return launch_status(pkv::launch_decode(a, p->head_dim, p->k_codec, p->v_codec, stream));
+}
+
+int pkv_lse_combine(int32_t rows, int32_t num_parts, int32_t head_dim, const float* part_acc,
+                    const float* part_ml, float* out, float* lse, void* stream) {
+  if (rows < 0 || num_parts < 1 || head_dim < 1 || head_dim > 512) return PKV_ERR_INVALID_ARG;
+  if (rows == 0) return PKV_OK;
+  if (!part_acc || !part_ml || !out || !lse) return PKV_ERR_INVALID_ARG;
+  if (!aligned(part_acc, 4) || !aligned(part_ml, 4) || !aligned(out, 4) || !aligned(lse, 4))
+    return PKV_ERR_INVALID_ARG;
+  if (rows > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+  return pkv::launch_combine(rows, num_parts, head_dim, part_acc, part_ml, out, lse, stream) == 0
+             ? PKV_OK
+             : PKV_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Internal interface between the C ABI shim (pkv_api.cpp) and the kernels
+// (pkv_kernels.hip). Not installed; no part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Everything one decode launch needs, resolved on the host.
+struct DecodeArgs {
+  const uint16_t* q;        // fp16 [B][Hq][D]
+  const uint8_t* pool;      // byte arena
+  const uint64_t* koff;     // [num_pages]
+  const uint64_t* voff;     // [num_pages]
+  const uint8_t* codec;     // [num_pages]
+  const float* scale;       // [num_pages][Hkv][2] or nullptr
+  const int32_t* bt;        // [B][max_pages]
+  const int32_t* seq_lens;  // [B]
+  const int32_t* sel;       // [B][max_sel] or nullptr
+  const int32_t* sel_lens;  // [B] or nullptr
+  float* out;               // [B][Hq][D]
+  float* lse;               // [B][Hq]
+  float* part_acc;          // [B*Hq][nparts][D]   (nparts > 1)
+  float* part_ml;           // [B*Hq][nparts][2]   (nparts > 1)
+  int32_t* err;             // device counter or nullptr
+  int32_t rows, hq, hkv, group, page, num_pages, max_pages, max_sel;
+  int32_t pages_per_part;   // pages (dense) or selection entries (sparse) per partition
+  int32_t nparts;
+  int32_t sparse;
+  int32_t final_out;        // 1: write out/lse (single partition); 0: write partials
+  float scale_log2;         // softmax_scale * log2(e)
+  uint64_t pool_bytes;      // size of the arena; planes must lie inside it
+};
+
+// Launches the decode kernel for (head_dim, k codec, v codec); codec -1 means
+// per-page dispatch. Returns 0 on success, -2 if no kernel exists for the
+// combination, -4 if the launch failed.
+int launch_decode(const DecodeArgs& a, int head_dim, int k_codec, int v_codec, void* stream);
+
+// Launches the log-sum-exp fold over `rows` rows of `nparts` partials.
+int launch_combine(int rows, int nparts, int head_dim, const float* part_acc,
+                   const float* part_ml, float* out, float* lse, void* stream);
+
+}  // namespace pkv

@@ -1,0 +1,715 @@
+// Decode attention over a mixed-codec paged KV cache, gfx950 (CDNA4).
+//
+// One workgroup of four 64-lane waves owns one (partition, KV head, row).
+// It first gathers the partition's page descriptors (selection entry ->
+// block table -> codec, plane offsets, FP8 scales) into LDS, then each wave
+// walks 16-token tiles of those pages: exact conversion of the codes to fp16
+// in registers, MFMA for the q.K scores and for P.V, and an exact online
+// softmax (ARGUS "Direct paged attention": tile-by-tile online softmax over
+// an SoA page table; FreeToken PR #499 "Design": block-table translation).
+// The waves' states are merged through LDS; a row split into several
+// partitions leaves (acc, max, sum) partials that a second kernel folds by
+// log-sum-exp (PR #499 discussion, in-place host K/V design).
+//
+// Tile layout seen by one wave (lane l, col = l % 16, kq = l / 16):
+//  * scores use v_mfma_f32_16x16x32_f16 with A = K (row = token col of the
+//    tile, 8 dims per lane) and B = q^T (col = query head of the group);
+//    lane l receives scores of tokens 4*kq + j (j = 0..3) for head col.
+//  * P.V uses v_mfma_f32_16x16x16_f16 with A = P (those same four scores,
+//    which is exactly the A operand layout) and B = V (4 tokens of one dim,
+//    which the V plane layout stores contiguously per lane); lane l
+//    accumulates out[head 4*kq + j][dim 16*n + col].
+// Every code converts to fp16 exactly (FP8 e4m3, int8, int4 and -- within
+// fp16 range -- bf16), so each product is exact and accumulates in fp32;
+// scales are applied in fp32 to the scores (K) or folded into P (V).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+enum : int { C_FP16 = 0, C_BF16 = 1, C_FP8 = 2, C_INT8 = 3, C_INT4 = 4, C_ANY = 15 };
+
+constexpr int WAVES = 4;
+constexpr int THREADS = 64 * WAVES;
+constexpr int MAX_DESC = 256;  // page descriptors staged in LDS at a time
+constexpr float NEG_INF = -__builtin_huge_valf();
+constexpr float LN2 = 0.693147180559945309f;
+
+__host__ __device__ constexpr int bits_of(int c) { return c <= C_BF16 ? 16 : (c == C_INT4 ? 4 : 8); }
+__host__ __device__ constexpr bool is_int(int c) { return c == C_INT8 || c == C_INT4; }
+
+// Bytes of one plane (codes of every head, then INT group scales).
+__device__ inline uint64_t plane_bytes(int c, int hkv, int page, int d) {
+  const uint64_t codes = (uint64_t)hkv * page * d * bits_of(c) / 8;
+  return codes + (is_int(c) ? (uint64_t)hkv * page * (d / 32) * 2 : 0);
+}
+
+// Page descriptor staged in LDS (32 bytes).
+struct Desc {
+  uint64_t k;      // address of the K plane (0 if the page is skipped)
+  uint64_t v;      // address of the V plane
+  float sk, sv;    // FP8 scales of this KV head (1 for other codecs)
+  int32_t valid;   // attended tokens of the page (0 if skipped)
+  int32_t codec;   // K codec | V codec << 4
+};
+
+// Raw codes of one 16-token tile for one lane. Sizes per codec class; the
+// per-page dispatch variant (C_ANY) reserves the largest.
+template <int D, int KC, int VC>
+struct Tile {
+  static constexpr int KB = KC == C_ANY ? 16 : bits_of(KC);
+  static constexpr int VB = VC == C_ANY ? 16 : bits_of(VC);
+  static constexpr int KW = D * KB / 128;  // 32-bit words of K codes per lane
+  static constexpr int VW = D * VB / 128;
+  static constexpr int SW = D / 16;        // words of 4 tokens x D/32 fp16 scales
+  static constexpr bool KS = KC == C_ANY || is_int(KC);
+  static constexpr bool VS = VC == C_ANY || is_int(VC);
+  uint32_t k[KW];
+  uint32_t v[VW];
+  uint32_t ks[KS ? SW : 1];
+  uint32_t vs[VS ? SW : 1];
+};
+
+struct TileInfo {
+  int valid;  // tokens of the tile to attend (0: skip the tile)
+  int kc, vc;
+  float sk, sv;
+};
+
+__device__ inline void count_error(int32_t* err) {
+  if (err) atomicAdd(err, 1);
+}
+
+__device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline uint64_t uni64(uint64_t x) {
+  uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ inline float unif(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+// ---------------------------------------------------------------- loads
+// K: lane reads token `tok` of the head block, dims 32c + 8kq .. +7 for each c.
+template <int D, int C>
+__device__ inline void load_k(uint32_t* w, const uint8_t* head, int tok, int kq) {
+  constexpr int NC = D / 32;
+  if constexpr (bits_of(C) == 16) {
+    const uint8_t* p = head + (size_t)(tok * D + 8 * kq) * 2;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u4 x = *reinterpret_cast<const u4*>(p + 64 * c);
+      w[4 * c + 0] = x[0]; w[4 * c + 1] = x[1]; w[4 * c + 2] = x[2]; w[4 * c + 3] = x[3];
+    }
+  } else if constexpr (bits_of(C) == 8) {
+    const uint8_t* p = head + (size_t)(tok * D + 8 * kq);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u2 x = *reinterpret_cast<const u2*>(p + 32 * c);
+      w[2 * c + 0] = x[0]; w[2 * c + 1] = x[1];
+    }
+  } else {
+    const uint8_t* p = head + (size_t)(tok * D + 8 * kq) / 2;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) w[c] = *reinterpret_cast<const uint32_t*>(p + 16 * c);
+  }
+}
+
+// V: lane l reads its contiguous run of D/4 elements inside the tile.
+template <int D, int C>
+__device__ inline void load_v(uint32_t* w, const uint8_t* head, int sub, int lane) {
+  constexpr int RUN_BYTES = D * bits_of(C) / 32;
+  const uint8_t* p = head + ((size_t)sub * 16 * D + (size_t)lane * (D / 4)) * bits_of(C) / 8;
+  if constexpr (RUN_BYTES >= 16) {
+#pragma unroll
+    for (int i = 0; i < RUN_BYTES / 16; ++i) {
+      u4 x = *reinterpret_cast<const u4*>(p + 16 * i);
+      w[4 * i + 0] = x[0]; w[4 * i + 1] = x[1]; w[4 * i + 2] = x[2]; w[4 * i + 3] = x[3];
+    }
+  } else {
+    u2 x = *reinterpret_cast<const u2*>(p);
+    w[0] = x[0]; w[1] = x[1];
+  }
+}
+
+// Group scales of tokens tok0 .. tok0+3, all D/32 groups (fp16, token-major).
+template <int D>
+__device__ inline void load_scales(uint32_t* w, const uint8_t* p) {
+  if constexpr (D == 128) {
+    u4 x = *reinterpret_cast<const u4*>(p);
+    u4 y = *reinterpret_cast<const u4*>(p + 16);
+    w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
+    w[4] = y[0]; w[5] = y[1]; w[6] = y[2]; w[7] = y[3];
+  } else {
+    u4 x = *reinterpret_cast<const u4*>(p);
+    w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
+  }
+}
+
+// ---------------------------------------------------------------- decode
+__device__ inline h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
+
+// two bf16 -> two fp16 (exact inside fp16 range)
+__device__ inline h2 bf16x2(uint32_t w) {
+  float lo = __builtin_bit_cast(float, w << 16);
+  float hi = __builtin_bit_cast(float, w & 0xffff0000u);
+  return h2{(_Float16)lo, (_Float16)hi};
+}
+
+// two OCP e4m3 codes (bytes 0,1 or 2,3 of w) -> two fp16 (exact)
+template <bool HI>
+__device__ inline h2 fp8x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+
+// four int8 codes -> four fp16 (exact): 0x64XX is 1024 + XX, XX = code + 128
+__device__ inline h4 int8x4(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  const h2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  h2 a = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - off;
+  h2 b = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - off;
+  return h4{a[0], a[1], b[0], b[1]};
+}
+
+// eight int4 codes of one word -> fp16 pairs (elements 0,1 | 2,3 | 4,5 | 6,7)
+__device__ inline void int4x8(uint32_t w, h2* o) {
+  const uint32_t u = w ^ 0x88888888u;
+  const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) o[s] = as_h2(((u >> (4 * s)) & 0x000f000fu) | 0x64006400u) - off;
+}
+
+// A operand of the score MFMA: dims 32c + 8kq .. +7 of the lane's token.
+template <int C, int D>
+__device__ inline h8 k_frag(const uint32_t* w, int c) {
+  if constexpr (C == C_FP16) {
+    return __builtin_bit_cast(h8, u4{w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]});
+  } else if constexpr (C == C_BF16) {
+    h2 a = bf16x2(w[4 * c]), b = bf16x2(w[4 * c + 1]), d = bf16x2(w[4 * c + 2]), e = bf16x2(w[4 * c + 3]);
+    return h8{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
+  } else if constexpr (C == C_FP8) {
+    h2 a = fp8x2<false>(w[2 * c]), b = fp8x2<true>(w[2 * c]);
+    h2 d = fp8x2<false>(w[2 * c + 1]), e = fp8x2<true>(w[2 * c + 1]);
+    return h8{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
+  } else if constexpr (C == C_INT8) {
+    h4 a = int8x4(w[2 * c]), b = int8x4(w[2 * c + 1]);
+    return h8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  } else {
+    h2 o[4];
+    int4x8(w[c], o);
+    return h8{o[0][0], o[0][1], o[1][0], o[1][1], o[2][0], o[2][1], o[3][0], o[3][1]};
+  }
+}
+
+// B operand of the P.V MFMA: tokens 4kq .. +3 of dim 16n + col.
+template <int C, int D>
+__device__ inline h4 v_frag(const uint32_t* w, int n) {
+  if constexpr (C == C_FP16) {
+    return __builtin_bit_cast(h4, u2{w[2 * n], w[2 * n + 1]});
+  } else if constexpr (C == C_BF16) {
+    h2 a = bf16x2(w[2 * n]), b = bf16x2(w[2 * n + 1]);
+    return h4{a[0], a[1], b[0], b[1]};
+  } else if constexpr (C == C_FP8) {
+    h2 a = fp8x2<false>(w[n]), b = fp8x2<true>(w[n]);
+    return h4{a[0], a[1], b[0], b[1]};
+  } else if constexpr (C == C_INT8) {
+    return int8x4(w[n]);
+  } else {
+    h2 o[4];
+    int4x8(w[n / 2], o);
+    return (n & 1) ? h4{o[2][0], o[2][1], o[3][0], o[3][1]} : h4{o[0][0], o[0][1], o[1][0], o[1][1]};
+  }
+}
+
+// Runtime-dispatched variants for pages of mixed codecs.
+template <int D>
+__device__ inline h8 k_frag_any(const uint32_t* w, int c, int codec) {
+  switch (codec) {
+    case C_FP16: return k_frag<C_FP16, D>(w, c);
+    case C_BF16: return k_frag<C_BF16, D>(w, c);
+    case C_FP8: return k_frag<C_FP8, D>(w, c);
+    case C_INT8: return k_frag<C_INT8, D>(w, c);
+    default: return k_frag<C_INT4, D>(w, c);
+  }
+}
+template <int D>
+__device__ inline h4 v_frag_any(const uint32_t* w, int n, int codec) {
+  switch (codec) {
+    case C_FP16: return v_frag<C_FP16, D>(w, n);
+    case C_BF16: return v_frag<C_BF16, D>(w, n);
+    case C_FP8: return v_frag<C_FP8, D>(w, n);
+    case C_INT8: return v_frag<C_INT8, D>(w, n);
+    default: return v_frag<C_INT4, D>(w, n);
+  }
+}
+
+template <int D, int C>
+__device__ inline void load_k_c(uint32_t* w, const uint8_t* plane, int h, int page, int tok, int kq) {
+  load_k<D, C>(w, plane + (size_t)h * page * D * bits_of(C) / 8, tok, kq);
+}
+template <int D, int C>
+__device__ inline void load_v_c(uint32_t* w, const uint8_t* plane, int h, int page, int sub, int lane) {
+  load_v<D, C>(w, plane + (size_t)h * page * D * bits_of(C) / 8, sub, lane);
+}
+
+// Issue the loads of tile `k` of the staged pages into `t`.
+template <int D, int KC, int VC>
+__device__ inline TileInfo issue_tile(Tile<D, KC, VC>& t, const Desc* desc, int k, int tpp,
+                                      const DecodeArgs& a, int h, int lane) {
+  const int i = k / tpp;
+  const int sub = k - i * tpp;
+  TileInfo ti;
+  const int pvalid = uni(desc[i].valid);
+  ti.valid = min(max(pvalid - 16 * sub, 0), 16);
+  if (ti.valid == 0) return ti;
+  const int codec = uni(desc[i].codec);
+  ti.kc = KC == C_ANY ? (codec & 15) : KC;
+  ti.vc = VC == C_ANY ? (codec >> 4) : VC;
+  ti.sk = unif(desc[i].sk);
+  ti.sv = unif(desc[i].sv);
+  const uint8_t* kp = reinterpret_cast<const uint8_t*>(uni64(desc[i].k));
+  const uint8_t* vp = reinterpret_cast<const uint8_t*>(uni64(desc[i].v));
+  const int col = lane & 15, kq = lane >> 4;
+  const int tok = 16 * sub + col;
+  const int page = a.page;
+  if constexpr (KC == C_ANY) {
+    switch (ti.kc) {
+      case C_FP16: case C_BF16: load_k_c<D, C_FP16>(t.k, kp, h, page, tok, kq); break;
+      case C_FP8: case C_INT8: load_k_c<D, C_FP8>(t.k, kp, h, page, tok, kq); break;
+      default: load_k_c<D, C_INT4>(t.k, kp, h, page, tok, kq); break;
+    }
+  } else {
+    load_k_c<D, KC>(t.k, kp, h, page, tok, kq);
+  }
+  if constexpr (VC == C_ANY) {
+    switch (ti.vc) {
+      case C_FP16: case C_BF16: load_v_c<D, C_FP16>(t.v, vp, h, page, sub, lane); break;
+      case C_FP8: case C_INT8: load_v_c<D, C_FP8>(t.v, vp, h, page, sub, lane); break;
+      default: load_v_c<D, C_INT4>(t.v, vp, h, page, sub, lane); break;
+    }
+  } else {
+    load_v_c<D, VC>(t.v, vp, h, page, sub, lane);
+  }
+  const size_t tok0 = (size_t)h * page + 16 * sub + 4 * kq;
+  if constexpr (Tile<D, KC, VC>::KS) {
+    if (is_int(ti.kc)) {
+      const size_t codes = (size_t)a.hkv * page * D * bits_of(ti.kc) / 8;
+      load_scales<D>(t.ks, kp + codes + tok0 * (D / 32) * 2);
+    }
+  }
+  if constexpr (Tile<D, KC, VC>::VS) {
+    if (is_int(ti.vc)) {
+      const size_t codes = (size_t)a.hkv * page * D * bits_of(ti.vc) / 8;
+      load_scales<D>(t.vs, vp + codes + tok0 * (D / 32) * 2);
+    }
+  }
+  return ti;
+}
+
+__device__ inline f4 mfma32(h8 a, h8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ inline f4 mfma16(h4 a, h4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// Scores, online-softmax update and P.V of one staged tile.
+template <int D, int KC, int VC>
+__device__ inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti, const h8* qv,
+                                    float scale_log2, float& m_run, float& l_run, f4* acc,
+                                    int lane) {
+  constexpr int NC = D / 32, NB = D / 16;
+  if (ti.valid == 0) return;
+  const int kq = lane >> 4;
+  const f4 zero = {0.f, 0.f, 0.f, 0.f};
+  float s[4];
+  const bool kgrouped = KC == C_ANY ? is_int(ti.kc) : is_int(KC);
+  if (KC == C_ANY || is_int(KC)) {
+    // one accumulator per 32-dim group, scaled per (token, group)
+    f4 sc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      h8 kf = KC == C_ANY ? k_frag_any<D>(t.k, c, ti.kc) : k_frag<KC == C_ANY ? 0 : KC, D>(t.k, c);
+      sc[c] = mfma32(kf, qv[c], zero);
+    }
+    if (kgrouped) {
+      const _Float16* ks = reinterpret_cast<const _Float16*>(t.ks);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float x = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) x += (float)ks[j * NC + c] * sc[c][j];
+        s[j] = x * scale_log2;
+      }
+    } else {
+      const float f = scale_log2 * ti.sk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float x = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) x += sc[c][j];
+        s[j] = x * f;
+      }
+    }
+  } else {
+    f4 sc = zero;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) sc = mfma32(k_frag<KC, D>(t.k, c), qv[c], sc);
+    const float f = scale_log2 * ti.sk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[j] = sc[j] * f;
+  }
+  const bool partial = ti.valid < 16;
+  if (partial) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[j] = (4 * kq + j < ti.valid) ? s[j] : NEG_INF;
+  }
+
+  // online softmax over this tile's 16 tokens (lanes col, col+16, col+32, col+48)
+  float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m_run, mx);
+  if (__any(m_new > m_run)) {
+    const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+    l_run *= alpha;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float aj = __shfl(alpha, 4 * kq + j);
+#pragma unroll
+      for (int n = 0; n < NB; ++n) acc[n][j] *= aj;
+    }
+    m_run = m_new;
+  }
+  const float mu = m_run == NEG_INF ? 0.f : m_run;
+  float p[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(s[j] - mu);
+  l_run += (p[0] + p[1]) + (p[2] + p[3]);
+
+  // P.V
+  const bool vgrouped = VC == C_ANY ? is_int(ti.vc) : is_int(VC);
+  h4 pa[NC];
+  if (vgrouped) {
+    const _Float16* vs = reinterpret_cast<const _Float16*>(t.vs);
+#pragma unroll
+    for (int g = 0; g < NC; ++g)
+      pa[g] = h4{(_Float16)(p[0] * (float)vs[0 * NC + g]), (_Float16)(p[1] * (float)vs[1 * NC + g]),
+                 (_Float16)(p[2] * (float)vs[2 * NC + g]), (_Float16)(p[3] * (float)vs[3 * NC + g])};
+  } else {
+    const float f = ti.sv;
+    pa[0] = h4{(_Float16)(p[0] * f), (_Float16)(p[1] * f), (_Float16)(p[2] * f), (_Float16)(p[3] * f)};
+#pragma unroll
+    for (int g = 1; g < NC; ++g) pa[g] = pa[0];
+  }
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    h4 vf = VC == C_ANY ? v_frag_any<D>(t.v, n, ti.vc) : v_frag<VC == C_ANY ? 0 : VC, D>(t.v, n);
+    if (partial) {
+      // tail tokens may hold any bytes (even NaN codes): zero them, P is 0 there
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vf[j] = (4 * kq + j < ti.valid) ? vf[j] : (_Float16)0.0f;
+    }
+    acc[n] = mfma16(pa[n / 2], vf, acc[n]);
+  }
+}
+
+template <int D, int KC, int VC>
+__global__ void __launch_bounds__(THREADS) decode_kernel(const DecodeArgs a) {
+  constexpr int NC = D / 32, NB = D / 16;
+  constexpr int RED_BYTES = (WAVES * 16 * D + 2 * WAVES * 16) * 4;
+  constexpr int DESC_BYTES = MAX_DESC * (int)sizeof(Desc);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[RED_BYTES > DESC_BYTES ? RED_BYTES : DESC_BYTES];
+  Desc* desc = reinterpret_cast<Desc*>(smem);
+
+  const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, kq = lane >> 4;
+  const int G = a.group;
+  const int P = a.page;
+
+  // ---- extent of this row and of this partition
+  int L = a.seq_lens[b];
+  const bool report_row = part == 0 && h == 0 && tid == 0;
+  if (L < 0) {
+    if (report_row) count_error(a.err);
+    L = 0;
+  }
+  int npg;
+  if (a.sparse) {
+    npg = a.sel_lens[b];
+    if (npg < 0 || npg > a.max_sel) {
+      if (report_row) count_error(a.err);
+      npg = min(max(npg, 0), a.max_sel);
+    }
+  } else {
+    npg = L / P + (L % P != 0);
+    if (npg > a.max_pages) {
+      if (report_row) count_error(a.err);
+      npg = a.max_pages;
+    }
+  }
+  const int s0 = part * a.pages_per_part;
+  const int s1 = min(s0 + a.pages_per_part, npg);
+
+  // ---- q of this KV head's query group (B operand of the score MFMA)
+  h8 qv[NC];
+  {
+    const _Float16* qp = reinterpret_cast<const _Float16*>(a.q) +
+                         ((size_t)b * a.hq + (size_t)h * G + col) * D + 8 * kq;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (col < G) {
+        qv[c] = *reinterpret_cast<const h8*>(qp + 32 * c);
+      } else {
+        qv[c] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+  }
+
+  float m_run = NEG_INF, l_run = 0.f;
+  f4 acc[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) acc[n] = f4{0.f, 0.f, 0.f, 0.f};
+
+  const int tpp = P / 16;
+  for (int cbase = s0; cbase < s1; cbase += MAX_DESC) {
+    const int cn = min(MAX_DESC, s1 - cbase);
+    __syncthreads();
+    if (tid < cn) {
+      const int s = cbase + tid;
+      Desc d;
+      d.k = 0; d.v = 0; d.sk = 1.f; d.sv = 1.f; d.valid = 0; d.codec = 0;
+      bool ok = true;
+      const int lp = a.sparse ? a.sel[(size_t)b * a.max_sel + s] : s;
+      if ((unsigned)lp >= (unsigned)a.max_pages) ok = false;
+      int pp = -1;
+      if (ok) {
+        pp = a.bt[(size_t)b * a.max_pages + lp];
+        if ((unsigned)pp >= (unsigned)a.num_pages) ok = false;
+      }
+      int kc = 0, vc = 0, cod = 0;
+      if (ok) {
+        cod = a.codec[pp];
+        kc = cod & 15;
+        vc = cod >> 4;
+        if (kc > C_INT4 || vc > C_INT4) ok = false;
+        if (KC != C_ANY && kc != KC) ok = false;
+        if (VC != C_ANY && vc != VC) ok = false;
+        if ((kc == C_FP8 || vc == C_FP8) && a.scale == nullptr) ok = false;
+      }
+      uint64_t ko = 0, vo = 0;
+      if (ok) {
+        ko = a.koff[pp];
+        vo = a.voff[pp];
+        if ((ko | vo) & 15) ok = false;
+        if (ko > a.pool_bytes || a.pool_bytes - ko < plane_bytes(kc, a.hkv, P, D)) ok = false;
+        if (vo > a.pool_bytes || a.pool_bytes - vo < plane_bytes(vc, a.hkv, P, D)) ok = false;
+      }
+      if (ok) {
+        const long long rem = (long long)L - (long long)lp * P;
+        d.valid = (int)(rem < 0 ? 0 : (rem > P ? P : rem));
+        d.k = (uint64_t)(a.pool + ko);
+        d.v = (uint64_t)(a.pool + vo);
+        if (kc == C_FP8) d.sk = a.scale[((size_t)pp * a.hkv + h) * 2 + 0];
+        if (vc == C_FP8) d.sv = a.scale[((size_t)pp * a.hkv + h) * 2 + 1];
+        d.codec = cod;
+      } else if (h == 0) {
+        count_error(a.err);
+      }
+      desc[tid] = d;
+    }
+    __syncthreads();
+
+    const int ntiles = cn * tpp;
+    Tile<D, KC, VC> ta, tb;
+    TileInfo ia, ib;
+    int k = wave;
+    if (k < ntiles) ia = issue_tile<D, KC, VC>(ta, desc, k, tpp, a, h, lane);
+    while (k < ntiles) {
+      const int k2 = k + WAVES;
+      if (k2 < ntiles) ib = issue_tile<D, KC, VC>(tb, desc, k2, tpp, a, h, lane);
+      consume_tile<D, KC, VC>(ta, ia, qv, a.scale_log2, m_run, l_run, acc, lane);
+      k = k2;
+      if (k >= ntiles) break;
+      const int k3 = k + WAVES;
+      if (k3 < ntiles) ia = issue_tile<D, KC, VC>(ta, desc, k3, tpp, a, h, lane);
+      consume_tile<D, KC, VC>(tb, ib, qv, a.scale_log2, m_run, l_run, acc, lane);
+      k = k3;
+    }
+  }
+
+  // ---- merge the four waves' (m, l, acc) through LDS
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  __syncthreads();
+  float* red_acc = reinterpret_cast<float*>(smem);
+  float* red_m = red_acc + WAVES * 16 * D;
+  float* red_l = red_m + WAVES * 16;
+  if (lane < 16) {
+    red_m[wave * 16 + lane] = m_run;
+    red_l[wave * 16 + lane] = l_run;
+  }
+#pragma unroll
+  for (int n = 0; n < NB; ++n)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red_acc[(wave * 16 + 4 * kq + j) * D + 16 * n + col] = acc[n][j];
+  __syncthreads();
+
+  for (int idx = tid; idx < G * D; idx += THREADS) {
+    const int g = idx / D, d = idx - g * D;
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, red_m[w * 16 + g]);
+    float Ls = 0.f, A = 0.f;
+    if (M != NEG_INF) {
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float mw = red_m[w * 16 + g];
+        if (mw != NEG_INF) {
+          const float e = __builtin_amdgcn_exp2f(mw - M);
+          Ls += e * red_l[w * 16 + g];
+          A += e * red_acc[(w * 16 + g) * D + d];
+        }
+      }
+    }
+    const size_t row = (size_t)b * a.hq + (size_t)h * G + g;
+    if (a.final_out) {
+      a.out[row * D + d] = Ls > 0.f ? A / Ls : 0.f;
+      if (d == 0) a.lse[row] = Ls > 0.f ? M * LN2 + logf(Ls) : NEG_INF;
+    } else {
+      const size_t pi = row * a.nparts + part;
+      a.part_acc[pi * D + d] = A;
+      if (d == 0) {
+        a.part_ml[2 * pi + 0] = Ls > 0.f ? M * LN2 : NEG_INF;
+        a.part_ml[2 * pi + 1] = Ls;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fold
+// One workgroup per row. Thread t handles 4 dims (t % (D/4)) of the parts
+// p = t / (D/4) + k * groups, ascending; the groups are then summed in a
+// fixed order, so the result is run-to-run identical.
+__global__ void __launch_bounds__(256) combine_kernel(int nparts, int D, const float* __restrict__ part_acc,
+                                                      const float* __restrict__ part_ml,
+                                                      float* __restrict__ out, float* __restrict__ lse) {
+  __shared__ float red[256 * 4 + 256];
+  __shared__ float s_M;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const float* ml = part_ml + (size_t)row * nparts * 2;
+  const float* acc = part_acc + (size_t)row * nparts * D;
+
+  float M = NEG_INF;
+  for (int p = tid; p < nparts; p += 256) {
+    const float m = ml[2 * p], l = ml[2 * p + 1];
+    if (l > 0.f) M = fmaxf(M, m);
+  }
+  red[tid] = M;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+    __syncthreads();
+  }
+  if (tid == 0) s_M = red[0];
+  __syncthreads();
+  M = s_M;
+  __syncthreads();
+
+  const int lanes_per_part = (D + 3) / 4;             // threads covering one part's dims
+  const int groups = 256 / lanes_per_part;            // part groups
+  const int dl = tid % lanes_per_part, pg = tid / lanes_per_part;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, L = 0.f;
+  if (pg < groups && M != NEG_INF) {
+    for (int p = pg; p < nparts; p += groups) {
+      const float m = ml[2 * p], l = ml[2 * p + 1];
+      if (!(l > 0.f)) continue;
+      const float w = __expf(m - M);
+      L += w * l;
+      const float* ap = acc + (size_t)p * D + 4 * dl;
+      if (4 * dl + 3 < D) {
+        a0 += w * ap[0]; a1 += w * ap[1]; a2 += w * ap[2]; a3 += w * ap[3];
+      } else {
+        if (4 * dl + 0 < D) a0 += w * ap[0];
+        if (4 * dl + 1 < D) a1 += w * ap[1];
+        if (4 * dl + 2 < D) a2 += w * ap[2];
+      }
+    }
+  }
+  red[tid * 4 + 0] = a0; red[tid * 4 + 1] = a1; red[tid * 4 + 2] = a2; red[tid * 4 + 3] = a3;
+  red[1024 + tid] = L;
+  __syncthreads();
+  if (pg == 0) {
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f, Ls = 0.f;
+    for (int g = 0; g < groups; ++g) {
+      const int t = g * lanes_per_part + dl;
+      s0 += red[t * 4 + 0]; s1 += red[t * 4 + 1]; s2 += red[t * 4 + 2]; s3 += red[t * 4 + 3];
+      Ls += red[1024 + t];
+    }
+    float* o = out + (size_t)row * D + 4 * dl;
+    const bool any = M != NEG_INF && Ls > 0.f;
+    const float inv = any ? 1.f / Ls : 0.f;
+    if (4 * dl + 0 < D) o[0] = any ? s0 / Ls : 0.f;
+    if (4 * dl + 1 < D) o[1] = any ? s1 / Ls : 0.f;
+    if (4 * dl + 2 < D) o[2] = any ? s2 / Ls : 0.f;
+    if (4 * dl + 3 < D) o[3] = any ? s3 / Ls : 0.f;
+    (void)inv;
+    if (dl == 0) lse[row] = any ? M + logf(Ls) : NEG_INF;
+  }
+}
+
+template <int D, int KC, int VC>
+int launch_t(const DecodeArgs& a, hipStream_t s) {
+  dim3 grid(a.nparts, a.hkv, a.rows);
+  hipLaunchKernelGGL((decode_kernel<D, KC, VC>), grid, dim3(THREADS), 0, s, a);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+template <int D>
+int launch_d(const DecodeArgs& a, int kc, int vc, hipStream_t s) {
+#define PKV_PAIR(K, V) \
+  if (kc == K && vc == V) return launch_t<D, K, V>(a, s);
+  PKV_PAIR(C_FP16, C_FP16)
+  PKV_PAIR(C_BF16, C_BF16)
+  PKV_PAIR(C_FP8, C_FP8)
+  PKV_PAIR(C_INT8, C_INT4)
+  PKV_PAIR(C_INT8, C_INT8)
+  PKV_PAIR(C_INT4, C_INT4)
+#undef PKV_PAIR
+  return launch_t<D, C_ANY, C_ANY>(a, s);
+}
+
+}  // namespace
+
+int launch_decode(const DecodeArgs& a, int head_dim, int k_codec, int v_codec, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int kc = k_codec < 0 ? C_ANY : k_codec;
+  const int vc = v_codec < 0 ? C_ANY : v_codec;
+  if (head_dim == 128) return launch_d<128>(a, kc, vc, s);
+  if (head_dim == 64) return launch_d<64>(a, kc, vc, s);
+  return -2;
+}
+
+int launch_combine(int rows, int nparts, int head_dim, const float* part_acc, const float* part_ml,
+                   float* out, float* lse, void* stream) {
+  if (rows == 0) return 0;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(256), 0, s, nparts, head_dim, part_acc, part_ml,
+                     out, lse);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // namespace pkv

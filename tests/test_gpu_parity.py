@@ -1,0 +1,189 @@
+"""HIP path vs the float64 oracle on small and ragged workloads (GPU).
+
+Tolerances: max-abs 1e-3 on out and 1e-4 on lse, the bar set for the
+workloads; empty rows must give out = 0 and lse = -inf exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_182_amd as pkv
+import synth
+from synth.device import to_device
+from synth.layout import BF16, FP8, FP16, INT4, INT8
+from gpu_util import compare, params_for, poison_tails, run
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [(FP16, FP16), (BF16, BF16), (FP8, FP8), (INT8, INT4), (INT8, INT8), (INT4, INT4),
+         (FP8, FP16), (INT4, FP8), (FP16, INT8)]
+
+
+def small(seq_lens, kc, vc, hq, hkv, dim, page, seed=7, **kw):
+    return synth.build_workload(f"gpu_{kc}{vc}", rows=len(seq_lens), hq=hq, hkv=hkv, dim=dim,
+                                page=page, seq_lens=seq_lens,
+                                codec_of=kw.pop("codec_of", lambda r, lp: (kc, vc)), seed=seed, **kw)
+
+
+def check(w, partition_tokens=None, what="", **pk):
+    dw = to_device(w)
+    out, lse = run(dw, params_for(w, partition_tokens, **pk))
+    ref_out, ref_lse = oracle.decode_attention(w)
+    return compare(out, lse, ref_out, ref_lse, what or w.name)
+
+
+@pytest.mark.parametrize("kc,vc", PAIRS)
+@pytest.mark.parametrize("dim", [64, 128])
+def test_codec_pairs_ragged(kc, vc, dim):
+    print(f"case codecs=({kc},{vc}) dim={dim}", flush=True)
+    w = poison_tails(small([1, 15, 17, 300, 513], kc, vc, hq=8, hkv=2, dim=dim, page=32))
+    check(w, partition_tokens=64)
+    check(w, partition_tokens=0)
+
+
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (4, 1), (14, 2), (16, 2), (32, 8), (16, 1)])
+def test_group_sizes(hq, hkv):
+    print(f"case hq={hq} hkv={hkv}", flush=True)
+    w = poison_tails(small([77, 250], FP8, FP8, hq=hq, hkv=hkv, dim=128, page=16))
+    check(w, partition_tokens=64)
+
+
+def test_mixed_codecs_per_page():
+    print("case mixed", flush=True)
+    cyc = [(FP16, FP16), (FP8, FP8), (INT8, INT4), (BF16, INT8), (INT4, FP16)]
+    w = poison_tails(small([40, 333, 160], None, None, hq=8, hkv=2, dim=128, page=16,
+                           codec_of=lambda r, lp: cyc[(r + lp) % len(cyc)]))
+    check(w, partition_tokens=32)
+    check(w, partition_tokens=0)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_configs_small(cid):
+    print(f"case config {cid} small", flush=True)
+    w = synth.config(cid, small=cid != 1)
+    if not w.sparse:
+        poison_tails(w)
+    check(w)
+
+
+def test_partition_invariance_and_determinism():
+    print("case partition invariance", flush=True)
+    w = small([2000, 1111], FP8, FP8, hq=16, hkv=2, dim=128, page=16, q_scale=3.0)
+    dw = to_device(w)
+    res = []
+    for T in (16, 64, 512, 2048):
+        o, l = run(dw, params_for(w, T))
+        res.append((o, l))
+    for o, l in res[1:]:
+        assert np.max(np.abs(o - res[0][0])) <= 1e-5 and np.max(np.abs(l - res[0][1])) <= 1e-5
+    o2, l2 = run(dw, params_for(w, 64))
+    assert np.array_equal(o2, res[1][0]) and np.array_equal(l2, res[1][1])
+
+
+def test_empty_rows_and_partitions():
+    print("case empty", flush=True)
+    w = small([0, 5, 0, 1000], INT8, INT4, hq=8, hkv=2, dim=128, page=16)
+    check(w, partition_tokens=16)
+    ws = synth.config(4, small=True)
+    ws.sel_lens[0] = 0
+    ws.sel_lens[2] = 3
+    check(ws)
+
+
+def test_sparse_selection_order_and_unselected_poison():
+    print("case sparse order", flush=True)
+    w = synth.config(4, small=True)
+    dw = to_device(w)
+    p = params_for(w)
+    o1, l1 = run(dw, p)
+    rng = np.random.default_rng(1)
+    for r in range(w.rows):
+        w.page_sel[r] = rng.permutation(w.page_sel[r])
+    dw2 = to_device(w)
+    o2, l2 = run(dw2, p)
+    ref = oracle.decode_attention(w)
+    compare(o2, l2, *ref, "shuffled selection")
+    assert np.max(np.abs(o1 - o2)) <= 1e-5 and np.max(np.abs(l1 - l2)) <= 1e-5
+
+
+def test_device_errors_counted_and_skipped():
+    print("case device errors", flush=True)
+    w = small([64, 64, 64], FP8, FP8, hq=8, hkv=2, dim=128, page=16)
+    dw = to_device(w)
+    bt = w.block_table.copy()
+    bt[0, 1] = w.num_pages + 5          # out-of-range physical page
+    bt[1, 2] = -3
+    dw.block_table = torch.from_numpy(bt).cuda()
+    codec = w.page_codec.copy()
+    codec[int(w.block_table[2, 0])] = 0x99   # unknown codec nibbles
+    dw.page_codec = torch.from_numpy(codec).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, lse = run(dw, params_for(w, 16, k_codec=FP8, v_codec=FP8), err=err)
+    assert int(err.item()) == 3
+    # expected: each row without its bad page (sparse oracle over the good pages)
+    sel = np.array([[0, 2, 3], [0, 1, 3], [1, 2, 3]], dtype=np.int32)
+    w.page_sel, w.sel_lens = sel, np.full(3, 3, dtype=np.int32)
+    ref = oracle.decode_attention(w)
+    compare(out, lse, *ref, "bad pages skipped")
+
+
+def test_declared_codec_mismatch_is_counted():
+    print("case codec mismatch", flush=True)
+    w = small([48], INT8, INT4, hq=4, hkv=1, dim=64, page=16)
+    dw = to_device(w)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, lse = run(dw, params_for(w, 16, k_codec=FP8, v_codec=FP8), err=err)
+    assert int(err.item()) == 3 and np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+# ------------------------------------------------- every code, exactly (V path)
+def one_token_v_codes(codec, codes_for_row):
+    """Workload with one token per row whose V values are given codes; q = 0
+    makes out = V of that token exactly."""
+    rows = len(codes_for_row)
+    w = small([1] * rows, FP16, codec, hq=2, hkv=1, dim=128, page=16)
+    from oracle.layout import BITS, element_index
+    arr = w.pool.as_array()
+    idx = element_index(16, 128, True)[0]          # token 0, dims 0..127
+    for r, codes in enumerate(codes_for_row):
+        pp = int(w.block_table[r, 0])
+        off = int(w.page_v_off[pp])
+        if BITS[codec] == 16:
+            b = np.asarray(codes, dtype="<u2").view(np.uint8).reshape(-1, 2)
+            arr[off + 2 * idx] = b[:, 0]
+            arr[off + 2 * idx + 1] = b[:, 1]
+        elif BITS[codec] == 8:
+            arr[off + idx] = np.asarray(codes, dtype=np.uint8)
+        else:
+            raise AssertionError
+        if codec == INT8:
+            sc = off + 16 * 128
+            arr[sc:sc + 8] = np.frombuffer(np.float16([1, 1, 1, 1]).tobytes(), np.uint8)
+    w.page_scale[:] = 1.0
+    w.q[:] = 0
+    return w
+
+
+@pytest.mark.parametrize("codec", [FP8, INT8])
+def test_every_byte_code_exact(codec):
+    print(f"case all codes {codec}", flush=True)
+    codes = np.arange(256)
+    if codec == FP8:
+        codes = codes[(codes & 0x7F) != 0x7F]     # drop the two NaN codes
+    codes = np.resize(codes, 256).reshape(2, 128)
+    w = one_token_v_codes(codec, list(codes))
+    out, _ = run(to_device(w), params_for(w, 0))
+    ref, _ = oracle.decode_attention(w)
+    assert np.array_equal(out, ref.astype(np.float32).astype(np.float64))
+
+
+def test_fp16_codes_exact():
+    print("case fp16 codes", flush=True)
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 1 << 16, size=(8, 128)).astype(np.uint16)
+    codes[(codes & 0x7C00) == 0x7C00] = 0x3C00       # no inf/NaN
+    w = one_token_v_codes(FP16, list(codes))
+    out, _ = run(to_device(w), params_for(w, 0))
+    ref, _ = oracle.decode_attention(w)
+    assert np.array_equal(out, ref.astype(np.float32).astype(np.float64))
