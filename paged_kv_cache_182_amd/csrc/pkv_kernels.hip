@@ -325,6 +325,18 @@ __device__ inline f4 mfma16(h4 a, h4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
+// B operand of P.V for dim block n, with tail tokens zeroed (their codes may
+// be any bytes, even NaN, and 0 * NaN would poison the MFMA).
+template <int D, int VC, class T>
+__device__ inline h4 v_operand(const T& t, const TileInfo& ti, int n, int kq, bool partial) {
+  h4 vf = VC == C_ANY ? v_frag_any<D>(t.v, n, ti.vc) : v_frag<VC == C_ANY ? 0 : VC, D>(t.v, n);
+  if (partial) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vf[j] = (4 * kq + j < ti.valid) ? vf[j] : (_Float16)0.0f;
+  }
+  return vf;
+}
+
 // Scores, online-softmax update and P.V of one staged tile.
 template <int D, int KC, int VC>
 __device__ inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti, const h8* qv,
@@ -399,30 +411,40 @@ __device__ inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti
   for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(s[j] - mu);
   l_run += (p[0] + p[1]) + (p[2] + p[3]);
 
-  // P.V
-  const bool vgrouped = VC == C_ANY ? is_int(ti.vc) : is_int(VC);
-  h4 pa[NC];
-  if (vgrouped) {
+  // P.V. The weights go to the MFMA in fp16; where a V scale multiplies them
+  // it is applied so that a weight of exactly 1 stays exact: INT group scales
+  // are fp16 already, the fp32 FP8 page scale is split into an fp16 high and
+  // low part (two MFMAs, 22 significant bits). Tail tokens get weight 0 by
+  // selection, never by multiplying a possibly non-finite scale.
+  const int vc = VC == C_ANY ? ti.vc : VC;
+  auto keep = [&](int j) { return !partial || 4 * kq + j < ti.valid; };
+  if (is_int(vc)) {
     const _Float16* vs = reinterpret_cast<const _Float16*>(t.vs);
+    h4 pa[NC];
 #pragma unroll
     for (int g = 0; g < NC; ++g)
-      pa[g] = h4{(_Float16)(p[0] * (float)vs[0 * NC + g]), (_Float16)(p[1] * (float)vs[1 * NC + g]),
-                 (_Float16)(p[2] * (float)vs[2 * NC + g]), (_Float16)(p[3] * (float)vs[3 * NC + g])};
-  } else {
-    const float f = ti.sv;
-    pa[0] = h4{(_Float16)(p[0] * f), (_Float16)(p[1] * f), (_Float16)(p[2] * f), (_Float16)(p[3] * f)};
 #pragma unroll
-    for (int g = 1; g < NC; ++g) pa[g] = pa[0];
-  }
+      for (int j = 0; j < 4; ++j) pa[g][j] = keep(j) ? (_Float16)(p[j] * (float)vs[j * NC + g]) : (_Float16)0.0f;
 #pragma unroll
-  for (int n = 0; n < NB; ++n) {
-    h4 vf = VC == C_ANY ? v_frag_any<D>(t.v, n, ti.vc) : v_frag<VC == C_ANY ? 0 : VC, D>(t.v, n);
-    if (partial) {
-      // tail tokens may hold any bytes (even NaN codes): zero them, P is 0 there
+    for (int n = 0; n < NB; ++n) acc[n] = mfma16(pa[n / 2], v_operand<D, VC>(t, ti, n, kq, partial), acc[n]);
+  } else if (vc == C_FP8) {
+    h4 hi, lo;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) vf[j] = (4 * kq + j < ti.valid) ? vf[j] : (_Float16)0.0f;
+    for (int j = 0; j < 4; ++j) {
+      const float x = p[j] * ti.sv;
+      hi[j] = (_Float16)x;
+      lo[j] = (_Float16)(x - (float)hi[j]);
     }
-    acc[n] = mfma16(pa[n / 2], vf, acc[n]);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const h4 vf = v_operand<D, VC>(t, ti, n, kq, partial);
+      acc[n] = mfma16(hi, vf, acc[n]);
+      acc[n] = mfma16(lo, vf, acc[n]);
+    }
+  } else {
+    const h4 pa = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] = mfma16(pa, v_operand<D, VC>(t, ti, n, kq, partial), acc[n]);
   }
 }
 

@@ -40,6 +40,7 @@ def compare(out, lse, ref_out, ref_lse, what=""):
     assert np.all(np.isfinite(out)), f"{what}: non-finite out"
     eo = float(np.max(np.abs(out - ref_out))) if out.size else 0.0
     el = float(np.max(np.abs(lse[fin] - ref_lse[fin]))) if fin.any() else 0.0
+    print(f"parity {what}: out max-abs {eo:.3e} lse max-abs {el:.3e}", flush=True)
     assert eo <= OUT_TOL, f"{what}: out max-abs {eo:.3g} > {OUT_TOL}"
     assert el <= LSE_TOL, f"{what}: lse max-abs {el:.3g} > {LSE_TOL}"
     return eo, el

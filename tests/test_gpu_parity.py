@@ -68,15 +68,21 @@ def test_configs_small(cid):
 
 
 def test_partition_invariance_and_determinism():
+    """Every partition size matches the oracle; sizes agree with each other to
+    1e-4 (each partition has its own running max, so the fp16 softmax weights
+    round differently: per token a relative 2^-11, about |v| * 2^-11 * sqrt(sum
+    w^2) on out, a few 1e-5 here); a repeated launch is bit-identical."""
     print("case partition invariance", flush=True)
     w = small([2000, 1111], FP8, FP8, hq=16, hkv=2, dim=128, page=16, q_scale=3.0)
     dw = to_device(w)
+    ref = oracle.decode_attention(w)
     res = []
     for T in (16, 64, 512, 2048):
         o, l = run(dw, params_for(w, T))
+        compare(o, l, *ref, f"partition_tokens={T}")
         res.append((o, l))
     for o, l in res[1:]:
-        assert np.max(np.abs(o - res[0][0])) <= 1e-5 and np.max(np.abs(l - res[0][1])) <= 1e-5
+        assert np.max(np.abs(o - res[0][0])) <= 1e-4 and np.max(np.abs(l - res[0][1])) <= 1e-5
     o2, l2 = run(dw, params_for(w, 64))
     assert np.array_equal(o2, res[1][0]) and np.array_equal(l2, res[1][1])
 
