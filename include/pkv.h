@@ -182,7 +182,7 @@ int pkv_decode_partials(const pkv_params* p, const void* q, const uint8_t* page_
  *   M = max_p m_p;  w_p = exp(m_p - M);  L = sum_p w_p l_p;
  *   out = sum_p w_p acc_p / L;  lse = M + ln L,
  *
- * summing parts in ascending order (run-to-run deterministic). Parts with
+ * summing the parts in a fixed order (run-to-run identical results). Parts with
  * m_p = -inf or l_p = 0 are empty; a row whose parts are all empty gets
  * out = 0 and lse = -inf.
  *

@@ -20,6 +20,8 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
     # no packed-fp32 instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: no AGPR copies around the online-softmax rescale
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}",
 ]
@@ -32,10 +34,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libpkv.so")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libpkv.so (always recompiles). Returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def build(verbose: bool = False, out: str = LIB, extra: tuple = ()) -> str:
+    """Compile every source into libpkv.so (always recompiles). Returns its path.
+    `extra` adds compiler flags (for example -D variants of a tuning macro)."""
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *FLAGS, *extra, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,8 +49,8 @@ def build(verbose: bool = False) -> str:
              if ln.strip() and "packed-fp32-ops" not in ln and "is not a recognized feature" not in ln]
     if verbose and noise:
         print("\n".join(noise))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

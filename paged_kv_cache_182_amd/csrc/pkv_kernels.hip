@@ -40,6 +40,13 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 enum : int { C_FP16 = 0, C_BF16 = 1, C_FP8 = 2, C_INT8 = 3, C_INT4 = 4, C_ANY = 15 };
 
+#ifndef PKV_RING_WORDS
+#define PKV_RING_WORDS 32  // 32-bit words of tile codes a wave keeps in flight
+#endif
+#ifndef PKV_KPERM
+#define PKV_KPERM 1  // contiguous K loads for codecs with one scale per page
+#endif
+
 constexpr int WAVES = 4;
 constexpr int THREADS = 64 * WAVES;
 constexpr int MAX_DESC = 256;  // page descriptors staged in LDS at a time
@@ -50,15 +57,35 @@ __host__ __device__ constexpr int bits_of(int c) { return c <= C_BF16 ? 16 : (c 
 __host__ __device__ constexpr bool is_int(int c) { return c == C_INT8 || c == C_INT4; }
 
 // Bytes of one plane (codes of every head, then INT group scales).
-__device__ inline uint64_t plane_bytes(int c, int hkv, int page, int d) {
+__host__ __device__ inline uint64_t plane_bytes(int c, int hkv, int page, int d) {
   const uint64_t codes = (uint64_t)hkv * page * d * bits_of(c) / 8;
   return codes + (is_int(c) ? (uint64_t)hkv * page * (d / 32) * 2 : 0);
 }
 
+// Raw buffer loads through a per-plane resource: the base and size live in
+// scalar registers, every lane supplies a 32-bit offset, and an offset past
+// the size reads zeros instead of faulting. A skipped tile gets size 0, so
+// every tile issues the same loads and the wait counts stay exact.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int RSRC_WORD3 = 0x00020000;  // gfx9-family raw buffer format
+
+__device__ inline rsrc_t make_rsrc(const uint8_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, RSRC_WORD3);
+}
+__device__ inline u4 bload16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ inline u2 bload8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ inline uint32_t bload4(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
 // Page descriptor staged in LDS (32 bytes).
 struct Desc {
-  uint64_t k;      // address of the K plane (0 if the page is skipped)
-  uint64_t v;      // address of the V plane
+  uint64_t k;      // byte offset of the K plane in the pool (0 if the page is skipped)
+  uint64_t v;      // byte offset of the V plane
   float sk, sv;    // FP8 scales of this KV head (1 for other codecs)
   int32_t valid;   // attended tokens of the page (0 if skipped)
   int32_t codec;   // K codec | V codec << 4
@@ -81,6 +108,26 @@ struct Tile {
   uint32_t vs[VS ? SW : 1];
 };
 
+template <int D, int KC, int VC>
+__host__ __device__ constexpr int ring_depth() {
+  using T = Tile<D, KC, VC>;
+  constexpr int words = T::KW + T::VW + (T::KS ? T::SW : 0) + (T::VS ? T::SW : 0);
+  constexpr int d = PKV_RING_WORDS / words;
+  return d < 2 ? 2 : (d > 8 ? 8 : d);
+}
+
+// Occupancy asked of the compiler: four waves per SIMD (a whole 1024-
+// workgroup grid resident at once) where the tile ring is small enough,
+// three for the codecs with group scales (more state per tile).
+template <int D, int KC, int VC>
+__host__ __device__ constexpr int waves_per_eu() {
+#ifdef PKV_WAVES
+  return PKV_WAVES;
+#else
+  return (D == 64 || (KC == C_FP8 && VC == C_FP8)) ? 4 : 3;
+#endif
+}
+
 struct TileInfo {
   int valid;  // tokens of the tile to attend (0: skip the tile)
   int kc, vc;
@@ -102,59 +149,75 @@ __device__ inline float unif(float x) {
 }
 
 // ---------------------------------------------------------------- loads
-// K: lane reads token `tok` of the head block, dims 32c + 8kq .. +7 for each c.
-template <int D, int C>
-__device__ inline void load_k(uint32_t* w, const uint8_t* head, int tok, int kq) {
+// K: lane reads token `tok` of head block `head` (byte offset in the plane),
+// 8 dims for each of the D/32 score MFMAs. With PERM (codecs with one scale per
+// page) the lane's dims are (D/4)kq .. (D/4)kq + D/4 - 1, one contiguous run;
+// otherwise (group scales) MFMA c must see exactly group c, so the lane reads
+// dims 32c + 8kq .. +7 for each c. q is permuted the same way, so the dot
+// products are unchanged.
+template <int D, int C, bool PERM>
+__device__ inline void load_k(uint32_t* w, rsrc_t r, uint32_t head, int tok, int kq) {
   constexpr int NC = D / 32;
-  if constexpr (bits_of(C) == 16) {
-    const uint8_t* p = head + (size_t)(tok * D + 8 * kq) * 2;
+  if constexpr (PERM && bits_of(C) == 16) {
+    const uint32_t o = head + (uint32_t)(tok * D + (D / 4) * kq) * 2;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      u4 x = *reinterpret_cast<const u4*>(p + 64 * c);
+      const u4 x = bload16(r, o + 16 * c);
+      w[4 * c + 0] = x[0]; w[4 * c + 1] = x[1]; w[4 * c + 2] = x[2]; w[4 * c + 3] = x[3];
+    }
+  } else if constexpr (PERM && bits_of(C) == 8) {
+    const uint32_t o = head + (uint32_t)(tok * D + (D / 4) * kq);
+#pragma unroll
+    for (int i = 0; i < NC / 2; ++i) {
+      const u4 x = bload16(r, o + 16 * i);
+      w[4 * i + 0] = x[0]; w[4 * i + 1] = x[1]; w[4 * i + 2] = x[2]; w[4 * i + 3] = x[3];
+    }
+  } else if constexpr (bits_of(C) == 16) {
+    const uint32_t o = head + (uint32_t)(tok * D + 8 * kq) * 2;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const u4 x = bload16(r, o + 64 * c);
       w[4 * c + 0] = x[0]; w[4 * c + 1] = x[1]; w[4 * c + 2] = x[2]; w[4 * c + 3] = x[3];
     }
   } else if constexpr (bits_of(C) == 8) {
-    const uint8_t* p = head + (size_t)(tok * D + 8 * kq);
+    const uint32_t o = head + (uint32_t)(tok * D + 8 * kq);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      u2 x = *reinterpret_cast<const u2*>(p + 32 * c);
+      const u2 x = bload8(r, o + 32 * c);
       w[2 * c + 0] = x[0]; w[2 * c + 1] = x[1];
     }
   } else {
-    const uint8_t* p = head + (size_t)(tok * D + 8 * kq) / 2;
+    const uint32_t o = head + (uint32_t)(tok * D + 8 * kq) / 2;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) w[c] = *reinterpret_cast<const uint32_t*>(p + 16 * c);
+    for (int c = 0; c < NC; ++c) w[c] = bload4(r, o + 16 * c);
   }
 }
 
-// V: lane l reads its contiguous run of D/4 elements inside the tile.
+// V: lane l reads its contiguous run of D/4 elements inside tile `sub`.
 template <int D, int C>
-__device__ inline void load_v(uint32_t* w, const uint8_t* head, int sub, int lane) {
+__device__ inline void load_v(uint32_t* w, rsrc_t r, uint32_t head, int sub, int lane) {
   constexpr int RUN_BYTES = D * bits_of(C) / 32;
-  const uint8_t* p = head + ((size_t)sub * 16 * D + (size_t)lane * (D / 4)) * bits_of(C) / 8;
+  const uint32_t o = head + (uint32_t)(sub * 16 * D + lane * (D / 4)) * bits_of(C) / 8;
   if constexpr (RUN_BYTES >= 16) {
 #pragma unroll
     for (int i = 0; i < RUN_BYTES / 16; ++i) {
-      u4 x = *reinterpret_cast<const u4*>(p + 16 * i);
+      const u4 x = bload16(r, o + 16 * i);
       w[4 * i + 0] = x[0]; w[4 * i + 1] = x[1]; w[4 * i + 2] = x[2]; w[4 * i + 3] = x[3];
     }
   } else {
-    u2 x = *reinterpret_cast<const u2*>(p);
+    const u2 x = bload8(r, o);
     w[0] = x[0]; w[1] = x[1];
   }
 }
 
-// Group scales of tokens tok0 .. tok0+3, all D/32 groups (fp16, token-major).
+// Group scales of 4 consecutive tokens, all D/32 groups (fp16, token-major).
 template <int D>
-__device__ inline void load_scales(uint32_t* w, const uint8_t* p) {
+__device__ inline void load_scales(uint32_t* w, rsrc_t r, uint32_t off) {
+  const u4 x = bload16(r, off);
+  w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
   if constexpr (D == 128) {
-    u4 x = *reinterpret_cast<const u4*>(p);
-    u4 y = *reinterpret_cast<const u4*>(p + 16);
-    w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
+    const u4 y = bload16(r, off + 16);
     w[4] = y[0]; w[5] = y[1]; w[6] = y[2]; w[7] = y[3];
-  } else {
-    u4 x = *reinterpret_cast<const u4*>(p);
-    w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
   }
 }
 
@@ -255,65 +318,64 @@ __device__ inline h4 v_frag_any(const uint32_t* w, int n, int codec) {
   }
 }
 
-template <int D, int C>
-__device__ inline void load_k_c(uint32_t* w, const uint8_t* plane, int h, int page, int tok, int kq) {
-  load_k<D, C>(w, plane + (size_t)h * page * D * bits_of(C) / 8, tok, kq);
+// Whether a kernel variant reads K with the contiguous (permuted-dims) layout.
+template <int KC>
+__host__ __device__ constexpr bool k_perm() {
+  return PKV_KPERM && KC != C_ANY && !is_int(KC) && KC <= C_INT4;
 }
-template <int D, int C>
-__device__ inline void load_v_c(uint32_t* w, const uint8_t* plane, int h, int page, int sub, int lane) {
-  load_v<D, C>(w, plane + (size_t)h * page * D * bits_of(C) / 8, sub, lane);
+// Byte offset of head h's codes inside a plane.
+template <int D>
+__device__ inline uint32_t head_off(int codec, int h, int page) {
+  return (uint32_t)(h * page * D * bits_of(codec) / 8);
 }
 
-// Issue the loads of tile `k` of the staged pages into `t`.
+// Issue the loads of tile `k` of the staged pages into `t`. Every call issues
+// the same loads: a tile with nothing to attend reads through a zero-size
+// resource (zeros, no fault) and is skipped when consumed.
 template <int D, int KC, int VC>
 __device__ inline TileInfo issue_tile(Tile<D, KC, VC>& t, const Desc* desc, int k, int tpp,
                                       const DecodeArgs& a, int h, int lane) {
   const int i = k / tpp;
   const int sub = k - i * tpp;
   TileInfo ti;
-  const int pvalid = uni(desc[i].valid);
-  ti.valid = min(max(pvalid - 16 * sub, 0), 16);
-  if (ti.valid == 0) return ti;
+  ti.valid = min(max(uni(desc[i].valid) - 16 * sub, 0), 16);
   const int codec = uni(desc[i].codec);
   ti.kc = KC == C_ANY ? (codec & 15) : KC;
   ti.vc = VC == C_ANY ? (codec >> 4) : VC;
   ti.sk = unif(desc[i].sk);
   ti.sv = unif(desc[i].sv);
-  const uint8_t* kp = reinterpret_cast<const uint8_t*>(uni64(desc[i].k));
-  const uint8_t* vp = reinterpret_cast<const uint8_t*>(uni64(desc[i].v));
+  const bool live = ti.valid > 0;
+  const int page = a.page;
+  const rsrc_t rk = make_rsrc(a.pool + uni64(desc[i].k), live ? (uint32_t)plane_bytes(ti.kc, a.hkv, page, D) : 0u);
+  const rsrc_t rv = make_rsrc(a.pool + uni64(desc[i].v), live ? (uint32_t)plane_bytes(ti.vc, a.hkv, page, D) : 0u);
   const int col = lane & 15, kq = lane >> 4;
   const int tok = 16 * sub + col;
-  const int page = a.page;
   if constexpr (KC == C_ANY) {
     switch (ti.kc) {
-      case C_FP16: case C_BF16: load_k_c<D, C_FP16>(t.k, kp, h, page, tok, kq); break;
-      case C_FP8: case C_INT8: load_k_c<D, C_FP8>(t.k, kp, h, page, tok, kq); break;
-      default: load_k_c<D, C_INT4>(t.k, kp, h, page, tok, kq); break;
+      case C_FP16: case C_BF16: load_k<D, C_FP16, false>(t.k, rk, head_off<D>(C_FP16, h, page), tok, kq); break;
+      case C_FP8: case C_INT8: load_k<D, C_FP8, false>(t.k, rk, head_off<D>(C_FP8, h, page), tok, kq); break;
+      default: load_k<D, C_INT4, false>(t.k, rk, head_off<D>(C_INT4, h, page), tok, kq); break;
     }
   } else {
-    load_k_c<D, KC>(t.k, kp, h, page, tok, kq);
+    load_k<D, KC, k_perm<KC>()>(t.k, rk, head_off<D>(KC, h, page), tok, kq);
   }
   if constexpr (VC == C_ANY) {
     switch (ti.vc) {
-      case C_FP16: case C_BF16: load_v_c<D, C_FP16>(t.v, vp, h, page, sub, lane); break;
-      case C_FP8: case C_INT8: load_v_c<D, C_FP8>(t.v, vp, h, page, sub, lane); break;
-      default: load_v_c<D, C_INT4>(t.v, vp, h, page, sub, lane); break;
+      case C_FP16: case C_BF16: load_v<D, C_FP16>(t.v, rv, head_off<D>(C_FP16, h, page), sub, lane); break;
+      case C_FP8: case C_INT8: load_v<D, C_FP8>(t.v, rv, head_off<D>(C_FP8, h, page), sub, lane); break;
+      default: load_v<D, C_INT4>(t.v, rv, head_off<D>(C_INT4, h, page), sub, lane); break;
     }
   } else {
-    load_v_c<D, VC>(t.v, vp, h, page, sub, lane);
+    load_v<D, VC>(t.v, rv, head_off<D>(VC, h, page), sub, lane);
   }
-  const size_t tok0 = (size_t)h * page + 16 * sub + 4 * kq;
+  const uint32_t tok0 = (uint32_t)(h * page + 16 * sub + 4 * kq);
   if constexpr (Tile<D, KC, VC>::KS) {
-    if (is_int(ti.kc)) {
-      const size_t codes = (size_t)a.hkv * page * D * bits_of(ti.kc) / 8;
-      load_scales<D>(t.ks, kp + codes + tok0 * (D / 32) * 2);
-    }
+    if (is_int(ti.kc))
+      load_scales<D>(t.ks, rk, (uint32_t)(a.hkv * page * D * bits_of(ti.kc) / 8) + tok0 * (D / 32) * 2);
   }
   if constexpr (Tile<D, KC, VC>::VS) {
-    if (is_int(ti.vc)) {
-      const size_t codes = (size_t)a.hkv * page * D * bits_of(ti.vc) / 8;
-      load_scales<D>(t.vs, vp + codes + tok0 * (D / 32) * 2);
-    }
+    if (is_int(ti.vc))
+      load_scales<D>(t.vs, rv, (uint32_t)(a.hkv * page * D * bits_of(ti.vc) / 8) + tok0 * (D / 32) * 2);
   }
   return ti;
 }
@@ -449,7 +511,7 @@ __device__ inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti
 }
 
 template <int D, int KC, int VC>
-__global__ void __launch_bounds__(THREADS) decode_kernel(const DecodeArgs a) {
+__global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>()))) decode_kernel(const DecodeArgs a) {
   constexpr int NC = D / 32, NB = D / 16;
   constexpr int RED_BYTES = (WAVES * 16 * D + 2 * WAVES * 16) * 4;
   constexpr int DESC_BYTES = MAX_DESC * (int)sizeof(Desc);
@@ -457,44 +519,41 @@ __global__ void __launch_bounds__(THREADS) decode_kernel(const DecodeArgs a) {
   Desc* desc = reinterpret_cast<Desc*>(smem);
 
   const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loop control scalar
   const int col = lane & 15, kq = lane >> 4;
   const int G = a.group;
   const int P = a.page;
 
-  // ---- extent of this row and of this partition
-  int L = a.seq_lens[b];
-  const bool report_row = part == 0 && h == 0 && tid == 0;
-  if (L < 0) {
-    if (report_row) count_error(a.err);
-    L = 0;
-  }
+  // ---- extent of this row and of this partition (wave-uniform values)
+  int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+  bool bad_row = L < 0;
+  L = L < 0 ? 0 : L;
   int npg;
   if (a.sparse) {
-    npg = a.sel_lens[b];
-    if (npg < 0 || npg > a.max_sel) {
-      if (report_row) count_error(a.err);
-      npg = min(max(npg, 0), a.max_sel);
-    }
+    const int n = __builtin_amdgcn_readfirstlane(a.sel_lens[b]);
+    bad_row = bad_row || n < 0 || n > a.max_sel;
+    npg = min(max(n, 0), a.max_sel);
   } else {
-    npg = L / P + (L % P != 0);
-    if (npg > a.max_pages) {
-      if (report_row) count_error(a.err);
-      npg = a.max_pages;
-    }
+    const int n = L / P + (L % P != 0);
+    bad_row = bad_row || n > a.max_pages;
+    npg = min(n, a.max_pages);
   }
+  npg = __builtin_amdgcn_readfirstlane(npg);
+  if (bad_row && part == 0 && h == 0 && tid == 0) count_error(a.err);
   const int s0 = part * a.pages_per_part;
   const int s1 = min(s0 + a.pages_per_part, npg);
 
   // ---- q of this KV head's query group (B operand of the score MFMA)
   h8 qv[NC];
   {
+    constexpr bool PERM = k_perm<KC>();
     const _Float16* qp = reinterpret_cast<const _Float16*>(a.q) +
-                         ((size_t)b * a.hq + (size_t)h * G + col) * D + 8 * kq;
+                         ((size_t)b * a.hq + (size_t)h * G + col) * D + (PERM ? D / 4 : 8) * kq;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (col < G) {
-        qv[c] = *reinterpret_cast<const h8*>(qp + 32 * c);
+        qv[c] = *reinterpret_cast<const h8*>(qp + (PERM ? 8 : 32) * c);
       } else {
         qv[c] = h8{0, 0, 0, 0, 0, 0, 0, 0};
       }
@@ -543,8 +602,8 @@ __global__ void __launch_bounds__(THREADS) decode_kernel(const DecodeArgs a) {
       if (ok) {
         const long long rem = (long long)L - (long long)lp * P;
         d.valid = (int)(rem < 0 ? 0 : (rem > P ? P : rem));
-        d.k = (uint64_t)(a.pool + ko);
-        d.v = (uint64_t)(a.pool + vo);
+        d.k = ko;
+        d.v = vo;
         if (kc == C_FP8) d.sk = a.scale[((size_t)pp * a.hkv + h) * 2 + 0];
         if (vc == C_FP8) d.sv = a.scale[((size_t)pp * a.hkv + h) * 2 + 1];
         d.codec = cod;
@@ -555,21 +614,29 @@ __global__ void __launch_bounds__(THREADS) decode_kernel(const DecodeArgs a) {
     }
     __syncthreads();
 
+    // Ring of DEPTH tiles: while the oldest is consumed, the loads of the
+    // next DEPTH-1 are in flight. Issues are unconditional (past the end the
+    // wave re-issues its last tile and never consumes the copy), so the
+    // compiler's wait counts stay exact.
     const int ntiles = cn * tpp;
-    Tile<D, KC, VC> ta, tb;
-    TileInfo ia, ib;
-    int k = wave;
-    if (k < ntiles) ia = issue_tile<D, KC, VC>(ta, desc, k, tpp, a, h, lane);
-    while (k < ntiles) {
-      const int k2 = k + WAVES;
-      if (k2 < ntiles) ib = issue_tile<D, KC, VC>(tb, desc, k2, tpp, a, h, lane);
-      consume_tile<D, KC, VC>(ta, ia, qv, a.scale_log2, m_run, l_run, acc, lane);
-      k = k2;
-      if (k >= ntiles) break;
-      const int k3 = k + WAVES;
-      if (k3 < ntiles) ia = issue_tile<D, KC, VC>(ta, desc, k3, tpp, a, h, lane);
-      consume_tile<D, KC, VC>(tb, ib, qv, a.scale_log2, m_run, l_run, acc, lane);
-      k = k3;
+    if (wave < ntiles) {
+      constexpr int DEPTH = ring_depth<D, KC, VC>();
+      const int nmine = (ntiles - wave + WAVES - 1) / WAVES;
+      const int klast = wave + (nmine - 1) * WAVES;
+      Tile<D, KC, VC> t[DEPTH];
+      TileInfo inf[DEPTH];
+#pragma unroll
+      for (int s = 0; s < DEPTH - 1; ++s)
+        inf[s] = issue_tile<D, KC, VC>(t[s], desc, min(wave + s * WAVES, klast), tpp, a, h, lane);
+      for (int it = 0; it < nmine; it += DEPTH) {
+#pragma unroll
+        for (int s = 0; s < DEPTH; ++s) {
+          const int kn = min(wave + (it + s + DEPTH - 1) * WAVES, klast);
+          const int nx = (s + DEPTH - 1) % DEPTH;
+          inf[nx] = issue_tile<D, KC, VC>(t[nx], desc, kn, tpp, a, h, lane);
+          if (it + s < nmine) consume_tile<D, KC, VC>(t[s], inf[s], qv, a.scale_log2, m_run, l_run, acc, lane);
+        }
+      }
     }
   }
 
@@ -623,26 +690,30 @@ __global__ void __launch_bounds__(THREADS) decode_kernel(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------- fold
-// One workgroup per row. Thread t handles 4 dims (t % (D/4)) of the parts
-// p = t / (D/4) + k * groups, ascending; the groups are then summed in a
-// fixed order, so the result is run-to-run identical.
-__global__ void __launch_bounds__(256) combine_kernel(int nparts, int D, const float* __restrict__ part_acc,
-                                                      const float* __restrict__ part_ml,
-                                                      float* __restrict__ out, float* __restrict__ lse) {
-  __shared__ float red[256 * 4 + 256];
+// Grid (row, 32-dim chunk). Thread t covers 4 dims (t % 8) of the parts
+// p = t / 8 + 32k; the 32 part groups are then summed in a fixed order, so
+// the result is run-to-run identical. Every thread's loads are independent,
+// which keeps a few hundred bytes per thread in flight.
+constexpr int FOLD_THREADS = 256;
+constexpr int FOLD_GROUPS = FOLD_THREADS / 8;
+
+__global__ void __launch_bounds__(FOLD_THREADS) combine_kernel(int nparts, int D, const float* __restrict__ part_acc,
+                                                               const float* __restrict__ part_ml,
+                                                               float* __restrict__ out, float* __restrict__ lse) {
+  __shared__ float red[FOLD_THREADS * 5];
   __shared__ float s_M;
   const int row = blockIdx.x, tid = threadIdx.x;
   const float* ml = part_ml + (size_t)row * nparts * 2;
   const float* acc = part_acc + (size_t)row * nparts * D;
 
   float M = NEG_INF;
-  for (int p = tid; p < nparts; p += 256) {
+  for (int p = tid; p < nparts; p += FOLD_THREADS) {
     const float m = ml[2 * p], l = ml[2 * p + 1];
     if (l > 0.f) M = fmaxf(M, m);
   }
   red[tid] = M;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
+  for (int s = FOLD_THREADS / 2; s > 0; s >>= 1) {
     if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
     __syncthreads();
   }
@@ -651,46 +722,102 @@ __global__ void __launch_bounds__(256) combine_kernel(int nparts, int D, const f
   M = s_M;
   __syncthreads();
 
-  const int lanes_per_part = (D + 3) / 4;             // threads covering one part's dims
-  const int groups = 256 / lanes_per_part;            // part groups
-  const int dl = tid % lanes_per_part, pg = tid / lanes_per_part;
+  const int dq = tid & 7, pg = tid >> 3;
+  const int d0 = 32 * blockIdx.y + 4 * dq;
+  const bool vec = (D & 3) == 0;
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, L = 0.f;
-  if (pg < groups && M != NEG_INF) {
-    for (int p = pg; p < nparts; p += groups) {
-      const float m = ml[2 * p], l = ml[2 * p + 1];
-      if (!(l > 0.f)) continue;
-      const float w = __expf(m - M);
-      L += w * l;
-      const float* ap = acc + (size_t)p * D + 4 * dl;
-      if (4 * dl + 3 < D) {
-        a0 += w * ap[0]; a1 += w * ap[1]; a2 += w * ap[2]; a3 += w * ap[3];
-      } else {
-        if (4 * dl + 0 < D) a0 += w * ap[0];
-        if (4 * dl + 1 < D) a1 += w * ap[1];
-        if (4 * dl + 2 < D) a2 += w * ap[2];
+  constexpr int BATCH = 8;  // parts whose loads are all issued before any is used
+  if (M != NEG_INF) {
+    for (int p0 = pg; p0 < nparts; p0 += FOLD_GROUPS * BATCH) {
+      float m[BATCH], l[BATCH];
+      f4 x[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int p = p0 + u * FOLD_GROUPS;
+        const bool in = p < nparts;
+        m[u] = in ? ml[2 * p] : NEG_INF;
+        l[u] = in ? ml[2 * p + 1] : 0.f;
+        const float* ap = acc + (size_t)(in ? p : 0) * D + d0;
+        if (in && vec && d0 + 3 < D) {
+          x[u] = *reinterpret_cast<const f4*>(ap);
+        } else {
+          x[u] = f4{in && d0 + 0 < D ? ap[0] : 0.f, in && d0 + 1 < D ? ap[1] : 0.f,
+                    in && d0 + 2 < D ? ap[2] : 0.f, in && d0 + 3 < D ? ap[3] : 0.f};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        if (l[u] > 0.f) {
+          const float w = __expf(m[u] - M);
+          L += w * l[u];
+          a0 += w * x[u][0]; a1 += w * x[u][1]; a2 += w * x[u][2]; a3 += w * x[u][3];
+        }
       }
     }
   }
   red[tid * 4 + 0] = a0; red[tid * 4 + 1] = a1; red[tid * 4 + 2] = a2; red[tid * 4 + 3] = a3;
-  red[1024 + tid] = L;
+  red[FOLD_THREADS * 4 + tid] = L;
   __syncthreads();
   if (pg == 0) {
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f, Ls = 0.f;
-    for (int g = 0; g < groups; ++g) {
-      const int t = g * lanes_per_part + dl;
+    for (int g = 0; g < FOLD_GROUPS; ++g) {
+      const int t = g * 8 + dq;
       s0 += red[t * 4 + 0]; s1 += red[t * 4 + 1]; s2 += red[t * 4 + 2]; s3 += red[t * 4 + 3];
-      Ls += red[1024 + t];
+      Ls += red[FOLD_THREADS * 4 + t];
     }
-    float* o = out + (size_t)row * D + 4 * dl;
     const bool any = M != NEG_INF && Ls > 0.f;
-    const float inv = any ? 1.f / Ls : 0.f;
-    if (4 * dl + 0 < D) o[0] = any ? s0 / Ls : 0.f;
-    if (4 * dl + 1 < D) o[1] = any ? s1 / Ls : 0.f;
-    if (4 * dl + 2 < D) o[2] = any ? s2 / Ls : 0.f;
-    if (4 * dl + 3 < D) o[3] = any ? s3 / Ls : 0.f;
-    (void)inv;
-    if (dl == 0) lse[row] = any ? M + logf(Ls) : NEG_INF;
+    float* o = out + (size_t)row * D + d0;
+    if (d0 + 0 < D) o[0] = any ? s0 / Ls : 0.f;
+    if (d0 + 1 < D) o[1] = any ? s1 / Ls : 0.f;
+    if (d0 + 2 < D) o[2] = any ? s2 / Ls : 0.f;
+    if (d0 + 3 < D) o[3] = any ? s3 / Ls : 0.f;
+    if (blockIdx.y == 0 && dq == 0) lse[row] = any ? M + logf(Ls) : NEG_INF;
   }
+}
+
+// Fold for few parts per row: one thread per (row, dim), every part's loads
+// issued before they are used, parts summed in ascending order.
+constexpr int FOLD_SMALL_MAX = 64;
+
+__global__ void __launch_bounds__(256) combine_small_kernel(int rows, int nparts, int D,
+                                                            const float* __restrict__ part_acc,
+                                                            const float* __restrict__ part_ml,
+                                                            float* __restrict__ out, float* __restrict__ lse) {
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long row = gid / D;
+  const int d = (int)(gid - row * D);
+  if (row >= rows) return;
+  const float* ml = part_ml + row * nparts * 2;
+  const float* acc = part_acc + row * nparts * D + d;
+  float M = NEG_INF, L = 0.f, A = 0.f;
+  for (int p0 = 0; p0 < nparts; p0 += 8) {
+    float m[8], l[8], x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u;
+      m[u] = p < nparts ? ml[2 * p] : NEG_INF;
+      l[u] = p < nparts ? ml[2 * p + 1] : 0.f;
+      x[u] = p < nparts ? acc[(long long)p * D] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (l[u] > 0.f) {
+        // running log-sum-exp over the parts seen so far
+        if (m[u] > M) {
+          const float c = M == NEG_INF ? 0.f : __expf(M - m[u]);
+          L *= c;
+          A *= c;
+          M = m[u];
+        }
+        const float w = __expf(m[u] - M);
+        L += w * l[u];
+        A += w * x[u];
+      }
+    }
+  }
+  const bool any = M != NEG_INF && L > 0.f;
+  out[row * D + d] = any ? A / L : 0.f;
+  if (d == 0) lse[row] = any ? M + logf(L) : NEG_INF;
 }
 
 template <int D, int KC, int VC>
@@ -729,8 +856,14 @@ int launch_combine(int rows, int nparts, int head_dim, const float* part_acc, co
                    float* out, float* lse, void* stream) {
   if (rows == 0) return 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(256), 0, s, nparts, head_dim, part_acc, part_ml,
-                     out, lse);
+  if (nparts <= FOLD_SMALL_MAX) {
+    const long long threads = (long long)rows * head_dim;
+    hipLaunchKernelGGL(combine_small_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, rows,
+                       nparts, head_dim, part_acc, part_ml, out, lse);
+  } else {
+    hipLaunchKernelGGL(combine_kernel, dim3(rows, (head_dim + 31) / 32), dim3(FOLD_THREADS), 0, s, nparts,
+                       head_dim, part_acc, part_ml, out, lse);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

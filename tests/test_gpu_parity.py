@@ -193,3 +193,54 @@ def test_fp16_codes_exact():
     out, _ = run(to_device(w), params_for(w, 0))
     ref, _ = oracle.decode_attention(w)
     assert np.array_equal(out, ref.astype(np.float32).astype(np.float64))
+
+
+# ------------------------------------------------ partials and the fold alone
+def test_decode_partials_match_oracle_partials():
+    print("case partials", flush=True)
+    w = small([300, 17, 0, 129], FP8, INT8, hq=8, hkv=2, dim=128, page=16)
+    dw = to_device(w)
+    T = 64
+    p = params_for(w, T)
+    n = pkv.num_partitions(p)
+    acc, ml = pkv.decode_partials(p, *dw.args())
+    torch.cuda.synchronize()
+    acc, ml = acc.cpu().numpy().astype(np.float64), ml.cpu().numpy().astype(np.float64)
+    G = 4
+    from oracle.attention import gather_kv
+    for r in range(w.rows):
+        L = int(w.seq_lens[r])
+        bounds = [min(L, i * T) for i in range(n + 1)]
+        for h in range(2):
+            K, V = gather_kv(w, r, h)
+            q = w.q[r, h * G:(h + 1) * G].astype(np.float64)
+            oa, om, ol = oracle.partials(K, V, q, w.softmax_scale, bounds)
+            ga, gm, gl = acc[r, h * G:(h + 1) * G], ml[r, h * G:(h + 1) * G, :, 0], ml[r, h * G:(h + 1) * G, :, 1]
+            empty = ol == 0
+            assert np.array_equal(gl == 0, empty) and np.all(np.isneginf(gm[empty]))
+            ok = ~empty
+            assert np.max(np.abs(gm[ok] - om[ok]), initial=0) <= 1e-5
+            # acc/l is the partition's own normalised output
+            assert np.max(np.abs(ga[ok] / gl[ok][:, None] - oa[ok] / ol[ok][:, None]), initial=0) <= 1e-3
+            assert np.max(np.abs(np.log(gl[ok]) - np.log(ol[ok])), initial=0) <= 1e-4
+
+
+@pytest.mark.parametrize("rows,parts,dim", [(5, 1, 128), (16, 512, 128), (7, 33, 64), (3, 9, 30), (2, 4, 512)])
+def test_lse_combine_matches_oracle_fold(rows, parts, dim):
+    print(f"case fold {rows} {parts} {dim}", flush=True)
+    rng = np.random.default_rng(rows * 1000 + parts)
+    m = (3 * rng.standard_normal((rows, parts))).astype(np.float32)
+    l = rng.uniform(0.5, 50, (rows, parts)).astype(np.float32)
+    acc = (rng.standard_normal((rows, parts, dim)) * l[..., None]).astype(np.float32)
+    empty = rng.random((rows, parts)) < 0.2
+    m[empty], l[empty], acc[empty] = -np.inf, 0, 0
+    if rows > 2:
+        m[1], l[1], acc[1] = -np.inf, 0, 0                  # a row with no tokens at all
+    ml = np.stack([m, l], axis=-1)
+    out, lse = pkv.lse_combine(torch.from_numpy(acc).cuda(), torch.from_numpy(ml).cuda())
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.fold(acc.astype(np.float64), m.astype(np.float64), l.astype(np.float64))
+    out, lse = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.max(np.abs(out - ref_out)) <= 1e-5 and np.max(np.abs(lse[fin] - ref_lse[fin]), initial=0) <= 1e-5
