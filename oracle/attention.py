@@ -45,19 +45,19 @@ def attended_pages(w, row: int) -> list[tuple[int, int]]:
 def gather_kv(w, row: int, h: int) -> tuple[np.ndarray, np.ndarray]:
     """K, V float64 [N, D] of KV head ``h`` over the row's attended tokens."""
     D, P, hkv = w.head_dim, w.page_size, w.num_kv_heads
-    ks, vs = [], []
-    for lp, valid in attended_pages(w, row):
-        if valid == 0:
-            continue
+    pages = [(lp, valid) for lp, valid in attended_pages(w, row) if valid > 0]
+    n = sum(valid for _, valid in pages)
+    K, V = np.empty((n, D)), np.empty((n, D))
+    t = 0
+    for lp, valid in pages:
         pp = int(w.block_table[row, lp])
         codec = int(w.page_codec[pp])
         kc, vc = codec & 0xF, codec >> 4
         sk, sv = w.page_scale[pp, h]
-        ks.append(plane_values(w.pool, int(w.page_k_off[pp]), kc, hkv, P, D, h, sk, False, valid))
-        vs.append(plane_values(w.pool, int(w.page_v_off[pp]), vc, hkv, P, D, h, sv, True, valid))
-    if not ks:
-        return np.zeros((0, D)), np.zeros((0, D))
-    return np.concatenate(ks), np.concatenate(vs)
+        K[t:t + valid] = plane_values(w.pool, int(w.page_k_off[pp]), kc, hkv, P, D, h, sk, False, valid)
+        V[t:t + valid] = plane_values(w.pool, int(w.page_v_off[pp]), vc, hkv, P, D, h, sv, True, valid)
+        t += valid
+    return K, V
 
 
 def _softmax_attention(K, V, q, tau):

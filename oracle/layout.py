@@ -1,29 +1,39 @@
 """Reads one (page, KV head) plane from the byte arena as float64 values.
 
 In-page layout being read (the library's own definition; the pages give codec
-semantics, not a bit layout): a plane is the codes of every KV head, head by
-head, then -- for INT8/INT4 only -- fp16 group scales ``[Hkv][P][D/32]``.
-Within one head's codes, element (t, i) sits at element index
+semantics, not a bit layout). A plane is the codes of every KV head, head
+after head, then -- for INT8/INT4 only -- fp16 group scales
+``[Hkv][P][D/32]`` (token-major). One head's codes are P/16 tiles of 16
+tokens, each TB = 16*D*bits/8 bytes. Inside a tile, each of 64 "lanes" owns
+a run of R = TB/64 bytes:
 
-* K:  t*D + i;
-* V:  (t // 16)*16*D + ((t % 16)//4 * 16 + i % 16) * (D//16) * 4
-      + (i // 16) * 4 + t % 4;
+* K, codecs with one scale per page (FP16, BF16, FP8): lane 16*kq + t holds
+  token t, dims (D/4)*kq + e, e = 0 .. D/4-1 (run element e);
+* K, group-scale codecs (INT8, INT4): lane 16*kq + t holds token t, dims
+  32*c + 8*kq + j as run element e = 8*c + j;
+* V (all codecs): lane 16*qd + c holds tokens 4*qd + j and dims 16*n + c as
+  run element e = 4*n + j.
 
-and INT4 packs eight elements per 32-bit little-endian word: element e is in
-word e // 8 at nibble slot (r % 2)*4 + r // 2 with r = e % 8 (even elements
-in the low half-word, odd ones in the high half-word).
+Run element e occupies run bytes e*bits/8 (INT4: eight elements per 32-bit
+word, element r = e % 8 of word e // 8 in nibble slot (r % 2)*4 + r // 2).
+Run byte rb of lane L is stored at tile offset (rb // 16)*1024 + 16*L +
+rb % 16 when R >= 16, else at R*L + rb.
+
 Pinned in tests/test_oracle_layout.py by hand-placed single codes.
 """
 from __future__ import annotations
 
+import functools
+
 import numpy as np
 
-from .codecs import decode_bf16, decode_fp8_e4m3, decode_fp16, decode_int4, decode_int8
+from .codecs import decode_bf16, decode_fp8_e4m3, decode_fp16, decode_int8
 
 FP16, BF16, FP8, INT8, INT4 = 0, 1, 2, 3, 4
 BITS = {FP16: 16, BF16: 16, FP8: 8, INT8: 8, INT4: 4}
 _FP8_TABLE = decode_fp8_e4m3(np.arange(256))
 _INT8_TABLE = decode_int8(np.arange(256))
+_INT4_TABLE = np.array([v - 16 if v >= 8 else v for v in range(16)], dtype=np.float64)
 
 
 def _read(pool, off: int, n: int) -> np.ndarray:
@@ -34,14 +44,41 @@ def _read(pool, off: int, n: int) -> np.ndarray:
     return pool.read(off, n)
 
 
-def element_index(P: int, D: int, is_v: bool) -> np.ndarray:
-    """[P, D] element index of (t, i) inside one head's codes."""
+@functools.lru_cache(maxsize=None)
+def code_position(P: int, D: int, codec: int, is_v: bool):
+    """Byte offset inside one head's codes of element (t, i), shape [P, D],
+    and for INT4 the nibble (0 = bits 0..3, 1 = bits 4..7); read-only."""
+    bits = BITS[codec]
     t = np.arange(P)[:, None]
     i = np.arange(D)[None, :]
-    if not is_v:
-        return t * D + i
-    return ((t // 16) * 16 * D + ((t % 16) // 4 * 16 + i % 16) * (D // 16) * 4
-            + (i // 16) * 4 + t % 4)
+    tile, tt = t // 16, t % 16
+    if is_v:
+        lane = 16 * (tt // 4) + i % 16
+        e = 4 * (i // 16) + tt % 4
+    elif codec in (INT8, INT4):
+        lane = 16 * ((i % 32) // 8) + tt
+        e = 8 * (i // 32) + i % 8
+    else:
+        lane = 16 * (i // (D // 4)) + tt
+        e = i % (D // 4)
+    tb = 16 * D * bits // 8
+    run = tb // 64
+    nib = None
+    if bits == 4:
+        r = e % 8
+        slot = (r % 2) * 4 + r // 2
+        rb = 4 * (e // 8) + slot // 2
+        nib = np.broadcast_to(slot % 2, (P, D)).copy()
+        nib.setflags(write=False)
+    else:
+        rb = e * (bits // 8)
+    if run >= 16:
+        off = tile * tb + (rb // 16) * 1024 + 16 * lane + rb % 16
+    else:
+        off = tile * tb + run * lane + rb
+    off = np.broadcast_to(off, (P, D)).copy()
+    off.setflags(write=False)
+    return off, nib
 
 
 def plane_values(pool, off: int, codec: int, hkv: int, P: int, D: int, h: int,
@@ -51,17 +88,17 @@ def plane_values(pool, off: int, codec: int, hkv: int, P: int, D: int, h: int,
         raise ValueError(f"unknown codec {codec}")
     head_bytes = P * D * BITS[codec] // 8
     raw = _read(pool, int(off) + h * head_bytes, head_bytes)
-    if codec == FP16:
-        vals = decode_fp16(raw.view("<u2"))
-    elif codec == BF16:
-        vals = decode_bf16(raw.view("<u2"))
+    pos, nib = code_position(P, D, codec, is_v)
+    pos = pos[:valid]
+    if codec in (FP16, BF16):
+        code = raw[pos].astype(np.int64) | (raw[pos + 1].astype(np.int64) << 8)
+        x = decode_fp16(code) if codec == FP16 else decode_bf16(code)
     elif codec == FP8:
-        vals = _FP8_TABLE[raw]
+        x = _FP8_TABLE[raw[pos]]
     elif codec == INT8:
-        vals = _INT8_TABLE[raw]
+        x = _INT8_TABLE[raw[pos]]
     else:
-        vals = decode_int4(raw)
-    x = vals[element_index(P, D, is_v)[:valid]]
+        x = _INT4_TABLE[(raw[pos] >> (4 * nib[:valid])) & 0xF]
     if codec == FP8:
         x = x * float(fp8_scale)
     elif codec in (INT8, INT4):

@@ -43,9 +43,6 @@ enum : int { C_FP16 = 0, C_BF16 = 1, C_FP8 = 2, C_INT8 = 3, C_INT4 = 4, C_ANY = 
 #ifndef PKV_RING_WORDS
 #define PKV_RING_WORDS 32  // 32-bit words of tile codes a wave keeps in flight
 #endif
-#ifndef PKV_KPERM
-#define PKV_KPERM 1  // contiguous K loads for codecs with one scale per page
-#endif
 
 constexpr int WAVES = 4;
 constexpr int THREADS = 64 * WAVES;
@@ -72,14 +69,14 @@ constexpr int RSRC_WORD3 = 0x00020000;  // gfx9-family raw buffer format
 __device__ inline rsrc_t make_rsrc(const uint8_t* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, RSRC_WORD3);
 }
+constexpr int CPOL_NT = 2;  // non-temporal: page codes are read once
+template <int CPOL = 0>
 __device__ inline u4 bload16(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CPOL));
 }
+template <int CPOL = 0>
 __device__ inline u2 bload8(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
-}
-__device__ inline uint32_t bload4(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+  return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, CPOL));
 }
 
 // Page descriptor staged in LDS (32 bytes).
@@ -149,63 +146,27 @@ __device__ inline float unif(float x) {
 }
 
 // ---------------------------------------------------------------- loads
-// K: lane reads token `tok` of head block `head` (byte offset in the plane),
-// 8 dims for each of the D/32 score MFMAs. With PERM (codecs with one scale per
-// page) the lane's dims are (D/4)kq .. (D/4)kq + D/4 - 1, one contiguous run;
-// otherwise (group scales) MFMA c must see exactly group c, so the lane reads
-// dims 32c + 8kq .. +7 for each c. q is permuted the same way, so the dot
-// products are unchanged.
-template <int D, int C, bool PERM>
-__device__ inline void load_k(uint32_t* w, rsrc_t r, uint32_t head, int tok, int kq) {
-  constexpr int NC = D / 32;
-  if constexpr (PERM && bits_of(C) == 16) {
-    const uint32_t o = head + (uint32_t)(tok * D + (D / 4) * kq) * 2;
+// The lane's run of one 16-token tile: R = D*bits/32 bytes. Tiles are stored
+// as the image of the 64 lanes' registers, 16-byte chunks interleaved over the
+// lanes (chunk i of lane L at i*1024 + 16*L), so every load instruction of a
+// wave covers 1 KB of consecutive bytes: whole cache lines, read once, which
+// is what lets the non-temporal hint pay off. The run holds, for K, token
+// lane%16 and dims (D/4)(lane/16) + e (one scale per page) or 32c + 8(lane/16)
+// + j (group scales); for V, tokens 4(lane/16) + j of dim 16n + lane%16.
+template <int D, int BITS>
+__device__ inline void load_run(uint32_t* w, rsrc_t r, uint32_t head, int sub, int lane) {
+  constexpr int R = D * BITS / 32;
+  constexpr int TB = 16 * D * BITS / 8;
+  const uint32_t base = head + (uint32_t)sub * TB;
+  if constexpr (R >= 16) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const u4 x = bload16(r, o + 16 * c);
-      w[4 * c + 0] = x[0]; w[4 * c + 1] = x[1]; w[4 * c + 2] = x[2]; w[4 * c + 3] = x[3];
-    }
-  } else if constexpr (PERM && bits_of(C) == 8) {
-    const uint32_t o = head + (uint32_t)(tok * D + (D / 4) * kq);
-#pragma unroll
-    for (int i = 0; i < NC / 2; ++i) {
-      const u4 x = bload16(r, o + 16 * i);
-      w[4 * i + 0] = x[0]; w[4 * i + 1] = x[1]; w[4 * i + 2] = x[2]; w[4 * i + 3] = x[3];
-    }
-  } else if constexpr (bits_of(C) == 16) {
-    const uint32_t o = head + (uint32_t)(tok * D + 8 * kq) * 2;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const u4 x = bload16(r, o + 64 * c);
-      w[4 * c + 0] = x[0]; w[4 * c + 1] = x[1]; w[4 * c + 2] = x[2]; w[4 * c + 3] = x[3];
-    }
-  } else if constexpr (bits_of(C) == 8) {
-    const uint32_t o = head + (uint32_t)(tok * D + 8 * kq);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const u2 x = bload8(r, o + 32 * c);
-      w[2 * c + 0] = x[0]; w[2 * c + 1] = x[1];
-    }
-  } else {
-    const uint32_t o = head + (uint32_t)(tok * D + 8 * kq) / 2;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) w[c] = bload4(r, o + 16 * c);
-  }
-}
-
-// V: lane l reads its contiguous run of D/4 elements inside tile `sub`.
-template <int D, int C>
-__device__ inline void load_v(uint32_t* w, rsrc_t r, uint32_t head, int sub, int lane) {
-  constexpr int RUN_BYTES = D * bits_of(C) / 32;
-  const uint32_t o = head + (uint32_t)(sub * 16 * D + lane * (D / 4)) * bits_of(C) / 8;
-  if constexpr (RUN_BYTES >= 16) {
-#pragma unroll
-    for (int i = 0; i < RUN_BYTES / 16; ++i) {
-      const u4 x = bload16(r, o + 16 * i);
+    for (int i = 0; i < R / 16; ++i) {
+      const u4 x = bload16<CPOL_NT>(r, base + 1024 * i + 16 * lane);
       w[4 * i + 0] = x[0]; w[4 * i + 1] = x[1]; w[4 * i + 2] = x[2]; w[4 * i + 3] = x[3];
     }
   } else {
-    const u2 x = bload8(r, o);
+    static_assert(R == 8, "run of 8 bytes expected");
+    const u2 x = bload8<CPOL_NT>(r, base + 8 * lane);
     w[0] = x[0]; w[1] = x[1];
   }
 }
@@ -318,10 +279,11 @@ __device__ inline h4 v_frag_any(const uint32_t* w, int n, int codec) {
   }
 }
 
-// Whether a kernel variant reads K with the contiguous (permuted-dims) layout.
+// Whether K runs hold a contiguous stretch of dims (codecs with one scale per
+// page) rather than 8 dims of each 32-dim group (group-scale codecs).
 template <int KC>
 __host__ __device__ constexpr bool k_perm() {
-  return PKV_KPERM && KC != C_ANY && !is_int(KC) && KC <= C_INT4;
+  return KC != C_ANY && !is_int(KC);
 }
 // Byte offset of head h's codes inside a plane.
 template <int D>
@@ -348,25 +310,24 @@ __device__ inline TileInfo issue_tile(Tile<D, KC, VC>& t, const Desc* desc, int 
   const int page = a.page;
   const rsrc_t rk = make_rsrc(a.pool + uni64(desc[i].k), live ? (uint32_t)plane_bytes(ti.kc, a.hkv, page, D) : 0u);
   const rsrc_t rv = make_rsrc(a.pool + uni64(desc[i].v), live ? (uint32_t)plane_bytes(ti.vc, a.hkv, page, D) : 0u);
-  const int col = lane & 15, kq = lane >> 4;
-  const int tok = 16 * sub + col;
+  const int kq = lane >> 4;
   if constexpr (KC == C_ANY) {
-    switch (ti.kc) {
-      case C_FP16: case C_BF16: load_k<D, C_FP16, false>(t.k, rk, head_off<D>(C_FP16, h, page), tok, kq); break;
-      case C_FP8: case C_INT8: load_k<D, C_FP8, false>(t.k, rk, head_off<D>(C_FP8, h, page), tok, kq); break;
-      default: load_k<D, C_INT4, false>(t.k, rk, head_off<D>(C_INT4, h, page), tok, kq); break;
+    switch (bits_of(ti.kc)) {
+      case 16: load_run<D, 16>(t.k, rk, head_off<D>(C_FP16, h, page), sub, lane); break;
+      case 8: load_run<D, 8>(t.k, rk, head_off<D>(C_FP8, h, page), sub, lane); break;
+      default: load_run<D, 4>(t.k, rk, head_off<D>(C_INT4, h, page), sub, lane); break;
     }
   } else {
-    load_k<D, KC, k_perm<KC>()>(t.k, rk, head_off<D>(KC, h, page), tok, kq);
+    load_run<D, bits_of(KC)>(t.k, rk, head_off<D>(KC, h, page), sub, lane);
   }
   if constexpr (VC == C_ANY) {
-    switch (ti.vc) {
-      case C_FP16: case C_BF16: load_v<D, C_FP16>(t.v, rv, head_off<D>(C_FP16, h, page), sub, lane); break;
-      case C_FP8: case C_INT8: load_v<D, C_FP8>(t.v, rv, head_off<D>(C_FP8, h, page), sub, lane); break;
-      default: load_v<D, C_INT4>(t.v, rv, head_off<D>(C_INT4, h, page), sub, lane); break;
+    switch (bits_of(ti.vc)) {
+      case 16: load_run<D, 16>(t.v, rv, head_off<D>(C_FP16, h, page), sub, lane); break;
+      case 8: load_run<D, 8>(t.v, rv, head_off<D>(C_FP8, h, page), sub, lane); break;
+      default: load_run<D, 4>(t.v, rv, head_off<D>(C_INT4, h, page), sub, lane); break;
     }
   } else {
-    load_v<D, VC>(t.v, rv, head_off<D>(VC, h, page), sub, lane);
+    load_run<D, bits_of(VC)>(t.v, rv, head_off<D>(VC, h, page), sub, lane);
   }
   const uint32_t tok0 = (uint32_t)(h * page + 16 * sub + 4 * kq);
   if constexpr (Tile<D, KC, VC>::KS) {
@@ -402,7 +363,7 @@ __device__ inline h4 v_operand(const T& t, const TileInfo& ti, int n, int kq, bo
 // Scores, online-softmax update and P.V of one staged tile.
 template <int D, int KC, int VC>
 __device__ inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti, const h8* qv,
-                                    float scale_log2, float& m_run, float& l_run, f4* acc,
+                                    const h8* qg, float scale_log2, float& m_run, float& l_run, f4* acc,
                                     int lane) {
   constexpr int NC = D / 32, NB = D / 16;
   if (ti.valid == 0) return;
@@ -416,7 +377,7 @@ __device__ inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       h8 kf = KC == C_ANY ? k_frag_any<D>(t.k, c, ti.kc) : k_frag<KC == C_ANY ? 0 : KC, D>(t.k, c);
-      sc[c] = mfma32(kf, qv[c], zero);
+      sc[c] = mfma32(kf, (KC == C_ANY && kgrouped) ? qg[c] : qv[c], zero);
     }
     if (kgrouped) {
       const _Float16* ks = reinterpret_cast<const _Float16*>(t.ks);
@@ -544,19 +505,20 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
   const int s0 = part * a.pages_per_part;
   const int s1 = min(s0 + a.pages_per_part, npg);
 
-  // ---- q of this KV head's query group (B operand of the score MFMA)
+  // ---- q of this KV head's query group (B operand of the score MFMA), in
+  // the dim order of the K runs: qv for one-scale codecs (and the per-page
+  // dispatch variant), qg for group-scale codecs
   h8 qv[NC];
+  h8 qg[KC == C_ANY ? NC : 1];
   {
-    constexpr bool PERM = k_perm<KC>();
-    const _Float16* qp = reinterpret_cast<const _Float16*>(a.q) +
-                         ((size_t)b * a.hq + (size_t)h * G + col) * D + (PERM ? D / 4 : 8) * kq;
+    const _Float16* qrow = reinterpret_cast<const _Float16*>(a.q) + ((size_t)b * a.hq + (size_t)h * G + col) * D;
+    constexpr bool PERM = KC == C_ANY || k_perm<KC>();
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      if (col < G) {
-        qv[c] = *reinterpret_cast<const h8*>(qp + (PERM ? 8 : 32) * c);
-      } else {
-        qv[c] = h8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
+      const int d0 = PERM ? (D / 4) * kq + 8 * c : 32 * c + 8 * kq;
+      qv[c] = col < G ? *reinterpret_cast<const h8*>(qrow + d0) : h8{0, 0, 0, 0, 0, 0, 0, 0};
+      if constexpr (KC == C_ANY)
+        qg[c] = col < G ? *reinterpret_cast<const h8*>(qrow + 32 * c + 8 * kq) : h8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
 
@@ -634,7 +596,7 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
           const int kn = min(wave + (it + s + DEPTH - 1) * WAVES, klast);
           const int nx = (s + DEPTH - 1) % DEPTH;
           inf[nx] = issue_tile<D, KC, VC>(t[nx], desc, kn, tpp, a, h, lane);
-          if (it + s < nmine) consume_tile<D, KC, VC>(t[s], inf[s], qv, a.scale_log2, m_run, l_run, acc, lane);
+          if (it + s < nmine) consume_tile<D, KC, VC>(t[s], inf[s], qv, qg, a.scale_log2, m_run, l_run, acc, lane);
         }
       }
     }

@@ -1,16 +1,23 @@
 """Writes physical pages (all KV heads) into their K and V planes.
 
 In-page layout (this library's own definition; the pages fix codec semantics
-but no bit layout). For a page of P tokens, Hkv heads and head_dim D, each
-plane is ``codes[Hkv][...]`` followed, for INT8/INT4, by
+but no bit layout). A plane is ``codes[Hkv][...]`` followed, for INT8/INT4, by
 ``scales[Hkv][P][D/32]`` fp16 (token-major, one scale per 32 dims).
 
-* K codes, per head: token-major rows, element (t, i) at element index t*D + i.
-* V codes, per head: 16-token tiles; inside a tile the element order is
-  (token quad qd, dim-in-block c, dim block n, token-in-quad j) with
-  t = 16*tile + 4*qd + j and i = 16*n + c.
-* INT4 packs 8 elements per 32-bit word: even elements in the low half-word,
-  odd elements in the high half-word, each half in element order.
+One head's codes are P/16 tiles of 16 tokens. A tile is stored as the image
+of 64 lanes' registers: lane L owns a run of R = tile_bytes / 64 bytes, and
+for R >= 16 the runs are interleaved in 16-byte chunks (chunk i of every
+lane, lane after lane, then chunk i+1), so each 16-byte-per-lane load covers
+1 KB of consecutive bytes. Which elements a lane's run holds:
+
+* K, one scale per page (FP16/BF16/FP8): lane 16*kq + t = token t, dims
+  (D/4)*kq .. (D/4)*kq + D/4 - 1;
+* K, group scales (INT8/INT4): lane 16*kq + t = token t, dims 32*c + 8*kq + j
+  in the order (c, j);
+* V: lane 16*qd + c = tokens 4*qd + j and dims 16*n + c in the order (n, j).
+
+INT4 packs 8 elements per 32-bit word: even elements in the low half-word,
+odd elements in the high half-word, each half in element order.
 """
 from __future__ import annotations
 
@@ -42,18 +49,31 @@ def align(n: int, a: int = PLANE_ALIGN) -> int:
     return (n + a - 1) // a * a
 
 
-def v_tile_order(x: np.ndarray) -> np.ndarray:
-    """[..., P, D] natural values -> [..., P*D] in the V tile order."""
+def lane_runs(x: np.ndarray, is_v: bool, grouped: bool) -> np.ndarray:
+    """[..., P, D] natural values -> [..., P/16, 64, D/4]: per tile, per lane,
+    the lane's run of elements."""
     *lead, p, d = x.shape
-    assert p % 16 == 0 and d % 16 == 0
-    y = x.reshape(*lead, p // 16, 4, 4, d // 16, 16)          # tile, qd, j, n, c
     nl = len(lead)
-    perm = list(range(nl)) + [nl + 0, nl + 1, nl + 4, nl + 3, nl + 2]  # tile, qd, c, n, j
-    return y.transpose(perm).reshape(*lead, p * d)
+    ax = list(range(nl))
+    if is_v:
+        y = x.reshape(*lead, p // 16, 4, 4, d // 16, 16)           # tile, qd, j, n, c
+        y = y.transpose(*ax, nl, nl + 1, nl + 4, nl + 3, nl + 2)    # tile, qd, c, n, j
+    elif grouped:
+        y = x.reshape(*lead, p // 16, 16, d // 32, 4, 8)           # tile, t, c, kq, j
+        y = y.transpose(*ax, nl, nl + 3, nl + 1, nl + 2, nl + 4)    # tile, kq, t, c, j
+    else:
+        y = x.reshape(*lead, p // 16, 16, 4, d // 4)               # tile, t, kq, e
+        y = y.transpose(*ax, nl, nl + 2, nl + 1, nl + 3)            # tile, kq, t, e
+    return y.reshape(*lead, p // 16, 64, d // 4)
 
 
-def _k_order(x: np.ndarray) -> np.ndarray:
-    return x.reshape(*x.shape[:-2], x.shape[-2] * x.shape[-1])
+def interleave_chunks(b: np.ndarray) -> np.ndarray:
+    """Run bytes [..., T, 64, R] -> [..., T*64*R]: for R >= 16 chunk i of all
+    64 lanes is stored before chunk i+1."""
+    *lead, t, lanes, r = b.shape
+    if r >= 16:
+        b = b.reshape(*lead, t, lanes, r // 16, 16).swapaxes(-3, -2)
+    return np.ascontiguousarray(b).reshape(*lead, t * lanes * r)
 
 
 def fp8_scales(x: np.ndarray) -> np.ndarray:
@@ -70,23 +90,29 @@ def encode_plane(x: np.ndarray, codec: int, v_order: bool) -> tuple[np.ndarray, 
     the scales are 1.0 for codecs other than FP8).
     """
     n, hkv, p, d = x.shape
-    order = v_tile_order if v_order else _k_order
     ones = np.ones((n, hkv), dtype=np.float32)
+    grouped = codec in (INT8, INT4)
+
+    def place(codes_elems: np.ndarray) -> np.ndarray:
+        runs = lane_runs(codes_elems, v_order, grouped)              # [n, Hkv, T, 64, D/4]
+        if codec == INT4:
+            rb = pack_int4(runs)                                      # [..., D/8] bytes
+        else:
+            rb = np.ascontiguousarray(runs).view(np.uint8)            # little-endian bytes
+        return interleave_chunks(rb).reshape(n, -1)
+
     if codec in (FP16, BF16):
         enc = encode_fp16 if codec == FP16 else encode_bf16
-        body = np.ascontiguousarray(order(enc(x))).astype("<u2").view(np.uint8)
-        return body.reshape(n, -1), ones
+        return place(enc(x).astype("<u2")), ones
     if codec == FP8:
         s = fp8_scales(x)
         y = np.clip(x / s[..., None, None], -FP8_MAX, FP8_MAX).astype(np.float32)
         codes = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn)
-        codes = codes.view(torch.uint8).numpy()
-        return np.ascontiguousarray(order(codes)).reshape(n, -1), s
+        return place(codes.view(torch.uint8).numpy()), s
     if codec in (INT8, INT4):
         qmax = 127 if codec == INT8 else 7
         codes, scales = encode_int_g32(x, qmax)
-        flat = np.ascontiguousarray(order(codes))               # [n, Hkv, P*D] int8
-        body = flat.view(np.uint8) if codec == INT8 else pack_int4(flat)
+        body = place(codes)
         sc = np.ascontiguousarray(scales).astype("<f2").view(np.uint8)
-        return np.concatenate([body.reshape(n, -1), sc.reshape(n, -1)], axis=1), ones
+        return np.concatenate([body, sc.reshape(n, -1)], axis=1), ones
     raise ValueError(f"unknown codec {codec}")

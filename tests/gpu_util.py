@@ -49,7 +49,7 @@ def compare(out, lse, ref_out, ref_lse, what=""):
 def poison_tails(w):
     """Overwrite every byte the row lengths exclude inside attended pages'
     tail tokens with bytes that decode to NaN/huge values in every codec."""
-    from oracle.layout import BITS, element_index
+    from oracle.layout import BITS, code_position
     P, D, hkv = w.page_size, w.head_dim, w.num_kv_heads
     arr = w.pool.as_array() if w.pool.is_dense else None
     assert arr is not None
@@ -63,26 +63,25 @@ def poison_tails(w):
         c = int(w.page_codec[pp])
         for off, codec, is_v in ((int(w.page_k_off[pp]), c & 15, False), (int(w.page_v_off[pp]), c >> 4, True)):
             bits = BITS[codec]
-            idx = element_index(P, D, is_v)[valid:].ravel()
+            pos, nib = code_position(P, D, codec, is_v)
+            pos = pos[valid:].ravel()
             head_bytes = P * D * bits // 8
             for h in range(hkv):
                 base = off + h * head_bytes
                 if bits == 16:
-                    for k in (0, 1):
-                        arr[base + 2 * idx + k] = 0xFF           # fp16/bf16 NaN
+                    arr[base + pos] = 0xFF                        # fp16/bf16 NaN
+                    arr[base + pos + 1] = 0xFF
                 elif bits == 8:
-                    arr[base + idx] = 0x7F if codec == synth.FP8 else 0x80  # NaN / -128
-                else:                                            # int4: nibble -8
-                    r = idx % 8
-                    slot = (r % 2) * 4 + r // 2
-                    byte = base + 4 * (idx // 8) + slot // 2
-                    hi = (slot % 2) == 1
-                    arr[byte[hi]] = (arr[byte[hi]] & 0x0F) | 0x80
-                    arr[byte[~hi]] = (arr[byte[~hi]] & 0xF0) | 0x08
+                    arr[base + pos] = 0x7F if codec == synth.FP8 else 0x80  # NaN / -128
+                else:                                             # int4: nibble -8
+                    hi = nib[valid:].ravel() == 1
+                    b_hi, b_lo = base + pos[hi], base + pos[~hi]
+                    arr[b_hi] = (arr[b_hi] & 0x0F) | 0x80
+                    arr[b_lo] = (arr[b_lo] & 0xF0) | 0x08
             if codec in (synth.INT8, synth.INT4):
                 sc = off + hkv * P * D * bits // 8
                 for h in range(hkv):
                     s0 = sc + (h * P + valid) * (D // 32) * 2
                     s1 = sc + (h * P + P) * (D // 32) * 2
-                    arr[s0:s1] = 0x7C                             # fp16 ~ 0x7C7C: NaN
+                    arr[s0:s1] = 0x7C                             # fp16 0x7C7C: NaN
     return w

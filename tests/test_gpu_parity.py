@@ -149,16 +149,16 @@ def one_token_v_codes(codec, codes_for_row):
     makes out = V of that token exactly."""
     rows = len(codes_for_row)
     w = small([1] * rows, FP16, codec, hq=2, hkv=1, dim=128, page=16)
-    from oracle.layout import BITS, element_index
+    from oracle.layout import BITS, code_position
     arr = w.pool.as_array()
-    idx = element_index(16, 128, True)[0]          # token 0, dims 0..127
+    idx = code_position(16, 128, codec, True)[0][0]   # token 0, dims 0..127
     for r, codes in enumerate(codes_for_row):
         pp = int(w.block_table[r, 0])
         off = int(w.page_v_off[pp])
         if BITS[codec] == 16:
             b = np.asarray(codes, dtype="<u2").view(np.uint8).reshape(-1, 2)
-            arr[off + 2 * idx] = b[:, 0]
-            arr[off + 2 * idx + 1] = b[:, 1]
+            arr[off + idx] = b[:, 0]                      # byte offsets, little-endian
+            arr[off + idx + 1] = b[:, 1]
         elif BITS[codec] == 8:
             arr[off + idx] = np.asarray(codes, dtype=np.uint8)
         else:

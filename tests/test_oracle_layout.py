@@ -9,48 +9,66 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.layout import element_index, plane_values
+from oracle.layout import code_position, plane_values
 from synth.encode import encode_int_g32
 from synth.layout import BF16, FP8, FP16, INT4, INT8, encode_plane
 
 
-def test_element_index_hand_worked():
-    # P=32, D=32. K: (t, i) -> t*32 + i.
-    k = element_index(32, 32, is_v=False)
-    assert k[5, 7] == 167 and k[31, 31] == 1023
-    v = element_index(32, 32, is_v=True)
-    # (t=5, i=7): tile 0, quad 1, token-in-quad 1, dim block 0, dim-in-block 7
-    #   -> ((1*16 + 7) * 2 + 0) * 4 + 1 = 185
+def test_code_position_hand_worked():
+    # FP8, P=32, D=32: tile 512 B, run R = 8 B (no chunk interleave).
+    k, _ = code_position(32, 32, FP8, is_v=False)
+    # K (5, 7): kq = 7 // 8 = 0, e = 7 -> lane 5 -> 8*5 + 7 = 47
+    assert k[5, 7] == 47
+    # K (21, 19): tile 1, kq = 2, e = 3 -> lane 37 -> 512 + 8*37 + 3 = 811
+    assert k[21, 19] == 811
+    v, _ = code_position(32, 32, FP8, is_v=True)
+    # V (5, 7): qd 1, j 1, c 7 -> lane 23, e = 1 -> 8*23 + 1 = 185
     assert v[5, 7] == 185
-    # (t=21, i=19): tile 1 (base 512), quad 1, j 1, block 1, c 3
-    #   -> 512 + ((16 + 3) * 2 + 1) * 4 + 1 = 669
+    # V (21, 19): tile 1, qd 1, j 1, n 1, c 3 -> lane 19, e = 5 -> 512 + 152 + 5 = 669
     assert v[21, 19] == 669
-    # (t=0, i=16): block 1 of lane (0, 0) -> 4
-    assert v[0, 16] == 4
-    # every position used exactly once
-    assert np.array_equal(np.sort(v.ravel()), np.arange(32 * 32))
+    for pos in (k, v):
+        assert np.array_equal(np.sort(pos.ravel()), np.arange(32 * 32))
+    # FP8, D=128: run 32 B, two 16-byte chunks interleaved over the 64 lanes.
+    k, _ = code_position(16, 128, FP8, is_v=False)
+    # (3, 100): kq 3, e 4 -> lane 51, chunk 0 -> 16*51 + 4 = 820
+    assert k[3, 100] == 820
+    # (3, 121): kq 3, e 25 -> lane 51, chunk 1 -> 1024 + 816 + 9 = 1849
+    assert k[3, 121] == 1849
+    assert np.array_equal(np.sort(k.ravel()), np.arange(16 * 128))
+    # FP16 V, D=128: run 64 B. (6, 37): qd 1, j 2, c 5, n 2 -> lane 21,
+    # e = 10 -> run byte 20 -> chunk 1 -> 1024 + 16*21 + 4 = 1364
+    v, _ = code_position(16, 128, FP16, is_v=True)
+    assert v[6, 37] == 1364
+    # INT8 K (group scales), D=64: run 16 B. (2, 45): c 1, kq 1, j 5 ->
+    # lane 18, e = 13 -> 16*18 + 13 = 301
+    k, _ = code_position(16, 64, INT8, is_v=False)
+    assert k[2, 45] == 301
+    # INT4 K, D=32: run 4 B. (3, 5): lane 3, e 5 -> nibble slot 6 -> byte
+    # 4*3 + 3 = 15, low nibble
+    k, nib = code_position(16, 32, INT4, is_v=False)
+    assert k[3, 5] == 15 and nib[3, 5] == 0
 
 
 def test_single_fp16_code_in_k_and_v():
     hkv, P, D = 2, 32, 32
     pool = np.zeros(hkv * P * D * 2, dtype=np.uint8)
     head = 1
-    pos = head * P * D * 2 + 669 * 2                  # V element (21, 19) of head 1
+    # V (21, 19) of head 1: tile 1 (1024 B each), lane 19, e = 5 -> byte 1338
+    pos = head * P * D * 2 + 1338
     pool[pos:pos + 2] = np.frombuffer(np.float16(1.5).tobytes(), np.uint8)
     v = plane_values(pool, 0, FP16, hkv, P, D, head, 1.0, True, P)
     assert v[21, 19] == 1.5 and np.count_nonzero(v) == 1
+    # the same bytes read as K: lane 19 = 16*1 + 3 -> token 19, dim 8 + 5
     k = plane_values(pool, 0, FP16, hkv, P, D, head, 1.0, False, P)
-    t, i = divmod(669, D)
-    assert k[t, i] == 1.5 and np.count_nonzero(k) == 1
+    assert k[19, 13] == 1.5 and np.count_nonzero(k) == 1
 
 
 def test_single_int4_code_and_scale():
     hkv, P, D = 1, 16, 32
     codes = P * D // 2
     pool = np.zeros(codes + P * (D // 32) * 2, dtype=np.uint8)
-    # K element (3, 5) -> element 101 -> word 12, r = 5 -> nibble slot 6
-    # (bits 24..27) -> byte 48 + 3 = 51, low nibble; value -3 -> 0xD
-    pool[51] = 0x0D
+    # K element (3, 5) -> byte 15, low nibble; value -3 -> 0xD
+    pool[15] = 0x0D
     # scale of token 3, group 0 -> fp16 at codes + 3*2
     pool[codes + 6:codes + 8] = np.frombuffer(np.float16(0.25).tobytes(), np.uint8)
     k = plane_values(pool, 0, INT4, hkv, P, D, 0, 1.0, False, P)
