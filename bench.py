@@ -33,6 +33,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_182_amd", "csrc", "pkv_kernels.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "splitk_fp8_1m_traffic.md")
+COPY_BYTES = 256 << 20
 METRIC = "effective KV-read GB/s (% of HBM peak) + decode-attn steps/s at 32K and 1M ctx"
 
 
@@ -196,28 +199,75 @@ def time_workload(torch, pkv, w, steps, warmup, min_rot_bytes):
     return res
 
 
-def cpu_baseline(w_full):
-    """The oracle, as it is, on a bounded sample of the headline workload: all
-    8 query heads of one KV head over the whole 1M-token row."""
-    import numpy as np
+def cpu_baseline(w_full, min_seconds=10.0):
+    """The oracle, as it is, on a bounded sample of the headline workload:
+    whole 1M-token steps (both KV heads, all 16 query heads), repeated until
+    at least ``min_seconds`` of CPU work."""
+    import oracle
     from synth import effective_kv_bytes_formula
-    from oracle.attention import _softmax_attention, gather_kv
     try:
         from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas = 1
-    G = w_full.num_q_heads // w_full.num_kv_heads
-    t = time.perf_counter()
-    K, V = gather_kv(w_full, 0, 1)
-    _softmax_attention(K, V, w_full.q[0, G:2 * G].astype(np.float64), w_full.softmax_scale)
-    dt = time.perf_counter() - t
-    sample_bytes = effective_kv_bytes_formula(w_full) / w_full.num_kv_heads
-    return {"value": sample_bytes / dt / 1e9, "unit": "GB/s", "cores": int(blas), "kind": "oracle",
-            "sample": f"{w_full.name}: KV head 1 (8 query heads) of the 1M-token row, "
-                      f"{sample_bytes / 2**20:.1f} MiB effective, {dt:.1f} s; float64 numpy, "
-                      f"page gather single-threaded, BLAS with {blas} threads",
-            "seconds": dt}
+    reps, t = 0, time.perf_counter()
+    while True:
+        oracle.decode_attention(w_full)
+        reps += 1
+        dt = time.perf_counter() - t
+        if dt >= min_seconds or reps >= 50:
+            break
+    eff = effective_kv_bytes_formula(w_full)
+    return {"value": reps * eff / dt / 1e9, "unit": "GB/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"{reps} whole step(s) of {w_full.name} ({eff / 2**20:.1f} MiB effective each) "
+                      f"in {dt:.1f} s; float64 numpy, page gather single-threaded, BLAS with "
+                      f"{blas} threads",
+            "seconds": dt, "steps_per_s": reps / dt}
+
+
+def kernel_source_sha256() -> str:
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per split-K launch from the committed rocprofv3 counter
+    summary, or None when it is missing or the kernel source changed since."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(ln.split(":", 1) for ln in text.splitlines() if ln.startswith("traffic_"))
+    try:
+        if fields["traffic_kernel_sha256"].strip() != kernel_source_sha256():
+            return None
+        return int(fields["traffic_bytes_per_launch"].strip())
+    except (KeyError, ValueError):
+        return None
+
+
+def profile_pass(torch, pkv, synth):
+    """Short run for rocprofv3: the 1M-token split-K kernel (partials only) ten
+    times over two pool copies, then a plain device copy of COPY_BYTES three
+    times, whose counters calibrate the per-dispatch byte counts."""
+    from synth.device import to_device
+    w = synth.config(5)
+    dw = to_device(w)
+    p = params_for(pkv, w)
+    rot, _ = rotations(torch, dw, 1 << 30)
+    n = pkv.num_partitions(p)
+    pacc = torch.empty((w.rows, w.num_q_heads, n, w.head_dim), dtype=torch.float32, device="cuda")
+    pml = torch.empty((w.rows, w.num_q_heads, n, 2), dtype=torch.float32, device="cuda")
+    for i in range(10):
+        pkv.decode_partials(p, *rot[i % len(rot)], part_acc=pacc, part_ml=pml)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"profile pass done: split-K x10 ({w.name}), elementwise copy of {COPY_BYTES} B x3; "
+        f"kernel source sha256 {kernel_source_sha256()}")
 
 
 def main():
@@ -227,6 +277,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="headline workload only, no CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="short run for rocprofv3 (split-K kernel + calibration copy), no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -241,6 +293,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     log(f"device {torch.cuda.get_device_name(0)}")
+    if args.profile_pass:
+        profile_pass(torch, pkv, synth)
+        return
 
     min_rot = 1 << 30
     log("generating 1M-token split-K workload")
@@ -272,7 +327,8 @@ def main():
         "pct_hbm_peak": round(head["pct_hbm_peak"], 2),
         "steps_per_s_1m": round(head["steps_per_s"], 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic()},
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "seconds"},
         "detail": {"headline": head, **also},
     }
