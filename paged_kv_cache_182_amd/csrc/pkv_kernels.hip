@@ -296,11 +296,11 @@ __device__ inline uint32_t head_off(int codec, int h, int page) {
 // resource (zeros, no fault) and is skipped when consumed.
 template <int D, int KC, int VC>
 __device__ inline TileInfo issue_tile(Tile<D, KC, VC>& t, const Desc* desc, int k, int tpp,
-                                      const DecodeArgs& a, int h, int lane) {
+                                      const DecodeArgs& a, int h, int lane, bool dead = false) {
   const int i = k / tpp;
   const int sub = k - i * tpp;
   TileInfo ti;
-  ti.valid = min(max(uni(desc[i].valid) - 16 * sub, 0), 16);
+  ti.valid = dead ? 0 : min(max(uni(desc[i].valid) - 16 * sub, 0), 16);
   const int codec = uni(desc[i].codec);
   ti.kc = KC == C_ANY ? (codec & 15) : KC;
   ti.vc = VC == C_ANY ? (codec >> 4) : VC;
@@ -578,8 +578,8 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
 
     // Ring of DEPTH tiles: while the oldest is consumed, the loads of the
     // next DEPTH-1 are in flight. Issues are unconditional (past the end the
-    // wave re-issues its last tile and never consumes the copy), so the
-    // compiler's wait counts stay exact.
+    // wave issues its last tile again through a zero-size resource and never
+    // consumes it), so the compiler's wait counts stay exact.
     const int ntiles = cn * tpp;
     if (wave < ntiles) {
       constexpr int DEPTH = ring_depth<D, KC, VC>();
@@ -589,13 +589,15 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
       TileInfo inf[DEPTH];
 #pragma unroll
       for (int s = 0; s < DEPTH - 1; ++s)
-        inf[s] = issue_tile<D, KC, VC>(t[s], desc, min(wave + s * WAVES, klast), tpp, a, h, lane);
+        inf[s] = issue_tile<D, KC, VC>(t[s], desc, min(wave + s * WAVES, klast), tpp, a, h, lane,
+                                       wave + s * WAVES > klast);
       for (int it = 0; it < nmine; it += DEPTH) {
 #pragma unroll
         for (int s = 0; s < DEPTH; ++s) {
-          const int kn = min(wave + (it + s + DEPTH - 1) * WAVES, klast);
+          const int kn = wave + (it + s + DEPTH - 1) * WAVES;
           const int nx = (s + DEPTH - 1) % DEPTH;
-          inf[nx] = issue_tile<D, KC, VC>(t[nx], desc, kn, tpp, a, h, lane);
+          // past the end: same loads through a zero-size resource (no traffic)
+          inf[nx] = issue_tile<D, KC, VC>(t[nx], desc, min(kn, klast), tpp, a, h, lane, kn > klast);
           if (it + s < nmine) consume_tile<D, KC, VC>(t[s], inf[s], qv, qg, a.scale_log2, m_run, l_run, acc, lane);
         }
       }
@@ -652,88 +654,80 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
 }
 
 // ---------------------------------------------------------------- fold
-// Grid (row, 32-dim chunk). Thread t covers 4 dims (t % 8) of the parts
-// p = t / 8 + 32k; the 32 part groups are then summed in a fixed order, so
-// the result is run-to-run identical. Every thread's loads are independent,
-// which keeps a few hundred bytes per thread in flight.
-constexpr int FOLD_THREADS = 256;
+// Grid (row, 32-dim chunk), 1024 threads. Thread t covers 4 dims (t % 8) of
+// the parts p = t/8 + 128k, keeping a running log-sum-exp (one batch of loads
+// in flight per thread); the 128 part groups are then merged through LDS by a
+// fixed-order tree, so results are run-to-run identical.
+constexpr int FOLD_THREADS = 1024;
 constexpr int FOLD_GROUPS = FOLD_THREADS / 8;
+
+__device__ inline void lse_merge(float& M, float& L, f4& A, float m2, float l2, f4 a2) {
+  if (m2 == NEG_INF) return;
+  if (M == NEG_INF) { M = m2; L = l2; A = a2; return; }
+  const float mx = fmaxf(M, m2);
+  const float c1 = __expf(M - mx), c2 = __expf(m2 - mx);
+  L = L * c1 + l2 * c2;
+  A = A * c1 + a2 * c2;
+  M = mx;
+}
 
 __global__ void __launch_bounds__(FOLD_THREADS) combine_kernel(int nparts, int D, const float* __restrict__ part_acc,
                                                                const float* __restrict__ part_ml,
                                                                float* __restrict__ out, float* __restrict__ lse) {
-  __shared__ float red[FOLD_THREADS * 5];
-  __shared__ float s_M;
+  __shared__ float sm[FOLD_THREADS], sl[FOLD_THREADS];
+  __shared__ f4 sa[FOLD_THREADS];
   const int row = blockIdx.x, tid = threadIdx.x;
   const float* ml = part_ml + (size_t)row * nparts * 2;
   const float* acc = part_acc + (size_t)row * nparts * D;
-
-  float M = NEG_INF;
-  for (int p = tid; p < nparts; p += FOLD_THREADS) {
-    const float m = ml[2 * p], l = ml[2 * p + 1];
-    if (l > 0.f) M = fmaxf(M, m);
-  }
-  red[tid] = M;
-  __syncthreads();
-  for (int s = FOLD_THREADS / 2; s > 0; s >>= 1) {
-    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
-    __syncthreads();
-  }
-  if (tid == 0) s_M = red[0];
-  __syncthreads();
-  M = s_M;
-  __syncthreads();
-
   const int dq = tid & 7, pg = tid >> 3;
   const int d0 = 32 * blockIdx.y + 4 * dq;
-  const bool vec = (D & 3) == 0;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, L = 0.f;
-  constexpr int BATCH = 8;  // parts whose loads are all issued before any is used
-  if (M != NEG_INF) {
-    for (int p0 = pg; p0 < nparts; p0 += FOLD_GROUPS * BATCH) {
-      float m[BATCH], l[BATCH];
-      f4 x[BATCH];
+  const bool vec = (D & 3) == 0 && d0 + 3 < D;
+  float M = NEG_INF, L = 0.f;
+  f4 A = {0.f, 0.f, 0.f, 0.f};
+  constexpr int BATCH = 4;
+  for (int p0 = pg; p0 < nparts; p0 += FOLD_GROUPS * BATCH) {
+    float m[BATCH], l[BATCH];
+    f4 x[BATCH];
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int p = p0 + u * FOLD_GROUPS;
-        const bool in = p < nparts;
-        m[u] = in ? ml[2 * p] : NEG_INF;
-        l[u] = in ? ml[2 * p + 1] : 0.f;
-        const float* ap = acc + (size_t)(in ? p : 0) * D + d0;
-        if (in && vec && d0 + 3 < D) {
-          x[u] = *reinterpret_cast<const f4*>(ap);
-        } else {
-          x[u] = f4{in && d0 + 0 < D ? ap[0] : 0.f, in && d0 + 1 < D ? ap[1] : 0.f,
-                    in && d0 + 2 < D ? ap[2] : 0.f, in && d0 + 3 < D ? ap[3] : 0.f};
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        if (l[u] > 0.f) {
-          const float w = __expf(m[u] - M);
-          L += w * l[u];
-          a0 += w * x[u][0]; a1 += w * x[u][1]; a2 += w * x[u][2]; a3 += w * x[u][3];
-        }
+    for (int u = 0; u < BATCH; ++u) {
+      const int p = p0 + u * FOLD_GROUPS;
+      const bool in = p < nparts;
+      m[u] = in ? ml[2 * p] : NEG_INF;
+      l[u] = in ? ml[2 * p + 1] : 0.f;
+      const float* ap = acc + (size_t)(in ? p : 0) * D + d0;
+      if (in && vec) {
+        x[u] = *reinterpret_cast<const f4*>(ap);
+      } else {
+        x[u] = f4{in && d0 + 0 < D ? ap[0] : 0.f, in && d0 + 1 < D ? ap[1] : 0.f,
+                  in && d0 + 2 < D ? ap[2] : 0.f, in && d0 + 3 < D ? ap[3] : 0.f};
       }
     }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u)
+      if (l[u] > 0.f) lse_merge(M, L, A, m[u], l[u], x[u]);
   }
-  red[tid * 4 + 0] = a0; red[tid * 4 + 1] = a1; red[tid * 4 + 2] = a2; red[tid * 4 + 3] = a3;
-  red[FOLD_THREADS * 4 + tid] = L;
+  sm[tid] = M; sl[tid] = L; sa[tid] = A;
   __syncthreads();
-  if (pg == 0) {
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f, Ls = 0.f;
-    for (int g = 0; g < FOLD_GROUPS; ++g) {
-      const int t = g * 8 + dq;
-      s0 += red[t * 4 + 0]; s1 += red[t * 4 + 1]; s2 += red[t * 4 + 2]; s3 += red[t * 4 + 3];
-      Ls += red[FOLD_THREADS * 4 + t];
+  for (int span = FOLD_GROUPS / 2; span > 0; span >>= 1) {
+    if (pg < span) {
+      const int o = tid + 8 * span;
+      float m1 = sm[tid], l1 = sl[tid];
+      f4 a1 = sa[tid];
+      lse_merge(m1, l1, a1, sm[o], sl[o], sa[o]);
+      sm[tid] = m1; sl[tid] = l1; sa[tid] = a1;
     }
-    const bool any = M != NEG_INF && Ls > 0.f;
+    __syncthreads();
+  }
+  if (pg == 0) {
+    const float Mf = sm[tid], Lf = sl[tid];
+    const f4 Af = sa[tid];
+    const bool any = Mf != NEG_INF && Lf > 0.f;
     float* o = out + (size_t)row * D + d0;
-    if (d0 + 0 < D) o[0] = any ? s0 / Ls : 0.f;
-    if (d0 + 1 < D) o[1] = any ? s1 / Ls : 0.f;
-    if (d0 + 2 < D) o[2] = any ? s2 / Ls : 0.f;
-    if (d0 + 3 < D) o[3] = any ? s3 / Ls : 0.f;
-    if (blockIdx.y == 0 && dq == 0) lse[row] = any ? M + logf(Ls) : NEG_INF;
+    if (d0 + 0 < D) o[0] = any ? Af[0] / Lf : 0.f;
+    if (d0 + 1 < D) o[1] = any ? Af[1] / Lf : 0.f;
+    if (d0 + 2 < D) o[2] = any ? Af[2] / Lf : 0.f;
+    if (d0 + 3 < D) o[3] = any ? Af[3] / Lf : 0.f;
+    if (blockIdx.y == 0 && dq == 0) lse[row] = any ? Mf + logf(Lf) : NEG_INF;
   }
 }
 
