@@ -248,8 +248,9 @@ def measured_traffic():
 
 def profile_pass(torch, pkv, synth):
     """Short run for rocprofv3: the 1M-token split-K kernel (partials only) ten
-    times over two pool copies, then a plain device copy of COPY_BYTES three
-    times, whose counters calibrate the per-dispatch byte counts."""
+    times over two pool copies, ten whole steps (split-K kernel + fold), then a
+    plain device copy of COPY_BYTES three times, whose counters calibrate the
+    per-dispatch byte counts."""
     from synth.device import to_device
     w = synth.config(5)
     dw = to_device(w)
@@ -260,13 +261,18 @@ def profile_pass(torch, pkv, synth):
     pml = torch.empty((w.rows, w.num_q_heads, n, 2), dtype=torch.float32, device="cuda")
     for i in range(10):
         pkv.decode_partials(p, *rot[i % len(rot)], part_acc=pacc, part_ml=pml)
+    out = torch.empty((w.rows, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.rows, w.num_q_heads), dtype=torch.float32, device="cuda")
+    ws = torch.empty(pkv.workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    for i in range(10):
+        pkv.decode_attention(p, *rot[i % len(rot)], out=out, lse=lse, workspace=ws)
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(3):
         torch.mul(src, 2.0, out=dst)
     torch.cuda.synchronize()
-    log(f"profile pass done: split-K x10 ({w.name}), elementwise copy of {COPY_BYTES} B x3; "
+    log(f"profile pass done: split-K x10 + whole step x10 ({w.name}), elementwise copy of {COPY_BYTES} B x3; "
         f"kernel source sha256 {kernel_source_sha256()}")
 
 

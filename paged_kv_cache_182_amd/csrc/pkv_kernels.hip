@@ -78,6 +78,10 @@ template <int CPOL = 0>
 __device__ inline u2 bload8(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, CPOL));
 }
+__device__ inline uint32_t bload4(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+constexpr uint32_t OFF_NONE = 0xFFFFFF00u;  // past any plane: reads zero, no traffic
 
 // Page descriptor staged in LDS (32 bytes).
 struct Desc {
@@ -99,16 +103,20 @@ struct Tile {
   static constexpr int SW = D / 16;        // words of 4 tokens x D/32 fp16 scales
   static constexpr bool KS = KC == C_ANY || is_int(KC);
   static constexpr bool VS = VC == C_ANY || is_int(VC);
+  static constexpr bool GS = KS || VS;     // some plane may carry group scales
   uint32_t k[KW];
   uint32_t v[VW];
-  uint32_t ks[KS ? SW : 1];
-  uint32_t vs[VS ? SW : 1];
+  // Group scales of the tile, one word per lane: the 16 tokens x D/32 fp16
+  // K scales in lanes 0 .. D/4-1 (sk), the V scales in lanes 32 .. 32+D/4-1
+  // (sv); zero elsewhere. Spread to the lanes that use them through LDS.
+  uint32_t sk[1];
+  uint32_t sv[1];
 };
 
 template <int D, int KC, int VC>
 __host__ __device__ constexpr int ring_depth() {
   using T = Tile<D, KC, VC>;
-  constexpr int words = T::KW + T::VW + (T::KS ? T::SW : 0) + (T::VS ? T::SW : 0);
+  constexpr int words = T::KW + T::VW + (T::KS ? 1 : 0) + (T::VS ? 1 : 0);
   constexpr int d = PKV_RING_WORDS / words;
   return d < 2 ? 2 : (d > 8 ? 8 : d);
 }
@@ -171,17 +179,6 @@ __device__ inline void load_run(uint32_t* w, rsrc_t r, uint32_t head, int sub, i
   }
 }
 
-// Group scales of 4 consecutive tokens, all D/32 groups (fp16, token-major).
-template <int D>
-__device__ inline void load_scales(uint32_t* w, rsrc_t r, uint32_t off) {
-  const u4 x = bload16(r, off);
-  w[0] = x[0]; w[1] = x[1]; w[2] = x[2]; w[3] = x[3];
-  if constexpr (D == 128) {
-    const u4 y = bload16(r, off + 16);
-    w[4] = y[0]; w[5] = y[1]; w[6] = y[2]; w[7] = y[3];
-  }
-}
-
 // ---------------------------------------------------------------- decode
 __device__ inline h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
 
@@ -207,12 +204,20 @@ __device__ inline h4 int8x4(uint32_t w) {
   return h4{a[0], a[1], b[0], b[1]};
 }
 
-// eight int4 codes of one word -> fp16 pairs (elements 0,1 | 2,3 | 4,5 | 6,7)
+// eight int4 codes of one word -> fp16 pairs (elements 0,1 | 2,3 | 4,5 | 6,7).
+// Element pair s sits in bits 4s..4s+3 of each 16-bit half. Masking a nibble
+// in place under the fp16 pattern of 1024 and flipping its top bit gives
+// 1024 + (c + 8) (bits 0..3) or 1024 + 16 (c + 8) (bits 4..7); one packed
+// subtract or fused multiply-add (1/16, -72) then yields c exactly.
 __device__ inline void int4x8(uint32_t w, h2* o) {
-  const uint32_t u = w ^ 0x88888888u;
   const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
-#pragma unroll
-  for (int s = 0; s < 4; ++s) o[s] = as_h2(((u >> (4 * s)) & 0x000f000fu) | 0x64006400u) - off;
+  const h2 s16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const h2 off16 = {(_Float16)72.0f, (_Float16)72.0f};
+  const uint32_t u8 = w >> 8;
+  o[0] = as_h2((w & 0x000f000fu) ^ 0x64086408u) - off;
+  o[1] = __builtin_elementwise_fma(as_h2((w & 0x00f000f0u) ^ 0x64806480u), s16, -off16);
+  o[2] = as_h2((u8 & 0x000f000fu) ^ 0x64086408u) - off;
+  o[3] = __builtin_elementwise_fma(as_h2((u8 & 0x00f000f0u) ^ 0x64806480u), s16, -off16);
 }
 
 // A operand of the score MFMA: dims 32c + 8kq .. +7 of the lane's token.
@@ -310,7 +315,19 @@ __device__ inline TileInfo issue_tile(Tile<D, KC, VC>& t, const Desc* desc, int 
   const int page = a.page;
   const rsrc_t rk = make_rsrc(a.pool + uni64(desc[i].k), live ? (uint32_t)plane_bytes(ti.kc, a.hkv, page, D) : 0u);
   const rsrc_t rv = make_rsrc(a.pool + uni64(desc[i].v), live ? (uint32_t)plane_bytes(ti.vc, a.hkv, page, D) : 0u);
-  const int kq = lane >> 4;
+  // group scales first: loads complete in order and the scores need them early
+  if constexpr (Tile<D, KC, VC>::GS) {
+    constexpr int NW = D / 4;  // words of one tile's scales (16 tokens x D/32 fp16)
+    const uint32_t blk = (uint32_t)((h * page + 16 * sub) * (D / 32) * 2);
+    if constexpr (Tile<D, KC, VC>::KS) {
+      const uint32_t base = (uint32_t)(a.hkv * page * D * bits_of(ti.kc) / 8) + blk;
+      t.sk[0] = bload4(rk, is_int(ti.kc) && lane < NW ? base + 4 * lane : OFF_NONE);
+    }
+    if constexpr (Tile<D, KC, VC>::VS) {
+      const uint32_t base = (uint32_t)(a.hkv * page * D * bits_of(ti.vc) / 8) + blk;
+      t.sv[0] = bload4(rv, is_int(ti.vc) && lane >= 32 && lane < 32 + NW ? base + 4 * (lane - 32) : OFF_NONE);
+    }
+  }
   if constexpr (KC == C_ANY) {
     switch (bits_of(ti.kc)) {
       case 16: load_run<D, 16>(t.k, rk, head_off<D>(C_FP16, h, page), sub, lane); break;
@@ -329,15 +346,6 @@ __device__ inline TileInfo issue_tile(Tile<D, KC, VC>& t, const Desc* desc, int 
   } else {
     load_run<D, bits_of(VC)>(t.v, rv, head_off<D>(VC, h, page), sub, lane);
   }
-  const uint32_t tok0 = (uint32_t)(h * page + 16 * sub + 4 * kq);
-  if constexpr (Tile<D, KC, VC>::KS) {
-    if (is_int(ti.kc))
-      load_scales<D>(t.ks, rk, (uint32_t)(a.hkv * page * D * bits_of(ti.kc) / 8) + tok0 * (D / 32) * 2);
-  }
-  if constexpr (Tile<D, KC, VC>::VS) {
-    if (is_int(ti.vc))
-      load_scales<D>(t.vs, rv, (uint32_t)(a.hkv * page * D * bits_of(ti.vc) / 8) + tok0 * (D / 32) * 2);
-  }
   return ti;
 }
 
@@ -348,44 +356,129 @@ __device__ inline f4 mfma16(h4 a, h4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
-// B operand of P.V for dim block n, with tail tokens zeroed (their codes may
-// be any bytes, even NaN, and 0 * NaN would poison the MFMA).
-template <int D, int VC, class T>
-__device__ inline h4 v_operand(const T& t, const TileInfo& ti, int n, int kq, bool partial) {
-  h4 vf = VC == C_ANY ? v_frag_any<D>(t.v, n, ti.vc) : v_frag<VC == C_ANY ? 0 : VC, D>(t.v, n);
-  if (partial) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) vf[j] = (4 * kq + j < ti.valid) ? vf[j] : (_Float16)0.0f;
+// Max and sum over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows
+// that hold one column), with the row-swapping permutes of gfx950: swapping
+// the odd rows of one copy with the even rows of another (16-lane rows, then
+// 32-lane halves) leaves each lane its own value in one result and its
+// partner row's value in the other. The two results are read straight from
+// the builtin's vector and pass through an empty asm: reading them through a
+// bit cast of the pair has been seen to let the optimizer merge them.
+template <int ROWS>
+__device__ inline void swap_rows(float x, float& a, float& b) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  uint32_t lo, hi;
+  if constexpr (ROWS == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    lo = r[0]; hi = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = r[0]; hi = r[1];
   }
-  return vf;
+  asm volatile("" : "+v"(lo), "+v"(hi));
+  a = __builtin_bit_cast(float, lo);
+  b = __builtin_bit_cast(float, hi);
+}
+__device__ inline float row4_max(float x) {
+  float a, b;
+  swap_rows<16>(x, a, b);
+  swap_rows<32>(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ inline float row4_sum(float x) {
+  float a, b;
+  swap_rows<16>(x, a, b);
+  swap_rows<32>(a + b, a, b);
+  return a + b;
 }
 
-// Scores, online-softmax update and P.V of one staged tile.
+// Zero the V codes of this lane's tokens 4*kq + j, j >= nv (past the end of
+// the sequence): their bytes may be anything, even NaN codes, and 0 * NaN
+// would poison the MFMA. A zero code decodes to 0 in every codec. Word n of
+// an 8-bit run holds tokens j in bytes j; 16-bit runs hold tokens 0,1 in even
+// and 2,3 in odd words; an int4 word holds token j in the nibbles below.
+__device__ inline void mask_v_run(uint32_t* v, int words, int bits, int nv) {
+  if (bits == 8) {
+    const uint32_t m = nv >= 4 ? ~0u : (1u << (8 * nv)) - 1u;
+    for (int i = 0; i < words; ++i) v[i] &= m;
+  } else if (bits == 16) {
+    const uint32_t m0 = nv >= 2 ? ~0u : (nv == 1 ? 0x0000ffffu : 0u);
+    const uint32_t m1 = nv >= 4 ? ~0u : (nv == 3 ? 0x0000ffffu : 0u);
+    for (int i = 0; i < words; ++i) v[i] &= (i & 1) ? m1 : m0;
+  } else {
+    const uint32_t m = (nv > 0 ? 0x00000f0fu : 0u) | (nv > 1 ? 0x0f0f0000u : 0u) |
+                       (nv > 2 ? 0x0000f0f0u : 0u) | (nv > 3 ? 0xf0f00000u : 0u);
+    for (int i = 0; i < words; ++i) v[i] &= m;
+  }
+}
+
+// Scores, online-softmax update and P.V of one staged tile with ti.valid > 0
+// tokens. `sc` is this wave's 64-word LDS slot for the group scales (null
+// when no plane has them).
 template <int D, int KC, int VC>
 __device__ inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti, const h8* qv,
                                     const h8* qg, float scale_log2, float& m_run, float& l_run, f4* acc,
-                                    int lane) {
+                                    uint32_t* sc, int lane) {
   constexpr int NC = D / 32, NB = D / 16;
-  if (ti.valid == 0) return;
+  using T = Tile<D, KC, VC>;
   const int kq = lane >> 4;
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
+  const bool partial = ti.valid < 16;  // wave-uniform
+  const int vc = VC == C_ANY ? ti.vc : VC;
+
+  uint32_t vw[T::VW];
+#pragma unroll
+  for (int i = 0; i < T::VW; ++i) vw[i] = t.v[i];
+  if (partial) {
+    const int nv = min(max(ti.valid - 4 * kq, 0), 4);
+    constexpr int VWORDS = VC == C_ANY ? T::VW : D * bits_of(VC) / 128;
+    mask_v_run(vw, VWORDS, VC == C_ANY ? bits_of(vc) : bits_of(VC), nv);
+  }
+
+  // group scales of this lane's four tokens (4 x NC fp16 each for K and V);
+  // the words of tokens past the end are written as zero
+  uint32_t ks[T::KS ? NC * 2 : 1], vs[T::VS ? NC * 2 : 1];
+  if constexpr (T::GS) {
+    const int w = lane & 31;
+    const uint32_t word = (T::KS ? t.sk[0] : 0u) | (T::VS ? t.sv[0] : 0u);
+    __builtin_amdgcn_wave_barrier();
+    sc[lane] = (2 * w) / NC < ti.valid ? word : 0u;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if constexpr (T::KS) {
+#pragma unroll
+      for (int i = 0; i < NC * 2; i += 4) {
+        const u4 x = *reinterpret_cast<const u4*>(sc + 2 * NC * kq + i);
+        ks[i] = x[0]; ks[i + 1] = x[1]; ks[i + 2] = x[2]; ks[i + 3] = x[3];
+      }
+    }
+    if constexpr (T::VS) {
+#pragma unroll
+      for (int i = 0; i < NC * 2; i += 4) {
+        const u4 x = *reinterpret_cast<const u4*>(sc + 32 + 2 * NC * kq + i);
+        vs[i] = x[0]; vs[i + 1] = x[1]; vs[i + 2] = x[2]; vs[i + 3] = x[3];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+
   float s[4];
   const bool kgrouped = KC == C_ANY ? is_int(ti.kc) : is_int(KC);
   if (KC == C_ANY || is_int(KC)) {
     // one accumulator per 32-dim group, scaled per (token, group)
-    f4 sc[NC];
+    f4 scg[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       h8 kf = KC == C_ANY ? k_frag_any<D>(t.k, c, ti.kc) : k_frag<KC == C_ANY ? 0 : KC, D>(t.k, c);
-      sc[c] = mfma32(kf, (KC == C_ANY && kgrouped) ? qg[c] : qv[c], zero);
+      scg[c] = mfma32(kf, (KC == C_ANY && kgrouped) ? qg[c] : qv[c], zero);
     }
     if (kgrouped) {
-      const _Float16* ks = reinterpret_cast<const _Float16*>(t.ks);
+      const _Float16* k16 = reinterpret_cast<const _Float16*>(ks);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float x = 0.f;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) x += (float)ks[j * NC + c] * sc[c][j];
+        for (int c = 0; c < NC; ++c) x += (float)k16[j * NC + c] * scg[c][j];
         s[j] = x * scale_log2;
       }
     } else {
@@ -394,28 +487,25 @@ __device__ inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti
       for (int j = 0; j < 4; ++j) {
         float x = 0.f;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) x += sc[c][j];
+        for (int c = 0; c < NC; ++c) x += scg[c][j];
         s[j] = x * f;
       }
     }
   } else {
-    f4 sc = zero;
+    f4 acc_s = zero;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) sc = mfma32(k_frag<KC, D>(t.k, c), qv[c], sc);
+    for (int c = 0; c < NC; ++c) acc_s = mfma32(k_frag<KC, D>(t.k, c), qv[c], acc_s);
     const float f = scale_log2 * ti.sk;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s[j] = sc[j] * f;
+    for (int j = 0; j < 4; ++j) s[j] = acc_s[j] * f;
   }
-  const bool partial = ti.valid < 16;
   if (partial) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) s[j] = (4 * kq + j < ti.valid) ? s[j] : NEG_INF;
   }
 
   // online softmax over this tile's 16 tokens (lanes col, col+16, col+32, col+48)
-  float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mx = row4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
   const float m_new = fmaxf(m_run, mx);
   if (__any(m_new > m_run)) {
     const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
@@ -437,19 +527,20 @@ __device__ inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti
   // P.V. The weights go to the MFMA in fp16; where a V scale multiplies them
   // it is applied so that a weight of exactly 1 stays exact: INT group scales
   // are fp16 already, the fp32 FP8 page scale is split into an fp16 high and
-  // low part (two MFMAs, 22 significant bits). Tail tokens get weight 0 by
-  // selection, never by multiplying a possibly non-finite scale.
-  const int vc = VC == C_ANY ? ti.vc : VC;
-  auto keep = [&](int j) { return !partial || 4 * kq + j < ti.valid; };
+  // low part (two MFMAs, 22 significant bits). Tail tokens have weight 0,
+  // zero V codes and zero scales, so nothing non-finite reaches the MFMA.
+  auto vfrag = [&](int n) {
+    return VC == C_ANY ? v_frag_any<D>(vw, n, ti.vc) : v_frag<VC == C_ANY ? 0 : VC, D>(vw, n);
+  };
   if (is_int(vc)) {
-    const _Float16* vs = reinterpret_cast<const _Float16*>(t.vs);
+    const _Float16* v16 = reinterpret_cast<const _Float16*>(vs);
     h4 pa[NC];
 #pragma unroll
     for (int g = 0; g < NC; ++g)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pa[g][j] = keep(j) ? (_Float16)(p[j] * (float)vs[j * NC + g]) : (_Float16)0.0f;
+      for (int j = 0; j < 4; ++j) pa[g][j] = (_Float16)__builtin_fmaf(p[j], (float)v16[j * NC + g], 0.0f);
 #pragma unroll
-    for (int n = 0; n < NB; ++n) acc[n] = mfma16(pa[n / 2], v_operand<D, VC>(t, ti, n, kq, partial), acc[n]);
+    for (int n = 0; n < NB; ++n) acc[n] = mfma16(pa[n / 2], vfrag(n), acc[n]);
   } else if (vc == C_FP8) {
     h4 hi, lo;
 #pragma unroll
@@ -460,14 +551,14 @@ __device__ inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti
     }
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      const h4 vf = v_operand<D, VC>(t, ti, n, kq, partial);
+      const h4 vf = vfrag(n);
       acc[n] = mfma16(hi, vf, acc[n]);
       acc[n] = mfma16(lo, vf, acc[n]);
     }
   } else {
     const h4 pa = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
 #pragma unroll
-    for (int n = 0; n < NB; ++n) acc[n] = mfma16(pa, v_operand<D, VC>(t, ti, n, kq, partial), acc[n]);
+    for (int n = 0; n < NB; ++n) acc[n] = mfma16(pa, vfrag(n), acc[n]);
   }
 }
 
@@ -477,11 +568,13 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
   constexpr int RED_BYTES = (WAVES * 16 * D + 2 * WAVES * 16) * 4;
   constexpr int DESC_BYTES = MAX_DESC * (int)sizeof(Desc);
   __shared__ __attribute__((aligned(16))) unsigned char smem[RED_BYTES > DESC_BYTES ? RED_BYTES : DESC_BYTES];
+  __shared__ __attribute__((aligned(16))) uint32_t scale_slots[Tile<D, KC, VC>::GS ? WAVES * 64 : 4];
   Desc* desc = reinterpret_cast<Desc*>(smem);
 
   const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loop control scalar
+  uint32_t* const sc = Tile<D, KC, VC>::GS ? scale_slots + 64 * wave : nullptr;
   const int col = lane & 15, kq = lane >> 4;
   const int G = a.group;
   const int P = a.page;
@@ -598,15 +691,15 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
           const int nx = (s + DEPTH - 1) % DEPTH;
           // past the end: same loads through a zero-size resource (no traffic)
           inf[nx] = issue_tile<D, KC, VC>(t[nx], desc, min(kn, klast), tpp, a, h, lane, kn > klast);
-          if (it + s < nmine) consume_tile<D, KC, VC>(t[s], inf[s], qv, qg, a.scale_log2, m_run, l_run, acc, lane);
+          if (it + s < nmine && inf[s].valid > 0)
+            consume_tile<D, KC, VC>(t[s], inf[s], qv, qg, a.scale_log2, m_run, l_run, acc, sc, lane);
         }
       }
     }
   }
 
   // ---- merge the four waves' (m, l, acc) through LDS
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = row4_sum(l_run);
   __syncthreads();
   float* red_acc = reinterpret_cast<float*>(smem);
   float* red_m = red_acc + WAVES * 16 * D;
