@@ -82,6 +82,7 @@ __device__ inline uint32_t bload4(rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
 constexpr uint32_t OFF_NONE = 0xFFFFFF00u;  // past any plane: reads zero, no traffic
+constexpr int VMCNT0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt left free (gfx9 encoding)
 
 // Page descriptor staged in LDS (32 bytes).
 struct Desc {
@@ -141,6 +142,15 @@ struct TileInfo {
 
 __device__ inline void count_error(int32_t* err) {
   if (err) atomicAdd(err, 1);
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS
+// accesses, not for its global loads in flight (q, tiles), which
+// __syncthreads would also drain.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -594,9 +604,62 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
     npg = min(n, a.max_pages);
   }
   npg = __builtin_amdgcn_readfirstlane(npg);
-  if (bad_row && part == 0 && h == 0 && tid == 0) count_error(a.err);
   const int s0 = part * a.pages_per_part;
   const int s1 = min(s0 + a.pages_per_part, npg);
+
+  // ---- page descriptors of this partition, MAX_DESC at a time. Entries run
+  // as far as the tables go; the row length (s1) may cut them shorter. The
+  // first chunk is gathered before the row length is known and before q is
+  // read: its table reads go out at once, and every read of a chunk is issued
+  // before any result is checked, so the gather costs two dependent rounds
+  // (three with a selection).
+  const int s_lim = min(s0 + a.pages_per_part, a.sparse ? a.max_sel : a.max_pages);
+  auto stage = [&](int cbase, int chunk) {
+    if (tid < chunk) {
+      const int s = cbase + tid;
+      // reads (indices clamped into their tables; results checked below)
+      const int lp = a.sparse ? a.sel[(size_t)b * a.max_sel + s] : s;
+      const bool lp_ok = (unsigned)lp < (unsigned)a.max_pages;
+      const int pp = a.bt[(size_t)b * a.max_pages + (lp_ok ? lp : 0)];
+      const bool pp_ok = lp_ok && (unsigned)pp < (unsigned)a.num_pages;
+      const int pq = pp_ok ? pp : 0;
+      const int cod = a.codec[pq];
+      const uint64_t ko = a.koff[pq];
+      const uint64_t vo = a.voff[pq];
+      float sk = 1.f, sv = 1.f;
+      if (a.scale != nullptr) {
+        sk = a.scale[((size_t)pq * a.hkv + h) * 2 + 0];
+        sv = a.scale[((size_t)pq * a.hkv + h) * 2 + 1];
+      }
+      // checks
+      const int kc = cod & 15, vc = cod >> 4;
+      bool ok = pp_ok && kc <= C_INT4 && vc <= C_INT4;
+      if (KC != C_ANY && kc != KC) ok = false;
+      if (VC != C_ANY && vc != VC) ok = false;
+      if ((kc == C_FP8 || vc == C_FP8) && a.scale == nullptr) ok = false;
+      if ((ko | vo) & 15) ok = false;
+      if (ok && (ko > a.pool_bytes || a.pool_bytes - ko < plane_bytes(kc, a.hkv, P, D))) ok = false;
+      if (ok && (vo > a.pool_bytes || a.pool_bytes - vo < plane_bytes(vc, a.hkv, P, D))) ok = false;
+      const bool live = s < s1;  // inside the row: a bad entry here is an input error
+      Desc d;
+      d.k = 0; d.v = 0; d.sk = 1.f; d.sv = 1.f; d.valid = 0; d.codec = 0;
+      if (ok && live) {
+        const long long rem = (long long)L - (long long)lp * P;
+        d.valid = (int)(rem < 0 ? 0 : (rem > P ? P : rem));
+        d.k = ko;
+        d.v = vo;
+        if (kc == C_FP8) d.sk = sk;
+        if (vc == C_FP8) d.sv = sv;
+        d.codec = cod;
+      } else if (live && h == 0) {
+        count_error(a.err);
+      }
+      desc[tid] = d;
+    }
+  };
+  int cbase = s0;
+  int chunk = min(MAX_DESC, s_lim - cbase);
+  if (chunk > 0) stage(cbase, chunk);
 
   // ---- q of this KV head's query group (B operand of the score MFMA), in
   // the dim order of the K runs: qv for one-scale codecs (and the per-page
@@ -621,53 +684,9 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
   for (int n = 0; n < NB; ++n) acc[n] = f4{0.f, 0.f, 0.f, 0.f};
 
   const int tpp = P / 16;
-  for (int cbase = s0; cbase < s1; cbase += MAX_DESC) {
-    const int cn = min(MAX_DESC, s1 - cbase);
-    __syncthreads();
-    if (tid < cn) {
-      const int s = cbase + tid;
-      Desc d;
-      d.k = 0; d.v = 0; d.sk = 1.f; d.sv = 1.f; d.valid = 0; d.codec = 0;
-      bool ok = true;
-      const int lp = a.sparse ? a.sel[(size_t)b * a.max_sel + s] : s;
-      if ((unsigned)lp >= (unsigned)a.max_pages) ok = false;
-      int pp = -1;
-      if (ok) {
-        pp = a.bt[(size_t)b * a.max_pages + lp];
-        if ((unsigned)pp >= (unsigned)a.num_pages) ok = false;
-      }
-      int kc = 0, vc = 0, cod = 0;
-      if (ok) {
-        cod = a.codec[pp];
-        kc = cod & 15;
-        vc = cod >> 4;
-        if (kc > C_INT4 || vc > C_INT4) ok = false;
-        if (KC != C_ANY && kc != KC) ok = false;
-        if (VC != C_ANY && vc != VC) ok = false;
-        if ((kc == C_FP8 || vc == C_FP8) && a.scale == nullptr) ok = false;
-      }
-      uint64_t ko = 0, vo = 0;
-      if (ok) {
-        ko = a.koff[pp];
-        vo = a.voff[pp];
-        if ((ko | vo) & 15) ok = false;
-        if (ko > a.pool_bytes || a.pool_bytes - ko < plane_bytes(kc, a.hkv, P, D)) ok = false;
-        if (vo > a.pool_bytes || a.pool_bytes - vo < plane_bytes(vc, a.hkv, P, D)) ok = false;
-      }
-      if (ok) {
-        const long long rem = (long long)L - (long long)lp * P;
-        d.valid = (int)(rem < 0 ? 0 : (rem > P ? P : rem));
-        d.k = ko;
-        d.v = vo;
-        if (kc == C_FP8) d.sk = a.scale[((size_t)pp * a.hkv + h) * 2 + 0];
-        if (vc == C_FP8) d.sv = a.scale[((size_t)pp * a.hkv + h) * 2 + 1];
-        d.codec = cod;
-      } else if (h == 0) {
-        count_error(a.err);
-      }
-      desc[tid] = d;
-    }
-    __syncthreads();
+  while (chunk > 0) {
+    lds_barrier();
+    const int cn = max(0, min(chunk, s1 - cbase));
 
     // Ring of DEPTH tiles: while the oldest is consumed, the loads of the
     // next DEPTH-1 are in flight. Issues are unconditional (past the end the
@@ -696,11 +715,25 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
         }
       }
     }
+    // Drain the ring's discarded loads (zero-size reads, no traffic): with
+    // nothing in flight across the loop edge, the wait counts at the top of
+    // the loop only cover q, not the tile registers.
+    __builtin_amdgcn_s_waitcnt(VMCNT0);
+    if (cbase + chunk >= s1) break;  // the row ends inside this chunk
+    cbase += MAX_DESC;
+    chunk = min(MAX_DESC, s_lim - cbase);
+    if (chunk <= 0) break;
+    lds_barrier();  // every wave is done with the previous chunk
+    stage(cbase, chunk);
   }
+
+  // reported here, not where found, so that no wait on the row length sits
+  // in front of the table reads
+  if (bad_row && part == 0 && h == 0 && tid == 0) count_error(a.err);
 
   // ---- merge the four waves' (m, l, acc) through LDS
   l_run = row4_sum(l_run);
-  __syncthreads();
+  lds_barrier();
   float* red_acc = reinterpret_cast<float*>(smem);
   float* red_m = red_acc + WAVES * 16 * D;
   float* red_l = red_m + WAVES * 16;
@@ -712,7 +745,7 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
   for (int n = 0; n < NB; ++n)
 #pragma unroll
     for (int j = 0; j < 4; ++j) red_acc[(wave * 16 + 4 * kq + j) * D + 16 * n + col] = acc[n][j];
-  __syncthreads();
+  lds_barrier();
 
   for (int idx = tid; idx < G * D; idx += THREADS) {
     const int g = idx / D, d = idx - g * D;
@@ -747,16 +780,14 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
 }
 
 // ---------------------------------------------------------------- fold
-// Grid (row, 32-dim chunk), 1024 threads. Thread t covers 4 dims (t % 8) of
-// the parts p = t/8 + 128k, keeping a running log-sum-exp (one batch of loads
-// in flight per thread); the 128 part groups are then merged through LDS by a
-// fixed-order tree, so results are run-to-run identical.
-constexpr int FOLD_THREADS = 1024;
-constexpr int FOLD_GROUPS = FOLD_THREADS / 8;
-
+// Grid (row, 4-dim group), one wave each: spread over the whole chip, one
+// round of loads, no LDS. Lane l keeps a running log-sum-exp over the parts
+// p = l + 64k (every load of a batch in flight together); the 64 lanes then
+// merge by a fixed butterfly (lane distance 32, 16, ..., 1), so results are
+// run-to-run identical.
 __device__ inline void lse_merge(float& M, float& L, f4& A, float m2, float l2, f4 a2) {
-  if (m2 == NEG_INF) return;
-  if (M == NEG_INF) { M = m2; L = l2; A = a2; return; }
+  if (!(l2 > 0.f)) return;
+  if (!(L > 0.f)) { M = m2; L = l2; A = a2; return; }
   const float mx = fmaxf(M, m2);
   const float c1 = __expf(M - mx), c2 = __expf(m2 - mx);
   L = L * c1 + l2 * c2;
@@ -764,30 +795,27 @@ __device__ inline void lse_merge(float& M, float& L, f4& A, float m2, float l2, 
   M = mx;
 }
 
-__global__ void __launch_bounds__(FOLD_THREADS) combine_kernel(int nparts, int D, const float* __restrict__ part_acc,
-                                                               const float* __restrict__ part_ml,
-                                                               float* __restrict__ out, float* __restrict__ lse) {
-  __shared__ float sm[FOLD_THREADS], sl[FOLD_THREADS];
-  __shared__ f4 sa[FOLD_THREADS];
-  const int row = blockIdx.x, tid = threadIdx.x;
+// `vec`: D % 4 == 0 and part_acc 16-byte aligned, so 4 dims load as one vector.
+__global__ void __launch_bounds__(64) combine_kernel(int nparts, int D, int vec, const float* __restrict__ part_acc,
+                                                     const float* __restrict__ part_ml, float* __restrict__ out,
+                                                     float* __restrict__ lse) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  const int d0 = 4 * blockIdx.y;
   const float* ml = part_ml + (size_t)row * nparts * 2;
-  const float* acc = part_acc + (size_t)row * nparts * D;
-  const int dq = tid & 7, pg = tid >> 3;
-  const int d0 = 32 * blockIdx.y + 4 * dq;
-  const bool vec = (D & 3) == 0 && d0 + 3 < D;
+  const float* acc = part_acc + (size_t)row * nparts * D + d0;
   float M = NEG_INF, L = 0.f;
   f4 A = {0.f, 0.f, 0.f, 0.f};
-  constexpr int BATCH = 4;
-  for (int p0 = pg; p0 < nparts; p0 += FOLD_GROUPS * BATCH) {
+  constexpr int BATCH = 8;
+  for (int p0 = lane; p0 < nparts; p0 += 64 * BATCH) {
     float m[BATCH], l[BATCH];
     f4 x[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      const int p = p0 + u * FOLD_GROUPS;
+      const int p = p0 + 64 * u;
       const bool in = p < nparts;
-      m[u] = in ? ml[2 * p] : NEG_INF;
-      l[u] = in ? ml[2 * p + 1] : 0.f;
-      const float* ap = acc + (size_t)(in ? p : 0) * D + d0;
+      m[u] = in ? ml[2 * (size_t)p] : NEG_INF;
+      l[u] = in ? ml[2 * (size_t)p + 1] : 0.f;
+      const float* ap = acc + (size_t)(in ? p : 0) * D;
       if (in && vec) {
         x[u] = *reinterpret_cast<const f4*>(ap);
       } else {
@@ -796,31 +824,21 @@ __global__ void __launch_bounds__(FOLD_THREADS) combine_kernel(int nparts, int D
       }
     }
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u)
-      if (l[u] > 0.f) lse_merge(M, L, A, m[u], l[u], x[u]);
+    for (int u = 0; u < BATCH; ++u) lse_merge(M, L, A, m[u], l[u], x[u]);
   }
-  sm[tid] = M; sl[tid] = L; sa[tid] = A;
-  __syncthreads();
-  for (int span = FOLD_GROUPS / 2; span > 0; span >>= 1) {
-    if (pg < span) {
-      const int o = tid + 8 * span;
-      float m1 = sm[tid], l1 = sl[tid];
-      f4 a1 = sa[tid];
-      lse_merge(m1, l1, a1, sm[o], sl[o], sa[o]);
-      sm[tid] = m1; sl[tid] = l1; sa[tid] = a1;
-    }
-    __syncthreads();
+#pragma unroll
+  for (int dist = 32; dist >= 1; dist >>= 1) {
+    const float m2 = __shfl_xor(M, dist), l2 = __shfl_xor(L, dist);
+    const f4 a2 = {__shfl_xor(A[0], dist), __shfl_xor(A[1], dist), __shfl_xor(A[2], dist), __shfl_xor(A[3], dist)};
+    lse_merge(M, L, A, m2, l2, a2);
   }
-  if (pg == 0) {
-    const float Mf = sm[tid], Lf = sl[tid];
-    const f4 Af = sa[tid];
-    const bool any = Mf != NEG_INF && Lf > 0.f;
+  if (lane == 0) {
+    const bool any = L > 0.f;
     float* o = out + (size_t)row * D + d0;
-    if (d0 + 0 < D) o[0] = any ? Af[0] / Lf : 0.f;
-    if (d0 + 1 < D) o[1] = any ? Af[1] / Lf : 0.f;
-    if (d0 + 2 < D) o[2] = any ? Af[2] / Lf : 0.f;
-    if (d0 + 3 < D) o[3] = any ? Af[3] / Lf : 0.f;
-    if (blockIdx.y == 0 && dq == 0) lse[row] = any ? Mf + logf(Lf) : NEG_INF;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (d0 + j < D) o[j] = any ? A[j] / L : 0.f;
+    if (blockIdx.y == 0) lse[row] = any ? M + logf(L) : NEG_INF;
   }
 }
 
@@ -910,8 +928,9 @@ int launch_combine(int rows, int nparts, int head_dim, const float* part_acc, co
     hipLaunchKernelGGL(combine_small_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, rows,
                        nparts, head_dim, part_acc, part_ml, out, lse);
   } else {
-    hipLaunchKernelGGL(combine_kernel, dim3(rows, (head_dim + 31) / 32), dim3(FOLD_THREADS), 0, s, nparts,
-                       head_dim, part_acc, part_ml, out, lse);
+    const int vec = (head_dim % 4 == 0) && (reinterpret_cast<uintptr_t>(part_acc) % 16 == 0);
+    hipLaunchKernelGGL(combine_kernel, dim3(rows, (head_dim + 3) / 4), dim3(64), 0, s, nparts, head_dim, vec,
+                       part_acc, part_ml, out, lse);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

@@ -225,9 +225,14 @@ def test_decode_partials_match_oracle_partials():
             assert np.max(np.abs(np.log(gl[ok]) - np.log(ol[ok])), initial=0) <= 1e-4
 
 
-@pytest.mark.parametrize("rows,parts,dim", [(5, 1, 128), (16, 512, 128), (7, 33, 64), (3, 9, 30), (2, 4, 512)])
-def test_lse_combine_matches_oracle_fold(rows, parts, dim):
-    print(f"case fold {rows} {parts} {dim}", flush=True)
+@pytest.mark.parametrize("rows,parts,dim,shift", [
+    (5, 1, 128, 0), (16, 512, 128, 0), (7, 33, 64, 0), (3, 9, 30, 0), (2, 4, 512, 0),
+    (3, 130, 30, 0),      # many parts, head_dim not a multiple of 4
+    (4, 200, 128, 1),     # part_acc only 4-byte aligned (one float into its buffer)
+    (2, 1000, 64, 3),
+])
+def test_lse_combine_matches_oracle_fold(rows, parts, dim, shift):
+    print(f"case fold {rows} {parts} {dim} shift {shift}", flush=True)
     rng = np.random.default_rng(rows * 1000 + parts)
     m = (3 * rng.standard_normal((rows, parts))).astype(np.float32)
     l = rng.uniform(0.5, 50, (rows, parts)).astype(np.float32)
@@ -237,7 +242,10 @@ def test_lse_combine_matches_oracle_fold(rows, parts, dim):
     if rows > 2:
         m[1], l[1], acc[1] = -np.inf, 0, 0                  # a row with no tokens at all
     ml = np.stack([m, l], axis=-1)
-    out, lse = pkv.lse_combine(torch.from_numpy(acc).cuda(), torch.from_numpy(ml).cuda())
+    buf = torch.zeros(acc.size + shift, dtype=torch.float32, device="cuda")
+    acc_t = buf[shift:].view(rows, parts, dim)
+    acc_t.copy_(torch.from_numpy(acc))
+    out, lse = pkv.lse_combine(acc_t, torch.from_numpy(ml).cuda())
     torch.cuda.synchronize()
     ref_out, ref_lse = oracle.fold(acc.astype(np.float64), m.astype(np.float64), l.astype(np.float64))
     out, lse = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
