@@ -795,6 +795,18 @@ __device__ inline void lse_merge(float& M, float& L, f4& A, float m2, float l2, 
   M = mx;
 }
 
+template <int CTRL>
+__device__ inline float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// Merge this lane's (M, L, A) with its partner's under the lane map `partner`.
+template <class F>
+__device__ inline void fold_step(float& M, float& L, f4& A, F partner) {
+  const float m2 = partner(M), l2 = partner(L);
+  const f4 a2 = {partner(A[0]), partner(A[1]), partner(A[2]), partner(A[3])};
+  lse_merge(M, L, A, m2, l2, a2);
+}
+
 // `vec`: D % 4 == 0 and part_acc 16-byte aligned, so 4 dims load as one vector.
 __global__ void __launch_bounds__(64) combine_kernel(int nparts, int D, int vec, const float* __restrict__ part_acc,
                                                      const float* __restrict__ part_ml, float* __restrict__ out,
@@ -826,12 +838,16 @@ __global__ void __launch_bounds__(64) combine_kernel(int nparts, int D, int vec,
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) lse_merge(M, L, A, m[u], l[u], x[u]);
   }
-#pragma unroll
-  for (int dist = 32; dist >= 1; dist >>= 1) {
-    const float m2 = __shfl_xor(M, dist), l2 = __shfl_xor(L, dist);
-    const f4 a2 = {__shfl_xor(A[0], dist), __shfl_xor(A[1], dist), __shfl_xor(A[2], dist), __shfl_xor(A[3], dist)};
-    lse_merge(M, L, A, m2, l2, a2);
-  }
+  // butterfly: lane pairs inside quads (DPP quad permutes), across quads and
+  // half-rows (DPP mirrors), then across 16-lane rows and 32-lane halves
+  // (row swaps). Every step is an involution, so after six steps every lane
+  // holds the merge of all 64.
+  fold_step(M, L, A, [](float x) { return dpp_f<0xB1>(x); });   // quad_perm [1,0,3,2]
+  fold_step(M, L, A, [](float x) { return dpp_f<0x4E>(x); });   // quad_perm [2,3,0,1]
+  fold_step(M, L, A, [](float x) { return dpp_f<0x141>(x); });  // row_half_mirror
+  fold_step(M, L, A, [](float x) { return dpp_f<0x140>(x); });  // row_mirror
+  fold_step(M, L, A, [lane](float x) { float a, b; swap_rows<16>(x, a, b); return (lane & 16) ? a : b; });
+  fold_step(M, L, A, [lane](float x) { float a, b; swap_rows<32>(x, a, b); return (lane & 32) ? a : b; });
   if (lane == 0) {
     const bool any = L > 0.f;
     float* o = out + (size_t)row * D + d0;
