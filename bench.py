@@ -7,17 +7,24 @@ every stage of the path (selection/block-table gather, codec decode, scores,
 online softmax, P.V, partition partials, log-sum-exp fold). The headline
 workload is the 1M-token split-K FP8 decode (batch 1, 16 query / 2 KV heads,
 head_dim 128, 64-token pages, 512 partitions). The 32K batched INT8-K/INT4-V
-workload and the sparse 48-row FP8 selection are timed the same way and
-reported beside it.
+workload, the sparse 48-row FP8 selection and the 24-layer mixed FP16/FP8
+workload are timed the same way and reported beside it.
 
 Inputs are resident in HBM before timing. Each step reads a different copy
 of the pool (or, for the sparse workload, a different placement of its
 pages), so that the working set of consecutive steps exceeds the 256 MB
 last-level cache and the bytes really come from HBM.
 
-The value is effective KV bytes (codes + scales of attended tokens) divided
-by the step time. roofline.achieved uses the split-K kernel alone, timed with
-HIP events around each launch on the stream it runs on.
+After the warm-up, K steps are timed between two synchronised HIP events,
+seven times over; the step time is the median of the seven blocks (the first
+block and all seven are in `detail`). The value is effective KV bytes (codes
++ scales of attended tokens) divided by that step time; `total_bytes` beside
+it counts q, outputs, tables and partials too. roofline.achieved uses the
+split-K kernel alone, timed with HIP events around each launch on the stream
+it runs on. The 24-layer workload is also timed as a model calls it, one
+launch per layer, the 24 launches captured in a HIP graph. The read probes
+(libpkv_probe.so: a linear stream and random 2 KB chunks) give the measured
+ceiling on the same device.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -35,6 +42,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_182_amd", "csrc", "pkv_kernels.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "splitk_fp8_1m_traffic.md")
+PROBE_LIB = os.path.join(ROOT, "paged_kv_cache_182_amd", "libpkv_probe.so")
 COPY_BYTES = 256 << 20
 METRIC = "effective KV-read GB/s (% of HBM peak) + decode-attn steps/s at 32K and 1M ctx"
 
@@ -98,6 +106,19 @@ def rotations(torch, dw, min_bytes):
     return out, f"{n} page placements"
 
 
+def total_bytes(w, nparts, eff):
+    """Every byte a step moves, beside the effective KV bytes: q, out, lse, the
+    row lengths, the tables of the attended pages (block table, selection,
+    plane offsets, codec, the per-head FP8 scale pair) and, with several
+    partitions, the partials written by the split-K kernel and read by the fold."""
+    rows, hq, hkv, d = w.rows, w.num_q_heads, w.num_kv_heads, w.head_dim
+    pages = sum(len(pg) for pg in w.attended_pages())
+    tables = pages * (4 + (4 if w.sparse else 0) + 8 + 8 + 1 + 8 * hkv)
+    io = rows * hq * d * 2 + rows * hq * d * 4 + rows * hq * 4 + rows * 4 * (2 if w.sparse else 1)
+    partials = 2 * rows * hq * nparts * (d + 2) * 4 if nparts > 1 else 0
+    return int(eff + tables + io + partials)
+
+
 def time_workload(torch, pkv, w, steps, warmup, min_rot_bytes):
     import numpy as np
     from synth import effective_kv_bytes_formula
@@ -139,7 +160,18 @@ def time_workload(torch, pkv, w, steps, warmup, min_rot_bytes):
         step(i)
     t1.record(stream)
     torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / steps
+    ms_first = t0.elapsed_time(t1) / steps
+    # six more repeats of the same cold loop; the step time is the median of
+    # the seven blocks (each exactly `steps` steps between synchronisations)
+    reps = [ms_first]
+    for _ in range(6):
+        t0.record(stream)
+        for i in range(steps):
+            step(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        reps.append(t0.elapsed_time(t1) / steps)
+    ms_step = float(np.median(reps))
 
     # warm number: same copy every step (served partly from the last-level cache)
     t0.record(stream)
@@ -190,11 +222,126 @@ def time_workload(torch, pkv, w, steps, warmup, min_rot_bytes):
         "ms_per_step_warm": ms_warm, "effective_gbps_warm": eff / ms_warm / 1e6,
         "ms_split_k_kernel": ms_kernel, "split_k_kernel_gbps": eff / ms_kernel / 1e6,
         "ms_combine_kernel": ms_combine, "rotation": rot_desc,
+        "ms_per_step_blocks": reps, "ms_per_step_first_block": ms_first,
+        "total_bytes": total_bytes(w, nparts, eff), "total_gbps": total_bytes(w, nparts, eff) / ms_step / 1e6,
     }
     log(f"{w.name}: {ms_step * 1e3:.1f} us/step cold ({res['effective_gbps']:.0f} GB/s, "
         f"{res['pct_hbm_peak']:.1f}% of peak), warm {ms_warm * 1e3:.1f} us, split-K kernel "
         f"{ms_kernel * 1e3:.1f} us ({res['split_k_kernel_gbps']:.0f} GB/s), combine {ms_combine * 1e3:.1f} us")
     del rot, dw
+    torch.cuda.empty_cache()
+    return res
+
+
+def read_probe(torch):
+    """Measured read ceilings on this device (libpkv_probe.so, outside the
+    decode library): a linear non-temporal stream over 2 GiB, and 512 MiB of
+    random 2 KB chunks drawn from the same 2 GiB (the paged access pattern).
+    Median of 5 launches each."""
+    import ctypes
+    import numpy as np
+    lib = ctypes.CDLL(PROBE_LIB)
+    vp = ctypes.c_void_p
+    lib.pkv_probe_read_linear.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_int, vp]
+    lib.pkv_probe_read_chunks.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, vp]
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    grid, per_wg = 2048, 8
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    idx = torch.randint(0, nbytes // 2048, (grid * per_wg * 16,), generator=gen, device="cuda").to(torch.int32)
+    stream = torch.cuda.current_stream()
+
+    def timed(call):
+        assert call() == 0
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            assert call() == 0
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    lin = timed(lambda: lib.pkv_probe_read_linear(buf.data_ptr(), nbytes, sink.data_ptr(), grid,
+                                                  stream.cuda_stream))
+    chk = timed(lambda: lib.pkv_probe_read_chunks(buf.data_ptr(), idx.data_ptr(), grid, per_wg,
+                                                  sink.data_ptr(), stream.cuda_stream))
+    touched = grid * per_wg * 32768
+    res = {"linear_read_gbps": nbytes / lin / 1e6, "random_2k_read_gbps": touched / chk / 1e6,
+           "what": "2 GiB linear non-temporal stream; 512 MiB of random 2 KB chunks of the same 2 GiB; "
+                   "median of 5 launches each"}
+    del buf, idx
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_per_layer_graph(torch, pkv, w, steps, warmup, min_rot_bytes):
+    """The 24-layer workload as a model would call it: one launch per layer
+    (one row each, that layer's block table, lengths, q and outputs), the 24
+    launches of a step captured in a HIP graph, one graph per pool copy.
+    Every graph's output is checked against the eager launches before timing."""
+    from synth import effective_kv_bytes_formula
+    from synth.device import to_device
+    dw = to_device(w)
+    p = params_for(pkv, w)
+    p.num_rows = 1
+    rot, rot_desc = rotations(torch, dw, min_rot_bytes)
+    L, hq, d = w.rows, w.num_q_heads, w.head_dim
+    out = torch.empty((L, hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((L, hq), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(pkv.workspace_bytes(p), 16), dtype=torch.uint8, device="cuda")
+
+    def layers(args):
+        q, pool, koff, voff, codec, scale, bt, lens, _, _ = args
+        for layer in range(L):
+            pkv.decode_attention(p, q[layer:layer + 1], pool, koff, voff, codec, scale, bt[layer:layer + 1],
+                                 lens[layer:layer + 1], out=out[layer:layer + 1], lse=lse[layer:layer + 1],
+                                 workspace=ws)
+
+    layers(rot[0])
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(side):
+        for args in rot:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                layers(args)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for _ in range(3):  # replays interleaved with eager work, each checked
+        for g in graphs:
+            out.zero_()
+            lse.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), "graph replay differs from eager"
+        layers(rot[-1])
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    eff = effective_kv_bytes_formula(w)
+    res = {"workload": w.name + "_per_layer_graph", "launches_per_step": L, "ms_per_step": ms,
+           "steps_per_s": 1e3 / ms, "effective_gbps": eff / ms / 1e6, "rotation": rot_desc}
+    log(f"{res['workload']}: {ms * 1e3:.1f} us/step ({L} launches in a HIP graph), "
+        f"{res['effective_gbps']:.0f} GB/s effective")
+    del graphs, rot, dw
     torch.cuda.empty_cache()
     return res
 
@@ -246,13 +393,14 @@ def measured_traffic():
         return None
 
 
-def profile_pass(torch, pkv, synth):
-    """Short run for rocprofv3: the 1M-token split-K kernel (partials only) ten
-    times over two pool copies, ten whole steps (split-K kernel + fold), then a
-    plain device copy of COPY_BYTES three times, whose counters calibrate the
-    per-dispatch byte counts."""
+def profile_pass(torch, pkv, synth, cid=5):
+    """Short run for rocprofv3: the split-K kernel (partials only) of workload
+    `cid` (default the 1M-token one) ten times over its rotation copies, ten
+    whole steps (split-K kernel + fold), then a plain device copy of
+    COPY_BYTES three times, whose counters calibrate the per-dispatch byte
+    counts."""
     from synth.device import to_device
-    w = synth.config(5)
+    w = synth.config(cid)
     dw = to_device(w)
     p = params_for(pkv, w)
     rot, _ = rotations(torch, dw, 1 << 30)
@@ -280,9 +428,11 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--quick", action="store_true", help="headline workload only, no CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-workload", type=int, default=5, choices=(3, 4, 5),
+                    help="workload of --profile-pass (3: batched 32K INT8/INT4, 4: sparse FP8, 5: 1M FP8)")
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for rocprofv3 (split-K kernel + calibration copy), no JSON")
     args = ap.parse_args()
@@ -300,7 +450,7 @@ def main():
         sys.exit(1)
     log(f"device {torch.cuda.get_device_name(0)}")
     if args.profile_pass:
-        profile_pass(torch, pkv, synth)
+        profile_pass(torch, pkv, synth, args.profile_workload)
         return
 
     min_rot = 1 << 30
@@ -308,12 +458,23 @@ def main():
     w5 = synth.config(5)
     head = time_workload(torch, pkv, w5, args.steps, args.warmup, min_rot)
     also = {}
+    probe = None
     if not args.quick:
         for cid in (3, 4):
             log(f"generating workload {cid}")
             w = synth.config(cid)
             also[w.name] = time_workload(torch, pkv, w, args.steps, args.warmup, min_rot)
             del w
+        log("generating workload 2 (24 layers)")
+        w = synth.config(2)
+        also[w.name] = time_workload(torch, pkv, w, args.steps, args.warmup, min_rot)
+        g = time_per_layer_graph(torch, pkv, w, args.steps, args.warmup, min_rot)
+        also[g["workload"]] = g
+        del w
+        log("read probes")
+        probe = read_probe(torch)
+        log(f"probe: linear {probe['linear_read_gbps']:.0f} GB/s, random 2 KB chunks "
+            f"{probe['random_2k_read_gbps']:.0f} GB/s")
     cpu = None
     if not args.quick and not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
@@ -336,6 +497,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic()},
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "seconds"},
+        "read_probe": probe,
+        "pct_of_probe": None if probe is None else round(100 * head["effective_gbps"] / probe["linear_read_gbps"], 2),
         "detail": {"headline": head, **also},
     }
     c3 = also.get(synth.NAMES[3])

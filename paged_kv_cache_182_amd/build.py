@@ -1,4 +1,6 @@
-"""Builds libpkv.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+"""Builds libpkv.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc,
+and libpkv_probe.so, the benchmark's read-bandwidth probes (not part of the
+decode library or its ABI).
 
     python -m paged_kv_cache_182_amd.build
 """
@@ -14,6 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libpkv.so")
 SOURCES = ["pkv_kernels.hip", "pkv_api.cpp"]
+PROBE_LIB = os.path.join(HERE, "libpkv_probe.so")
+PROBE_SOURCES = ["read_probe.hip"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -34,11 +38,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libpkv.so")
 
 
-def build(verbose: bool = False, out: str = LIB, extra: tuple = ()) -> str:
-    """Compile every source into libpkv.so (always recompiles). Returns its path.
-    `extra` adds compiler flags (for example -D variants of a tuning macro)."""
+def build(verbose: bool = False, out: str = LIB, extra: tuple = (), sources=None) -> str:
+    """Compile the decode library's sources into libpkv.so (always recompiles).
+    Returns its path. `extra` adds compiler flags (for example -D variants of
+    a tuning macro); `sources` replaces the source list."""
     tmp = out + ".tmp"
-    cmd = [hipcc(), *FLAGS, *extra, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    srcs = SOURCES if sources is None else sources
+    cmd = [hipcc(), *FLAGS, *extra, *[os.path.join(CSRC, s) for s in srcs], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,5 +59,11 @@ def build(verbose: bool = False, out: str = LIB, extra: tuple = ()) -> str:
     return out
 
 
+def build_probe(verbose: bool = False) -> str:
+    """Compile libpkv_probe.so (the benchmark's read probes)."""
+    return build(verbose, out=PROBE_LIB, sources=PROBE_SOURCES)
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probe(verbose=True))
