@@ -24,6 +24,9 @@ What it computes (sources are the three pages' own sections):
   windows folded by log-sum-exp into an fp32 accumulator).
 * Byte accounting (``accounting``): bytes of codes + scales, pinned to the
   memory figures ARGUS prints for its engine at 32K ("Direct paged attention").
+* Write side (``encode``): a new token appended into its 16-bit page, and
+  full 16-bit pages re-encoded (demoted) to FP8 / INT8 / INT4 (ARGUS "v0.5"
+  and "Adaptive activation"; FreeToken PR #499 update, item 1).
 
 Pins live in ``tests/test_oracle_*.py``; see each function for what pins it.
 """
@@ -31,3 +34,4 @@ from .codecs import (decode_bf16, decode_fp16, decode_fp8_e4m3, decode_int4,  # 
                      decode_int8)
 from .attention import decode_attention, fold, gather_kv, partials  # noqa: F401
 from .accounting import kv_bytes_per_token  # noqa: F401
+from .encode import append_token, encode_page  # noqa: F401
