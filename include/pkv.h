@@ -194,6 +194,71 @@ int pkv_decode_partials(const pkv_params* p, const void* q, const uint8_t* page_
 int pkv_lse_combine(int32_t rows, int32_t num_parts, int32_t head_dim, const float* part_acc,
                     const float* part_ml, float* out, float* lse, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Write side: the steps right before this read path, producing exactly the
+ * page format it reads. Recent pages stay 16-bit while they fill; full older
+ * pages are re-encoded into a compact codec (ARGUS "Adaptive activation" and
+ * "v0.5": tiered pages, FP16 for the recent window). FP8 pages hold e4m3
+ * codes plus fp32 scales (FreeToken PR #499 update, item 1); INT8/INT4 pages
+ * hold one fp16 scale per token and group of 32 (GGML Q8/Q4 pages).
+ * Both calls use num_rows (append only), num_kv_heads, head_dim (64 or 128),
+ * page_size, num_pages, max_pages_per_row (append only) and pool_bytes of p;
+ * the other fields are ignored. Asynchronous on `stream`, like the rest.
+ * ------------------------------------------------------------------------- */
+
+/* Stores one new token per row in its 16-bit page.
+ *
+ *   k_new, v_new  fp16 [num_rows][Hkv][D], 2-byte aligned.
+ *   seq_lens      [num_rows] lengths BEFORE the append: row b's token goes to
+ *                 slot seq_lens[b] % P of logical page seq_lens[b] / P, i.e.
+ *                 physical page block_table[b][seq_lens[b] / P]. The caller
+ *                 advances seq_lens afterwards.
+ *   Other tables as in pkv_decode_attention; the page's K and V planes must
+ *   be FP16 or BF16 (a BF16 plane stores the value rounded to nearest even).
+ *
+ * Writes 2*Hkv*D codes per row and nothing else. A row whose length is
+ * negative or beyond max_pages_per_row, whose page id is out of range, whose
+ * page is not 16-bit in both planes or whose plane lies outside the pool is
+ * counted in *err_count (if given) and skipped. Host-visible errors as in
+ * pkv_decode_attention. */
+int pkv_append_kv(const pkv_params* p, const void* k_new, const void* v_new, uint8_t* page_pool,
+                  const uint64_t* page_k_off, const uint64_t* page_v_off, const uint8_t* page_codec,
+                  const int32_t* block_table, const int32_t* seq_lens, int32_t* err_count, void* stream);
+
+/* Re-encodes n full 16-bit pages into another codec (demotion).
+ *
+ *   src_pages, dst_pages  [n] physical page ids: page src_pages[i] (FP16 or
+ *                 BF16 in both planes) is read, every slot of it, and page
+ *                 dst_pages[i] is written. The destination planes live at
+ *                 page_k_off / page_v_off[dst] (16-byte aligned, inside the
+ *                 pool, sized for dst_codec) and must not overlap the source
+ *                 planes. No destination may appear twice, or as a source, in
+ *                 one call (not checked).
+ *   dst_codec     K codec in the low nibble, V codec in the high nibble:
+ *                 FP16, BF16, FP8 e4m3, INT8 or INT4. Encoding, decided in
+ *                 fp32:
+ *                   FP8: s = fp32(absmax / 448) per (page, KV head, plane),
+ *                        1 if the block is all zero; code = e4m3 nearest to
+ *                        fp32(x / s), ties to even.
+ *                   INT8/INT4: s = fp16(fp32(absmax) / qmax) per (token, 32
+ *                        dims), qmax 127 / 7, 1 if the group is all zero;
+ *                        code = clip(rint(fp32(x) / fp32(s)), -qmax, qmax).
+ *                   BF16/FP16: the value, rounded to nearest even.
+ *   page_codec    page_codec[dst] is set to dst_codec.
+ *   page_scale    [num_pages][Hkv][2]; page_scale[dst][h] is set to the FP8
+ *                 scales (1 for a plane in another codec). May be NULL only
+ *                 if neither plane is FP8.
+ *
+ * A pair with an id out of range, equal ids, a source that is not 16-bit,
+ * a plane outside the pool, a misaligned plane or overlapping planes is
+ * counted in *err_count (if given) and skipped. Host-visible errors as in
+ * pkv_decode_attention; PKV_ERR_INVALID_ARG also for a bad codec nibble or a
+ * missing page_scale. */
+int pkv_encode_pages(const pkv_params* p, int32_t n, const int32_t* src_pages, const int32_t* dst_pages,
+                     int32_t dst_codec, uint8_t* page_pool, const uint64_t* page_k_off,
+                     const uint64_t* page_v_off, uint8_t* page_codec, float* page_scale, int32_t* err_count,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

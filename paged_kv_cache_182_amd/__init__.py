@@ -4,5 +4,6 @@ The compute lives in ``libpkv.so`` (HIP kernels behind the C ABI declared in
 ``include/pkv.h``); ``_lib`` is a thin ctypes binding with the same names.
 """
 from ._lib import (BF16, CODEC_MIXED, FP8_E4M3, FP16, INT4_G32, INT8_G32, EXPORTS,  # noqa: F401
-                   LIB_PATH, Params, PkvError, decode_attention, decode_partials, hip_runtime_copies, load,
-                   lse_combine, make_params, num_partitions, status_string, workspace_bytes)
+                   LIB_PATH, Params, PkvError, append_kv, decode_attention, decode_partials, encode_pages,
+                   hip_runtime_copies, load, lse_combine, make_params, num_partitions, status_string,
+                   workspace_bytes)

@@ -21,7 +21,7 @@ FP16, BF16, FP8_E4M3, INT8_G32, INT4_G32, CODEC_MIXED = 0, 1, 2, 3, 4, -1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "pkv_num_partitions",
            "pkv_workspace_bytes", "pkv_decode_attention", "pkv_decode_partials",
-           "pkv_lse_combine")
+           "pkv_lse_combine", "pkv_append_kv", "pkv_encode_pages")
 
 
 class PkvError(RuntimeError):
@@ -67,6 +67,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_decode_partials.argtypes = [pp] + [vp] * 12 + [vp, vp]
     lib.pkv_lse_combine.restype = ctypes.c_int
     lib.pkv_lse_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.pkv_append_kv.restype = ctypes.c_int
+    lib.pkv_append_kv.argtypes = [pp] + [vp] * 10
+    lib.pkv_encode_pages.restype = ctypes.c_int
+    lib.pkv_encode_pages.argtypes = [pp, i32, vp, vp, i32] + [vp] * 7
     if lib.pkv_abi_version() != 1:
         raise RuntimeError("libpkv ABI version mismatch")
     _lib = lib
@@ -197,6 +201,42 @@ def lse_combine(part_acc, part_ml, out=None, lse=None, stream=None):
     if st != OK:
         raise PkvError(st, "pkv_lse_combine")
     return out, lse
+
+
+def append_kv(p: Params, k_new, v_new, page_pool, page_k_off, page_v_off, page_codec, block_table,
+              seq_lens, *, err_count=None, stream=None) -> None:
+    """Enqueue pkv_append_kv: k_new, v_new fp16 [rows, Hkv, D]; seq_lens are
+    the lengths before the append. Raises PkvError on a bad status."""
+    lib = load()
+    dev = k_new.device
+    st = lib.pkv_append_kv(
+        ctypes.byref(p), _ptr(k_new, torch.float16, "k_new", dev), _ptr(v_new, torch.float16, "v_new", dev),
+        _ptr(page_pool, torch.uint8, "page_pool", dev), _ptr(page_k_off, torch.uint64, "page_k_off", dev),
+        _ptr(page_v_off, torch.uint64, "page_v_off", dev), _ptr(page_codec, torch.uint8, "page_codec", dev),
+        _ptr(block_table, torch.int32, "block_table", dev), _ptr(seq_lens, torch.int32, "seq_lens", dev),
+        _ptr(err_count, torch.int32, "err_count", dev), _stream(stream))
+    if st != OK:
+        raise PkvError(st, "pkv_append_kv")
+
+
+def encode_pages(p: Params, src_pages, dst_pages, dst_codec: int, page_pool, page_k_off, page_v_off,
+                 page_codec, page_scale=None, *, err_count=None, stream=None) -> None:
+    """Enqueue pkv_encode_pages: re-encode pages src_pages[i] into dst_pages[i]
+    with dst_codec (K | V << 4). Raises PkvError on a bad status."""
+    lib = load()
+    dev = page_pool.device
+    n = int(src_pages.numel())
+    if int(dst_pages.numel()) != n:
+        raise ValueError("src_pages and dst_pages must have the same length")
+    st = lib.pkv_encode_pages(
+        ctypes.byref(p), n, _ptr(src_pages, torch.int32, "src_pages", dev),
+        _ptr(dst_pages, torch.int32, "dst_pages", dev), int(dst_codec),
+        _ptr(page_pool, torch.uint8, "page_pool", dev), _ptr(page_k_off, torch.uint64, "page_k_off", dev),
+        _ptr(page_v_off, torch.uint64, "page_v_off", dev), _ptr(page_codec, torch.uint8, "page_codec", dev),
+        _ptr(page_scale, torch.float32, "page_scale", dev), _ptr(err_count, torch.int32, "err_count", dev),
+        _stream(stream))
+    if st != OK:
+        raise PkvError(st, "pkv_encode_pages")
 
 
 def hip_runtime_copies() -> list[str]:

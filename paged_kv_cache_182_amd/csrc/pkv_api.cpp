@@ -211,3 +211,94 @@ int pkv_lse_combine(int32_t rows, int32_t num_parts, int32_t head_dim, const flo
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ write side
+namespace {
+
+// Plain-value checks shared by the write-side calls (q heads and codecs of
+// the read path are not used).
+int check_write_params(const pkv_params* p) {
+  if (!p) return PKV_ERR_INVALID_ARG;
+  if (p->num_rows < 0 || p->num_kv_heads <= 0 || p->num_pages < 0) return PKV_ERR_INVALID_ARG;
+  if (p->page_size <= 0 || p->page_size % 16 != 0 || p->max_pages_per_row < 1) return PKV_ERR_INVALID_ARG;
+  if (p->head_dim != 64 && p->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (p->num_rows > 65535 || p->num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_append_kv(const pkv_params* p, const void* k_new, const void* v_new, uint8_t* page_pool,
+                  const uint64_t* page_k_off, const uint64_t* page_v_off, const uint8_t* page_codec,
+                  const int32_t* block_table, const int32_t* seq_lens, int32_t* err_count, void* stream) {
+  const int st = check_write_params(p);
+  if (st != PKV_OK) return st;
+  if (p->num_rows == 0) return PKV_OK;
+  if (!k_new || !v_new || !page_pool || !page_k_off || !page_v_off || !page_codec || !block_table || !seq_lens)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned(k_new, 2) || !aligned(v_new, 2) || !aligned(page_pool, 256) || !aligned(page_k_off, 8) ||
+      !aligned(page_v_off, 8) || !aligned(block_table, 4) || !aligned(seq_lens, 4) ||
+      (err_count && !aligned(err_count, 4)))
+    return PKV_ERR_INVALID_ARG;
+  pkv::AppendArgs a{};
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.pool = page_pool;
+  a.koff = page_k_off;
+  a.voff = page_v_off;
+  a.codec = page_codec;
+  a.bt = block_table;
+  a.seq_lens = seq_lens;
+  a.err = err_count;
+  a.rows = p->num_rows;
+  a.hkv = p->num_kv_heads;
+  a.head_dim = p->head_dim;
+  a.page = p->page_size;
+  a.num_pages = p->num_pages;
+  a.max_pages = p->max_pages_per_row;
+  a.pool_bytes = p->pool_bytes;
+  return pkv::launch_append(a, stream) == 0 ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_encode_pages(const pkv_params* p, int32_t n, const int32_t* src_pages, const int32_t* dst_pages,
+                     int32_t dst_codec, uint8_t* page_pool, const uint64_t* page_k_off,
+                     const uint64_t* page_v_off, uint8_t* page_codec, float* page_scale, int32_t* err_count,
+                     void* stream) {
+  const int st = check_write_params(p);
+  if (st != PKV_OK) return st;
+  const int kc = dst_codec & 15, vc = (dst_codec >> 4) & 15;
+  if (n < 0 || dst_codec < 0 || dst_codec > 0xFF || kc > PKV_INT4_G32 || vc > PKV_INT4_G32)
+    return PKV_ERR_INVALID_ARG;
+  if (n == 0) return PKV_OK;
+  if (n > 0x7fffffff / 2) return PKV_ERR_UNSUPPORTED;
+  if (!src_pages || !dst_pages || !page_pool || !page_k_off || !page_v_off || !page_codec)
+    return PKV_ERR_INVALID_ARG;
+  if ((kc == PKV_FP8_E4M3 || vc == PKV_FP8_E4M3) && !page_scale) return PKV_ERR_INVALID_ARG;
+  if (!aligned(src_pages, 4) || !aligned(dst_pages, 4) || !aligned(page_pool, 256) ||
+      !aligned(page_k_off, 8) || !aligned(page_v_off, 8) || (page_scale && !aligned(page_scale, 4)) ||
+      (err_count && !aligned(err_count, 4)))
+    return PKV_ERR_INVALID_ARG;
+  pkv::EncodeArgs a{};
+  a.src = src_pages;
+  a.dst = dst_pages;
+  a.pool = page_pool;
+  a.koff = page_k_off;
+  a.voff = page_v_off;
+  a.codec = page_codec;
+  a.codec_out = page_codec;
+  a.scale = page_scale;
+  a.err = err_count;
+  a.n = n;
+  a.dst_codec = dst_codec;
+  a.hkv = p->num_kv_heads;
+  a.head_dim = p->head_dim;
+  a.page = p->page_size;
+  a.num_pages = p->num_pages;
+  a.pool_bytes = p->pool_bytes;
+  const int r = pkv::launch_encode(a, stream);
+  return r == 0 ? PKV_OK : (r == -2 ? PKV_ERR_UNSUPPORTED : PKV_ERR_HIP);
+}
+
+}  // extern "C"

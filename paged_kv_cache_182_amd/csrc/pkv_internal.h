@@ -33,6 +33,39 @@ struct DecodeArgs {
   uint64_t pool_bytes;      // size of the arena; planes must lie inside it
 };
 
+// One token per row into its 16-bit page (pkv_append_kv).
+struct AppendArgs {
+  const uint16_t* k_new;    // fp16 [rows][Hkv][D]
+  const uint16_t* v_new;
+  uint8_t* pool;
+  const uint64_t* koff;
+  const uint64_t* voff;
+  const uint8_t* codec;
+  const int32_t* bt;        // [rows][max_pages]
+  const int32_t* seq_lens;  // [rows], lengths before the append
+  int32_t* err;
+  int32_t rows, hkv, head_dim, page, num_pages, max_pages;
+  uint64_t pool_bytes;
+};
+
+// Re-encode n 16-bit pages (pkv_encode_pages).
+struct EncodeArgs {
+  const int32_t* src;       // [n] physical page ids read
+  const int32_t* dst;       // [n] physical page ids written
+  uint8_t* pool;
+  const uint64_t* koff;
+  const uint64_t* voff;
+  const uint8_t* codec;     // read: source codecs
+  uint8_t* codec_out;       // written: page_codec[dst] = dst_codec
+  float* scale;             // [num_pages][Hkv][2] or nullptr
+  int32_t* err;
+  int32_t n, dst_codec, hkv, head_dim, page, num_pages;
+  uint64_t pool_bytes;
+};
+
+int launch_append(const AppendArgs& a, void* stream);
+int launch_encode(const EncodeArgs& a, void* stream);
+
 // Launches the decode kernel for (head_dim, k codec, v codec); codec -1 means
 // per-page dispatch. Returns 0 on success, -2 if no kernel exists for the
 // combination, -4 if the launch failed.

@@ -99,3 +99,35 @@ def test_host_rejects_bad_pointers_and_workspace():
     assert pkv.load().pkv_lse_combine(4, 0, 128, 4096, 4096, 4096, 4096, 0) == -1
     assert pkv.load().pkv_lse_combine(4, 2, 1024, 4096, 4096, 4096, 4096, 0) == -1
     assert pkv.load().pkv_lse_combine(0, 2, 128, 0, 0, 0, 0, 0) == 0
+
+
+def wbase(**kw):
+    d = dict(rows=4, num_q_heads=16, num_kv_heads=2, head_dim=128, page_size=64, num_pages=64,
+             max_pages_per_row=16, pool_bytes=1 << 24)
+    d.update(kw)
+    return pkv.make_params(**d)
+
+
+def test_append_host_checks():
+    lib = pkv.load()
+    p = wbase()
+    good = [4096] * 8          # fake addresses: every call below must be rejected on the host
+    assert lib.pkv_append_kv(ctypes.byref(p), 0, *good[1:], 0, 0) == -1           # k_new missing
+    assert lib.pkv_append_kv(ctypes.byref(p), 4097, *good[1:], 0, 0) == -1        # k_new odd address
+    assert lib.pkv_append_kv(ctypes.byref(p), 4096, 4096, 4096 + 16, *good[3:], 0, 0) == -1  # pool alignment
+    assert lib.pkv_append_kv(ctypes.byref(wbase(head_dim=96)), *good, 0, 0) == -2
+    assert lib.pkv_append_kv(ctypes.byref(wbase(page_size=24)), *good, 0, 0) == -1
+    assert lib.pkv_append_kv(ctypes.byref(wbase(rows=0)), 0, 0, 0, 0, 0, 0, 0, 0, 0, 0) == 0
+
+
+def test_encode_host_checks():
+    lib = pkv.load()
+    p = wbase()
+    args = [4096] * 5                                  # pool, k_off, v_off, codec, scale
+    assert lib.pkv_encode_pages(ctypes.byref(p), 0, 0, 0, 0x22, *args, 0, 0) == 0      # nothing to do
+    assert lib.pkv_encode_pages(ctypes.byref(p), -1, 4096, 4096, 0x22, *args, 0, 0) == -1
+    assert lib.pkv_encode_pages(ctypes.byref(p), 4, 4096, 4096, 0x25, *args, 0, 0) == -1  # K nibble 5
+    assert lib.pkv_encode_pages(ctypes.byref(p), 4, 4096, 4096, 0x122, *args, 0, 0) == -1  # > one byte
+    assert lib.pkv_encode_pages(ctypes.byref(p), 4, 4096, 4096, 0x22, 4096, 4096, 4096, 4096, 0, 0, 0) == -1  # FP8 needs scales
+    assert lib.pkv_encode_pages(ctypes.byref(p), 4, 0, 4096, 0x43, *args, 0, 0) == -1      # src missing
+    assert lib.pkv_encode_pages(ctypes.byref(wbase(head_dim=256)), 4, 4096, 4096, 0x43, *args, 0, 0) == -2
