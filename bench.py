@@ -346,6 +346,89 @@ def time_per_layer_graph(torch, pkv, w, steps, warmup, min_rot_bytes):
     return res
 
 
+def time_write_side(torch, pkv, steps):
+    """The write side, measured on its own: demotion of full FP16 pages
+    (pkv_encode_pages) at the 1M FP8 and 32K INT8-K/INT4-V geometries, and one
+    decode step's append (pkv_append_kv) for the 8-row batch. The source pages
+    hold random fp16 values; every call re-encodes the same pages."""
+    import numpy as np
+
+    def aligned(x):
+        return (x + 255) // 256 * 256
+
+    def plane(c, hkv, P, D):
+        bits = 16 if c <= 1 else (4 if c == 4 else 8)
+        return hkv * P * D * bits // 8 + (hkv * P * (D // 32) * 2 if c in (3, 4) else 0)
+
+    def timed(call, n):
+        call()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+    res = {}
+    for name, n, hkv, P, D, dst_codec in (("demote_fp16_to_fp8_1m", 16384, 2, 64, 128, 0x22),
+                                          ("demote_fp16_to_int8k_int4v_32k", 14720, 8, 16, 128, 0x43)):
+        sp = aligned(plane(0, hkv, P, D))
+        dk, dv = aligned(plane(dst_codec & 15, hkv, P, D)), aligned(plane(dst_codec >> 4, hkv, P, D))
+        base = n * 2 * sp
+        total = base + n * (dk + dv)
+        pool = torch.empty(total, dtype=torch.uint8, device="cuda")
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(11)
+        pool[:base].view(torch.float16).normal_(generator=gen)
+        idx = torch.arange(n, dtype=torch.int64, device="cuda")
+        ih = np.arange(n, dtype=np.uint64)
+        koff = torch.from_numpy(np.concatenate([ih * (2 * sp), base + ih * (dk + dv)])).cuda()
+        voff = torch.from_numpy(np.concatenate([ih * (2 * sp) + sp, base + ih * (dk + dv) + dk])).cuda()
+        codec = torch.cat([torch.zeros(n, dtype=torch.uint8, device="cuda"),
+                           torch.full((n,), 0x77, dtype=torch.uint8, device="cuda")])
+        scale = torch.zeros((2 * n, hkv, 2), dtype=torch.float32, device="cuda")
+        src = idx.to(torch.int32)
+        dst = (idx + n).to(torch.int32)
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        p = pkv.make_params(rows=1, num_q_heads=hkv, num_kv_heads=hkv, head_dim=D, page_size=P,
+                            num_pages=2 * n, max_pages_per_row=1, pool_bytes=total)
+        ms = timed(lambda: pkv.encode_pages(p, src, dst, dst_codec, pool, koff, voff, codec, scale,
+                                            err_count=err), max(steps // 5, 5))
+        assert int(err.item()) == 0 and bool((codec[n:] == dst_codec).all()), "demotion failed"
+        moved = n * (2 * plane(0, hkv, P, D) + plane(dst_codec & 15, hkv, P, D) + plane(dst_codec >> 4, hkv, P, D))
+        if dst_codec & 15 == 2 or dst_codec >> 4 == 2:
+            moved += n * hkv * 8
+        res[name] = {"pages": n, "ms": ms, "pages_per_s": n / ms * 1e3, "algorithmic_bytes": moved,
+                     "gbps": moved / ms / 1e6, "frac_of_8tbs": moved / ms / 1e6 / HBM_PEAK_GBPS}
+        log(f"{name}: {n} pages in {ms * 1e3:.1f} us, {res[name]['gbps']:.0f} GB/s read+written")
+        del pool, koff, voff, codec, scale
+        torch.cuda.empty_cache()
+
+    # one decode step's append: 8 rows x 8 KV heads x 128 dims, FP16 pages of 16 tokens
+    rows, hkv, P, D = 8, 8, 16, 128
+    sp = aligned(plane(0, hkv, P, D))
+    pool = torch.zeros(rows * 2 * sp, dtype=torch.uint8, device="cuda")
+    idx = torch.arange(rows, dtype=torch.int64, device="cuda")
+    ir = np.arange(rows, dtype=np.uint64)
+    koff = torch.from_numpy(ir * (2 * sp)).cuda()
+    voff = torch.from_numpy(ir * (2 * sp) + sp).cuda()
+    codec = torch.zeros(rows, dtype=torch.uint8, device="cuda")
+    bt = idx.to(torch.int32)[:, None].contiguous()
+    lens = torch.tensor([3, 15, 0, 7, 9, 1, 12, 5], dtype=torch.int32, device="cuda")
+    k_new = torch.randn((rows, hkv, D), dtype=torch.float16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    p = pkv.make_params(rows=rows, num_q_heads=hkv, num_kv_heads=hkv, head_dim=D, page_size=P,
+                        num_pages=rows, max_pages_per_row=1, pool_bytes=pool.numel())
+    ms = timed(lambda: pkv.append_kv(p, k_new, k_new, pool, koff, voff, codec, bt, lens, err_count=err), steps)
+    assert int(err.item()) == 0, "append failed"
+    res["append_8rows_8kvheads"] = {"us_per_call": ms * 1e3, "bytes_written": rows * hkv * D * 2 * 2}
+    log(f"append (8 rows x 8 KV heads): {ms * 1e3:.1f} us per call")
+    return res
+
+
 def cpu_baseline(w_full, min_seconds=10.0):
     """The oracle, as it is, on a bounded sample of the headline workload:
     whole 1M-token steps (both KV heads, all 16 query heads), repeated until
@@ -471,6 +554,8 @@ def main():
         g = time_per_layer_graph(torch, pkv, w, args.steps, args.warmup, min_rot)
         also[g["workload"]] = g
         del w
+        log("write side")
+        also["write_side"] = time_write_side(torch, pkv, args.steps)
         log("read probes")
         probe = read_probe(torch)
         log(f"probe: linear {probe['linear_read_gbps']:.0f} GB/s, random 2 KB chunks "

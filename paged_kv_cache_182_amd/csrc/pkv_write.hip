@@ -137,15 +137,74 @@ __global__ void __launch_bounds__(64) append_kernel(AppendArgs a) {
 }
 
 // ------------------------------------------------------------------ encode
-constexpr int ENC_THREADS = 256;
-constexpr int ENC_TILES = ENC_THREADS / 64;   // tiles staged at once
+// Codes of one destination run (lane L of a tile): D/4 elements from the
+// staged tile x[token][dim], written with 16-byte (8 for INT4 at D = 64)
+// stores at the run's chunk positions.
+template <int D, int DC, bool IS_V>
+__device__ __attribute__((always_inline)) inline void emit_run(const float (*x)[D + 1], const float (*sc)[D / 32], float s8, uint8_t* td,
+                                int lane) {
+  constexpr int BITS = DC <= W_BF16 ? 16 : (DC == W_INT4 ? 4 : 8);
+  constexpr int E = D / 4, RD = D * BITS / 32;
+  constexpr bool GROUPED = (DC == W_INT8 || DC == W_INT4) && !IS_V;
+  constexpr float QMAX = DC == W_INT8 ? 127.0f : 7.0f;
+  uint32_t word[RD / 4];
+#pragma unroll
+  for (int k = 0; k < RD / 4; ++k) word[k] = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    int tt, d;
+    run_elem(lane, e, D, IS_V, GROUPED, tt, d);
+    const float v = x[tt][d];
+    uint32_t code;
+    if constexpr (DC == W_FP16) {
+      code = __builtin_bit_cast(uint16_t, (_Float16)v);
+    } else if constexpr (DC == W_BF16) {
+      code = f_to_bf16(v);
+    } else if constexpr (DC == W_FP8) {
+      code = f_to_e4m3(fminf(fmaxf(__fdiv_rn(v, s8), -448.0f), 448.0f));
+    } else {
+      const float q = __builtin_rintf(__fdiv_rn(v, sc[tt][d / 32]));
+      code = (uint32_t)(int)fminf(fmaxf(q, -QMAX), QMAX);
+    }
+    if constexpr (BITS == 16) {
+      word[e >> 1] |= (code & 0xFFFFu) << (16 * (e & 1));
+    } else if constexpr (BITS == 8) {
+      word[e >> 2] |= (code & 0xFFu) << (8 * (e & 3));
+    } else {
+      const int r = e & 7, nslot = (r & 1) * 4 + (r >> 1);
+      word[e >> 3] |= (code & 0xFu) << (4 * nslot);
+    }
+  }
+  if constexpr (RD >= 16) {
+#pragma unroll
+    for (int c = 0; c < RD / 16; ++c)
+      *reinterpret_cast<u4*>(td + run_byte(lane, 16 * c, RD)) =
+          u4{word[4 * c], word[4 * c + 1], word[4 * c + 2], word[4 * c + 3]};
+  } else {
+    *reinterpret_cast<uint2*>(td + run_byte(lane, 0, RD)) = uint2{word[0], word[1]};
+  }
+}
 
-// Grid (pair i, KV head, plane).
-template <int D>
-__global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
-  __shared__ float xs[ENC_TILES][16][D + 1];          // staged tiles, [token][dim]
-  __shared__ float sc[ENC_TILES][16][D / 32];         // INT group scales (fp32 of the fp16 value)
-  __shared__ float red[ENC_THREADS / 64];
+template <int D, bool IS_V>
+__device__ __attribute__((always_inline)) inline void emit_any(int dc, const float (*x)[D + 1], const float (*sc)[D / 32], float s8, uint8_t* td,
+                                int lane) {
+  switch (dc) {
+    case W_FP16: emit_run<D, W_FP16, IS_V>(x, sc, s8, td, lane); break;
+    case W_BF16: emit_run<D, W_BF16, IS_V>(x, sc, s8, td, lane); break;
+    case W_FP8: emit_run<D, W_FP8, IS_V>(x, sc, s8, td, lane); break;
+    case W_INT8: emit_run<D, W_INT8, IS_V>(x, sc, s8, td, lane); break;
+    default: emit_run<D, W_INT4, IS_V>(x, sc, s8, td, lane); break;
+  }
+}
+
+// Grid (pair i, KV head, plane); TILES tiles of 16 tokens staged at once, one
+// 64-lane slot each (TILES = min(4, P/16), so no slot idles on small pages).
+template <int D, int TILES>
+__global__ void __launch_bounds__(64 * TILES) encode_kernel(EncodeArgs a) {
+  constexpr int THREADS = 64 * TILES;
+  __shared__ float xs[TILES][16][D + 1];              // staged tiles, [token][dim]
+  __shared__ float scs[TILES][16][D / 32];            // INT group scales (fp32 of the fp16 value)
+  __shared__ float red[TILES];
   const int i = blockIdx.x, h = blockIdx.y, plane = blockIdx.z, tid = threadIdx.x;
   const int P = a.page, hkv = a.hkv;
   const int lane = tid & 63, slot = tid >> 6;
@@ -165,7 +224,7 @@ __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
     const uint64_t sb = wplane_bytes(scodec, hkv, P, D), db = wplane_bytes(dcodec, hkv, P, D);
     ok = ok && ((so | dof) & 15) == 0 && so <= a.pool_bytes && a.pool_bytes - so >= sb &&
          dof <= a.pool_bytes && a.pool_bytes - dof >= db;
-    // the destination planes must not overlap either source plane
+    // the destination plane must not overlap either source plane
     const uint64_t sk = a.koff[src], sv = a.voff[src];
     const uint64_t skb = wplane_bytes(cb & 15, hkv, P, D), svb = wplane_bytes(cb >> 4, hkv, P, D);
     ok = ok && (dof + db <= sk || sk + skb <= dof) && (dof + db <= sv || sv + svb <= dof);
@@ -174,15 +233,20 @@ __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
     if (h == 0 && plane == 0 && tid == 0) count_err(a.err);
     return;
   }
+  const int dbits = wbits(dcodec);
   const uint8_t* sp = a.pool + so + (size_t)h * P * D * 2;
-  uint8_t* dp = a.pool + dof + (size_t)h * P * D * wbits(dcodec) / 8;
+  uint8_t* dp = a.pool + dof + (size_t)h * P * D * dbits / 8;
 
-  // ---- FP8: the block's absmax first (one streaming pass over the head's codes)
+  // ---- FP8 scale: from the absmax of the head's whole block. A page that
+  // fits one staging round takes it while staging (one read of the page);
+  // a longer page takes it in a streaming pass first.
+  const int ntiles = P / 16;
+  const bool one_round = ntiles <= TILES;
   float s8 = 1.f;
-  if (dcodec == W_FP8) {
+  if (dcodec == W_FP8 && !one_round) {
     float m = 0.f;
     const uint32_t n16 = (uint32_t)(P * D * 2 / 16);
-    for (uint32_t c = tid; c < n16; c += ENC_THREADS) {
+    for (uint32_t c = tid; c < n16; c += THREADS) {
       const u4 w = *reinterpret_cast<const u4*>(sp + 16 * (size_t)c);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -193,99 +257,75 @@ __global__ void __launch_bounds__(ENC_THREADS) encode_kernel(EncodeArgs a) {
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
     if (lane == 0) red[slot] = m;
     __syncthreads();
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    m = red[0];
+#pragma unroll
+    for (int k = 1; k < TILES; ++k) m = fmaxf(m, red[k]);
     s8 = m == 0.f ? 1.f : __fdiv_rn(m, 448.0f);
     if (tid == 0 && a.scale) a.scale[((size_t)dst * hkv + h) * 2 + plane] = s8;
-  } else if (tid == 0 && a.scale) {
+  } else if (dcodec != W_FP8 && tid == 0 && a.scale) {
     a.scale[((size_t)dst * hkv + h) * 2 + plane] = 1.f;
   }
   if (h == 0 && plane == 0 && tid == 0) a.codec_out[dst] = (uint8_t)a.dst_codec;
 
   const bool is_v = plane == 1;
-  constexpr int E = D / 4;                               // run elements per lane
-  constexpr int Rs = D / 2;                              // source run bytes (16-bit)
-  const int dbits = wbits(dcodec);
-  const int Rd = D * dbits / 32;                         // destination run bytes
-  const bool dgrouped = wint(dcodec) && !is_v;
-  const int qmax = dcodec == W_INT8 ? 127 : 7;
-  const int ntiles = P / 16;
+  constexpr int RS = D / 2;                              // source run bytes (16-bit)
   constexpr int G = D / 32;
+  const float qmax = dcodec == W_INT8 ? 127.0f : 7.0f;
 
-  for (int t0 = 0; t0 < ntiles; t0 += ENC_TILES) {
+  for (int t0 = 0; t0 < ntiles; t0 += TILES) {
     const int tile = t0 + slot;
     const bool live = tile < ntiles;
     __syncthreads();
     // stage: lane L of this slot reads its source run (16-bit layout, ungrouped K)
+    float mloc = 0.f;
     if (live) {
       const uint8_t* ts = sp + (size_t)tile * 16 * D * 2;
 #pragma unroll
-      for (int c = 0; c < Rs / 16; ++c) {
-        const u4 w = *reinterpret_cast<const u4*>(ts + run_byte(lane, 16 * c, Rs));
+      for (int c = 0; c < RS / 16; ++c) {
+        const u4 w = *reinterpret_cast<const u4*>(ts + run_byte(lane, 16 * c, RS));
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const int e = 8 * c + k;
           int tt, d;
-          run_elem(lane, e, D, is_v, false, tt, d);
+          run_elem(lane, 8 * c + k, D, is_v, false, tt, d);
           const uint16_t code = (uint16_t)((k & 1) ? (w[k >> 1] >> 16) : (w[k >> 1] & 0xFFFF));
-          xs[slot][tt][d] = h16_to_f(code, scodec);
+          const float v = h16_to_f(code, scodec);
+          xs[slot][tt][d] = v;
+          mloc = fmaxf(mloc, __builtin_fabsf(v));
         }
       }
     }
+    if (dcodec == W_FP8 && one_round) {   // the whole page is staged: its absmax
+      for (int o = 32; o >= 1; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
+      if (lane == 0) red[slot] = mloc;
+    }
     __syncthreads();
-    // INT group scales: one (token, group) per thread of the slot
+    if (dcodec == W_FP8 && one_round) {
+      float m = red[0];
+#pragma unroll
+      for (int k = 1; k < TILES; ++k) m = fmaxf(m, red[k]);
+      s8 = m == 0.f ? 1.f : __fdiv_rn(m, 448.0f);
+      if (tid == 0 && a.scale) a.scale[((size_t)dst * hkv + h) * 2 + plane] = s8;
+    }
+    // INT group scales: one (token, group) per lane of the slot
     if (live && wint(dcodec)) {
       for (int q = lane; q < 16 * G; q += 64) {
         const int tt = q / G, g = q % G;
         float m = 0.f;
+#pragma unroll 8
         for (int j = 0; j < 32; ++j) m = fmaxf(m, __builtin_fabsf(xs[slot][tt][32 * g + j]));
-        const _Float16 s16 = m == 0.f ? (_Float16)1.0f : (_Float16)__fdiv_rn(m, (float)qmax);
-        sc[slot][tt][g] = (float)s16;
+        const _Float16 s16 = m == 0.f ? (_Float16)1.0f : (_Float16)__fdiv_rn(m, qmax);
+        scs[slot][tt][g] = (float)s16;
         const size_t so16 = (size_t)hkv * P * D * dbits / 8 + ((size_t)h * P + 16 * tile + tt) * G * 2 + 2 * g;
         *reinterpret_cast<_Float16*>(a.pool + dof + so16) = s16;
       }
     }
     __syncthreads();
     if (!live) continue;
-    // destination run of lane L: E elements, Rd bytes, written 16 (or 8) bytes at a time
     uint8_t* td = dp + (size_t)tile * 16 * D * dbits / 8;
-    uint32_t word[D / 8];                               // the run: up to D/2 bytes
-#pragma unroll
-    for (int k = 0; k < D / 8; ++k) word[k] = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      int tt, d;
-      run_elem(lane, e, D, is_v, dgrouped, tt, d);
-      const float x = xs[slot][tt][d];
-      uint32_t code;
-      if (dcodec == W_FP16) {
-        code = __builtin_bit_cast(uint16_t, (_Float16)x);
-      } else if (dcodec == W_BF16) {
-        code = f_to_bf16(x);
-      } else if (dcodec == W_FP8) {
-        const float y = fminf(fmaxf(__fdiv_rn(x, s8), -448.0f), 448.0f);
-        code = f_to_e4m3(y);
-      } else {
-        const float q = __builtin_rintf(__fdiv_rn(x, sc[slot][tt][d / 32]));
-        code = (uint32_t)(int)fminf(fmaxf(q, (float)-qmax), (float)qmax);
-      }
-      if (dbits == 16) {
-        word[e >> 1] |= (code & 0xFFFFu) << (16 * (e & 1));
-      } else if (dbits == 8) {
-        word[e >> 2] |= (code & 0xFFu) << (8 * (e & 3));
-      } else {
-        const int r = e & 7, nslot = (r & 1) * 4 + (r >> 1);
-        word[e >> 3] |= (code & 0xFu) << (4 * nslot);
-      }
-    }
-    if (Rd >= 16) {
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c)
-        if (16 * c < Rd)
-        *reinterpret_cast<u4*>(td + run_byte(lane, 16 * c, Rd)) =
-            u4{word[4 * c], word[4 * c + 1], word[4 * c + 2], word[4 * c + 3]};
-    } else {   // INT4, D = 64: 8-byte runs
-      *reinterpret_cast<uint2*>(td + run_byte(lane, 0, Rd)) = uint2{word[0], word[1]};
-    }
+    if (is_v)
+      emit_any<D, true>(dcodec, xs[slot], scs[slot], s8, td, lane);
+    else
+      emit_any<D, false>(dcodec, xs[slot], scs[slot], s8, td, lane);
   }
 }
 
@@ -301,12 +341,20 @@ int launch_encode(const EncodeArgs& a, void* stream) {
   if (a.n == 0) return 0;
   const dim3 grid(a.n, a.hkv, 2);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (a.head_dim == 64)
-    hipLaunchKernelGGL(encode_kernel<64>, grid, dim3(ENC_THREADS), 0, s, a);
-  else if (a.head_dim == 128)
-    hipLaunchKernelGGL(encode_kernel<128>, grid, dim3(ENC_THREADS), 0, s, a);
-  else
+  const int tiles = a.page >= 64 ? 4 : a.page / 16;     // page is a multiple of 16
+  if (a.head_dim == 64) {
+    if (tiles >= 4) hipLaunchKernelGGL((encode_kernel<64, 4>), grid, dim3(256), 0, s, a);
+    else if (tiles == 3) hipLaunchKernelGGL((encode_kernel<64, 3>), grid, dim3(192), 0, s, a);
+    else if (tiles == 2) hipLaunchKernelGGL((encode_kernel<64, 2>), grid, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((encode_kernel<64, 1>), grid, dim3(64), 0, s, a);
+  } else if (a.head_dim == 128) {
+    if (tiles >= 4) hipLaunchKernelGGL((encode_kernel<128, 4>), grid, dim3(256), 0, s, a);
+    else if (tiles == 3) hipLaunchKernelGGL((encode_kernel<128, 3>), grid, dim3(192), 0, s, a);
+    else if (tiles == 2) hipLaunchKernelGGL((encode_kernel<128, 2>), grid, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((encode_kernel<128, 1>), grid, dim3(64), 0, s, a);
+  } else {
     return -2;
+  }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

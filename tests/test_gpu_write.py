@@ -198,3 +198,43 @@ def test_write_side_errors_are_counted_and_skipped():
     torch.cuda.synchronize()
     assert int(err.item()) == 3
     assert torch.equal(pool_t, before)
+
+
+@pytest.mark.parametrize("dst", [FP8, INT8, INT4])
+def test_encode_rounding_ties(dst):
+    """Values whose quotient lands exactly halfway between two codes: the
+    device rounds them like the oracle (to the even code)."""
+    print(f"case encode ties {dst}", flush=True)
+    hkv, P, D = 1, 16, 64
+    from oracle.encode import _E4M3_POS
+    if dst == FP8:
+        pos = _E4M3_POS
+        mids = (pos[:-1] + pos[1:]) / 2                  # 126 midpoints, all fp16-exact below 448
+        mids = mids[np.isfinite(mids.astype(np.float16))]
+        vals = np.concatenate([mids, -mids])
+        x = np.resize(vals, (P, D)).astype(np.float32)
+        x[0, 0] = 448.0                                  # absmax 448: s = 1 exactly, x / s = x
+    else:
+        qmax = 127 if dst == INT8 else 7
+        half = np.arange(-qmax, qmax) + 0.5              # k + 0.5 for every k in range
+        x = np.resize(np.concatenate([half, -half]), (P, D)).astype(np.float32)
+        x.reshape(P, D // 32, 32)[:, :, 0] = qmax        # absmax qmax in every group: s = 1
+    assert np.array_equal(x.astype(np.float16).astype(np.float32), x)
+    kb, _ = slay.encode_plane(np.stack([x])[None], FP16, v_order=False)
+    vb, _ = slay.encode_plane(np.stack([x])[None], FP16, v_order=True)
+    sk = align(slay.plane_bytes(FP16, hkv, P, D))
+    dk = align(slay.plane_bytes(dst, hkv, P, D))
+    pool = np.zeros(2 * sk + 2 * dk, np.uint8)
+    pool[:len(kb[0])], pool[sk:sk + len(vb[0])] = kb[0], vb[0]
+    koff = np.array([0, 2 * sk], np.uint64)
+    voff = np.array([sk, 2 * sk + dk], np.uint64)
+    codec = np.array([0x00, 0x77], np.uint8)
+    scale = np.zeros((2, hkv, 2), np.float32)
+    src, dst_ids = np.array([0], np.int32), np.array([1], np.int32)
+    pool_t, koff_t, voff_t, codec_t, scale_t, src_t, dst_t = to_dev(pool, koff, voff, codec, scale, src, dst_ids)
+    p = params(2, hkv, P, D, pool.size)
+    pkv.encode_pages(p, src_t, dst_t, dst | dst << 4, pool_t, koff_t, voff_t, codec_t, scale_t)
+    torch.cuda.synchronize()
+    ref, rs, rc = oracle_encode(pool, koff, voff, codec, scale, src, dst_ids, dst | dst << 4, hkv, P, D)
+    assert np.array_equal(pool_t.cpu().numpy(), ref)
+    assert np.array_equal(scale_t.cpu().numpy(), rs)
