@@ -34,14 +34,21 @@
  *
  * In-page layout (this library's definition). page_k_off[p] / page_v_off[p]
  * are byte offsets from page_pool to the K and V planes of physical page p;
- * both must be multiples of 16. A plane holds codes[Hkv][...] head after
- * head (each head's block is page_size * head_dim values), then, for the
- * INT codecs only, fp16 scales[Hkv][page_size][head_dim/32].
- *   K codes, per head: element (t, i) at index t*D + i.
- *   V codes, per head: element (t, i) at index
- *       (t/16)*16*D + ((t%16)/4*16 + i%16) * (D/16)*4 + (i/16)*4 + t%4.
- *   INT4: eight elements per 32-bit little-endian word, element r of the word
- *   in nibble slot (r%2)*4 + r/2 (even elements in the low half-word).
+ * both must be multiples of 16. A plane holds the codes of every KV head,
+ * head after head (page_size * head_dim codes each), then, for the INT codecs
+ * only, fp16 scales[Hkv][page_size][head_dim/32]. One head's codes are
+ * page_size/16 tiles of 16 tokens, tile after tile; a tile (16*D*bits/8
+ * bytes) is the register image of the 64 lanes of the wave that consumes it.
+ * Lane L (0..63) owns a run of D/4 consecutive elements, R = D*bits/32 bytes:
+ * with R >= 16 the runs are interleaved in 16-byte chunks (chunk c of lane L
+ * at byte c*1024 + 16*L of the tile), else run L sits at byte R*L. Element e
+ * of lane L's run holds, with tt the token within the tile:
+ *   K, FP16/BF16/FP8:  tt = L%16, dim = (D/4)*(L/16) + e;
+ *   K, INT8/INT4:      tt = L%16, dim = 32*(e/8) + 8*(L/16) + e%8;
+ *   V, every codec:    tt = 4*(L/16) + e%4, dim = 16*(e/4) + L%16.
+ * Elements are little-endian; INT4 packs eight elements per 32-bit word,
+ * element r of the word in nibble slot (r%2)*4 + r/2 (even elements in the
+ * low half-word).
  *
  * Threading and ownership. The caller owns every buffer (device memory
  * unless stated otherwise). Calls enqueue work on `stream` (a hipStream_t;

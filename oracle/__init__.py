@@ -27,6 +27,10 @@ What it computes (sources are the three pages' own sections):
 * Write side (``encode``): a new token appended into its 16-bit page, and
   full 16-bit pages re-encoded (demoted) to FP8 / INT8 / INT4 (ARGUS "v0.5"
   and "Adaptive activation"; FreeToken PR #499 update, item 1).
+* Chunked prefill (``prefill``): a chunk of new query tokens per row attends
+  the cache causally, window by window, and the windows' results are folded
+  by their log-sum-exp into an accumulator (PR #499 discussion, in-place host
+  K/V design).
 
 Pins live in ``tests/test_oracle_*.py``; see each function for what pins it.
 """
@@ -35,3 +39,4 @@ from .codecs import (decode_bf16, decode_fp16, decode_fp8_e4m3, decode_int4,  # 
 from .attention import decode_attention, fold, gather_kv, partials  # noqa: F401
 from .accounting import kv_bytes_per_token  # noqa: F401
 from .encode import append_token, encode_page  # noqa: F401
+from .prefill import fold_into, prefill_attention  # noqa: F401

@@ -202,3 +202,12 @@ def build_workload(name: str, *, rows: int, hq: int, hkv: int, dim: int, page: i
                     block_table=block_table, page_sel=page_sel, sel_lens=sel_lens,
                     page_k_off=page_k_off, page_v_off=page_v_off, page_codec=page_codec,
                     page_scale=page_scale, pool=pool, info=info)
+
+
+def prefill_queries(seed: int, rows: int, tokens: int, hq: int, dim: int, q_scale: float = 1.0) -> np.ndarray:
+    """float16 [rows, tokens, Hq, D]: the queries of a chunk of new tokens per
+    row, N(0, q_scale^2) before rounding, from a stream of their own (the
+    workload's streams are untouched)."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0x5052])))
+    x = g.standard_normal((rows, tokens, hq, dim), dtype=np.float32)
+    return (np.float32(q_scale) * x).astype(np.float16)
