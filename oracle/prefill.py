@@ -27,8 +27,10 @@ holds the result over the windows seen so far (both as (out, lse)):
     M = max(lse_a, lse_b);  w_a = exp(lse_a - M);  w_b = exp(lse_b - M)
     out = (w_a out_a + w_b out_b) / (w_a + w_b);  lse = M + ln(w_a + w_b)
 
-with both empty (-inf) giving (0, -inf). Folding the windows of a partition
-of the key range in any order gives the result over the whole range.
+with both empty (-inf) giving (0, -inf). An empty side holds no attended
+token, so it contributes no term: its out values are undefined and are
+never read into the result. Folding the windows of a partition of the key
+range in any order gives the result over the whole range.
 
 Pins: tests/test_oracle_prefill.py (torch SDPA with an explicit boolean mask
 in float64, the decode oracle at T = 1, closed forms of the causal edge,
@@ -85,5 +87,7 @@ def fold_into(acc_out, acc_lse, out, lse):
     wb = np.where(np.isfinite(bl), np.exp(bl - Ms), 0.0)
     den = wa + wb
     safe = np.where(finite, den, 1.0)
-    res = np.where(finite[..., None], (wa[..., None] * ao + wb[..., None] * bo) / safe[..., None], 0.0)
+    ta = np.where((wa > 0)[..., None], wa[..., None] * ao, 0.0)    # an empty side adds no term
+    tb = np.where((wb > 0)[..., None], wb[..., None] * bo, 0.0)
+    res = np.where(finite[..., None], (ta + tb) / safe[..., None], 0.0)
     return res, np.where(finite, Ms + np.log(safe), -np.inf)

@@ -171,6 +171,12 @@ def test_fold_into_identities():
     # the partial-result fold with unit sums: acc_p = out_p, m_p = lse_p, l_p = 1
     f_o, f_l = fold(np.stack([o1, o2], axis=1), np.stack([l1, l2], axis=1), np.ones((5, 2)))
     assert np.max(np.abs(x - f_o)) <= 1e-14 and np.max(np.abs(y - f_l)) <= 1e-14
+    # an empty side's values are undefined and never enter the result
+    junk = np.full((5, 8), np.nan)
+    a, b = fold_into(o1, l1, junk, empty_l)
+    assert np.array_equal(a, o1) and np.array_equal(b, l1)
+    a, b = fold_into(junk, empty_l, junk, empty_l)
+    assert np.all(a == 0) and np.all(b == -np.inf)
     # closed form: lse = ln(e^l1 + e^l2)
     assert np.max(np.abs(y - np.logaddexp(l1, l2))) <= 1e-14
 
