@@ -266,6 +266,66 @@ int pkv_encode_pages(const pkv_params* p, int32_t n, const int32_t* src_pages, c
                      const uint64_t* page_v_off, uint8_t* page_codec, float* page_scale, int32_t* err_count,
                      void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Chunked prefill: a chunk of new query tokens per row attends the cache,
+ * window by window, with the windows folded by their log-sum-exp into an
+ * fp32 accumulator (FreeToken PR #499 discussion, in-place host K/V design;
+ * ARGUS "Why decode is slow" for grouped-query attention).
+ *
+ * The chunk's T = q_tokens tokens have already been appended, so they are
+ * the last T of row b's L = seq_lens[b] tokens: query t sits at position
+ * pos = L - T + t and attends, causally, the keys
+ *
+ *     j in [kv_begin, min(kv_end, pos + 1))        (kv_end < 0: no bound)
+ *
+ * with the scores, softmax, out and lse of pkv_decode_attention (natural-log
+ * lse; an empty key set, e.g. pos < 0 when T > L, gives out = 0 and
+ * lse = -inf). With T = 1 and the whole range this is the decode result. The
+ * key range is split into partitions of partition_tokens (0: chosen by the
+ * library) starting at kv_begin rounded down to a page boundary; their
+ * partials are folded as by pkv_lse_combine.
+ *
+ * Dense mode only: max_sel_pages must be 0. Codecs, the page tables, the
+ * device-visible error counting and the threading rules are those of
+ * pkv_decode_attention (each bad page is counted once per partition and
+ * row).
+ */
+
+/* Partitions of the key range for this call (>= 1), or a negative status. */
+int pkv_prefill_num_partitions(const pkv_params* p, int32_t q_tokens, int32_t kv_begin, int32_t kv_end);
+
+/* Device workspace bytes pkv_prefill_attention needs:
+ * rows*q_tokens*Hq*partitions*(D + 2)*4 when partitions > 1, else 0 (also 0
+ * for invalid arguments; the call then reports the error). */
+size_t pkv_prefill_workspace_bytes(const pkv_params* p, int32_t q_tokens, int32_t kv_begin, int32_t kv_end);
+
+/*   q          fp16 [B][q_tokens][Hq][D], 16-byte aligned.
+ *   out        fp32 [B][q_tokens][Hq][D] (written).
+ *   lse        fp32 [B][q_tokens][Hq] (written).
+ *   workspace  pkv_prefill_workspace_bytes() bytes, 16-byte aligned (NULL when 0).
+ * Other arguments as for pkv_decode_attention. Returns PKV_ERR_INVALID_ARG for
+ * q_tokens < 0, kv_begin < 0, 0 <= kv_end < kv_begin or max_sel_pages != 0. */
+int pkv_prefill_attention(const pkv_params* p, int32_t q_tokens, int32_t kv_begin, int32_t kv_end,
+                          const void* q, const uint8_t* page_pool, const uint64_t* page_k_off,
+                          const uint64_t* page_v_off, const uint8_t* page_codec, const float* page_scale,
+                          const int32_t* block_table, const int32_t* seq_lens, float* out, float* lse,
+                          void* workspace, size_t workspace_bytes, int32_t* err_count, void* stream);
+
+/* Folds one window's result into a running accumulator, in place (PR #499
+ * discussion: windows folded by log-sum-exp into an fp32 accumulator). Per
+ * row r, with M = max(acc_lse[r], lse[r]), w_a = exp(acc_lse[r] - M) and
+ * w_b = exp(lse[r] - M):
+ *
+ *   acc_out[r] = (w_a acc_out[r] + w_b out[r]) / (w_a + w_b)
+ *   acc_lse[r] = M + ln(w_a + w_b)
+ *
+ * A side with lse = -inf contributes nothing (its out values are not read
+ * into the result); both -inf gives acc_out = 0, acc_lse = -inf. Start an
+ * accumulator with acc_lse = -inf. acc_out, out fp32 [rows][head_dim];
+ * acc_lse, lse fp32 [rows]; 4-byte aligned; 1 <= head_dim <= 512. */
+int pkv_lse_fold_into(int32_t rows, int32_t head_dim, float* acc_out, float* acc_lse, const float* out,
+                      const float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

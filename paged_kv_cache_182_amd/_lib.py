@@ -21,7 +21,8 @@ FP16, BF16, FP8_E4M3, INT8_G32, INT4_G32, CODEC_MIXED = 0, 1, 2, 3, 4, -1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "pkv_num_partitions",
            "pkv_workspace_bytes", "pkv_decode_attention", "pkv_decode_partials",
-           "pkv_lse_combine", "pkv_append_kv", "pkv_encode_pages")
+           "pkv_lse_combine", "pkv_append_kv", "pkv_encode_pages", "pkv_prefill_num_partitions",
+           "pkv_prefill_workspace_bytes", "pkv_prefill_attention", "pkv_lse_fold_into")
 
 
 class PkvError(RuntimeError):
@@ -71,6 +72,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_append_kv.argtypes = [pp] + [vp] * 10
     lib.pkv_encode_pages.restype = ctypes.c_int
     lib.pkv_encode_pages.argtypes = [pp, i32, vp, vp, i32] + [vp] * 7
+    lib.pkv_prefill_num_partitions.restype = ctypes.c_int
+    lib.pkv_prefill_num_partitions.argtypes = [pp, i32, i32, i32]
+    lib.pkv_prefill_workspace_bytes.restype = sz
+    lib.pkv_prefill_workspace_bytes.argtypes = [pp, i32, i32, i32]
+    lib.pkv_prefill_attention.restype = ctypes.c_int
+    lib.pkv_prefill_attention.argtypes = [pp, i32, i32, i32] + [vp] * 10 + [vp, sz, vp, vp]
+    lib.pkv_lse_fold_into.restype = ctypes.c_int
+    lib.pkv_lse_fold_into.argtypes = [i32, i32, vp, vp, vp, vp, vp]
     if lib.pkv_abi_version() != 1:
         raise RuntimeError("libpkv ABI version mismatch")
     _lib = lib
@@ -237,6 +246,69 @@ def encode_pages(p: Params, src_pages, dst_pages, dst_codec: int, page_pool, pag
         _stream(stream))
     if st != OK:
         raise PkvError(st, "pkv_encode_pages")
+
+
+def prefill_num_partitions(p: Params, q_tokens: int, kv_begin: int = 0, kv_end: int = -1) -> int:
+    n = load().pkv_prefill_num_partitions(ctypes.byref(p), int(q_tokens), int(kv_begin), int(kv_end))
+    if n < 0:
+        raise PkvError(n, "pkv_prefill_num_partitions")
+    return n
+
+
+def prefill_workspace_bytes(p: Params, q_tokens: int, kv_begin: int = 0, kv_end: int = -1) -> int:
+    return int(load().pkv_prefill_workspace_bytes(ctypes.byref(p), int(q_tokens), int(kv_begin), int(kv_end)))
+
+
+def prefill_attention(p: Params, q, page_pool, page_k_off, page_v_off, page_codec, page_scale, block_table,
+                      seq_lens, *, kv_begin: int = 0, kv_end: int = -1, out=None, lse=None, workspace=None,
+                      err_count=None, stream=None):
+    """Enqueue pkv_prefill_attention: q fp16 [rows, T, Hq, D], the last T
+    tokens of each row. Returns (out [rows, T, Hq, D], lse [rows, T, Hq]);
+    allocates them (and the workspace) with torch when not given."""
+    lib = load()
+    dev = q.device
+    if dev.type != "cuda" or q.dim() != 4:
+        raise ValueError("q must be a device tensor [rows, T, Hq, D]")
+    T = int(q.shape[1])
+    if out is None:
+        out = torch.empty((p.num_rows, T, p.num_q_heads, p.head_dim), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((p.num_rows, T, p.num_q_heads), dtype=torch.float32, device=dev)
+    need = prefill_workspace_bytes(p, T, kv_begin, kv_end)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = 0 if workspace is None else _ptr(workspace, torch.uint8, "workspace", dev)
+    ws_len = 0 if workspace is None else workspace.numel()
+    st = lib.pkv_prefill_attention(
+        ctypes.byref(p), T, int(kv_begin), int(kv_end), _ptr(q, torch.float16, "q", dev),
+        _ptr(page_pool, torch.uint8, "page_pool", dev),
+        _ptr(page_k_off, torch.uint64, "page_k_off", dev),
+        _ptr(page_v_off, torch.uint64, "page_v_off", dev),
+        _ptr(page_codec, torch.uint8, "page_codec", dev),
+        _ptr(page_scale, torch.float32, "page_scale", dev),
+        _ptr(block_table, torch.int32, "block_table", dev),
+        _ptr(seq_lens, torch.int32, "seq_lens", dev),
+        _ptr(out, torch.float32, "out", dev), _ptr(lse, torch.float32, "lse", dev),
+        ws_ptr, ws_len, _ptr(err_count, torch.int32, "err_count", dev), _stream(stream))
+    if st != OK:
+        raise PkvError(st, "pkv_prefill_attention")
+    return out, lse
+
+
+def lse_fold_into(acc_out, acc_lse, out, lse, stream=None) -> None:
+    """Enqueue pkv_lse_fold_into: fold (out, lse) into (acc_out, acc_lse) in
+    place; acc_out/out [..., D], acc_lse/lse [...]."""
+    lib = load()
+    dev = acc_out.device
+    d = int(acc_out.shape[-1])
+    rows = int(acc_lse.numel())
+    if acc_out.numel() != rows * d or out.numel() != rows * d or lse.numel() != rows:
+        raise ValueError("lse_fold_into: shapes do not match")
+    st = lib.pkv_lse_fold_into(rows, d, _ptr(acc_out, torch.float32, "acc_out", dev),
+                               _ptr(acc_lse, torch.float32, "acc_lse", dev), _ptr(out, torch.float32, "out", dev),
+                               _ptr(lse, torch.float32, "lse", dev), _stream(stream))
+    if st != OK:
+        raise PkvError(st, "pkv_lse_fold_into")
 
 
 def hip_runtime_copies() -> list[str]:

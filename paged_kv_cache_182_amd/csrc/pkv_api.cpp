@@ -302,3 +302,139 @@ int pkv_encode_pages(const pkv_params* p, int32_t n, const int32_t* src_pages, c
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ chunked prefill
+namespace {
+
+constexpr int kPrefillCols = 128;  // query columns (token, head-of-group pairs) per workgroup
+
+struct PrefillPlan {
+  int64_t base, end;        // partitions cover [base, end): base = kv_begin rounded down to a page
+  int64_t part_tokens;
+  int64_t nparts;
+  int64_t col_groups;
+};
+
+// Validates the prefill-specific values and sizes the partitions.
+int plan_prefill(const pkv_params* p, int32_t q_tokens, int32_t kv_begin, int32_t kv_end, PrefillPlan* pl) {
+  int st = check_params(p);
+  if (st != PKV_OK) return st;
+  if (p->max_sel_pages != 0) return PKV_ERR_INVALID_ARG;  // the prefill attends the dense cache
+  if (q_tokens < 0 || kv_begin < 0 || (kv_end >= 0 && kv_end < kv_begin)) return PKV_ERR_INVALID_ARG;
+  const int64_t cap = (int64_t)p->max_pages_per_row * p->page_size;
+  pl->base = (int64_t)kv_begin / p->page_size * p->page_size;
+  pl->end = kv_end < 0 ? cap : (kv_end < cap ? kv_end : cap);
+  const int64_t span = pl->end > pl->base ? pl->end - pl->base : 0;
+  const int64_t cols = (int64_t)q_tokens * (p->num_q_heads / p->num_kv_heads);
+  pl->col_groups = cols > 0 ? (cols + kPrefillCols - 1) / kPrefillCols : 1;
+  if (p->partition_tokens > 0) {
+    pl->part_tokens = p->partition_tokens;
+  } else {
+    const int64_t units = (int64_t)(p->num_rows > 0 ? p->num_rows : 1) * p->num_kv_heads * pl->col_groups;
+    int64_t parts = (kWorkgroupsWanted + units - 1) / units;
+    if (parts < 1) parts = 1;
+    int64_t pt = (span + parts - 1) / parts;
+    if (pt < kMinPartitionTokens) pt = kMinPartitionTokens;
+    pt = (pt + p->page_size - 1) / p->page_size * p->page_size;
+    pl->part_tokens = pt;
+  }
+  pl->nparts = span > 0 ? (span + pl->part_tokens - 1) / pl->part_tokens : 1;
+  if (pl->nparts < 1) pl->nparts = 1;
+  if (pl->end > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_prefill_num_partitions(const pkv_params* p, int32_t q_tokens, int32_t kv_begin, int32_t kv_end) {
+  PrefillPlan pl;
+  const int st = plan_prefill(p, q_tokens, kv_begin, kv_end, &pl);
+  if (st != PKV_OK) return st;
+  return pl.nparts > 0x7fffffff ? PKV_ERR_UNSUPPORTED : (int)pl.nparts;
+}
+
+size_t pkv_prefill_workspace_bytes(const pkv_params* p, int32_t q_tokens, int32_t kv_begin, int32_t kv_end) {
+  PrefillPlan pl;
+  if (plan_prefill(p, q_tokens, kv_begin, kv_end, &pl) != PKV_OK || pl.nparts <= 1) return 0;
+  return (size_t)p->num_rows * q_tokens * p->num_q_heads * pl.nparts * (p->head_dim + 2) * sizeof(float);
+}
+
+int pkv_prefill_attention(const pkv_params* p, int32_t q_tokens, int32_t kv_begin, int32_t kv_end,
+                          const void* q, const uint8_t* page_pool, const uint64_t* page_k_off,
+                          const uint64_t* page_v_off, const uint8_t* page_codec, const float* page_scale,
+                          const int32_t* block_table, const int32_t* seq_lens, float* out, float* lse,
+                          void* workspace, size_t workspace_bytes, int32_t* err_count, void* stream) {
+  PrefillPlan pl;
+  int st = plan_prefill(p, q_tokens, kv_begin, kv_end, &pl);
+  if (st != PKV_OK) return st;
+  if (p->num_rows == 0 || q_tokens == 0) return PKV_OK;
+  if (!q || !page_pool || !page_k_off || !page_v_off || !page_codec || !block_table || !seq_lens || !out || !lse)
+    return PKV_ERR_INVALID_ARG;
+  if ((p->k_codec == PKV_FP8_E4M3 || p->v_codec == PKV_FP8_E4M3) && !page_scale) return PKV_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(page_pool, 256) || !aligned(page_k_off, 8) || !aligned(page_v_off, 8) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(out, 4) || !aligned(lse, 4) ||
+      (page_scale && !aligned(page_scale, 4)) || (err_count && !aligned(err_count, 4)))
+    return PKV_ERR_INVALID_ARG;
+  const int64_t gx = (pl.nparts + 7) / 8 * 8 * pl.col_groups;
+  if (gx > 0x7fffffff || p->num_rows > 65535 || p->num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)p->num_rows * q_tokens * p->num_q_heads;
+  if (rows > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+
+  pkv::PrefillArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.pool = page_pool;
+  a.koff = page_k_off;
+  a.voff = page_v_off;
+  a.codec = page_codec;
+  a.scale = page_scale;
+  a.bt = block_table;
+  a.seq_lens = seq_lens;
+  a.err = err_count;
+  a.rows = p->num_rows;
+  a.tokens = q_tokens;
+  a.hq = p->num_q_heads;
+  a.hkv = p->num_kv_heads;
+  a.group = p->num_q_heads / p->num_kv_heads;
+  a.page = p->page_size;
+  a.num_pages = p->num_pages;
+  a.max_pages = p->max_pages_per_row;
+  a.kv_begin = kv_begin;
+  a.kv_end = (int32_t)pl.end;
+  a.part_base = (int32_t)pl.base;
+  a.part_tokens = (int32_t)pl.part_tokens;
+  a.nparts = (int32_t)pl.nparts;
+  a.col_groups = (int32_t)pl.col_groups;
+  a.k_codec = p->k_codec;
+  a.v_codec = p->v_codec;
+  a.scale_log2 = p->softmax_scale * 1.44269504088896340736f;
+  a.pool_bytes = p->pool_bytes;
+  if (pl.nparts > 1) {
+    const size_t need = pkv_prefill_workspace_bytes(p, q_tokens, kv_begin, kv_end);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return PKV_ERR_WORKSPACE;
+    a.part_acc = static_cast<float*>(workspace);
+    a.part_ml = a.part_acc + (size_t)rows * pl.nparts * p->head_dim;
+    a.final_out = 0;
+  } else {
+    a.out = out;
+    a.lse = lse;
+    a.final_out = 1;
+  }
+  st = launch_status(pkv::launch_prefill(a, p->head_dim, stream));
+  if (st != PKV_OK || pl.nparts == 1) return st;
+  return launch_status(
+      pkv::launch_combine((int)rows, a.nparts, p->head_dim, a.part_acc, a.part_ml, out, lse, stream));
+}
+
+int pkv_lse_fold_into(int32_t rows, int32_t head_dim, float* acc_out, float* acc_lse, const float* out,
+                      const float* lse, void* stream) {
+  if (rows < 0 || head_dim < 1 || head_dim > 512) return PKV_ERR_INVALID_ARG;
+  if (rows == 0) return PKV_OK;
+  if (!acc_out || !acc_lse || !out || !lse) return PKV_ERR_INVALID_ARG;
+  if (!aligned(acc_out, 4) || !aligned(acc_lse, 4) || !aligned(out, 4) || !aligned(lse, 4))
+    return PKV_ERR_INVALID_ARG;
+  return pkv::launch_fold_into(rows, head_dim, acc_out, acc_lse, out, lse, stream) == 0 ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // extern "C"

@@ -63,6 +63,37 @@ struct EncodeArgs {
   uint64_t pool_bytes;
 };
 
+// Chunked-prefill attention (pkv_prefill_attention).
+struct PrefillArgs {
+  const uint16_t* q;        // fp16 [B][T][Hq][D]
+  const uint8_t* pool;
+  const uint64_t* koff;
+  const uint64_t* voff;
+  const uint8_t* codec;
+  const float* scale;       // [num_pages][Hkv][2] or nullptr
+  const int32_t* bt;        // [B][max_pages]
+  const int32_t* seq_lens;  // [B]
+  float* out;               // [B][T][Hq][D]   (final_out)
+  float* lse;               // [B][T][Hq]      (final_out)
+  float* part_acc;          // [B*T*Hq][nparts][D]
+  float* part_ml;           // [B*T*Hq][nparts][2]
+  int32_t* err;
+  int32_t rows, tokens, hq, hkv, group, page, num_pages, max_pages;
+  int32_t kv_begin;         // first key position attended (>= 0)
+  int32_t kv_end;           // one past the last key position (already capped at max_pages * page)
+  int32_t part_base;        // kv_begin rounded down to a page boundary: partitions start here
+  int32_t part_tokens;      // a multiple of page
+  int32_t nparts, col_groups, final_out;
+  int32_t k_codec, v_codec; // declared codecs, -1 for any
+  float scale_log2;
+  uint64_t pool_bytes;
+};
+
+int launch_prefill(const PrefillArgs& a, int head_dim, void* stream);
+// acc <- log-sum-exp fold of (acc, (out, lse)), rows of head_dim values.
+int launch_fold_into(int rows, int head_dim, float* acc_out, float* acc_lse, const float* out,
+                     const float* lse, void* stream);
+
 int launch_append(const AppendArgs& a, void* stream);
 int launch_encode(const EncodeArgs& a, void* stream);
 

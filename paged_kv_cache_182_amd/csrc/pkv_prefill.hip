@@ -1,0 +1,627 @@
+// Chunked-prefill attention over the mixed-codec paged cache, gfx950, and
+// the log-sum-exp fold of one window's result into an accumulator.
+//
+// A chunk of T new query tokens per row has been appended to the cache; query
+// t sits at position L - T + t and attends, causally, the cached keys up to
+// its own position, restricted to a key window [kv_begin, kv_end). The key
+// range is cut into partitions attended in parallel and folded by their
+// log-sum-exp (FreeToken PR #499 discussion, in-place host K/V design: a
+// prefill attends window by window and folds the windows into an fp32
+// accumulator; ARGUS "Why decode is slow" for grouped-query attention).
+//
+// Work unit: one workgroup of four waves owns (partition, KV head, row, group
+// of 128 query columns), a column being one (query token, query head of the
+// KV head's group) pair; each wave owns 32 columns. Every 16-token tile of
+// the partition is converted once, by the whole workgroup, from its page
+// codes into an fp16 image in LDS (double-buffered, one barrier per tile);
+// each wave then reads the image as MFMA operands:
+//  * scores: v_mfma_f32_16x16x32_f16, A = K (row = token, 8 dims per lane),
+//    B = q^T (col = query column); lane l gets tokens 4*(l/16) + j of column
+//    l % 16. The K image keeps dims in natural order: step c of lane l holds
+//    dims 32c + 8(l/16) .. +7, so one 32-dim step is one INT scale group.
+//  * P.V: v_mfma_f32_16x16x16_f16, A = P (the same four scores), B = V (four
+//    tokens of one dim, the V layout of every codec).
+// Codes convert to fp16 exactly. Scales stay in fp32 as in the decode path:
+// FP8 K scales multiply the scores, INT K group scales weight one score
+// accumulator per group, V scales multiply P (FP8 through an fp16 high and
+// low part, INT group scales per group), so a weight of 1 stays exact.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+enum : int { C_FP16 = 0, C_BF16 = 1, C_FP8 = 2, C_INT8 = 3, C_INT4 = 4 };
+
+constexpr int WAVES = 4;
+constexpr int THREADS = 64 * WAVES;
+constexpr int NBC = 2;                    // 16-column blocks per wave
+constexpr int COLS = 16 * NBC * WAVES;    // query columns per workgroup
+constexpr int RING = 2;                   // tiles of codes in flight per thread
+constexpr float NEG_INF = -__builtin_huge_valf();
+constexpr float LN2 = 0.693147180559945309f;
+
+__host__ __device__ constexpr int bits_of(int c) { return c <= C_BF16 ? 16 : (c == C_INT4 ? 4 : 8); }
+__host__ __device__ constexpr bool is_int(int c) { return c == C_INT8 || c == C_INT4; }
+
+__device__ inline uint64_t plane_bytes(int c, int hkv, int page, int d) {
+  const uint64_t codes = (uint64_t)hkv * page * d * bits_of(c) / 8;
+  return codes + (is_int(c) ? (uint64_t)hkv * page * (d / 32) * 2 : 0);
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int RSRC_WORD3 = 0x00020000;  // gfx9-family raw buffer format
+constexpr int CPOL_NT = 2;              // non-temporal
+constexpr uint32_t OFF_NONE = 0xFFFFFF00u;
+
+__device__ inline rsrc_t make_rsrc(const uint8_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, RSRC_WORD3);
+}
+
+__device__ inline void count_error(int32_t* err) {
+  if (err) atomicAdd(err, 1);
+}
+
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---------------------------------------------------------------- codes -> fp16
+__device__ inline h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
+
+__device__ inline uint32_t bf16x2_to_h2(uint32_t w) {
+  const float lo = __builtin_bit_cast(float, w << 16);
+  const float hi = __builtin_bit_cast(float, w & 0xffff0000u);
+  return __builtin_bit_cast(uint32_t, h2{(_Float16)lo, (_Float16)hi});
+}
+
+template <bool HI>
+__device__ inline uint32_t fp8x2_to_h2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+// four int8 codes -> four fp16 (two words): 0x64XX is 1024 + XX, XX = code + 128
+__device__ inline u2 int8x4_to_h4(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  const h2 off = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const h2 a = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - off;
+  const h2 b = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - off;
+  return u2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+}
+
+// eight int4 codes of one word (element r in nibble slot (r%2)*4 + r/2) ->
+// eight fp16 in element order. Masking a nibble under the fp16 pattern of
+// 1024 and flipping its top bit gives 1024 + (c + 8) or 1024 + 16 (c + 8).
+__device__ inline u4 int4x8_to_h8(uint32_t w) {
+  const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const h2 s16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const h2 off16 = {(_Float16)72.0f, (_Float16)72.0f};
+  const uint32_t u8 = w >> 8;
+  const h2 o0 = as_h2((w & 0x000f000fu) ^ 0x64086408u) - off;
+  const h2 o1 = __builtin_elementwise_fma(as_h2((w & 0x00f000f0u) ^ 0x64806480u), s16, -off16);
+  const h2 o2 = as_h2((u8 & 0x000f000fu) ^ 0x64086408u) - off;
+  const h2 o3 = __builtin_elementwise_fma(as_h2((u8 & 0x00f000f0u) ^ 0x64806480u), s16, -off16);
+  return u4{__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1), __builtin_bit_cast(uint32_t, o2),
+            __builtin_bit_cast(uint32_t, o3)};
+}
+
+// Eight consecutive run elements, raw (16, 8 or 4 bytes in the low words) ->
+// eight fp16.
+__device__ inline u4 to_h8(u4 r, int codec) {
+  switch (codec) {
+    case C_FP16: return r;
+    case C_BF16: return u4{bf16x2_to_h2(r[0]), bf16x2_to_h2(r[1]), bf16x2_to_h2(r[2]), bf16x2_to_h2(r[3])};
+    case C_FP8:
+      return u4{fp8x2_to_h2<false>(r[0]), fp8x2_to_h2<true>(r[0]), fp8x2_to_h2<false>(r[1]),
+                fp8x2_to_h2<true>(r[1])};
+    case C_INT8: {
+      const u2 a = int8x4_to_h4(r[0]), b = int8x4_to_h4(r[1]);
+      return u4{a[0], a[1], b[0], b[1]};
+    }
+    default: return int4x8_to_h8(r[0]);
+  }
+}
+
+// ---------------------------------------------------------------- tile staging
+// Per-tile values every thread holds alike (wave-uniform, so scalar).
+struct TileMeta {
+  uint64_t koff, voff;  // plane offsets of the page (0 when dead)
+  float sk, sv;         // FP8 scales of this KV head (1 otherwise)
+  int valid;            // tokens of the tile inside the row (0: dead tile)
+  int kc, vc;
+  int j0;               // position of the tile's first token
+};
+
+// Raw codes of one tile held by one thread: its K and V jobs (eight elements
+// each) and, for a few threads, 16 bytes of INT group scales.
+template <int D>
+struct Raw {
+  static constexpr int JOBS = D / 64;  // jobs per thread (K and V jobs together)
+  u4 x[JOBS];
+  u4 sc;
+};
+
+// Byte offset inside a tile of run byte rb of lane L (R run bytes).
+__device__ inline uint32_t run_byte(int L, int rb, int R) {
+  return R >= 16 ? (uint32_t)((rb >> 4) * 1024 + 16 * L + (rb & 15)) : (uint32_t)(R * L + rb);
+}
+
+template <int D>
+__device__ inline u4 load_bits(rsrc_t r, uint32_t off, int bits) {
+  if (bits == 16) return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CPOL_NT));
+  if (bits == 8) {
+    const u2 v = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, CPOL_NT));
+    return u4{v[0], v[1], 0u, 0u};
+  }
+  return u4{(uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, CPOL_NT), 0u, 0u, 0u};
+}
+
+// Job j of a tile: plane (K for j < 64*NC), run chunk c of eight elements,
+// lane L of the consuming wave. K jobs gather the eight dims 32c + 8(L/16) ..
+// of token L%16 (natural order) from wherever the page's K layout keeps them;
+// V jobs take run elements 8c .. 8c+7 of lane L (the V layout of every codec).
+template <int D>
+__device__ inline void job_source(int j, int kc, int vc, bool& is_v, int& c, int& L, int& bits, uint32_t& off) {
+  constexpr int NC = D / 32;
+  is_v = j >= 64 * NC;
+  const int jj = is_v ? j - 64 * NC : j;
+  c = jj >> 6;
+  L = jj & 63;
+  const int codec = is_v ? vc : kc;
+  bits = bits_of(codec);
+  const int R = D * bits / 32;
+  int Ls, e0;
+  if (is_v || is_int(codec)) {
+    Ls = L;
+    e0 = 8 * c;
+  } else {
+    const int d0 = 32 * c + 8 * (L >> 4);
+    Ls = 16 * (d0 / (D / 4)) + (L & 15);
+    e0 = d0 % (D / 4);
+  }
+  off = run_byte(Ls, e0 * bits / 8, R);
+}
+
+template <int D>
+__device__ inline void issue(Raw<D>& raw, const TileMeta& m, const PrefillArgs& a, int h, int tid) {
+  constexpr int NC = D / 32;
+  const bool live = m.valid > 0;
+  const int P = a.page;
+  const rsrc_t rk = make_rsrc(a.pool + m.koff, live ? (uint32_t)plane_bytes(m.kc, a.hkv, P, D) : 0u);
+  const rsrc_t rv = make_rsrc(a.pool + m.voff, live ? (uint32_t)plane_bytes(m.vc, a.hkv, P, D) : 0u);
+  const int sub = (m.j0 % P) / 16;
+  // INT group scales of the tile: 16 tokens x NC fp16 per plane, 16 bytes a thread
+  {
+    const bool kjob = tid < 2 * NC, vjob = tid >= 64 && tid < 64 + 2 * NC;
+    const int i = kjob ? tid : tid - 64;
+    const int codec = vjob ? m.vc : m.kc;
+    const uint32_t base = (uint32_t)((uint64_t)a.hkv * P * D * bits_of(codec) / 8) +
+                          (uint32_t)((h * P + 16 * sub) * NC * 2) + 16 * i;
+    const bool want = (kjob || vjob) && is_int(codec);
+    raw.sc = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(vjob ? rv : rk, (int)(want ? base : OFF_NONE),
+                                                                           0, 0));
+  }
+#pragma unroll
+  for (int q = 0; q < Raw<D>::JOBS; ++q) {
+    bool is_v;
+    int c, L, bits;
+    uint32_t off;
+    job_source<D>(tid + THREADS * q, m.kc, m.vc, is_v, c, L, bits, off);
+    const uint32_t head = (uint32_t)(h * P * D * bits / 8) + (uint32_t)(sub * 16 * D * bits / 8);
+    raw.x[q] = load_bits<D>(is_v ? rv : rk, head + off, bits);
+  }
+}
+
+// LDS image of one tile: K and V fp16 images (chunk c of lane L at c*1024 +
+// 16L bytes) and the INT group scales as fp32 [16 tokens][NC].
+template <int D>
+struct Stage {
+  static constexpr int IMG = 32 * D;  // bytes of one fp16 image (16 tokens x D)
+  static constexpr int SCL = 16 * (D / 32);
+  u4 k[IMG / 16];
+  u4 v[IMG / 16];
+  float ks[SCL];
+  float vs[SCL];
+};
+
+template <int D>
+__device__ inline void produce(const Raw<D>& raw, const TileMeta& m, Stage<D>& st, int tid) {
+  constexpr int NC = D / 32;
+#pragma unroll
+  for (int q = 0; q < Raw<D>::JOBS; ++q) {
+    const int j = tid + THREADS * q;
+    const bool is_v = j >= 64 * NC;
+    const int jj = is_v ? j - 64 * NC : j;
+    u4 x = to_h8(raw.x[q], is_v ? m.vc : m.kc);
+    if (is_v && m.valid < 16) {
+      // tokens past the row: zero values (their bytes may be anything)
+      const int L = jj & 63;
+      const int nv = min(max(m.valid - 4 * (L >> 4), 0), 4);  // live tokens of this lane: 4(L/16) + 0 .. nv-1
+      // element e = 8c + i holds token 4(L/16) + i%4; words hold elements (0,1), (2,3), ...
+      const uint32_t m01 = nv >= 2 ? ~0u : (nv == 1 ? 0x0000ffffu : 0u);
+      const uint32_t m23 = nv >= 4 ? ~0u : (nv == 3 ? 0x0000ffffu : 0u);
+      x = u4{x[0] & m01, x[1] & m23, x[2] & m01, x[3] & m23};
+    }
+    (is_v ? st.v : st.k)[jj] = x;
+  }
+  const bool kjob = tid < 2 * NC, vjob = tid >= 64 && tid < 64 + 2 * NC;
+  if (kjob || vjob) {
+    const int i = kjob ? tid : tid - 64;
+    const int codec = vjob ? m.vc : m.kc;
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w = raw.sc[e >> 1];
+      const uint16_t hbits = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+      // INT scale of (token (8i + e) / NC); zero past the row, 1 for other codecs
+      const int tok = (8 * i + e) / NC;
+      f[e] = !is_int(codec) ? 1.0f : (tok < m.valid ? (float)__builtin_bit_cast(_Float16, hbits) : 0.0f);
+    }
+    float* dst = (vjob ? st.vs : st.ks) + 8 * i;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e] = f[e];
+  }
+}
+
+__device__ inline f4 mfma32(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+__device__ inline f4 mfma16(h4 a, h4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
+
+// Max and sum over lanes l, l^16, l^32, l^48 (the rows holding one column);
+// the swap results are read from the builtin's vector and pinned by an empty
+// asm so the optimizer cannot merge the two halves.
+template <int ROWS>
+__device__ inline void swap_rows(float x, float& a, float& b) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  uint32_t lo, hi;
+  if constexpr (ROWS == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    lo = r[0]; hi = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = r[0]; hi = r[1];
+  }
+  asm volatile("" : "+v"(lo), "+v"(hi));
+  a = __builtin_bit_cast(float, lo);
+  b = __builtin_bit_cast(float, hi);
+}
+__device__ inline float row4_max(float x) {
+  float a, b;
+  swap_rows<16>(x, a, b);
+  swap_rows<32>(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ inline float row4_sum(float x) {
+  float a, b;
+  swap_rows<16>(x, a, b);
+  swap_rows<32>(a + b, a, b);
+  return a + b;
+}
+
+// ---------------------------------------------------------------- kernel
+template <int D>
+__global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
+  constexpr int NC = D / 32, NB = D / 16;
+  __shared__ Stage<D> stage[2];
+
+  // block -> (partition, column group): the column groups of one partition
+  // sit 8 blocks apart, on one XCD (blocks are dealt round-robin over the 8
+  // XCDs), so its pages are fetched into that XCD's L2 once.
+  const int id = blockIdx.x;
+  const int kk = id >> 3;
+  const int cg = kk % a.col_groups;
+  const int part = (kk / a.col_groups) * 8 + (id & 7);
+  if (part >= a.nparts) return;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, kq = lane >> 4;
+  const int G = a.group, T = a.tokens, P = a.page;
+  const int ncols = T * G;
+  // the last column group reaches the furthest keys, so it meets every page
+  // any group of this partition reads: it alone reports page errors
+  const bool reporter = h == 0 && cg == a.col_groups - 1 && tid == 0;
+
+  // ---- row extent
+  int L = a.seq_lens[b];
+  const bool bad_row = L < 0 || (int64_t)L > (int64_t)a.max_pages * P;
+  L = min(max(L, 0), a.max_pages * P);
+  if (bad_row && reporter && part == 0) count_error(a.err);
+
+  // ---- key range of this partition, and of this workgroup's columns
+  const int p_lo = max(a.part_base + part * a.part_tokens, a.kv_begin);
+  const int p_hi = min(min(a.part_base + (part + 1) * a.part_tokens, a.kv_end), L);
+  const int c_first = cg * COLS;
+  const int c_last = min(c_first + COLS, ncols) - 1;  // >= c_first: the host launches no empty group
+  const int wg_hi = min(p_hi, L - T + c_last / G + 1);
+  // this wave's columns
+  const int w_first = c_first + 32 * wave;
+  const int w_last = min(w_first + 32, ncols) - 1;
+  const bool wave_live = w_first < ncols;
+  const int w_hi_min = min(p_hi, L - T + w_first / G + 1);
+  const int w_hi_max = wave_live ? min(p_hi, L - T + w_last / G + 1) : p_lo;
+
+  // ---- q (B operand of the score MFMA), natural dim order
+  h8 qf[NBC][NC];
+  int hi_col[NBC];  // key limit of the lane's column in each block
+#pragma unroll
+  for (int cb = 0; cb < NBC; ++cb) {
+    const int c = w_first + 16 * cb + col;
+    const bool real = c < ncols;
+    const int t = real ? c / G : 0, g = real ? c % G : 0;
+    hi_col[cb] = real ? min(p_hi, L - T + t + 1) : p_lo;
+    const _Float16* qrow = reinterpret_cast<const _Float16*>(a.q) + (((size_t)b * T + t) * a.hq + (size_t)h * G + g) * D;
+#pragma unroll
+    for (int c2 = 0; c2 < NC; ++c2)
+      qf[cb][c2] = real ? *reinterpret_cast<const h8*>(qrow + 32 * c2 + 8 * kq) : h8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  float m_run[NBC], l_run[NBC];
+  f4 acc[NBC][NB];
+#pragma unroll
+  for (int cb = 0; cb < NBC; ++cb) {
+    m_run[cb] = NEG_INF;
+    l_run[cb] = 0.f;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[cb][n] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- tiles [t0, t1): 16-token tiles of the partition up to the last key
+  // any column of the workgroup attends
+  const int t0 = p_lo & ~15;
+  const int ntiles = wg_hi > p_lo ? (wg_hi - t0 + 15) / 16 : 0;
+
+  auto meta = [&](int i) {
+    TileMeta m;
+    m.j0 = t0 + 16 * i;
+    m.koff = 0; m.voff = 0; m.sk = 1.f; m.sv = 1.f; m.kc = 0; m.vc = 0; m.valid = 0;
+    if (i >= ntiles) return m;
+    const int lp = m.j0 / P;
+    const int pp = a.bt[(size_t)b * a.max_pages + lp];
+    bool ok = (unsigned)pp < (unsigned)a.num_pages;
+    const int pq = ok ? pp : 0;
+    const int cod = a.codec[pq];
+    const int kc = cod & 15, vc = cod >> 4;
+    const uint64_t ko = a.koff[pq], vo = a.voff[pq];
+    ok = ok && kc <= C_INT4 && vc <= C_INT4;
+    ok = ok && (a.k_codec < 0 || kc == a.k_codec) && (a.v_codec < 0 || vc == a.v_codec);
+    ok = ok && !((kc == C_FP8 || vc == C_FP8) && a.scale == nullptr) && ((ko | vo) & 15) == 0;
+    ok = ok && ko <= a.pool_bytes && a.pool_bytes - ko >= plane_bytes(kc, a.hkv, P, D);
+    ok = ok && vo <= a.pool_bytes && a.pool_bytes - vo >= plane_bytes(vc, a.hkv, P, D);
+    if (!ok) {
+      // one report per page: from the tile where the workgroup first meets it
+      if (reporter && (m.j0 % P == 0 || i == 0)) count_error(a.err);
+      return m;
+    }
+    m.kc = kc; m.vc = vc; m.koff = ko; m.voff = vo;
+    if (kc == C_FP8) m.sk = a.scale[((size_t)pq * a.hkv + h) * 2 + 0];
+    if (vc == C_FP8) m.sv = a.scale[((size_t)pq * a.hkv + h) * 2 + 1];
+    m.valid = min(L - m.j0, 16);
+    return m;
+  };
+
+  Raw<D> raw[RING];
+  TileMeta mt[RING];
+#pragma unroll
+  for (int s = 0; s < RING; ++s) {
+    mt[s] = meta(s);
+    issue<D>(raw[s], mt[s], a, h, tid);
+  }
+
+  const f4 zero = {0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < ntiles; it += RING) {
+#pragma unroll
+    for (int s = 0; s < RING; ++s) {
+      const int i = it + s;
+      if (i >= ntiles) break;
+      Stage<D>& st = stage[s & 1];  // RING is even: tile i uses buffer i % 2
+      const TileMeta m = mt[s];
+      if (m.valid > 0) produce<D>(raw[s], m, st, tid);
+      mt[s] = meta(i + RING);
+      issue<D>(raw[s], mt[s], a, h, tid);
+      lds_barrier();
+      if (m.valid <= 0 || !wave_live || m.j0 >= w_hi_max) continue;
+
+      // ---- operands of this tile
+      h8 kf[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kf[c] = __builtin_bit_cast(h8, st.k[64 * c + lane]);
+      h4 vf[NB];
+#pragma unroll
+      for (int c = 0; c < NB / 2; ++c) {
+        const u4 x = st.v[64 * c + lane];
+        vf[2 * c] = __builtin_bit_cast(h4, u2{x[0], x[1]});
+        vf[2 * c + 1] = __builtin_bit_cast(h4, u2{x[2], x[3]});
+      }
+      const bool kint = is_int(m.kc), vint = is_int(m.vc), vfp8 = m.vc == C_FP8;
+      float ksc[4][NC], vsc[4][NC];
+      if (kint) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int g = 0; g < NC; ++g) ksc[j][g] = st.ks[(4 * kq + j) * NC + g];
+      }
+      if (vint) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int g = 0; g < NC; ++g) vsc[j][g] = st.vs[(4 * kq + j) * NC + g];
+      }
+      const bool masked = m.j0 < p_lo || m.j0 + 16 > w_hi_min;
+      const float fk = a.scale_log2 * m.sk;
+
+#pragma unroll
+      for (int cb = 0; cb < NBC; ++cb) {
+        float s[4];
+        if (kint) {
+          f4 sg[NC];
+#pragma unroll
+          for (int c = 0; c < NC; ++c) sg[c] = mfma32(kf[c], qf[cb][c], zero);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float x = 0.f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) x += ksc[j][c] * sg[c][j];
+            s[j] = x * a.scale_log2;
+          }
+        } else {
+          f4 sa = zero;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) sa = mfma32(kf[c], qf[cb][c], sa);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s[j] = sa[j] * fk;
+        }
+        if (masked) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int pos = m.j0 + 4 * kq + j;
+            s[j] = (pos >= p_lo && pos < hi_col[cb]) ? s[j] : NEG_INF;
+          }
+        }
+        const float mx = row4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+        const float m_new = fmaxf(m_run[cb], mx);
+        if (__any(m_new > m_run[cb])) {
+          const float alpha = m_new > m_run[cb] ? __builtin_amdgcn_exp2f(m_run[cb] - m_new) : 1.0f;
+          l_run[cb] *= alpha;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float aj = __shfl(alpha, 4 * kq + j);
+#pragma unroll
+            for (int n = 0; n < NB; ++n) acc[cb][n][j] *= aj;
+          }
+          m_run[cb] = m_new;
+        }
+        const float mu = m_run[cb] == NEG_INF ? 0.f : m_run[cb];
+        float p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(s[j] - mu);
+        l_run[cb] += (p[0] + p[1]) + (p[2] + p[3]);
+
+        if (vint) {
+          h4 pa[NC];
+#pragma unroll
+          for (int g = 0; g < NC; ++g)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pa[g][j] = (_Float16)(p[j] * vsc[j][g]);
+#pragma unroll
+          for (int n = 0; n < NB; ++n) acc[cb][n] = mfma16(pa[n / 2], vf[n], acc[cb][n]);
+        } else if (vfp8) {
+          h4 hi, lo;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x = p[j] * m.sv;
+            hi[j] = (_Float16)x;
+            lo[j] = (_Float16)(x - (float)hi[j]);
+          }
+#pragma unroll
+          for (int n = 0; n < NB; ++n) {
+            acc[cb][n] = mfma16(hi, vf[n], acc[cb][n]);
+            acc[cb][n] = mfma16(lo, vf[n], acc[cb][n]);
+          }
+        } else {
+          const h4 pa = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+#pragma unroll
+          for (int n = 0; n < NB; ++n) acc[cb][n] = mfma16(pa, vf[n], acc[cb][n]);
+        }
+      }
+    }
+  }
+  if (!wave_live) return;
+
+  // ---- results: lane holds out[column 16cb + 4kq + j][dim 16n + col]
+#pragma unroll
+  for (int cb = 0; cb < NBC; ++cb) {
+    const float l_tot = row4_sum(l_run[cb]);
+    // own column (lanes of row 0 write lse / (m, l))
+    {
+      const int c = w_first + 16 * cb + col;
+      if (kq == 0 && c < ncols) {
+        const int t = c / G, g = c % G;
+        const size_t r = ((size_t)b * T + t) * a.hq + (size_t)h * G + g;
+        if (a.final_out) {
+          a.lse[r] = l_tot > 0.f ? m_run[cb] * LN2 + logf(l_tot) : NEG_INF;
+        } else {
+          const size_t pi = r * a.nparts + part;
+          a.part_ml[2 * pi + 0] = l_tot > 0.f ? m_run[cb] * LN2 : NEG_INF;
+          a.part_ml[2 * pi + 1] = l_tot;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lj = __shfl(l_tot, 4 * kq + j);
+      const int c = w_first + 16 * cb + 4 * kq + j;
+      if (c >= ncols) continue;
+      const int t = c / G, g = c % G;
+      const size_t r = ((size_t)b * T + t) * a.hq + (size_t)h * G + g;
+      if (a.final_out) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n) a.out[r * D + 16 * n + col] = lj > 0.f ? acc[cb][n][j] / lj : 0.f;
+      } else {
+        float* dst = a.part_acc + (r * a.nparts + part) * D;
+#pragma unroll
+        for (int n = 0; n < NB; ++n) dst[16 * n + col] = acc[cb][n][j];
+      }
+    }
+  }
+}
+
+// acc <- fold(acc, (out, lse)); one 64-lane block per row.
+__global__ void __launch_bounds__(64) fold_into_kernel(int rows, int D, float* acc_out, float* acc_lse,
+                                                       const float* out, const float* lse) {
+  for (int r = blockIdx.x; r < rows; r += gridDim.x) {
+    const float la = acc_lse[r], lb = lse[r];
+    const float M = fmaxf(la, lb);
+    float wa = 0.f, wb = 0.f;
+    if (M != NEG_INF) {
+      wa = la == NEG_INF ? 0.f : expf(la - M);
+      wb = lb == NEG_INF ? 0.f : expf(lb - M);
+    }
+    const float den = wa + wb;
+    for (int d = threadIdx.x; d < D; d += 64) {
+      // an empty side contributes nothing, whatever its values hold
+      const size_t i = (size_t)r * D + d;
+      const float x = (wa > 0.f ? wa * acc_out[i] : 0.f) + (wb > 0.f ? wb * out[i] : 0.f);
+      acc_out[i] = M == NEG_INF ? 0.f : x / den;
+    }
+    if (threadIdx.x == 0) acc_lse[r] = M == NEG_INF ? NEG_INF : M + logf(den);
+  }
+}
+
+}  // namespace
+
+int launch_prefill(const PrefillArgs& a, int head_dim, void* stream) {
+  if (a.rows == 0 || a.tokens == 0) return 0;
+  const long long gx = (long long)((a.nparts + 7) / 8) * 8 * a.col_groups;
+  const dim3 grid((unsigned)gx, a.hkv, a.rows);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (head_dim == 64)
+    hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(THREADS), 0, s, a);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(THREADS), 0, s, a);
+  else
+    return -2;
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_fold_into(int rows, int head_dim, float* acc_out, float* acc_lse, const float* out, const float* lse,
+                     void* stream) {
+  if (rows == 0) return 0;
+  const int grid = rows < 65536 ? rows : 65536;
+  hipLaunchKernelGGL(fold_into_kernel, dim3(grid), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), rows,
+                     head_dim, acc_out, acc_lse, out, lse);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // namespace pkv

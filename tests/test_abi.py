@@ -131,3 +131,56 @@ def test_encode_host_checks():
     assert lib.pkv_encode_pages(ctypes.byref(p), 4, 4096, 4096, 0x22, 4096, 4096, 4096, 4096, 0, 0, 0) == -1  # FP8 needs scales
     assert lib.pkv_encode_pages(ctypes.byref(p), 4, 0, 4096, 0x43, *args, 0, 0) == -1      # src missing
     assert lib.pkv_encode_pages(ctypes.byref(wbase(head_dim=256)), 4, 4096, 4096, 0x43, *args, 0, 0) == -2
+
+
+def pcall(p, T=16, kv_begin=0, kv_end=-1, **ptrs):
+    """pkv_prefill_attention with fake (never dereferenced) pointers; only for
+    arguments the host check must reject before any launch."""
+    names = ["q", "pool", "koff", "voff", "codec", "scale", "bt", "lens", "out", "lse"]
+    vals = {n: 4096 for n in names}
+    vals.update(ptrs)
+    ws = vals.pop("ws", 0)
+    wsb = vals.pop("wsb", 0)
+    return pkv.load().pkv_prefill_attention(ctypes.byref(p), T, kv_begin, kv_end, *[vals[n] for n in names],
+                                            ws, wsb, 0, 0)
+
+
+def test_prefill_partitions_and_workspace():
+    p = base(partition_tokens=8192)                     # 1M tokens of 64-token pages
+    assert pkv.prefill_num_partitions(p, 64) == 128
+    assert pkv.prefill_workspace_bytes(p, 64) == 64 * 16 * 128 * 130 * 4
+    # partitions start at kv_begin rounded down to a page and end at kv_end
+    assert pkv.prefill_num_partitions(p, 64, 100, 8192 + 64) == 1   # [64, 8256): one partition
+    assert pkv.prefill_num_partitions(p, 64, 100, 8192 + 65) == 2
+    assert pkv.prefill_num_partitions(p, 64, 8192, 8192 * 2) == 1
+    assert pkv.prefill_workspace_bytes(p, 64, 8192, 8192 * 2) == 0
+    auto = base(partition_tokens=0)
+    n = pkv.prefill_num_partitions(auto, 64)           # 4 column groups x 2 KV heads
+    assert n >= 128 and 8 * n >= 1024
+    assert pkv.prefill_num_partitions(auto, 64, 5, 5) == 1   # empty window
+
+
+def test_prefill_host_checks():
+    p = base()
+    lib = pkv.load()
+    assert lib.pkv_prefill_num_partitions(ctypes.byref(p), -1, 0, -1) == -1
+    assert lib.pkv_prefill_num_partitions(ctypes.byref(p), 4, -3, -1) == -1
+    assert lib.pkv_prefill_num_partitions(ctypes.byref(p), 4, 100, 50) == -1
+    assert lib.pkv_prefill_num_partitions(ctypes.byref(base(max_sel_pages=8)), 4, 0, -1) == -1
+    assert lib.pkv_prefill_num_partitions(ctypes.byref(base(head_dim=96)), 4, 0, -1) == -2
+    assert pcall(p, T=-1) == -1
+    assert pcall(p, kv_begin=10, kv_end=5) == -1
+    assert pcall(p, q=0) == -1
+    assert pcall(p, q=4104) == -1                       # q not 16-byte aligned
+    assert pcall(p, pool=4096 + 64) == -1               # pool not 256-byte aligned
+    assert pcall(p, scale=0) == -1                      # FP8 declared without scales
+    assert pcall(p) == -3                               # 512 partitions need a workspace
+    assert pcall(p, ws=4096, wsb=1000) == -3
+    assert pcall(base(max_sel_pages=8)) == -1           # the prefill reads the dense cache
+    assert pcall(p, T=0, q=0) == 0                      # nothing to do
+    assert pcall(base(rows=0), q=0) == 0
+    assert lib.pkv_lse_fold_into(4, 0, 4096, 4096, 4096, 4096, 0) == -1
+    assert lib.pkv_lse_fold_into(4, 513, 4096, 4096, 4096, 4096, 0) == -1
+    assert lib.pkv_lse_fold_into(4, 128, 0, 4096, 4096, 4096, 0) == -1
+    assert lib.pkv_lse_fold_into(4, 128, 4098, 4096, 4096, 4096, 0) == -1
+    assert lib.pkv_lse_fold_into(0, 128, 0, 0, 0, 0, 0) == 0

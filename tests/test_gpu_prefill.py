@@ -1,0 +1,194 @@
+"""Chunked-prefill attention and the window fold on the GPU vs the float64
+oracle (oracle/prefill.py).
+
+Tolerances as for decode: max-abs 1e-3 on out and 1e-4 on lse; queries with
+an empty key set must give out = 0 and lse = -inf exactly. The kernel forms
+the same fp16 MFMA operands and applies the scales in fp32 as the decode
+kernel does, so the decode bar applies unchanged.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_182_amd as pkv
+import synth
+from synth.device import to_device
+from synth.layout import BF16, FP8, FP16, INT4, INT8
+from gpu_util import compare, params_for, poison_tails
+
+pytestmark = pytest.mark.gpu
+
+# Two GPU results over different splittings of the keys: P.V weights are
+# rounded to fp16 relative to each split's own running max (relative error
+# up to 2^-11 per weight), so their outputs may differ by a few fp16 ulps of
+# the weighted values (|v| up to ~4 here, 2^-11 * 4 = 2e-3 at worst; random
+# signs average most of it out); lse is summed in fp32 and moves by
+# fp32 rounding only.
+SPLIT_OUT_TOL = 5e-4
+SPLIT_LSE_TOL = 2e-5
+
+PAIRS = [(FP16, FP16), (BF16, BF16), (FP8, FP8), (INT8, INT4), (INT4, INT8), (FP8, FP16), (FP16, INT8)]
+
+
+def small(seq_lens, kc, vc, hq, hkv, dim, page, seed=7, **kw):
+    return synth.build_workload(f"pf_{kc}{vc}", rows=len(seq_lens), hq=hq, hkv=hkv, dim=dim, page=page,
+                                seq_lens=seq_lens, codec_of=kw.pop("codec_of", lambda r, lp: (kc, vc)),
+                                seed=seed, **kw)
+
+
+def run_prefill(w, q, kv_begin=0, kv_end=-1, partition_tokens=0, dw=None, expect_err=0, **pk):
+    dw = dw or to_device(w)
+    p = params_for(w, partition_tokens, **pk)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qd = torch.from_numpy(np.ascontiguousarray(q)).cuda()
+    out, lse = pkv.prefill_attention(p, qd, dw.pool, dw.page_k_off, dw.page_v_off, dw.page_codec, dw.page_scale,
+                                     dw.block_table, dw.seq_lens, kv_begin=kv_begin, kv_end=kv_end, err_count=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == expect_err
+    return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def check(w, T, kv_begin=0, kv_end=-1, partition_tokens=0, seed=3, what="", q_scale=1.0, **pk):
+    q = synth.prefill_queries(seed, w.rows, T, w.num_q_heads, w.head_dim, q_scale)
+    out, lse = run_prefill(w, q, kv_begin, kv_end, partition_tokens, **pk)
+    ref_o, ref_l = oracle.prefill_attention(w, q, kv_begin, None if kv_end < 0 else kv_end)
+    return compare(out, lse, ref_o, ref_l, what or f"{w.name} T={T} kv=[{kv_begin},{kv_end}) pt={partition_tokens}")
+
+
+@pytest.mark.parametrize("kc,vc", PAIRS)
+@pytest.mark.parametrize("dim", [64, 128])
+def test_codec_pairs_ragged(kc, vc, dim):
+    print(f"case codecs=({kc},{vc}) dim={dim}", flush=True)
+    w = poison_tails(small([1, 15, 17, 300, 513], kc, vc, hq=8, hkv=2, dim=dim, page=32))
+    check(w, 7, partition_tokens=64)
+    check(w, 40, partition_tokens=0)
+
+
+@pytest.mark.parametrize("T", [1, 2, 16, 33, 64])
+def test_chunk_lengths(T):
+    print(f"case T={T}", flush=True)
+    w = poison_tails(small([70, 200, 1000], FP8, FP8, hq=16, hkv=2, dim=128, page=64))
+    check(w, T, partition_tokens=128)
+    check(w, T, partition_tokens=0)
+
+
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (4, 1), (14, 2), (32, 8), (16, 1)])
+def test_group_sizes_and_column_groups(hq, hkv):
+    """T*G from 5 to 640 columns: one or several groups of 128 columns."""
+    print(f"case hq={hq} hkv={hkv}", flush=True)
+    w = poison_tails(small([77, 250], INT8, INT4, hq=hq, hkv=hkv, dim=128, page=16))
+    check(w, 40, partition_tokens=64)
+
+
+@pytest.mark.parametrize("kv_begin,kv_end", [(0, 100), (5, 77), (64, 256), (100, 101), (130, -1), (600, -1),
+                                             (50, 50), (17, 1000)])
+def test_key_windows(kv_begin, kv_end):
+    print(f"case window=[{kv_begin},{kv_end})", flush=True)
+    w = poison_tails(small([150, 300, 260], FP16, INT8, hq=8, hkv=2, dim=64, page=32))
+    check(w, 24, kv_begin, kv_end, partition_tokens=64)
+    check(w, 24, kv_begin, kv_end, partition_tokens=0)
+
+
+def test_chunk_longer_than_row_and_empty_rows():
+    """T > L: the first T - L queries sit before the row (empty, out 0 and
+    lse -inf); an empty row gives empty results throughout."""
+    w = small([0, 5, 40], FP16, FP16, hq=4, hkv=2, dim=64, page=16)
+    check(w, 12, partition_tokens=16)
+    check(w, 12)
+
+
+def test_mixed_codecs_per_page():
+    pairs = [(FP16, FP16), (FP8, FP8), (INT8, INT4), (BF16, FP8), (INT4, INT8)]
+    rng = np.random.default_rng(4)
+    pick = {}
+
+    def codec_of(r, lp):
+        if (r, lp) not in pick:
+            pick[(r, lp)] = pairs[int(rng.integers(len(pairs)))]
+        return pick[(r, lp)]
+
+    w = poison_tails(small([400, 129, 64], 0, 0, hq=8, hkv=2, dim=128, page=16, codec_of=codec_of))
+    check(w, 20, partition_tokens=64)
+    check(w, 20, partition_tokens=0, k_codec=pkv.CODEC_MIXED, v_codec=pkv.CODEC_MIXED)
+
+
+@pytest.mark.parametrize("cuts", [[0, 128, 256, 1024], [0, 100, 101, 400, 1024], [0, 1024]])
+def test_window_fold_on_device(cuts):
+    """Windows attended one call each and folded by pkv_lse_fold_into equal
+    one call over the whole range (and the oracle)."""
+    w = small([700, 1000], FP8, INT8, hq=8, hkv=2, dim=128, page=64, seed=9)
+    T = 48
+    q = synth.prefill_queries(2, w.rows, T, w.num_q_heads, w.head_dim)
+    dw = to_device(w)
+    full_o, full_l = run_prefill(w, q, dw=dw)
+    acc_o = torch.zeros((w.rows, T, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    acc_l = torch.full((w.rows, T, w.num_q_heads), float("-inf"), dtype=torch.float32, device="cuda")
+    for i in range(len(cuts) - 1):
+        o, l = run_prefill(w, q, cuts[i], cuts[i + 1], dw=dw)
+        pkv.lse_fold_into(acc_o, acc_l, torch.from_numpy(o.astype(np.float32)).cuda(),
+                          torch.from_numpy(l.astype(np.float32)).cuda())
+    torch.cuda.synchronize()
+    ao, al = acc_o.cpu().numpy().astype(np.float64), acc_l.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(full_l)
+    assert np.array_equal(np.isfinite(al), fin)
+    eo, el = np.max(np.abs(ao - full_o)), np.max(np.abs(al[fin] - full_l[fin]))
+    print(f"windowed vs one call: out {eo:.3e} lse {el:.3e}", flush=True)
+    assert eo <= SPLIT_OUT_TOL and el <= SPLIT_LSE_TOL
+    ref_o, ref_l = oracle.prefill_attention(w, q)
+    compare(ao, al, ref_o, ref_l, "windowed fold")
+
+
+def test_fold_into_matches_oracle():
+    rng = np.random.default_rng(8)
+    rows, D = 300, 128
+    ao, bo = rng.standard_normal((rows, D)).astype(np.float32), rng.standard_normal((rows, D)).astype(np.float32)
+    al, bl = (rng.standard_normal(rows) * 4).astype(np.float32), (rng.standard_normal(rows) * 4).astype(np.float32)
+    al[:20] = -np.inf
+    bl[10:30] = -np.inf                    # rows 10..19 empty on both sides
+    bo[20:30] = np.nan                     # an empty side's values are never read into the result
+    ref_o, ref_l = oracle.fold_into(ao, al, bo, bl)
+    t = [torch.from_numpy(x.copy()).cuda() for x in (ao, al, bo, bl)]
+    pkv.lse_fold_into(*t)
+    torch.cuda.synchronize()
+    go, gl = t[0].cpu().numpy().astype(np.float64), t[1].cpu().numpy().astype(np.float64)
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(np.isfinite(gl), fin) and np.all(go[~fin] == 0)
+    assert np.max(np.abs(go - ref_o)) <= 1e-5 and np.max(np.abs(gl[fin] - ref_l[fin])) <= 1e-5
+
+
+def test_bad_pages_are_counted_and_skipped():
+    w = small([96, 64], FP8, FP8, hq=8, hkv=2, dim=128, page=32)
+    bt = w.block_table.copy()
+    bt[0, 1] = w.num_pages + 5             # page id out of range
+    w2 = synth.Workload(**{**w.__dict__, "block_table": bt})
+    T = 10
+    q = synth.prefill_queries(1, w.rows, T, 8, 128)
+    out, lse = run_prefill(w2, q, partition_tokens=32, expect_err=1)   # one page, one partition: one count
+    ref_o, ref_l = oracle.prefill_attention(w, q)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    # row 1 is untouched by the bad entry
+    compare(out[1:], lse[1:], ref_o[1:], ref_l[1:], "rows without a bad page")
+
+
+def test_repeat_runs_bit_identical():
+    w = small([1000, 333], INT8, INT4, hq=16, hkv=2, dim=128, page=16)
+    q = synth.prefill_queries(5, w.rows, 37, 16, 128)
+    dw = to_device(w)
+    a = run_prefill(w, q, dw=dw)
+    b = run_prefill(w, q, dw=dw)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_partition_sizes_agree():
+    w = small([3000], FP8, FP8, hq=16, hkv=2, dim=128, page=64)
+    q = synth.prefill_queries(6, 1, 64, 16, 128, 3.6)
+    dw = to_device(w)
+    ref = run_prefill(w, q, dw=dw, partition_tokens=64)
+    for pt in (128, 1024, 4096):
+        o, l = run_prefill(w, q, dw=dw, partition_tokens=pt)
+        eo, el = np.max(np.abs(o - ref[0])), np.max(np.abs(l - ref[1]))
+        print(f"partition {pt} vs 64: out {eo:.3e} lse {el:.3e}", flush=True)
+        assert eo <= SPLIT_OUT_TOL and el <= SPLIT_LSE_TOL
+    ref_o, ref_l = oracle.prefill_attention(w, q)
+    compare(ref[0], ref[1], ref_o, ref_l, "3000 tokens, 64 queries")
