@@ -346,6 +346,89 @@ def time_per_layer_graph(torch, pkv, w, steps, warmup, min_rot_bytes):
     return res
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
+
+
+def time_prefill(torch, pkv, w, steps, tokens=64, window=131072, q_scale=3.6):
+    """Chunked prefill over the 1M-token FP8 cache: a chunk of `tokens` new
+    queries (the last `tokens` positions) attends the whole cache causally,
+    (a) in one pkv_prefill_attention call (partitions folded by the library),
+    (b) window by window, `window` tokens per call, each window's result
+    folded into an fp32 accumulator by pkv_lse_fold_into. Inputs stay in HBM;
+    the pool is one copy (the kernel is bound by MFMA/VALU work, not HBM)."""
+    import numpy as np
+    import synth
+    from synth import effective_kv_bytes_formula
+    from synth.device import to_device
+    dw = to_device(w)
+    p = params_for(pkv, w)
+    p.partition_tokens = 0
+    L = int(w.seq_lens[0])
+    T, hq, D = tokens, w.num_q_heads, w.head_dim
+    q = torch.from_numpy(synth.prefill_queries(11, 1, T, hq, D, q_scale)).cuda()
+    args = (q, dw.pool, dw.page_k_off, dw.page_v_off, dw.page_codec, dw.page_scale, dw.block_table, dw.seq_lens)
+    out = torch.empty((1, T, hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((1, T, hq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(pkv.prefill_workspace_bytes(p, T), 16), dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    nwin = -(-L // window)
+    win_ws = torch.empty(max(max(pkv.prefill_workspace_bytes(p, T, k * window, (k + 1) * window)
+                                 for k in range(nwin)), 16), dtype=torch.uint8, device="cuda")
+    wo = torch.empty_like(out)
+    wl = torch.empty_like(lse)
+    acc_o = torch.empty_like(out)
+    acc_l = torch.empty_like(lse)
+
+    def one():
+        pkv.prefill_attention(p, *args, out=out, lse=lse, workspace=ws, err_count=err, stream=stream)
+
+    def windowed():
+        acc_l.fill_(float("-inf"))
+        for k in range(nwin):
+            pkv.prefill_attention(p, *args, kv_begin=k * window, kv_end=(k + 1) * window, out=wo, lse=wl,
+                                  workspace=win_ws, err_count=err, stream=stream)
+            pkv.lse_fold_into(acc_o, acc_l, wo, wl, stream=stream)
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = []
+        for _ in range(7):
+            t0.record(stream)
+            for _ in range(n):
+                fn()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            reps.append(t0.elapsed_time(t1) / n)
+        return float(np.median(reps))
+
+    n = max(steps // 5, 5)
+    ms_one = timed(one, n)
+    ms_win = timed(windowed, n)
+    assert int(err.item()) == 0, "device-visible input errors"
+    d_out = float((acc_o - out).abs().max())
+    d_lse = float((acc_l - lse).abs().max())
+    assert bool(torch.isfinite(out).all()) and d_out <= 5e-4 and d_lse <= 2e-5, (d_out, d_lse)
+    flops = hq * 4 * D * (T * (L - T) + T * (T + 1) // 2)
+    kv = effective_kv_bytes_formula(w)
+    res = {"workload": f"prefill_chunk{T}_fp8_1m", "context_tokens": L, "chunk_tokens": T, "q_heads": hq,
+           "kv_heads": w.num_kv_heads, "head_dim": D, "partitions": pkv.prefill_num_partitions(p, T),
+           "algorithmic_flops": flops, "effective_kv_bytes": kv,
+           "ms_one_call": ms_one, "tflops_one_call": flops / ms_one / 1e9,
+           "frac_of_mfma_f16_peak": flops / ms_one / 1e9 / MFMA_F16_PEAK_TFLOPS,
+           "kv_gbps_one_call": kv / ms_one / 1e6,
+           "window_tokens": window, "windows": nwin, "ms_windowed": ms_win,
+           "tflops_windowed": flops / ms_win / 1e9, "windowed_vs_one_call_max_abs": [d_out, d_lse]}
+    log(f"{res['workload']}: one call {ms_one * 1e3:.1f} us ({res['tflops_one_call']:.0f} TFLOP/s, "
+        f"{100 * res['frac_of_mfma_f16_peak']:.1f}% of fp16 MFMA peak, {res['kv_gbps_one_call']:.0f} GB/s of KV); "
+        f"{nwin} windows folded: {ms_win * 1e3:.1f} us")
+    del dw, ws, win_ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_write_side(torch, pkv, steps):
     """The write side, measured on its own: demotion of full FP16 pages
     (pkv_encode_pages) at the 1M FP8 and 32K INT8-K/INT4-V geometries, and one
@@ -556,6 +639,8 @@ def main():
         del w
         log("write side")
         also["write_side"] = time_write_side(torch, pkv, args.steps)
+        log("chunked prefill")
+        also["prefill"] = time_prefill(torch, pkv, w5, args.steps)
         log("read probes")
         probe = read_probe(torch)
         log(f"probe: linear {probe['linear_read_gbps']:.0f} GB/s, random 2 KB chunks "

@@ -41,7 +41,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-enum : int { C_FP16 = 0, C_BF16 = 1, C_FP8 = 2, C_INT8 = 3, C_INT4 = 4 };
+enum : int { C_FP16 = 0, C_BF16 = 1, C_FP8 = 2, C_INT8 = 3, C_INT4 = 4, C_ANY = 15 };
 
 constexpr int WAVES = 4;
 constexpr int THREADS = 64 * WAVES;
@@ -68,8 +68,27 @@ __device__ inline rsrc_t make_rsrc(const uint8_t* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, RSRC_WORD3);
 }
 
-__device__ inline void count_error(int32_t* err) {
-  if (err) atomicAdd(err, 1);
+// Table reads inside the tile loop as explicit scalar loads. The loop's LDS
+// fences count as clobbers of all memory to the optimizer, which would turn
+// these uniform reads into vector loads whose vmcnt(0) wait also drains the
+// tile loads in flight; scalar loads wait on the LGKM counter instead. Reads
+// only (read-only tables, 4-byte aligned addresses).
+__device__ inline uint32_t sload32(const void* p) {
+  uint32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+  return v;
+}
+__device__ inline uint64_t sload64(const void* p) {
+  uint64_t v;
+  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+  return v;
+}
+
+// a <= b for uniform 64-bit values, from 32-bit halves (scalar compares; a
+// 64-bit unsigned compare would move them to vector registers)
+__device__ inline bool le64(uint64_t a, uint64_t b) {
+  const uint32_t ah = (uint32_t)(a >> 32), bh = (uint32_t)(b >> 32);
+  return ah < bh || (ah == bh && (uint32_t)a <= (uint32_t)b);
 }
 
 __device__ inline void lds_barrier() {
@@ -119,6 +138,21 @@ __device__ inline u4 int4x8_to_h8(uint32_t w) {
 
 // Eight consecutive run elements, raw (16, 8 or 4 bytes in the low words) ->
 // eight fp16.
+template <int C>
+__device__ inline u4 to_h8_c(u4 r) {
+  if constexpr (C == C_FP16) {
+    return r;
+  } else if constexpr (C == C_BF16) {
+    return u4{bf16x2_to_h2(r[0]), bf16x2_to_h2(r[1]), bf16x2_to_h2(r[2]), bf16x2_to_h2(r[3])};
+  } else if constexpr (C == C_FP8) {
+    return u4{fp8x2_to_h2<false>(r[0]), fp8x2_to_h2<true>(r[0]), fp8x2_to_h2<false>(r[1]), fp8x2_to_h2<true>(r[1])};
+  } else if constexpr (C == C_INT8) {
+    const u2 a = int8x4_to_h4(r[0]), b = int8x4_to_h4(r[1]);
+    return u4{a[0], a[1], b[0], b[1]};
+  } else {
+    return int4x8_to_h8(r[0]);
+  }
+}
 __device__ inline u4 to_h8(u4 r, int codec) {
   switch (codec) {
     case C_FP16: return r;
@@ -149,7 +183,8 @@ struct TileMeta {
 template <int D>
 struct Raw {
   static constexpr int JOBS = D / 64;  // jobs per thread (K and V jobs together)
-  u4 x[JOBS];
+  u4 x[JOBS];                          // the aligned 16-byte chunk of each job
+  uint32_t off[JOBS];                  // byte offset of the job's run bytes
   u4 sc;
 };
 
@@ -158,29 +193,29 @@ __device__ inline uint32_t run_byte(int L, int rb, int R) {
   return R >= 16 ? (uint32_t)((rb >> 4) * 1024 + 16 * L + (rb & 15)) : (uint32_t)(R * L + rb);
 }
 
-template <int D>
-__device__ inline u4 load_bits(rsrc_t r, uint32_t off, int bits) {
-  if (bits == 16) return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CPOL_NT));
-  if (bits == 8) {
-    const u2 v = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, CPOL_NT));
-    return u4{v[0], v[1], 0u, 0u};
-  }
-  return u4{(uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, CPOL_NT), 0u, 0u, 0u};
+// Every job issues the same single 16-byte load (the aligned chunk holding its
+// bytes; 8- and 4-byte runs share the chunk with a neighbour lane's, so HBM
+// traffic is unchanged), with no control flow around it: the wait counts
+// stay exact and the next tile's loads stay in flight. `sel` picks the bytes.
+__device__ inline u4 load_chunk(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off & ~15u), 0, CPOL_NT));
+}
+__device__ inline u4 select_bytes(u4 x, uint32_t off, int bits) {
+  if (bits == 16) return x;
+  if (bits == 8) return (off & 8) ? u4{x[2], x[3], 0u, 0u} : u4{x[0], x[1], 0u, 0u};
+  const uint32_t k = (off >> 2) & 3;
+  return u4{k == 0 ? x[0] : (k == 1 ? x[1] : (k == 2 ? x[2] : x[3])), 0u, 0u, 0u};
 }
 
-// Job j of a tile: plane (K for j < 64*NC), run chunk c of eight elements,
-// lane L of the consuming wave. K jobs gather the eight dims 32c + 8(L/16) ..
-// of token L%16 (natural order) from wherever the page's K layout keeps them;
-// V jobs take run elements 8c .. 8c+7 of lane L (the V layout of every codec).
+// Load job q of a thread: wave-level job wj = wave + WAVES*q picks the plane
+// (K for wj < NC) and the run chunk c = wj % NC, the same for the whole wave,
+// so the buffer resource stays uniform; lane L is the consuming lane. K jobs
+// gather the eight dims 32c + 8(L/16) .. of token L%16 (natural order) from
+// wherever the page's K layout keeps them; V jobs take run elements 8c ..
+// 8c+7 of lane L (the V layout of every codec).
 template <int D>
-__device__ inline void job_source(int j, int kc, int vc, bool& is_v, int& c, int& L, int& bits, uint32_t& off) {
-  constexpr int NC = D / 32;
-  is_v = j >= 64 * NC;
-  const int jj = is_v ? j - 64 * NC : j;
-  c = jj >> 6;
-  L = jj & 63;
-  const int codec = is_v ? vc : kc;
-  bits = bits_of(codec);
+__device__ inline uint32_t job_offset(bool is_v, int c, int L, int codec) {
+  const int bits = bits_of(codec);
   const int R = D * bits / 32;
   int Ls, e0;
   if (is_v || is_int(codec)) {
@@ -191,36 +226,38 @@ __device__ inline void job_source(int j, int kc, int vc, bool& is_v, int& c, int
     Ls = 16 * (d0 / (D / 4)) + (L & 15);
     e0 = d0 % (D / 4);
   }
-  off = run_byte(Ls, e0 * bits / 8, R);
+  return run_byte(Ls, e0 * bits / 8, R);
 }
 
 template <int D>
-__device__ inline void issue(Raw<D>& raw, const TileMeta& m, const PrefillArgs& a, int h, int tid) {
+__device__ inline void issue(Raw<D>& raw, const TileMeta& m, const PrefillArgs& a, int h, int wave, int lane) {
   constexpr int NC = D / 32;
   const bool live = m.valid > 0;
   const int P = a.page;
   const rsrc_t rk = make_rsrc(a.pool + m.koff, live ? (uint32_t)plane_bytes(m.kc, a.hkv, P, D) : 0u);
   const rsrc_t rv = make_rsrc(a.pool + m.voff, live ? (uint32_t)plane_bytes(m.vc, a.hkv, P, D) : 0u);
   const int sub = (m.j0 % P) / 16;
-  // INT group scales of the tile: 16 tokens x NC fp16 per plane, 16 bytes a thread
+  // INT group scales of the tile, 16 tokens x NC fp16 per plane: lanes
+  // 0 .. 2NC-1 of wave 0 (K) and of wave 1 (V), 16 bytes each
   {
-    const bool kjob = tid < 2 * NC, vjob = tid >= 64 && tid < 64 + 2 * NC;
-    const int i = kjob ? tid : tid - 64;
-    const int codec = vjob ? m.vc : m.kc;
+    const bool sv = wave == 1;
+    const int codec = sv ? m.vc : m.kc;
     const uint32_t base = (uint32_t)((uint64_t)a.hkv * P * D * bits_of(codec) / 8) +
-                          (uint32_t)((h * P + 16 * sub) * NC * 2) + 16 * i;
-    const bool want = (kjob || vjob) && is_int(codec);
-    raw.sc = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(vjob ? rv : rk, (int)(want ? base : OFF_NONE),
+                          (uint32_t)((h * P + 16 * sub) * NC * 2) + 16 * lane;
+    const bool want = wave < 2 && lane < 2 * NC && is_int(codec);
+    raw.sc = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(sv ? rv : rk, (int)(want ? base : OFF_NONE),
                                                                            0, 0));
   }
 #pragma unroll
   for (int q = 0; q < Raw<D>::JOBS; ++q) {
-    bool is_v;
-    int c, L, bits;
-    uint32_t off;
-    job_source<D>(tid + THREADS * q, m.kc, m.vc, is_v, c, L, bits, off);
+    const int wj = wave + WAVES * q;
+    const bool is_v = wj >= NC;
+    const int c = is_v ? wj - NC : wj;
+    const int codec = is_v ? m.vc : m.kc;
+    const int bits = bits_of(codec);
     const uint32_t head = (uint32_t)(h * P * D * bits / 8) + (uint32_t)(sub * 16 * D * bits / 8);
-    raw.x[q] = load_bits<D>(is_v ? rv : rk, head + off, bits);
+    raw.off[q] = head + job_offset<D>(is_v, c, lane, codec);
+    raw.x[q] = load_chunk(is_v ? rv : rk, raw.off[q]);
   }
 }
 
@@ -236,40 +273,44 @@ struct Stage {
   float vs[SCL];
 };
 
-template <int D>
-__device__ inline void produce(const Raw<D>& raw, const TileMeta& m, Stage<D>& st, int tid) {
+template <int C>
+__device__ inline u4 convert(u4 raw, uint32_t off, int codec) {
+  if constexpr (C == C_ANY) return to_h8(select_bytes(raw, off, bits_of(codec)), codec);
+  else return to_h8_c<C>(select_bytes(raw, off, bits_of(C)));
+}
+
+template <int D, int KC, int VC>
+__device__ inline void produce(const Raw<D>& raw, const TileMeta& m, Stage<D>& st, int wave, int lane) {
   constexpr int NC = D / 32;
 #pragma unroll
   for (int q = 0; q < Raw<D>::JOBS; ++q) {
-    const int j = tid + THREADS * q;
-    const bool is_v = j >= 64 * NC;
-    const int jj = is_v ? j - 64 * NC : j;
-    u4 x = to_h8(raw.x[q], is_v ? m.vc : m.kc);
+    const int wj = wave + WAVES * q;
+    const bool is_v = wj >= NC;
+    const int c = is_v ? wj - NC : wj;
+    u4 x = is_v ? convert<VC>(raw.x[q], raw.off[q], m.vc) : convert<KC>(raw.x[q], raw.off[q], m.kc);
     if (is_v && m.valid < 16) {
-      // tokens past the row: zero values (their bytes may be anything)
-      const int L = jj & 63;
-      const int nv = min(max(m.valid - 4 * (L >> 4), 0), 4);  // live tokens of this lane: 4(L/16) + 0 .. nv-1
-      // element e = 8c + i holds token 4(L/16) + i%4; words hold elements (0,1), (2,3), ...
+      // tokens past the row: zero values (their bytes may be anything).
+      // Element e = 8c + i holds token 4(L/16) + i%4; word k holds elements 2k, 2k+1.
+      const int nv = min(max(m.valid - 4 * (lane >> 4), 0), 4);
       const uint32_t m01 = nv >= 2 ? ~0u : (nv == 1 ? 0x0000ffffu : 0u);
       const uint32_t m23 = nv >= 4 ? ~0u : (nv == 3 ? 0x0000ffffu : 0u);
       x = u4{x[0] & m01, x[1] & m23, x[2] & m01, x[3] & m23};
     }
-    (is_v ? st.v : st.k)[jj] = x;
+    (is_v ? st.v : st.k)[64 * c + lane] = x;
   }
-  const bool kjob = tid < 2 * NC, vjob = tid >= 64 && tid < 64 + 2 * NC;
-  if (kjob || vjob) {
-    const int i = kjob ? tid : tid - 64;
-    const int codec = vjob ? m.vc : m.kc;
+  if (wave < 2 && lane < 2 * NC) {
+    const bool sv = wave == 1;
+    const int codec = sv ? m.vc : m.kc;
     float f[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t w = raw.sc[e >> 1];
       const uint16_t hbits = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
-      // INT scale of (token (8i + e) / NC); zero past the row, 1 for other codecs
-      const int tok = (8 * i + e) / NC;
+      // INT scale of token (8 lane + e) / NC; zero past the row, 1 for other codecs
+      const int tok = (8 * lane + e) / NC;
       f[e] = !is_int(codec) ? 1.0f : (tok < m.valid ? (float)__builtin_bit_cast(_Float16, hbits) : 0.0f);
     }
-    float* dst = (vjob ? st.vs : st.ks) + 8 * i;
+    float* dst = (sv ? st.vs : st.ks) + 8 * lane;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dst[e] = f[e];
   }
@@ -310,7 +351,7 @@ __device__ inline float row4_sum(float x) {
 }
 
 // ---------------------------------------------------------------- kernel
-template <int D>
+template <int D, int KC, int VC>
 __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
   constexpr int NC = D / 32, NB = D / 16;
   __shared__ Stage<D> stage[2];
@@ -334,10 +375,13 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
   const bool reporter = h == 0 && cg == a.col_groups - 1 && tid == 0;
 
   // ---- row extent
+  // Errors are counted in a register and added once at the end: no global
+  // write or atomic may sit between the table reads, or they stop being scalar.
+  int nerr = 0;
   int L = a.seq_lens[b];
   const bool bad_row = L < 0 || (int64_t)L > (int64_t)a.max_pages * P;
   L = min(max(L, 0), a.max_pages * P);
-  if (bad_row && reporter && part == 0) count_error(a.err);
+  if (bad_row && part == 0) ++nerr;
 
   // ---- key range of this partition, and of this workgroup's columns
   const int p_lo = max(a.part_base + part * a.part_tokens, a.kv_begin);
@@ -385,28 +429,36 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
   auto meta = [&](int i) {
     TileMeta m;
     m.j0 = t0 + 16 * i;
-    m.koff = 0; m.voff = 0; m.sk = 1.f; m.sv = 1.f; m.kc = 0; m.vc = 0; m.valid = 0;
+    m.koff = 0; m.voff = 0; m.sk = 1.f; m.sv = 1.f; m.valid = 0;
+    m.kc = KC == C_ANY ? 0 : KC;
+    m.vc = VC == C_ANY ? 0 : VC;
     if (i >= ntiles) return m;
-    const int lp = m.j0 / P;
-    const int pp = a.bt[(size_t)b * a.max_pages + lp];
+    // indices moved to scalar registers so the table reads are scalar loads
+    const int lp = __builtin_amdgcn_readfirstlane(m.j0 / P);
+    const int pp = (int)sload32(a.bt + (size_t)b * a.max_pages + lp);
     bool ok = (unsigned)pp < (unsigned)a.num_pages;
-    const int pq = ok ? pp : 0;
-    const int cod = a.codec[pq];
+    const int pq = __builtin_amdgcn_readfirstlane(ok ? pp : 0);
+    // the codec byte through its aligned 32-bit word (scalar loads are dwords)
+    const uintptr_t cb = reinterpret_cast<uintptr_t>(a.codec) + (uintptr_t)pq;
+    const uint32_t cw = sload32(reinterpret_cast<const void*>(cb & ~(uintptr_t)3));
+    const int cod = (int)((cw >> (8 * (cb & 3))) & 0xffu);
     const int kc = cod & 15, vc = cod >> 4;
-    const uint64_t ko = a.koff[pq], vo = a.voff[pq];
-    ok = ok && kc <= C_INT4 && vc <= C_INT4;
+    const uint64_t ko = sload64(a.koff + pq), vo = sload64(a.voff + pq);
+    ok = ok && kc <= C_INT4 && vc <= C_INT4 && (KC == C_ANY || kc == KC) && (VC == C_ANY || vc == VC);
     ok = ok && (a.k_codec < 0 || kc == a.k_codec) && (a.v_codec < 0 || vc == a.v_codec);
     ok = ok && !((kc == C_FP8 || vc == C_FP8) && a.scale == nullptr) && ((ko | vo) & 15) == 0;
-    ok = ok && ko <= a.pool_bytes && a.pool_bytes - ko >= plane_bytes(kc, a.hkv, P, D);
-    ok = ok && vo <= a.pool_bytes && a.pool_bytes - vo >= plane_bytes(vc, a.hkv, P, D);
+    ok = ok && le64(ko, a.pool_bytes) && le64(plane_bytes(kc, a.hkv, P, D), a.pool_bytes - ko);
+    ok = ok && le64(vo, a.pool_bytes) && le64(plane_bytes(vc, a.hkv, P, D), a.pool_bytes - vo);
     if (!ok) {
       // one report per page: from the tile where the workgroup first meets it
-      if (reporter && (m.j0 % P == 0 || i == 0)) count_error(a.err);
+      if (m.j0 % P == 0 || i == 0) ++nerr;
       return m;
     }
-    m.kc = kc; m.vc = vc; m.koff = ko; m.voff = vo;
-    if (kc == C_FP8) m.sk = a.scale[((size_t)pq * a.hkv + h) * 2 + 0];
-    if (vc == C_FP8) m.sv = a.scale[((size_t)pq * a.hkv + h) * 2 + 1];
+    m.kc = KC == C_ANY ? kc : KC;
+    m.vc = VC == C_ANY ? vc : VC;
+    m.koff = ko; m.voff = vo;
+    if (kc == C_FP8) m.sk = __builtin_bit_cast(float, sload32(a.scale + ((size_t)pq * a.hkv + h) * 2 + 0));
+    if (vc == C_FP8) m.sv = __builtin_bit_cast(float, sload32(a.scale + ((size_t)pq * a.hkv + h) * 2 + 1));
     m.valid = min(L - m.j0, 16);
     return m;
   };
@@ -416,7 +468,7 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
   for (int s = 0; s < RING; ++s) {
     mt[s] = meta(s);
-    issue<D>(raw[s], mt[s], a, h, tid);
+    issue<D>(raw[s], mt[s], a, h, wave, lane);
   }
 
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -427,9 +479,11 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
       if (i >= ntiles) break;
       Stage<D>& st = stage[s & 1];  // RING is even: tile i uses buffer i % 2
       const TileMeta m = mt[s];
-      if (m.valid > 0) produce<D>(raw[s], m, st, tid);
+      // unconditional: a dead tile converts zeros that are never read, and the
+      // ring registers are always consumed before they are loaded again
+      produce<D, KC, VC>(raw[s], m, st, wave, lane);
       mt[s] = meta(i + RING);
-      issue<D>(raw[s], mt[s], a, h, tid);
+      issue<D>(raw[s], mt[s], a, h, wave, lane);
       lds_barrier();
       if (m.valid <= 0 || !wave_live || m.j0 >= w_hi_max) continue;
 
@@ -444,7 +498,8 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
         vf[2 * c] = __builtin_bit_cast(h4, u2{x[0], x[1]});
         vf[2 * c + 1] = __builtin_bit_cast(h4, u2{x[2], x[3]});
       }
-      const bool kint = is_int(m.kc), vint = is_int(m.vc), vfp8 = m.vc == C_FP8;
+      const int kcod = KC == C_ANY ? m.kc : KC, vcod = VC == C_ANY ? m.vc : VC;
+      const bool kint = is_int(kcod), vint = is_int(vcod), vfp8 = vcod == C_FP8;
       float ksc[4][NC], vsc[4][NC];
       if (kint) {
 #pragma unroll
@@ -537,6 +592,7 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
       }
     }
   }
+  if (reporter && nerr > 0 && a.err) atomicAdd(a.err, nerr);
   if (!wave_live) return;
 
   // ---- results: lane holds out[column 16cb + 4kq + j][dim 16n + col]
@@ -601,18 +657,40 @@ __global__ void __launch_bounds__(64) fold_into_kernel(int rows, int D, float* a
 
 }  // namespace
 
+namespace {
+
+template <int D, int KC, int VC>
+int launch_prefill_t(const PrefillArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((prefill_kernel<D, KC, VC>), grid, dim3(THREADS), 0, s, a);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// Kernels specialised for one codec pair (the codec dispatch compiled away),
+// and the per-page dispatch variant for any other declaration.
+template <int D>
+int launch_prefill_d(const PrefillArgs& a, dim3 grid, hipStream_t s) {
+  const int kc = a.k_codec < 0 ? C_ANY : a.k_codec;
+  const int vc = a.v_codec < 0 ? C_ANY : a.v_codec;
+#define PKV_PAIR(K, V) \
+  if (kc == K && vc == V) return launch_prefill_t<D, K, V>(a, grid, s);
+  PKV_PAIR(C_FP16, C_FP16)
+  PKV_PAIR(C_BF16, C_BF16)
+  PKV_PAIR(C_FP8, C_FP8)
+  PKV_PAIR(C_INT8, C_INT4)
+#undef PKV_PAIR
+  return launch_prefill_t<D, C_ANY, C_ANY>(a, grid, s);
+}
+
+}  // namespace
+
 int launch_prefill(const PrefillArgs& a, int head_dim, void* stream) {
   if (a.rows == 0 || a.tokens == 0) return 0;
   const long long gx = (long long)((a.nparts + 7) / 8) * 8 * a.col_groups;
   const dim3 grid((unsigned)gx, a.hkv, a.rows);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (head_dim == 64)
-    hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(THREADS), 0, s, a);
-  else if (head_dim == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(THREADS), 0, s, a);
-  else
-    return -2;
-  return hipGetLastError() == hipSuccess ? 0 : -4;
+  if (head_dim == 64) return launch_prefill_d<64>(a, grid, s);
+  if (head_dim == 128) return launch_prefill_d<128>(a, grid, s);
+  return -2;
 }
 
 int launch_fold_into(int rows, int head_dim, float* acc_out, float* acc_lse, const float* out, const float* lse,
