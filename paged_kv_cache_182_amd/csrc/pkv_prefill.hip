@@ -68,29 +68,6 @@ __device__ inline rsrc_t make_rsrc(const uint8_t* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, RSRC_WORD3);
 }
 
-// Table reads inside the tile loop as explicit scalar loads. The loop's LDS
-// fences count as clobbers of all memory to the optimizer, which would turn
-// these uniform reads into vector loads whose vmcnt(0) wait also drains the
-// tile loads in flight; scalar loads wait on the LGKM counter instead. Reads
-// only (read-only tables, 4-byte aligned addresses).
-__device__ inline uint32_t sload32(const void* p) {
-  uint32_t v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
-  return v;
-}
-__device__ inline uint64_t sload64(const void* p) {
-  uint64_t v;
-  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
-  return v;
-}
-
-// a <= b for uniform 64-bit values, from 32-bit halves (scalar compares; a
-// 64-bit unsigned compare would move them to vector registers)
-__device__ inline bool le64(uint64_t a, uint64_t b) {
-  const uint32_t ah = (uint32_t)(a >> 32), bh = (uint32_t)(b >> 32);
-  return ah < bh || (ah == bh && (uint32_t)a <= (uint32_t)b);
-}
-
 __device__ inline void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
@@ -177,6 +154,15 @@ struct TileMeta {
   int kc, vc;
   int j0;               // position of the tile's first token
 };
+
+// Page descriptor staged in LDS (32 bytes).
+struct PDesc {
+  uint64_t k, v;   // plane offsets (0 if the page is skipped)
+  float sk, sv;    // FP8 scales of this KV head (1 otherwise)
+  int32_t valid;   // tokens of the page inside the row (0: skipped)
+  int32_t codec;   // K codec | V codec << 4
+};
+constexpr int MAX_DESC = 256;  // page descriptors staged at a time
 
 // Raw codes of one tile held by one thread: its K and V jobs (eight elements
 // each) and, for a few threads, 16 bytes of INT group scales.
@@ -355,6 +341,7 @@ template <int D, int KC, int VC>
 __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
   constexpr int NC = D / 32, NB = D / 16;
   __shared__ Stage<D> stage[2];
+  __shared__ PDesc desc[MAX_DESC];
 
   // block -> (partition, column group): the column groups of one partition
   // sit 8 blocks apart, on one XCD (blocks are dealt round-robin over the 8
@@ -372,16 +359,15 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
   const int ncols = T * G;
   // the last column group reaches the furthest keys, so it meets every page
   // any group of this partition reads: it alone reports page errors
-  const bool reporter = h == 0 && cg == a.col_groups - 1 && tid == 0;
+  const bool reporter = h == 0 && cg == a.col_groups - 1;
 
   // ---- row extent
-  // Errors are counted in a register and added once at the end: no global
-  // write or atomic may sit between the table reads, or they stop being scalar.
+  // Errors are counted per thread and added once at the end.
   int nerr = 0;
   int L = a.seq_lens[b];
   const bool bad_row = L < 0 || (int64_t)L > (int64_t)a.max_pages * P;
   L = min(max(L, 0), a.max_pages * P);
-  if (bad_row && part == 0) ++nerr;
+  if (bad_row && part == 0 && tid == 0) ++nerr;
 
   // ---- key range of this partition, and of this workgroup's columns
   const int p_lo = max(a.part_base + part * a.part_tokens, a.kv_begin);
@@ -421,173 +407,198 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
     for (int n = 0; n < NB; ++n) acc[cb][n] = f4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- tiles [t0, t1): 16-token tiles of the partition up to the last key
-  // any column of the workgroup attends
+  const f4 zero = {0.f, 0.f, 0.f, 0.f};
+  // ---- tiles [t0, t0 + 16 ntiles): 16-token tiles of the partition up to
+  // the last key any column of the workgroup attends
   const int t0 = p_lo & ~15;
   const int ntiles = wg_hi > p_lo ? (wg_hi - t0 + 15) / 16 : 0;
+  const int t_end = t0 + 16 * ntiles;
+  const int tpp = P / 16;
 
-  auto meta = [&](int i) {
-    TileMeta m;
-    m.j0 = t0 + 16 * i;
-    m.koff = 0; m.voff = 0; m.sk = 1.f; m.sv = 1.f; m.valid = 0;
-    m.kc = KC == C_ANY ? 0 : KC;
-    m.vc = VC == C_ANY ? 0 : VC;
-    if (i >= ntiles) return m;
-    // indices moved to scalar registers so the table reads are scalar loads
-    const int lp = __builtin_amdgcn_readfirstlane(m.j0 / P);
-    const int pp = (int)sload32(a.bt + (size_t)b * a.max_pages + lp);
-    bool ok = (unsigned)pp < (unsigned)a.num_pages;
-    const int pq = __builtin_amdgcn_readfirstlane(ok ? pp : 0);
-    // the codec byte through its aligned 32-bit word (scalar loads are dwords)
-    const uintptr_t cb = reinterpret_cast<uintptr_t>(a.codec) + (uintptr_t)pq;
-    const uint32_t cw = sload32(reinterpret_cast<const void*>(cb & ~(uintptr_t)3));
-    const int cod = (int)((cw >> (8 * (cb & 3))) & 0xffu);
-    const int kc = cod & 15, vc = cod >> 4;
-    const uint64_t ko = sload64(a.koff + pq), vo = sload64(a.voff + pq);
-    ok = ok && kc <= C_INT4 && vc <= C_INT4 && (KC == C_ANY || kc == KC) && (VC == C_ANY || vc == VC);
-    ok = ok && (a.k_codec < 0 || kc == a.k_codec) && (a.v_codec < 0 || vc == a.v_codec);
-    ok = ok && !((kc == C_FP8 || vc == C_FP8) && a.scale == nullptr) && ((ko | vo) & 15) == 0;
-    ok = ok && le64(ko, a.pool_bytes) && le64(plane_bytes(kc, a.hkv, P, D), a.pool_bytes - ko);
-    ok = ok && le64(vo, a.pool_bytes) && le64(plane_bytes(vc, a.hkv, P, D), a.pool_bytes - vo);
-    if (!ok) {
-      // one report per page: from the tile where the workgroup first meets it
-      if (m.j0 % P == 0 || i == 0) ++nerr;
-      return m;
+  // Page descriptors of the tiles, MAX_DESC pages at a time, gathered into LDS
+  // by the whole workgroup (table reads once per page, validated here); the
+  // tile loop then reads one descriptor from LDS per tile.
+  for (int g0 = t0 / P; ntiles > 0 && g0 * P < t_end; g0 += MAX_DESC) {
+    const int g1 = min(g0 + MAX_DESC, (t_end + P - 1) / P);
+    lds_barrier();  // the previous chunk's tiles are consumed
+    if (tid < g1 - g0) {
+      const int lp = g0 + tid;
+      const int pp = a.bt[(size_t)b * a.max_pages + lp];
+      bool ok = (unsigned)pp < (unsigned)a.num_pages;
+      const int pq = ok ? pp : 0;
+      const int cod = a.codec[pq];
+      const int kc = cod & 15, vc = cod >> 4;
+      const uint64_t ko = a.koff[pq], vo = a.voff[pq];
+      ok = ok && kc <= C_INT4 && vc <= C_INT4 && (KC == C_ANY || kc == KC) && (VC == C_ANY || vc == VC);
+      ok = ok && (a.k_codec < 0 || kc == a.k_codec) && (a.v_codec < 0 || vc == a.v_codec);
+      ok = ok && !((kc == C_FP8 || vc == C_FP8) && a.scale == nullptr) && ((ko | vo) & 15) == 0;
+      ok = ok && ko <= a.pool_bytes && a.pool_bytes - ko >= plane_bytes(kc, a.hkv, P, D);
+      ok = ok && vo <= a.pool_bytes && a.pool_bytes - vo >= plane_bytes(vc, a.hkv, P, D);
+      PDesc d;
+      d.k = ok ? ko : 0;
+      d.v = ok ? vo : 0;
+      d.sk = ok && kc == C_FP8 ? a.scale[((size_t)pq * a.hkv + h) * 2 + 0] : 1.f;
+      d.sv = ok && vc == C_FP8 ? a.scale[((size_t)pq * a.hkv + h) * 2 + 1] : 1.f;
+      d.valid = ok ? min(P, L - lp * P) : 0;
+      d.codec = ok ? cod : 0;
+      if (!ok) ++nerr;
+      desc[tid] = d;
     }
-    m.kc = KC == C_ANY ? kc : KC;
-    m.vc = VC == C_ANY ? vc : VC;
-    m.koff = ko; m.voff = vo;
-    if (kc == C_FP8) m.sk = __builtin_bit_cast(float, sload32(a.scale + ((size_t)pq * a.hkv + h) * 2 + 0));
-    if (vc == C_FP8) m.sv = __builtin_bit_cast(float, sload32(a.scale + ((size_t)pq * a.hkv + h) * 2 + 1));
-    m.valid = min(L - m.j0, 16);
-    return m;
-  };
+    lds_barrier();
 
-  Raw<D> raw[RING];
-  TileMeta mt[RING];
-#pragma unroll
-  for (int s = 0; s < RING; ++s) {
-    mt[s] = meta(s);
-    issue<D>(raw[s], mt[s], a, h, wave, lane);
-  }
+    // tiles of this chunk: [c0, c1)
+    const int c0 = max(t0, g0 * P), c1 = min(t_end, g1 * P);
+    const int nt = (c1 - c0) / 16;
+    int ipg = c0 / P - g0, isub = (c0 % P) / 16;  // page and tile of the next tile issued
+    auto meta = [&](int i) {
+      TileMeta m;
+      m.j0 = c0 + 16 * i;
+      m.koff = 0; m.voff = 0; m.sk = 1.f; m.sv = 1.f; m.valid = 0;
+      m.kc = KC == C_ANY ? 0 : KC;
+      m.vc = VC == C_ANY ? 0 : VC;
+      if (i >= nt) return m;
+      const PDesc& d = desc[ipg];
+      const int valid = __builtin_amdgcn_readfirstlane(d.valid) - 16 * isub;
+      m.valid = min(max(valid, 0), 16);
+      m.koff = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(d.k >> 32)) << 32) |
+               __builtin_amdgcn_readfirstlane((uint32_t)d.k);
+      m.voff = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(d.v >> 32)) << 32) |
+               __builtin_amdgcn_readfirstlane((uint32_t)d.v);
+      m.sk = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, d.sk)));
+      m.sv = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, d.sv)));
+      const int cod = __builtin_amdgcn_readfirstlane(d.codec);
+      if (KC == C_ANY) m.kc = cod & 15;
+      if (VC == C_ANY) m.vc = cod >> 4;
+      if (++isub == tpp) { isub = 0; ++ipg; }
+      return m;
+    };
 
-  const f4 zero = {0.f, 0.f, 0.f, 0.f};
-  for (int it = 0; it < ntiles; it += RING) {
+    Raw<D> raw[RING];
+    TileMeta mt[RING];
 #pragma unroll
     for (int s = 0; s < RING; ++s) {
-      const int i = it + s;
-      if (i >= ntiles) break;
-      Stage<D>& st = stage[s & 1];  // RING is even: tile i uses buffer i % 2
-      const TileMeta m = mt[s];
-      // unconditional: a dead tile converts zeros that are never read, and the
-      // ring registers are always consumed before they are loaded again
-      produce<D, KC, VC>(raw[s], m, st, wave, lane);
-      mt[s] = meta(i + RING);
+      mt[s] = meta(s);
       issue<D>(raw[s], mt[s], a, h, wave, lane);
-      lds_barrier();
-      if (m.valid <= 0 || !wave_live || m.j0 >= w_hi_max) continue;
+    }
+    for (int it = 0; it < nt; it += RING) {
+#pragma unroll
+      for (int s = 0; s < RING; ++s) {
+        const int i = it + s;
+        if (i >= nt) break;
+        Stage<D>& st = stage[s & 1];  // RING is even: tile i uses buffer i % 2
+        const TileMeta m = mt[s];
+        // unconditional: a dead tile converts zeros that are never read, and the
+        // ring registers are always consumed before they are loaded again
+        produce<D, KC, VC>(raw[s], m, st, wave, lane);
+        mt[s] = meta(i + RING);
+        issue<D>(raw[s], mt[s], a, h, wave, lane);
+        lds_barrier();
+        if (m.valid <= 0 || !wave_live || m.j0 >= w_hi_max) continue;
 
-      // ---- operands of this tile
-      h8 kf[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) kf[c] = __builtin_bit_cast(h8, st.k[64 * c + lane]);
-      h4 vf[NB];
-#pragma unroll
-      for (int c = 0; c < NB / 2; ++c) {
-        const u4 x = st.v[64 * c + lane];
-        vf[2 * c] = __builtin_bit_cast(h4, u2{x[0], x[1]});
-        vf[2 * c + 1] = __builtin_bit_cast(h4, u2{x[2], x[3]});
-      }
-      const int kcod = KC == C_ANY ? m.kc : KC, vcod = VC == C_ANY ? m.vc : VC;
-      const bool kint = is_int(kcod), vint = is_int(vcod), vfp8 = vcod == C_FP8;
-      float ksc[4][NC], vsc[4][NC];
-      if (kint) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int g = 0; g < NC; ++g) ksc[j][g] = st.ks[(4 * kq + j) * NC + g];
-      }
-      if (vint) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int g = 0; g < NC; ++g) vsc[j][g] = st.vs[(4 * kq + j) * NC + g];
-      }
-      const bool masked = m.j0 < p_lo || m.j0 + 16 > w_hi_min;
-      const float fk = a.scale_log2 * m.sk;
-
-#pragma unroll
-      for (int cb = 0; cb < NBC; ++cb) {
-        float s[4];
+        // ---- operands of this tile
+        h8 kf[NC];
+  #pragma unroll
+        for (int c = 0; c < NC; ++c) kf[c] = __builtin_bit_cast(h8, st.k[64 * c + lane]);
+        h4 vf[NB];
+  #pragma unroll
+        for (int c = 0; c < NB / 2; ++c) {
+          const u4 x = st.v[64 * c + lane];
+          vf[2 * c] = __builtin_bit_cast(h4, u2{x[0], x[1]});
+          vf[2 * c + 1] = __builtin_bit_cast(h4, u2{x[2], x[3]});
+        }
+        const int kcod = KC == C_ANY ? m.kc : KC, vcod = VC == C_ANY ? m.vc : VC;
+        const bool kint = is_int(kcod), vint = is_int(vcod), vfp8 = vcod == C_FP8;
+        float ksc[4][NC], vsc[4][NC];
         if (kint) {
-          f4 sg[NC];
-#pragma unroll
-          for (int c = 0; c < NC; ++c) sg[c] = mfma32(kf[c], qf[cb][c], zero);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float x = 0.f;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) x += ksc[j][c] * sg[c][j];
-            s[j] = x * a.scale_log2;
-          }
-        } else {
-          f4 sa = zero;
-#pragma unroll
-          for (int c = 0; c < NC; ++c) sa = mfma32(kf[c], qf[cb][c], sa);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) s[j] = sa[j] * fk;
+  #pragma unroll
+          for (int j = 0; j < 4; ++j)
+  #pragma unroll
+            for (int g = 0; g < NC; ++g) ksc[j][g] = st.ks[(4 * kq + j) * NC + g];
         }
-        if (masked) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int pos = m.j0 + 4 * kq + j;
-            s[j] = (pos >= p_lo && pos < hi_col[cb]) ? s[j] : NEG_INF;
-          }
-        }
-        const float mx = row4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
-        const float m_new = fmaxf(m_run[cb], mx);
-        if (__any(m_new > m_run[cb])) {
-          const float alpha = m_new > m_run[cb] ? __builtin_amdgcn_exp2f(m_run[cb] - m_new) : 1.0f;
-          l_run[cb] *= alpha;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float aj = __shfl(alpha, 4 * kq + j);
-#pragma unroll
-            for (int n = 0; n < NB; ++n) acc[cb][n][j] *= aj;
-          }
-          m_run[cb] = m_new;
-        }
-        const float mu = m_run[cb] == NEG_INF ? 0.f : m_run[cb];
-        float p[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(s[j] - mu);
-        l_run[cb] += (p[0] + p[1]) + (p[2] + p[3]);
-
         if (vint) {
-          h4 pa[NC];
-#pragma unroll
-          for (int g = 0; g < NC; ++g)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pa[g][j] = (_Float16)(p[j] * vsc[j][g]);
-#pragma unroll
-          for (int n = 0; n < NB; ++n) acc[cb][n] = mfma16(pa[n / 2], vf[n], acc[cb][n]);
-        } else if (vfp8) {
-          h4 hi, lo;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x = p[j] * m.sv;
-            hi[j] = (_Float16)x;
-            lo[j] = (_Float16)(x - (float)hi[j]);
+  #pragma unroll
+          for (int j = 0; j < 4; ++j)
+  #pragma unroll
+            for (int g = 0; g < NC; ++g) vsc[j][g] = st.vs[(4 * kq + j) * NC + g];
+        }
+        const bool masked = m.j0 < p_lo || m.j0 + 16 > w_hi_min;
+        const float fk = a.scale_log2 * m.sk;
+
+  #pragma unroll
+        for (int cb = 0; cb < NBC; ++cb) {
+          float s[4];
+          if (kint) {
+            f4 sg[NC];
+  #pragma unroll
+            for (int c = 0; c < NC; ++c) sg[c] = mfma32(kf[c], qf[cb][c], zero);
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              float x = 0.f;
+  #pragma unroll
+              for (int c = 0; c < NC; ++c) x += ksc[j][c] * sg[c][j];
+              s[j] = x * a.scale_log2;
+            }
+          } else {
+            f4 sa = zero;
+  #pragma unroll
+            for (int c = 0; c < NC; ++c) sa = mfma32(kf[c], qf[cb][c], sa);
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) s[j] = sa[j] * fk;
           }
-#pragma unroll
-          for (int n = 0; n < NB; ++n) {
-            acc[cb][n] = mfma16(hi, vf[n], acc[cb][n]);
-            acc[cb][n] = mfma16(lo, vf[n], acc[cb][n]);
+          if (masked) {
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int pos = m.j0 + 4 * kq + j;
+              s[j] = (pos >= p_lo && pos < hi_col[cb]) ? s[j] : NEG_INF;
+            }
           }
-        } else {
-          const h4 pa = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
-#pragma unroll
-          for (int n = 0; n < NB; ++n) acc[cb][n] = mfma16(pa, vf[n], acc[cb][n]);
+          const float mx = row4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+          const float m_new = fmaxf(m_run[cb], mx);
+          if (__any(m_new > m_run[cb])) {
+            const float alpha = m_new > m_run[cb] ? __builtin_amdgcn_exp2f(m_run[cb] - m_new) : 1.0f;
+            l_run[cb] *= alpha;
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float aj = __shfl(alpha, 4 * kq + j);
+  #pragma unroll
+              for (int n = 0; n < NB; ++n) acc[cb][n][j] *= aj;
+            }
+            m_run[cb] = m_new;
+          }
+          const float mu = m_run[cb] == NEG_INF ? 0.f : m_run[cb];
+          float p[4];
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(s[j] - mu);
+          l_run[cb] += (p[0] + p[1]) + (p[2] + p[3]);
+
+          if (vint) {
+            h4 pa[NC];
+  #pragma unroll
+            for (int g = 0; g < NC; ++g)
+  #pragma unroll
+              for (int j = 0; j < 4; ++j) pa[g][j] = (_Float16)(p[j] * vsc[j][g]);
+  #pragma unroll
+            for (int n = 0; n < NB; ++n) acc[cb][n] = mfma16(pa[n / 2], vf[n], acc[cb][n]);
+          } else if (vfp8) {
+            // weights p * s_V as an fp16 high and low part, fed as the two
+            // k-halves of one 16x16x32 MFMA against V stacked twice
+            h8 hl;
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float x = p[j] * m.sv;
+              hl[j] = (_Float16)x;
+              hl[4 + j] = (_Float16)(x - (float)hl[j]);
+            }
+  #pragma unroll
+            for (int n = 0; n < NB; ++n) {
+              const h8 vv = {vf[n][0], vf[n][1], vf[n][2], vf[n][3], vf[n][0], vf[n][1], vf[n][2], vf[n][3]};
+              acc[cb][n] = mfma32(hl, vv, acc[cb][n]);
+            }
+          } else {
+            const h4 pa = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+  #pragma unroll
+            for (int n = 0; n < NB; ++n) acc[cb][n] = mfma16(pa, vf[n], acc[cb][n]);
+          }
         }
       }
     }
