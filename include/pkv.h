@@ -285,6 +285,9 @@ int pkv_encode_pages(const pkv_params* p, int32_t n, const int32_t* src_pages, c
  * library) starting at kv_begin rounded down to a page boundary; their
  * partials are folded as by pkv_lse_combine.
  *
+ * FP8 page scales must be finite and nonzero here (the encoder's always
+ * are): the kernel keeps its V sums in units of the current page's V scale.
+ *
  * Dense mode only: max_sel_pages must be 0. Codecs, the page tables, the
  * device-visible error counting and the threading rules are those of
  * pkv_decode_attention (each bad page is counted once per partition and

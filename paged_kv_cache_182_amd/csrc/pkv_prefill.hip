@@ -21,10 +21,12 @@
 //    dims 32c + 8(l/16) .. +7, so one 32-dim step is one INT scale group.
 //  * P.V: v_mfma_f32_16x16x16_f16, A = P (the same four scores), B = V (four
 //    tokens of one dim, the V layout of every codec).
-// Codes convert to fp16 exactly. Scales stay in fp32 as in the decode path:
-// FP8 K scales multiply the scores, INT K group scales weight one score
-// accumulator per group, V scales multiply P (FP8 through an fp16 high and
-// low part, INT group scales per group), so a weight of 1 stays exact.
+// Codes convert to fp16 exactly, and scales stay in fp32: FP8 K scales
+// multiply the scores, INT K group scales weight one score accumulator per
+// group, INT V group scales multiply the weights per group (fp16 scales, so a
+// weight of 1 stays exact), and the FP8 V page scale multiplies the output:
+// the accumulator is kept in units of the current page's scale and rescaled
+// when a page with another scale comes.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -398,6 +400,11 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
   }
 
   float m_run[NBC], l_run[NBC];
+  // acc holds the P.V sums divided by sv_cur, the FP8 V scale of the page
+  // last attended: a page with another scale rescales acc once, so FP8 V
+  // weights go to the MFMA as plain fp16(p) (exact at p = 1), as for 16-bit
+  // pages, and the V codes stay exact fp16 values
+  float sv_cur = 1.f;
   f4 acc[NBC][NB];
 #pragma unroll
   for (int cb = 0; cb < NBC; ++cb) {
@@ -497,106 +504,102 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
 
         // ---- operands of this tile
         h8 kf[NC];
-  #pragma unroll
+#pragma unroll
         for (int c = 0; c < NC; ++c) kf[c] = __builtin_bit_cast(h8, st.k[64 * c + lane]);
         h4 vf[NB];
-  #pragma unroll
+#pragma unroll
         for (int c = 0; c < NB / 2; ++c) {
           const u4 x = st.v[64 * c + lane];
           vf[2 * c] = __builtin_bit_cast(h4, u2{x[0], x[1]});
           vf[2 * c + 1] = __builtin_bit_cast(h4, u2{x[2], x[3]});
         }
         const int kcod = KC == C_ANY ? m.kc : KC, vcod = VC == C_ANY ? m.vc : VC;
-        const bool kint = is_int(kcod), vint = is_int(vcod), vfp8 = vcod == C_FP8;
+        const bool kint = is_int(kcod), vint = is_int(vcod);
         float ksc[4][NC], vsc[4][NC];
         if (kint) {
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 4; ++j)
-  #pragma unroll
+#pragma unroll
             for (int g = 0; g < NC; ++g) ksc[j][g] = st.ks[(4 * kq + j) * NC + g];
         }
         if (vint) {
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 4; ++j)
-  #pragma unroll
+#pragma unroll
             for (int g = 0; g < NC; ++g) vsc[j][g] = st.vs[(4 * kq + j) * NC + g];
         }
         const bool masked = m.j0 < p_lo || m.j0 + 16 > w_hi_min;
-        const float fk = a.scale_log2 * m.sk;
+        // scores in log2 units are raw * f: f > 0 goes into the max and the exp
+        const float f = kint ? a.scale_log2 : a.scale_log2 * m.sk;
+        if (m.sv != sv_cur) {  // another V scale (1 for pages without FP8 V)
+          const float r = sv_cur / m.sv;
+#pragma unroll
+          for (int cb = 0; cb < NBC; ++cb)
+#pragma unroll
+            for (int n = 0; n < NB; ++n) acc[cb][n] *= r;
+          sv_cur = m.sv;
+        }
 
-  #pragma unroll
+#pragma unroll
         for (int cb = 0; cb < NBC; ++cb) {
           float s[4];
           if (kint) {
+            // one accumulator per 32-dim group, weighted by its fp16 scale
             f4 sg[NC];
-  #pragma unroll
+#pragma unroll
             for (int c = 0; c < NC; ++c) sg[c] = mfma32(kf[c], qf[cb][c], zero);
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < 4; ++j) {
               float x = 0.f;
-  #pragma unroll
+#pragma unroll
               for (int c = 0; c < NC; ++c) x += ksc[j][c] * sg[c][j];
-              s[j] = x * a.scale_log2;
+              s[j] = x;
             }
           } else {
             f4 sa = zero;
-  #pragma unroll
+#pragma unroll
             for (int c = 0; c < NC; ++c) sa = mfma32(kf[c], qf[cb][c], sa);
-  #pragma unroll
-            for (int j = 0; j < 4; ++j) s[j] = sa[j] * fk;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s[j] = sa[j];
           }
           if (masked) {
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int pos = m.j0 + 4 * kq + j;
               s[j] = (pos >= p_lo && pos < hi_col[cb]) ? s[j] : NEG_INF;
             }
           }
-          const float mx = row4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+          const float mx = row4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * f;
           const float m_new = fmaxf(m_run[cb], mx);
           if (__any(m_new > m_run[cb])) {
             const float alpha = m_new > m_run[cb] ? __builtin_amdgcn_exp2f(m_run[cb] - m_new) : 1.0f;
             l_run[cb] *= alpha;
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < 4; ++j) {
               const float aj = __shfl(alpha, 4 * kq + j);
-  #pragma unroll
+#pragma unroll
               for (int n = 0; n < NB; ++n) acc[cb][n][j] *= aj;
             }
             m_run[cb] = m_new;
           }
           const float mu = m_run[cb] == NEG_INF ? 0.f : m_run[cb];
           float p[4];
-  #pragma unroll
-          for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(s[j] - mu);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], f, -mu));
           l_run[cb] += (p[0] + p[1]) + (p[2] + p[3]);
 
           if (vint) {
+            // INT V: the weights times the token's fp16 group scale, per group
             h4 pa[NC];
-  #pragma unroll
+#pragma unroll
             for (int g = 0; g < NC; ++g)
-  #pragma unroll
+#pragma unroll
               for (int j = 0; j < 4; ++j) pa[g][j] = (_Float16)(p[j] * vsc[j][g]);
-  #pragma unroll
+#pragma unroll
             for (int n = 0; n < NB; ++n) acc[cb][n] = mfma16(pa[n / 2], vf[n], acc[cb][n]);
-          } else if (vfp8) {
-            // weights p * s_V as an fp16 high and low part, fed as the two
-            // k-halves of one 16x16x32 MFMA against V stacked twice
-            h8 hl;
-  #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float x = p[j] * m.sv;
-              hl[j] = (_Float16)x;
-              hl[4 + j] = (_Float16)(x - (float)hl[j]);
-            }
-  #pragma unroll
-            for (int n = 0; n < NB; ++n) {
-              const h8 vv = {vf[n][0], vf[n][1], vf[n][2], vf[n][3], vf[n][0], vf[n][1], vf[n][2], vf[n][3]};
-              acc[cb][n] = mfma32(hl, vv, acc[cb][n]);
-            }
           } else {
             const h4 pa = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
-  #pragma unroll
+#pragma unroll
             for (int n = 0; n < NB; ++n) acc[cb][n] = mfma16(pa, vf[n], acc[cb][n]);
           }
         }
@@ -634,11 +637,11 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
       const size_t r = ((size_t)b * T + t) * a.hq + (size_t)h * G + g;
       if (a.final_out) {
 #pragma unroll
-        for (int n = 0; n < NB; ++n) a.out[r * D + 16 * n + col] = lj > 0.f ? acc[cb][n][j] / lj : 0.f;
+        for (int n = 0; n < NB; ++n) a.out[r * D + 16 * n + col] = lj > 0.f ? acc[cb][n][j] * sv_cur / lj : 0.f;
       } else {
         float* dst = a.part_acc + (r * a.nparts + part) * D;
 #pragma unroll
-        for (int n = 0; n < NB; ++n) dst[16 * n + col] = acc[cb][n][j];
+        for (int n = 0; n < NB; ++n) dst[16 * n + col] = acc[cb][n][j] * sv_cur;
       }
     }
   }
