@@ -31,6 +31,9 @@ What it computes (sources are the three pages' own sections):
   the cache causally, window by window, and the windows' results are folded
   by their log-sum-exp into an accumulator (PR #499 discussion, in-place host
   K/V design).
+* Page selection (``select``): an indexer's block top-k over a compressed
+  slab, and the selected pages compacted into a fixed-capacity list with a
+  drop counter (PR #499 "Why this works" and "Design").
 
 Pins live in ``tests/test_oracle_*.py``; see each function for what pins it.
 """
@@ -40,3 +43,4 @@ from .attention import decode_attention, fold, gather_kv, partials  # noqa: F401
 from .accounting import kv_bytes_per_token  # noqa: F401
 from .encode import append_token, encode_page  # noqa: F401
 from .prefill import fold_into, prefill_attention  # noqa: F401
+from .select import select_pages  # noqa: F401
