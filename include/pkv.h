@@ -329,6 +329,50 @@ int pkv_prefill_attention(const pkv_params* p, int32_t q_tokens, int32_t kv_begi
 int pkv_lse_fold_into(int32_t rows, int32_t head_dim, float* acc_out, float* acc_lse, const float* out,
                       const float* lse, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Page selection for the sparse path: an indexer's block top-k over a
+ * compressed slab, and the selected pages compacted into the fixed-capacity
+ * page_sel / sel_lens arrays that pkv_decode_attention reads in sparse mode
+ * (FreeToken PR #499 "Why this works": top-k block selection over a
+ * compressed slab, on the GPU, fixed shape; "Design": compaction with a drop
+ * counter, capacity 2 * block_topk + 8).
+ *
+ * Row b's L = seq_lens[b] tokens are cut into blocks of block_tokens; block j
+ * covers [j*BT, min((j+1)*BT, L)). Its score is the dot product of the row's
+ * indexer query q_idx[b] with the block's summary slab[b][j], both fp16,
+ * accumulated in fp32 in index order (one rounding per term; reproducible bit
+ * for bit). The block_topk best scores are taken (ties to the lower block,
+ * NaN below every number; all blocks when block_topk >= their number). The
+ * selection is every page a chosen block touches, plus the row's first
+ * sink_pages and last recent_pages pages, in ascending order; the first
+ * max_sel_pages are written to page_sel[b], sel_lens[b] gets their number,
+ * and *dropped grows by the pages that did not fit.
+ */
+
+/* Pages a selection can need at most: with g = gcd(BT, P), a block touches at
+ * most (P - g + BT - 1) / P + 1 pages, so this is that times block_topk plus
+ * sink_pages + recent_pages (for BT <= P and sink + recent = 8, at most the
+ * pages' 2 * block_topk + 8). Negative status for invalid arguments. */
+int pkv_select_capacity(int32_t page_size, int32_t block_tokens, int32_t block_topk, int32_t sink_pages,
+                        int32_t recent_pages);
+
+/* Uses p->num_rows (B), p->page_size (P), p->max_pages_per_row (rows longer
+ * than max_pages_per_row * P are clamped and counted in *err_count; at most
+ * 262,144) and p->max_sel_pages (the capacity of a page_sel row, >= 1).
+ *   q_idx         fp16 [B][idx_dim], idx_dim a positive multiple of 8 (<= 4096).
+ *   slab          fp16 [B][max_blocks][idx_dim], 16-byte aligned; a row with
+ *                 more than max_blocks blocks is cut to max_blocks and counted
+ *                 in *err_count.
+ *   block_scores  fp32 [B][max_blocks]: written with the scores of the row's
+ *                 blocks (the scratch the selection reads).
+ *   page_sel      int32 [B][max_sel_pages], sel_lens int32 [B] (written).
+ *   dropped, err_count  device int32 counters, or NULL.
+ */
+int pkv_select_pages(const pkv_params* p, int32_t block_tokens, int32_t block_topk, int32_t sink_pages,
+                     int32_t recent_pages, int32_t idx_dim, int32_t max_blocks, const void* q_idx, const void* slab,
+                     const int32_t* seq_lens, float* block_scores, int32_t* page_sel, int32_t* sel_lens,
+                     int32_t* dropped, int32_t* err_count, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "pkv_num_partitions",
            "pkv_workspace_bytes", "pkv_decode_attention", "pkv_decode_partials",
            "pkv_lse_combine", "pkv_append_kv", "pkv_encode_pages", "pkv_prefill_num_partitions",
-           "pkv_prefill_workspace_bytes", "pkv_prefill_attention", "pkv_lse_fold_into")
+           "pkv_prefill_workspace_bytes", "pkv_prefill_attention", "pkv_lse_fold_into", "pkv_select_capacity",
+           "pkv_select_pages")
 
 
 class PkvError(RuntimeError):
@@ -79,6 +80,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_prefill_attention.restype = ctypes.c_int
     lib.pkv_prefill_attention.argtypes = [pp, i32, i32, i32] + [vp] * 10 + [vp, sz, vp, vp]
     lib.pkv_lse_fold_into.restype = ctypes.c_int
+    lib.pkv_select_capacity.restype = ctypes.c_int
+    lib.pkv_select_capacity.argtypes = [i32] * 5
+    lib.pkv_select_pages.restype = ctypes.c_int
+    lib.pkv_select_pages.argtypes = [pp] + [i32] * 6 + [vp] * 9
     lib.pkv_lse_fold_into.argtypes = [i32, i32, vp, vp, vp, vp, vp]
     if lib.pkv_abi_version() != 1:
         raise RuntimeError("libpkv ABI version mismatch")
@@ -309,6 +314,44 @@ def lse_fold_into(acc_out, acc_lse, out, lse, stream=None) -> None:
                                _ptr(lse, torch.float32, "lse", dev), _stream(stream))
     if st != OK:
         raise PkvError(st, "pkv_lse_fold_into")
+
+
+def select_capacity(page_size: int, block_tokens: int, block_topk: int, sink_pages: int = 0,
+                    recent_pages: int = 0) -> int:
+    n = load().pkv_select_capacity(int(page_size), int(block_tokens), int(block_topk), int(sink_pages),
+                                   int(recent_pages))
+    if n < 0:
+        raise PkvError(n, "pkv_select_capacity")
+    return n
+
+
+def select_pages(p: Params, q_idx, slab, seq_lens, *, block_tokens: int, block_topk: int, sink_pages: int = 0,
+                 recent_pages: int = 0, block_scores=None, page_sel=None, sel_lens=None, dropped=None,
+                 err_count=None, stream=None):
+    """Enqueue pkv_select_pages: q_idx fp16 [rows, idx_dim], slab fp16
+    [rows, max_blocks, idx_dim]. Returns (page_sel [rows, max_sel_pages],
+    sel_lens [rows], block_scores [rows, max_blocks]); allocates those not given."""
+    lib = load()
+    dev = q_idx.device
+    rows, idx_dim = int(q_idx.shape[0]), int(q_idx.shape[1])
+    max_blocks = int(slab.shape[1])
+    if int(slab.shape[0]) != rows or int(slab.shape[2]) != idx_dim:
+        raise ValueError("slab must be [rows, max_blocks, idx_dim]")
+    if page_sel is None:
+        page_sel = torch.empty((p.num_rows, p.max_sel_pages), dtype=torch.int32, device=dev)
+    if sel_lens is None:
+        sel_lens = torch.empty((p.num_rows,), dtype=torch.int32, device=dev)
+    if block_scores is None:
+        block_scores = torch.empty((rows, max(max_blocks, 1)), dtype=torch.float32, device=dev)
+    st = lib.pkv_select_pages(
+        ctypes.byref(p), int(block_tokens), int(block_topk), int(sink_pages), int(recent_pages), idx_dim, max_blocks,
+        _ptr(q_idx, torch.float16, "q_idx", dev), _ptr(slab, torch.float16, "slab", dev),
+        _ptr(seq_lens, torch.int32, "seq_lens", dev), _ptr(block_scores, torch.float32, "block_scores", dev),
+        _ptr(page_sel, torch.int32, "page_sel", dev), _ptr(sel_lens, torch.int32, "sel_lens", dev),
+        _ptr(dropped, torch.int32, "dropped", dev), _ptr(err_count, torch.int32, "err_count", dev), _stream(stream))
+    if st != OK:
+        raise PkvError(st, "pkv_select_pages")
+    return page_sel, sel_lens, block_scores
 
 
 def hip_runtime_copies() -> list[str]:

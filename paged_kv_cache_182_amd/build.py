@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libpkv.so")
-SOURCES = ["pkv_kernels.hip", "pkv_write.hip", "pkv_prefill.hip", "pkv_api.cpp"]
+SOURCES = ["pkv_kernels.hip", "pkv_write.hip", "pkv_prefill.hip", "pkv_select.hip", "pkv_api.cpp"]
 PROBE_LIB = os.path.join(HERE, "libpkv_probe.so")
 PROBE_SOURCES = ["read_probe.hip"]
 ARCH = "gfx950"

@@ -438,3 +438,73 @@ int pkv_lse_fold_into(int32_t rows, int32_t head_dim, float* acc_out, float* acc
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ page selection
+namespace {
+
+constexpr int32_t kSelectMaxPages = 262144;  // one LDS bit per page of a row
+
+int64_t gcd64(int64_t x, int64_t y) {
+  while (y) {
+    const int64_t t = x % y;
+    x = y;
+    y = t;
+  }
+  return x;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_select_capacity(int32_t page_size, int32_t block_tokens, int32_t block_topk, int32_t sink_pages,
+                        int32_t recent_pages) {
+  if (page_size <= 0 || block_tokens <= 0 || block_topk < 0 || sink_pages < 0 || recent_pages < 0)
+    return PKV_ERR_INVALID_ARG;
+  const int64_t g = gcd64(block_tokens, page_size);
+  const int64_t per_block = (page_size - g + block_tokens - 1) / page_size + 1;
+  const int64_t cap = per_block * block_topk + sink_pages + recent_pages;
+  return cap > 0x7fffffff ? PKV_ERR_UNSUPPORTED : (int)cap;
+}
+
+int pkv_select_pages(const pkv_params* p, int32_t block_tokens, int32_t block_topk, int32_t sink_pages,
+                     int32_t recent_pages, int32_t idx_dim, int32_t max_blocks, const void* q_idx, const void* slab,
+                     const int32_t* seq_lens, float* block_scores, int32_t* page_sel, int32_t* sel_lens,
+                     int32_t* dropped, int32_t* err_count, void* stream) {
+  if (!p || p->num_rows < 0 || p->page_size <= 0 || p->page_size % 16 != 0 || p->max_pages_per_row < 1 ||
+      p->max_sel_pages < 1)
+    return PKV_ERR_INVALID_ARG;
+  if (block_tokens <= 0 || block_topk < 0 || sink_pages < 0 || recent_pages < 0 || idx_dim <= 0 ||
+      idx_dim % 8 != 0 || max_blocks < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (idx_dim > 4096 || p->max_pages_per_row > kSelectMaxPages || p->num_rows > 65535) return PKV_ERR_UNSUPPORTED;
+  if (p->num_rows == 0) return PKV_OK;
+  if (!q_idx || !seq_lens || !page_sel || !sel_lens || (max_blocks > 0 && (!slab || !block_scores)))
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned(q_idx, 2) || !aligned(seq_lens, 4) || !aligned(page_sel, 4) || !aligned(sel_lens, 4) ||
+      (slab && !aligned(slab, 16)) || (block_scores && !aligned(block_scores, 4)) ||
+      (dropped && !aligned(dropped, 4)) || (err_count && !aligned(err_count, 4)))
+    return PKV_ERR_INVALID_ARG;
+  pkv::SelectArgs a{};
+  a.q_idx = static_cast<const uint16_t*>(q_idx);
+  a.slab = static_cast<const uint16_t*>(slab);
+  a.seq_lens = seq_lens;
+  a.scores = block_scores;
+  a.sel = page_sel;
+  a.sel_lens = sel_lens;
+  a.dropped = dropped;
+  a.err = err_count;
+  a.rows = p->num_rows;
+  a.page = p->page_size;
+  a.max_pages = p->max_pages_per_row;
+  a.max_sel = p->max_sel_pages;
+  a.block_tokens = block_tokens;
+  a.block_topk = block_topk;
+  a.sink_pages = sink_pages;
+  a.recent_pages = recent_pages;
+  a.idx_dim = idx_dim;
+  a.max_blocks = max_blocks;
+  return pkv::launch_select(a, stream) == 0 ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // extern "C"

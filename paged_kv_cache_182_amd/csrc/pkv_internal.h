@@ -94,6 +94,22 @@ int launch_prefill(const PrefillArgs& a, int head_dim, void* stream);
 int launch_fold_into(int rows, int head_dim, float* acc_out, float* acc_lse, const float* out,
                      const float* lse, void* stream);
 
+// Block top-k page selection (pkv_select_pages).
+struct SelectArgs {
+  const uint16_t* q_idx;    // fp16 [B][idx_dim]
+  const uint16_t* slab;     // fp16 [B][max_blocks][idx_dim]
+  const int32_t* seq_lens;  // [B]
+  float* scores;            // [B][max_blocks] (written for the row's blocks)
+  int32_t* sel;             // [B][max_sel]
+  int32_t* sel_lens;        // [B]
+  int32_t* dropped;         // device counter or nullptr
+  int32_t* err;             // device counter or nullptr
+  int32_t rows, page, max_pages, max_sel;
+  int32_t block_tokens, block_topk, sink_pages, recent_pages, idx_dim, max_blocks;
+};
+
+int launch_select(const SelectArgs& a, void* stream);
+
 int launch_append(const AppendArgs& a, void* stream);
 int launch_encode(const EncodeArgs& a, void* stream);
 

@@ -184,3 +184,31 @@ def test_prefill_host_checks():
     assert lib.pkv_lse_fold_into(4, 128, 0, 4096, 4096, 4096, 0) == -1
     assert lib.pkv_lse_fold_into(4, 128, 4098, 4096, 4096, 4096, 0) == -1
     assert lib.pkv_lse_fold_into(0, 128, 0, 0, 0, 0, 0) == 0
+
+
+def test_select_capacity_and_host_checks():
+    assert pkv.select_capacity(16, 16, 127, 0, 1) == 128
+    assert pkv.select_capacity(16, 12, 32, 4, 4) == 2 * 32 + 8       # the pages' 2 * block_topk + 8
+    assert pkv.select_capacity(16, 40, 10, 0, 0) == 30
+    lib = pkv.load()
+    assert lib.pkv_select_capacity(0, 16, 1, 0, 0) == -1
+    assert lib.pkv_select_capacity(16, 16, -1, 0, 0) == -1
+    p = pkv.make_params(rows=2, num_q_heads=1, num_kv_heads=1, head_dim=128, page_size=16, num_pages=1,
+                        max_pages_per_row=64, pool_bytes=0, max_sel_pages=32)
+
+    def sel(pp=p, bt=16, k=4, dim=64, mb=64, **ptr):
+        v = dict(q=4096, slab=4096, lens=4096, scores=4096, out=4096, n=4096)
+        v.update(ptr)
+        return lib.pkv_select_pages(ctypes.byref(pp), bt, k, 0, 1, dim, mb, v["q"], v["slab"], v["lens"],
+                                    v["scores"], v["out"], v["n"], 0, 0, 0)
+    assert sel(dim=12) == -1                          # idx_dim not a multiple of 8
+    assert sel(bt=0) == -1
+    assert sel(k=-1) == -1
+    assert sel(q=0) == -1
+    assert sel(slab=4104) == -1                       # slab not 16-byte aligned
+    assert sel(pp=pkv.make_params(rows=2, num_q_heads=1, num_kv_heads=1, head_dim=128, page_size=16,
+                                  num_pages=1, max_pages_per_row=64, pool_bytes=0, max_sel_pages=0)) == -1
+    assert sel(pp=pkv.make_params(rows=2, num_q_heads=1, num_kv_heads=1, head_dim=128, page_size=16,
+                                  num_pages=1, max_pages_per_row=1 << 20, pool_bytes=0, max_sel_pages=8)) == -2
+    assert sel(pp=pkv.make_params(rows=0, num_q_heads=1, num_kv_heads=1, head_dim=128, page_size=16,
+                                  num_pages=1, max_pages_per_row=64, pool_bytes=0, max_sel_pages=8), q=0) == 0
