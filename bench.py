@@ -429,6 +429,59 @@ def time_prefill(torch, pkv, w, steps, tokens=64, window=131072, q_scale=3.6):
     return res
 
 
+def time_select(torch, pkv, steps, rows=48, context=262144, page=16, idx_dim=64, topk=127):
+    """GPU page selection at the sparse workload's shape: 48 rows (12 layers x
+    4 sequences) of a 262,144-token context in 16-token pages, one indexer
+    block per page, a 64-dim fp16 slab, 127 blocks + the last page selected
+    (the 128-page selection the sparse decode step reads). Three slab copies
+    rotate so consecutive calls read different memory."""
+    import numpy as np
+    nblocks = context // page
+    cap = pkv.select_capacity(page, page, topk, 0, 1)
+    p = pkv.make_params(rows=rows, num_q_heads=16, num_kv_heads=2, head_dim=128, page_size=page, num_pages=1,
+                        max_pages_per_row=nblocks, pool_bytes=0, max_sel_pages=cap)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(17)
+    slabs = [torch.randn((rows, nblocks, idx_dim), generator=gen, device="cuda").to(torch.float16) for _ in range(3)]
+    q = torch.randn((rows, idx_dim), generator=gen, device="cuda").to(torch.float16)
+    lens = torch.full((rows,), context, dtype=torch.int32, device="cuda")
+    scores = torch.empty((rows, nblocks), dtype=torch.float32, device="cuda")
+    sel = torch.empty((rows, cap), dtype=torch.int32, device="cuda")
+    n = torch.empty((rows,), dtype=torch.int32, device="cuda")
+    dropped = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        pkv.select_pages(p, q, slabs[i % 3], lens, block_tokens=page, block_topk=topk, recent_pages=1,
+                         block_scores=scores, page_sel=sel, sel_lens=n, dropped=dropped, stream=stream)
+
+    call(0)
+    torch.cuda.synchronize()
+    # 127 best blocks and the last page (which may be one of them)
+    assert int(dropped.item()) == 0 and bool(((n >= topk) & (n <= topk + 1)).all()), "selection size"
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = []
+    nrep = max(steps // 2, 10)
+    for _ in range(7):
+        t0.record(stream)
+        for i in range(nrep):
+            call(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        reps.append(t0.elapsed_time(t1) / nrep)
+    ms = float(np.median(reps))
+    slab_bytes = rows * nblocks * idx_dim * 2
+    moved = slab_bytes + rows * idx_dim * 2 + 2 * rows * nblocks * 4 + rows * (cap + 1) * 4
+    res = {"workload": f"select_{rows}rows_{context // 1024}k_top{topk}", "rows": rows, "blocks_per_row": nblocks,
+           "idx_dim": idx_dim, "capacity": cap, "us": ms * 1e3, "slab_bytes": slab_bytes,
+           "algorithmic_bytes": moved, "gbps": moved / ms / 1e6, "frac_of_8tbs": moved / ms / 1e6 / HBM_PEAK_GBPS}
+    log(f"{res['workload']}: {ms * 1e3:.1f} us per selection ({res['gbps']:.0f} GB/s, "
+        f"{100 * res['frac_of_8tbs']:.1f}% of HBM peak)")
+    del slabs
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_write_side(torch, pkv, steps):
     """The write side, measured on its own: demotion of full FP16 pages
     (pkv_encode_pages) at the 1M FP8 and 32K INT8-K/INT4-V geometries, and one
@@ -641,6 +694,8 @@ def main():
         also["write_side"] = time_write_side(torch, pkv, args.steps)
         log("chunked prefill")
         also["prefill"] = time_prefill(torch, pkv, w5, args.steps)
+        log("page selection")
+        also["select"] = time_select(torch, pkv, args.steps)
         log("read probes")
         probe = read_probe(torch)
         log(f"probe: linear {probe['linear_read_gbps']:.0f} GB/s, random 2 KB chunks "
