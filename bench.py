@@ -652,6 +652,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-workload", type=int, default=5, choices=(3, 4, 5),
                     help="workload of --profile-pass (3: batched 32K INT8/INT4, 4: sparse FP8, 5: 1M FP8)")
+    ap.add_argument("--profile-rows", action="store_true",
+                    help="short run of the widened rows for rocprofv3 (write side, chunked prefill, page selection)")
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for rocprofv3 (split-K kernel + calibration copy), no JSON")
     args = ap.parse_args()
@@ -670,6 +672,14 @@ def main():
     log(f"device {torch.cuda.get_device_name(0)}")
     if args.profile_pass:
         profile_pass(torch, pkv, synth, args.profile_workload)
+        return
+    if args.profile_rows:
+        # each timing function runs its kernels a handful of times (5 steps)
+        time_write_side(torch, pkv, 5)
+        w5 = synth.config(5)
+        time_prefill(torch, pkv, w5, 5)
+        time_select(torch, pkv, 5)
+        log("profile-rows pass done")
         return
 
     min_rot = 1 << 30
