@@ -12,14 +12,17 @@ been appended to the cache, so it is the last T of the row's L tokens: query
 t sits at position pos = L - T + t and, causally, attends the cached tokens
 j <= pos. A call may restrict the keys to a window [kv_begin, kv_end):
 
-    keys(t) = { j : max(kv_begin, 0) <= j < min(kv_end, pos + 1) }
+    keys(t) = { j : max(kv_begin, 0, pos + 1 - W) <= j < min(kv_end, pos + 1) }
     s_j     = tau * sum_i q[t][hq][i] * K_j[h][i]            (h = hq // G)
     out     = sum_j exp(s_j - m) V_j[h] / sum_j exp(s_j - m),   m = max_j s_j
     lse     = m + ln(sum_j exp(s_j - m))                       (natural log)
 
-An empty key set (a window that misses the query's range, or pos < 0 when
-T > L) gives out = 0 and lse = -inf. With T = 1 this is the decode
-definition of ``attention.decode_attention``.
+with W the sliding-window length (ARGUS v0.5: direct attention supports
+sliding-window masks): each query sees at most its last W positions, its
+own included; W <= 0 means no sliding window. An empty key set (a window
+that misses the query's range, or pos < 0 when T > L) gives out = 0 and
+lse = -inf. With T = 1 and no sliding window this is the decode definition
+of ``attention.decode_attention``.
 
 ``fold_into`` merges the result of one more window into an accumulator that
 holds the result over the windows seen so far (both as (out, lse)):
@@ -44,7 +47,7 @@ import numpy as np
 from .attention import _softmax_attention, gather_kv
 
 
-def prefill_attention(w, q, kv_begin: int = 0, kv_end: int | None = None, rows=None):
+def prefill_attention(w, q, kv_begin: int = 0, kv_end: int | None = None, rows=None, window: int = 0):
     """q: [rows_all, T, Hq, D] (fp16 values). Dense workloads only.
 
     Returns out float64 [len(rows), T, Hq, D] and lse float64 [len(rows), T, Hq]."""
@@ -66,10 +69,11 @@ def prefill_attention(w, q, kv_begin: int = 0, kv_end: int | None = None, rows=N
             for t in range(T):
                 pos = L - T + t
                 hi = pos + 1 if kv_end is None else min(int(kv_end), pos + 1)
-                if hi <= lo:
+                lo_t = max(lo, pos + 1 - int(window)) if window > 0 else lo
+                if hi <= lo_t:
                     continue
                 qt = q[r, t, h * G:(h + 1) * G].astype(np.float64)
-                o, s = _softmax_attention(K[lo:hi], V[lo:hi], qt, tau)
+                o, s = _softmax_attention(K[lo_t:hi], V[lo_t:hi], qt, tau)
                 out[ri, t, h * G:(h + 1) * G] = o
                 lse[ri, t, h * G:(h + 1) * G] = s
     return out, lse

@@ -38,7 +38,7 @@ def logical_values(w, row, h):
     return np.concatenate(ks), np.concatenate(vs)
 
 
-def sdpa_reference(w, q, kv_begin, kv_end):
+def sdpa_reference(w, q, kv_begin, kv_end, window=0):
     """torch SDPA (float64, GQA) with the causal/window mask as a boolean matrix."""
     T, hq, D = q.shape[1], w.num_q_heads, w.head_dim
     hkv = w.num_kv_heads
@@ -52,6 +52,8 @@ def sdpa_reference(w, q, kv_begin, kv_end):
         mask = (j[None, :] <= pos[:, None]) & (j[None, :] >= max(kv_begin, 0))
         if kv_end is not None:
             mask &= j[None, :] < kv_end
+        if window > 0:
+            mask &= j[None, :] > pos[:, None] - window
         qt = torch.from_numpy(q[r].astype(np.float64)).permute(1, 0, 2)[None]    # [1, Hq, T, D]
         o = torch.nn.functional.scaled_dot_product_attention(qt, K, V, attn_mask=mask, scale=w.softmax_scale,
                                                              enable_gqa=True)
@@ -186,3 +188,35 @@ def test_rejects_sparse_workloads():
                              codec_of=lambda r, lp: (FP16, FP16), seed=1, selection=np.array([[0, 2]]))
     with pytest.raises(ValueError):
         prefill_attention(w, np.zeros((1, 1, 2, 32), np.float16))
+
+
+@pytest.mark.parametrize("window,kv_begin,kv_end", [(1, 0, None), (5, 0, None), (40, 0, None), (33, 20, 90),
+                                                    (1000, 0, None)])
+def test_sliding_window_equals_banded_sdpa(window, kv_begin, kv_end):
+    w = small([100, 64, 131], hq=6, hkv=2, dim=32)
+    T = 9
+    q = synth.prefill_queries(8, w.rows, T, w.num_q_heads, w.head_dim)
+    out, lse = prefill_attention(w, q, kv_begin, kv_end, window=window)
+    ref_o, ref_l = sdpa_reference(w, q, kv_begin, kv_end, window)
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(np.isfinite(lse), fin)                     # empty windows: -inf on both
+    assert np.all(out[~fin] == 0)
+    assert np.max(np.abs(out[fin] - ref_o[fin])) <= 1e-12 and np.max(np.abs(lse[fin] - ref_l[fin])) <= 1e-12
+
+
+def test_sliding_window_closed_forms():
+    """W = 1: every query sees only itself (out = V_pos, lse = s_pos); W at
+    least the row: the plain causal result."""
+    w = small([50], hq=2, hkv=1, dim=32)
+    T = 6
+    q = synth.prefill_queries(12, 1, T, 2, 32)
+    out, lse = prefill_attention(w, q, window=1)
+    K, V = logical_values(w, 0, 0)
+    for t in range(T):
+        pos = 50 - T + t
+        for hq in range(2):
+            assert np.array_equal(out[0, t, hq], V[pos])
+            assert lse[0, t, hq] == pytest.approx(w.softmax_scale * q[0, t, hq].astype(np.float64) @ K[pos], abs=1e-13)
+    full = prefill_attention(w, q)
+    wide = prefill_attention(w, q, window=50)
+    assert np.array_equal(full[0], wide[0]) and np.array_equal(full[1], wide[1])
