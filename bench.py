@@ -404,14 +404,25 @@ def time_prefill(torch, pkv, w, steps, tokens=64, window=131072, q_scale=3.6):
             reps.append(t0.elapsed_time(t1) / n)
         return float(np.median(reps))
 
+    so = torch.empty_like(out)
+    sl = torch.empty_like(lse)
+    ws_s = torch.empty(max(pkv.prefill_workspace_bytes(p, T, L - T + 1 - 8192), 16), dtype=torch.uint8, device="cuda")
+
+    def sliding():
+        # the keys in play start at the first query's position - W + 1
+        pkv.prefill_attention(p, *args, kv_begin=L - T + 1 - 8192, window=8192, out=so, lse=sl, workspace=ws_s,
+                              err_count=err, stream=stream)
+
     n = max(steps // 5, 5)
     ms_one = timed(one, n)
     ms_win = timed(windowed, n)
+    ms_slide = timed(sliding, n)
     assert int(err.item()) == 0, "device-visible input errors"
     d_out = float((acc_o - out).abs().max())
     d_lse = float((acc_l - lse).abs().max())
     assert bool(torch.isfinite(out).all()) and d_out <= 5e-4 and d_lse <= 2e-5, (d_out, d_lse)
     flops = hq * 4 * D * (T * (L - T) + T * (T + 1) // 2)
+    slide_flops = hq * 4 * D * T * 8192          # every query sees 8,192 keys
     kv = effective_kv_bytes_formula(w)
     res = {"workload": f"prefill_chunk{T}_fp8_1m", "context_tokens": L, "chunk_tokens": T, "q_heads": hq,
            "kv_heads": w.num_kv_heads, "head_dim": D, "partitions": pkv.prefill_num_partitions(p, T),
@@ -420,10 +431,13 @@ def time_prefill(torch, pkv, w, steps, tokens=64, window=131072, q_scale=3.6):
            "frac_of_mfma_f16_peak": flops / ms_one / 1e9 / MFMA_F16_PEAK_TFLOPS,
            "kv_gbps_one_call": kv / ms_one / 1e6,
            "window_tokens": window, "windows": nwin, "ms_windowed": ms_win,
-           "tflops_windowed": flops / ms_win / 1e9, "windowed_vs_one_call_max_abs": [d_out, d_lse]}
+           "tflops_windowed": flops / ms_win / 1e9, "windowed_vs_one_call_max_abs": [d_out, d_lse],
+           "sliding_window_8192": {"ms": ms_slide, "algorithmic_flops": slide_flops,
+                                   "tflops": slide_flops / ms_slide / 1e9}}
     log(f"{res['workload']}: one call {ms_one * 1e3:.1f} us ({res['tflops_one_call']:.0f} TFLOP/s, "
         f"{100 * res['frac_of_mfma_f16_peak']:.1f}% of fp16 MFMA peak, {res['kv_gbps_one_call']:.0f} GB/s of KV); "
-        f"{nwin} windows folded: {ms_win * 1e3:.1f} us")
+        f"{nwin} windows folded: {ms_win * 1e3:.1f} us; sliding window 8192: {ms_slide * 1e3:.1f} us "
+        f"({slide_flops / ms_slide / 1e9:.0f} TFLOP/s)")
     del dw, ws, win_ws
     torch.cuda.empty_cache()
     return res

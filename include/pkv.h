@@ -276,14 +276,20 @@ int pkv_encode_pages(const pkv_params* p, int32_t n, const int32_t* src_pages, c
  * the last T of row b's L = seq_lens[b] tokens: query t sits at position
  * pos = L - T + t and attends, causally, the keys
  *
- *     j in [kv_begin, min(kv_end, pos + 1))        (kv_end < 0: no bound)
+ *     j in [max(kv_begin, pos + 1 - W), min(kv_end, pos + 1))
  *
+ * (kv_end < 0: no bound; W = window_tokens, the sliding window: each query
+ * sees at most its last W positions, its own included; W <= 0: none; ARGUS
+ * v0.5: direct attention with sliding-window masks)
  * with the scores, softmax, out and lse of pkv_decode_attention (natural-log
  * lse; an empty key set, e.g. pos < 0 when T > L, gives out = 0 and
- * lse = -inf). With T = 1 and the whole range this is the decode result. The
+ * lse = -inf). With T = 1, the whole range and no sliding window this is the
+ * decode result (with a sliding window, T = 1 is sliding-window decode). The
  * key range is split into partitions of partition_tokens (0: chosen by the
  * library) starting at kv_begin rounded down to a page boundary; their
- * partials are folded as by pkv_lse_combine.
+ * partials are folded as by pkv_lse_combine. With a sliding window, passing
+ * kv_begin = (the smallest first-query position) - W + 1 lets the partitions
+ * cover only the keys in play.
  *
  * FP8 page scales must be finite and nonzero here (the encoder's always
  * are): the kernel keeps its V sums in units of the current page's V scale.
@@ -309,7 +315,7 @@ size_t pkv_prefill_workspace_bytes(const pkv_params* p, int32_t q_tokens, int32_
  * Other arguments as for pkv_decode_attention. Returns PKV_ERR_INVALID_ARG for
  * q_tokens < 0, kv_begin < 0, 0 <= kv_end < kv_begin or max_sel_pages != 0. */
 int pkv_prefill_attention(const pkv_params* p, int32_t q_tokens, int32_t kv_begin, int32_t kv_end,
-                          const void* q, const uint8_t* page_pool, const uint64_t* page_k_off,
+                          int32_t window_tokens, const void* q, const uint8_t* page_pool, const uint64_t* page_k_off,
                           const uint64_t* page_v_off, const uint8_t* page_codec, const float* page_scale,
                           const int32_t* block_table, const int32_t* seq_lens, float* out, float* lse,
                           void* workspace, size_t workspace_bytes, int32_t* err_count, void* stream);

@@ -78,7 +78,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_prefill_workspace_bytes.restype = sz
     lib.pkv_prefill_workspace_bytes.argtypes = [pp, i32, i32, i32]
     lib.pkv_prefill_attention.restype = ctypes.c_int
-    lib.pkv_prefill_attention.argtypes = [pp, i32, i32, i32] + [vp] * 10 + [vp, sz, vp, vp]
+    lib.pkv_prefill_attention.argtypes = [pp, i32, i32, i32, i32] + [vp] * 10 + [vp, sz, vp, vp]
     lib.pkv_lse_fold_into.restype = ctypes.c_int
     lib.pkv_select_capacity.restype = ctypes.c_int
     lib.pkv_select_capacity.argtypes = [i32] * 5
@@ -265,10 +265,10 @@ def prefill_workspace_bytes(p: Params, q_tokens: int, kv_begin: int = 0, kv_end:
 
 
 def prefill_attention(p: Params, q, page_pool, page_k_off, page_v_off, page_codec, page_scale, block_table,
-                      seq_lens, *, kv_begin: int = 0, kv_end: int = -1, out=None, lse=None, workspace=None,
-                      err_count=None, stream=None):
+                      seq_lens, *, kv_begin: int = 0, kv_end: int = -1, window: int = 0, out=None, lse=None,
+                      workspace=None, err_count=None, stream=None):
     """Enqueue pkv_prefill_attention: q fp16 [rows, T, Hq, D], the last T
-    tokens of each row. Returns (out [rows, T, Hq, D], lse [rows, T, Hq]);
+    tokens of each row; `window` > 0 is a sliding window of that many positions. Returns (out [rows, T, Hq, D], lse [rows, T, Hq]);
     allocates them (and the workspace) with torch when not given."""
     lib = load()
     dev = q.device
@@ -285,7 +285,7 @@ def prefill_attention(p: Params, q, page_pool, page_k_off, page_v_off, page_code
     ws_ptr = 0 if workspace is None else _ptr(workspace, torch.uint8, "workspace", dev)
     ws_len = 0 if workspace is None else workspace.numel()
     st = lib.pkv_prefill_attention(
-        ctypes.byref(p), T, int(kv_begin), int(kv_end), _ptr(q, torch.float16, "q", dev),
+        ctypes.byref(p), T, int(kv_begin), int(kv_end), int(window), _ptr(q, torch.float16, "q", dev),
         _ptr(page_pool, torch.uint8, "page_pool", dev),
         _ptr(page_k_off, torch.uint64, "page_k_off", dev),
         _ptr(page_v_off, torch.uint64, "page_v_off", dev),

@@ -362,7 +362,7 @@ size_t pkv_prefill_workspace_bytes(const pkv_params* p, int32_t q_tokens, int32_
 }
 
 int pkv_prefill_attention(const pkv_params* p, int32_t q_tokens, int32_t kv_begin, int32_t kv_end,
-                          const void* q, const uint8_t* page_pool, const uint64_t* page_k_off,
+                          int32_t window_tokens, const void* q, const uint8_t* page_pool, const uint64_t* page_k_off,
                           const uint64_t* page_v_off, const uint8_t* page_codec, const float* page_scale,
                           const int32_t* block_table, const int32_t* seq_lens, float* out, float* lse,
                           void* workspace, size_t workspace_bytes, int32_t* err_count, void* stream) {
@@ -402,6 +402,7 @@ int pkv_prefill_attention(const pkv_params* p, int32_t q_tokens, int32_t kv_begi
   a.max_pages = p->max_pages_per_row;
   a.kv_begin = kv_begin;
   a.kv_end = (int32_t)pl.end;
+  a.window = window_tokens > 0 ? window_tokens : 0;
   a.part_base = (int32_t)pl.base;
   a.part_tokens = (int32_t)pl.part_tokens;
   a.nparts = (int32_t)pl.nparts;

@@ -81,6 +81,7 @@ struct PrefillArgs {
   int32_t rows, tokens, hq, hkv, group, page, num_pages, max_pages;
   int32_t kv_begin;         // first key position attended (>= 0)
   int32_t kv_end;           // one past the last key position (already capped at max_pages * page)
+  int32_t window;           // sliding window: a query sees its last `window` positions (<= 0: no window)
   int32_t part_base;        // kv_begin rounded down to a page boundary: partitions start here
   int32_t part_tokens;      // a multiple of page
   int32_t nparts, col_groups, final_out;

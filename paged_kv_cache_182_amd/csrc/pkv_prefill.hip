@@ -3,7 +3,9 @@
 //
 // A chunk of T new query tokens per row has been appended to the cache; query
 // t sits at position L - T + t and attends, causally, the cached keys up to
-// its own position, restricted to a key window [kv_begin, kv_end). The key
+// its own position, restricted to a key window [kv_begin, kv_end) and, with a
+// sliding window of W, to its last W positions (ARGUS v0.5: sliding-window
+// masks). The key
 // range is cut into partitions attended in parallel and folded by their
 // log-sum-exp (FreeToken PR #499 discussion, in-place host K/V design: a
 // prefill attends window by window and folds the windows into an fp32
@@ -377,22 +379,29 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
   const int c_first = cg * COLS;
   const int c_last = min(c_first + COLS, ncols) - 1;  // >= c_first: the host launches no empty group
   const int wg_hi = min(p_hi, L - T + c_last / G + 1);
+  // key limits of the column of query token t: [lo_of(t), hi_of(t))
+  auto hi_of = [&](int t) { return min(p_hi, L - T + t + 1); };
+  auto lo_of = [&](int t) { return a.window > 0 ? max(p_lo, L - T + t + 1 - a.window) : p_lo; };
+  const int wg_lo = lo_of(c_first / G);
   // this wave's columns
   const int w_first = c_first + 32 * wave;
   const int w_last = min(w_first + 32, ncols) - 1;
   const bool wave_live = w_first < ncols;
-  const int w_hi_min = min(p_hi, L - T + w_first / G + 1);
-  const int w_hi_max = wave_live ? min(p_hi, L - T + w_last / G + 1) : p_lo;
+  const int w_hi_min = hi_of(w_first / G);
+  const int w_hi_max = wave_live ? hi_of(w_last / G) : p_lo;
+  const int w_lo_min = lo_of(w_first / G);
+  const int w_lo_max = wave_live ? lo_of(w_last / G) : p_lo;
 
   // ---- q (B operand of the score MFMA), natural dim order
   h8 qf[NBC][NC];
-  int hi_col[NBC];  // key limit of the lane's column in each block
+  int hi_col[NBC], lo_col[NBC];  // key limits of the lane's column in each block
 #pragma unroll
   for (int cb = 0; cb < NBC; ++cb) {
     const int c = w_first + 16 * cb + col;
     const bool real = c < ncols;
     const int t = real ? c / G : 0, g = real ? c % G : 0;
-    hi_col[cb] = real ? min(p_hi, L - T + t + 1) : p_lo;
+    hi_col[cb] = real ? hi_of(t) : p_lo;
+    lo_col[cb] = real ? lo_of(t) : p_lo;
     const _Float16* qrow = reinterpret_cast<const _Float16*>(a.q) + (((size_t)b * T + t) * a.hq + (size_t)h * G + g) * D;
 #pragma unroll
     for (int c2 = 0; c2 < NC; ++c2)
@@ -417,8 +426,8 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
   // ---- tiles [t0, t0 + 16 ntiles): 16-token tiles of the partition up to
   // the last key any column of the workgroup attends
-  const int t0 = p_lo & ~15;
-  const int ntiles = wg_hi > p_lo ? (wg_hi - t0 + 15) / 16 : 0;
+  const int t0 = wg_lo & ~15;
+  const int ntiles = wg_hi > wg_lo ? (wg_hi - t0 + 15) / 16 : 0;
   const int t_end = t0 + 16 * ntiles;
   const int tpp = P / 16;
 
@@ -500,7 +509,7 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
         mt[s] = meta(i + RING);
         issue<D>(raw[s], mt[s], a, h, wave, lane);
         lds_barrier();
-        if (m.valid <= 0 || !wave_live || m.j0 >= w_hi_max) continue;
+        if (m.valid <= 0 || !wave_live || m.j0 >= w_hi_max || m.j0 + 16 <= w_lo_min) continue;
 
         // ---- operands of this tile
         h8 kf[NC];
@@ -528,7 +537,7 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
             for (int g = 0; g < NC; ++g) vsc[j][g] = st.vs[(4 * kq + j) * NC + g];
         }
-        const bool masked = m.j0 < p_lo || m.j0 + 16 > w_hi_min;
+        const bool masked = m.j0 < w_lo_max || m.j0 + 16 > w_hi_min;
         // scores in log2 units are raw * f: f > 0 goes into the max and the exp
         const float f = kint ? a.scale_log2 : a.scale_log2 * m.sk;
         if (m.sv != sv_cur) {  // another V scale (1 for pages without FP8 V)
@@ -566,7 +575,7 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int pos = m.j0 + 4 * kq + j;
-              s[j] = (pos >= p_lo && pos < hi_col[cb]) ? s[j] : NEG_INF;
+              s[j] = (pos >= lo_col[cb] && pos < hi_col[cb]) ? s[j] : NEG_INF;
             }
           }
           const float mx = row4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * f;

@@ -141,7 +141,7 @@ def pcall(p, T=16, kv_begin=0, kv_end=-1, **ptrs):
     vals.update(ptrs)
     ws = vals.pop("ws", 0)
     wsb = vals.pop("wsb", 0)
-    return pkv.load().pkv_prefill_attention(ctypes.byref(p), T, kv_begin, kv_end, *[vals[n] for n in names],
+    return pkv.load().pkv_prefill_attention(ctypes.byref(p), T, kv_begin, kv_end, 0, *[vals[n] for n in names],
                                             ws, wsb, 0, 0)
 
 

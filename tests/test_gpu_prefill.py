@@ -37,22 +37,23 @@ def small(seq_lens, kc, vc, hq, hkv, dim, page, seed=7, **kw):
                                 seed=seed, **kw)
 
 
-def run_prefill(w, q, kv_begin=0, kv_end=-1, partition_tokens=0, dw=None, expect_err=0, **pk):
+def run_prefill(w, q, kv_begin=0, kv_end=-1, partition_tokens=0, dw=None, expect_err=0, window=0, **pk):
     dw = dw or to_device(w)
     p = params_for(w, partition_tokens, **pk)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     qd = torch.from_numpy(np.ascontiguousarray(q)).cuda()
     out, lse = pkv.prefill_attention(p, qd, dw.pool, dw.page_k_off, dw.page_v_off, dw.page_codec, dw.page_scale,
-                                     dw.block_table, dw.seq_lens, kv_begin=kv_begin, kv_end=kv_end, err_count=err)
+                                     dw.block_table, dw.seq_lens, kv_begin=kv_begin, kv_end=kv_end, window=window,
+                                     err_count=err)
     torch.cuda.synchronize()
     assert int(err.item()) == expect_err
     return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def check(w, T, kv_begin=0, kv_end=-1, partition_tokens=0, seed=3, what="", q_scale=1.0, **pk):
+def check(w, T, kv_begin=0, kv_end=-1, partition_tokens=0, seed=3, what="", q_scale=1.0, window=0, **pk):
     q = synth.prefill_queries(seed, w.rows, T, w.num_q_heads, w.head_dim, q_scale)
-    out, lse = run_prefill(w, q, kv_begin, kv_end, partition_tokens, **pk)
-    ref_o, ref_l = oracle.prefill_attention(w, q, kv_begin, None if kv_end < 0 else kv_end)
+    out, lse = run_prefill(w, q, kv_begin, kv_end, partition_tokens, window=window, **pk)
+    ref_o, ref_l = oracle.prefill_attention(w, q, kv_begin, None if kv_end < 0 else kv_end, window=window)
     return compare(out, lse, ref_o, ref_l, what or f"{w.name} T={T} kv=[{kv_begin},{kv_end}) pt={partition_tokens}")
 
 
@@ -192,3 +193,21 @@ def test_partition_sizes_agree():
         assert eo <= SPLIT_OUT_TOL and el <= SPLIT_LSE_TOL
     ref_o, ref_l = oracle.prefill_attention(w, q)
     compare(ref[0], ref[1], ref_o, ref_l, "3000 tokens, 64 queries")
+
+
+@pytest.mark.parametrize("window", [1, 7, 16, 100, 333, 4096])
+def test_sliding_window(window):
+    """Sliding-window attention (each query sees its last W positions); T = 1
+    is sliding-window decode."""
+    print(f"case window={window}", flush=True)
+    w = poison_tails(small([1, 40, 300, 1000], FP8, INT8, hq=16, hkv=2, dim=128, page=16))
+    check(w, 24, window=window, partition_tokens=64)
+    check(w, 1, window=window, partition_tokens=0)
+    check(w, 37, 100, 900, window=window, partition_tokens=0)
+
+
+def test_sliding_window_mixed_codecs_and_groups():
+    pairs = [(FP16, FP16), (FP8, FP8), (INT8, INT4), (BF16, FP8)]
+    w = poison_tails(small([700, 129], 0, 0, hq=14, hkv=2, dim=64, page=32,
+                           codec_of=lambda r, lp: pairs[(r + lp) % len(pairs)]))
+    check(w, 50, window=64, partition_tokens=64, k_codec=pkv.CODEC_MIXED, v_codec=pkv.CODEC_MIXED)
