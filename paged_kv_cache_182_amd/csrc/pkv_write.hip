@@ -71,23 +71,6 @@ __device__ inline uint16_t f_to_bf16(float x) {
   return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
 }
 
-// fp32 -> OCP e4m3 code, nearest even; |y| <= 448, finite.
-__device__ inline uint32_t f_to_e4m3(float y) {
-  const uint32_t bits = __builtin_bit_cast(uint32_t, y);
-  const uint32_t sign = (bits >> 31) << 7;
-  const float a = __builtin_fabsf(y);
-  uint32_t code;
-  if (a < 0.015625f) {                 // below 2^-6: subnormal steps of 2^-9
-    code = (uint32_t)__builtin_rintf(a * 512.0f);   // 0..8; 8 is the smallest normal
-  } else {
-    int E = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFF) - 127;   // -6 .. 8
-    float r = __builtin_rintf(__builtin_ldexpf(a, 3 - E));                 // 8 .. 16
-    if (r >= 16.0f) { r = 8.0f; ++E; }
-    code = (uint32_t)((E + 7) << 3) + (uint32_t)r - 8u;
-  }
-  return sign | code;
-}
-
 __device__ inline void count_err(int32_t* err) {
   if (err) atomicAdd(err, 1);
 }
@@ -150,8 +133,24 @@ __device__ __attribute__((always_inline)) inline void emit_run(const float (*x)[
   uint32_t word[RD / 4];
 #pragma unroll
   for (int k = 0; k < RD / 4; ++k) word[k] = 0;
+  if constexpr (DC == W_FP8) {
+    // two elements per hardware conversion (OCP e4m3, nearest even) after the
+    // correctly rounded quotient is clipped to +-448
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
+    for (int e = 0; e < E; e += 2) {
+      int tt0, d0, tt1, d1;
+      run_elem(lane, e, D, IS_V, GROUPED, tt0, d0);
+      run_elem(lane, e + 1, D, IS_V, GROUPED, tt1, d1);
+      const float y0 = fminf(fmaxf(__fdiv_rn(x[tt0][d0], s8), -448.0f), 448.0f);
+      const float y1 = fminf(fmaxf(__fdiv_rn(x[tt1][d1], s8), -448.0f), 448.0f);
+      if ((e >> 1) & 1)
+        word[e >> 2] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, (int)word[e >> 2], true);
+      else
+        word[e >> 2] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, (int)word[e >> 2], false);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < (DC == W_FP8 ? 0 : E); ++e) {
     int tt, d;
     run_elem(lane, e, D, IS_V, GROUPED, tt, d);
     const float v = x[tt][d];
@@ -160,8 +159,6 @@ __device__ __attribute__((always_inline)) inline void emit_run(const float (*x)[
       code = __builtin_bit_cast(uint16_t, (_Float16)v);
     } else if constexpr (DC == W_BF16) {
       code = f_to_bf16(v);
-    } else if constexpr (DC == W_FP8) {
-      code = f_to_e4m3(fminf(fmaxf(__fdiv_rn(v, s8), -448.0f), 448.0f));
     } else {
       const float q = __builtin_rintf(__fdiv_rn(v, sc[tt][d / 32]));
       code = (uint32_t)(int)fminf(fmaxf(q, -QMAX), QMAX);
