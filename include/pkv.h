@@ -248,7 +248,8 @@ int pkv_append_kv(const pkv_params* p, const void* k_new, const void* v_new, uin
  *                        1 if the block is all zero; code = e4m3 nearest to
  *                        fp32(x / s), ties to even.
  *                   INT8/INT4: s = fp16(fp32(absmax) / qmax) per (token, 32
- *                        dims), qmax 127 / 7, 1 if the group is all zero;
+ *                        dims), qmax 127 / 7, kept inside fp16's finite range
+ *                        [2^-24, 65504], 1 if the group is all zero;
  *                        code = clip(rint(fp32(x) / fp32(s)), -qmax, qmax).
  *                   BF16/FP16: the value, rounded to nearest even.
  *   page_codec    page_codec[dst] is set to dst_codec.

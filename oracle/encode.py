@@ -20,9 +20,11 @@ What the device path computes (the write side of the paged cache):
     value nearest to fp32(x / s), ties to the even code. |x / s| <= 448 up to
     the rounding of the division, and the quotient is clipped to +-448.
   - INT8 / INT4: one fp16 scale per (token, group of 32 dims),
-    s = fp16(fp32(absmax) / qmax) with qmax 127 / 7, or 1 for an all-zero
-    group; the code is clip(rint(fp32(x) / fp32(s)), -qmax, qmax), rint
-    rounding half to even.
+    s = fp16(fp32(absmax) / qmax) with qmax 127 / 7, kept inside fp16's
+    positive finite range [2^-24, 65504] (a tiny group's scale would round to
+    0, a huge BF16 group's to infinity), or 1 for an all-zero group; the
+    code is clip(rint(fp32(x) / fp32(s)), -qmax, qmax), rint rounding half
+    to even.
 
   Every code is decided in fp32 (the division and the rounding), the
   precision the device path computes in.
@@ -77,7 +79,9 @@ def encode_groups_int(x: np.ndarray, qmax: int) -> tuple[np.ndarray, np.ndarray]
     p, d = x.shape
     g = x.reshape(p, d // 32, 32)
     amax = np.max(np.abs(g), axis=-1).astype(np.float32)
-    s = (amax / np.float32(qmax)).astype(np.float32).astype(np.float16)
+    with np.errstate(over="ignore"):                      # a huge group's scale overflows, then is clamped
+        s = (amax / np.float32(qmax)).astype(np.float32).astype(np.float16)
+    s = np.minimum(np.maximum(s, np.float16(2.0 ** -24)), np.float16(65504.0))   # inside fp16's finite range
     s = np.where(amax == 0, np.float16(1.0), s)
     q = np.rint((g / s.astype(np.float32)[..., None]).astype(np.float32))
     return np.clip(q, -qmax, qmax).astype(np.int8).reshape(p, d), s

@@ -310,7 +310,11 @@ __global__ void __launch_bounds__(64 * TILES) encode_kernel(EncodeArgs a) {
         float m = 0.f;
 #pragma unroll 8
         for (int j = 0; j < 32; ++j) m = fmaxf(m, __builtin_fabsf(xs[slot][tt][32 * g + j]));
-        const _Float16 s16 = m == 0.f ? (_Float16)1.0f : (_Float16)__fdiv_rn(m, qmax);
+        // fp16 scale kept inside its positive finite range [2^-24, 65504]
+        _Float16 s16 = (_Float16)__fdiv_rn(m, qmax);
+        s16 = s16 == (_Float16)0.0f ? __builtin_bit_cast(_Float16, (uint16_t)0x0001) : s16;
+        s16 = s16 > (_Float16)65504.0f ? (_Float16)65504.0f : s16;
+        s16 = m == 0.f ? (_Float16)1.0f : s16;
         scs[slot][tt][g] = (float)s16;
         const size_t so16 = (size_t)hkv * P * D * dbits / 8 + ((size_t)h * P + 16 * tile + tt) * G * 2 + 2 * g;
         *reinterpret_cast<_Float16*>(a.pool + dof + so16) = s16;

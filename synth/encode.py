@@ -45,8 +45,11 @@ def encode_int_g32(x: np.ndarray, qmax: int) -> tuple[np.ndarray, np.ndarray]:
     assert d % 32 == 0
     g = x.reshape(*x.shape[:-1], d // 32, 32)
     amax = np.max(np.abs(g), axis=-1)
-    s16 = (amax / np.float32(qmax)).astype(np.float16)
-    s16 = np.where(s16 == 0, np.float16(1.0), s16)
+    with np.errstate(over="ignore"):
+        s16 = (amax / np.float32(qmax)).astype(np.float16)
+    # kept inside fp16's positive finite range; an all-zero group gets 1
+    s16 = np.clip(s16, np.float16(2.0 ** -24), np.float16(65504.0))
+    s16 = np.where(amax == 0, np.float16(1.0), s16)
     s32 = s16.astype(np.float32)[..., None]
     c = np.clip(np.rint(g / s32), -qmax, qmax).astype(np.int8)
     return c.reshape(x.shape), s16

@@ -238,3 +238,39 @@ def test_encode_rounding_ties(dst):
     ref, rs, rc = oracle_encode(pool, koff, voff, codec, scale, src, dst_ids, dst | dst << 4, hkv, P, D)
     assert np.array_equal(pool_t.cpu().numpy(), ref)
     assert np.array_equal(scale_t.cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("dst", [INT8, INT4])
+@pytest.mark.parametrize("src", [FP16, BF16])
+def test_encode_extreme_int_groups(dst, src):
+    """Groups whose scale leaves fp16's finite range: a group of fp16
+    subnormals (scale clamped to 2^-24) and, from BF16, huge groups (scale
+    clamped to 65504, codes saturated); bit-exact with the oracle."""
+    print(f"case extreme groups src={src} dst={dst}", flush=True)
+    hkv, P, D = 1, 16, 64
+    rng = np.random.default_rng(src * 10 + dst)
+    x = rng.standard_normal((P, D)).astype(np.float32)
+    x[:, :32] = np.float32(2.0 ** -24) * rng.integers(-3, 4, (P, 32)).astype(np.float32)   # fp16 subnormals
+    x[0, :32] = 0.0                                                                          # one all-zero group
+    if src == BF16:
+        x[:8, 32:] = np.float32(1e30) * rng.standard_normal((8, 32)).astype(np.float32)
+        x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    else:
+        x = x.astype(np.float16).astype(np.float32)
+    kb, _ = slay.encode_plane(np.stack([x])[None], src, v_order=False)
+    vb, _ = slay.encode_plane(np.stack([x])[None], src, v_order=True)
+    sk = align(slay.plane_bytes(src, hkv, P, D))
+    dk = align(slay.plane_bytes(dst, hkv, P, D))
+    pool = np.zeros(2 * sk + 2 * dk, np.uint8)
+    pool[:len(kb[0])], pool[sk:sk + len(vb[0])] = kb[0], vb[0]
+    koff = np.array([0, 2 * sk], np.uint64)
+    voff = np.array([sk, 2 * sk + dk], np.uint64)
+    codec = np.array([src | src << 4, 0x77], np.uint8)
+    scale = np.zeros((2, hkv, 2), np.float32)
+    srcs, dsts = np.array([0], np.int32), np.array([1], np.int32)
+    pool_t, koff_t, voff_t, codec_t, scale_t, src_t, dst_t = to_dev(pool, koff, voff, codec, scale, srcs, dsts)
+    p = params(2, hkv, P, D, pool.size)
+    pkv.encode_pages(p, src_t, dst_t, dst | dst << 4, pool_t, koff_t, voff_t, codec_t, scale_t)
+    torch.cuda.synchronize()
+    ref, rs, rc = oracle_encode(pool, koff, voff, codec, scale, srcs, dsts, dst | dst << 4, hkv, P, D)
+    assert np.array_equal(pool_t.cpu().numpy(), ref)

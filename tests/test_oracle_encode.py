@@ -94,6 +94,26 @@ def test_int_groups_closed_forms_and_bound(qmax):
 
 
 @pytest.mark.parametrize("qmax", [127, 7])
+def test_int_scale_stays_inside_fp16_range(qmax):
+    """A group whose absmax / qmax rounds to 0 in fp16 gets the smallest
+    positive fp16 scale 2^-24 (codes x / 2^-24, exact here); one whose scale
+    overflows gets 65504 and saturated codes."""
+    x = np.zeros((2, 64), np.float32)
+    x[0, :32] = np.float32(2.0 ** -24) * np.array([1, -1] * 16, np.float32)   # fp16 min subnormal
+    x[0, 32:] = np.float32(2.0 ** -23)
+    x[1, :32] = np.float32(1e30) * np.array([1, -1] * 16, np.float32)          # a BF16-range group
+    x[1, 32:] = np.float32(1e6)
+    codes, s = encode_groups_int(x, qmax)
+    assert s[0, 0] == np.float16(2.0 ** -24) and s[0, 1] == np.float16(2.0 ** -24)
+    assert np.array_equal(codes[0, :32], np.array([1, -1] * 16)) and np.all(codes[0, 32:] == 2)
+    assert s[1, 0] == np.float16(65504.0) and np.array_equal(codes[1, :32], np.array([qmax, -qmax] * 16))
+    want = np.float16(min(1e6 / qmax, 65504.0))
+    assert s[1, 1] == want and np.all(np.isfinite(codes.astype(np.float64)))
+    c_gen, s_gen = senc.encode_int_g32(x, qmax)
+    assert np.array_equal(codes, c_gen) and np.array_equal(s, s_gen)
+
+
+@pytest.mark.parametrize("qmax", [127, 7])
 def test_int_groups_equal_the_generator(qmax):
     x = np.random.default_rng(11).standard_normal((8, 64, 128)).astype(np.float16).astype(np.float32)
     c_gen, s_gen = senc.encode_int_g32(x, qmax)
