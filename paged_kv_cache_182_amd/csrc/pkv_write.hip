@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -330,6 +332,343 @@ __global__ void __launch_bounds__(64 * TILES) encode_kernel(EncodeArgs a) {
   }
 }
 
+// x / s for a scale s with r = RN(1 / s): one product and one correction.
+// Equal to the correctly rounded quotient on every code the encoder can
+// produce from the inputs it can meet (|x| <= the block's or group's absmax;
+// FP8 scales of at least 2^-100): checked exhaustively over every fp16 and
+// bf16 source value by tests/division/check_recip_div.c.
+__device__ inline float recip_div(float x, float s, float r) {
+  const float q0 = __fmul_rn(x, r);
+  return __builtin_fmaf(-__builtin_fmaf(q0, s, -x), r, q0);
+}
+
+// ------------------------------------------------------ encode, register path
+// Pages of up to four tiles (P <= 64): one wave per unit (page pair, KV head,
+// plane), units dealt round-robin over the waves of the grid. The wave holds
+// its unit's source in registers -- each lane the 16-byte chunks holding the
+// elements of its own destination run (its own source run, except for grouped
+// INT K, whose dims come from other lanes' runs) -- takes the FP8 block absmax
+// or the INT group maxima by cross-lane reductions, and writes its
+// destination run. The next unit's loads are issued before the current unit
+// is encoded, so they are in flight meanwhile. No barriers.
+
+constexpr int EW = 4;  // waves per workgroup
+
+__device__ inline float dpp_f(float x, int ctrl) {
+  switch (ctrl) {  // the control must be a constant
+    case 0xB1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+    case 0x4E: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+    case 0x141: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+    default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+  }
+}
+// max over the 16 lanes of this lane's row (quad swaps, then half-row and row mirrors)
+__device__ inline float row16_max(float x) {
+  x = fmaxf(x, dpp_f(x, 0xB1));
+  x = fmaxf(x, dpp_f(x, 0x4E));
+  x = fmaxf(x, dpp_f(x, 0x141));
+  return fmaxf(x, dpp_f(x, 0x140));
+}
+// max over lanes l, l^16, l^32, l^48
+__device__ inline float rows4_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+// element i (0..7) of a 16-byte chunk of 16-bit codes (BF16 or FP16), as float
+template <bool BF>
+__device__ inline float chunk_elem(const u4& x, int i) {
+  const uint32_t w = x[i >> 1];
+  if constexpr (BF) return __builtin_bit_cast(float, (i & 1) ? (w & 0xffff0000u) : (w << 16));
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)((i & 1) ? (w >> 16) : (w & 0xffffu)));
+}
+
+// Pair checks of unit (i, plane); the same answer in every lane.
+__device__ inline bool check_pair(const EncodeArgs& a, int i, int plane, int D, int& dst, int& scodec, int& dcodec,
+                                  uint64_t& so, uint64_t& dof) {
+  const int P = a.page, hkv = a.hkv;
+  const int src = a.src[i];
+  dst = a.dst[i];
+  dcodec = plane ? (a.dst_codec >> 4) : (a.dst_codec & 15);
+  bool ok = (unsigned)src < (unsigned)a.num_pages && (unsigned)dst < (unsigned)a.num_pages && src != dst;
+  scodec = 0;
+  so = 0;
+  dof = 0;
+  if (!ok) return false;
+  const int cb = a.codec[src];
+  ok = w16(cb & 15) && w16(cb >> 4);
+  scodec = plane ? (cb >> 4) : (cb & 15);
+  so = plane ? a.voff[src] : a.koff[src];
+  dof = plane ? a.voff[dst] : a.koff[dst];
+  const uint64_t sb = wplane_bytes(scodec, hkv, P, D), db = wplane_bytes(dcodec, hkv, P, D);
+  ok = ok && ((so | dof) & 15) == 0 && so <= a.pool_bytes && a.pool_bytes - so >= sb && dof <= a.pool_bytes &&
+       a.pool_bytes - dof >= db;
+  const uint64_t sk = a.koff[src], sv = a.voff[src];
+  const uint64_t skb = wplane_bytes(cb & 15, hkv, P, D), svb = wplane_bytes(cb >> 4, hkv, P, D);
+  return ok && (dof + db <= sk || sk + skb <= dof) && (dof + db <= sv || sv + svb <= dof);
+}
+
+// Source chunks of one unit: tile t, chunk c (elements 8c .. 8c+7 of the lane's
+// destination run).
+template <int D, int NT>
+struct UnitSrc {
+  static constexpr int NC = D / 32;
+  u4 x[NT][NC];
+};
+
+template <int D, int NT>
+__device__ inline void load_unit(UnitSrc<D, NT>& u, const uint8_t* sp, bool grouped_k, int lane) {
+  constexpr int NC = D / 32;
+  constexpr int RS = D / 2;  // 16-bit source run bytes
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const uint8_t* ts = sp + (size_t)t * 16 * D * 2;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint32_t off;
+      if (grouped_k) {  // dims 32c + 8(lane/16) .. +7 of token lane%16, from the lane whose run holds them
+        const int d0 = 32 * c + 8 * (lane >> 4);
+        const int ls = 16 * (d0 / (D / 4)) + (lane & 15);
+        off = run_byte(ls, 2 * (d0 % (D / 4)), RS);
+      } else {
+        off = run_byte(lane, 16 * c, RS);
+      }
+      u.x[t][c] = *reinterpret_cast<const u4*>(ts + off);
+    }
+  }
+}
+
+// Encode one tile's destination run from the lane's eight-element source
+// chunks x[c] (elements 8c .. 8c+7 of the run) and write it. INT scales come
+// as s2[j][g] with their reciprocals r2: element e uses entry (e % 4, e / 8)
+// (for V runs: token 4(lane/16) + e % 4, group e / 8; grouped K runs fill
+// every j of group g alike).
+template <int D, int DC, bool BF>
+__device__ inline void store_run(const u4* x, const float (*s2)[D / 32], const float (*r2)[D / 32], float s8, float r8,
+                                 bool fast8, uint8_t* td, int lane) {
+  constexpr int BITS = DC <= W_BF16 ? 16 : (DC == W_INT4 ? 4 : 8);
+  constexpr int E = D / 4, RD = D * BITS / 32;
+  constexpr float QMAX = DC == W_INT8 ? 127.0f : 7.0f;
+  uint32_t word[RD / 4];
+#pragma unroll
+  for (int k = 0; k < RD / 4; ++k) word[k] = 0;
+  if constexpr (DC == W_FP8) {
+#pragma unroll
+    for (int e = 0; e < E; e += 2) {
+      const float v0 = chunk_elem<BF>(x[e >> 3], e & 7), v1 = chunk_elem<BF>(x[e >> 3], (e + 1) & 7);
+      const float q0 = fast8 ? recip_div(v0, s8, r8) : __fdiv_rn(v0, s8);
+      const float q1 = fast8 ? recip_div(v1, s8, r8) : __fdiv_rn(v1, s8);
+      const float y0 = fminf(fmaxf(q0, -448.0f), 448.0f);
+      const float y1 = fminf(fmaxf(q1, -448.0f), 448.0f);
+      if ((e >> 1) & 1)
+        word[e >> 2] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, (int)word[e >> 2], true);
+      else
+        word[e >> 2] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, (int)word[e >> 2], false);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float v = chunk_elem<BF>(x[e >> 3], e & 7);
+      uint32_t code;
+      if constexpr (DC == W_FP16) {
+        code = __builtin_bit_cast(uint16_t, (_Float16)v);
+      } else if constexpr (DC == W_BF16) {
+        code = f_to_bf16(v);
+      } else {
+        const float q = __builtin_rintf(recip_div(v, s2[e & 3][e >> 3], r2[e & 3][e >> 3]));
+        code = (uint32_t)(int)fminf(fmaxf(q, -QMAX), QMAX);
+      }
+      if constexpr (BITS == 16) {
+        word[e >> 1] |= (code & 0xFFFFu) << (16 * (e & 1));
+      } else if constexpr (BITS == 8) {
+        word[e >> 2] |= (code & 0xFFu) << (8 * (e & 3));
+      } else {
+        const int r = e & 7, nslot = (r & 1) * 4 + (r >> 1);
+        word[e >> 3] |= (code & 0xFu) << (4 * nslot);
+      }
+    }
+  }
+  if constexpr (RD >= 16) {
+#pragma unroll
+    for (int c = 0; c < RD / 16; ++c)
+      *reinterpret_cast<u4*>(td + run_byte(lane, 16 * c, RD)) =
+          u4{word[4 * c], word[4 * c + 1], word[4 * c + 2], word[4 * c + 3]};
+  } else {
+    *reinterpret_cast<uint2*>(td + run_byte(lane, 0, RD)) = uint2{word[0], word[1]};
+  }
+}
+
+template <int D, int NT>
+__global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int nunits) {
+  constexpr int NC = D / 32, E = D / 4;
+  __shared__ float sx[EW][4][16];  // per wave: INT V scales of its tile, [row][combo]
+  __shared__ float rx[EW][4][16];  // and their reciprocals RN(1 / s)
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int gw = blockIdx.x * EW + wv, nw = gridDim.x * EW;
+  const int P = a.page, hkv = a.hkv;
+  const int kq = lane >> 4, l16 = lane & 15;
+
+  auto unit_of = [&](int u, int& i, int& h, int& plane) {
+    plane = u & 1;
+    h = (u >> 1) % hkv;
+    i = (u >> 1) / hkv;
+  };
+  // the next unit is prefetched while the current one is encoded when both fit
+  // in registers; larger units are loaded at the start of their turn and
+  // other waves hide the latency
+  constexpr bool PREFETCH = NT * NC <= 8;
+  UnitSrc<D, NT> cur, nxt;
+  int u = gw;
+  bool have = false;
+  int i = 0, h = 0, plane = 0, dst = 0, scodec = 0, dcodec = 0;
+  uint64_t so = 0, dof = 0;
+  bool ok = false;
+  if (u < nunits) {
+    unit_of(u, i, h, plane);
+    ok = check_pair(a, i, plane, D, dst, scodec, dcodec, so, dof);
+    if (ok) load_unit<D, NT>(cur, a.pool + so + (size_t)h * P * D * 2, wint(dcodec) && plane == 0, lane);
+    have = true;
+  }
+  while (have) {
+    // the next unit's checks and loads first
+    const int un = u + nw;
+    int i2 = 0, h2 = 0, plane2 = 0, dst2 = 0, scodec2 = 0, dcodec2 = 0;
+    uint64_t so2 = 0, dof2 = 0;
+    bool ok2 = false;
+    const bool have2 = un < nunits;
+    if (have2) {
+      unit_of(un, i2, h2, plane2);
+      ok2 = check_pair(a, i2, plane2, D, dst2, scodec2, dcodec2, so2, dof2);
+      if (PREFETCH && ok2) load_unit<D, NT>(nxt, a.pool + so2 + (size_t)h2 * P * D * 2, wint(dcodec2) && plane2 == 0, lane);
+    }
+
+    if (!ok) {
+      if (h == 0 && plane == 0 && lane == 0) count_err(a.err);
+    } else {
+      // the unit's work, compiled once per source codec (the choice is per unit)
+      auto work = [&](auto bf_tag) {
+        constexpr bool BF = decltype(bf_tag)::value;
+        const bool is_v = plane == 1;
+        const int dbits = wbits(dcodec);
+        uint8_t* dp = a.pool + dof + (size_t)h * P * D * dbits / 8;
+        // FP8: absmax of the whole (page, head, plane) block
+        float s8 = 1.f;
+        if (dcodec == W_FP8) {
+          float m = 0.f;
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+              for (int k = 0; k < 8; ++k) m = fmaxf(m, __builtin_fabsf(chunk_elem<BF>(cur.x[t][c], k)));
+          m = rows4_max(row16_max(m));
+          s8 = m == 0.f ? 1.f : __fdiv_rn(m, 448.0f);
+        }
+        const float r8 = __fdiv_rn(1.0f, s8);
+        const bool fast8 = s8 >= 0x1p-100f;  // smaller scales keep the correctly rounded division
+        // the conversions of the absmax pass are recomputed below, not kept
+        // live across it (an empty asm hides the chunks' values)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(cur.x[t][c]));
+        if (lane == 0 && a.scale) a.scale[((size_t)dst * hkv + h) * 2 + plane] = s8;
+        if (h == 0 && plane == 0 && lane == 0) a.codec_out[dst] = (uint8_t)a.dst_codec;
+        const float qmax = dcodec == W_INT8 ? 127.0f : 7.0f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const u4* x = cur.x[t];
+          float s2[4][NC], r2[4][NC];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < NC; ++g) s2[j][g] = r2[j][g] = 1.f;
+          if (wint(dcodec)) {
+            const size_t sc_base = (size_t)hkv * P * D * dbits / 8 + ((size_t)h * P + 16 * t) * NC * 2;
+            auto scale_of = [&](float m) {  // fp16 scale kept inside fp16's finite range
+              _Float16 s16 = (_Float16)__fdiv_rn(m, qmax);
+              s16 = s16 == (_Float16)0.0f ? __builtin_bit_cast(_Float16, (uint16_t)0x0001) : s16;
+              s16 = s16 > (_Float16)65504.0f ? (_Float16)65504.0f : s16;
+              return m == 0.f ? (_Float16)1.0f : s16;
+            };
+            if (is_v) {
+              // group g of token 4kq + j: elements 8g + j and 8g + 4 + j on the 16 lanes of row kq;
+              // lane l16 < 4 NC of each row computes combo (j, g) = (l16 / NC, l16 % NC)
+              float mine = 0.f;
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int g = 0; g < NC; ++g) {
+                  const float mg = row16_max(fmaxf(__builtin_fabsf(chunk_elem<BF>(x[g], j)),
+                                                   __builtin_fabsf(chunk_elem<BF>(x[g], 4 + j))));
+                  mine = (l16 == j * NC + g) ? mg : mine;
+                }
+              if (l16 < 4 * NC) {
+                const _Float16 s16 = scale_of(mine);
+                sx[wv][kq][l16] = (float)s16;
+                rx[wv][kq][l16] = __fdiv_rn(1.0f, (float)s16);
+                const int j = l16 / NC, g = l16 % NC;
+                *reinterpret_cast<_Float16*>(a.pool + dof + sc_base + ((size_t)(4 * kq + j) * NC + g) * 2) = s16;
+              }
+              __builtin_amdgcn_wave_barrier();
+              __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int g = 0; g < NC; ++g) {
+                  s2[j][g] = sx[wv][kq][j * NC + g];
+                  r2[j][g] = rx[wv][kq][j * NC + g];
+                }
+              __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+              __builtin_amdgcn_wave_barrier();
+            } else {
+              // grouped K: chunk c is group c of token lane%16, spread over the 4 rows
+#pragma unroll
+              for (int c = 0; c < NC; ++c) {
+                float m = 0.f;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) m = fmaxf(m, __builtin_fabsf(chunk_elem<BF>(x[c], k)));
+                m = rows4_max(m);
+                const _Float16 s16 = scale_of(m);
+                const float sf = (float)s16, rf = __fdiv_rn(1.0f, sf);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  s2[j][c] = sf;
+                  r2[j][c] = rf;
+                }
+                if (kq == (c & 3) && (NC == 4 || kq < NC))
+                  *reinterpret_cast<_Float16*>(a.pool + dof + sc_base + ((size_t)l16 * NC + c) * 2) = s16;
+              }
+            }
+          }
+          uint8_t* td = dp + (size_t)t * 16 * D * dbits / 8;
+          switch (dcodec) {
+            case W_FP16: store_run<D, W_FP16, BF>(x, s2, r2, s8, r8, fast8, td, lane); break;
+            case W_BF16: store_run<D, W_BF16, BF>(x, s2, r2, s8, r8, fast8, td, lane); break;
+            case W_FP8: store_run<D, W_FP8, BF>(x, s2, r2, s8, r8, fast8, td, lane); break;
+            case W_INT8: store_run<D, W_INT8, BF>(x, s2, r2, s8, r8, fast8, td, lane); break;
+            default: store_run<D, W_INT4, BF>(x, s2, r2, s8, r8, fast8, td, lane); break;
+          }
+        }
+      };
+      if (scodec == W_BF16) work(std::integral_constant<bool, true>{});
+      else work(std::integral_constant<bool, false>{});
+    }
+    have = have2;
+    u = un;
+    i = i2; h = h2; plane = plane2; dst = dst2; scodec = scodec2; dcodec = dcodec2; so = so2; dof = dof2; ok = ok2;
+    if constexpr (PREFETCH) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) cur.x[t][c] = nxt.x[t][c];
+    } else if (have && ok) {
+      load_unit<D, NT>(cur, a.pool + so + (size_t)h * P * D * 2, wint(dcodec) && plane == 0, lane);
+    }
+  }
+}
+
 }  // namespace
 
 int launch_append(const AppendArgs& a, void* stream) {
@@ -338,24 +677,42 @@ int launch_append(const AppendArgs& a, void* stream) {
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
+namespace {
+
+template <int D, int NT>
+void launch_encode_reg(const EncodeArgs& a, hipStream_t s) {
+  const int nunits = a.n * a.hkv * 2;
+  int wgs = (nunits + EW - 1) / EW;
+  if (wgs > 4096) wgs = 4096;  // waves loop over the rest, prefetching the next unit
+  hipLaunchKernelGGL((encode_reg_kernel<D, NT>), dim3(wgs), dim3(64 * EW), 0, s, a, nunits);
+}
+
+}  // namespace
+
 int launch_encode(const EncodeArgs& a, void* stream) {
   if (a.n == 0) return 0;
-  const dim3 grid(a.n, a.hkv, 2);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int tiles = a.page >= 64 ? 4 : a.page / 16;     // page is a multiple of 16
-  if (a.head_dim == 64) {
-    if (tiles >= 4) hipLaunchKernelGGL((encode_kernel<64, 4>), grid, dim3(256), 0, s, a);
-    else if (tiles == 3) hipLaunchKernelGGL((encode_kernel<64, 3>), grid, dim3(192), 0, s, a);
-    else if (tiles == 2) hipLaunchKernelGGL((encode_kernel<64, 2>), grid, dim3(128), 0, s, a);
-    else hipLaunchKernelGGL((encode_kernel<64, 1>), grid, dim3(64), 0, s, a);
-  } else if (a.head_dim == 128) {
-    if (tiles >= 4) hipLaunchKernelGGL((encode_kernel<128, 4>), grid, dim3(256), 0, s, a);
-    else if (tiles == 3) hipLaunchKernelGGL((encode_kernel<128, 3>), grid, dim3(192), 0, s, a);
-    else if (tiles == 2) hipLaunchKernelGGL((encode_kernel<128, 2>), grid, dim3(128), 0, s, a);
-    else hipLaunchKernelGGL((encode_kernel<128, 1>), grid, dim3(64), 0, s, a);
-  } else {
-    return -2;
+  const int tiles = a.page / 16;  // page is a multiple of 16
+  if (a.head_dim != 64 && a.head_dim != 128) return -2;
+  if (tiles <= 4 && (long long)a.n * a.hkv * 2 <= 0x7fffffff) {
+    // register path: one wave per (pair, head, plane)
+#define PKV_REG(DD)                                                   \
+  if (tiles == 4) launch_encode_reg<DD, 4>(a, s);                     \
+  else if (tiles == 3) launch_encode_reg<DD, 3>(a, s);                \
+  else if (tiles == 2) launch_encode_reg<DD, 2>(a, s);                \
+  else launch_encode_reg<DD, 1>(a, s);
+    if (a.head_dim == 64) {
+      PKV_REG(64)
+    } else {
+      PKV_REG(128)
+    }
+#undef PKV_REG
+    return hipGetLastError() == hipSuccess ? 0 : -4;
   }
+  // longer pages: staged through LDS, four tiles at a time
+  const dim3 grid(a.n, a.hkv, 2);
+  if (a.head_dim == 64) hipLaunchKernelGGL((encode_kernel<64, 4>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((encode_kernel<128, 4>), grid, dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -1,0 +1,23 @@
+"""The page encoder's division (a reciprocal and one fused correction) decides
+every stored code exactly as correctly rounded division does, over every
+input the encoder can meet: an exhaustive check over all fp16 and bf16 source
+values, in C (tests/division/check_recip_div.c), no GPU."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "division", "check_recip_div.c")
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_reciprocal_division_is_exact_on_reachable_inputs(tmp_path):
+    exe = str(tmp_path / "check_recip_div")
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-o", exe, SRC, "-lm"], check=True)
+    env = dict(os.environ, OMP_NUM_THREADS=str(min(os.cpu_count() or 1, 16)))
+    res = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=900)
+    print(res.stdout)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert res.stdout.split() == ["fp8_fp16", "0", "fp8_bf16", "0", "int_fp16", "0", "int_bf16", "0"]

@@ -84,6 +84,7 @@ def oracle_encode(pool, koff, voff, codec, scale, src, dst, dst_codec, hkv, P, D
 CASES = [  # (K codec, V codec, head_dim, page)
     (FP8, FP8, 128, 64), (INT8, INT4, 128, 16), (INT8, INT8, 64, 32), (INT4, INT4, 64, 16),
     (FP8, INT4, 128, 32), (BF16, BF16, 64, 16), (FP16, FP8, 128, 16),
+    (INT8, INT4, 128, 48), (FP8, FP8, 64, 128), (INT8, FP8, 128, 256),   # three tiles; longer pages
 ]
 
 
