@@ -13,16 +13,20 @@
 //
 // Work unit: one workgroup of four waves owns (partition, KV head, row, group
 // of 128 query columns), a column being one (query token, query head of the
-// KV head's group) pair; each wave owns 32 columns. Every 16-token tile of
-// the partition is converted once, by the whole workgroup, from its page
-// codes into an fp16 image in LDS (double-buffered, one barrier per tile);
-// each wave then reads the image as MFMA operands:
-//  * scores: v_mfma_f32_16x16x32_f16, A = K (row = token, 8 dims per lane),
-//    B = q^T (col = query column); lane l gets tokens 4*(l/16) + j of column
-//    l % 16. The K image keeps dims in natural order: step c of lane l holds
-//    dims 32c + 8(l/16) .. +7, so one 32-dim step is one INT scale group.
-//  * P.V: v_mfma_f32_16x16x16_f16, A = P (the same four scores), B = V (four
-//    tokens of one dim, the V layout of every codec).
+// KV head's group) pair; each wave owns 32 columns. The partition's 16-token
+// tiles go two at a time: each pair is converted once, by the whole
+// workgroup, from its page codes into an fp16 image in LDS (double-buffered,
+// one barrier per pair); each wave then reads the image as MFMA operands:
+//  * scores: v_mfma_f32_16x16x32_f16 per tile, A = K (row = token, 8 dims
+//    per lane), B = q^T (col = query column); lane l gets tokens 4*(l/16) + j
+//    of column l % 16. The K image keeps dims in natural order: step c of
+//    lane l holds dims 32c + 8(l/16) .. +7, so one 32-dim step is one INT
+//    scale group.
+//  * one online-softmax update per pair, over the lane's eight scores.
+//  * P.V: v_mfma_f32_16x16x32_f16, A = P (the lane's four scores of each
+//    tile), B = V (the same tokens of one dim; the V layout of every codec
+//    gives a lane those four tokens, so the pair image interleaves the two
+//    tiles' runs).
 // Codes convert to fp16 exactly, and scales stay in fp32: FP8 K scales
 // multiply the scores, INT K group scales weight one score accumulator per
 // group, INT V group scales multiply the weights per group (fp16 scales, so a
@@ -51,7 +55,7 @@ constexpr int WAVES = 4;
 constexpr int THREADS = 64 * WAVES;
 constexpr int NBC = 2;                    // 16-column blocks per wave
 constexpr int COLS = 16 * NBC * WAVES;    // query columns per workgroup
-constexpr int RING = 2;                   // tiles of codes in flight per thread
+constexpr int PAIR_RING = 1;              // tile pairs of codes in flight per thread
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr float LN2 = 0.693147180559945309f;
 
@@ -157,6 +161,7 @@ struct TileMeta {
   int valid;            // tokens of the tile inside the row (0: dead tile)
   int kc, vc;
   int j0;               // position of the tile's first token
+  int sub;              // tile of the page (j0 = page start + 16 sub)
 };
 
 // Page descriptor staged in LDS (32 bytes).
@@ -226,7 +231,7 @@ __device__ inline void issue(Raw<D>& raw, const TileMeta& m, const PrefillArgs& 
   const int P = a.page;
   const rsrc_t rk = make_rsrc(a.pool + m.koff, live ? (uint32_t)plane_bytes(m.kc, a.hkv, P, D) : 0u);
   const rsrc_t rv = make_rsrc(a.pool + m.voff, live ? (uint32_t)plane_bytes(m.vc, a.hkv, P, D) : 0u);
-  const int sub = (m.j0 % P) / 16;
+  const int sub = m.sub;
   // INT group scales of the tile, 16 tokens x NC fp16 per plane: lanes
   // 0 .. 2NC-1 of wave 0 (K) and of wave 1 (V), 16 bytes each
   {
@@ -251,16 +256,18 @@ __device__ inline void issue(Raw<D>& raw, const TileMeta& m, const PrefillArgs& 
   }
 }
 
-// LDS image of one tile: K and V fp16 images (chunk c of lane L at c*1024 +
-// 16L bytes) and the INT group scales as fp32 [16 tokens][NC].
+// LDS image of one pair of tiles. K: one fp16 image per tile (chunk c of lane
+// L at [c*64 + L]). V: the P.V operand of the pair, dims 16n .. 16n+15 of
+// lane L at v[n][L]: tile A's four tokens 4(L/16) .. +3, then tile B's (the
+// order of the weights). INT group scales as fp32 [tile][16 tokens][NC].
 template <int D>
-struct Stage {
-  static constexpr int IMG = 32 * D;  // bytes of one fp16 image (16 tokens x D)
+struct PairStage {
+  static constexpr int IMG = 32 * D;  // bytes of one fp16 tile image (16 tokens x D)
   static constexpr int SCL = 16 * (D / 32);
-  u4 k[IMG / 16];
-  u4 v[IMG / 16];
-  float ks[SCL];
-  float vs[SCL];
+  u4 k[2][IMG / 16];
+  u4 v[D / 16][64];
+  float ks[2][SCL];
+  float vs[2][SCL];
 };
 
 template <int C>
@@ -269,25 +276,23 @@ __device__ inline u4 convert(u4 raw, uint32_t off, int codec) {
   else return to_h8_c<C>(select_bytes(raw, off, bits_of(C)));
 }
 
-template <int D, int KC, int VC>
-__device__ inline void produce(const Raw<D>& raw, const TileMeta& m, Stage<D>& st, int wave, int lane) {
+// Zero the V values of tokens past the row (their bytes may be anything): run
+// element e = 8c + i of lane L holds token 4(L/16) + i%4; word k holds
+// elements 2k and 2k+1.
+__device__ inline u4 mask_v_tail(u4 x, int valid, int lane) {
+  if (valid >= 16) return x;
+  const int nv = min(max(valid - 4 * (lane >> 4), 0), 4);
+  const uint32_t m01 = nv >= 2 ? ~0u : (nv == 1 ? 0x0000ffffu : 0u);
+  const uint32_t m23 = nv >= 4 ? ~0u : (nv == 3 ? 0x0000ffffu : 0u);
+  return u4{x[0] & m01, x[1] & m23, x[2] & m01, x[3] & m23};
+}
+
+// INT group scales of one tile into LDS: lanes 0 .. 2NC-1 of wave 0 (K) and
+// of wave 1 (V); zero past the row, 1 for the other codecs.
+template <int D>
+__device__ inline void stage_scales(const Raw<D>& raw, const TileMeta& m, float* ks, float* vs, int wave,
+                                    int lane) {
   constexpr int NC = D / 32;
-#pragma unroll
-  for (int q = 0; q < Raw<D>::JOBS; ++q) {
-    const int wj = wave + WAVES * q;
-    const bool is_v = wj >= NC;
-    const int c = is_v ? wj - NC : wj;
-    u4 x = is_v ? convert<VC>(raw.x[q], raw.off[q], m.vc) : convert<KC>(raw.x[q], raw.off[q], m.kc);
-    if (is_v && m.valid < 16) {
-      // tokens past the row: zero values (their bytes may be anything).
-      // Element e = 8c + i holds token 4(L/16) + i%4; word k holds elements 2k, 2k+1.
-      const int nv = min(max(m.valid - 4 * (lane >> 4), 0), 4);
-      const uint32_t m01 = nv >= 2 ? ~0u : (nv == 1 ? 0x0000ffffu : 0u);
-      const uint32_t m23 = nv >= 4 ? ~0u : (nv == 3 ? 0x0000ffffu : 0u);
-      x = u4{x[0] & m01, x[1] & m23, x[2] & m01, x[3] & m23};
-    }
-    (is_v ? st.v : st.k)[64 * c + lane] = x;
-  }
   if (wave < 2 && lane < 2 * NC) {
     const bool sv = wave == 1;
     const int codec = sv ? m.vc : m.kc;
@@ -296,18 +301,43 @@ __device__ inline void produce(const Raw<D>& raw, const TileMeta& m, Stage<D>& s
     for (int e = 0; e < 8; ++e) {
       const uint32_t w = raw.sc[e >> 1];
       const uint16_t hbits = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
-      // INT scale of token (8 lane + e) / NC; zero past the row, 1 for other codecs
       const int tok = (8 * lane + e) / NC;
       f[e] = !is_int(codec) ? 1.0f : (tok < m.valid ? (float)__builtin_bit_cast(_Float16, hbits) : 0.0f);
     }
-    float* dst = (sv ? st.vs : st.ks) + 8 * lane;
+    float* dst = (sv ? vs : ks) + 8 * lane;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dst[e] = f[e];
   }
 }
 
+// Convert the codes of a pair of tiles into the pair's LDS image. The thread
+// holds the same jobs of both tiles, so it writes the interleaved V operand.
+template <int D, int KC, int VC>
+__device__ inline void produce_pair(const Raw<D>& ra, const Raw<D>& rb, const TileMeta& ma, const TileMeta& mb,
+                                    PairStage<D>& st, int wave, int lane) {
+  constexpr int NC = D / 32;
+#pragma unroll
+  for (int q = 0; q < Raw<D>::JOBS; ++q) {
+    const int wj = wave + WAVES * q;
+    const bool is_v = wj >= NC;
+    const int c = is_v ? wj - NC : wj;
+    if (is_v) {
+      const u4 xa = mask_v_tail(convert<VC>(ra.x[q], ra.off[q], ma.vc), ma.valid, lane);
+      const u4 xb = mask_v_tail(convert<VC>(rb.x[q], rb.off[q], mb.vc), mb.valid, lane);
+      st.v[2 * c][lane] = u4{xa[0], xa[1], xb[0], xb[1]};
+      st.v[2 * c + 1][lane] = u4{xa[2], xa[3], xb[2], xb[3]};
+    } else {
+      st.k[0][64 * c + lane] = convert<KC>(ra.x[q], ra.off[q], ma.kc);
+      st.k[1][64 * c + lane] = convert<KC>(rb.x[q], rb.off[q], mb.kc);
+    }
+  }
+  if constexpr (KC == C_ANY || VC == C_ANY || is_int(KC) || is_int(VC)) {
+    stage_scales<D>(ra, ma, st.ks[0], st.vs[0], wave, lane);
+    stage_scales<D>(rb, mb, st.ks[1], st.vs[1], wave, lane);
+  }
+}
+
 __device__ inline f4 mfma32(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
-__device__ inline f4 mfma16(h4 a, h4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
 
 // Max and sum over lanes l, l^16, l^32, l^48 (the rows holding one column);
 // the swap results are read from the builtin's vector and pinned by an empty
@@ -340,11 +370,60 @@ __device__ inline float row4_sum(float x) {
   return a + b;
 }
 
+// Raw scores of one staged tile for the wave's NBC column blocks (lane l:
+// tokens 4(l/16) + j of column l % 16), before the K scale. INT K: one
+// accumulator per 32-dim group, weighted by the token's fp16 group scale.
+template <int D>
+__device__ inline void tile_scores(const u4* kimg, const float* ks, bool kint, const h8 (&qf)[NBC][D / 32],
+                                   int lane, f4 (&s)[NBC]) {
+  constexpr int NC = D / 32;
+  const int kq = lane >> 4;
+  const f4 zero = {0.f, 0.f, 0.f, 0.f};
+  h8 kf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) kf[c] = __builtin_bit_cast(h8, kimg[64 * c + lane]);
+  if (kint) {
+    float ksc[4][NC];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int g = 0; g < NC; ++g) ksc[j][g] = ks[(4 * kq + j) * NC + g];
+#pragma unroll
+    for (int cb = 0; cb < NBC; ++cb) {
+      f4 sg[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sg[c] = mfma32(kf[c], qf[cb][c], zero);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float x = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) x += ksc[j][c] * sg[c][j];
+        s[cb][j] = x;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int cb = 0; cb < NBC; ++cb) {
+      f4 sa = zero;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sa = mfma32(kf[c], qf[cb][c], sa);
+      s[cb] = sa;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- kernel
+// Waves per SIMD asked of the compiler: two where the pair's registers fit in
+// half the file, one for the group-scale and per-page dispatch variants.
 template <int D, int KC, int VC>
-__global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
+__host__ __device__ constexpr int prefill_waves() {
+  return (D == 128 && (is_int(KC) || is_int(VC) || KC == C_ANY || VC == C_ANY)) ? 1 : 2;
+}
+
+template <int D, int KC, int VC>
+__global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(prefill_waves<D, KC, VC>()))) prefill_kernel(const PrefillArgs a) {
   constexpr int NC = D / 32, NB = D / 16;
-  __shared__ Stage<D> stage[2];
+  __shared__ PairStage<D> stage[2];
   __shared__ PDesc desc[MAX_DESC];
 
   // block -> (partition, column group): the column groups of one partition
@@ -469,7 +548,7 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
     auto meta = [&](int i) {
       TileMeta m;
       m.j0 = c0 + 16 * i;
-      m.koff = 0; m.voff = 0; m.sk = 1.f; m.sv = 1.f; m.valid = 0;
+      m.koff = 0; m.voff = 0; m.sk = 1.f; m.sv = 1.f; m.valid = 0; m.sub = 0;
       m.kc = KC == C_ANY ? 0 : KC;
       m.vc = VC == C_ANY ? 0 : VC;
       if (i >= nt) return m;
@@ -485,100 +564,94 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
       const int cod = __builtin_amdgcn_readfirstlane(d.codec);
       if (KC == C_ANY) m.kc = cod & 15;
       if (VC == C_ANY) m.vc = cod >> 4;
+      m.sub = isub;
       if (++isub == tpp) { isub = 0; ++ipg; }
       return m;
     };
 
-    Raw<D> raw[RING];
-    TileMeta mt[RING];
+    // Tiles go in pairs, 32 keys per step: one barrier, one online-softmax
+    // update and 16x16x32 P.V MFMAs per pair. The ring holds the codes of
+    // PAIR_RING pairs: while one pair is consumed the next ones are in flight.
+    Raw<D> raw[2 * PAIR_RING];
+    TileMeta mt[2 * PAIR_RING];
 #pragma unroll
-    for (int s = 0; s < RING; ++s) {
+    for (int s = 0; s < 2 * PAIR_RING; ++s) {
       mt[s] = meta(s);
       issue<D>(raw[s], mt[s], a, h, wave, lane);
     }
-    for (int it = 0; it < nt; it += RING) {
+    for (int it = 0; it < nt; it += 2 * PAIR_RING) {
 #pragma unroll
-      for (int s = 0; s < RING; ++s) {
-        const int i = it + s;
+      for (int s = 0; s < PAIR_RING; ++s) {
+        const int i = it + 2 * s;
         if (i >= nt) break;
-        Stage<D>& st = stage[s & 1];  // RING is even: tile i uses buffer i % 2
-        const TileMeta m = mt[s];
+        PairStage<D>& st = stage[(i >> 1) & 1];
+        const TileMeta mA = mt[2 * s], mB = mt[2 * s + 1];
         // unconditional: a dead tile converts zeros that are never read, and the
         // ring registers are always consumed before they are loaded again
-        produce<D, KC, VC>(raw[s], m, st, wave, lane);
-        mt[s] = meta(i + RING);
-        issue<D>(raw[s], mt[s], a, h, wave, lane);
+        produce_pair<D, KC, VC>(raw[2 * s], raw[2 * s + 1], mA, mB, st, wave, lane);
+        mt[2 * s] = meta(i + 2 * PAIR_RING);
+        issue<D>(raw[2 * s], mt[2 * s], a, h, wave, lane);
+        mt[2 * s + 1] = meta(i + 2 * PAIR_RING + 1);
+        issue<D>(raw[2 * s + 1], mt[2 * s + 1], a, h, wave, lane);
         lds_barrier();
-        if (m.valid <= 0 || !wave_live || m.j0 >= w_hi_max || m.j0 + 16 <= w_lo_min) continue;
+        // a tile attends nothing for this wave when it is dead or outside every
+        // column's key range; the pair is skipped when both do
+        const bool offA = mA.valid <= 0 || mA.j0 >= w_hi_max || mA.j0 + 16 <= w_lo_min;
+        const bool offB = mB.valid <= 0 || mB.j0 >= w_hi_max || mB.j0 + 16 <= w_lo_min;
+        if (!wave_live || (offA && offB)) continue;
 
-        // ---- operands of this tile
-        h8 kf[NC];
-#pragma unroll
-        for (int c = 0; c < NC; ++c) kf[c] = __builtin_bit_cast(h8, st.k[64 * c + lane]);
-        h4 vf[NB];
-#pragma unroll
-        for (int c = 0; c < NB / 2; ++c) {
-          const u4 x = st.v[64 * c + lane];
-          vf[2 * c] = __builtin_bit_cast(h4, u2{x[0], x[1]});
-          vf[2 * c + 1] = __builtin_bit_cast(h4, u2{x[2], x[3]});
-        }
-        const int kcod = KC == C_ANY ? m.kc : KC, vcod = VC == C_ANY ? m.vc : VC;
-        const bool kint = is_int(kcod), vint = is_int(vcod);
-        float ksc[4][NC], vsc[4][NC];
-        if (kint) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int g = 0; g < NC; ++g) ksc[j][g] = st.ks[(4 * kq + j) * NC + g];
-        }
-        if (vint) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int g = 0; g < NC; ++g) vsc[j][g] = st.vs[(4 * kq + j) * NC + g];
-        }
-        const bool masked = m.j0 < w_lo_max || m.j0 + 16 > w_hi_min;
+        // ---- scores of both tiles (before the K scale)
+        const int kcA = KC == C_ANY ? mA.kc : KC, kcB = KC == C_ANY ? mB.kc : KC;
+        const int vcA = VC == C_ANY ? mA.vc : VC, vcB = VC == C_ANY ? mB.vc : VC;
+        f4 sA[NBC], sB[NBC];
+        tile_scores<D>(st.k[0], st.ks[0], is_int(kcA), qf, lane, sA);
+        tile_scores<D>(st.k[1], st.ks[1], is_int(kcB), qf, lane, sB);
         // scores in log2 units are raw * f: f > 0 goes into the max and the exp
-        const float f = kint ? a.scale_log2 : a.scale_log2 * m.sk;
-        if (m.sv != sv_cur) {  // another V scale (1 for pages without FP8 V)
-          const float r = sv_cur / m.sv;
+        const float fA = is_int(kcA) ? a.scale_log2 : a.scale_log2 * mA.sk;
+        const float fB = is_int(kcB) ? a.scale_log2 : a.scale_log2 * mB.sk;
+        const bool masked = offA || offB || mA.j0 < w_lo_max || mB.j0 + 16 > w_hi_min;
+
+        // ---- FP8 V scales: acc is kept in units of sv_cur. A tile that attends
+        // nothing takes its partner's scale; two different scales (a pair
+        // across pages) split the P.V in two, with a rescale between the halves
+        const float svB = offB ? mA.sv : mB.sv;
+        const float svA = offA ? svB : mA.sv;
+        const bool split = svA != svB;
+        if (svA != sv_cur) {
+          const float r = sv_cur / svA;
 #pragma unroll
           for (int cb = 0; cb < NBC; ++cb)
 #pragma unroll
             for (int n = 0; n < NB; ++n) acc[cb][n] *= r;
-          sv_cur = m.sv;
+          sv_cur = svA;
         }
+        const float r_split = svA / svB;
 
+        const bool vint = is_int(vcA) || is_int(vcB);
+
+        // ---- online softmax of both column blocks; pa holds the P operand
+        // (INT V: the weights times the token's fp16 group scale, one operand
+        // per group; the staged scales are 1 for other codecs)
+        h8 pa[NBC][NC];
 #pragma unroll
         for (int cb = 0; cb < NBC; ++cb) {
-          float s[4];
-          if (kint) {
-            // one accumulator per 32-dim group, weighted by its fp16 scale
-            f4 sg[NC];
+          float s8[8];
 #pragma unroll
-            for (int c = 0; c < NC; ++c) sg[c] = mfma32(kf[c], qf[cb][c], zero);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              float x = 0.f;
-#pragma unroll
-              for (int c = 0; c < NC; ++c) x += ksc[j][c] * sg[c][j];
-              s[j] = x;
-            }
-          } else {
-            f4 sa = zero;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) sa = mfma32(kf[c], qf[cb][c], sa);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) s[j] = sa[j];
+          for (int j = 0; j < 4; ++j) {
+            s8[j] = sA[cb][j];
+            s8[4 + j] = sB[cb][j];
           }
           if (masked) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const int pos = m.j0 + 4 * kq + j;
-              s[j] = (pos >= lo_col[cb] && pos < hi_col[cb]) ? s[j] : NEG_INF;
+              const int pa_ = mA.j0 + 4 * kq + j, pb_ = mB.j0 + 4 * kq + j;
+              s8[j] = (mA.valid > 0 && pa_ >= lo_col[cb] && pa_ < hi_col[cb]) ? s8[j] : NEG_INF;
+              s8[4 + j] = (mB.valid > 0 && pb_ >= lo_col[cb] && pb_ < hi_col[cb]) ? s8[4 + j] : NEG_INF;
             }
           }
-          const float mx = row4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * f;
+          const float mxa = fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])) * fA;
+          const float mxb = fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])) * fB;
+          const float mx = row4_max(fmaxf(mxa, mxb));
           const float m_new = fmaxf(m_run[cb], mx);
           if (__any(m_new > m_run[cb])) {
             const float alpha = m_new > m_run[cb] ? __builtin_amdgcn_exp2f(m_run[cb] - m_new) : 1.0f;
@@ -592,26 +665,62 @@ __global__ void __launch_bounds__(THREADS) prefill_kernel(const PrefillArgs a) {
             m_run[cb] = m_new;
           }
           const float mu = m_run[cb] == NEG_INF ? 0.f : m_run[cb];
-          float p[4];
+          float p[8];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], f, -mu));
-          l_run[cb] += (p[0] + p[1]) + (p[2] + p[3]);
-
+          for (int j = 0; j < 4; ++j) {
+            p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s8[j], fA, -mu));
+            p[4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s8[4 + j], fB, -mu));
+          }
+          l_run[cb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
           if (vint) {
-            // INT V: the weights times the token's fp16 group scale, per group
-            h4 pa[NC];
 #pragma unroll
             for (int g = 0; g < NC; ++g)
 #pragma unroll
-              for (int j = 0; j < 4; ++j) pa[g][j] = (_Float16)(p[j] * vsc[j][g]);
-#pragma unroll
-            for (int n = 0; n < NB; ++n) acc[cb][n] = mfma16(pa[n / 2], vf[n], acc[cb][n]);
+              for (int j = 0; j < 4; ++j) {
+                pa[cb][g][j] = (_Float16)(p[j] * st.vs[0][(4 * kq + j) * NC + g]);
+                pa[cb][g][4 + j] = (_Float16)(p[4 + j] * st.vs[1][(4 * kq + j) * NC + g]);
+              }
           } else {
-            const h4 pa = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
 #pragma unroll
-            for (int n = 0; n < NB; ++n) acc[cb][n] = mfma16(pa, vf[n], acc[cb][n]);
+            for (int j = 0; j < 8; ++j) pa[cb][0][j] = (_Float16)p[j];
           }
         }
+
+        // ---- P.V, dims 16n .. 16n+15 at a time
+        auto vfrag = [&](int n) { return __builtin_bit_cast(h8, st.v[n][lane]); };
+        if (!split) {
+#pragma unroll
+          for (int n = 0; n < NB; ++n) {
+            const h8 vf = vfrag(n);
+#pragma unroll
+            for (int cb = 0; cb < NBC; ++cb) acc[cb][n] = mfma32(pa[cb][vint ? n / 2 : 0], vf, acc[cb][n]);
+          }
+        } else {
+          const _Float16 z = 0;
+#pragma unroll
+          for (int n = 0; n < NB; ++n) {
+            const h8 vf = vfrag(n);
+#pragma unroll
+            for (int cb = 0; cb < NBC; ++cb) {
+              const h8 w = pa[cb][vint ? n / 2 : 0];
+              acc[cb][n] = mfma32(h8{w[0], w[1], w[2], w[3], z, z, z, z}, vf, acc[cb][n]);
+            }
+          }
+#pragma unroll
+          for (int cb = 0; cb < NBC; ++cb)
+#pragma unroll
+            for (int n = 0; n < NB; ++n) acc[cb][n] *= r_split;
+#pragma unroll
+          for (int n = 0; n < NB; ++n) {
+            const h8 vf = vfrag(n);
+#pragma unroll
+            for (int cb = 0; cb < NBC; ++cb) {
+              const h8 w = pa[cb][vint ? n / 2 : 0];
+              acc[cb][n] = mfma32(h8{z, z, z, z, w[4], w[5], w[6], w[7]}, vf, acc[cb][n]);
+            }
+          }
+        }
+        if (split) sv_cur = svB;
       }
     }
   }
