@@ -53,11 +53,13 @@ __device__ inline int clamp_len(int L, const SelectArgs& a) {
   return L < 0 ? 0 : (int)((int64_t)L > cap ? cap : L);
 }
 
-// Summaries are staged through LDS 32 dims at a time with coalesced 16-byte
-// loads (a workgroup's 256 rows are contiguous in the slab), then each thread
+// Summaries are staged through LDS 64 dims at a time with coalesced 16-byte
+// loads (a workgroup's 256 rows are contiguous in the slab; every thread
+// issues its eight loads of a round before storing any), then each thread
 // accumulates its own row in index order from LDS.
-constexpr int CH = 32;                 // dims per staging round
-constexpr int ROW_WORDS = CH / 2 + 4;  // one staged row: 64 bytes + 16 bytes of padding
+constexpr int CH = 64;                 // dims per staging round
+constexpr int ROW_WORDS = CH / 2 + 4;  // one staged row: 128 bytes + 16 bytes of padding
+constexpr int LOADS = CH / 8;          // 16-byte loads per thread per full round
 
 __global__ void __launch_bounds__(SCORE_THREADS) score_kernel(const SelectArgs a) {
   extern __shared__ float qs[];  // the row's indexer query in fp32
@@ -78,10 +80,19 @@ __global__ void __launch_bounds__(SCORE_THREADS) score_kernel(const SelectArgs a
     const int w = min(CH, a.idx_dim - d0);  // dims this round (a multiple of 8)
     const int chunks = w / 8;               // 16-byte chunks per row
     __syncthreads();
-    for (int e = tid; e < nrows * chunks; e += SCORE_THREADS) {
+    const int total = nrows * chunks;  // <= LOADS * SCORE_THREADS
+    u4 x[LOADS];
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) {
+      const int e = tid + k * SCORE_THREADS;
       const int r = e / chunks, c = e % chunks;
-      const u4 x = *reinterpret_cast<const u4*>(base + r * row_bytes + (size_t)(d0 + 8 * c) * 2);
-      *reinterpret_cast<u4*>(&stage[r * ROW_WORDS + 4 * c]) = x;
+      if (e < total) x[k] = *reinterpret_cast<const u4*>(base + r * row_bytes + (size_t)(d0 + 8 * c) * 2);
+    }
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) {
+      const int e = tid + k * SCORE_THREADS;
+      const int r = e / chunks, c = e % chunks;
+      if (e < total) *reinterpret_cast<u4*>(&stage[r * ROW_WORDS + 4 * c]) = x[k];
     }
     __syncthreads();
     if (tid < nrows) {
