@@ -108,8 +108,14 @@ typedef struct pkv_params {
   int32_t num_pages;         /* physical pages described by the page tables            */
   int32_t max_pages_per_row; /* row stride of block_table (entries), >= 1               */
   int32_t max_sel_pages;     /* 0: dense mode; > 0: sparse mode, row stride of page_sel */
-  int32_t partition_tokens;  /* split-K partition length in attended tokens: 0 = chosen
-                                by the library, else a positive multiple of page_size   */
+  int32_t partition_tokens;  /* split-K partition length in tokens, a positive multiple
+                                of 16 (decode; prefill: of page_size). A row's 16-token
+                                tiles run through its pages (dense) or its selected
+                                pages in list order (sparse); partition i covers tiles
+                                [i*T/16, (i+1)*T/16), so partitions may split a page.
+                                0: the library splits each row's tiles evenly into
+                                pkv_num_partitions(p) partitions (decode), or picks a
+                                whole-page length (prefill)                              */
   int32_t k_codec;           /* codec of every K plane in this call, or PKV_CODEC_MIXED */
   int32_t v_codec;           /* codec of every V plane in this call, or PKV_CODEC_MIXED */
   float softmax_scale;       /* tau, finite (1/sqrt(head_dim) in the usual case)        */
@@ -124,7 +130,13 @@ int pkv_abi_version(void);
 const char* pkv_status_string(int status);
 
 /* Partitions each row is split into for these params (>= 1), or a negative
- * status if the params are invalid. Sizes the workspace and the partials. */
+ * status if the params are invalid. Sizes the workspace and the partials.
+ * With partition_tokens = 0: as many as fill one round of resident
+ * workgroups (256 compute units x the kernel's waves per SIMD, four waves per
+ * workgroup, rows x KV heads workgroups per partition index), at most one per
+ * 4 tiles of the longest row and at least 1; row b's partition i then covers
+ * tiles [i c, (i + 1) c), c = max(1, ceil(ceil(L_b / 16) / n)) (dense) or
+ * ceil(sel_lens[b] P / 16 / n) (sparse). */
 int pkv_num_partitions(const pkv_params* p);
 
 /* Bytes of device workspace pkv_decode_attention needs for these params:
@@ -153,7 +165,8 @@ size_t pkv_workspace_bytes(const pkv_params* p);
  *   workspace    device scratch of pkv_workspace_bytes(p) bytes, 16-byte aligned,
  *                NULL allowed when that is 0. Contents need no initialization.
  *   err_count    device int32 counter incremented per device-visible problem,
- *                or NULL.
+ *                or NULL. A bad page is counted once by every partition whose
+ *                tiles reach it (partitions finer than a page share pages).
  *   stream       hipStream_t to enqueue on (NULL: default stream).
  */
 int pkv_decode_attention(const pkv_params* p, const void* q, const uint8_t* page_pool,

@@ -10,8 +10,10 @@
 
 namespace {
 
-constexpr int kWorkgroupsWanted = 1024;  // about four workgroups per compute unit
+constexpr int kWorkgroupsWanted = 1024;  // prefill: about four workgroups per compute unit
 constexpr int kMinPartitionTokens = 256;
+constexpr int kComputeUnits = 256;       // gfx950 (MI350X / MI355X): 8 XCDs x 32 compute units
+constexpr int kMinTilesPerPartition = 4; // decode: one 16-token tile per wave of a workgroup
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -24,7 +26,7 @@ int check_params(const pkv_params* p) {
   if (p->num_q_heads % p->num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
   if (p->page_size <= 0 || p->page_size % 16 != 0) return PKV_ERR_INVALID_ARG;
   if (p->num_pages < 0 || p->max_pages_per_row < 1 || p->max_sel_pages < 0) return PKV_ERR_INVALID_ARG;
-  if (p->partition_tokens < 0 || p->partition_tokens % p->page_size != 0) return PKV_ERR_INVALID_ARG;
+  if (p->partition_tokens < 0 || p->partition_tokens % 16 != 0) return PKV_ERR_INVALID_ARG;
   if (!isfinite(p->softmax_scale)) return PKV_ERR_INVALID_ARG;
   if (!valid_codec(p->k_codec) || !valid_codec(p->v_codec)) return PKV_ERR_INVALID_ARG;
   if (p->head_dim != 64 && p->head_dim != 128) return PKV_ERR_UNSUPPORTED;
@@ -37,23 +39,26 @@ int64_t row_capacity(const pkv_params* p) {
   return p->max_sel_pages > 0 ? p->max_sel_pages : p->max_pages_per_row;
 }
 
-// Pages per partition after resolving partition_tokens == 0.
-int64_t pages_per_partition(const pkv_params* p) {
-  const int64_t cap = row_capacity(p);
-  if (p->partition_tokens > 0) return p->partition_tokens / p->page_size;
-  const int64_t units = (int64_t)(p->num_rows > 0 ? p->num_rows : 1) * p->num_kv_heads;
-  int64_t parts = (kWorkgroupsWanted + units - 1) / units;
-  if (parts < 1) parts = 1;
-  int64_t ppp = (cap + parts - 1) / parts;
-  const int64_t min_pages = (kMinPartitionTokens + p->page_size - 1) / p->page_size;
-  if (ppp < min_pages) ppp = min_pages;
-  if (ppp > cap) ppp = cap;
-  return ppp < 1 ? 1 : ppp;
-}
+// 16-token tiles a row can reach at most.
+int64_t row_tiles(const pkv_params* p) { return row_capacity(p) * (p->page_size / 16); }
 
+// Partitions per row. A positive partition_tokens fixes their length; 0 lets
+// the library split each row's tiles evenly into as many partitions as fill
+// one round of resident decode workgroups (compute units x waves per SIMD;
+// four waves per workgroup), with at least one tile per wave in a partition.
 int64_t partitions(const pkv_params* p) {
-  const int64_t ppp = pages_per_partition(p);
-  return (row_capacity(p) + ppp - 1) / ppp;
+  const int64_t tiles = row_tiles(p);
+  if (p->partition_tokens > 0) {
+    const int64_t tpart = p->partition_tokens / 16;
+    return (tiles + tpart - 1) / tpart;
+  }
+  const int64_t units = (int64_t)(p->num_rows > 0 ? p->num_rows : 1) * p->num_kv_heads;
+  const int64_t resident =
+      (int64_t)kComputeUnits * pkv::decode_waves_per_simd(p->head_dim, p->k_codec, p->v_codec);
+  int64_t parts = resident / units;
+  const int64_t most = (tiles + kMinTilesPerPartition - 1) / kMinTilesPerPartition;
+  if (parts > most) parts = most;
+  return parts < 1 ? 1 : parts;
 }
 
 }  // namespace
@@ -109,6 +114,7 @@ int prepare(const pkv_params* p, const void* q, const uint8_t* page_pool,
   const int64_t nparts = partitions(p);
   if (nparts > 65535 || (int64_t)p->num_rows > 65535 || p->num_kv_heads > 65535)
     return PKV_ERR_UNSUPPORTED;  // grid dimension limits
+  if (row_capacity(p) * p->page_size > 0x7fffffff) return PKV_ERR_UNSUPPORTED;  // token positions are int32
 
   a->q = static_cast<const uint16_t*>(q);
   a->pool = page_pool;
@@ -133,7 +139,7 @@ int prepare(const pkv_params* p, const void* q, const uint8_t* page_pool,
   a->num_pages = p->num_pages;
   a->max_pages = p->max_pages_per_row;
   a->max_sel = p->max_sel_pages;
-  a->pages_per_part = (int32_t)pages_per_partition(p);
+  a->tiles_per_part = p->partition_tokens / 16;  // 0: even split of each row
   a->nparts = (int32_t)nparts;
   a->sparse = sparse ? 1 : 0;
   a->final_out = 0;
@@ -320,6 +326,7 @@ int plan_prefill(const pkv_params* p, int32_t q_tokens, int32_t kv_begin, int32_
   int st = check_params(p);
   if (st != PKV_OK) return st;
   if (p->max_sel_pages != 0) return PKV_ERR_INVALID_ARG;  // the prefill attends the dense cache
+  if (p->partition_tokens % p->page_size != 0) return PKV_ERR_INVALID_ARG;  // prefill partitions are whole pages
   if (q_tokens < 0 || kv_begin < 0 || (kv_end >= 0 && kv_end < kv_begin)) return PKV_ERR_INVALID_ARG;
   const int64_t cap = (int64_t)p->max_pages_per_row * p->page_size;
   pl->base = (int64_t)kv_begin / p->page_size * p->page_size;

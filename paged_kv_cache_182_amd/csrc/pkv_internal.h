@@ -7,6 +7,14 @@
 
 namespace pkv {
 
+// Waves per SIMD the decode kernel for (head_dim, K codec, V codec) is built
+// for (codec -1: per-page dispatch): four where the tile ring fits 128 VGPRs,
+// three for the codecs with group scales. Sizes the library-chosen partition
+// count (workgroups resident at once = compute units x this).
+constexpr int decode_waves_per_simd(int head_dim, int k_codec, int v_codec) {
+  return (head_dim == 64 || (k_codec == 2 && v_codec == 2)) ? 4 : 3;
+}
+
 // Everything one decode launch needs, resolved on the host.
 struct DecodeArgs {
   const uint16_t* q;        // fp16 [B][Hq][D]
@@ -25,7 +33,7 @@ struct DecodeArgs {
   float* part_ml;           // [B*Hq][nparts][2]   (nparts > 1)
   int32_t* err;             // device counter or nullptr
   int32_t rows, hq, hkv, group, page, num_pages, max_pages, max_sel;
-  int32_t pages_per_part;   // pages (dense) or selection entries (sparse) per partition
+  int32_t tiles_per_part;   // 16-token tiles per partition; 0: each row's tiles split evenly into nparts
   int32_t nparts;
   int32_t sparse;
   int32_t final_out;        // 1: write out/lse (single partition); 0: write partials

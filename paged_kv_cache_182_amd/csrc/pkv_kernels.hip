@@ -134,7 +134,7 @@ __host__ __device__ constexpr int waves_per_eu() {
 #ifdef PKV_WAVES
   return PKV_WAVES;
 #else
-  return (D == 64 || (KC == C_FP8 && VC == C_FP8)) ? 4 : 3;
+  return decode_waves_per_simd(D, KC == C_ANY ? -1 : KC, VC == C_ANY ? -1 : VC);
 #endif
 }
 
@@ -609,16 +609,30 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
     npg = min(n, a.max_pages);
   }
   npg = __builtin_amdgcn_readfirstlane(npg);
-  const int s0 = part * a.pages_per_part;
-  const int s1 = min(s0 + a.pages_per_part, npg);
+
+  // ---- this partition's 16-token tiles [t0, t1) of the row. A row's tiles
+  // run through its pages (dense) or its selected pages in list order
+  // (sparse), tpp per page; only tiles that can hold attended tokens count.
+  // Partitions are either a fixed number of tiles (tiles_per_part) or, with
+  // tiles_per_part = 0, the row's tiles split evenly into nparts, so rows of
+  // different lengths give workgroups of equal work.
+  const int tpp = P / 16;
+  const int ntl = a.sparse ? npg * tpp : min(L / 16 + (L % 16 != 0), npg * tpp);
+  const int tpart = a.tiles_per_part > 0 ? a.tiles_per_part : max(1, (ntl + a.nparts - 1) / a.nparts);
+  const int t0 = part * tpart;
+  const int t1 = min(t0 + tpart, ntl);
+  // table entries the partition touches inside the row: [s0, s1)
+  const int s0 = t0 / tpp;
+  const int s1 = t1 > t0 ? (t1 + tpp - 1) / tpp : s0;
 
   // ---- page descriptors of this partition, MAX_DESC at a time. Entries run
-  // as far as the tables go; the row length (s1) may cut them shorter. The
-  // first chunk is gathered before the row length is known and before q is
-  // read: its table reads go out at once, and every read of a chunk is issued
-  // before any result is checked, so the gather costs two dependent rounds
-  // (three with a selection).
-  const int s_lim = min(s0 + a.pages_per_part, a.sparse ? a.max_sel : a.max_pages);
+  // as far as the tables go; the row length (s1) may cut them shorter. With
+  // fixed-size partitions the first chunk is gathered before the row length
+  // is known and before q is read: its table reads go out at once, and every
+  // read of a chunk is issued before any result is checked, so the gather
+  // costs two dependent rounds (three with a selection); an even split waits
+  // for the row length first.
+  const int s_lim = min((t0 + tpart + tpp - 1) / tpp, a.sparse ? a.max_sel : a.max_pages);
   auto stage = [&](int cbase, int chunk) {
     if (tid < chunk) {
       const int s = cbase + tid;
@@ -688,30 +702,34 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
 #pragma unroll
   for (int n = 0; n < NB; ++n) acc[n] = f4{0.f, 0.f, 0.f, 0.f};
 
-  const int tpp = P / 16;
   while (chunk > 0) {
     lds_barrier();
-    const int cn = max(0, min(chunk, s1 - cbase));
+    // the partition's tiles among this chunk's: [klo, khi), counted from the
+    // chunk's first tile
+    const int kb = cbase * tpp;
+    const int klo = max(t0 - kb, 0);
+    const int khi = min(t1 - kb, chunk * tpp);
 
     // Ring of DEPTH tiles: while the oldest is consumed, the loads of the
     // next DEPTH-1 are in flight. Issues are unconditional (past the end the
     // wave issues its last tile again through a zero-size resource and never
     // consumes it), so the compiler's wait counts stay exact.
-    const int ntiles = cn * tpp;
+    const int ntiles = khi - klo;
     if (wave < ntiles) {
       constexpr int DEPTH = ring_depth<D, KC, VC>();
       const int nmine = (ntiles - wave + WAVES - 1) / WAVES;
-      const int klast = wave + (nmine - 1) * WAVES;
+      const int kfirst = klo + wave;
+      const int klast = kfirst + (nmine - 1) * WAVES;
       Tile<D, KC, VC> t[DEPTH];
       TileInfo inf[DEPTH];
 #pragma unroll
       for (int s = 0; s < DEPTH - 1; ++s)
-        inf[s] = issue_tile<D, KC, VC>(t[s], desc, min(wave + s * WAVES, klast), tpp, a, h, lane,
-                                       wave + s * WAVES > klast);
+        inf[s] = issue_tile<D, KC, VC>(t[s], desc, min(kfirst + s * WAVES, klast), tpp, a, h, lane,
+                                       kfirst + s * WAVES > klast);
       for (int it = 0; it < nmine; it += DEPTH) {
 #pragma unroll
         for (int s = 0; s < DEPTH; ++s) {
-          const int kn = wave + (it + s + DEPTH - 1) * WAVES;
+          const int kn = kfirst + (it + s + DEPTH - 1) * WAVES;
           const int nx = (s + DEPTH - 1) % DEPTH;
           // past the end: same loads through a zero-size resource (no traffic)
           inf[nx] = issue_tile<D, KC, VC>(t[nx], desc, min(kn, klast), tpp, a, h, lane, kn > klast);

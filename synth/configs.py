@@ -45,14 +45,14 @@ def config(cid: int, small: bool = False) -> Workload:
             page=page, seq_lens=[pages * page] * layers,
             codec_of=lambda r, lp: (FP16, FP16) if lp >= fp16_from else (FP8, FP8),
             seed=seed, rng=rng, outlier_frac=0.01, outlier_mult=8.0,
-            partition_tokens=page, info={"config": 2, "layers": layers, "batch": 1})
+            partition_tokens=0 if not small else page, info={"config": 2, "layers": layers, "batch": 1})
     if cid == 3:
         rows, lo, hi, width = (8, 24576, 32768, 2048) if not small else (3, 300, 700, 48)
         lens = rng["lengths"].integers(lo, hi, endpoint=True, size=rows)
         return build_workload(
             NAMES[3] + ("_small" if small else ""), rows=rows, hq=32, hkv=8, dim=128,
             page=16, seq_lens=lens, codec_of=lambda r, lp: (INT8, INT4), seed=seed,
-            rng=rng, max_pages=width, partition_tokens=2048 if not small else 128,
+            rng=rng, max_pages=width, partition_tokens=0 if not small else 128,
             info={"config": 3, "layers": 1, "batch": rows})
     if cid == 4:
         layers, batch, ctx, nsel = (12, 4, 262144, 128) if not small else (2, 2, 4096, 16)

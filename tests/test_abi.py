@@ -54,15 +54,29 @@ def test_partitions_and_workspace():
     assert pkv.num_partitions(one) == 1 and pkv.workspace_bytes(one) == 0
     sparse = base(rows=48, page_size=16, max_pages_per_row=16384, max_sel_pages=128, partition_tokens=256)
     assert pkv.num_partitions(sparse) == 8
+    # partitions of any multiple of 16 tokens, also finer than a page
+    sub = base(num_pages=16, max_pages_per_row=16, page_size=1024, partition_tokens=48)
+    assert pkv.num_partitions(sub) == 342                     # ceil(1024 tiles / 3)
+    # 0: each row split evenly into as many partitions as fill one round of
+    # resident workgroups (256 compute units x waves per SIMD of the kernel),
+    # at least 4 tiles per partition
     auto = base(rows=8, num_q_heads=32, num_kv_heads=8, page_size=16, max_pages_per_row=2048,
-                partition_tokens=0)
-    n = pkv.num_partitions(auto)
-    assert 1 <= n <= 2048 and 8 * 8 * n >= 1024
+                partition_tokens=0, k_codec=pkv.INT8_G32, v_codec=pkv.INT4_G32)
+    assert pkv.num_partitions(auto) == 768 // 64               # three waves per SIMD
+    auto8 = base(rows=8, num_q_heads=32, num_kv_heads=8, page_size=16, max_pages_per_row=2048,
+                 partition_tokens=0)
+    assert pkv.num_partitions(auto8) == 1024 // 64             # FP8: four waves per SIMD
+    layer = base(num_q_heads=14, head_dim=64, page_size=1024, num_pages=16, max_pages_per_row=16,
+                 partition_tokens=0, k_codec=pkv.CODEC_MIXED, v_codec=pkv.CODEC_MIXED)
+    assert pkv.num_partitions(layer) == 256                    # 1024 tiles, 4 per partition
+    many = base(rows=2000, partition_tokens=0)
+    assert pkv.num_partitions(many) == 1
 
 
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 96, -2), ("head_dim", 256, -2), ("page_size", 8, -1), ("page_size", 24, -1),
     ("num_q_heads", 15, -1), ("num_q_heads", 34, -2), ("partition_tokens", 100, -1),
+    ("partition_tokens", 8, -1), ("partition_tokens", -16, -1),
     ("num_rows", -1, -1), ("max_pages_per_row", 0, -1), ("k_codec", 9, -1),
 ])
 def test_bad_params_rejected(field, value, status):
@@ -163,6 +177,9 @@ def test_prefill_partitions_and_workspace():
 def test_prefill_host_checks():
     p = base()
     lib = pkv.load()
+    # prefill partitions are whole pages (decode accepts any multiple of 16)
+    assert lib.pkv_prefill_num_partitions(ctypes.byref(base(partition_tokens=48)), 4, 0, -1) == -1
+    assert pkv.num_partitions(base(partition_tokens=48)) > 0
     assert lib.pkv_prefill_num_partitions(ctypes.byref(p), -1, 0, -1) == -1
     assert lib.pkv_prefill_num_partitions(ctypes.byref(p), 4, -3, -1) == -1
     assert lib.pkv_prefill_num_partitions(ctypes.byref(p), 4, 100, 50) == -1

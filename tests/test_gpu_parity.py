@@ -97,6 +97,60 @@ def test_empty_rows_and_partitions():
     check(ws)
 
 
+# ------------------------------------------------ partitions finer than a page, even splits
+@pytest.mark.parametrize("kc,vc,page", [(FP8, FP8, 64), (INT8, INT4, 64), (FP16, FP16, 1024), (None, None, 1024)])
+def test_sub_page_partitions(kc, vc, page):
+    """Partitions of any multiple of 16 tokens, also inside one page, and the
+    library's even split (partition_tokens = 0) match the oracle."""
+    print(f"case sub-page partitions ({kc},{vc}) page={page}", flush=True)
+    cyc = [(FP16, FP16), (FP8, FP8)]
+    codec_of = (lambda r, lp: cyc[(r + lp) % 2]) if kc is None else (lambda r, lp: (kc, vc))
+    w = poison_tails(small([1, 40, 1500, 2100, 3000], kc, vc, hq=16, hkv=2, dim=128 if page == 64 else 64,
+                           page=page, codec_of=codec_of))
+    for T in (16, 48, 80, 0):
+        check(w, partition_tokens=T, what=f"{w.name} page={page} T={T}")
+
+
+def test_sparse_sub_page_partitions():
+    """Sparse mode: a partition's tiles run through the selected pages in list
+    order, so partitions finer than a page split selected pages."""
+    print("case sparse sub-page partitions", flush=True)
+    rng = np.random.default_rng(5)
+    lens = [1000, 777, 64]
+    sel = []
+    for L in lens:
+        last = -(-L // 64) - 1
+        rest = rng.choice([x for x in range(16) if x != last], 5, replace=False)
+        sel.append(rng.permutation(np.concatenate([[last], rest])))
+    sel = np.array(sel, dtype=np.int32)
+    w = synth.build_workload("gpu_sparse64", rows=3, hq=8, hkv=2, dim=128, page=64, seq_lens=lens,
+                             codec_of=lambda r, lp: (FP8, FP8), seed=11, selection=sel)
+    w.sel_lens = np.array([6, 4, 6], dtype=np.int32)
+    for T in (16, 32, 96, 0):
+        check(w, partition_tokens=T, what=f"sparse page=64 T={T}")
+
+
+def test_bad_page_counted_per_partition():
+    """A bad page is counted once by every partition whose tiles reach it."""
+    print("case bad page per partition", flush=True)
+    w = small([128, 128], FP8, FP8, hq=8, hkv=2, dim=128, page=64)
+    dw = to_device(w)
+    bt = w.block_table.copy()
+    bt[0, 1] = w.num_pages + 5
+    dw.block_table = torch.from_numpy(bt).cuda()
+    results = []
+    for T, expect in ((64, 1), (32, 2), (16, 4)):
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        out, lse = run(dw, params_for(w, T, k_codec=FP8, v_codec=FP8), err=err)
+        assert int(err.item()) == expect, (T, int(err.item()))
+        results.append((T, out, lse))
+    # expected: row 0 without its bad page (sparse oracle over the good pages)
+    w.page_sel, w.sel_lens = np.array([[0, 0], [0, 1]], dtype=np.int32), np.array([1, 2], dtype=np.int32)
+    ref = oracle.decode_attention(w)
+    for T, out, lse in results:
+        compare(out, lse, *ref, f"bad page skipped T={T}")
+
+
 def test_sparse_selection_order_and_unselected_poison():
     print("case sparse order", flush=True)
     w = synth.config(4, small=True)
@@ -199,19 +253,38 @@ def test_fp16_codes_exact():
 def test_decode_partials_match_oracle_partials():
     print("case partials", flush=True)
     w = small([300, 17, 0, 129], FP8, INT8, hq=8, hkv=2, dim=128, page=16)
-    dw = to_device(w)
     T = 64
+    check_partials(w, T, lambda L, n: [min(L, i * T) for i in range(n + 1)])
+
+
+def test_even_split_partials_bounds():
+    """partition_tokens = 0: partition i of a row of n_t = ceil(L / 16) tiles
+    covers tiles [i c, (i + 1) c), c = max(1, ceil(n_t / n))."""
+    print("case even-split partials", flush=True)
+    w = small([300, 17, 0, 2000], FP8, FP8, hq=8, hkv=2, dim=128, page=64)
+
+    def bounds(L, n):
+        c = max(1, -(-(-(-L // 16)) // n))
+        return [min(L, 16 * c * i) for i in range(n + 1)]
+    n = check_partials(w, 0, bounds)
+    assert n == 32          # 128 tiles at most per row, 4 per partition
+
+
+def check_partials(w, T, bounds_of):
+    """pkv_decode_partials against the oracle's partials over the token ranges
+    bounds_of(L, n) of each row."""
+    dw = to_device(w)
     p = params_for(w, T)
     n = pkv.num_partitions(p)
     acc, ml = pkv.decode_partials(p, *dw.args())
     torch.cuda.synchronize()
     acc, ml = acc.cpu().numpy().astype(np.float64), ml.cpu().numpy().astype(np.float64)
-    G = 4
+    G = w.num_q_heads // w.num_kv_heads
     from oracle.attention import gather_kv
     for r in range(w.rows):
         L = int(w.seq_lens[r])
-        bounds = [min(L, i * T) for i in range(n + 1)]
-        for h in range(2):
+        bounds = bounds_of(L, n)
+        for h in range(w.num_kv_heads):
             K, V = gather_kv(w, r, h)
             q = w.q[r, h * G:(h + 1) * G].astype(np.float64)
             oa, om, ol = oracle.partials(K, V, q, w.softmax_scale, bounds)
@@ -223,6 +296,7 @@ def test_decode_partials_match_oracle_partials():
             # acc/l is the partition's own normalised output
             assert np.max(np.abs(ga[ok] / gl[ok][:, None] - oa[ok] / ol[ok][:, None]), initial=0) <= 1e-3
             assert np.max(np.abs(np.log(gl[ok]) - np.log(ol[ok])), initial=0) <= 1e-4
+    return n
 
 
 @pytest.mark.parametrize("rows,parts,dim,shift", [
