@@ -8,10 +8,13 @@
 namespace pkv {
 
 // Waves per SIMD the decode kernel for (head_dim, K codec, V codec) is built
-// for (codec -1: per-page dispatch): four where the tile ring fits 128 VGPRs,
-// three for the codecs with group scales. Sizes the library-chosen partition
-// count (workgroups resident at once = compute units x this).
+// for: four where the tile ring fits 128 VGPRs, three for the codecs with
+// group scales; the per-page dispatch kernel (codec -1), which holds the
+// largest tile of every codec and the code of several, one fewer. Sizes the
+// library-chosen partition count (workgroups resident at once = compute
+// units x this).
 constexpr int decode_waves_per_simd(int head_dim, int k_codec, int v_codec) {
+  if (k_codec < 0 || v_codec < 0) return head_dim == 64 ? 3 : 2;
   return (head_dim == 64 || (k_codec == 2 && v_codec == 2)) ? 4 : 3;
 }
 

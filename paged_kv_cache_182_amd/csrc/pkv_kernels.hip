@@ -310,6 +310,32 @@ __device__ inline uint32_t head_off(int codec, int h, int page) {
   return (uint32_t)(h * page * D * bits_of(codec) / 8);
 }
 
+// The lane's run of a plane whose codec is known only at run time: the same
+// D/32 16-byte loads for every codec, branch-free, so the compiler's wait
+// counts stay exact across pages of different codecs. Loads past the run
+// (8- and 4-bit codes) read through an offset beyond the plane: zeros, no
+// traffic. A 4-bit run of 8 bytes (D = 64) is taken from the 16-byte chunk
+// that holds it (two lanes per chunk, the same cache lines).
+template <int D>
+__device__ inline void load_run_any(uint32_t* w, rsrc_t r, int codec, int h, int page, int sub, int lane) {
+  constexpr int NL = D / 32;  // 16-byte loads of a 16-bit run
+  const int bits = bits_of(codec);
+  const uint32_t head = (uint32_t)(h * page * D * bits / 8);
+  const uint32_t base = head + (uint32_t)sub * (uint32_t)(16 * D * bits / 8);
+  const int nreal = bits == 16 ? NL : (bits == 8 ? NL / 2 : 1);
+  const bool half = D * 4 / 32 < 16 && bits == 4;  // 8-byte runs
+  const uint32_t lane_off = half ? 16u * (uint32_t)(lane >> 1) : 16u * (uint32_t)lane;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const u4 x = bload16<CPOL_NT>(r, i < nreal ? base + 1024u * i + lane_off : OFF_NONE);
+    w[4 * i + 0] = x[0]; w[4 * i + 1] = x[1]; w[4 * i + 2] = x[2]; w[4 * i + 3] = x[3];
+  }
+  if (half && (lane & 1)) {
+    w[0] = w[2];
+    w[1] = w[3];
+  }
+}
+
 // Issue the loads of tile `k` of the staged pages into `t`. Every call issues
 // the same loads: a tile with nothing to attend reads through a zero-size
 // resource (zeros, no fault) and is skipped when consumed.
@@ -343,20 +369,12 @@ __device__ inline TileInfo issue_tile(Tile<D, KC, VC>& t, const Desc* desc, int 
     }
   }
   if constexpr (KC == C_ANY) {
-    switch (bits_of(ti.kc)) {
-      case 16: load_run<D, 16>(t.k, rk, head_off<D>(C_FP16, h, page), sub, lane); break;
-      case 8: load_run<D, 8>(t.k, rk, head_off<D>(C_FP8, h, page), sub, lane); break;
-      default: load_run<D, 4>(t.k, rk, head_off<D>(C_INT4, h, page), sub, lane); break;
-    }
+    load_run_any<D>(t.k, rk, ti.kc, h, page, sub, lane);
   } else {
     load_run<D, bits_of(KC)>(t.k, rk, head_off<D>(KC, h, page), sub, lane);
   }
   if constexpr (VC == C_ANY) {
-    switch (bits_of(ti.vc)) {
-      case 16: load_run<D, 16>(t.v, rv, head_off<D>(C_FP16, h, page), sub, lane); break;
-      case 8: load_run<D, 8>(t.v, rv, head_off<D>(C_FP8, h, page), sub, lane); break;
-      default: load_run<D, 4>(t.v, rv, head_off<D>(C_INT4, h, page), sub, lane); break;
-    }
+    load_run_any<D>(t.v, rv, ti.vc, h, page, sub, lane);
   } else {
     load_run<D, bits_of(VC)>(t.v, rv, head_off<D>(VC, h, page), sub, lane);
   }
@@ -576,6 +594,37 @@ __device__ inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti
   }
 }
 
+// A tile of a kernel built for any codec, consumed by the code of the pair
+// (K2, V2) its page holds: its raw words are that pair's run layout.
+template <int D, int K2, int V2, int KC, int VC>
+__device__ inline void consume_as(const Tile<D, KC, VC>& t, const TileInfo& ti, const h8* qv, const h8* qg,
+                                  float scale_log2, float& m_run, float& l_run, f4* acc, int lane) {
+  Tile<D, K2, V2> u;
+#pragma unroll
+  for (int i = 0; i < Tile<D, K2, V2>::KW; ++i) u.k[i] = t.k[i];
+#pragma unroll
+  for (int i = 0; i < Tile<D, K2, V2>::VW; ++i) u.v[i] = t.v[i];
+  consume_tile<D, K2, V2>(u, ti, qv, qg, scale_log2, m_run, l_run, acc, nullptr, lane);
+}
+
+// Consume one tile. With codecs known only at run time, pages of the common
+// one-scale pairs (FP8, FP16, BF16 for both planes) branch once to their own
+// code: no group-scale exchange and no per-fragment codec dispatch; other
+// pairs take the generic path.
+template <int D, int KC, int VC>
+__device__ inline void consume(const Tile<D, KC, VC>& t, const TileInfo& ti, const h8* qv, const h8* qg,
+                               float scale_log2, float& m_run, float& l_run, f4* acc, uint32_t* sc, int lane) {
+  if constexpr (KC == C_ANY && VC == C_ANY) {
+    if (ti.kc == C_FP8 && ti.vc == C_FP8)
+      return consume_as<D, C_FP8, C_FP8>(t, ti, qv, qg, scale_log2, m_run, l_run, acc, lane);
+    if (ti.kc == C_FP16 && ti.vc == C_FP16)
+      return consume_as<D, C_FP16, C_FP16>(t, ti, qv, qg, scale_log2, m_run, l_run, acc, lane);
+    if (ti.kc == C_BF16 && ti.vc == C_BF16)
+      return consume_as<D, C_BF16, C_BF16>(t, ti, qv, qg, scale_log2, m_run, l_run, acc, lane);
+  }
+  consume_tile<D, KC, VC>(t, ti, qv, qg, scale_log2, m_run, l_run, acc, sc, lane);
+}
+
 template <int D, int KC, int VC>
 __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>()))) decode_kernel(const DecodeArgs a) {
   constexpr int NC = D / 32, NB = D / 16;
@@ -734,7 +783,7 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
           // past the end: same loads through a zero-size resource (no traffic)
           inf[nx] = issue_tile<D, KC, VC>(t[nx], desc, min(kn, klast), tpp, a, h, lane, kn > klast);
           if (it + s < nmine && inf[s].valid > 0)
-            consume_tile<D, KC, VC>(t[s], inf[s], qv, qg, a.scale_log2, m_run, l_run, acc, sc, lane);
+            consume<D, KC, VC>(t[s], inf[s], qv, qg, a.scale_log2, m_run, l_run, acc, sc, lane);
         }
       }
     }

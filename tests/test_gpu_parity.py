@@ -49,10 +49,11 @@ def test_group_sizes(hq, hkv):
     check(w, partition_tokens=64)
 
 
-def test_mixed_codecs_per_page():
-    print("case mixed", flush=True)
-    cyc = [(FP16, FP16), (FP8, FP8), (INT8, INT4), (BF16, INT8), (INT4, FP16)]
-    w = poison_tails(small([40, 333, 160], None, None, hq=8, hkv=2, dim=128, page=16,
+@pytest.mark.parametrize("dim", [64, 128])
+def test_mixed_codecs_per_page(dim):
+    print(f"case mixed dim={dim}", flush=True)
+    cyc = [(FP16, FP16), (FP8, FP8), (INT8, INT4), (BF16, INT8), (INT4, FP16), (BF16, BF16), (FP16, INT4)]
+    w = poison_tails(small([40, 333, 160], None, None, hq=8, hkv=2, dim=dim, page=16,
                            codec_of=lambda r, lp: cyc[(r + lp) % len(cyc)]))
     check(w, partition_tokens=32)
     check(w, partition_tokens=0)
