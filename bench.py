@@ -664,8 +664,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--quick", action="store_true", help="headline workload only, no CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-workload", type=int, default=5, choices=(3, 4, 5),
-                    help="workload of --profile-pass (3: batched 32K INT8/INT4, 4: sparse FP8, 5: 1M FP8)")
+    ap.add_argument("--profile-workload", type=int, default=5, choices=(2, 3, 4, 5),
+                    help="workload of --profile-pass (2: 24-layer mixed FP16/FP8, 3: batched 32K INT8/INT4, 4: sparse FP8, 5: 1M FP8)")
     ap.add_argument("--profile-rows", action="store_true",
                     help="short run of the widened rows for rocprofv3 (write side, chunked prefill, page selection)")
     ap.add_argument("--profile-pass", action="store_true",
