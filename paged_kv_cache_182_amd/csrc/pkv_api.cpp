@@ -140,6 +140,8 @@ int prepare(const pkv_params* p, const void* q, const uint8_t* page_pool,
   a->max_pages = p->max_pages_per_row;
   a->max_sel = p->max_sel_pages;
   a->tiles_per_part = p->partition_tokens / 16;  // 0: even split of each row
+  const int tpp = p->page_size / 16;
+  a->tile_shift = (tpp & (tpp - 1)) == 0 ? __builtin_ctz((unsigned)tpp) : -1;
   a->nparts = (int32_t)nparts;
   a->sparse = sparse ? 1 : 0;
   a->final_out = 0;

@@ -37,6 +37,7 @@ struct DecodeArgs {
   int32_t* err;             // device counter or nullptr
   int32_t rows, hq, hkv, group, page, num_pages, max_pages, max_sel;
   int32_t tiles_per_part;   // 16-token tiles per partition; 0: each row's tiles split evenly into nparts
+  int32_t tile_shift;       // log2(page / 16) when that is a power of two, else -1
   int32_t nparts;
   int32_t sparse;
   int32_t final_out;        // 1: write out/lse (single partition); 0: write partials

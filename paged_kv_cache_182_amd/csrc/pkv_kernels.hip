@@ -342,7 +342,9 @@ __device__ inline void load_run_any(uint32_t* w, rsrc_t r, int codec, int h, int
 template <int D, int KC, int VC>
 __device__ inline TileInfo issue_tile(Tile<D, KC, VC>& t, const Desc* desc, int k, int tpp,
                                       const DecodeArgs& a, int h, int lane, bool dead = false) {
-  const int i = k / tpp;
+  // page of the tile and tile within the page: a shift when tiles per page
+  // is a power of two (every usual page size), else a division
+  const int i = a.tile_shift >= 0 ? k >> a.tile_shift : k / tpp;
   const int sub = k - i * tpp;
   TileInfo ti;
   ti.valid = dead ? 0 : min(max(uni(desc[i].valid) - 16 * sub, 0), 16);

@@ -112,6 +112,18 @@ def test_sub_page_partitions(kc, vc, page):
         check(w, partition_tokens=T, what=f"{w.name} page={page} T={T}")
 
 
+@pytest.mark.parametrize("kc,vc", [(FP8, FP8), (INT8, INT4), (None, None)])
+def test_page_size_not_power_of_two(kc, vc):
+    """48-token pages (three tiles): the tile's page comes from a division
+    instead of a shift; fixed, sub-page and even-split partitions."""
+    print(f"case page 48 ({kc},{vc})", flush=True)
+    cyc = [(FP16, FP16), (FP8, FP8), (INT8, INT4)]
+    codec_of = (lambda r, lp: cyc[(r + lp) % 3]) if kc is None else (lambda r, lp: (kc, vc))
+    w = poison_tails(small([47, 48, 49, 700, 1201], kc, vc, hq=8, hkv=2, dim=128, page=48, codec_of=codec_of))
+    for T in (48, 32, 144, 0):
+        check(w, partition_tokens=T, what=f"{w.name} page=48 T={T}")
+
+
 def test_sparse_sub_page_partitions():
     """Sparse mode: a partition's tiles run through the selected pages in list
     order, so partitions finer than a page split selected pages."""
