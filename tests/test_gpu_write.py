@@ -111,6 +111,42 @@ def test_encode_bytes_match_oracle(kc, vc, D, P, src_codec):
     assert np.array_equal(scale_t.cpu().numpy(), rs)
 
 
+@pytest.mark.parametrize("kc,vc,P", [(FP8, FP8, 64), (INT8, INT4, 16)])
+def test_encode_many_units_sampled(kc, vc, P):
+    """More (page, head, plane) units than the launch has waves (4,096
+    workgroups x 4 waves), so waves loop and encode a prefetched second unit:
+    a sample of destination pages, the last ones included, byte-exact with the
+    oracle (each sampled pair encoded by the oracle in a pool of its own)."""
+    hkv, D, n_src = 16, 128, 520            # 520 x 16 x 2 = 16,640 units
+    print(f"case encode many units ({kc},{vc}) P={P}", flush=True)
+    dst_codec = kc | vc << 4
+    x, pool, koff, voff, codec, scale = build_pool(7 + kc, n_src, hkv, P, D, FP16, dst_codec)
+    src = np.arange(n_src, dtype=np.int32)
+    dst = src + n_src
+    pool_t, koff_t, voff_t, codec_t, scale_t, src_t, dst_t = to_dev(pool, koff, voff, codec, scale, src, dst)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    p = params(len(codec), hkv, P, D, pool.size)
+    pkv.encode_pages(p, src_t, dst_t, dst_codec, pool_t, koff_t, voff_t, codec_t, scale_t, err_count=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = pool_t.cpu().numpy()
+    got_scale = scale_t.cpu().numpy()
+    sk = align(slay.plane_bytes(FP16, hkv, P, D))
+    dk = align(slay.plane_bytes(dst_codec & 15, hkv, P, D))
+    dv = align(slay.plane_bytes(dst_codec >> 4, hkv, P, D))
+    rng = np.random.default_rng(3)
+    for i in sorted({0, 1, 255, 511, 512, 515, n_src - 1, *rng.integers(0, n_src, 6).tolist()}):
+        mini = np.zeros(2 * sk + dk + dv, np.uint8)
+        mini[:2 * sk] = pool[koff[i]: koff[i] + 2 * sk]
+        ref, sc = encode_page(mini, 0, sk, int(codec[i]), 2 * sk, 2 * sk + dk, dst_codec, hkv, P, D)
+        d = int(dst[i])
+        nk, nv = slay.plane_bytes(dst_codec & 15, hkv, P, D), slay.plane_bytes(dst_codec >> 4, hkv, P, D)
+        assert np.array_equal(got[koff[d]: koff[d] + nk], ref[2 * sk: 2 * sk + nk]), f"K plane of page {i}"
+        assert np.array_equal(got[voff[d]: voff[d] + nv], ref[2 * sk + dk: 2 * sk + dk + nv]), f"V plane of page {i}"
+        assert np.array_equal(got_scale[d], sc), f"scales of page {i}"
+    assert np.all(codec_t.cpu().numpy()[n_src:] == dst_codec)
+
+
 @pytest.mark.parametrize("kc,vc,D,P", [(FP8, FP8, 128, 64), (INT8, INT4, 128, 16), (INT4, INT4, 64, 32)])
 def test_read_path_on_encoded_pages(kc, vc, D, P):
     """Encode on the device, then decode attention over the destination pages:
