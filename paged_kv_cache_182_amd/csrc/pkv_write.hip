@@ -498,8 +498,10 @@ __device__ inline void store_run(const u4* x, const float (*s2)[D / 32], const f
   }
 }
 
-// DK: the destination codec of both planes when the call fixes one the
-// kernel is specialised for (FP8), else -1 (any pair, chosen per plane).
+// DK: the destination codec pair (K low nibble, V high nibble) the kernel is
+// specialised for (FP8/FP8), else -1 (any pair, chosen per plane at run
+// time). A call has one destination pair. (An INT8/INT4 specialisation held
+// as many registers as the generic kernel and is not built.)
 template <int D, int NT, int DK>
 __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int nunits) {
   constexpr int NC = D / 32, E = D / 4;
@@ -520,7 +522,7 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
   // in registers (the FP8 kernel, free of the INT scale state, holds two
   // 64-token units at head_dim 128 in 224 VGPRs); larger units are loaded at
   // the start of their turn and other waves hide the latency
-  constexpr bool PREFETCH = NT * NC <= (DK == W_FP8 ? 16 : 8);
+  constexpr bool PREFETCH = NT * NC <= (DK == (W_FP8 | W_FP8 << 4) ? 16 : 8);
   UnitSrc<D, NT> cur, nxt;
   int u = gw;
   bool have = false;
@@ -530,7 +532,7 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
   if (u < nunits) {
     unit_of(u, i, h, plane);
     ok = check_pair(a, i, plane, D, dst, scodec, dcodec, so, dof);
-    if (DK >= 0) dcodec = DK;
+    if (DK >= 0) dcodec = plane ? DK >> 4 : DK & 15;
     if (ok) load_unit<D, NT>(cur, a.pool + so + (size_t)h * P * D * 2, wint(dcodec) && plane == 0, lane);
     have = true;
   }
@@ -544,7 +546,7 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
     if (have2) {
       unit_of(un, i2, h2, plane2);
       ok2 = check_pair(a, i2, plane2, D, dst2, scodec2, dcodec2, so2, dof2);
-      if (DK >= 0) dcodec2 = DK;
+      if (DK >= 0) dcodec2 = plane2 ? DK >> 4 : DK & 15;
       if (PREFETCH && ok2) load_unit<D, NT>(nxt, a.pool + so2 + (size_t)h2 * P * D * 2, wint(dcodec2) && plane2 == 0, lane);
     }
 
@@ -556,7 +558,7 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
       auto work = [&](auto bf_tag) {
         constexpr bool BF = decltype(bf_tag)::value;
         const bool is_v = plane == 1;
-        const int dcodec = DK >= 0 ? DK : dcodec_unit;  // a constant in the specialised kernel
+        const int dcodec = DK >= 0 ? (is_v ? DK >> 4 : DK & 15) : dcodec_unit;  // one of two constants when specialised
         const int dbits = wbits(dcodec);
         uint8_t* dp = a.pool + dof + (size_t)h * P * D * dbits / 8;
         // FP8: absmax of the whole (page, head, plane) block
@@ -692,7 +694,7 @@ void launch_encode_reg(const EncodeArgs& a, hipStream_t s) {
   int wgs = (nunits + EW - 1) / EW;
   if (wgs > 4096) wgs = 4096;  // waves loop over the rest, prefetching the next unit
   if (a.dst_codec == (W_FP8 | W_FP8 << 4))
-    hipLaunchKernelGGL((encode_reg_kernel<D, NT, W_FP8>), dim3(wgs), dim3(64 * EW), 0, s, a, nunits);
+    hipLaunchKernelGGL((encode_reg_kernel<D, NT, W_FP8 | W_FP8 << 4>), dim3(wgs), dim3(64 * EW), 0, s, a, nunits);
   else
     hipLaunchKernelGGL((encode_reg_kernel<D, NT, -1>), dim3(wgs), dim3(64 * EW), 0, s, a, nunits);
 }
