@@ -280,27 +280,30 @@ def read_probe(torch):
 
 
 def time_per_layer_graph(torch, pkv, w, steps, warmup, min_rot_bytes):
-    """The 24-layer workload as a model would call it: one launch per layer
-    (one row each, that layer's block table, lengths, q and outputs), the 24
-    launches of a step captured in a HIP graph, one graph per pool copy.
+    """A multi-layer workload as a model would call it: one launch per layer
+    (that layer's rows: its block table, lengths, selection, q and outputs),
+    the launches of a step captured in a HIP graph, one graph per rotation.
     Every graph's output is checked against the eager launches before timing."""
     from synth import effective_kv_bytes_formula
     from synth.device import to_device
     dw = to_device(w)
     p = params_for(pkv, w)
-    p.num_rows = 1
+    per = int(w.info.get("batch", 1))      # rows of one layer
+    L = w.rows // per                       # launches per step
+    p.num_rows = per
     rot, rot_desc = rotations(torch, dw, min_rot_bytes)
-    L, hq, d = w.rows, w.num_q_heads, w.head_dim
-    out = torch.empty((L, hq, d), dtype=torch.float32, device="cuda")
-    lse = torch.empty((L, hq), dtype=torch.float32, device="cuda")
+    hq, d = w.num_q_heads, w.head_dim
+    out = torch.empty((w.rows, hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.rows, hq), dtype=torch.float32, device="cuda")
     ws = torch.zeros(max(pkv.workspace_bytes(p), 16), dtype=torch.uint8, device="cuda")
 
     def layers(args):
-        q, pool, koff, voff, codec, scale, bt, lens, _, _ = args
+        q, pool, koff, voff, codec, scale, bt, lens, sel, sel_lens = args
         for layer in range(L):
-            pkv.decode_attention(p, q[layer:layer + 1], pool, koff, voff, codec, scale, bt[layer:layer + 1],
-                                 lens[layer:layer + 1], out=out[layer:layer + 1], lse=lse[layer:layer + 1],
-                                 workspace=ws)
+            r = slice(layer * per, (layer + 1) * per)
+            pkv.decode_attention(p, q[r], pool, koff, voff, codec, scale, bt[r], lens[r],
+                                 None if sel is None else sel[r], None if sel_lens is None else sel_lens[r],
+                                 out=out[r], lse=lse[r], workspace=ws)
 
     layers(rot[0])
     torch.cuda.synchronize()
@@ -707,6 +710,9 @@ def main():
             log(f"generating workload {cid}")
             w = synth.config(cid)
             also[w.name] = time_workload(torch, pkv, w, args.steps, args.warmup, min_rot)
+            if cid == 4:  # also as a model calls it: one launch of 4 rows per layer
+                g = time_per_layer_graph(torch, pkv, w, args.steps, args.warmup, min_rot)
+                also[g["workload"]] = g
             del w
         log("generating workload 2 (24 layers)")
         w = synth.config(2)
