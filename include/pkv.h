@@ -300,7 +300,8 @@ int pkv_encode_pages(const pkv_params* p, int32_t n, const int32_t* src_pages, c
  * lse = -inf). With T = 1, the whole range and no sliding window this is the
  * decode result (with a sliding window, T = 1 is sliding-window decode). The
  * key range is split into partitions of partition_tokens (0: chosen by the
- * library) starting at kv_begin rounded down to a page boundary; their
+ * library: as many as fill one round of resident workgroups, whole pages of
+ * at least 256 tokens) starting at kv_begin rounded down to a page boundary; their
  * partials are folded as by pkv_lse_combine. With a sliding window, passing
  * kv_begin = (the smallest first-query position) - W + 1 lets the partitions
  * cover only the keys in play.

@@ -10,7 +10,6 @@
 
 namespace {
 
-constexpr int kWorkgroupsWanted = 1024;  // prefill: about four workgroups per compute unit
 constexpr int kMinPartitionTokens = 256;
 constexpr int kComputeUnits = 256;       // gfx950 (MI350X / MI355X): 8 XCDs x 32 compute units
 constexpr int kMinTilesPerPartition = 4; // decode: one 16-token tile per wave of a workgroup
@@ -339,8 +338,12 @@ int plan_prefill(const pkv_params* p, int32_t q_tokens, int32_t kv_begin, int32_
   if (p->partition_tokens > 0) {
     pl->part_tokens = p->partition_tokens;
   } else {
+    // as many partitions as fill one round of resident workgroups (a partial
+    // last round leaves most of the chip idle while it runs)
     const int64_t units = (int64_t)(p->num_rows > 0 ? p->num_rows : 1) * p->num_kv_heads * pl->col_groups;
-    int64_t parts = (kWorkgroupsWanted + units - 1) / units;
+    const int64_t resident =
+        (int64_t)kComputeUnits * pkv::prefill_waves_per_simd(p->head_dim, p->k_codec, p->v_codec);
+    int64_t parts = resident / units;
     if (parts < 1) parts = 1;
     int64_t pt = (span + parts - 1) / parts;
     if (pt < kMinPartitionTokens) pt = kMinPartitionTokens;

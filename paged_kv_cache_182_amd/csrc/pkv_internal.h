@@ -18,6 +18,15 @@ constexpr int decode_waves_per_simd(int head_dim, int k_codec, int v_codec) {
   return (head_dim == 64 || (k_codec == 2 && v_codec == 2)) ? 4 : 3;
 }
 
+// Waves per SIMD of the prefill kernel for (head_dim, K codec, V codec) as
+// compiled (its register count decides): three / two at head_dim 64 and two /
+// one at 128, the second figure for the group-scale and per-page dispatch
+// variants. Sizes the library-chosen prefill partition count.
+constexpr int prefill_waves_per_simd(int head_dim, int k_codec, int v_codec) {
+  const bool fp_pair = k_codec >= 0 && k_codec <= 2 && k_codec == v_codec;
+  return head_dim == 64 ? (fp_pair ? 3 : 2) : (fp_pair ? 2 : 1);
+}
+
 // Everything one decode launch needs, resolved on the host.
 struct DecodeArgs {
   const uint16_t* q;        // fp16 [B][Hq][D]
