@@ -630,8 +630,10 @@ __device__ inline void consume(const Tile<D, KC, VC>& t, const TileInfo& ti, con
 template <int D, int KC, int VC>
 __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>()))) decode_kernel(const DecodeArgs a) {
   constexpr int NC = D / 32, NB = D / 16;
-  constexpr int DH = D / 2;  // the waves merge half the head dims at a time (LDS per workgroup ~17 KB)
-  constexpr int RED_BYTES = (WAVES * 16 * DH + 2 * WAVES * 16) * 4;
+  // the waves' states merge through LDS in one pass over all head dims
+  // (33 KB per workgroup at D 128: four FP8 workgroups per compute unit still
+  // fit; two passes over half the dims, 17 KB, measured 1-2% slower)
+  constexpr int RED_BYTES = (WAVES * 16 * D + 2 * WAVES * 16) * 4;
   constexpr int DESC_BYTES = MAX_DESC * (int)sizeof(Desc);
   __shared__ __attribute__((aligned(16))) unsigned char smem[RED_BYTES > DESC_BYTES ? RED_BYTES : DESC_BYTES];
   __shared__ __attribute__((aligned(16))) uint32_t scale_slots[Tile<D, KC, VC>::GS ? WAVES * 64 : 4];
@@ -805,54 +807,49 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
   // in front of the table reads
   if (bad_row && part == 0 && h == 0 && tid == 0) count_error(a.err);
 
-  // ---- merge the four waves' (m, l, acc) through LDS, half the dims per pass
+  // ---- merge the four waves' (m, l, acc) through LDS
   l_run = row4_sum(l_run);
   float* red_acc = reinterpret_cast<float*>(smem);
-  float* red_m = red_acc + WAVES * 16 * DH;
+  float* red_m = red_acc + WAVES * 16 * D;
   float* red_l = red_m + WAVES * 16;
+  lds_barrier();  // the descriptors are no longer read
+  if (lane < 16) {
+    red_m[wave * 16 + lane] = m_run;
+    red_l[wave * 16 + lane] = l_run;
+  }
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    lds_barrier();  // descriptors (first pass) or the previous half (second) are no longer read
-    if (half == 0 && lane < 16) {
-      red_m[wave * 16 + lane] = m_run;
-      red_l[wave * 16 + lane] = l_run;
-    }
+  for (int n = 0; n < NB; ++n)
 #pragma unroll
-    for (int n = half * NB / 2; n < (half + 1) * NB / 2; ++n)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        red_acc[(wave * 16 + 4 * kq + j) * DH + 16 * (n - half * NB / 2) + col] = acc[n][j];
-    lds_barrier();
+    for (int j = 0; j < 4; ++j) red_acc[(wave * 16 + 4 * kq + j) * D + 16 * n + col] = acc[n][j];
+  lds_barrier();
 
-    for (int idx = tid; idx < G * DH; idx += THREADS) {
-      const int g = idx / DH, dl = idx - g * DH;
-      const int d = half * DH + dl;
-      float M = NEG_INF;
+  for (int idx = tid; idx < G * D; idx += THREADS) {
+    const int g = idx / D, d = idx - g * D;
+    float M = NEG_INF;
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) M = fmaxf(M, red_m[w * 16 + g]);
-      float Ls = 0.f, A = 0.f;
-      if (M != NEG_INF) {
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, red_m[w * 16 + g]);
+    float Ls = 0.f, A = 0.f;
+    if (M != NEG_INF) {
 #pragma unroll
-        for (int w = 0; w < WAVES; ++w) {
-          const float mw = red_m[w * 16 + g];
-          if (mw != NEG_INF) {
-            const float e = __builtin_amdgcn_exp2f(mw - M);
-            Ls += e * red_l[w * 16 + g];
-            A += e * red_acc[(w * 16 + g) * DH + dl];
-          }
+      for (int w = 0; w < WAVES; ++w) {
+        const float mw = red_m[w * 16 + g];
+        if (mw != NEG_INF) {
+          const float e = __builtin_amdgcn_exp2f(mw - M);
+          Ls += e * red_l[w * 16 + g];
+          A += e * red_acc[(w * 16 + g) * D + d];
         }
       }
-      const size_t row = (size_t)b * a.hq + (size_t)h * G + g;
-      if (a.final_out) {
-        a.out[row * D + d] = Ls > 0.f ? A / Ls : 0.f;
-        if (d == 0) a.lse[row] = Ls > 0.f ? M * LN2 + logf(Ls) : NEG_INF;
-      } else {
-        const size_t pi = row * a.nparts + part;
-        a.part_acc[pi * D + d] = A;
-        if (d == 0) {
-          a.part_ml[2 * pi + 0] = Ls > 0.f ? M * LN2 : NEG_INF;
-          a.part_ml[2 * pi + 1] = Ls;
-        }
+    }
+    const size_t row = (size_t)b * a.hq + (size_t)h * G + g;
+    if (a.final_out) {
+      a.out[row * D + d] = Ls > 0.f ? A / Ls : 0.f;
+      if (d == 0) a.lse[row] = Ls > 0.f ? M * LN2 + logf(Ls) : NEG_INF;
+    } else {
+      const size_t pi = row * a.nparts + part;
+      a.part_acc[pi * D + d] = A;
+      if (d == 0) {
+        a.part_ml[2 * pi + 0] = Ls > 0.f ? M * LN2 : NEG_INF;
+        a.part_ml[2 * pi + 1] = Ls;
       }
     }
   }
