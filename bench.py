@@ -707,14 +707,14 @@ def main():
     probe = None
     if not args.quick:
         for cid in (3, 4):
-            log(f"generating workload {cid}")
+            log(f"generating {synth.NAMES[cid]}")
             w = synth.config(cid)
             also[w.name] = time_workload(torch, pkv, w, args.steps, args.warmup, min_rot)
             if cid == 4:  # also as a model calls it: one launch of 4 rows per layer
                 g = time_per_layer_graph(torch, pkv, w, args.steps, args.warmup, min_rot)
                 also[g["workload"]] = g
             del w
-        log("generating workload 2 (24 layers)")
+        log("generating the 24-layer mixed FP16/FP8 workload")
         w = synth.config(2)
         also[w.name] = time_workload(torch, pkv, w, args.steps, args.warmup, min_rot)
         g = time_per_layer_graph(torch, pkv, w, args.steps, args.warmup, min_rot)

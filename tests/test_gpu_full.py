@@ -36,12 +36,12 @@ def test_full_config(cid):
         from oracle.attention import _softmax_attention, gather_kv
         K, V = gather_kv(w, 0, 1)
         ref_o, ref_l = _softmax_attention(K, V, w.q[0, 8:16].astype(np.float64), w.softmax_scale)
-        compare(out[0, 8:16], lse[0, 8:16], ref_o, ref_l, "config 5 head 1")
+        compare(out[0, 8:16], lse[0, 8:16], ref_o, ref_l, "splitk_fp8_1m head 1")
         # the softmax is peaked on about 1% of tokens (top-1% mass reported)
         s = w.softmax_scale * (K @ w.q[0, 8].astype(np.float64))
         top = np.sort(s)[-len(s) // 100:]
         mass = np.exp(top - s.max()).sum() / np.exp(s - s.max()).sum()
-        print(f"config 5 top-1% softmax mass {mass:.3f}", flush=True)
+        print(f"splitk_fp8_1m top-1% softmax mass {mass:.3f}", flush=True)
         return
     ref_o, ref_l = oracle.decode_attention(w, rows=rows)
     if rows is not None:

@@ -63,7 +63,7 @@ def test_fp16_config1_equals_sdpa_with_gqa():
 
 
 def logical_values_cfg1(w, h):
-    # config 1 is generated without keep_values; rebuild it with them
+    # the tiny FP16 workload is generated without keep_values; rebuild it with them
     global _CFG1
     try:
         w1 = _CFG1
