@@ -8,14 +8,24 @@
 namespace pkv {
 
 // Waves per SIMD the decode kernel for (head_dim, K codec, V codec) is built
-// for: four where the tile ring fits 128 VGPRs, three for the codecs with
-// group scales; the per-page dispatch kernel (codec -1), which holds the
-// largest tile of every codec and the code of several, one fewer. Sizes the
-// library-chosen partition count (workgroups resident at once = compute
-// units x this).
+// for. head_dim 128: four for FP8 (the tile ring fits 128 VGPRs), three for
+// the other fixed pairs; head_dim 64: six for the one-scale codecs (80
+// VGPRs), four for the pairs with group scales; the per-page dispatch kernel
+// (codec -1, and every declared pair without a kernel of its own), which
+// holds the largest tile of every codec and the code of several: three at 64,
+// two at 128. Sizes the library-chosen partition count
+// (workgroups resident at once = compute units x this).
+// Whether a declared (K, V) codec pair has a decode kernel of its own: the
+// pairs launch_decode instantiates (FP16, BF16, FP8, INT8 and INT4 with
+// themselves, INT8-K with INT4-V); every other pair runs the per-page kernel.
+constexpr bool decode_pair_kernel(int k_codec, int v_codec) {
+  return (k_codec == v_codec && k_codec >= 0 && k_codec <= 4) || (k_codec == 3 && v_codec == 4);
+}
 constexpr int decode_waves_per_simd(int head_dim, int k_codec, int v_codec) {
-  if (k_codec < 0 || v_codec < 0) return head_dim == 64 ? 3 : 2;
-  return (head_dim == 64 || (k_codec == 2 && v_codec == 2)) ? 4 : 3;
+  if (!decode_pair_kernel(k_codec, v_codec)) return head_dim == 64 ? 3 : 2;
+  const bool one_scale = k_codec <= 2 && v_codec <= 2;
+  if (head_dim == 64) return one_scale ? 6 : 4;
+  return (k_codec == 2 && v_codec == 2) ? 4 : 3;
 }
 
 // Waves per SIMD of the prefill kernel for (head_dim, K codec, V codec) as

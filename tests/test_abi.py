@@ -69,6 +69,12 @@ def test_partitions_and_workspace():
     layer = base(num_q_heads=14, head_dim=64, page_size=1024, num_pages=16, max_pages_per_row=16,
                  partition_tokens=0, k_codec=pkv.CODEC_MIXED, v_codec=pkv.CODEC_MIXED)
     assert pkv.num_partitions(layer) == 256                    # 1024 tiles, 4 per partition
+    # a declared pair without a kernel of its own runs the per-page kernel
+    # (two waves per SIMD at head_dim 128, three at 64)
+    fp8k_fp16v = base(rows=2, partition_tokens=0, v_codec=pkv.FP16)
+    assert pkv.num_partitions(fp8k_fp16v) == 512 // 4
+    d64 = base(rows=2, head_dim=64, partition_tokens=0)       # FP8 at head_dim 64: six waves
+    assert pkv.num_partitions(d64) == 1536 // 4
     many = base(rows=2000, partition_tokens=0)
     assert pkv.num_partitions(many) == 1
 
