@@ -54,6 +54,8 @@ def log(msg):
 def params_for(pkv, w):
     codes = {int(c) for c in w.page_codec}
     kcs, vcs = {c & 15 for c in codes}, {c >> 4 for c in codes}
+    if len(codes) > 1 and all((c & 15) == (c >> 4) <= pkv.FP8_E4M3 for c in codes):
+        kcs, vcs = {pkv.CODEC_MIXED_FLOAT}, {pkv.CODEC_MIXED_FLOAT}   # float pages of several codecs: the smaller per-page kernel
     return pkv.make_params(
         rows=w.rows, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
         page_size=w.page_size, num_pages=w.num_pages, max_pages_per_row=w.max_pages, pool_bytes=w.pool.nbytes,

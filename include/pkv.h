@@ -85,7 +85,12 @@ enum {
   PKV_FP8_E4M3 = 2,
   PKV_INT8_G32 = 3,
   PKV_INT4_G32 = 4,
-  PKV_CODEC_MIXED = -1 /* pkv_params.k_codec / v_codec: any codec per page */
+  PKV_CODEC_MIXED = -1,      /* pkv_params.k_codec / v_codec: any codec per page and plane */
+  PKV_CODEC_MIXED_FLOAT = -2 /* both k_codec and v_codec: each page holds K and V in one of
+                                FP16, BF16, FP8 (the same for both planes), chosen per page.
+                                Runs a smaller decode kernel than PKV_CODEC_MIXED; a page in
+                                another codec is a device-visible error. The prefill treats
+                                it as PKV_CODEC_MIXED. */
 };
 
 /* Status codes. */
@@ -116,8 +121,8 @@ typedef struct pkv_params {
                                 0: the library splits each row's tiles evenly into
                                 pkv_num_partitions(p) partitions (decode), or picks a
                                 whole-page length (prefill)                              */
-  int32_t k_codec;           /* codec of every K plane in this call, or PKV_CODEC_MIXED */
-  int32_t v_codec;           /* codec of every V plane in this call, or PKV_CODEC_MIXED */
+  int32_t k_codec;           /* codec of every K plane in this call, or PKV_CODEC_MIXED(_FLOAT) */
+  int32_t v_codec;           /* codec of every V plane in this call, or PKV_CODEC_MIXED(_FLOAT) */
   float softmax_scale;       /* tau, finite (1/sqrt(head_dim) in the usual case)        */
   uint64_t pool_bytes;       /* size of page_pool in bytes: a plane that does not fit
                                 inside it is a device-visible error                      */

@@ -16,7 +16,9 @@ constexpr int kMinTilesPerPartition = 4; // decode: one 16-token tile per wave o
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-bool valid_codec(int32_t c) { return c == PKV_CODEC_MIXED || (c >= PKV_FP16 && c <= PKV_INT4_G32); }
+bool valid_codec(int32_t c) {
+  return c == PKV_CODEC_MIXED || c == PKV_CODEC_MIXED_FLOAT || (c >= PKV_FP16 && c <= PKV_INT4_G32);
+}
 
 // Checks the plain-value part of the params. Returns PKV_OK or an error.
 int check_params(const pkv_params* p) {
@@ -28,6 +30,7 @@ int check_params(const pkv_params* p) {
   if (p->partition_tokens < 0 || p->partition_tokens % 16 != 0) return PKV_ERR_INVALID_ARG;
   if (!isfinite(p->softmax_scale)) return PKV_ERR_INVALID_ARG;
   if (!valid_codec(p->k_codec) || !valid_codec(p->v_codec)) return PKV_ERR_INVALID_ARG;
+  if ((p->k_codec == PKV_CODEC_MIXED_FLOAT) != (p->v_codec == PKV_CODEC_MIXED_FLOAT)) return PKV_ERR_INVALID_ARG;
   if (p->head_dim != 64 && p->head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (p->num_q_heads / p->num_kv_heads > 16) return PKV_ERR_UNSUPPORTED;
   return PKV_OK;

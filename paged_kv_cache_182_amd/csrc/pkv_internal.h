@@ -13,7 +13,8 @@ namespace pkv {
 // VGPRs), four for the pairs with group scales; the per-page dispatch kernel
 // (codec -1, and every declared pair without a kernel of its own), which
 // holds the largest tile of every codec and the code of several: three at 64,
-// two at 128. Sizes the library-chosen partition count
+// two at 128; its float-only variant (codec -2): four at 64, two at 128.
+// Sizes the library-chosen partition count
 // (workgroups resident at once = compute units x this).
 // Whether a declared (K, V) codec pair has a decode kernel of its own: the
 // pairs launch_decode instantiates (FP16, BF16, FP8, INT8 and INT4 with
@@ -22,6 +23,7 @@ constexpr bool decode_pair_kernel(int k_codec, int v_codec) {
   return (k_codec == v_codec && k_codec >= 0 && k_codec <= 4) || (k_codec == 3 && v_codec == 4);
 }
 constexpr int decode_waves_per_simd(int head_dim, int k_codec, int v_codec) {
+  if (k_codec == -2 && v_codec == -2) return head_dim == 64 ? 4 : 2;  // float pages only
   if (!decode_pair_kernel(k_codec, v_codec)) return head_dim == 64 ? 3 : 2;
   const bool one_scale = k_codec <= 2 && v_codec <= 2;
   if (head_dim == 64) return one_scale ? 6 : 4;

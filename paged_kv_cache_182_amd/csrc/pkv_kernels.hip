@@ -38,7 +38,10 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-enum : int { C_FP16 = 0, C_BF16 = 1, C_FP8 = 2, C_INT8 = 3, C_INT4 = 4, C_ANY = 15 };
+enum : int { C_FP16 = 0, C_BF16 = 1, C_FP8 = 2, C_INT8 = 3, C_INT4 = 4, C_FLT = 14, C_ANY = 15 };
+// C_ANY: any codec per page and plane. C_FLT: per page one of FP16, BF16, FP8,
+// the same for K and V (no group scales: a smaller kernel than C_ANY's).
+__host__ __device__ constexpr bool per_page(int c) { return c == C_ANY || c == C_FLT; }
 
 #ifndef PKV_RING_WORDS
 #define PKV_RING_WORDS 32  // 32-bit words of tile codes a wave keeps in flight
@@ -97,8 +100,8 @@ struct Desc {
 // per-page dispatch variant (C_ANY) reserves the largest.
 template <int D, int KC, int VC>
 struct Tile {
-  static constexpr int KB = KC == C_ANY ? 16 : bits_of(KC);
-  static constexpr int VB = VC == C_ANY ? 16 : bits_of(VC);
+  static constexpr int KB = per_page(KC) ? 16 : bits_of(KC);
+  static constexpr int VB = per_page(VC) ? 16 : bits_of(VC);
   static constexpr int KW = D * KB / 128;  // 32-bit words of K codes per lane
   static constexpr int VW = D * VB / 128;
   static constexpr int SW = D / 16;        // words of 4 tokens x D/32 fp16 scales
@@ -134,7 +137,7 @@ __host__ __device__ constexpr int waves_per_eu() {
 #ifdef PKV_WAVES
   return PKV_WAVES;
 #else
-  return decode_waves_per_simd(D, KC == C_ANY ? -1 : KC, VC == C_ANY ? -1 : VC);
+  return decode_waves_per_simd(D, KC == C_ANY ? -1 : (KC == C_FLT ? -2 : KC), VC == C_ANY ? -1 : (VC == C_FLT ? -2 : VC));
 #endif
 }
 
@@ -302,7 +305,7 @@ __device__ inline h4 v_frag_any(const uint32_t* w, int n, int codec) {
 // page) rather than 8 dims of each 32-dim group (group-scale codecs).
 template <int KC>
 __host__ __device__ constexpr bool k_perm() {
-  return KC != C_ANY && !is_int(KC);
+  return KC != C_ANY && !is_int(KC);  // C_FLT: one-scale codecs only
 }
 // Byte offset of head h's codes inside a plane.
 template <int D>
@@ -349,8 +352,8 @@ __device__ inline TileInfo issue_tile(Tile<D, KC, VC>& t, const Desc* desc, int 
   TileInfo ti;
   ti.valid = dead ? 0 : min(max(uni(desc[i].valid) - 16 * sub, 0), 16);
   const int codec = uni(desc[i].codec);
-  ti.kc = KC == C_ANY ? (codec & 15) : KC;
-  ti.vc = VC == C_ANY ? (codec >> 4) : VC;
+  ti.kc = per_page(KC) ? (codec & 15) : KC;
+  ti.vc = per_page(VC) ? (codec >> 4) : VC;
   ti.sk = unif(desc[i].sk);
   ti.sv = unif(desc[i].sv);
   const bool live = ti.valid > 0;
@@ -370,12 +373,12 @@ __device__ inline TileInfo issue_tile(Tile<D, KC, VC>& t, const Desc* desc, int 
       t.sv[0] = bload4(rv, is_int(ti.vc) && lane >= 32 && lane < 32 + NW ? base + 4 * (lane - 32) : OFF_NONE);
     }
   }
-  if constexpr (KC == C_ANY) {
+  if constexpr (per_page(KC)) {
     load_run_any<D>(t.k, rk, ti.kc, h, page, sub, lane);
   } else {
     load_run<D, bits_of(KC)>(t.k, rk, head_off<D>(KC, h, page), sub, lane);
   }
-  if constexpr (VC == C_ANY) {
+  if constexpr (per_page(VC)) {
     load_run_any<D>(t.v, rv, ti.vc, h, page, sub, lane);
   } else {
     load_run<D, bits_of(VC)>(t.v, rv, head_off<D>(VC, h, page), sub, lane);
@@ -612,11 +615,12 @@ __device__ inline void consume_as(const Tile<D, KC, VC>& t, const TileInfo& ti, 
 // Consume one tile. With codecs known only at run time, pages of the common
 // one-scale pairs (FP8, FP16, BF16 for both planes) branch once to their own
 // code: no group-scale exchange and no per-fragment codec dispatch; other
-// pairs take the generic path.
+// pairs take the generic path (C_ANY; the C_FLT kernel has no others: the
+// gather skipped and counted them).
 template <int D, int KC, int VC>
 __device__ inline void consume(const Tile<D, KC, VC>& t, const TileInfo& ti, const h8* qv, const h8* qg,
                                float scale_log2, float& m_run, float& l_run, f4* acc, uint32_t* sc, int lane) {
-  if constexpr (KC == C_ANY && VC == C_ANY) {
+  if constexpr ((KC == C_ANY && VC == C_ANY) || (KC == C_FLT && VC == C_FLT)) {
     if (ti.kc == C_FP8 && ti.vc == C_FP8)
       return consume_as<D, C_FP8, C_FP8>(t, ti, qv, qg, scale_log2, m_run, l_run, acc, lane);
     if (ti.kc == C_FP16 && ti.vc == C_FP16)
@@ -624,7 +628,7 @@ __device__ inline void consume(const Tile<D, KC, VC>& t, const TileInfo& ti, con
     if (ti.kc == C_BF16 && ti.vc == C_BF16)
       return consume_as<D, C_BF16, C_BF16>(t, ti, qv, qg, scale_log2, m_run, l_run, acc, lane);
   }
-  consume_tile<D, KC, VC>(t, ti, qv, qg, scale_log2, m_run, l_run, acc, sc, lane);
+  if constexpr (KC != C_FLT) consume_tile<D, KC, VC>(t, ti, qv, qg, scale_log2, m_run, l_run, acc, sc, lane);
 }
 
 template <int D, int KC, int VC>
@@ -706,8 +710,9 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
       // checks
       const int kc = cod & 15, vc = cod >> 4;
       bool ok = pp_ok && kc <= C_INT4 && vc <= C_INT4;
-      if (KC != C_ANY && kc != KC) ok = false;
-      if (VC != C_ANY && vc != VC) ok = false;
+      if (KC == C_FLT && !(kc == vc && kc <= C_FP8)) ok = false;  // a float page, one codec for both planes
+      if (!per_page(KC) && kc != KC) ok = false;
+      if (!per_page(VC) && vc != VC) ok = false;
       if ((kc == C_FP8 || vc == C_FP8) && a.scale == nullptr) ok = false;
       if ((ko | vo) & 15) ok = false;
       if (ok && (ko > a.pool_bytes || a.pool_bytes - ko < plane_bytes(kc, a.hkv, P, D))) ok = false;
@@ -997,6 +1002,7 @@ int launch_d(const DecodeArgs& a, int kc, int vc, hipStream_t s) {
   PKV_PAIR(C_INT8, C_INT8)
   PKV_PAIR(C_INT4, C_INT4)
 #undef PKV_PAIR
+  if (kc == C_FLT && vc == C_FLT) return launch_t<D, C_FLT, C_FLT>(a, s);
   return launch_t<D, C_ANY, C_ANY>(a, s);
 }
 
@@ -1004,8 +1010,8 @@ int launch_d(const DecodeArgs& a, int kc, int vc, hipStream_t s) {
 
 int launch_decode(const DecodeArgs& a, int head_dim, int k_codec, int v_codec, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int kc = k_codec < 0 ? C_ANY : k_codec;
-  const int vc = v_codec < 0 ? C_ANY : v_codec;
+  const int kc = k_codec == -2 ? C_FLT : (k_codec < 0 ? C_ANY : k_codec);
+  const int vc = v_codec == -2 ? C_FLT : (v_codec < 0 ? C_ANY : v_codec);
   if (head_dim == 128) return launch_d<128>(a, kc, vc, s);
   if (head_dim == 64) return launch_d<64>(a, kc, vc, s);
   return -2;

@@ -15,6 +15,9 @@ LSE_TOL = 1e-4   # max-abs on lse
 def params_for(w, partition_tokens=None, k_codec=None, v_codec=None):
     codes = {int(c) for c in w.page_codec}
     kcs, vcs = {c & 15 for c in codes}, {c >> 4 for c in codes}
+    if len(codes) > 1 and all((c & 15) == (c >> 4) <= pkv.FP8_E4M3 for c in codes):
+        # float pages of several codecs: the float per-page class, as the benchmark declares it
+        kcs, vcs = {pkv.CODEC_MIXED_FLOAT}, {pkv.CODEC_MIXED_FLOAT}
     if k_codec is None:
         k_codec = kcs.pop() if len(kcs) == 1 else pkv.CODEC_MIXED
     if v_codec is None:

@@ -75,6 +75,11 @@ def test_partitions_and_workspace():
     assert pkv.num_partitions(fp8k_fp16v) == 512 // 4
     d64 = base(rows=2, head_dim=64, partition_tokens=0)       # FP8 at head_dim 64: six waves
     assert pkv.num_partitions(d64) == 1536 // 4
+    # float pages of several codecs (each page one of FP16/BF16/FP8 for K and V):
+    # four waves per SIMD at head_dim 64, two at 128
+    flt = base(num_q_heads=14, head_dim=64, page_size=1024, num_pages=16, max_pages_per_row=16, rows=24,
+               partition_tokens=0, k_codec=pkv.CODEC_MIXED_FLOAT, v_codec=pkv.CODEC_MIXED_FLOAT)
+    assert pkv.num_partitions(flt) == 1024 // 48
     many = base(rows=2000, partition_tokens=0)
     assert pkv.num_partitions(many) == 1
 
@@ -83,6 +88,7 @@ def test_partitions_and_workspace():
     ("head_dim", 96, -2), ("head_dim", 256, -2), ("page_size", 8, -1), ("page_size", 24, -1),
     ("num_q_heads", 15, -1), ("num_q_heads", 34, -2), ("partition_tokens", 100, -1),
     ("partition_tokens", 8, -1), ("partition_tokens", -16, -1),
+    ("k_codec", -2, -1),   # the float class is declared for both planes or neither
     ("num_rows", -1, -1), ("max_pages_per_row", 0, -1), ("k_codec", 9, -1),
 ])
 def test_bad_params_rejected(field, value, status):

@@ -124,6 +124,34 @@ def test_page_size_not_power_of_two(kc, vc):
         check(w, partition_tokens=T, what=f"{w.name} page=48 T={T}")
 
 
+@pytest.mark.parametrize("dim", [64, 128])
+def test_float_class_pages(dim):
+    """PKV_CODEC_MIXED_FLOAT: every page FP16, BF16 or FP8 for both planes,
+    chosen per page (the smaller per-page kernel), any partition size."""
+    print(f"case float class dim={dim}", flush=True)
+    cyc = [(FP16, FP16), (FP8, FP8), (BF16, BF16)]
+    w = poison_tails(small([5, 300, 1000, 2047], None, None, hq=16, hkv=2, dim=dim, page=64,
+                           codec_of=lambda r, lp: cyc[(r + 2 * lp) % 3]))
+    assert params_for(w).k_codec == pkv.CODEC_MIXED_FLOAT
+    for T in (0, 48, 256):
+        check(w, partition_tokens=T, what=f"float class dim={dim} T={T}")
+
+
+def test_float_class_rejects_other_pages():
+    """Under the float declaration an INT page and a page with different K and
+    V codecs are device-visible errors: counted and skipped."""
+    print("case float class errors", flush=True)
+    codes = {(0, 0): (FP16, FP16), (0, 1): (INT8, INT4), (0, 2): (FP8, FP8),
+             (1, 0): (FP8, FP16), (1, 1): (FP8, FP8), (1, 2): (BF16, BF16)}
+    w = small([48, 48], None, None, hq=8, hkv=2, dim=128, page=16, codec_of=lambda r, lp: codes[(r, lp)])
+    dw = to_device(w)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, lse = run(dw, params_for(w, 16, k_codec=pkv.CODEC_MIXED_FLOAT, v_codec=pkv.CODEC_MIXED_FLOAT), err=err)
+    assert int(err.item()) == 2
+    w.page_sel, w.sel_lens = np.array([[0, 2], [1, 2]], dtype=np.int32), np.array([2, 2], dtype=np.int32)
+    compare(out, lse, *oracle.decode_attention(w), "float class skips other pages")
+
+
 def test_sparse_sub_page_partitions():
     """Sparse mode: a partition's tiles run through the selected pages in list
     order, so partitions finer than a page split selected pages."""
