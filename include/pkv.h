@@ -76,7 +76,9 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+/* 2: partitions are ranges of 16-token tiles (partition_tokens a multiple of
+ *    16; 0 splits each row evenly), PKV_CODEC_MIXED_FLOAT. */
+#define PKV_ABI_VERSION 2
 
 /* Page codecs; page_codec[p] = K codec | (V codec << 4). */
 enum {

@@ -85,7 +85,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_select_pages.restype = ctypes.c_int
     lib.pkv_select_pages.argtypes = [pp] + [i32] * 6 + [vp] * 9
     lib.pkv_lse_fold_into.argtypes = [i32, i32, vp, vp, vp, vp, vp]
-    if lib.pkv_abi_version() != 1:
+    if lib.pkv_abi_version() != 2:  # tile-range partitions, the float per-page codec class
         raise RuntimeError("libpkv ABI version mismatch")
     _lib = lib
     return lib

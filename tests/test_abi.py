@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(pkv.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pkv_abi_version() == 1
+    assert lib.pkv_abi_version() == 2
 
 
 def test_one_hip_runtime_in_process():
