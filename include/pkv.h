@@ -141,7 +141,7 @@ const char* pkv_status_string(int status);
  * With partition_tokens = 0: as many as fill one round of resident
  * workgroups (256 compute units x the kernel's waves per SIMD, four waves per
  * workgroup, rows x KV heads workgroups per partition index), at most one per
- * 4 tiles of the longest row and at least 1; row b's partition i then covers
+ * 8 tiles of the longest row and at least 1; row b's partition i then covers
  * tiles [i c, (i + 1) c), c = max(1, ceil(ceil(L_b / 16) / n)) (dense) or
  * ceil(sel_lens[b] P / 16 / n) (sparse). */
 int pkv_num_partitions(const pkv_params* p);

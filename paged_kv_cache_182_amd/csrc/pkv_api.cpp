@@ -12,7 +12,7 @@ namespace {
 
 constexpr int kMinPartitionTokens = 256;
 constexpr int kComputeUnits = 256;       // gfx950 (MI350X / MI355X): 8 XCDs x 32 compute units
-constexpr int kMinTilesPerPartition = 4; // decode: one 16-token tile per wave of a workgroup
+constexpr int kMinTilesPerPartition = 8; // decode: two 16-token tiles per wave of a workgroup
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -47,7 +47,8 @@ int64_t row_tiles(const pkv_params* p) { return row_capacity(p) * (p->page_size 
 // Partitions per row. A positive partition_tokens fixes their length; 0 lets
 // the library split each row's tiles evenly into as many partitions as fill
 // one round of resident decode workgroups (compute units x waves per SIMD;
-// four waves per workgroup), with at least one tile per wave in a partition.
+// four waves per workgroup), with at least two tiles per wave in a partition
+// (one per wave measured slower for one-row launches: more partials to fold).
 int64_t partitions(const pkv_params* p) {
   const int64_t tiles = row_tiles(p);
   if (p->partition_tokens > 0) {

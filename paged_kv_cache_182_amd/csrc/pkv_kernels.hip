@@ -1021,7 +1021,10 @@ int launch_combine(int rows, int nparts, int head_dim, const float* part_acc, co
                    float* out, float* lse, void* stream) {
   if (rows == 0) return 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (nparts <= FOLD_SMALL_MAX) {
+  // one thread per (row, dim) walks the parts eight at a time: right when
+  // that is one round of loads, or when there are threads enough to fill the
+  // chip; few rows with many parts go to one wave per (row, 4 dims)
+  if (nparts <= 8 || (nparts <= FOLD_SMALL_MAX && (long long)rows * head_dim >= 16384)) {
     const long long threads = (long long)rows * head_dim;
     hipLaunchKernelGGL(combine_small_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, rows,
                        nparts, head_dim, part_acc, part_ml, out, lse);
