@@ -8,7 +8,9 @@ online softmax, P.V, partition partials, log-sum-exp fold). The headline
 workload is the 1M-token split-K FP8 decode (batch 1, 16 query / 2 KV heads,
 head_dim 128, 64-token pages, 512 partitions). The 32K batched INT8-K/INT4-V
 workload, the sparse 48-row FP8 selection and the 24-layer mixed FP16/FP8
-workload are timed the same way and reported beside it.
+workload are timed the same way and reported beside it, and so are the write
+side (page demotion, token append), the chunked prefill and the GPU page
+selection.
 
 Inputs are resident in HBM before timing. Each step reads a different copy
 of the pool (or, for the sparse workload, a different placement of its
@@ -21,8 +23,9 @@ block and all seven are in `detail`). The value is effective KV bytes (codes
 + scales of attended tokens) divided by that step time; `total_bytes` beside
 it counts q, outputs, tables and partials too. roofline.achieved uses the
 split-K kernel alone, timed with HIP events around each launch on the stream
-it runs on. The 24-layer workload is also timed as a model calls it, one
-launch per layer, the 24 launches captured in a HIP graph. The read probes
+it runs on. The 24-layer and the sparse 12-layer workloads are also timed as
+a model calls them, one launch per layer (of 1 and 4 rows), the launches of
+a step captured in a HIP graph. The read probes
 (libpkv_probe.so: a linear stream and random 2 KB chunks) give the measured
 ceiling on the same device.
 
