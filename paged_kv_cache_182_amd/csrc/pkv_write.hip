@@ -342,6 +342,16 @@ __device__ inline float recip_div(float x, float s, float r) {
   return __builtin_fmaf(-__builtin_fmaf(q0, s, -x), r, q0);
 }
 
+// RN(1 / s) for a stored fp16 group scale s (as float, in [2^-24, 65504]):
+// the hardware reciprocal estimate and one Newton step. Exact for every such s
+// and every estimate within two units in the last place of the result, checked
+// exhaustively by tests/division/check_scale_div.c (which also covers the
+// group scale m / qmax taken through recip_div with the constant RN(1 / qmax)).
+__device__ inline float recip_fp16_scale(float s) {
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  return __builtin_fmaf(r0, __builtin_fmaf(-s, r0, 1.0f), r0);
+}
+
 // ------------------------------------------------------ encode, register path
 // Pages of up to four tiles (P <= 64): one wave per unit (page pair, KV head,
 // plane), units dealt round-robin over the waves of the grid. The wave holds
@@ -585,6 +595,7 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
         if (lane == 0 && a.scale) a.scale[((size_t)dst * hkv + h) * 2 + plane] = s8;
         if (h == 0 && plane == 0 && lane == 0) a.codec_out[dst] = (uint8_t)a.dst_codec;
         const float qmax = dcodec == W_INT8 ? 127.0f : 7.0f;
+        const float rqmax = dcodec == W_INT8 ? 1.0f / 127.0f : 1.0f / 7.0f;  // RN(1 / qmax), folded
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const u4* x = cur.x[t];
@@ -596,7 +607,7 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
           if (wint(dcodec)) {
             const size_t sc_base = (size_t)hkv * P * D * dbits / 8 + ((size_t)h * P + 16 * t) * NC * 2;
             auto scale_of = [&](float m) {  // fp16 scale kept inside fp16's finite range
-              _Float16 s16 = (_Float16)__fdiv_rn(m, qmax);
+              _Float16 s16 = (_Float16)recip_div(m, qmax, rqmax);  // = RN(m / qmax)
               s16 = s16 == (_Float16)0.0f ? __builtin_bit_cast(_Float16, (uint16_t)0x0001) : s16;
               s16 = s16 > (_Float16)65504.0f ? (_Float16)65504.0f : s16;
               return m == 0.f ? (_Float16)1.0f : s16;
@@ -616,7 +627,7 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
               if (l16 < 4 * NC) {
                 const _Float16 s16 = scale_of(mine);
                 sx[wv][kq][l16] = (float)s16;
-                rx[wv][kq][l16] = __fdiv_rn(1.0f, (float)s16);
+                rx[wv][kq][l16] = recip_fp16_scale((float)s16);
                 const int j = l16 / NC, g = l16 % NC;
                 *reinterpret_cast<_Float16*>(a.pool + dof + sc_base + ((size_t)(4 * kq + j) * NC + g) * 2) = s16;
               }
@@ -640,7 +651,7 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
                 for (int k = 0; k < 8; ++k) m = fmaxf(m, __builtin_fabsf(chunk_elem<BF>(x[c], k)));
                 m = rows4_max(m);
                 const _Float16 s16 = scale_of(m);
-                const float sf = (float)s16, rf = __fdiv_rn(1.0f, sf);
+                const float sf = (float)s16, rf = recip_fp16_scale(sf);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                   s2[j][c] = sf;

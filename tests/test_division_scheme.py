@@ -1,7 +1,7 @@
 """The page encoder's division (a reciprocal and one fused correction) decides
 every stored code exactly as correctly rounded division does, over every
 input the encoder can meet: an exhaustive check over all fp16 and bf16 source
-values, in C (tests/division/check_recip_div.c), no GPU."""
+values, in C (tests/division/check_recip_div.c and check_scale_div.c), no GPU."""
 import os
 import shutil
 import subprocess
@@ -21,3 +21,20 @@ def test_reciprocal_division_is_exact_on_reachable_inputs(tmp_path):
     print(res.stdout)
     assert res.returncode == 0, res.stdout + res.stderr
     assert res.stdout.split() == ["fp8_fp16", "0", "fp8_bf16", "0", "int_fp16", "0", "int_bf16", "0"]
+
+
+SCALE_SRC = os.path.join(HERE, "division", "check_scale_div.c")
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_group_scale_division_and_reciprocal_are_exact(tmp_path):
+    """The INT group scale m / qmax (a multiply by the constant RN(1 / qmax)
+    and one fused correction) and the reciprocal of the stored fp16 scale (the
+    hardware estimate and one Newton step) equal the correctly rounded results
+    for every fp16 and bf16 absmax and every fp16 scale."""
+    exe = str(tmp_path / "check_scale_div")
+    subprocess.run(["gcc", "-O2", "-o", exe, SCALE_SRC, "-lm"], check=True)
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    print(res.stdout)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert res.stdout.split() == ["scale_div", "0", "recip_fp16", "0"]
