@@ -502,7 +502,6 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
     for (int n = 0; n < NB; ++n) acc[cb][n] = f4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const f4 zero = {0.f, 0.f, 0.f, 0.f};
   // ---- tiles [t0, t0 + 16 ntiles): 16-token tiles of the partition up to
   // the last key any column of the workgroup attends
   const int t0 = wg_lo & ~15;

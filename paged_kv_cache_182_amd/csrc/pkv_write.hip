@@ -514,7 +514,7 @@ __device__ inline void store_run(const u4* x, const float (*s2)[D / 32], const f
 // as many registers as the generic kernel and is not built.)
 template <int D, int NT, int DK>
 __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int nunits) {
-  constexpr int NC = D / 32, E = D / 4;
+  constexpr int NC = D / 32;
   __shared__ float sx[EW][4][16];  // per wave: INT V scales of its tile, [row][combo]
   __shared__ float rx[EW][4][16];  // and their reciprocals RN(1 / s)
   const int lane = threadIdx.x & 63;

@@ -88,6 +88,15 @@ def test_large_rows_radix_select():
     check(lens, 16, 16, 127, 0, 1, 64, 128, seed=12, ties=True)
 
 
+@pytest.mark.parametrize("idx_dim", [64, 128])
+def test_many_rows_ragged_short_and_empty(idx_dim):
+    """34 rows of up to 16,384 blocks (2,176 scoring workgroups), ragged,
+    short and empty: workgroups past a row's last block have nothing to do,
+    and the last chunk of a row is partial."""
+    lens = [262144 - 37 * r for r in range(30)] + [0, 4097, 131072 + 3, 256 * 16 * 3]
+    check(lens, 16, 16, 127, 0, 1, idx_dim, pkv.select_capacity(16, 16, 127, 0, 1), seed=13 + idx_dim)
+
+
 def test_selection_feeds_sparse_decode():
     """GPU selection -> pkv_decode_attention in sparse mode == the oracle's
     decode over the same selected pages."""
