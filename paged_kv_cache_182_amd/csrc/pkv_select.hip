@@ -53,10 +53,11 @@ __device__ inline int clamp_len(int L, const SelectArgs& a) {
   return L < 0 ? 0 : (int)((int64_t)L > cap ? cap : L);
 }
 
-// Summaries are staged through LDS 64 dims at a time with coalesced 16-byte
-// loads (a workgroup's 256 rows are contiguous in the slab; every thread
-// issues its eight loads of a round before storing any), then each thread
-// accumulates its own row in index order from LDS.
+// Summaries are staged through LDS 64 dims at a time with coalesced,
+// non-temporal (read once) 16-byte loads (a workgroup's 256 rows are
+// contiguous in the slab; every thread issues its eight loads of a round
+// before storing any), then each thread accumulates its own row in index
+// order from LDS.
 constexpr int CH = 64;                 // dims per staging round
 constexpr int ROW_WORDS = CH / 2 + 4;  // one staged row: 128 bytes + 16 bytes of padding
 constexpr int LOADS = CH / 8;          // 16-byte loads per thread per full round
@@ -86,7 +87,7 @@ __global__ void __launch_bounds__(SCORE_THREADS) score_kernel(const SelectArgs a
     for (int k = 0; k < LOADS; ++k) {
       const int e = tid + k * SCORE_THREADS;
       const int r = e / chunks, c = e % chunks;
-      if (e < total) x[k] = *reinterpret_cast<const u4*>(base + r * row_bytes + (size_t)(d0 + 8 * c) * 2);
+      if (e < total) x[k] = __builtin_nontemporal_load(reinterpret_cast<const u4*>(base + r * row_bytes + (size_t)(d0 + 8 * c) * 2));
     }
 #pragma unroll
     for (int k = 0; k < LOADS; ++k) {
