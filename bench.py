@@ -606,10 +606,12 @@ def cpu_baseline(w_full, min_seconds=10.0):
         if dt >= min_seconds or reps >= 50:
             break
     eff = effective_kv_bytes_formula(w_full)
-    return {"value": reps * eff / dt / 1e9, "unit": "GB/s", "cores": int(blas), "kind": "oracle",
+    cores = len(os.sched_getaffinity(0))
+    return {"value": reps * eff / dt / 1e9, "unit": "GB/s", "cores": cores, "blas_threads": int(blas),
+            "kind": "oracle",
             "sample": f"{reps} whole step(s) of {w_full.name} ({eff / 2**20:.1f} MiB effective each) "
-                      f"in {dt:.1f} s; float64 numpy, page gather single-threaded, BLAS with "
-                      f"{blas} threads",
+                      f"in {dt:.1f} s on {cores} host cores; float64 numpy, page gather single-threaded, "
+                      f"BLAS with {blas} threads",
             "seconds": dt, "steps_per_s": reps / dt}
 
 

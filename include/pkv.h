@@ -54,8 +54,9 @@
  * unless stated otherwise). Calls enqueue work on `stream` (a hipStream_t;
  * NULL is the default stream) and return without synchronizing; buffers must
  * stay valid until that work completes. The library allocates nothing and
- * keeps no state, so calls are re-entrant; calls that share an output or a
- * workspace race unless ordered on one stream.
+ * keeps no state beyond a per-device cache of the compute-unit count, so
+ * calls are re-entrant; calls that share an output or a workspace race
+ * unless ordered on one stream.
  *
  * Errors. Return values report host-visible problems only. Problems that are
  * visible only on the device (a page id outside [0, num_pages), an unknown
@@ -139,8 +140,9 @@ const char* pkv_status_string(int status);
 /* Partitions each row is split into for these params (>= 1), or a negative
  * status if the params are invalid. Sizes the workspace and the partials.
  * With partition_tokens = 0: as many as fill one round of resident
- * workgroups (256 compute units x the kernel's waves per SIMD, four waves per
- * workgroup, rows x KV heads workgroups per partition index), at most one per
+ * workgroups (the current device's compute units -- 256 on MI355X -- x the
+ * kernel's waves per SIMD, four waves per workgroup, rows x KV heads
+ * workgroups per partition index), at most one per
  * 8 tiles of the longest row and at least 1; row b's partition i then covers
  * tiles [i c, (i + 1) c), c = max(1, ceil(ceil(L_b / 16) / n)) (dense) or
  * ceil(sel_lens[b] P / 16 / n) (sparse). */
@@ -209,9 +211,10 @@ int pkv_decode_partials(const pkv_params* p, const void* q, const uint8_t* page_
  *   M = max_p m_p;  w_p = exp(m_p - M);  L = sum_p w_p l_p;
  *   out = sum_p w_p acc_p / L;  lse = M + ln L,
  *
- * summing the parts in a fixed order (run-to-run identical results). Parts with
- * m_p = -inf or l_p = 0 are empty; a row whose parts are all empty gets
- * out = 0 and lse = -inf.
+ * summing the parts in a fixed order (run-to-run identical results). A part
+ * is empty unless l_p > 0 and m_p is finite (an empty partition writes
+ * (0, -inf, 0)); an empty part's acc is never read, and a row whose parts
+ * are all empty gets out = 0 and lse = -inf.
  *
  *   part_acc  fp32 [rows][num_parts][head_dim], unnormalised sum exp(s - m_p) v.
  *   part_ml   fp32 [rows][num_parts][2] = (m_p natural-log max, l_p sum).
@@ -245,8 +248,9 @@ int pkv_lse_combine(int32_t rows, int32_t num_parts, int32_t head_dim, const flo
  *
  * Writes 2*Hkv*D codes per row and nothing else. A row whose length is
  * negative or beyond max_pages_per_row, whose page id is out of range, whose
- * page is not 16-bit in both planes or whose plane lies outside the pool is
- * counted in *err_count (if given) and skipped. Host-visible errors as in
+ * page is not 16-bit in both planes or either of whose planes is misaligned
+ * or lies outside the pool is counted once in *err_count (if given) and
+ * skipped: neither plane is written. Host-visible errors as in
  * pkv_decode_attention. */
 int pkv_append_kv(const pkv_params* p, const void* k_new, const void* v_new, uint8_t* page_pool,
                   const uint64_t* page_k_off, const uint64_t* page_v_off, const uint8_t* page_codec,
@@ -258,9 +262,10 @@ int pkv_append_kv(const pkv_params* p, const void* k_new, const void* v_new, uin
  *                 BF16 in both planes) is read, every slot of it, and page
  *                 dst_pages[i] is written. The destination planes live at
  *                 page_k_off / page_v_off[dst] (16-byte aligned, inside the
- *                 pool, sized for dst_codec) and must not overlap the source
- *                 planes. No destination may appear twice, or as a source, in
- *                 one call (not checked).
+ *                 pool, sized for dst_codec) and must overlap neither the
+ *                 source planes nor each other. No destination may appear
+ *                 twice, or as a source of another pair, in one call (not
+ *                 checked).
  *   dst_codec     K codec in the low nibble, V codec in the high nibble:
  *                 FP16, BF16, FP8 e4m3, INT8 or INT4. Encoding, decided in
  *                 fp32:
@@ -278,8 +283,10 @@ int pkv_append_kv(const pkv_params* p, const void* k_new, const void* v_new, uin
  *                 if neither plane is FP8.
  *
  * A pair with an id out of range, equal ids, a source that is not 16-bit,
- * a plane outside the pool, a misaligned plane or overlapping planes is
- * counted in *err_count (if given) and skipped. Host-visible errors as in
+ * a plane outside the pool, a misaligned plane or overlapping planes -- in
+ * either plane -- is counted once in *err_count (if given) and skipped
+ * whole: no byte of either destination plane, no scale and no page_codec
+ * entry of it is written. Host-visible errors as in
  * pkv_decode_attention; PKV_ERR_INVALID_ARG also for a bad codec nibble or a
  * missing page_scale. */
 int pkv_encode_pages(const pkv_params* p, int32_t n, const int32_t* src_pages, const int32_t* dst_pages,

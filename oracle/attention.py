@@ -123,14 +123,19 @@ def fold(acc, m, l):
     acc [..., n, D], m [..., n], l [..., n] ->
     M = max_p m_p; w_p = exp(m_p - M); L = sum_p w_p l_p;
     out = sum_p w_p acc_p / L; lse = M + ln L. All parts empty -> (0, -inf).
+
+    A part is empty unless l_p > 0 and m_p is finite (an empty partition
+    leaves (0, -inf, 0)); empty parts take no part in M and their acc is
+    never read.
     """
     acc, m, l = np.asarray(acc, float), np.asarray(m, float), np.asarray(l, float)
-    M = m.max(axis=-1)
+    live = np.isfinite(m) & (l > 0)
+    M = np.where(live, m, -np.inf).max(axis=-1)
     finite = np.isfinite(M)
     Ms = np.where(finite, M, 0.0)
-    wts = np.where(np.isfinite(m), np.exp(m - Ms[..., None]), 0.0)
+    wts = np.where(live, np.exp(np.where(live, m, 0.0) - Ms[..., None]), 0.0)
     L = (wts * l).sum(axis=-1)
-    num = (wts[..., None] * acc).sum(axis=-2)
+    num = (np.where(live[..., None], wts[..., None] * np.where(live[..., None], acc, 0.0), 0.0)).sum(axis=-2)
     safe = np.where(finite & (L > 0), L, 1.0)
     out = np.where((finite & (L > 0))[..., None], num / safe[..., None], 0.0)
     lse = np.where(finite & (L > 0), Ms + np.log(safe), -np.inf)

@@ -3,16 +3,42 @@
 
 #include "../../include/pkv.h"
 
+#include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "pkv_internal.h"
 
 namespace {
 
 constexpr int kMinPartitionTokens = 256;
-constexpr int kComputeUnits = 256;       // gfx950 (MI350X / MI355X): 8 XCDs x 32 compute units
 constexpr int kMinTilesPerPartition = 8; // decode: two 16-token tiles per wave of a workgroup
+
+// Compute units of the current HIP device, read once per device and cached
+// (the only state the library keeps). Where no device can be queried (a
+// host without a GPU sizing partitions) the count of gfx950 parts, 256
+// (MI350X / MI355X: 8 XCDs x 32), is used.
+constexpr int kDefaultComputeUnits = 256;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int compute_units() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kDefaultComputeUnits;
+  }
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return kDefaultComputeUnits;
+  }
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -57,7 +83,7 @@ int64_t partitions(const pkv_params* p) {
   }
   const int64_t units = (int64_t)(p->num_rows > 0 ? p->num_rows : 1) * p->num_kv_heads;
   const int64_t resident =
-      (int64_t)kComputeUnits * pkv::decode_waves_per_simd(p->head_dim, p->k_codec, p->v_codec);
+      (int64_t)compute_units() * pkv::decode_waves_per_simd(p->head_dim, p->k_codec, p->v_codec);
   int64_t parts = resident / units;
   const int64_t most = (tiles + kMinTilesPerPartition - 1) / kMinTilesPerPartition;
   if (parts > most) parts = most;
@@ -346,7 +372,7 @@ int plan_prefill(const pkv_params* p, int32_t q_tokens, int32_t kv_begin, int32_
     // last round leaves most of the chip idle while it runs)
     const int64_t units = (int64_t)(p->num_rows > 0 ? p->num_rows : 1) * p->num_kv_heads * pl->col_groups;
     const int64_t resident =
-        (int64_t)kComputeUnits * pkv::prefill_waves_per_simd(p->head_dim, p->k_codec, p->v_codec);
+        (int64_t)compute_units() * pkv::prefill_waves_per_simd(p->head_dim, p->k_codec, p->v_codec);
     int64_t parts = resident / units;
     if (parts < 1) parts = 1;
     int64_t pt = (span + parts - 1) / parts;

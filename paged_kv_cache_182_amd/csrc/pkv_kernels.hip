@@ -866,8 +866,11 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
 // p = l + 64k (every load of a batch in flight together); the 64 lanes then
 // merge by a fixed butterfly (lane distance 32, 16, ..., 1), so results are
 // run-to-run identical.
+// A part is empty (and its acc never read) unless l > 0 and m is finite.
+__device__ inline bool live_part(float m, float l) { return l > 0.f && __builtin_isfinite(m); }
+
 __device__ inline void lse_merge(float& M, float& L, f4& A, float m2, float l2, f4 a2) {
-  if (!(l2 > 0.f)) return;
+  if (!live_part(m2, l2)) return;
   if (!(L > 0.f)) { M = m2; L = l2; A = a2; return; }
   const float mx = fmaxf(M, m2);
   const float c1 = __expf(M - mx), c2 = __expf(m2 - mx);
@@ -965,7 +968,7 @@ __global__ void __launch_bounds__(256) combine_small_kernel(int rows, int nparts
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      if (l[u] > 0.f) {
+      if (live_part(m[u], l[u])) {
         // running log-sum-exp over the parts seen so far
         if (m[u] > M) {
           const float c = M == NEG_INF ? 0.f : __expf(M - m[u]);

@@ -78,6 +78,46 @@ __device__ inline void count_err(int32_t* err) {
   if (err) atomicAdd(err, 1);
 }
 
+// A plane at byte offset `off` in codec c: 16-byte aligned and inside the pool.
+__device__ inline bool plane_fits(uint64_t off, int c, int hkv, int page, int d, uint64_t pool_bytes) {
+  return (off & 15) == 0 && off <= pool_bytes && pool_bytes - off >= wplane_bytes(c, hkv, page, d);
+}
+
+__device__ inline bool disjoint(uint64_t a, uint64_t an, uint64_t b, uint64_t bn) { return a + an <= b || b + bn <= a; }
+
+// Checks of encode pair i, for both planes at once (a pair with one bad plane
+// is skipped whole): ids in range and distinct, a 16-bit source in both
+// planes, every plane aligned and inside the pool, no destination plane
+// overlapping a source plane or the other destination plane. Returns the
+// answer (the same in every lane and every unit of the pair) and, for
+// `plane`, the destination id, the source and destination codecs and the
+// source and destination plane offsets.
+__device__ inline bool check_pair(const EncodeArgs& a, int i, int plane, int D, int& dst, int& scodec, int& dcodec,
+                                  uint64_t& so, uint64_t& dof) {
+  const int P = a.page, hkv = a.hkv;
+  const int src = a.src[i];
+  dst = a.dst[i];
+  const int dk = a.dst_codec & 15, dv = (a.dst_codec >> 4) & 15;
+  dcodec = plane ? dv : dk;
+  scodec = 0;
+  so = 0;
+  dof = 0;
+  if (!((unsigned)src < (unsigned)a.num_pages && (unsigned)dst < (unsigned)a.num_pages && src != dst)) return false;
+  const int cb = a.codec[src];
+  const int sk = cb & 15, sv = cb >> 4;
+  const uint64_t sko = a.koff[src], svo = a.voff[src], dko = a.koff[dst], dvo = a.voff[dst];
+  scodec = plane ? sv : sk;
+  so = plane ? svo : sko;
+  dof = plane ? dvo : dko;
+  if (!(w16(sk) && w16(sv))) return false;
+  const uint64_t skb = wplane_bytes(sk, hkv, P, D), svb = wplane_bytes(sv, hkv, P, D);
+  const uint64_t dkb = wplane_bytes(dk, hkv, P, D), dvb = wplane_bytes(dv, hkv, P, D);
+  const bool fit = plane_fits(sko, sk, hkv, P, D, a.pool_bytes) && plane_fits(svo, sv, hkv, P, D, a.pool_bytes) &&
+                   plane_fits(dko, dk, hkv, P, D, a.pool_bytes) && plane_fits(dvo, dv, hkv, P, D, a.pool_bytes);
+  return fit && disjoint(dko, dkb, sko, skb) && disjoint(dko, dkb, svo, svb) && disjoint(dvo, dvb, sko, skb) &&
+         disjoint(dvo, dvb, svo, svb) && disjoint(dko, dkb, dvo, dvb);
+}
+
 // ------------------------------------------------------------------ append
 // Grid (row, KV head, plane), 64 threads; thread = dims d, d + 64, ...
 __global__ void __launch_bounds__(64) append_kernel(AppendArgs a) {
@@ -93,11 +133,14 @@ __global__ void __launch_bounds__(64) append_kernel(AppendArgs a) {
   int codec = 0;
   uint64_t off = 0;
   if (ok) {
+    // both planes are checked in every unit, so a row with one bad plane
+    // writes neither of them (and is counted once)
     const int cb = a.codec[pp];
+    const uint64_t ko = a.koff[pp], vo = a.voff[pp];
+    ok = w16(cb & 15) && w16(cb >> 4) && plane_fits(ko, cb & 15, a.hkv, P, D, a.pool_bytes) &&
+         plane_fits(vo, cb >> 4, a.hkv, P, D, a.pool_bytes);
     codec = plane ? (cb >> 4) : (cb & 15);
-    ok = w16(cb & 15) && w16(cb >> 4);
-    off = plane ? a.voff[pp] : a.koff[pp];
-    ok = ok && (off & 15) == 0 && off <= a.pool_bytes && a.pool_bytes - off >= wplane_bytes(codec, a.hkv, P, D);
+    off = plane ? vo : ko;
   }
   if (!ok) {
     if (h == 0 && plane == 0 && tid == 0) count_err(a.err);
@@ -209,26 +252,10 @@ __global__ void __launch_bounds__(64 * TILES) encode_kernel(EncodeArgs a) {
   const int P = a.page, hkv = a.hkv;
   const int lane = tid & 63, slot = tid >> 6;
 
-  // ---- pair checks (every thread computes the same answer)
-  const int src = a.src[i], dst = a.dst[i];
-  const int dcodec = plane ? (a.dst_codec >> 4) : (a.dst_codec & 15);
-  bool ok = (unsigned)src < (unsigned)a.num_pages && (unsigned)dst < (unsigned)a.num_pages && src != dst;
-  int scodec = 0;
-  uint64_t so = 0, dof = 0;
-  if (ok) {
-    const int cb = a.codec[src];
-    ok = w16(cb & 15) && w16(cb >> 4);
-    scodec = plane ? (cb >> 4) : (cb & 15);
-    so = plane ? a.voff[src] : a.koff[src];
-    dof = plane ? a.voff[dst] : a.koff[dst];
-    const uint64_t sb = wplane_bytes(scodec, hkv, P, D), db = wplane_bytes(dcodec, hkv, P, D);
-    ok = ok && ((so | dof) & 15) == 0 && so <= a.pool_bytes && a.pool_bytes - so >= sb &&
-         dof <= a.pool_bytes && a.pool_bytes - dof >= db;
-    // the destination plane must not overlap either source plane
-    const uint64_t sk = a.koff[src], sv = a.voff[src];
-    const uint64_t skb = wplane_bytes(cb & 15, hkv, P, D), svb = wplane_bytes(cb >> 4, hkv, P, D);
-    ok = ok && (dof + db <= sk || sk + skb <= dof) && (dof + db <= sv || sv + svb <= dof);
-  }
+  // ---- pair checks (every thread of every unit of the pair computes the same answer)
+  int dst, scodec, dcodec;
+  uint64_t so, dof;
+  const bool ok = check_pair(a, i, plane, D, dst, scodec, dcodec, so, dof);
   if (!ok) {
     if (h == 0 && plane == 0 && tid == 0) count_err(a.err);
     return;
@@ -392,31 +419,6 @@ __device__ inline float chunk_elem(const u4& x, int i) {
   const uint32_t w = x[i >> 1];
   if constexpr (BF) return __builtin_bit_cast(float, (i & 1) ? (w & 0xffff0000u) : (w << 16));
   else return (float)__builtin_bit_cast(_Float16, (uint16_t)((i & 1) ? (w >> 16) : (w & 0xffffu)));
-}
-
-// Pair checks of unit (i, plane); the same answer in every lane.
-__device__ inline bool check_pair(const EncodeArgs& a, int i, int plane, int D, int& dst, int& scodec, int& dcodec,
-                                  uint64_t& so, uint64_t& dof) {
-  const int P = a.page, hkv = a.hkv;
-  const int src = a.src[i];
-  dst = a.dst[i];
-  dcodec = plane ? (a.dst_codec >> 4) : (a.dst_codec & 15);
-  bool ok = (unsigned)src < (unsigned)a.num_pages && (unsigned)dst < (unsigned)a.num_pages && src != dst;
-  scodec = 0;
-  so = 0;
-  dof = 0;
-  if (!ok) return false;
-  const int cb = a.codec[src];
-  ok = w16(cb & 15) && w16(cb >> 4);
-  scodec = plane ? (cb >> 4) : (cb & 15);
-  so = plane ? a.voff[src] : a.koff[src];
-  dof = plane ? a.voff[dst] : a.koff[dst];
-  const uint64_t sb = wplane_bytes(scodec, hkv, P, D), db = wplane_bytes(dcodec, hkv, P, D);
-  ok = ok && ((so | dof) & 15) == 0 && so <= a.pool_bytes && a.pool_bytes - so >= sb && dof <= a.pool_bytes &&
-       a.pool_bytes - dof >= db;
-  const uint64_t sk = a.koff[src], sv = a.voff[src];
-  const uint64_t skb = wplane_bytes(cb & 15, hkv, P, D), svb = wplane_bytes(cb >> 4, hkv, P, D);
-  return ok && (dof + db <= sk || sk + skb <= dof) && (dof + db <= sv || sv + svb <= dof);
 }
 
 // Source chunks of one unit: tile t, chunk c (elements 8c .. 8c+7 of the lane's

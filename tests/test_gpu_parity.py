@@ -354,6 +354,11 @@ def test_lse_combine_matches_oracle_fold(rows, parts, dim, shift):
     acc = (rng.standard_normal((rows, parts, dim)) * l[..., None]).astype(np.float32)
     empty = rng.random((rows, parts)) < 0.2
     m[empty], l[empty], acc[empty] = -np.inf, 0, 0
+    # parts marked empty by one field only, with junk in the others: never read
+    half = rng.random((rows, parts)) < 0.1
+    m[half & ~empty], acc[half & ~empty] = -np.inf, 1e30
+    zero_l = (rng.random((rows, parts)) < 0.1) & ~empty & ~half
+    l[zero_l], m[zero_l], acc[zero_l] = 0, 80.0, -1e30
     if rows > 2:
         m[1], l[1], acc[1] = -np.inf, 0, 0                  # a row with no tokens at all
     ml = np.stack([m, l], axis=-1)
@@ -367,3 +372,61 @@ def test_lse_combine_matches_oracle_fold(rows, parts, dim, shift):
     fin = np.isfinite(ref_lse)
     assert np.array_equal(np.isfinite(lse), fin)
     assert np.max(np.abs(out - ref_out)) <= 1e-5 and np.max(np.abs(lse[fin] - ref_lse[fin]), initial=0) <= 1e-5
+
+
+# ------------------------------------------- partitions of more than 256 pages
+# The kernel stages a partition's page descriptors in LDS 256 at a time; a
+# partition that reaches more pages takes a second (third, ...) staging round.
+@pytest.mark.parametrize("kc,vc", [(FP8, FP8), (INT8, INT4), (None, None)])
+def test_partitions_over_256_pages(kc, vc):
+    """partition_tokens = 8192 at 16-token pages: 512 pages per partition, so
+    every full partition stages its descriptors in two rounds; rows end inside
+    the first round, on its boundary, inside the second and past one
+    partition. The even split (partition_tokens = 0) is checked as well."""
+    print(f"case >256 pages per partition ({kc},{vc})", flush=True)
+    cyc = [(FP16, FP16), (FP8, FP8), (INT8, INT4), (BF16, INT8)]
+    codec_of = (lambda r, lp: cyc[(r + lp) % 4]) if kc is None else (lambda r, lp: (kc, vc))
+    w = poison_tails(small([9000, 4096, 4097, 8192, 12001, 300], kc, vc, hq=8, hkv=2, dim=128, page=16,
+                           codec_of=codec_of, seed=21))
+    p = params_for(w, 8192)
+    assert pkv.num_partitions(p) == 2
+    check(w, partition_tokens=8192, what=f"{w.name} T=8192")
+    check(w, partition_tokens=0, what=f"{w.name} T=0")
+
+
+def test_library_single_partition_over_256_pages():
+    """partition_tokens = 0 with more (row, KV head) units than one round of
+    resident workgroups: the library gives each row one partition, here of
+    258-275 pages (two staging rounds), and writes out/lse directly."""
+    print("case library-chosen single partition > 256 pages", flush=True)
+    lens = np.random.default_rng(3).integers(4113, 4400, size=97)
+    w = poison_tails(small(lens, INT8, INT4, hq=32, hkv=8, dim=128, page=16, seed=23))
+    p = params_for(w, 0)
+    assert pkv.num_partitions(p) == 1 and pkv.workspace_bytes(p) == 0
+    check(w, partition_tokens=0, what="97 rows x 8 KV heads, one partition each")
+
+
+def test_sparse_selection_over_256_pages():
+    """Sparse mode with 300-400 selected pages in one partition (their
+    descriptors staged in two rounds), in shuffled order, with the last page
+    partial."""
+    print("case sparse > 256 selected pages", flush=True)
+    rng = np.random.default_rng(29)
+    lens = [16384 - 5, 16000, 9999]
+    nsel = [400, 300, 330]
+    sel = np.zeros((3, 400), dtype=np.int32)
+    for r, L in enumerate(lens):
+        # 400 distinct pages per row (all generated); the first nsel[r],
+        # the last page among them, are attended
+        last = -(-L // 16) - 1
+        rest = rng.choice(last, 399, replace=False)
+        sel[r, :nsel[r]] = rng.permutation(np.concatenate([[last], rest[:nsel[r] - 1]]))
+        sel[r, nsel[r]:] = rest[nsel[r] - 1:]
+    w = synth.build_workload("gpu_sparse400", rows=3, hq=16, hkv=2, dim=128, page=16, seq_lens=lens,
+                             codec_of=lambda r, lp: (FP8, FP8), seed=31, selection=sel,
+                             logical_pages=1024)
+    w.sel_lens = np.array(nsel, dtype=np.int32)
+    assert pkv.num_partitions(params_for(w, 8192)) == 1
+    check(w, partition_tokens=8192, what="sparse 300-400 pages, one partition")
+    check(w, partition_tokens=4096, what="sparse 300-400 pages, 256-page partitions")
+    check(w, partition_tokens=0, what="sparse 300-400 pages, even split")

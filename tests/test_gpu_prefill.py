@@ -211,3 +211,15 @@ def test_sliding_window_mixed_codecs_and_groups():
     w = poison_tails(small([700, 129], 0, 0, hq=14, hkv=2, dim=64, page=32,
                            codec_of=lambda r, lp: pairs[(r + lp) % len(pairs)]))
     check(w, 50, window=64, partition_tokens=64, k_codec=pkv.CODEC_MIXED, v_codec=pkv.CODEC_MIXED)
+
+
+@pytest.mark.parametrize("kc,vc", [(FP8, FP8), (INT8, INT4)])
+def test_partitions_over_256_pages(kc, vc):
+    """partition_tokens = 8192 at 16-token pages: 512 pages per partition,
+    staged into LDS in two rounds of 256 descriptors; rows end inside the
+    first round, on its boundary and inside the second; a key window starting
+    inside a partition's second round."""
+    print(f"case prefill >256 pages per partition ({kc},{vc})", flush=True)
+    w = poison_tails(small([9000, 4096, 12001], kc, vc, hq=8, hkv=2, dim=128, page=16, seed=13))
+    check(w, 5, partition_tokens=8192)
+    check(w, 33, 4200, -1, partition_tokens=8192)

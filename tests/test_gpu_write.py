@@ -237,6 +237,56 @@ def test_write_side_errors_are_counted_and_skipped():
     assert torch.equal(pool_t, before)
 
 
+@pytest.mark.parametrize("dst_codec", [FP8 | FP8 << 4, INT8 | INT4 << 4])
+def test_write_errors_in_one_plane_skip_the_pair(dst_codec):
+    """A pair whose K plane is fine but whose V plane is bad (or the reverse)
+    is counted once and skipped whole: neither plane, its scales nor its
+    page_codec entry is written."""
+    print(f"case one-plane write errors dst={dst_codec:#x}", flush=True)
+    hkv, P, D, n_src = 2, 16, 128, 7
+    x, pool, koff, voff, codec, scale = build_pool(8, n_src, hkv, P, D, FP16, dst_codec, extra_fp16=2)
+    src = np.arange(n_src, dtype=np.int32)
+    dst = np.arange(n_src, 2 * n_src, dtype=np.int32)
+    koff, voff = koff.copy(), voff.copy()
+    voff[dst[1]] += 8                                   # pair 1: V destination misaligned
+    koff[dst[2]] += 16 * 1024 * 1024                    # pair 2: K destination outside the pool
+    voff[dst[3]] = koff[src[3]]                         # pair 3: V destination overlaps the K source
+    koff[dst[4]] = voff[src[4]]                         # pair 4: K destination overlaps the V source
+    voff[src[5]] += 4                                   # pair 5: V source misaligned
+    voff[dst[6]] = koff[dst[6]]                         # pair 6: the two destination planes overlap
+    pool_t, koff_t, voff_t, codec_t, scale_t, src_t, dst_t = to_dev(pool, koff, voff, codec, scale, src, dst)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    p = params(len(codec), hkv, P, D, pool.size)
+    pkv.encode_pages(p, src_t, dst_t, dst_codec, pool_t, koff_t, voff_t, codec_t, scale_t, err_count=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 6
+    ref, rs, rc = oracle_encode(pool, koff, voff, codec, scale, [0], [dst[0]], dst_codec, hkv, P, D)
+    assert np.array_equal(pool_t.cpu().numpy(), ref)     # only pair 0 was written
+    assert np.array_equal(codec_t.cpu().numpy(), rc) and np.array_equal(scale_t.cpu().numpy(), rs)
+    # append: row 0 fine; row 1's page has its V plane outside the pool, row
+    # 2's its K plane misaligned: each counted once, neither plane written
+    a0, a1, a2 = 2 * n_src, 2 * n_src + 1, 0
+    koff2, voff2 = koff.copy(), voff.copy()
+    voff2[a1] = pool.size - 64
+    koff2[a2] += 2
+    pool_t, koff_t, voff_t = to_dev(pool, koff2, voff2)
+    codec2 = codec.copy()
+    codec2[a2] = FP16 | FP16 << 4
+    codec_t, = to_dev(codec2)
+    lens = np.array([3, 5, 7], np.int32)
+    bt = np.array([[a0], [a1], [a2]], np.int32)
+    k_new = (np.arange(3 * hkv * D).reshape(3, hkv, D) % 7).astype(np.float16)
+    lens_t, bt_t, k_t = to_dev(lens, bt, k_new)
+    err.zero_()
+    pa = params(len(codec), hkv, P, D, pool.size, rows=3, max_pages=1)
+    pkv.append_kv(pa, k_t, k_t, pool_t, koff_t, voff_t, codec_t, bt_t, lens_t, err_count=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 2
+    want = append_token(pool.copy(), int(koff2[a0]), int(voff2[a0]), int(codec2[a0]), hkv, P, D, 3,
+                        k_new[0].astype(np.float32), k_new[0].astype(np.float32))
+    assert np.array_equal(pool_t.cpu().numpy(), want)
+
+
 @pytest.mark.parametrize("dst", [FP8, INT8, INT4])
 def test_encode_rounding_ties(dst):
     """Values whose quotient lands exactly halfway between two codes: the

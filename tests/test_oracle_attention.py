@@ -262,6 +262,27 @@ def test_fold_all_empty():
     assert np.all(out == 0) and np.all(lse == -np.inf)
 
 
+def test_fold_ignores_parts_marked_empty():
+    """An empty part is marked by m = -inf or l = 0; its other fields are
+    never read. Extra parts (-inf, l > 0, junk acc) and (finite m, 0, junk
+    acc) -- the latter with a max far above every real one -- leave the fold
+    of the real parts unchanged, and a row of only such parts is empty."""
+    rng = np.random.default_rng(12)
+    n, D = 600, 16
+    K, V, q = rng.standard_normal((n, D)), rng.standard_normal((n, D)), 2 * rng.standard_normal((3, D))
+    acc, m, l = partials(K, V, q, 0.3, [0, 100, 350, n])
+    ref_out, ref_lse = fold(acc, m, l)
+    junk = rng.standard_normal((3, 2, D)) * 1e3
+    acc2 = np.concatenate([acc[:, :1], junk[:, :1], acc[:, 1:], junk[:, 1:]], axis=1)
+    m2 = np.concatenate([m[:, :1], np.full((3, 1), -np.inf), m[:, 1:], np.full((3, 1), 1e4)], axis=1)
+    l2 = np.concatenate([l[:, :1], np.full((3, 1), 5.0), l[:, 1:], np.zeros((3, 1))], axis=1)
+    out, lse = fold(acc2, m2, l2)
+    assert np.max(np.abs(out - ref_out)) <= 1e-12 and np.max(np.abs(lse - ref_lse)) <= 1e-12
+    out, lse = fold(junk, np.stack([np.full(3, -np.inf), np.full(3, 1e4)], 1),
+                    np.stack([np.full(3, 5.0), np.zeros(3)], 1))
+    assert np.all(out == 0) and np.all(lse == -np.inf)
+
+
 def dequant_reference(x, codec):
     """Pre-encoding float32 block [P, D] -> the value its codes denote (float64),
     computed from the codec definitions with library casts."""

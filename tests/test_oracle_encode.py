@@ -113,6 +113,28 @@ def test_int_scale_stays_inside_fp16_range(qmax):
     assert np.array_equal(codes, c_gen) and np.array_equal(s, s_gen)
 
 
+def test_int_ties_go_to_the_even_code():
+    """Quotients exactly halfway between two codes take the even one (rint,
+    ties to even), for both signs and both widths. The group's absmax is
+    qmax, so its scale is exactly 1 and each value is its own quotient; the
+    expected codes are written out by hand."""
+    # INT8 (qmax 127): value -> code
+    int8 = {0.5: 0, 1.5: 2, 2.5: 2, 3.5: 4, 64.5: 64, 65.5: 66, 125.5: 126, 126.5: 126,
+            -0.5: 0, -1.5: -2, -2.5: -2, -3.5: -4, -64.5: -64, -65.5: -66, -125.5: -126, -126.5: -126}
+    # INT4 (qmax 7)
+    int4 = {0.5: 0, 1.5: 2, 2.5: 2, 3.5: 4, 4.5: 4, 5.5: 6, 6.5: 6,
+            -0.5: 0, -1.5: -2, -2.5: -2, -3.5: -4, -4.5: -4, -5.5: -6, -6.5: -6}
+    for qmax, table in ((127, int8), (7, int4)):
+        vals = list(table)
+        x = np.zeros((1, 32 * ((len(vals) + 1 + 31) // 32)), np.float32)
+        x[0, 0] = qmax                                     # the group's absmax: scale 1
+        x[0, 1:1 + len(vals)] = vals
+        codes, s = encode_groups_int(x, qmax)
+        assert s[0, 0] == np.float16(1.0)
+        assert codes[0, 0] == qmax
+        assert [int(c) for c in codes[0, 1:1 + len(vals)]] == [table[v] for v in vals], qmax
+
+
 @pytest.mark.parametrize("qmax", [127, 7])
 def test_int_groups_equal_the_generator(qmax):
     x = np.random.default_rng(11).standard_normal((8, 64, 128)).astype(np.float16).astype(np.float32)
