@@ -78,8 +78,9 @@ extern "C" {
 #endif
 
 /* 2: partitions are ranges of 16-token tiles (partition_tokens a multiple of
- *    16; 0 splits each row evenly), PKV_CODEC_MIXED_FLOAT. */
-#define PKV_ABI_VERSION 2
+ *    16; 0 splits each row evenly), PKV_CODEC_MIXED_FLOAT.
+ * 3: pkv_decode_attention_noalloc, pkv_noalloc_scratch_bytes, PKV_ERR_SCRATCH. */
+#define PKV_ABI_VERSION 3
 
 /* Page codecs; page_codec[p] = K codec | (V codec << 4). */
 enum {
@@ -103,7 +104,9 @@ enum {
   PKV_ERR_UNSUPPORTED = -2, /* valid request with no kernel (fail closed: the
                                caller falls back; ARGUS "Why decode is slow")  */
   PKV_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required      */
-  PKV_ERR_HIP = -4          /* a HIP launch failed                             */
+  PKV_ERR_HIP = -4,         /* a HIP launch failed                             */
+  PKV_ERR_SCRATCH = -5      /* pkv_decode_attention_noalloc: the partials of the
+                               call exceed the library's built-in scratch      */
 };
 
 /* Geometry and launch description of one call. Plain values, host memory. */
@@ -185,6 +188,35 @@ int pkv_decode_attention(const pkv_params* p, const void* q, const uint8_t* page
                          const int32_t* page_sel, const int32_t* sel_lens, float* out,
                          float* lse, void* workspace, size_t workspace_bytes,
                          int32_t* err_count, void* stream);
+
+/* pkv_decode_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). The same work, kernels and results as pkv_decode_attention,
+ * bit for bit; the split-K partials go to a scratch array built into the
+ * library instead of a caller workspace, so there are no workspace
+ * arguments. The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).
+ *
+ * The scratch holds pkv_noalloc_scratch_bytes() bytes (8 MiB) per GPU, from
+ * the library's load until the process ends; a call whose
+ * pkv_workspace_bytes(p) exceeds it returns PKV_ERR_SCRATCH before touching
+ * the device (8 MiB holds, e.g., 16 query heads x 512 partitions of
+ * head_dim 128 at 4.3 MB). Every call on one GPU uses that GPU's one array:
+ * calls that overlap in time on one GPU (different streams, or different
+ * host threads without ordering) race on it and must be serialized by the
+ * caller, e.g. by issuing them on one stream. Nothing in the scratch needs to
+ * start at zero (every partial a call reads it has written). The first call
+ * on a device looks up that device's copy of the array (once per device).
+ * Arguments as for pkv_decode_attention. */
+int pkv_decode_attention_noalloc(const pkv_params* p, const void* q, const uint8_t* page_pool,
+                                 const uint64_t* page_k_off, const uint64_t* page_v_off,
+                                 const uint8_t* page_codec, const float* page_scale,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const int32_t* page_sel, const int32_t* sel_lens, float* out,
+                                 float* lse, int32_t* err_count, void* stream);
+
+/* Bytes of the built-in scratch of pkv_decode_attention_noalloc (per GPU). */
+size_t pkv_noalloc_scratch_bytes(void);
 
 /* The same work as pkv_decode_attention up to, but not including, the fold:
  * writes the unnormalised partial result of every partition instead of out and

@@ -18,12 +18,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpkv.so")
 
 FP16, BF16, FP8_E4M3, INT8_G32, INT4_G32, CODEC_MIXED, CODEC_MIXED_FLOAT = 0, 1, 2, 3, 4, -1, -2
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH = 0, -1, -2, -3, -4, -5
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "pkv_num_partitions",
            "pkv_workspace_bytes", "pkv_decode_attention", "pkv_decode_partials",
            "pkv_lse_combine", "pkv_append_kv", "pkv_encode_pages", "pkv_prefill_num_partitions",
            "pkv_prefill_workspace_bytes", "pkv_prefill_attention", "pkv_lse_fold_into", "pkv_select_capacity",
-           "pkv_select_pages")
+           "pkv_select_pages", "pkv_decode_attention_noalloc", "pkv_noalloc_scratch_bytes")
 
 
 class PkvError(RuntimeError):
@@ -65,6 +65,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_workspace_bytes.argtypes = [pp]
     lib.pkv_decode_attention.restype = ctypes.c_int
     lib.pkv_decode_attention.argtypes = [pp] + [vp] * 12 + [vp, sz, vp, vp]
+    lib.pkv_decode_attention_noalloc.restype = ctypes.c_int
+    lib.pkv_decode_attention_noalloc.argtypes = [pp] + [vp] * 12 + [vp, vp]
+    lib.pkv_noalloc_scratch_bytes.restype = sz
+    lib.pkv_noalloc_scratch_bytes.argtypes = []
     lib.pkv_decode_partials.restype = ctypes.c_int
     lib.pkv_decode_partials.argtypes = [pp] + [vp] * 12 + [vp, vp]
     lib.pkv_lse_combine.restype = ctypes.c_int
@@ -85,7 +89,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_select_pages.restype = ctypes.c_int
     lib.pkv_select_pages.argtypes = [pp] + [i32] * 6 + [vp] * 9
     lib.pkv_lse_fold_into.argtypes = [i32, i32, vp, vp, vp, vp, vp]
-    if lib.pkv_abi_version() != 2:  # tile-range partitions, the float per-page codec class
+    if lib.pkv_abi_version() != 3:  # the allocation-free decode entry point
         raise RuntimeError("libpkv ABI version mismatch")
     _lib = lib
     return lib
@@ -168,6 +172,35 @@ def decode_attention(p: Params, q, page_pool, page_k_off, page_v_off, page_codec
     if st != OK:
         raise PkvError(st, "pkv_decode_attention")
     return out, lse
+
+
+def decode_attention_noalloc(p: Params, q, page_pool, page_k_off, page_v_off, page_codec, page_scale,
+                             block_table, seq_lens, page_sel=None, sel_lens=None, *, out, lse,
+                             err_count=None, stream=None):
+    """Enqueue pkv_decode_attention_noalloc: out/lse must be given (nothing is
+    allocated here or in the library). Raises PkvError on a bad status."""
+    lib = load()
+    dev = q.device
+    st = lib.pkv_decode_attention_noalloc(
+        ctypes.byref(p), _ptr(q, torch.float16, "q", dev),
+        _ptr(page_pool, torch.uint8, "page_pool", dev),
+        _ptr(page_k_off, torch.uint64, "page_k_off", dev),
+        _ptr(page_v_off, torch.uint64, "page_v_off", dev),
+        _ptr(page_codec, torch.uint8, "page_codec", dev),
+        _ptr(page_scale, torch.float32, "page_scale", dev),
+        _ptr(block_table, torch.int32, "block_table", dev),
+        _ptr(seq_lens, torch.int32, "seq_lens", dev),
+        _ptr(page_sel, torch.int32, "page_sel", dev),
+        _ptr(sel_lens, torch.int32, "sel_lens", dev),
+        _ptr(out, torch.float32, "out", dev), _ptr(lse, torch.float32, "lse", dev),
+        _ptr(err_count, torch.int32, "err_count", dev), _stream(stream))
+    if st != OK:
+        raise PkvError(st, "pkv_decode_attention_noalloc")
+    return out, lse
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load().pkv_noalloc_scratch_bytes())
 
 
 def decode_partials(p: Params, q, page_pool, page_k_off, page_v_off, page_codec, page_scale,

@@ -103,6 +103,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP launch failed";
+    case PKV_ERR_SCRATCH: return "request exceeds the built-in scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }
@@ -213,6 +214,41 @@ int pkv_decode_attention(const pkv_params* p, const void* q, const uint8_t* page
   return launch_status(pkv::launch_combine(p->num_rows * p->num_q_heads, a.nparts, p->head_dim,
                                            a.part_acc, a.part_ml, out, lse, stream));
 }
+
+int pkv_decode_attention_noalloc(const pkv_params* p, const void* q, const uint8_t* page_pool,
+                                 const uint64_t* page_k_off, const uint64_t* page_v_off,
+                                 const uint8_t* page_codec, const float* page_scale,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const int32_t* page_sel, const int32_t* sel_lens, float* out,
+                                 float* lse, int32_t* err_count, void* stream) {
+  int st = check_params(p);
+  if (st != PKV_OK) return st;
+  if (p->num_rows == 0) return PKV_OK;
+  // the partials this call needs must fit the built-in scratch (checked
+  // before anything else touches the device)
+  if (pkv_workspace_bytes(p) > pkv::kNoAllocScratchBytes) return PKV_ERR_SCRATCH;
+  if (!out || !lse || !aligned(out, 4) || !aligned(lse, 4)) return PKV_ERR_INVALID_ARG;
+  pkv::DecodeArgs a;
+  st = prepare(p, q, page_pool, page_k_off, page_v_off, page_codec, page_scale, block_table,
+               seq_lens, page_sel, sel_lens, err_count, &a);
+  if (st != PKV_OK) return st;
+  if (a.nparts > 1) {
+    void* ws = nullptr;
+    if (pkv::noalloc_scratch(&ws) != 0) return PKV_ERR_HIP;
+    a.part_acc = static_cast<float*>(ws);
+    a.part_ml = a.part_acc + (size_t)p->num_rows * p->num_q_heads * a.nparts * p->head_dim;
+  } else {
+    a.out = out;
+    a.lse = lse;
+    a.final_out = 1;
+  }
+  st = launch_status(pkv::launch_decode(a, p->head_dim, p->k_codec, p->v_codec, stream));
+  if (st != PKV_OK || a.nparts == 1) return st;
+  return launch_status(pkv::launch_combine(p->num_rows * p->num_q_heads, a.nparts, p->head_dim,
+                                           a.part_acc, a.part_ml, out, lse, stream));
+}
+
+size_t pkv_noalloc_scratch_bytes(void) { return pkv::kNoAllocScratchBytes; }
 
 int pkv_decode_partials(const pkv_params* p, const void* q, const uint8_t* page_pool,
                         const uint64_t* page_k_off, const uint64_t* page_v_off,

@@ -152,6 +152,14 @@ int launch_encode(const EncodeArgs& a, void* stream);
 // combination, -4 if the launch failed.
 int launch_decode(const DecodeArgs& a, int head_dim, int k_codec, int v_codec, void* stream);
 
+// Size of the built-in scratch of pkv_decode_attention_noalloc (bytes).
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+
+// Device address of the current device's built-in scratch (looked up once per
+// device, then cached). Returns 0, or -4 if the device or the symbol cannot
+// be queried.
+int noalloc_scratch(void** ptr);
+
 // Launches the log-sum-exp fold over `rows` rows of `nparts` partials.
 int launch_combine(int rows, int nparts, int head_dim, const float* part_acc,
                    const float* part_ml, float* out, float* lse, void* stream);

@@ -26,6 +26,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -1009,7 +1011,32 @@ int launch_d(const DecodeArgs& a, int kc, int vc, hipStream_t s) {
   return launch_t<D, C_ANY, C_ANY>(a, s);
 }
 
+// Built-in scratch of the allocation-free decode entry point: the split-K
+// partials of one call. Every GPU the library runs on holds its own copy
+// until the process ends. Host code never passes this name to a kernel (on
+// the host it is only a stand-in for the symbol); it uses the device address
+// noalloc_scratch() returns.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+
 }  // namespace
+
+int noalloc_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return -4;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // once per device, with that device current: the address of this
+    // device's copy of the array
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return -4;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return 0;
+}
 
 int launch_decode(const DecodeArgs& a, int head_dim, int k_codec, int v_codec, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

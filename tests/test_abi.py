@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(pkv.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pkv_abi_version() == 2
+    assert lib.pkv_abi_version() == 3
 
 
 def test_one_hip_runtime_in_process():
@@ -34,7 +34,7 @@ def test_one_hip_runtime_in_process():
 
 
 def test_status_strings():
-    for st in (0, -1, -2, -3, -4, 7):
+    for st in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(pkv.status_string(st), str)
 
 
@@ -243,3 +243,19 @@ def test_select_capacity_and_host_checks():
                                   num_pages=1, max_pages_per_row=1 << 20, pool_bytes=0, max_sel_pages=8)) == -2
     assert sel(pp=pkv.make_params(rows=0, num_q_heads=1, num_kv_heads=1, head_dim=128, page_size=16,
                                   num_pages=1, max_pages_per_row=64, pool_bytes=0, max_sel_pages=8), q=0) == 0
+
+
+def test_noalloc_rejects_requests_beyond_its_scratch_on_the_host():
+    """The allocation-free entry point refuses, before touching the device,
+    a call whose partials exceed its built-in scratch (8 MiB); the 1M-token
+    workload's 4.26 MB fit."""
+    lib = pkv.load()
+    assert pkv.noalloc_scratch_bytes() == 8 << 20
+    assert pkv.workspace_bytes(base()) <= pkv.noalloc_scratch_bytes()
+    big = base(rows=4)                                     # 4 x 16 x 512 x 130 x 4 B = 17 MB
+    assert pkv.workspace_bytes(big) > pkv.noalloc_scratch_bytes()
+    fake = ctypes.c_void_p(1 << 20)                        # never dereferenced: rejected first
+    st = lib.pkv_decode_attention_noalloc(ctypes.byref(big), fake, fake, fake, fake, fake, fake, fake, fake,
+                                          None, None, fake, fake, None, None)
+    assert st == pkv.ERR_SCRATCH
+    assert "scratch" in pkv.status_string(st)
