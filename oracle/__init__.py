@@ -12,7 +12,9 @@ What it computes (sources are the three pages' own sections):
 * Codec values (``codecs``): FP16/BF16 pages; FP8 e4m3 codes times an fp32
   scale (FreeToken PR #499 update, item 1); INT8/INT4 with one scale per group
   of 32 along head_dim (GGML Q8/Q4 pages in ARGUS "v0.5" and "Direct paged
-  attention").
+  attention"); the INT2 and 1-bit tiers of ARGUS's cascade (intro), INT2 as
+  the unsigned-affine 2-bit kind of "Pluggable tiers" (offset + step * u per
+  group of 32) and 1-bit as sign times a group scale.
 * Attention (``attention``): for each query head, softmax over every attended
   token of the scaled q.k score, applied to V -- the exact result that ARGUS's
   page-at-a-time online-softmax recurrence reaches ("Why decode is slow",
@@ -37,8 +39,8 @@ What it computes (sources are the three pages' own sections):
 
 Pins live in ``tests/test_oracle_*.py``; see each function for what pins it.
 """
-from .codecs import (decode_bf16, decode_fp16, decode_fp8_e4m3, decode_int4,  # noqa: F401
-                     decode_int8)
+from .codecs import (decode_bf16, decode_bit1, decode_fp16, decode_fp8_e4m3, decode_int4,  # noqa: F401
+                     decode_int8, decode_uint2)
 from .attention import decode_attention, fold, gather_kv, partials  # noqa: F401
 from .accounting import kv_bytes_per_token  # noqa: F401
 from .encode import append_token, encode_page  # noqa: F401

@@ -8,7 +8,7 @@ plus the same 8.16 MiB of other memory.
 """
 from __future__ import annotations
 
-FP16, BF16, FP8, INT8, INT4 = 0, 1, 2, 3, 4
+FP16, BF16, FP8, INT8, INT4, INT2, BIT1 = 0, 1, 2, 3, 4, 5, 6
 
 
 def kv_bytes_per_token(codec: int, head_dim: int, page_size: int) -> float:
@@ -16,7 +16,9 @@ def kv_bytes_per_token(codec: int, head_dim: int, page_size: int) -> float:
 
     FP16/BF16: 2 bytes per value. FP8: 1 byte per value plus one fp32 scale
     per page (4 / page_size per token). INT8/INT4 with groups of 32: 1 or 1/2
-    byte per value plus one fp16 scale per 32 values.
+    byte per value plus one fp16 scale per 32 values. INT2: 1/4 byte per value
+    plus an fp16 scale and an fp16 offset per 32. BIT1: 1/8 byte per value
+    plus an fp16 scale per 32.
     """
     if codec in (FP16, BF16):
         return 2.0 * head_dim
@@ -26,4 +28,8 @@ def kv_bytes_per_token(codec: int, head_dim: int, page_size: int) -> float:
         return head_dim + 2.0 * head_dim / 32
     if codec == INT4:
         return head_dim / 2 + 2.0 * head_dim / 32
+    if codec == INT2:          # 2-bit steps, an fp16 scale and an fp16 offset per 32 values
+        return head_dim / 4 + 4.0 * head_dim / 32
+    if codec == BIT1:          # sign bits and an fp16 scale per 32 values
+        return head_dim / 8 + 2.0 * head_dim / 32
     raise ValueError(codec)

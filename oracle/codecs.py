@@ -1,9 +1,10 @@
 """Codec values from their definitions, as float64.
 
-Each decoder maps raw codes to the real number the code denotes; scales are
-applied by the caller. Pinned in tests/test_oracle_codecs.py against library
-conversions (numpy float16, torch bfloat16 and float8_e4m3fn) over every code,
-and against brute-force integer enumeration for INT8/INT4.
+Each decoder maps raw codes to the real number the code denotes; scales
+(and the INT2 offsets) are applied by the caller. Pinned in
+tests/test_oracle_codecs.py against library conversions (numpy float16, torch
+bfloat16 and float8_e4m3fn) over every code, and against brute-force integer
+enumeration for INT8/INT4/INT2/BIT1.
 """
 from __future__ import annotations
 
@@ -68,3 +69,20 @@ def decode_int4(packed: np.ndarray) -> np.ndarray:
         out[..., r] = (word >> (4 * ((r % 2) * 4 + r // 2))) & 0xF
     out = np.where(out >= 8, out - 16, out)
     return out.reshape(*lead, nb * 2).astype(np.float64)
+
+
+def decode_uint2(codes: np.ndarray) -> np.ndarray:
+    """Unsigned 2-bit code u in 0..3 (the step count of the unsigned affine
+    kind, ARGUS "Pluggable tiers": value = offset + scale * u)."""
+    u = np.asarray(codes).astype(np.int64)
+    if np.any((u < 0) | (u > 3)):
+        raise ValueError("2-bit codes are 0..3")
+    return u.astype(np.float64)
+
+
+def decode_bit1(bits: np.ndarray) -> np.ndarray:
+    """1-bit sign code: 0 -> +1, 1 -> -1 (times the group scale)."""
+    b = np.asarray(bits).astype(np.int64)
+    if np.any((b < 0) | (b > 1)):
+        raise ValueError("1-bit codes are 0 or 1")
+    return np.where(b == 1, -1.0, 1.0)

@@ -26,6 +26,18 @@ What the device path computes (the write side of the paged cache):
     code is clip(rint(fp32(x) / fp32(s)), -qmax, qmax), rint rounding half
     to even.
 
+  - INT2 (the 2-bit tier of ARGUS's cascade, taken as the unsigned-affine
+    2-bit kind of its "Pluggable tiers"): per (token, group of 32 dims) an
+    fp16 offset z = fp16(min) (clamped to +-65504) and an fp16 step
+    s = fp16(fp32(max - z) / 3), kept inside [2^-24, 65504], or 1 when
+    max - z <= 0; the code is u = clip(rint(fp32(x - z) / s), 0, 3) and
+    denotes z + s*u.
+  - BIT1 (the 1-bit tier): per (token, group of 32 dims) the sign bit
+    b = [x < 0] and one fp16 scale s = fp16(fp32(mean |x|)), the mean of
+    the 32 magnitudes taken exactly rounded in float64 (math.fsum; exact for
+    16-bit inputs) and capped at 65504; b denotes (1 - 2b)*s. An all-zero
+    group gets s = 0 and decodes to zeros.
+
   Every code is decided in fp32 (the division and the rounding), the
   precision the device path computes in.
 
@@ -36,8 +48,10 @@ from __future__ import annotations
 
 import numpy as np
 
+import math
+
 from .codecs import decode_bf16, decode_fp8_e4m3, decode_fp16
-from .layout import BITS, BF16, FP8, FP16, INT4, INT8, code_position
+from .layout import BITS, BF16, BIT1, FP8, FP16, INT2, INT4, INT8, code_bits, code_position
 
 FP8_MAX = np.float32(448.0)
 # Non-negative finite e4m3 values in code order 0x00 .. 0x7E (0x7F is NaN):
@@ -87,6 +101,53 @@ def encode_groups_int(x: np.ndarray, qmax: int) -> tuple[np.ndarray, np.ndarray]
     return np.clip(q, -qmax, qmax).astype(np.int8).reshape(p, d), s
 
 
+def encode_groups_affine2(x: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """x: float32 [P, D]; groups of 32 along D, one at a time.
+    Returns (codes uint8 [P, D] in 0..3, scales float16 [P, D/32], offsets
+    float16 [P, D/32])."""
+    x = np.asarray(x, dtype=np.float32)
+    p, d = x.shape
+    codes = np.zeros((p, d), np.uint8)
+    scales = np.zeros((p, d // 32), np.float16)
+    offs = np.zeros((p, d // 32), np.float16)
+    f16max = np.float16(65504.0)
+    for t in range(p):
+        for g in range(d // 32):
+            v = x[t, 32 * g: 32 * g + 32]
+            lo, hi = np.float32(v.min()), np.float32(v.max())
+            with np.errstate(over="ignore"):
+                z = np.float16(lo)
+            z = min(max(z, -f16max), f16max)                     # a BF16 minimum beyond fp16 saturates
+            z32 = np.float32(z)
+            span = np.float32(hi - z32)
+            if span > 0:
+                with np.errstate(over="ignore"):
+                    st = np.float16(np.float32(span / np.float32(3.0)))
+                st = min(max(st, np.float16(2.0 ** -24)), f16max)
+            else:
+                st = np.float16(1.0)
+            q = (v - z32).astype(np.float32) / np.float32(st)
+            codes[t, 32 * g: 32 * g + 32] = np.clip(np.rint(q.astype(np.float32)), 0, 3).astype(np.uint8)
+            scales[t, g], offs[t, g] = st, z
+    return codes, scales, offs
+
+
+def encode_groups_sign1(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """x: float32 [P, D]; groups of 32 along D. Returns (bits uint8 [P, D],
+    1 for x < 0; scales float16 [P, D/32] = fp16(fp32(mean |x|)), the mean
+    exactly rounded in float64, capped at 65504)."""
+    x = np.asarray(x, dtype=np.float32)
+    p, d = x.shape
+    bits = (x < 0).astype(np.uint8)
+    scales = np.zeros((p, d // 32), np.float16)
+    for t in range(p):
+        for g in range(d // 32):
+            mean = math.fsum(abs(float(a)) for a in x[t, 32 * g: 32 * g + 32]) / 32.0
+            with np.errstate(over="ignore"):
+                scales[t, g] = min(np.float16(np.float32(mean)), np.float16(65504.0))
+    return bits, scales
+
+
 def _plane_head_values(pool: np.ndarray, off: int, codec: int, hkv: int, P: int, D: int, h: int,
                        is_v: bool) -> np.ndarray:
     """float32 [P, D]: every slot of head h of a 16-bit plane (exact)."""
@@ -103,6 +164,14 @@ def _put_codes(pool: np.ndarray, off: int, codec: int, P: int, D: int, h: int, i
     """Store codes [P, D] of head h at their layout positions (in place)."""
     hb = P * D * BITS[codec] // 8
     base = int(off) + h * hb
+    if codec in (INT2, BIT1):
+        # several codes per byte: OR each into place at its bit
+        bpos, shift = code_bits(P, D, codec, is_v)
+        block = np.zeros(hb, dtype=np.uint64)
+        vals = (codes.astype(np.uint64) & np.uint64((1 << BITS[codec]) - 1)) << shift.astype(np.uint64)
+        np.bitwise_or.at(block, bpos.ravel(), vals.ravel())
+        pool[base: base + hb] = block.astype(np.uint8)
+        return
     pos, nib = code_position(P, D, codec, is_v)
     if codec in (FP16, BF16):
         c = codes.astype(np.uint16)
@@ -168,11 +237,21 @@ def encode_page(pool: np.ndarray, src_k: int, src_v: int, src_codec: int, dst_k:
                 codes, s = encode_block_fp8(x)
                 _put_codes(out, d_off, dc, P, D, h, is_v, codes)
                 scales[h, i] = s
-            elif dc in (INT8, INT4):
-                codes, s16 = encode_groups_int(x, 127 if dc == INT8 else 7)
+            elif dc in (INT8, INT4, INT2, BIT1):
+                z16 = None
+                if dc in (INT8, INT4):
+                    codes, s16 = encode_groups_int(x, 127 if dc == INT8 else 7)
+                elif dc == INT2:
+                    codes, s16, z16 = encode_groups_affine2(x)
+                else:
+                    codes, s16 = encode_groups_sign1(x)
                 _put_codes(out, d_off, dc, P, D, h, is_v, codes)
-                sc_off = int(d_off) + hkv * P * D * BITS[dc] // 8 + h * P * (D // 32) * 2
-                out[sc_off: sc_off + P * (D // 32) * 2] = np.ascontiguousarray(s16).astype("<f2").view(np.uint8).ravel()
+                gb = P * (D // 32) * 2                           # bytes of one head's scales
+                sc_off = int(d_off) + hkv * P * D * BITS[dc] // 8 + h * gb
+                out[sc_off: sc_off + gb] = np.ascontiguousarray(s16).astype("<f2").view(np.uint8).ravel()
+                if z16 is not None:                              # INT2 offsets after every head's scales
+                    z_off = int(d_off) + hkv * P * D * BITS[dc] // 8 + hkv * gb + h * gb
+                    out[z_off: z_off + gb] = np.ascontiguousarray(z16).astype("<f2").view(np.uint8).ravel()
             else:
                 raise ValueError(f"unknown codec {dc}")
     return out, scales

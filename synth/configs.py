@@ -15,7 +15,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .layout import FP8, FP16, INT4, INT8
+from .layout import BIT1, FP8, FP16, INT2, INT4, INT8
 from .workload import Workload, build_workload, streams
 
 NAMES = {
@@ -89,8 +89,10 @@ def effective_kv_bytes_formula(w: Workload) -> int:
             c = int(w.page_codec[pp])
             for codec in (c & 15, c >> 4):
                 per_tok = d * CODEC_BITS[codec] // 8
-                if codec in (INT8, INT4):
+                if codec in (INT8, INT4, BIT1):
                     per_tok += (d // 32) * 2
+                elif codec == INT2:
+                    per_tok += 2 * (d // 32) * 2          # scales and offsets
                 total += hkv * valid * per_tok
                 if codec == FP8:
                     total += hkv * 4        # one fp32 scale per (page, head, plane)

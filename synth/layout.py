@@ -17,19 +17,26 @@ lane, lane after lane, then chunk i+1), so each 16-byte-per-lane load covers
 * V: lane 16*qd + c = tokens 4*qd + j and dims 16*n + c in the order (n, j).
 
 INT4 packs 8 elements per 32-bit word: even elements in the low half-word,
-odd elements in the high half-word, each half in element order.
+odd elements in the high half-word, each half in element order. INT2 and
+BIT1 follow the same rule with 16 and 32 elements per word (a 16-bit unit
+for BIT1 at head_dim 64, whose runs are 2 bytes). INT2 and BIT1 use the
+grouped K order of INT8/INT4; INT2 planes hold fp16 offsets
+``[Hkv][P][D/32]`` after the scales.
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-from .encode import FP8_MAX, encode_bf16, encode_fp16, encode_int_g32, pack_int4
+from .encode import (FP8_MAX, encode_affine2_g32, encode_bf16, encode_fp16, encode_int_g32, encode_sign1_g32,
+                     pack_int4, pack_subbyte)
 
-FP16, BF16, FP8, INT8, INT4 = 0, 1, 2, 3, 4
-CODECS = (FP16, BF16, FP8, INT8, INT4)
-CODEC_NAMES = {FP16: "fp16", BF16: "bf16", FP8: "fp8_e4m3", INT8: "int8_g32", INT4: "int4_g32"}
-CODEC_BITS = {FP16: 16, BF16: 16, FP8: 8, INT8: 8, INT4: 4}
+FP16, BF16, FP8, INT8, INT4, INT2, BIT1 = 0, 1, 2, 3, 4, 5, 6
+CODECS = (FP16, BF16, FP8, INT8, INT4, INT2, BIT1)
+GROUPED = (INT8, INT4, INT2, BIT1)
+CODEC_NAMES = {FP16: "fp16", BF16: "bf16", FP8: "fp8_e4m3", INT8: "int8_g32", INT4: "int4_g32",
+               INT2: "int2_affine_g32", BIT1: "bit1_g32"}
+CODEC_BITS = {FP16: 16, BF16: 16, FP8: 8, INT8: 8, INT4: 4, INT2: 2, BIT1: 1}
 PLANE_ALIGN = 256
 
 
@@ -38,7 +45,9 @@ def codes_bytes(codec: int, hkv: int, page: int, dim: int) -> int:
 
 
 def scale_bytes(codec: int, hkv: int, page: int, dim: int) -> int:
-    return hkv * page * (dim // 32) * 2 if codec in (INT8, INT4) else 0
+    """Group scales (and, for INT2, the group offsets after them)."""
+    per = hkv * page * (dim // 32) * 2
+    return 2 * per if codec == INT2 else (per if codec in GROUPED else 0)
 
 
 def plane_bytes(codec: int, hkv: int, page: int, dim: int) -> int:
@@ -91,12 +100,14 @@ def encode_plane(x: np.ndarray, codec: int, v_order: bool) -> tuple[np.ndarray, 
     """
     n, hkv, p, d = x.shape
     ones = np.ones((n, hkv), dtype=np.float32)
-    grouped = codec in (INT8, INT4)
+    grouped = codec in GROUPED
 
     def place(codes_elems: np.ndarray) -> np.ndarray:
         runs = lane_runs(codes_elems, v_order, grouped)              # [n, Hkv, T, 64, D/4]
         if codec == INT4:
             rb = pack_int4(runs)                                      # [..., D/8] bytes
+        elif codec in (INT2, BIT1):
+            rb = pack_subbyte(runs, CODEC_BITS[codec])                # [..., D*bits/32] bytes
         else:
             rb = np.ascontiguousarray(runs).view(np.uint8)            # little-endian bytes
         return interleave_chunks(rb).reshape(n, -1)
@@ -115,4 +126,13 @@ def encode_plane(x: np.ndarray, codec: int, v_order: bool) -> tuple[np.ndarray, 
         body = place(codes)
         sc = np.ascontiguousarray(scales).astype("<f2").view(np.uint8)
         return np.concatenate([body, sc.reshape(n, -1)], axis=1), ones
+    if codec == INT2:
+        codes, scales, offs = encode_affine2_g32(x)
+        sc = np.ascontiguousarray(scales).astype("<f2").view(np.uint8).reshape(n, -1)
+        zo = np.ascontiguousarray(offs).astype("<f2").view(np.uint8).reshape(n, -1)
+        return np.concatenate([place(codes), sc, zo], axis=1), ones
+    if codec == BIT1:
+        codes, scales = encode_sign1_g32(x)
+        sc = np.ascontiguousarray(scales).astype("<f2").view(np.uint8).reshape(n, -1)
+        return np.concatenate([place(codes), sc], axis=1), ones
     raise ValueError(f"unknown codec {codec}")

@@ -50,3 +50,16 @@ def test_generator_effective_bytes_agree(cid):
     # FP8 scales are charged per page: a page counts 4 bytes per head per plane
     # whatever its valid tokens; all these workloads' FP8 pages are full.
     assert synth.effective_kv_bytes_formula(w) == pytest.approx(total, rel=0, abs=1e-6)
+
+
+def test_subbyte_group_costs_match_their_planes():
+    """INT2: 2 bits per value + an fp16 step and an fp16 offset per 32
+    values (3 bits per value); BIT1: 1 bit + an fp16 scale per 32 (1.5 bits
+    per value); each equals the generator's plane size per token."""
+    from oracle.accounting import kv_bytes_per_token
+    from synth.layout import BIT1, INT2, plane_bytes
+    for D in (64, 128):
+        assert kv_bytes_per_token(INT2, D, 16) == D * 3 / 8
+        assert kv_bytes_per_token(BIT1, D, 16) == D * 1.5 / 8
+        for codec in (INT2, BIT1):
+            assert kv_bytes_per_token(codec, D, 16) * 4 * 16 == plane_bytes(codec, 4, 16, D)

@@ -19,9 +19,10 @@ from hypothesis import given, settings, strategies as st
 import synth
 from oracle import decode_attention, fold, gather_kv, partials
 from oracle.layout import plane_values
-from synth.layout import BF16, FP8, FP16, INT4, INT8
+from synth.layout import BF16, BIT1, FP8, FP16, INT2, INT4, INT8
 
-ALL_PAIRS = [(FP16, FP16), (BF16, BF16), (FP8, FP8), (INT8, INT4), (INT4, INT8), (FP8, FP16)]
+ALL_PAIRS = [(FP16, FP16), (BF16, BF16), (FP8, FP8), (INT8, INT4), (INT4, INT8), (FP8, FP16),
+             (INT2, INT2), (BIT1, BIT1), (INT2, BIT1), (INT8, INT2)]
 
 
 def small(seq_lens, kc=FP16, vc=FP16, hq=4, hkv=2, dim=32, page=16, seed=5, **kw):
@@ -295,6 +296,14 @@ def dequant_reference(x, codec):
         s = np.float32(np.abs(x).max() / np.float32(448.0))
         c = torch.from_numpy(np.clip(x / s, -448, 448).astype(np.float32)).to(torch.float8_e4m3fn)
         return c.to(torch.float64).numpy() * float(s)
+    if codec == INT2:
+        from synth.encode import encode_affine2_g32
+        u, sc, z = encode_affine2_g32(x)
+        return z.astype(np.float64).repeat(32, axis=-1) + u * sc.astype(np.float64).repeat(32, axis=-1)
+    if codec == BIT1:
+        from synth.encode import encode_sign1_g32
+        b, sc = encode_sign1_g32(x)
+        return np.where(b == 1, -1.0, 1.0) * sc.astype(np.float64).repeat(32, axis=-1)
     cq, sc = encode_int_g32(x, 127 if codec == INT8 else 7)
     return cq.astype(np.float64) * sc.astype(np.float64).repeat(32, axis=-1)
 

@@ -6,9 +6,11 @@ by code, with an independent library conversion or with integer enumeration.
 import numpy as np
 import torch
 
-from oracle.codecs import (decode_bf16, decode_fp8_e4m3, decode_fp16, decode_int4,
-                           decode_int8)
-from synth.encode import encode_int_g32, pack_int4
+import pytest
+
+from oracle.codecs import (decode_bf16, decode_bit1, decode_fp8_e4m3, decode_fp16, decode_int4,
+                           decode_int8, decode_uint2)
+from synth.encode import encode_int_g32, pack_int4, pack_subbyte
 
 
 def _same(a, b):
@@ -74,3 +76,38 @@ def test_int_group_roundtrip_error_bound():
         amax = np.abs(x.reshape(5, 2, 32)).max(-1).repeat(32, -1)
         bound = s / 2 + np.abs(amax - qmax * s) + 1e-6
         assert np.all(np.abs(vals - x) <= bound)
+
+
+def test_uint2_and_bit1_every_code():
+    assert list(decode_uint2(np.arange(4))) == [0.0, 1.0, 2.0, 3.0]
+    assert list(decode_bit1(np.array([0, 1]))) == [1.0, -1.0]
+    with pytest.raises(ValueError):
+        decode_uint2(np.array([4]))
+    with pytest.raises(ValueError):
+        decode_bit1(np.array([2]))
+
+
+def test_subbyte_packing_hand_worked():
+    """The generator's packing of 2- and 1-bit codes, against words worked
+    out by hand from the rule: code r of a unit of m codes at slot
+    (r % 2) * (m / 2) + r // 2."""
+    def word(codes, bits):
+        b = pack_subbyte(np.asarray(codes, np.uint8)[None], bits)[0]
+        return int.from_bytes(b.tobytes(), "little")
+    z16 = [0] * 16
+    # INT2, 16 codes per 32-bit word: code 0 -> bits 0-1, code 1 -> slot 8
+    # (bits 16-17), code 15 -> slot 15 (bits 30-31), code 6 -> slot 3 (bits 6-7)
+    assert word([1] + z16[1:], 2) == 0x00000001
+    assert word([0, 3] + z16[2:], 2) == 0x00030000
+    assert word(z16[:15] + [2], 2) == 0x80000000
+    assert word(z16[:6] + [3] + z16[7:], 2) == 0x000000C0
+    # two words in a 32-code run: code 16 starts the second word
+    assert word([0] * 16 + [1] + [0] * 15, 2) == 1 << 32
+    # BIT1, 32 codes per word: code 1 -> bit 16, code 30 -> bit 15, code 31 -> bit 31
+    z32 = [0] * 32
+    assert word([0, 1] + z32[2:], 1) == 0x00010000
+    assert word(z32[:30] + [1, 0], 1) == 0x00008000
+    assert word(z32[:31] + [1], 1) == 0x80000000
+    # BIT1 in a 2-byte run (head_dim 64): 16-bit unit, code 1 -> bit 8, code 15 -> bit 15
+    assert word([0, 1] + z16[2:], 1) == 0x0100
+    assert word(z16[:15] + [1], 1) == 0x8000

@@ -11,9 +11,9 @@ import pytest
 import torch
 
 from oracle import codecs
-from oracle.encode import (append_token, encode_block_fp8, encode_groups_int, encode_page,
-                           fp32_to_e4m3)
-from oracle.layout import BF16, FP8, FP16, INT4, INT8, plane_values
+from oracle.encode import (append_token, encode_block_fp8, encode_groups_affine2, encode_groups_int,
+                           encode_groups_sign1, encode_page, fp32_to_e4m3)
+from oracle.layout import BF16, BIT1, FP8, FP16, INT2, INT4, INT8, plane_values
 from synth import encode as senc
 from synth import layout as slay
 
@@ -144,6 +144,64 @@ def test_int_groups_equal_the_generator(qmax):
         assert np.array_equal(c, c_gen[i]) and np.array_equal(s, s_gen[i])
 
 
+def test_affine2_closed_forms():
+    """INT2 (unsigned affine, 2 bits): hand-worked groups."""
+    x = np.zeros((3, 32), np.float32)
+    # group 0: min -1.5, max 1.5 -> z = -1.5, s = 1; the grid points and the
+    # three midpoints (quotients 0.5, 1.5, 2.5 go to the even code)
+    x[0, :7] = [-1.5, -0.5, 0.5, 1.5, -1.0, 0.0, 1.0]
+    x[0, 7:] = 0.5
+    # group 1: all equal -> s = 1, every code 0, decodes to the value exactly
+    x[1, :] = 2.5
+    # group 2: min 0.25 is exact in fp16, max 6.25 -> s = 2
+    x[2, :] = 0.25
+    x[2, 3], x[2, 4] = 6.25, 3.25
+    codes, s, z = encode_groups_affine2(x.reshape(1, 96))
+    assert list(s[0]) == [1.0, 1.0, 2.0] and list(z[0]) == [-1.5, 2.5, 0.25]
+    assert list(codes[0, :7]) == [0, 1, 2, 3, 0, 2, 2]
+    assert np.all(codes[0, 32:64] == 0)
+    assert codes[0, 64 + 3] == 3 and codes[0, 64 + 4] == 2 and codes[0, 64] == 0
+    # round trip within half a step on random groups
+    rng = np.random.default_rng(2)
+    y = (rng.standard_normal((16, 128)) * rng.uniform(0.1, 5, (16, 1))).astype(np.float16).astype(np.float32)
+    c, s, z = encode_groups_affine2(y)
+    dec = z.astype(np.float64).repeat(32, 1) + c * s.astype(np.float64).repeat(32, 1)
+    step = s.astype(np.float64).repeat(32, 1)
+    assert np.all(np.abs(dec - y) <= 0.5 * step * (1 + 1e-3) + 1e-3 * np.abs(y))
+    assert c.min() == 0 and c.max() == 3
+
+
+def test_sign1_closed_forms():
+    """BIT1: the sign bit (x < 0) and the exact mean magnitude."""
+    x = np.zeros((1, 96), np.float32)
+    x[0, :32] = np.where(np.arange(32) % 3 == 0, -0.75, 0.75)       # |x| = 0.75 -> s = 0.75
+    x[0, 32:64] = 0.0                                                 # all zero -> s = 0
+    x[0, 64:96] = np.arange(1, 33, dtype=np.float32) / 16            # mean (32*33/2)/16/32 = 1.03125
+    bits, s = encode_groups_sign1(x)
+    assert list(s[0]) == [0.75, 0.0, 1.03125]
+    assert np.array_equal(bits[0, :32], (np.arange(32) % 3 == 0).astype(np.uint8))
+    assert np.all(bits[0, 32:] == 0)
+    neg0 = np.full((1, 32), -0.0, np.float32)                        # -0 is not below zero
+    assert np.all(encode_groups_sign1(neg0)[0] == 0)
+
+
+@pytest.mark.parametrize("src", [np.float16, "bf16"])
+def test_affine2_and_sign1_equal_the_generator(src):
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal((4, 32, 128)) * rng.uniform(0.01, 30, (4, 32, 1))).astype(np.float32)
+    if src == "bf16":
+        x = torch.from_numpy(x * 1e3).to(torch.bfloat16).to(torch.float32).numpy()
+    else:
+        x = x.astype(np.float16).astype(np.float32)
+    gc, gs, gz = senc.encode_affine2_g32(x)
+    bc, bs = senc.encode_sign1_g32(x)
+    for i in range(4):
+        c, s, z = encode_groups_affine2(x[i])
+        assert np.array_equal(c, gc[i]) and np.array_equal(s, gs[i]) and np.array_equal(z, gz[i])
+        b, s1 = encode_groups_sign1(x[i])
+        assert np.array_equal(b, bc[i]) and np.array_equal(s1, bs[i])
+
+
 def fp16_page(rng, hkv, P, D, codec=FP16):
     """Random fp16 values [2 planes][Hkv][P][D] and their 16-bit plane bytes."""
     x = (rng.standard_normal((2, 1, hkv, P, D)) * 2).astype(np.float16).astype(np.float32)
@@ -152,7 +210,7 @@ def fp16_page(rng, hkv, P, D, codec=FP16):
     return x[:, 0], k[0], v[0]
 
 
-@pytest.mark.parametrize("dst", [FP8, INT8, INT4, BF16])
+@pytest.mark.parametrize("dst", [FP8, INT8, INT4, BF16, INT2, BIT1])
 @pytest.mark.parametrize("D", [64, 128])
 def test_encode_page_equals_the_generator_bytes(dst, D):
     rng = np.random.default_rng(D + dst)
@@ -176,7 +234,10 @@ def test_encode_page_equals_the_generator_bytes(dst, D):
     for h in range(hkv):
         for i, (off, is_v) in enumerate(((2 * pk, False), (2 * pk + dk, True))):
             val = plane_values(out, off, dst, hkv, P, D, h, scales[h, i], is_v, P)
-            tol = {FP8: 0.07, INT8: 0.01, INT4: 0.2, BF16: 0.01}[dst]
+            if dst == BIT1:       # sign times the group's mean magnitude: the signs survive
+                assert np.all((val < 0) == (x[i][h] < 0))
+                continue
+            tol = {FP8: 0.07, INT8: 0.01, INT4: 0.2, BF16: 0.01, INT2: 0.5}[dst]
             assert np.max(np.abs(val - x[i][h])) <= tol * np.max(np.abs(x[i][h]))
 
 
