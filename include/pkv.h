@@ -31,24 +31,35 @@
  *   PKV_FP8_E4M3  OCP E4M3FN codes times page_scale[page][h][K|V] (fp32).
  *   PKV_INT8_G32  int8 codes times one fp16 scale per (token, 32 dims).
  *   PKV_INT4_G32  int4 codes times one fp16 scale per (token, 32 dims).
+ *   PKV_INT2_G32  the INT2 tier of ARGUS's cascade (page intro), as the
+ *                 unsigned-affine 2-bit kind of its "Pluggable tiers": codes
+ *                 u in 0..3 denoting z + s*u, with an fp16 offset z and an
+ *                 fp16 step s per (token, 32 dims).
+ *   PKV_BIT1_G32  the 1-bit tier: sign codes (bit 1 = negative) times one
+ *                 fp16 scale per (token, 32 dims).
+ * The chunked prefill (pkv_prefill_attention) reads the first five only.
  *
  * In-page layout (this library's definition). page_k_off[p] / page_v_off[p]
  * are byte offsets from page_pool to the K and V planes of physical page p;
  * both must be multiples of 16. A plane holds the codes of every KV head,
- * head after head (page_size * head_dim codes each), then, for the INT codecs
- * only, fp16 scales[Hkv][page_size][head_dim/32]. One head's codes are
- * page_size/16 tiles of 16 tokens, tile after tile; a tile (16*D*bits/8
- * bytes) is the register image of the 64 lanes of the wave that consumes it.
- * Lane L (0..63) owns a run of D/4 consecutive elements, R = D*bits/32 bytes:
- * with R >= 16 the runs are interleaved in 16-byte chunks (chunk c of lane L
- * at byte c*1024 + 16*L of the tile), else run L sits at byte R*L. Element e
- * of lane L's run holds, with tt the token within the tile:
+ * head after head (page_size * head_dim codes each), then, for the group-scale
+ * codecs (INT8, INT4, INT2, BIT1), fp16 scales[Hkv][page_size][head_dim/32],
+ * and for INT2 then fp16 offsets[Hkv][page_size][head_dim/32]. One head's
+ * codes are page_size/16 tiles of 16 tokens, tile after tile; a tile
+ * (16*D*bits/8 bytes) is the register image of the 64 lanes of the wave that
+ * consumes it. Lane L (0..63) owns a run of D/4 consecutive elements,
+ * R = D*bits/32 bytes: with R >= 16 the runs are interleaved in 16-byte chunks
+ * (chunk c of lane L at byte c*1024 + 16*L of the tile), else run L sits at
+ * byte R*L. Element e of lane L's run holds, with tt the token within the
+ * tile:
  *   K, FP16/BF16/FP8:  tt = L%16, dim = (D/4)*(L/16) + e;
- *   K, INT8/INT4:      tt = L%16, dim = 32*(e/8) + 8*(L/16) + e%8;
+ *   K, group scales:   tt = L%16, dim = 32*(e/8) + 8*(L/16) + e%8;
  *   V, every codec:    tt = 4*(L/16) + e%4, dim = 16*(e/4) + L%16.
- * Elements are little-endian; INT4 packs eight elements per 32-bit word,
- * element r of the word in nibble slot (r%2)*4 + r/2 (even elements in the
- * low half-word).
+ * Elements are little-endian. Codes of fewer than 8 bits fill the run in
+ * little-endian units of min(32, run bits) bits holding m codes each; code r
+ * of a unit sits at slot (r%2)*(m/2) + r/2 (even codes in the low half):
+ * INT4 eight per 32-bit word (nibble slot (r%2)*4 + r/2), INT2 sixteen, BIT1
+ * thirty-two, or sixteen in a 16-bit unit at head_dim 64.
  *
  * Threading and ownership. The caller owns every buffer (device memory
  * unless stated otherwise). Calls enqueue work on `stream` (a hipStream_t;
@@ -89,6 +100,8 @@ enum {
   PKV_FP8_E4M3 = 2,
   PKV_INT8_G32 = 3,
   PKV_INT4_G32 = 4,
+  PKV_INT2_G32 = 5,          /* unsigned affine 2-bit: offset + step * u per (token, 32 dims) */
+  PKV_BIT1_G32 = 6,          /* 1-bit: sign times a scale per (token, 32 dims) */
   PKV_CODEC_MIXED = -1,      /* pkv_params.k_codec / v_codec: any codec per page and plane */
   PKV_CODEC_MIXED_FLOAT = -2 /* both k_codec and v_codec: each page holds K and V in one of
                                 FP16, BF16, FP8 (the same for both planes), chosen per page.
@@ -299,8 +312,8 @@ int pkv_append_kv(const pkv_params* p, const void* k_new, const void* v_new, uin
  *                 twice, or as a source of another pair, in one call (not
  *                 checked).
  *   dst_codec     K codec in the low nibble, V codec in the high nibble:
- *                 FP16, BF16, FP8 e4m3, INT8 or INT4. Encoding, decided in
- *                 fp32:
+ *                 FP16, BF16, FP8 e4m3, INT8, INT4, INT2 or BIT1. Encoding,
+ *                 decided in fp32:
  *                   FP8: s = fp32(absmax / 448) per (page, KV head, plane),
  *                        1 if the block is all zero; code = e4m3 nearest to
  *                        fp32(x / s), ties to even.
@@ -308,6 +321,13 @@ int pkv_append_kv(const pkv_params* p, const void* k_new, const void* v_new, uin
  *                        dims), qmax 127 / 7, kept inside fp16's finite range
  *                        [2^-24, 65504], 1 if the group is all zero;
  *                        code = clip(rint(fp32(x) / fp32(s)), -qmax, qmax).
+ *                   INT2: per (token, 32 dims) z = fp16(min) (saturated to
+ *                        +-65504), s = fp16(fp32(max - z) / 3) kept inside
+ *                        [2^-24, 65504], 1 when max - z <= 0;
+ *                        u = clip(rint(fp32(x - z) / s), 0, 3).
+ *                   BIT1: per (token, 32 dims) s = fp16(fp32(sum |x| / 32)),
+ *                        the sum taken in float64 (exact for 16-bit sources),
+ *                        capped at 65504; bit = x < 0.
  *                   BF16/FP16: the value, rounded to nearest even.
  *   page_codec    page_codec[dst] is set to dst_codec.
  *   page_scale    [num_pages][Hkv][2]; page_scale[dst][h] is set to the FP8
@@ -355,10 +375,12 @@ int pkv_encode_pages(const pkv_params* p, int32_t n, const int32_t* src_pages, c
  * FP8 page scales must be finite and nonzero here (the encoder's always
  * are): the kernel keeps its V sums in units of the current page's V scale.
  *
- * Dense mode only: max_sel_pages must be 0. Codecs, the page tables, the
- * device-visible error counting and the threading rules are those of
- * pkv_decode_attention (each bad page is counted once per partition and
- * row).
+ * Dense mode only: max_sel_pages must be 0. Codecs (FP16, BF16, FP8, INT8
+ * and INT4: a declared INT2 or BIT1 codec returns PKV_ERR_UNSUPPORTED, and
+ * such a page met under PKV_CODEC_MIXED is a device-visible error), the page
+ * tables, the device-visible error counting and the threading rules are
+ * those of pkv_decode_attention (each bad page is counted once per partition
+ * and row).
  */
 
 /* Partitions of the key range for this call (>= 1), or a negative status. */

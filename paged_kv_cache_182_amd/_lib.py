@@ -17,7 +17,7 @@ import torch  # loads the HIP runtime the library must share (import before libp
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpkv.so")
 
-FP16, BF16, FP8_E4M3, INT8_G32, INT4_G32, CODEC_MIXED, CODEC_MIXED_FLOAT = 0, 1, 2, 3, 4, -1, -2
+FP16, BF16, FP8_E4M3, INT8_G32, INT4_G32, INT2_G32, BIT1_G32, CODEC_MIXED, CODEC_MIXED_FLOAT = 0, 1, 2, 3, 4, 5, 6, -1, -2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH = 0, -1, -2, -3, -4, -5
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "pkv_num_partitions",
            "pkv_workspace_bytes", "pkv_decode_attention", "pkv_decode_partials",

@@ -43,7 +43,7 @@ int compute_units() {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 bool valid_codec(int32_t c) {
-  return c == PKV_CODEC_MIXED || c == PKV_CODEC_MIXED_FLOAT || (c >= PKV_FP16 && c <= PKV_INT4_G32);
+  return c == PKV_CODEC_MIXED || c == PKV_CODEC_MIXED_FLOAT || (c >= PKV_FP16 && c <= PKV_BIT1_G32);
 }
 
 // Checks the plain-value part of the params. Returns PKV_OK or an error.
@@ -342,7 +342,7 @@ int pkv_encode_pages(const pkv_params* p, int32_t n, const int32_t* src_pages, c
   const int st = check_write_params(p);
   if (st != PKV_OK) return st;
   const int kc = dst_codec & 15, vc = (dst_codec >> 4) & 15;
-  if (n < 0 || dst_codec < 0 || dst_codec > 0xFF || kc > PKV_INT4_G32 || vc > PKV_INT4_G32)
+  if (n < 0 || dst_codec < 0 || dst_codec > 0xFF || kc > PKV_BIT1_G32 || vc > PKV_BIT1_G32)
     return PKV_ERR_INVALID_ARG;
   if (n == 0) return PKV_OK;
   if (n > 0x7fffffff / 2) return PKV_ERR_UNSUPPORTED;
@@ -393,6 +393,8 @@ int plan_prefill(const pkv_params* p, int32_t q_tokens, int32_t kv_begin, int32_
   int st = check_params(p);
   if (st != PKV_OK) return st;
   if (p->max_sel_pages != 0) return PKV_ERR_INVALID_ARG;  // the prefill attends the dense cache
+  // the prefill kernel decodes FP16, BF16, FP8, INT8 and INT4 pages only
+  if (p->k_codec > PKV_INT4_G32 || p->v_codec > PKV_INT4_G32) return PKV_ERR_UNSUPPORTED;
   if (p->partition_tokens % p->page_size != 0) return PKV_ERR_INVALID_ARG;  // prefill partitions are whole pages
   if (q_tokens < 0 || kv_begin < 0 || (kv_end >= 0 && kv_end < kv_begin)) return PKV_ERR_INVALID_ARG;
   const int64_t cap = (int64_t)p->max_pages_per_row * p->page_size;

@@ -17,10 +17,11 @@ namespace pkv {
 // Sizes the library-chosen partition count
 // (workgroups resident at once = compute units x this).
 // Whether a declared (K, V) codec pair has a decode kernel of its own: the
-// pairs launch_decode instantiates (FP16, BF16, FP8, INT8 and INT4 with
-// themselves, INT8-K with INT4-V); every other pair runs the per-page kernel.
+// pairs launch_decode instantiates (FP16, BF16, FP8, INT8, INT4, INT2 and
+// BIT1 with themselves, INT8-K with INT4-V); every other pair runs the
+// per-page kernel.
 constexpr bool decode_pair_kernel(int k_codec, int v_codec) {
-  return (k_codec == v_codec && k_codec >= 0 && k_codec <= 4) || (k_codec == 3 && v_codec == 4);
+  return (k_codec == v_codec && k_codec >= 0 && k_codec <= 6) || (k_codec == 3 && v_codec == 4);
 }
 constexpr int decode_waves_per_simd(int head_dim, int k_codec, int v_codec) {
   if (k_codec == -2 && v_codec == -2) return head_dim == 64 ? 4 : 2;  // float pages only

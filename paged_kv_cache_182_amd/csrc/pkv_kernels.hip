@@ -19,9 +19,12 @@
 //    which is exactly the A operand layout) and B = V (4 tokens of one dim,
 //    which the V plane layout stores contiguously per lane); lane l
 //    accumulates out[head 4*kq + j][dim 16*n + col].
-// Every code converts to fp16 exactly (FP8 e4m3, int8, int4 and -- within
-// fp16 range -- bf16), so each product is exact and accumulates in fp32;
-// scales are applied in fp32 to the scores (K) or folded into P (V).
+// Every code converts to fp16 exactly (FP8 e4m3, int8, int4, the unsigned
+// 2-bit steps, the 1-bit signs and -- within fp16 range -- bf16), so each
+// product is exact and accumulates in fp32; scales are applied in fp32 to the
+// scores (K) or folded into P (V). The 2-bit codec's group offsets add one
+// term per group to the scores (offset times the group's query sum) and one
+// MFMA with the offsets as B operand to P.V.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -40,7 +43,8 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-enum : int { C_FP16 = 0, C_BF16 = 1, C_FP8 = 2, C_INT8 = 3, C_INT4 = 4, C_FLT = 14, C_ANY = 15 };
+enum : int { C_FP16 = 0, C_BF16 = 1, C_FP8 = 2, C_INT8 = 3, C_INT4 = 4, C_INT2 = 5, C_BIT1 = 6, C_FLT = 14, C_ANY = 15 };
+constexpr int C_LAST = C_BIT1;  // highest codec id a page may hold
 // C_ANY: any codec per page and plane. C_FLT: per page one of FP16, BF16, FP8,
 // the same for K and V (no group scales: a smaller kernel than C_ANY's).
 __host__ __device__ constexpr bool per_page(int c) { return c == C_ANY || c == C_FLT; }
@@ -55,13 +59,19 @@ constexpr int MAX_DESC = 256;  // page descriptors staged in LDS at a time
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr float LN2 = 0.693147180559945309f;
 
-__host__ __device__ constexpr int bits_of(int c) { return c <= C_BF16 ? 16 : (c == C_INT4 ? 4 : 8); }
-__host__ __device__ constexpr bool is_int(int c) { return c == C_INT8 || c == C_INT4; }
+__host__ __device__ constexpr int bits_of(int c) {
+  return c <= C_BF16 ? 16 : (c == C_INT4 ? 4 : (c == C_INT2 ? 2 : (c == C_BIT1 ? 1 : 8)));
+}
+// codecs with one fp16 scale per (token, 32 dims): INT8, INT4, INT2, BIT1
+__host__ __device__ constexpr bool is_int(int c) { return c == C_INT8 || c == C_INT4 || c == C_INT2 || c == C_BIT1; }
+// INT2 (unsigned affine) also holds one fp16 offset per (token, 32 dims)
+__host__ __device__ constexpr bool has_zero(int c) { return c == C_INT2; }
 
 // Bytes of one plane (codes of every head, then INT group scales).
 __host__ __device__ inline uint64_t plane_bytes(int c, int hkv, int page, int d) {
   const uint64_t codes = (uint64_t)hkv * page * d * bits_of(c) / 8;
-  return codes + (is_int(c) ? (uint64_t)hkv * page * (d / 32) * 2 : 0);
+  const uint64_t groups = (uint64_t)hkv * page * (d / 32) * 2;
+  return codes + (is_int(c) ? groups : 0) + (has_zero(c) ? groups : 0);
 }
 
 // Raw buffer loads through a per-plane resource: the base and size live in
@@ -83,8 +93,9 @@ template <int CPOL = 0>
 __device__ inline u2 bload8(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, CPOL));
 }
+template <int CPOL = 0>
 __device__ inline uint32_t bload4(rsrc_t r, uint32_t off) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, CPOL);
 }
 constexpr uint32_t OFF_NONE = 0xFFFFFF00u;  // past any plane: reads zero, no traffic
 constexpr int VMCNT0 = 0x0F70;  // s_waitcnt vmcnt(0), expcnt and lgkmcnt left free (gfx9 encoding)
@@ -104,17 +115,21 @@ template <int D, int KC, int VC>
 struct Tile {
   static constexpr int KB = per_page(KC) ? 16 : bits_of(KC);
   static constexpr int VB = per_page(VC) ? 16 : bits_of(VC);
-  static constexpr int KW = D * KB / 128;  // 32-bit words of K codes per lane
-  static constexpr int VW = D * VB / 128;
+  static constexpr int KW = D * KB < 128 ? 1 : D * KB / 128;  // 32-bit words of K codes per lane
+  static constexpr int VW = D * VB < 128 ? 1 : D * VB / 128;
   static constexpr int SW = D / 16;        // words of 4 tokens x D/32 fp16 scales
   static constexpr bool KS = KC == C_ANY || is_int(KC);
   static constexpr bool VS = VC == C_ANY || is_int(VC);
   static constexpr bool GS = KS || VS;     // some plane may carry group scales
+  static constexpr bool KZ = KC == C_ANY || has_zero(KC);  // and group offsets
+  static constexpr bool VZ = VC == C_ANY || has_zero(VC);
   uint32_t k[KW];
   uint32_t v[VW];
   // Group scales of the tile, one word per lane: the 16 tokens x D/32 fp16
   // K scales in lanes 0 .. D/4-1 (sk), the V scales in lanes 32 .. 32+D/4-1
-  // (sv); zero elsewhere. Spread to the lanes that use them through LDS.
+  // (sv); the INT2 offsets in the other half of each: K offsets in lanes
+  // 32 .. 32+D/4-1 of sk, V offsets in lanes 0 .. D/4-1 of sv; zero
+  // elsewhere. Spread to the lanes that use them through LDS.
   uint32_t sk[1];
   uint32_t sv[1];
 };
@@ -141,6 +156,14 @@ __host__ __device__ constexpr int waves_per_eu() {
 #else
   return decode_waves_per_simd(D, KC == C_ANY ? -1 : (KC == C_FLT ? -2 : KC), VC == C_ANY ? -1 : (VC == C_FLT ? -2 : VC));
 #endif
+}
+
+// Upper bound of the occupancy range: the same for the per-page kernels
+// (their registers are at the edge: aiming higher spills them), open for the
+// fixed pairs.
+template <int D, int KC, int VC>
+__host__ __device__ constexpr int max_waves_per_eu() {
+  return per_page(KC) ? waves_per_eu<D, KC, VC>() : 8;
 }
 
 struct TileInfo {
@@ -173,6 +196,12 @@ __device__ inline float unif(float x) {
 }
 
 // ---------------------------------------------------------------- loads
+// A 1-bit run of 16 codes (head_dim 64) is one 16-bit unit: even codes in
+// bits 0..7, odd codes in bits 8..15. Moving the odd byte to bits 16..23 gives
+// the layout of a 32-code word (even codes low, odd codes from bit 16), so
+// both head dims decode alike.
+__device__ inline uint32_t spread16(uint32_t u) { return (u & 0xffu) | ((u & 0xff00u) << 8); }
+
 // The lane's run of one 16-token tile: R = D*bits/32 bytes. Tiles are stored
 // as the image of the 64 lanes' registers, 16-byte chunks interleaved over the
 // lanes (chunk i of lane L at i*1024 + 16*L), so every load instruction of a
@@ -191,10 +220,15 @@ __device__ inline void load_run(uint32_t* w, rsrc_t r, uint32_t head, int sub, i
       const u4 x = bload16<CPOL_NT>(r, base + 1024 * i + 16 * lane);
       w[4 * i + 0] = x[0]; w[4 * i + 1] = x[1]; w[4 * i + 2] = x[2]; w[4 * i + 3] = x[3];
     }
-  } else {
-    static_assert(R == 8, "run of 8 bytes expected");
+  } else if constexpr (R == 8) {
     const u2 x = bload8<CPOL_NT>(r, base + 8 * lane);
     w[0] = x[0]; w[1] = x[1];
+  } else if constexpr (R == 4) {
+    w[0] = bload4<CPOL_NT>(r, base + 4 * lane);
+  } else {
+    static_assert(R == 2, "run of 2 bytes expected");
+    const uint32_t x = bload4<CPOL_NT>(r, base + 4 * (lane >> 1));
+    w[0] = spread16((lane & 1) ? x >> 16 : x & 0xffffu);
   }
 }
 
@@ -239,6 +273,18 @@ __device__ inline void int4x8(uint32_t w, h2* o) {
   o[3] = __builtin_elementwise_fma(as_h2((u8 & 0x00f000f0u) ^ 0x64806480u), s16, -off16);
 }
 
+// two unsigned 2-bit codes at bits s, s+1 and 16+s, 17+s -> fp16 pair (exact):
+// placed under the fp16 pattern of 1024 (0x6400), then 1024 subtracted
+__device__ inline h2 u2pair(uint32_t w, int s) {
+  const h2 off = {(_Float16)1024.0f, (_Float16)1024.0f};
+  return as_h2(((w >> s) & 0x00030003u) | 0x64006400u) - off;
+}
+// two sign codes at bits k and 16+k -> fp16 pair of +-1 (bit set: -1): each
+// bit moved into an fp16 sign bit over the pattern of 1.0 (0x3C00)
+__device__ inline h2 b1pair(uint32_t w, int k) {
+  return as_h2(((w << (15 - k)) & 0x80008000u) | 0x3C003C00u);
+}
+
 // A operand of the score MFMA: dims 32c + 8kq .. +7 of the lane's token.
 template <int C, int D>
 __device__ inline h8 k_frag(const uint32_t* w, int c) {
@@ -254,10 +300,21 @@ __device__ inline h8 k_frag(const uint32_t* w, int c) {
   } else if constexpr (C == C_INT8) {
     h4 a = int8x4(w[2 * c]), b = int8x4(w[2 * c + 1]);
     return h8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  } else {
+  } else if constexpr (C == C_INT4) {
     h2 o[4];
     int4x8(w[c], o);
     return h8{o[0][0], o[0][1], o[1][0], o[1][1], o[2][0], o[2][1], o[3][0], o[3][1]};
+  } else if constexpr (C == C_INT2) {
+    // elements 8(c % 2) + j of word c / 2: pair j, j + 1 at slots 4(c % 2) + j/2 and 8 + that
+    const uint32_t x = w[c >> 1];
+    const int s0 = 8 * (c & 1);
+    h2 a = u2pair(x, s0), b = u2pair(x, s0 + 2), d = u2pair(x, s0 + 4), e = u2pair(x, s0 + 6);
+    return h8{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
+  } else {
+    // elements 8c + j of the run's word: pair j, j + 1 at bits 4c + j/2 and 16 + that
+    const uint32_t x = w[0];
+    h2 a = b1pair(x, 4 * c), b = b1pair(x, 4 * c + 1), d = b1pair(x, 4 * c + 2), e = b1pair(x, 4 * c + 3);
+    return h8{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
   }
 }
 
@@ -274,10 +331,20 @@ __device__ inline h4 v_frag(const uint32_t* w, int n) {
     return h4{a[0], a[1], b[0], b[1]};
   } else if constexpr (C == C_INT8) {
     return int8x4(w[n]);
-  } else {
+  } else if constexpr (C == C_INT4) {
     h2 o[4];
     int4x8(w[n / 2], o);
     return (n & 1) ? h4{o[2][0], o[2][1], o[3][0], o[3][1]} : h4{o[0][0], o[0][1], o[1][0], o[1][1]};
+  } else if constexpr (C == C_INT2) {
+    // elements 4(n % 4) + j of word n / 4: tokens 0, 1 at bits 4(n % 4) and 16 + that,
+    // tokens 2, 3 two bits higher
+    const uint32_t x = w[n >> 2];
+    h2 a = u2pair(x, 4 * (n & 3)), b = u2pair(x, 4 * (n & 3) + 2);
+    return h4{a[0], a[1], b[0], b[1]};
+  } else {
+    // elements 4n + j: tokens 0, 1 at bits 2n and 16 + 2n, tokens 2, 3 one bit higher
+    h2 a = b1pair(w[0], 2 * n), b = b1pair(w[0], 2 * n + 1);
+    return h4{a[0], a[1], b[0], b[1]};
   }
 }
 
@@ -289,7 +356,9 @@ __device__ inline h8 k_frag_any(const uint32_t* w, int c, int codec) {
     case C_BF16: return k_frag<C_BF16, D>(w, c);
     case C_FP8: return k_frag<C_FP8, D>(w, c);
     case C_INT8: return k_frag<C_INT8, D>(w, c);
-    default: return k_frag<C_INT4, D>(w, c);
+    case C_INT4: return k_frag<C_INT4, D>(w, c);
+    case C_INT2: return k_frag<C_INT2, D>(w, c);
+    default: return k_frag<C_BIT1, D>(w, c);
   }
 }
 template <int D>
@@ -299,7 +368,9 @@ __device__ inline h4 v_frag_any(const uint32_t* w, int n, int codec) {
     case C_BF16: return v_frag<C_BF16, D>(w, n);
     case C_FP8: return v_frag<C_FP8, D>(w, n);
     case C_INT8: return v_frag<C_INT8, D>(w, n);
-    default: return v_frag<C_INT4, D>(w, n);
+    case C_INT4: return v_frag<C_INT4, D>(w, n);
+    case C_INT2: return v_frag<C_INT2, D>(w, n);
+    default: return v_frag<C_BIT1, D>(w, n);
   }
 }
 
@@ -318,26 +389,38 @@ __device__ inline uint32_t head_off(int codec, int h, int page) {
 // The lane's run of a plane whose codec is known only at run time: the same
 // D/32 16-byte loads for every codec, branch-free, so the compiler's wait
 // counts stay exact across pages of different codecs. Loads past the run
-// (8- and 4-bit codes) read through an offset beyond the plane: zeros, no
-// traffic. A 4-bit run of 8 bytes (D = 64) is taken from the 16-byte chunk
-// that holds it (two lanes per chunk, the same cache lines).
+// (codes of 8 bits or fewer) read through an offset beyond the plane: zeros,
+// no traffic. A run of R < 16 bytes (R = D * bits / 32) is taken from the
+// 16-byte chunk that holds it (16 / R lanes per chunk, the same cache lines)
+// and moved to the first words.
 template <int D>
 __device__ inline void load_run_any(uint32_t* w, rsrc_t r, int codec, int h, int page, int sub, int lane) {
   constexpr int NL = D / 32;  // 16-byte loads of a 16-bit run
   const int bits = bits_of(codec);
   const uint32_t head = (uint32_t)(h * page * D * bits / 8);
   const uint32_t base = head + (uint32_t)sub * (uint32_t)(16 * D * bits / 8);
-  const int nreal = bits == 16 ? NL : (bits == 8 ? NL / 2 : 1);
-  const bool half = D * 4 / 32 < 16 && bits == 4;  // 8-byte runs
-  const uint32_t lane_off = half ? 16u * (uint32_t)(lane >> 1) : 16u * (uint32_t)lane;
+  const int R = D * bits / 32;
+  const int nreal = R >= 16 ? R / 16 : 1;
+  const uint32_t lane_off = R >= 16 ? 16u * (uint32_t)lane : 16u * (uint32_t)((lane * R) >> 4);
+  u4 first;
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const u4 x = bload16<CPOL_NT>(r, i < nreal ? base + 1024u * i + lane_off : OFF_NONE);
+    if (i == 0) first = x;
     w[4 * i + 0] = x[0]; w[4 * i + 1] = x[1]; w[4 * i + 2] = x[2]; w[4 * i + 3] = x[3];
   }
-  if (half && (lane & 1)) {
-    w[0] = w[2];
-    w[1] = w[3];
+  // short runs: pick the run's words out of the loaded vector (selects on
+  // register values; an index into the tile array would move the whole tile
+  // ring to scratch memory)
+  if (R == 8) {
+    const bool odd = lane & 1;
+    w[0] = odd ? first[2] : first[0];
+    w[1] = odd ? first[3] : first[1];
+  } else if (R < 8) {
+    const int q = ((lane * R) & 15) >> 2;          // word of the chunk holding the run
+    const uint32_t lo = (q & 1) ? first[1] : first[0], hi = (q & 1) ? first[3] : first[2];
+    const uint32_t x = (q & 2) ? hi : lo;
+    w[0] = R == 4 ? x : spread16((lane & 1) ? x >> 16 : x & 0xffffu);
   }
 }
 
@@ -366,13 +449,19 @@ __device__ inline TileInfo issue_tile(Tile<D, KC, VC>& t, const Desc* desc, int 
   if constexpr (Tile<D, KC, VC>::GS) {
     constexpr int NW = D / 4;  // words of one tile's scales (16 tokens x D/32 fp16)
     const uint32_t blk = (uint32_t)((h * page + 16 * sub) * (D / 32) * 2);
+    // INT2 offsets follow every head's scales, laid out as the scales; they
+    // go to the other half of the lanes of the same word
+    const uint32_t zgap = (uint32_t)(a.hkv * page * (D / 32) * 2);
+    const int hl = lane & 31;
     if constexpr (Tile<D, KC, VC>::KS) {
       const uint32_t base = (uint32_t)(a.hkv * page * D * bits_of(ti.kc) / 8) + blk;
-      t.sk[0] = bload4(rk, is_int(ti.kc) && lane < NW ? base + 4 * lane : OFF_NONE);
+      const bool want = lane < 32 ? is_int(ti.kc) : (Tile<D, KC, VC>::KZ && has_zero(ti.kc));
+      t.sk[0] = bload4(rk, want && hl < NW ? base + (lane < 32 ? 0u : zgap) + 4 * hl : OFF_NONE);
     }
     if constexpr (Tile<D, KC, VC>::VS) {
       const uint32_t base = (uint32_t)(a.hkv * page * D * bits_of(ti.vc) / 8) + blk;
-      t.sv[0] = bload4(rv, is_int(ti.vc) && lane >= 32 && lane < 32 + NW ? base + 4 * (lane - 32) : OFF_NONE);
+      const bool want = lane >= 32 ? is_int(ti.vc) : (Tile<D, KC, VC>::VZ && has_zero(ti.vc));
+      t.sv[0] = bload4(rv, want && hl < NW ? base + (lane >= 32 ? 0u : zgap) + 4 * hl : OFF_NONE);
     }
   }
   if constexpr (per_page(KC)) {
@@ -435,6 +524,8 @@ __device__ inline float row4_sum(float x) {
 // would poison the MFMA. A zero code decodes to 0 in every codec. Word n of
 // an 8-bit run holds tokens j in bytes j; 16-bit runs hold tokens 0,1 in even
 // and 2,3 in odd words; an int4 word holds token j in the nibbles below.
+// 2- and 1-bit codes decode to finite values whatever their bits (their
+// scales and offsets of such tokens are zeroed instead), so they are left.
 __device__ inline void mask_v_run(uint32_t* v, int words, int bits, int nv) {
   if (bits == 8) {
     const uint32_t m = nv >= 4 ? ~0u : (1u << (8 * nv)) - 1u;
@@ -443,7 +534,7 @@ __device__ inline void mask_v_run(uint32_t* v, int words, int bits, int nv) {
     const uint32_t m0 = nv >= 2 ? ~0u : (nv == 1 ? 0x0000ffffu : 0u);
     const uint32_t m1 = nv >= 4 ? ~0u : (nv == 3 ? 0x0000ffffu : 0u);
     for (int i = 0; i < words; ++i) v[i] &= (i & 1) ? m1 : m0;
-  } else {
+  } else if (bits == 4) {
     const uint32_t m = (nv > 0 ? 0x00000f0fu : 0u) | (nv > 1 ? 0x0f0f0000u : 0u) |
                        (nv > 2 ? 0x0000f0f0u : 0u) | (nv > 3 ? 0xf0f00000u : 0u);
     for (int i = 0; i < words; ++i) v[i] &= m;
@@ -451,12 +542,13 @@ __device__ inline void mask_v_run(uint32_t* v, int words, int bits, int nv) {
 }
 
 // Scores, online-softmax update and P.V of one staged tile with ti.valid > 0
-// tokens. `sc` is this wave's 64-word LDS slot for the group scales (null
-// when no plane has them).
+// tokens. `sc` is this wave's 128-word LDS slot for the group scales and
+// offsets (null when no plane has them); qsum[c] is the sum of the lane's
+// query head over dims 32c .. 32c + 31 (for INT2 K offsets).
 template <int D, int KC, int VC>
-__device__ inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti, const h8* qv,
-                                    const h8* qg, float scale_log2, float& m_run, float& l_run, f4* acc,
-                                    uint32_t* sc, int lane) {
+__device__ __attribute__((always_inline)) inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti, const h8* qv,
+                                    const h8* qg, const float* qsum, float scale_log2, float& m_run,
+                                    float& l_run, f4* acc, uint32_t* sc, int lane) {
   constexpr int NC = D / 32, NB = D / 16;
   using T = Tile<D, KC, VC>;
   const int kq = lane >> 4;
@@ -473,28 +565,50 @@ __device__ inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti
     mask_v_run(vw, VWORDS, VC == C_ANY ? bits_of(vc) : bits_of(VC), nv);
   }
 
-  // group scales of this lane's four tokens (4 x NC fp16 each for K and V);
-  // the words of tokens past the end are written as zero
+  // group scales (and INT2 offsets) of this lane's four tokens (4 x NC fp16
+  // each for K and V); the words of tokens past the end are written as zero
   uint32_t ks[T::KS ? NC * 2 : 1], vs[T::VS ? NC * 2 : 1];
+  uint32_t kz[T::KZ ? NC * 2 : 1], vz[T::VZ ? NC * 2 : 1];
   if constexpr (T::GS) {
     const int w = lane & 31;
-    const uint32_t word = (T::KS ? t.sk[0] : 0u) | (T::VS ? t.sv[0] : 0u);
+    const bool live = (2 * w) / NC < ti.valid;
+    // slot words 0..31 K scales, 32..63 V scales, 64..95 V offsets, 96..127 K offsets
+    const uint32_t sk = T::KS ? t.sk[0] : 0u, sv = T::VS ? t.sv[0] : 0u;
     __builtin_amdgcn_wave_barrier();
-    sc[lane] = (2 * w) / NC < ti.valid ? word : 0u;
+    sc[lane] = live ? (lane < 32 ? sk : sv) : 0u;
+    if constexpr (T::KZ || T::VZ) sc[64 + lane] = live ? (lane < 32 ? sv : sk) : 0u;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    if constexpr (T::KS) {
+    if constexpr (T::KS && KC != C_ANY) {
 #pragma unroll
       for (int i = 0; i < NC * 2; i += 4) {
         const u4 x = *reinterpret_cast<const u4*>(sc + 2 * NC * kq + i);
         ks[i] = x[0]; ks[i + 1] = x[1]; ks[i + 2] = x[2]; ks[i + 3] = x[3];
       }
     }
-    if constexpr (T::VS) {
+    if constexpr (T::VS && VC != C_ANY) {
 #pragma unroll
       for (int i = 0; i < NC * 2; i += 4) {
         const u4 x = *reinterpret_cast<const u4*>(sc + 32 + 2 * NC * kq + i);
         vs[i] = x[0]; vs[i + 1] = x[1]; vs[i + 2] = x[2]; vs[i + 3] = x[3];
+      }
+    }
+    if constexpr (T::KZ && KC != C_ANY) {
+      if (has_zero(ti.kc)) {
+#pragma unroll
+        for (int i = 0; i < NC * 2; i += 4) {
+          const u4 x = *reinterpret_cast<const u4*>(sc + 96 + 2 * NC * kq + i);
+          kz[i] = x[0]; kz[i + 1] = x[1]; kz[i + 2] = x[2]; kz[i + 3] = x[3];
+        }
+      }
+    }
+    if constexpr (T::VZ && VC != C_ANY) {
+      if (has_zero(ti.vc)) {
+#pragma unroll
+        for (int i = 0; i < NC * 2; i += 4) {
+          const u4 x = *reinterpret_cast<const u4*>(sc + 64 + 2 * NC * kq + i);
+          vz[i] = x[0]; vz[i + 1] = x[1]; vz[i + 2] = x[2]; vz[i + 3] = x[3];
+        }
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -512,12 +626,20 @@ __device__ inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti
       scg[c] = mfma32(kf, (KC == C_ANY && kgrouped) ? qg[c] : qv[c], zero);
     }
     if (kgrouped) {
-      const _Float16* k16 = reinterpret_cast<const _Float16*>(ks);
+      // the per-page kernel reads scales and offsets from the LDS slot where used (registers are short there)
+      const _Float16* k16 = reinterpret_cast<const _Float16*>(KC == C_ANY ? sc + 2 * NC * kq : ks);
+      const bool kzero = T::KZ && has_zero(KC == C_ANY ? ti.kc : KC);
+      const _Float16* z16 = reinterpret_cast<const _Float16*>(KC == C_ANY ? sc + 96 + 2 * NC * kq : kz);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float x = 0.f;
 #pragma unroll
         for (int c = 0; c < NC; ++c) x += (float)k16[j * NC + c] * scg[c][j];
+        if (kzero) {
+          // INT2: the offset of each group times the query's sum over it
+#pragma unroll
+          for (int c = 0; c < NC; ++c) x += (float)z16[j * NC + c] * qsum[c];
+        }
         s[j] = x * scale_log2;
       }
     } else {
@@ -571,8 +693,41 @@ __device__ inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti
   auto vfrag = [&](int n) {
     return VC == C_ANY ? v_frag_any<D>(vw, n, ti.vc) : v_frag<VC == C_ANY ? 0 : VC, D>(vw, n);
   };
-  if (is_int(vc)) {
-    const _Float16* v16 = reinterpret_cast<const _Float16*>(vs);
+  if (T::VZ && has_zero(vc)) {
+    // INT2: V = z + s u. The offset and step terms are each rounded relative to
+    // their own size, which can far exceed their sum's, so both weights go in
+    // as fp16 high and low parts (22 significant bits): p s against the codes,
+    // and p against the offsets of the lane's four tokens (group n / 2 of dims
+    // 16n ..) as B, two MFMAs each per 16 dims.
+    const _Float16* v16 = reinterpret_cast<const _Float16*>(VC == C_ANY ? sc + 32 + 2 * NC * kq : vs);
+    const _Float16* z16 = reinterpret_cast<const _Float16*>(VC == C_ANY ? sc + 64 + 2 * NC * kq : vz);
+    h4 ph, pl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ph[j] = (_Float16)p[j];
+      pl[j] = (_Float16)(p[j] - (float)ph[j]);
+    }
+#pragma unroll
+    for (int g = 0; g < NC; ++g) {
+      h4 sh, sl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = p[j] * (float)v16[j * NC + g];
+        sh[j] = (_Float16)x;
+        sl[j] = (_Float16)(x - (float)sh[j]);
+      }
+      const h4 zf = {z16[0 * NC + g], z16[1 * NC + g], z16[2 * NC + g], z16[3 * NC + g]};
+#pragma unroll
+      for (int n = 2 * g; n < 2 * g + 2; ++n) {
+        const h4 vf = vfrag(n);
+        acc[n] = mfma16(sh, vf, acc[n]);
+        acc[n] = mfma16(sl, vf, acc[n]);
+        acc[n] = mfma16(ph, zf, acc[n]);
+        acc[n] = mfma16(pl, zf, acc[n]);
+      }
+    }
+  } else if (is_int(vc)) {
+    const _Float16* v16 = reinterpret_cast<const _Float16*>(VC == C_ANY ? sc + 32 + 2 * NC * kq : vs);
     h4 pa[NC];
 #pragma unroll
     for (int g = 0; g < NC; ++g)
@@ -604,14 +759,15 @@ __device__ inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti
 // A tile of a kernel built for any codec, consumed by the code of the pair
 // (K2, V2) its page holds: its raw words are that pair's run layout.
 template <int D, int K2, int V2, int KC, int VC>
-__device__ inline void consume_as(const Tile<D, KC, VC>& t, const TileInfo& ti, const h8* qv, const h8* qg,
-                                  float scale_log2, float& m_run, float& l_run, f4* acc, int lane) {
+__device__ __attribute__((always_inline)) inline void consume_as(const Tile<D, KC, VC>& t, const TileInfo& ti, const h8* qv, const h8* qg,
+                                  const float* qsum, float scale_log2, float& m_run, float& l_run, f4* acc,
+                                  int lane) {
   Tile<D, K2, V2> u;
 #pragma unroll
   for (int i = 0; i < Tile<D, K2, V2>::KW; ++i) u.k[i] = t.k[i];
 #pragma unroll
   for (int i = 0; i < Tile<D, K2, V2>::VW; ++i) u.v[i] = t.v[i];
-  consume_tile<D, K2, V2>(u, ti, qv, qg, scale_log2, m_run, l_run, acc, nullptr, lane);
+  consume_tile<D, K2, V2>(u, ti, qv, qg, qsum, scale_log2, m_run, l_run, acc, nullptr, lane);
 }
 
 // Consume one tile. With codecs known only at run time, pages of the common
@@ -620,21 +776,24 @@ __device__ inline void consume_as(const Tile<D, KC, VC>& t, const TileInfo& ti, 
 // pairs take the generic path (C_ANY; the C_FLT kernel has no others: the
 // gather skipped and counted them).
 template <int D, int KC, int VC>
-__device__ inline void consume(const Tile<D, KC, VC>& t, const TileInfo& ti, const h8* qv, const h8* qg,
-                               float scale_log2, float& m_run, float& l_run, f4* acc, uint32_t* sc, int lane) {
+__device__ __attribute__((always_inline)) inline void consume(const Tile<D, KC, VC>& t, const TileInfo& ti, const h8* qv, const h8* qg,
+                               const float* qsum, float scale_log2, float& m_run, float& l_run, f4* acc,
+                               uint32_t* sc, int lane) {
   if constexpr ((KC == C_ANY && VC == C_ANY) || (KC == C_FLT && VC == C_FLT)) {
     if (ti.kc == C_FP8 && ti.vc == C_FP8)
-      return consume_as<D, C_FP8, C_FP8>(t, ti, qv, qg, scale_log2, m_run, l_run, acc, lane);
+      return consume_as<D, C_FP8, C_FP8>(t, ti, qv, qg, qsum, scale_log2, m_run, l_run, acc, lane);
     if (ti.kc == C_FP16 && ti.vc == C_FP16)
-      return consume_as<D, C_FP16, C_FP16>(t, ti, qv, qg, scale_log2, m_run, l_run, acc, lane);
+      return consume_as<D, C_FP16, C_FP16>(t, ti, qv, qg, qsum, scale_log2, m_run, l_run, acc, lane);
     if (ti.kc == C_BF16 && ti.vc == C_BF16)
-      return consume_as<D, C_BF16, C_BF16>(t, ti, qv, qg, scale_log2, m_run, l_run, acc, lane);
+      return consume_as<D, C_BF16, C_BF16>(t, ti, qv, qg, qsum, scale_log2, m_run, l_run, acc, lane);
   }
-  if constexpr (KC != C_FLT) consume_tile<D, KC, VC>(t, ti, qv, qg, scale_log2, m_run, l_run, acc, sc, lane);
+  if constexpr (KC != C_FLT)
+    consume_tile<D, KC, VC>(t, ti, qv, qg, qsum, scale_log2, m_run, l_run, acc, sc, lane);
 }
 
 template <int D, int KC, int VC>
-__global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>()))) decode_kernel(const DecodeArgs a) {
+__global__ void __launch_bounds__(THREADS)
+__attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>(), max_waves_per_eu<D, KC, VC>()))) decode_kernel(const DecodeArgs a) {
   constexpr int NC = D / 32, NB = D / 16;
   // the waves' states merge through LDS in one pass over all head dims
   // (33 KB per workgroup at D 128: four FP8 workgroups per compute unit still
@@ -642,13 +801,13 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
   constexpr int RED_BYTES = (WAVES * 16 * D + 2 * WAVES * 16) * 4;
   constexpr int DESC_BYTES = MAX_DESC * (int)sizeof(Desc);
   __shared__ __attribute__((aligned(16))) unsigned char smem[RED_BYTES > DESC_BYTES ? RED_BYTES : DESC_BYTES];
-  __shared__ __attribute__((aligned(16))) uint32_t scale_slots[Tile<D, KC, VC>::GS ? WAVES * 64 : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t scale_slots[Tile<D, KC, VC>::GS ? WAVES * 128 : 4];
   Desc* desc = reinterpret_cast<Desc*>(smem);
 
   const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps loop control scalar
-  uint32_t* const sc = Tile<D, KC, VC>::GS ? scale_slots + 64 * wave : nullptr;
+  uint32_t* const sc = Tile<D, KC, VC>::GS ? scale_slots + 128 * wave : nullptr;
   const int col = lane & 15, kq = lane >> 4;
   const int G = a.group;
   const int P = a.page;
@@ -711,7 +870,7 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
       }
       // checks
       const int kc = cod & 15, vc = cod >> 4;
-      bool ok = pp_ok && kc <= C_INT4 && vc <= C_INT4;
+      bool ok = pp_ok && kc <= C_LAST && vc <= C_LAST;
       if (KC == C_FLT && !(kc == vc && kc <= C_FP8)) ok = false;  // a float page, one codec for both planes
       if (!per_page(KC) && kc != KC) ok = false;
       if (!per_page(VC) && vc != VC) ok = false;
@@ -757,6 +916,26 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
     }
   }
 
+  // query sums over each 32-dim group, for the offsets of INT2 K pages: the
+  // lane's eight dims of the grouped order, then the four rows of its column.
+  // The per-page kernel, at the edge of its registers, keeps them in LDS
+  // (read only for INT2 pages; the chunk loop's barrier orders the writes).
+  float qsum_reg[KC == C_INT2 ? NC : 1];
+  __shared__ float qsum_lds[KC == C_ANY ? WAVES * 16 * NC : 1];
+  if constexpr (KC == C_INT2 || KC == C_ANY) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const h8 x = KC == C_ANY ? qg[c] : qv[c];
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) part += (float)x[j];
+      const float qs = row4_sum(part);
+      if constexpr (KC == C_INT2) qsum_reg[c] = qs;
+      else if (lane < 16) qsum_lds[(wave * 16 + lane) * NC + c] = qs;
+    }
+  }
+  const float* const qsum = KC == C_ANY ? qsum_lds + (wave * 16 + col) * NC : qsum_reg;
+
   float m_run = NEG_INF, l_run = 0.f;
   f4 acc[NB];
 #pragma unroll
@@ -794,7 +973,7 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(wa
           // past the end: same loads through a zero-size resource (no traffic)
           inf[nx] = issue_tile<D, KC, VC>(t[nx], desc, min(kn, klast), tpp, a, h, lane, kn > klast);
           if (it + s < nmine && inf[s].valid > 0)
-            consume<D, KC, VC>(t[s], inf[s], qv, qg, a.scale_log2, m_run, l_run, acc, sc, lane);
+            consume<D, KC, VC>(t[s], inf[s], qv, qg, qsum, a.scale_log2, m_run, l_run, acc, sc, lane);
         }
       }
     }
@@ -1006,6 +1185,8 @@ int launch_d(const DecodeArgs& a, int kc, int vc, hipStream_t s) {
   PKV_PAIR(C_INT8, C_INT4)
   PKV_PAIR(C_INT8, C_INT8)
   PKV_PAIR(C_INT4, C_INT4)
+  PKV_PAIR(C_INT2, C_INT2)
+  PKV_PAIR(C_BIT1, C_BIT1)
 #undef PKV_PAIR
   if (kc == C_FLT && vc == C_FLT) return launch_t<D, C_FLT, C_FLT>(a, s);
   return launch_t<D, C_ANY, C_ANY>(a, s);

@@ -1,11 +1,16 @@
 // Write side of the paged cache, gfx950: token append into 16-bit pages and
-// re-encoding (demotion) of full 16-bit pages to FP8 / INT8 / INT4 / 16-bit.
+// re-encoding (demotion) of full 16-bit pages to FP8 / INT8 / INT4 / INT2 /
+// 1-bit / 16-bit.
 //
 // Recent pages stay FP16 while they fill; full older pages are re-encoded
 // into a compact codec (ARGUS "Adaptive activation" and "v0.5"). FP8 pages
 // hold e4m3 codes with one fp32 scale per (page, KV head, plane) (FreeToken
 // PR #499 update, item 1); INT8/INT4 pages hold one fp16 scale per token and
-// group of 32 dims (GGML Q8/Q4 pages, ARGUS "Direct paged attention").
+// group of 32 dims (GGML Q8/Q4 pages, ARGUS "Direct paged attention"). The
+// INT2 and 1-bit tiers of ARGUS's cascade (intro): INT2 as the unsigned-affine
+// 2-bit kind of its "Pluggable tiers" (an fp16 offset and step per token and
+// group), 1-bit as the sign with one fp16 scale (the mean magnitude) per token
+// and group.
 //
 // In-page layout (the library's definition; the decode kernels read it).
 // A plane is the codes of every KV head, head after head, then for INT8/INT4
@@ -17,8 +22,11 @@
 //  * K, one-scale codecs (FP16/BF16/FP8): token L%16, dim (D/4)(L/16) + e;
 //  * K, group-scale codecs (INT8/INT4):   token L%16, dim 32(e/8) + 8(L/16) + e%8;
 //  * V, every codec: token 4(L/16) + e%4, dim 16(e/4) + L%16.
-// INT4 packs eight elements per 32-bit word, element r of word w in nibble
-// slot (r%2)*4 + r/2.
+// Codes of fewer than 8 bits fill a run in units of min(32, run bits) bits,
+// m codes each: code r of a unit at slot (r%2)*(m/2) + r/2 (INT4: eight per
+// word; INT2: sixteen; BIT1: thirty-two, or sixteen in a 16-bit unit). The
+// group-scale codecs (INT8, INT4, INT2, BIT1) use the grouped K order; INT2
+// planes hold fp16 offsets [Hkv][P][D/32] after the scales.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -30,18 +38,24 @@
 namespace pkv {
 namespace {
 
-enum : int { W_FP16 = 0, W_BF16 = 1, W_FP8 = 2, W_INT8 = 3, W_INT4 = 4 };
+enum : int { W_FP16 = 0, W_BF16 = 1, W_FP8 = 2, W_INT8 = 3, W_INT4 = 4, W_INT2 = 5, W_BIT1 = 6 };
 
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
-__device__ inline int wbits(int c) { return c <= W_BF16 ? 16 : (c == W_INT4 ? 4 : 8); }
+__host__ __device__ constexpr int wbits(int c) {
+  return c <= W_BF16 ? 16 : (c == W_INT4 ? 4 : (c == W_INT2 ? 2 : (c == W_BIT1 ? 1 : 8)));
+}
 __device__ inline bool w16(int c) { return c == W_FP16 || c == W_BF16; }
-__device__ inline bool wint(int c) { return c == W_INT8 || c == W_INT4; }
+// symmetric integer codes: c = clip(rint(x / s), -qmax, qmax)
+__host__ __device__ constexpr bool wint(int c) { return c == W_INT8 || c == W_INT4; }
+// codecs with one fp16 scale per (token, 32 dims), in the grouped K order
+__host__ __device__ constexpr bool wgrp(int c) { return wint(c) || c == W_INT2 || c == W_BIT1; }
 
 __device__ inline uint64_t wplane_bytes(int c, int hkv, int page, int d) {
   const uint64_t codes = (uint64_t)hkv * page * d * wbits(c) / 8;
-  return codes + (wint(c) ? (uint64_t)hkv * page * (d / 32) * 2 : 0);
+  const uint64_t groups = (uint64_t)hkv * page * (d / 32) * 2;
+  return codes + (wgrp(c) ? groups : 0) + (c == W_INT2 ? groups : 0);
 }
 
 // (token in tile, dim) of run element e of lane L.
@@ -118,6 +132,68 @@ __device__ inline bool check_pair(const EncodeArgs& a, int i, int plane, int D, 
          disjoint(dvo, dvb, svo, svb) && disjoint(dko, dkb, dvo, dvb);
 }
 
+// OR the code of run element e (E elements of BITS bits) into the run's words.
+template <int BITS, int E>
+__device__ inline void put_code(uint32_t* word, int e, uint32_t code) {
+  if constexpr (BITS == 16) {
+    word[e >> 1] |= (code & 0xFFFFu) << (16 * (e & 1));
+  } else if constexpr (BITS == 8) {
+    word[e >> 2] |= (code & 0xFFu) << (8 * (e & 3));
+  } else {
+    constexpr int UB = E * BITS < 32 ? E * BITS : 32;  // unit bits
+    constexpr int M = UB / BITS;                        // codes per unit
+    const int r = e % M;
+    const int bit = (e / M) * UB + BITS * ((r & 1) * (M / 2) + (r >> 1));
+    word[bit >> 5] |= (code & ((1u << BITS) - 1u)) << (bit & 31);
+  }
+}
+
+// Store a destination run of RD bytes (lane L's run at its layout position).
+template <int RD, bool NT>
+__device__ inline void store_run_words(uint8_t* td, const uint32_t* word, int lane) {
+  if constexpr (RD >= 16) {
+#pragma unroll
+    for (int c = 0; c < RD / 16; ++c) {
+      const u4 x = {word[4 * c], word[4 * c + 1], word[4 * c + 2], word[4 * c + 3]};
+      u4* p = reinterpret_cast<u4*>(td + (c * 1024 + 16 * lane));
+      if constexpr (NT) __builtin_nontemporal_store(x, p); else *p = x;
+    }
+  } else if constexpr (RD == 8) {
+    u2* p = reinterpret_cast<u2*>(td + 8 * lane);
+    if constexpr (NT) __builtin_nontemporal_store(u2{word[0], word[1]}, p); else *p = u2{word[0], word[1]};
+  } else if constexpr (RD == 4) {
+    uint32_t* p = reinterpret_cast<uint32_t*>(td + 4 * lane);
+    if constexpr (NT) __builtin_nontemporal_store(word[0], p); else *p = word[0];
+  } else {
+    static_assert(RD == 2, "run of 2 bytes expected");
+    uint16_t* p = reinterpret_cast<uint16_t*>(td + 2 * lane);
+    if constexpr (NT) __builtin_nontemporal_store((uint16_t)word[0], p); else *p = (uint16_t)word[0];
+  }
+}
+
+// INT2 group offset and step from the group's minimum and maximum (fp32):
+// z = fp16(lo) saturated to +-65504; s = fp16(RN((hi - z) / 3)) kept inside
+// [2^-24, 65504], or 1 when hi - z <= 0. Returned as fp32 values.
+__device__ inline void affine2_params(float lo, float hi, float& z, float& st) {
+  z = fminf(fmaxf((float)(_Float16)lo, -65504.0f), 65504.0f);
+  const float span = hi - z;
+  if (span > 0.f) {
+    float s = (float)(_Float16)__fdiv_rn(span, 3.0f);
+    st = fminf(fmaxf(s, 0x1p-24f), 65504.0f);
+  } else {
+    st = 1.0f;
+  }
+}
+__device__ inline uint32_t affine2_code(float x, float z, float st) {
+  const float q = __builtin_rintf(__fdiv_rn(x - z, st));
+  return (uint32_t)(int)fminf(fmaxf(q, 0.0f), 3.0f);
+}
+// 1-bit group scale from the exact float64 sum of the group's magnitudes:
+// fp16(fp32(sum / 32)), capped at 65504 (0 for an all-zero group).
+__device__ inline float sign1_scale(double sum) {
+  return fminf((float)(_Float16)(float)(sum / 32.0), 65504.0f);
+}
+
 // ------------------------------------------------------------------ append
 // Grid (row, KV head, plane), 64 threads; thread = dims d, d + 64, ...
 __global__ void __launch_bounds__(64) append_kernel(AppendArgs a) {
@@ -170,15 +246,17 @@ __global__ void __launch_bounds__(64) append_kernel(AppendArgs a) {
 // staged tile x[token][dim], written with 16-byte (8 for INT4 at D = 64)
 // stores at the run's chunk positions.
 template <int D, int DC, bool IS_V>
-__device__ __attribute__((always_inline)) inline void emit_run(const float (*x)[D + 1], const float (*sc)[D / 32], float s8, uint8_t* td,
-                                int lane) {
-  constexpr int BITS = DC <= W_BF16 ? 16 : (DC == W_INT4 ? 4 : 8);
+__device__ __attribute__((always_inline)) inline void emit_run(const float (*x)[D + 1], const float (*sc)[D / 32],
+                                                               const float (*zs)[D / 32], float s8, uint8_t* td,
+                                                               int lane) {
+  constexpr int BITS = wbits(DC);
   constexpr int E = D / 4, RD = D * BITS / 32;
-  constexpr bool GROUPED = (DC == W_INT8 || DC == W_INT4) && !IS_V;
+  constexpr int NWD = RD < 4 ? 1 : RD / 4;
+  constexpr bool GROUPED = wgrp(DC) && !IS_V;
   constexpr float QMAX = DC == W_INT8 ? 127.0f : 7.0f;
-  uint32_t word[RD / 4];
+  uint32_t word[NWD];
 #pragma unroll
-  for (int k = 0; k < RD / 4; ++k) word[k] = 0;
+  for (int k = 0; k < NWD; ++k) word[k] = 0;
   if constexpr (DC == W_FP8) {
     // two elements per hardware conversion (OCP e4m3, nearest even) after the
     // correctly rounded quotient is clipped to +-448
@@ -205,48 +283,46 @@ __device__ __attribute__((always_inline)) inline void emit_run(const float (*x)[
       code = __builtin_bit_cast(uint16_t, (_Float16)v);
     } else if constexpr (DC == W_BF16) {
       code = f_to_bf16(v);
+    } else if constexpr (DC == W_INT2) {
+      code = affine2_code(v, zs[tt][d / 32], sc[tt][d / 32]);
+    } else if constexpr (DC == W_BIT1) {
+      code = v < 0.f ? 1u : 0u;
     } else {
       const float q = __builtin_rintf(__fdiv_rn(v, sc[tt][d / 32]));
       code = (uint32_t)(int)fminf(fmaxf(q, -QMAX), QMAX);
     }
-    if constexpr (BITS == 16) {
-      word[e >> 1] |= (code & 0xFFFFu) << (16 * (e & 1));
-    } else if constexpr (BITS == 8) {
-      word[e >> 2] |= (code & 0xFFu) << (8 * (e & 3));
-    } else {
-      const int r = e & 7, nslot = (r & 1) * 4 + (r >> 1);
-      word[e >> 3] |= (code & 0xFu) << (4 * nslot);
-    }
+    put_code<BITS, E>(word, e, code);
   }
-  if constexpr (RD >= 16) {
-#pragma unroll
-    for (int c = 0; c < RD / 16; ++c)
-      *reinterpret_cast<u4*>(td + run_byte(lane, 16 * c, RD)) =
-          u4{word[4 * c], word[4 * c + 1], word[4 * c + 2], word[4 * c + 3]};
-  } else {
-    *reinterpret_cast<uint2*>(td + run_byte(lane, 0, RD)) = uint2{word[0], word[1]};
-  }
+  store_run_words<RD, false>(td, word, lane);
 }
 
-template <int D, bool IS_V>
-__device__ __attribute__((always_inline)) inline void emit_any(int dc, const float (*x)[D + 1], const float (*sc)[D / 32], float s8, uint8_t* td,
-                                int lane) {
+// SUB: the kernel is built for destination pairs with an INT2 or BIT1 plane
+// (those codecs only; the other five codecs are built without them).
+template <int D, bool IS_V, bool SUB>
+__device__ __attribute__((always_inline)) inline void emit_any(int dc, const float (*x)[D + 1], const float (*sc)[D / 32],
+                                                               const float (*zs)[D / 32], float s8, uint8_t* td,
+                                                               int lane) {
+  if constexpr (SUB) {
+    if (dc == W_INT2) return emit_run<D, W_INT2, IS_V>(x, sc, zs, s8, td, lane);
+    if (dc == W_BIT1) return emit_run<D, W_BIT1, IS_V>(x, sc, zs, s8, td, lane);
+  }
   switch (dc) {
-    case W_FP16: emit_run<D, W_FP16, IS_V>(x, sc, s8, td, lane); break;
-    case W_BF16: emit_run<D, W_BF16, IS_V>(x, sc, s8, td, lane); break;
-    case W_FP8: emit_run<D, W_FP8, IS_V>(x, sc, s8, td, lane); break;
-    case W_INT8: emit_run<D, W_INT8, IS_V>(x, sc, s8, td, lane); break;
-    default: emit_run<D, W_INT4, IS_V>(x, sc, s8, td, lane); break;
+    case W_FP16: emit_run<D, W_FP16, IS_V>(x, sc, zs, s8, td, lane); break;
+    case W_BF16: emit_run<D, W_BF16, IS_V>(x, sc, zs, s8, td, lane); break;
+    case W_FP8: emit_run<D, W_FP8, IS_V>(x, sc, zs, s8, td, lane); break;
+    case W_INT8: emit_run<D, W_INT8, IS_V>(x, sc, zs, s8, td, lane); break;
+    default: emit_run<D, W_INT4, IS_V>(x, sc, zs, s8, td, lane); break;
   }
 }
 
 // Grid (pair i, KV head, plane); TILES tiles of 16 tokens staged at once, one
 // 64-lane slot each (TILES = min(4, P/16), so no slot idles on small pages).
-template <int D, int TILES>
+template <int D, int TILES, bool SUB>
 __global__ void __launch_bounds__(64 * TILES) encode_kernel(EncodeArgs a) {
   constexpr int THREADS = 64 * TILES;
   __shared__ float xs[TILES][16][D + 1];              // staged tiles, [token][dim]
-  __shared__ float scs[TILES][16][D / 32];            // INT group scales (fp32 of the fp16 value)
+  __shared__ float scs[TILES][16][D / 32];            // group scales (fp32 of the fp16 value)
+  __shared__ float zss[TILES][16][D / 32];            // INT2 group offsets
   __shared__ float red[TILES];
   const int i = blockIdx.x, h = blockIdx.y, plane = blockIdx.z, tid = threadIdx.x;
   const int P = a.page, hkv = a.hkv;
@@ -333,30 +409,52 @@ __global__ void __launch_bounds__(64 * TILES) encode_kernel(EncodeArgs a) {
       s8 = m == 0.f ? 1.f : __fdiv_rn(m, 448.0f);
       if (tid == 0 && a.scale) a.scale[((size_t)dst * hkv + h) * 2 + plane] = s8;
     }
-    // INT group scales: one (token, group) per lane of the slot
-    if (live && wint(dcodec)) {
+    // group scales (and INT2 offsets): one (token, group) per lane of the slot
+    if (live && wgrp(dcodec)) {
       for (int q = lane; q < 16 * G; q += 64) {
         const int tt = q / G, g = q % G;
-        float m = 0.f;
+        _Float16 s16, z16 = (_Float16)0.0f;
+        if (SUB && dcodec == W_INT2) {
+          float lo = xs[slot][tt][32 * g], hi = lo;
 #pragma unroll 8
-        for (int j = 0; j < 32; ++j) m = fmaxf(m, __builtin_fabsf(xs[slot][tt][32 * g + j]));
-        // fp16 scale kept inside its positive finite range [2^-24, 65504]
-        _Float16 s16 = (_Float16)__fdiv_rn(m, qmax);
-        s16 = s16 == (_Float16)0.0f ? __builtin_bit_cast(_Float16, (uint16_t)0x0001) : s16;
-        s16 = s16 > (_Float16)65504.0f ? (_Float16)65504.0f : s16;
-        s16 = m == 0.f ? (_Float16)1.0f : s16;
+          for (int j = 1; j < 32; ++j) {
+            lo = fminf(lo, xs[slot][tt][32 * g + j]);
+            hi = fmaxf(hi, xs[slot][tt][32 * g + j]);
+          }
+          float z, st;
+          affine2_params(lo, hi, z, st);
+          s16 = (_Float16)st;
+          z16 = (_Float16)z;
+        } else if (SUB && dcodec == W_BIT1) {
+          double sum = 0.0;                       // exact for 16-bit inputs
+#pragma unroll 8
+          for (int j = 0; j < 32; ++j) sum += (double)__builtin_fabsf(xs[slot][tt][32 * g + j]);
+          s16 = (_Float16)sign1_scale(sum);
+        } else {
+          float m = 0.f;
+#pragma unroll 8
+          for (int j = 0; j < 32; ++j) m = fmaxf(m, __builtin_fabsf(xs[slot][tt][32 * g + j]));
+          // fp16 scale kept inside its positive finite range [2^-24, 65504]
+          s16 = (_Float16)__fdiv_rn(m, qmax);
+          s16 = s16 == (_Float16)0.0f ? __builtin_bit_cast(_Float16, (uint16_t)0x0001) : s16;
+          s16 = s16 > (_Float16)65504.0f ? (_Float16)65504.0f : s16;
+          s16 = m == 0.f ? (_Float16)1.0f : s16;
+        }
         scs[slot][tt][g] = (float)s16;
+        zss[slot][tt][g] = (float)z16;
         const size_t so16 = (size_t)hkv * P * D * dbits / 8 + ((size_t)h * P + 16 * tile + tt) * G * 2 + 2 * g;
         *reinterpret_cast<_Float16*>(a.pool + dof + so16) = s16;
+        if (SUB && dcodec == W_INT2)
+          *reinterpret_cast<_Float16*>(a.pool + dof + so16 + (size_t)hkv * P * G * 2) = z16;
       }
     }
     __syncthreads();
     if (!live) continue;
     uint8_t* td = dp + (size_t)tile * 16 * D * dbits / 8;
     if (is_v)
-      emit_any<D, true>(dcodec, xs[slot], scs[slot], s8, td, lane);
+      emit_any<D, true, SUB>(dcodec, xs[slot], scs[slot], zss[slot], s8, td, lane);
     else
-      emit_any<D, false>(dcodec, xs[slot], scs[slot], s8, td, lane);
+      emit_any<D, false, SUB>(dcodec, xs[slot], scs[slot], zss[slot], s8, td, lane);
   }
 }
 
@@ -412,6 +510,17 @@ __device__ inline float rows4_max(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
   return fmaxf(x, __shfl_xor(x, 32));
 }
+__device__ inline float row16_min(float x) { return -row16_max(-x); }
+__device__ inline float rows4_min(float x) { return -rows4_max(-x); }
+// exact float64 sums (of 16-bit magnitudes) over the same lane sets
+__device__ inline double row16_sum(double x) {
+  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ inline double rows4_sum(double x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
 
 // element i (0..7) of a 16-byte chunk of 16-bit codes (BF16 or FP16), as float
 template <bool BF>
@@ -459,14 +568,15 @@ __device__ inline void load_unit(UnitSrc<D, NT>& u, const uint8_t* sp, bool grou
 // (for V runs: token 4(lane/16) + e % 4, group e / 8; grouped K runs fill
 // every j of group g alike).
 template <int D, int DC, bool BF>
-__device__ inline void store_run(const u4* x, const float (*s2)[D / 32], const float (*r2)[D / 32], float s8, float r8,
-                                 bool fast8, uint8_t* td, int lane) {
-  constexpr int BITS = DC <= W_BF16 ? 16 : (DC == W_INT4 ? 4 : 8);
+__device__ inline void store_run(const u4* x, const float (*s2)[D / 32], const float (*r2)[D / 32],
+                                 const float (*z2)[D / 32], float s8, float r8, bool fast8, uint8_t* td, int lane) {
+  constexpr int BITS = wbits(DC);
   constexpr int E = D / 4, RD = D * BITS / 32;
+  constexpr int NWD = RD < 4 ? 1 : RD / 4;
   constexpr float QMAX = DC == W_INT8 ? 127.0f : 7.0f;
-  uint32_t word[RD / 4];
+  uint32_t word[NWD];
 #pragma unroll
-  for (int k = 0; k < RD / 4; ++k) word[k] = 0;
+  for (int k = 0; k < NWD; ++k) word[k] = 0;
   if constexpr (DC == W_FP8) {
 #pragma unroll
     for (int e = 0; e < E; e += 2) {
@@ -489,39 +599,33 @@ __device__ inline void store_run(const u4* x, const float (*s2)[D / 32], const f
         code = __builtin_bit_cast(uint16_t, (_Float16)v);
       } else if constexpr (DC == W_BF16) {
         code = f_to_bf16(v);
+      } else if constexpr (DC == W_INT2) {
+        code = affine2_code(v, z2[e & 3][e >> 3], s2[e & 3][e >> 3]);
+      } else if constexpr (DC == W_BIT1) {
+        code = v < 0.f ? 1u : 0u;
       } else {
         const float q = __builtin_rintf(recip_div(v, s2[e & 3][e >> 3], r2[e & 3][e >> 3]));
         code = (uint32_t)(int)fminf(fmaxf(q, -QMAX), QMAX);
       }
-      if constexpr (BITS == 16) {
-        word[e >> 1] |= (code & 0xFFFFu) << (16 * (e & 1));
-      } else if constexpr (BITS == 8) {
-        word[e >> 2] |= (code & 0xFFu) << (8 * (e & 3));
-      } else {
-        const int r = e & 7, nslot = (r & 1) * 4 + (r >> 1);
-        word[e >> 3] |= (code & 0xFu) << (4 * nslot);
-      }
+      put_code<BITS, E>(word, e, code);
     }
   }
-  if constexpr (RD >= 16) {
-#pragma unroll
-    for (int c = 0; c < RD / 16; ++c)
-      __builtin_nontemporal_store(u4{word[4 * c], word[4 * c + 1], word[4 * c + 2], word[4 * c + 3]},
-                                  reinterpret_cast<u4*>(td + run_byte(lane, 16 * c, RD)));
-  } else {
-    __builtin_nontemporal_store(u2{word[0], word[1]}, reinterpret_cast<u2*>(td + run_byte(lane, 0, RD)));
-  }
+  store_run_words<RD, true>(td, word, lane);
 }
 
 // DK: the destination codec pair (K low nibble, V high nibble) the kernel is
-// specialised for (FP8/FP8), else -1 (any pair, chosen per plane at run
-// time). A call has one destination pair. (An INT8/INT4 specialisation held
-// as many registers as the generic kernel and is not built.)
+// specialised for (FP8/FP8), else -1 (any pair of FP16, BF16, FP8, INT8 and
+// INT4, chosen per plane at run time) or -2 (any pair with an INT2 or BIT1
+// plane: their reductions and packing are built only here, so the other
+// kernels keep their registers). A call has one destination pair. (An
+// INT8/INT4 specialisation held as many registers as the generic kernel and
+// is not built.)
 template <int D, int NT, int DK>
 __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int nunits) {
   constexpr int NC = D / 32;
   __shared__ float sx[EW][4][16];  // per wave: INT V scales of its tile, [row][combo]
   __shared__ float rx[EW][4][16];  // and their reciprocals RN(1 / s)
+  __shared__ float zx[EW][4][16];  // INT2 V offsets
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int gw = blockIdx.x * EW + wv, nw = gridDim.x * EW;
@@ -548,7 +652,7 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
     unit_of(u, i, h, plane);
     ok = check_pair(a, i, plane, D, dst, scodec, dcodec, so, dof);
     if (DK >= 0) dcodec = plane ? DK >> 4 : DK & 15;
-    if (ok) load_unit<D, NT>(cur, a.pool + so + (size_t)h * P * D * 2, wint(dcodec) && plane == 0, lane);
+    if (ok) load_unit<D, NT>(cur, a.pool + so + (size_t)h * P * D * 2, wgrp(dcodec) && plane == 0, lane);
     have = true;
   }
   while (have) {
@@ -562,7 +666,7 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
       unit_of(un, i2, h2, plane2);
       ok2 = check_pair(a, i2, plane2, D, dst2, scodec2, dcodec2, so2, dof2);
       if (DK >= 0) dcodec2 = plane2 ? DK >> 4 : DK & 15;
-      if (PREFETCH && ok2) load_unit<D, NT>(nxt, a.pool + so2 + (size_t)h2 * P * D * 2, wint(dcodec2) && plane2 == 0, lane);
+      if (PREFETCH && ok2) load_unit<D, NT>(nxt, a.pool + so2 + (size_t)h2 * P * D * 2, wgrp(dcodec2) && plane2 == 0, lane);
     }
 
     if (!ok) {
@@ -604,11 +708,86 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const u4* x = cur.x[t];
-          float s2[4][NC], r2[4][NC];
+          float s2[4][NC], r2[4][NC], z2[4][NC];
 #pragma unroll
           for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int g = 0; g < NC; ++g) s2[j][g] = r2[j][g] = 1.f;
+            for (int g = 0; g < NC; ++g) s2[j][g] = r2[j][g] = 1.f, z2[j][g] = 0.f;
+          if (DK == -2 && wgrp(dcodec) && !wint(dcodec)) {
+            // INT2 (offset and step per group) and BIT1 (mean magnitude per group)
+            const size_t sc_base = (size_t)hkv * P * D * dbits / 8 + ((size_t)h * P + 16 * t) * NC * 2;
+            const size_t zgap = (size_t)hkv * P * NC * 2;
+            const bool aff = dcodec == W_INT2;
+            if (is_v) {
+              // group g of token 4kq + j: elements 8g + j and 8g + 4 + j on the 16 lanes of row kq;
+              // lane l16 < 4 NC of each row keeps combo (j, g) = (l16 / NC, l16 % NC)
+              float mine_s = 1.f, mine_z = 0.f;
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int g = 0; g < NC; ++g) {
+                  const float e0 = chunk_elem<BF>(x[g], j), e1 = chunk_elem<BF>(x[g], 4 + j);
+                  float sv = 1.f, zv = 0.f;
+                  if (aff) {
+                    affine2_params(row16_min(fminf(e0, e1)), row16_max(fmaxf(e0, e1)), zv, sv);
+                  } else {
+                    sv = sign1_scale(row16_sum((double)__builtin_fabsf(e0) + (double)__builtin_fabsf(e1)));
+                  }
+                  const bool me = l16 == j * NC + g;
+                  mine_s = me ? sv : mine_s;
+                  mine_z = me ? zv : mine_z;
+                }
+              if (l16 < 4 * NC) {
+                sx[wv][kq][l16] = mine_s;
+                zx[wv][kq][l16] = mine_z;
+                const int j = l16 / NC, g = l16 % NC;
+                const size_t at = sc_base + ((size_t)(4 * kq + j) * NC + g) * 2;
+                *reinterpret_cast<_Float16*>(a.pool + dof + at) = (_Float16)mine_s;
+                if (aff) *reinterpret_cast<_Float16*>(a.pool + dof + at + zgap) = (_Float16)mine_z;
+              }
+              __builtin_amdgcn_wave_barrier();
+              __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int g = 0; g < NC; ++g) {
+                  s2[j][g] = sx[wv][kq][j * NC + g];
+                  z2[j][g] = zx[wv][kq][j * NC + g];
+                }
+              __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+              __builtin_amdgcn_wave_barrier();
+            } else {
+              // grouped K: chunk c is group c of token lane%16, spread over the 4 rows
+#pragma unroll
+              for (int c = 0; c < NC; ++c) {
+                float sv = 1.f, zv = 0.f;
+                if (aff) {
+                  float lo = chunk_elem<BF>(x[c], 0), hi = lo;
+#pragma unroll
+                  for (int k = 1; k < 8; ++k) {
+                    lo = fminf(lo, chunk_elem<BF>(x[c], k));
+                    hi = fmaxf(hi, chunk_elem<BF>(x[c], k));
+                  }
+                  affine2_params(rows4_min(lo), rows4_max(hi), zv, sv);
+                } else {
+                  double m = 0.0;
+#pragma unroll
+                  for (int k = 0; k < 8; ++k) m += (double)__builtin_fabsf(chunk_elem<BF>(x[c], k));
+                  sv = sign1_scale(rows4_sum(m));
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  s2[j][c] = sv;
+                  z2[j][c] = zv;
+                }
+                if (kq == (c & 3) && (NC == 4 || kq < NC)) {
+                  const size_t at = sc_base + ((size_t)l16 * NC + c) * 2;
+                  *reinterpret_cast<_Float16*>(a.pool + dof + at) = (_Float16)sv;
+                  if (aff) *reinterpret_cast<_Float16*>(a.pool + dof + at + zgap) = (_Float16)zv;
+                }
+              }
+            }
+          }
           if (wint(dcodec)) {
             const size_t sc_base = (size_t)hkv * P * D * dbits / 8 + ((size_t)h * P + 16 * t) * NC * 2;
             auto scale_of = [&](float m) {  // fp16 scale kept inside fp16's finite range
@@ -668,12 +847,20 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
             }
           }
           uint8_t* td = dp + (size_t)t * 16 * D * dbits / 8;
-          switch (dcodec) {
-            case W_FP16: store_run<D, W_FP16, BF>(x, s2, r2, s8, r8, fast8, td, lane); break;
-            case W_BF16: store_run<D, W_BF16, BF>(x, s2, r2, s8, r8, fast8, td, lane); break;
-            case W_FP8: store_run<D, W_FP8, BF>(x, s2, r2, s8, r8, fast8, td, lane); break;
-            case W_INT8: store_run<D, W_INT8, BF>(x, s2, r2, s8, r8, fast8, td, lane); break;
-            default: store_run<D, W_INT4, BF>(x, s2, r2, s8, r8, fast8, td, lane); break;
+          const bool sub = DK == -2 && (dcodec == W_INT2 || dcodec == W_BIT1);
+          if (sub) {
+            if constexpr (DK == -2) {
+              if (dcodec == W_INT2) store_run<D, W_INT2, BF>(x, s2, r2, z2, s8, r8, fast8, td, lane);
+              else store_run<D, W_BIT1, BF>(x, s2, r2, z2, s8, r8, fast8, td, lane);
+            }
+          } else {
+            switch (dcodec) {
+              case W_FP16: store_run<D, W_FP16, BF>(x, s2, r2, z2, s8, r8, fast8, td, lane); break;
+              case W_BF16: store_run<D, W_BF16, BF>(x, s2, r2, z2, s8, r8, fast8, td, lane); break;
+              case W_FP8: store_run<D, W_FP8, BF>(x, s2, r2, z2, s8, r8, fast8, td, lane); break;
+              case W_INT8: store_run<D, W_INT8, BF>(x, s2, r2, z2, s8, r8, fast8, td, lane); break;
+              default: store_run<D, W_INT4, BF>(x, s2, r2, z2, s8, r8, fast8, td, lane); break;
+            }
           }
         }
       };
@@ -689,7 +876,7 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
 #pragma unroll
         for (int c = 0; c < NC; ++c) cur.x[t][c] = nxt.x[t][c];
     } else if (have && ok) {
-      load_unit<D, NT>(cur, a.pool + so + (size_t)h * P * D * 2, wint(dcodec) && plane == 0, lane);
+      load_unit<D, NT>(cur, a.pool + so + (size_t)h * P * D * 2, wgrp(dcodec) && plane == 0, lane);
     }
   }
 }
@@ -704,6 +891,17 @@ int launch_append(const AppendArgs& a, void* stream) {
 
 namespace {
 
+// a destination pair with an INT2 or BIT1 plane
+bool sub_byte_dst(int dst_codec) {
+  const int k = dst_codec & 15, v = (dst_codec >> 4) & 15;
+  return k == W_INT2 || k == W_BIT1 || v == W_INT2 || v == W_BIT1;
+}
+// Whether such a pair takes the register path for units of NT tiles: its
+// tile loop, with the INT2/BIT1 reductions, unrolls (and the unit stays in
+// registers) up to 16 chunks of 16 bytes per lane; larger units are staged
+// through LDS.
+constexpr bool sub_reg_path(int D, int NT) { return NT * D / 32 <= 8; }
+
 template <int D, int NT>
 void launch_encode_reg(const EncodeArgs& a, hipStream_t s) {
   const int nunits = a.n * a.hkv * 2;
@@ -715,10 +913,14 @@ void launch_encode_reg(const EncodeArgs& a, hipStream_t s) {
   const bool fp8 = a.dst_codec == (W_FP8 | W_FP8 << 4);
   const int cap = fp8 ? 1536 : 4096;
   if (wgs > cap) wgs = cap;
-  if (fp8)
+  if (fp8) {
     hipLaunchKernelGGL((encode_reg_kernel<D, NT, W_FP8 | W_FP8 << 4>), dim3(wgs), dim3(64 * EW), 0, s, a, nunits);
-  else
+  } else if (sub_byte_dst(a.dst_codec)) {
+    if constexpr (sub_reg_path(D, NT))
+      hipLaunchKernelGGL((encode_reg_kernel<D, NT, -2>), dim3(wgs), dim3(64 * EW), 0, s, a, nunits);
+  } else {
     hipLaunchKernelGGL((encode_reg_kernel<D, NT, -1>), dim3(wgs), dim3(64 * EW), 0, s, a, nunits);
+  }
 }
 
 }  // namespace
@@ -728,7 +930,8 @@ int launch_encode(const EncodeArgs& a, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int tiles = a.page / 16;  // page is a multiple of 16
   if (a.head_dim != 64 && a.head_dim != 128) return -2;
-  if (tiles <= 4 && (long long)a.n * a.hkv * 2 <= 0x7fffffff) {
+  const bool staged_sub = sub_byte_dst(a.dst_codec) && !(tiles <= 4 && sub_reg_path(a.head_dim, tiles));
+  if (tiles <= 4 && !staged_sub && (long long)a.n * a.hkv * 2 <= 0x7fffffff) {
     // register path: one wave per (pair, head, plane)
 #define PKV_REG(DD)                                                   \
   if (tiles == 4) launch_encode_reg<DD, 4>(a, s);                     \
@@ -745,8 +948,14 @@ int launch_encode(const EncodeArgs& a, void* stream) {
   }
   // longer pages: staged through LDS, four tiles at a time
   const dim3 grid(a.n, a.hkv, 2);
-  if (a.head_dim == 64) hipLaunchKernelGGL((encode_kernel<64, 4>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((encode_kernel<128, 4>), grid, dim3(256), 0, s, a);
+  const bool sub = sub_byte_dst(a.dst_codec);
+  if (a.head_dim == 64) {
+    if (sub) hipLaunchKernelGGL((encode_kernel<64, 4, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((encode_kernel<64, 4, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (sub) hipLaunchKernelGGL((encode_kernel<128, 4, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((encode_kernel<128, 4, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

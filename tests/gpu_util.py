@@ -52,7 +52,7 @@ def compare(out, lse, ref_out, ref_lse, what=""):
 def poison_tails(w):
     """Overwrite every byte the row lengths exclude inside attended pages'
     tail tokens with bytes that decode to NaN/huge values in every codec."""
-    from oracle.layout import BITS, code_position
+    from oracle.layout import BITS, code_bits, code_position
     P, D, hkv = w.page_size, w.head_dim, w.num_kv_heads
     arr = w.pool.as_array() if w.pool.is_dense else None
     assert arr is not None
@@ -66,10 +66,18 @@ def poison_tails(w):
         c = int(w.page_codec[pp])
         for off, codec, is_v in ((int(w.page_k_off[pp]), c & 15, False), (int(w.page_v_off[pp]), c >> 4, True)):
             bits = BITS[codec]
-            pos, nib = code_position(P, D, codec, is_v)
-            pos = pos[valid:].ravel()
             head_bytes = P * D * bits // 8
-            for h in range(hkv):
+            if bits < 4:
+                # every 2- or 1-bit code is a valid code: set the tail's codes
+                # to all ones; the scales and offsets below carry the poison
+                bpos, shift = code_bits(P, D, codec, is_v)
+                ones = ((1 << bits) - 1) << shift[valid:].ravel()
+                for h in range(hkv):
+                    np.bitwise_or.at(arr, off + h * head_bytes + bpos[valid:].ravel(), ones.astype(np.uint8))
+            else:
+                pos, nib = code_position(P, D, codec, is_v)
+                pos = pos[valid:].ravel()
+            for h in range(hkv if bits >= 4 else 0):
                 base = off + h * head_bytes
                 if bits == 16:
                     arr[base + pos] = 0xFF                        # fp16/bf16 NaN
@@ -81,10 +89,13 @@ def poison_tails(w):
                     b_hi, b_lo = base + pos[hi], base + pos[~hi]
                     arr[b_hi] = (arr[b_hi] & 0x0F) | 0x80
                     arr[b_lo] = (arr[b_lo] & 0xF0) | 0x08
-            if codec in (synth.INT8, synth.INT4):
+            if codec in (synth.INT8, synth.INT4, synth.INT2, synth.BIT1):
                 sc = off + hkv * P * D * bits // 8
-                for h in range(hkv):
-                    s0 = sc + (h * P + valid) * (D // 32) * 2
-                    s1 = sc + (h * P + P) * (D // 32) * 2
-                    arr[s0:s1] = 0x7C                             # fp16 0x7C7C: NaN
+                regions = 2 if codec == synth.INT2 else 1         # INT2: offsets after the scales
+                for reg in range(regions):
+                    base = sc + reg * hkv * P * (D // 32) * 2
+                    for h in range(hkv):
+                        s0 = base + (h * P + valid) * (D // 32) * 2
+                        s1 = base + (h * P + P) * (D // 32) * 2
+                        arr[s0:s1] = 0x7C                         # fp16 0x7C7C: NaN
     return w

@@ -152,7 +152,7 @@ def test_encode_host_checks():
     args = [4096] * 5                                  # pool, k_off, v_off, codec, scale
     assert lib.pkv_encode_pages(ctypes.byref(p), 0, 0, 0, 0x22, *args, 0, 0) == 0      # nothing to do
     assert lib.pkv_encode_pages(ctypes.byref(p), -1, 4096, 4096, 0x22, *args, 0, 0) == -1
-    assert lib.pkv_encode_pages(ctypes.byref(p), 4, 4096, 4096, 0x25, *args, 0, 0) == -1  # K nibble 5
+    assert lib.pkv_encode_pages(ctypes.byref(p), 4, 4096, 4096, 0x27, *args, 0, 0) == -1  # K nibble 7
     assert lib.pkv_encode_pages(ctypes.byref(p), 4, 4096, 4096, 0x122, *args, 0, 0) == -1  # > one byte
     assert lib.pkv_encode_pages(ctypes.byref(p), 4, 4096, 4096, 0x22, 4096, 4096, 4096, 4096, 0, 0, 0) == -1  # FP8 needs scales
     assert lib.pkv_encode_pages(ctypes.byref(p), 4, 0, 4096, 0x43, *args, 0, 0) == -1      # src missing

@@ -11,13 +11,14 @@ import oracle
 import paged_kv_cache_182_amd as pkv
 import synth
 from synth.device import to_device
-from synth.layout import BF16, FP8, FP16, INT4, INT8
+from synth.layout import BF16, BIT1, FP8, FP16, INT2, INT4, INT8
 from gpu_util import compare, params_for, poison_tails, run
 
 pytestmark = pytest.mark.gpu
 
 PAIRS = [(FP16, FP16), (BF16, BF16), (FP8, FP8), (INT8, INT4), (INT8, INT8), (INT4, INT4),
-         (FP8, FP16), (INT4, FP8), (FP16, INT8)]
+         (FP8, FP16), (INT4, FP8), (FP16, INT8),
+         (INT2, INT2), (BIT1, BIT1), (INT8, INT2), (INT2, BIT1), (BIT1, FP16)]
 
 
 def small(seq_lens, kc, vc, hq, hkv, dim, page, seed=7, **kw):
@@ -52,7 +53,8 @@ def test_group_sizes(hq, hkv):
 @pytest.mark.parametrize("dim", [64, 128])
 def test_mixed_codecs_per_page(dim):
     print(f"case mixed dim={dim}", flush=True)
-    cyc = [(FP16, FP16), (FP8, FP8), (INT8, INT4), (BF16, INT8), (INT4, FP16), (BF16, BF16), (FP16, INT4)]
+    cyc = [(FP16, FP16), (FP8, FP8), (INT8, INT4), (BF16, INT8), (INT4, FP16), (BF16, BF16), (FP16, INT4),
+           (INT2, INT2), (BIT1, BIT1), (INT2, FP8), (BIT1, INT2)]
     w = poison_tails(small([40, 333, 160], None, None, hq=8, hkv=2, dim=dim, page=16,
                            codec_of=lambda r, lp: cyc[(r + lp) % len(cyc)]))
     check(w, partition_tokens=32)
@@ -430,3 +432,55 @@ def test_sparse_selection_over_256_pages():
     check(w, partition_tokens=8192, what="sparse 300-400 pages, one partition")
     check(w, partition_tokens=4096, what="sparse 300-400 pages, 256-page partitions")
     check(w, partition_tokens=0, what="sparse 300-400 pages, even split")
+
+
+
+@pytest.mark.parametrize("dim", [64, 128])
+def test_tier_cascade_rows(dim):
+    """A row whose pages sit in every tier of the cascade, newest FP16 to
+    oldest 1-bit (FP16, FP8, INT8, INT4, INT2, 1-bit), read by the per-page
+    kernel at fixed, sub-page and even-split partitions."""
+    print(f"case tier cascade dim={dim}", flush=True)
+    tiers = [BIT1, INT2, INT4, INT8, FP8, FP16]          # logical page 0 is the oldest
+
+    def codec_of(r, lp):
+        c = tiers[min(lp * len(tiers) // 12, len(tiers) - 1)]
+        return (c, c)
+    w = poison_tails(small([12 * 64 - 5, 700, 64], None, None, hq=16, hkv=2, dim=dim, page=64, codec_of=codec_of,
+                           seed=19, q_scale=2.0))
+    for T in (0, 48, 256):
+        check(w, partition_tokens=T, what=f"tier cascade dim={dim} T={T}")
+
+
+@pytest.mark.parametrize("codec", [INT2, BIT1])
+@pytest.mark.parametrize("dim", [64, 128])
+def test_subbyte_v_codes_exact(codec, dim):
+    """q = 0 and one token per row: out is that token's V exactly. Every
+    2-bit code (INT2: offset + step * u) or both signs (BIT1), with fp16
+    steps and offsets whose sums are exact in fp32."""
+    print(f"case sub-byte V codes {codec} dim={dim}", flush=True)
+    from oracle.layout import code_bits
+    rows = 4
+    w = small([1] * rows, FP16, codec, hq=2, hkv=1, dim=dim, page=16, seed=5)
+    arr = w.pool.as_array()
+    bpos, shift = code_bits(16, dim, codec, True)
+    rng = np.random.default_rng(9)
+    G = dim // 32
+    for r in range(rows):
+        pp = int(w.block_table[r, 0])
+        off = int(w.page_v_off[pp])
+        head_bytes = 16 * dim * (2 if codec == INT2 else 1) // 8
+        arr[off:off + head_bytes] = 0
+        codes = rng.integers(0, 4 if codec == INT2 else 2, size=dim)
+        np.bitwise_or.at(arr, off + bpos[0], (codes << shift[0]).astype(np.uint8))
+        sc = off + head_bytes
+        steps = np.float16(rng.choice([0.25, 0.5, 1.5, 3.0], size=G))
+        arr[sc:sc + 2 * G] = np.frombuffer(steps.tobytes(), np.uint8)
+        if codec == INT2:
+            zo = sc + 16 * G * 2
+            offs = np.float16(rng.choice([-2.0, -0.75, 0.125, 1.0], size=G))
+            arr[zo:zo + 2 * G] = np.frombuffer(offs.tobytes(), np.uint8)
+    w.q[:] = 0
+    out, _ = run(to_device(w), params_for(w, 0))
+    ref, _ = oracle.decode_attention(w)
+    assert np.array_equal(out, ref.astype(np.float32).astype(np.float64))

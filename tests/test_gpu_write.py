@@ -12,7 +12,7 @@ import oracle
 import paged_kv_cache_182_amd as pkv
 from oracle.encode import append_token, encode_page
 from synth import layout as slay
-from synth.layout import BF16, FP8, FP16, INT4, INT8
+from synth.layout import BF16, BIT1, FP8, FP16, INT2, INT4, INT8
 
 from gpu_util import compare
 
@@ -85,6 +85,10 @@ CASES = [  # (K codec, V codec, head_dim, page)
     (FP8, FP8, 128, 64), (INT8, INT4, 128, 16), (INT8, INT8, 64, 32), (INT4, INT4, 64, 16),
     (FP8, INT4, 128, 32), (BF16, BF16, 64, 16), (FP16, FP8, 128, 16),
     (INT8, INT4, 128, 48), (FP8, FP8, 64, 128), (INT8, FP8, 128, 256),   # three tiles; longer pages
+    # INT2 / 1-bit destinations: register path (16- and 32-token pages, head_dim 64 up to 64 tokens),
+    # staged path (longer units)
+    (INT2, INT2, 128, 16), (BIT1, BIT1, 128, 32), (INT2, BIT1, 64, 64), (BIT1, INT8, 64, 16),
+    (INT8, INT2, 128, 64), (BIT1, BIT1, 128, 128), (INT2, FP8, 64, 256),
 ]
 
 
@@ -147,7 +151,8 @@ def test_encode_many_units_sampled(kc, vc, P):
     assert np.all(codec_t.cpu().numpy()[n_src:] == dst_codec)
 
 
-@pytest.mark.parametrize("kc,vc,D,P", [(FP8, FP8, 128, 64), (INT8, INT4, 128, 16), (INT4, INT4, 64, 32)])
+@pytest.mark.parametrize("kc,vc,D,P", [(FP8, FP8, 128, 64), (INT8, INT4, 128, 16), (INT4, INT4, 64, 32),
+                                      (INT2, INT2, 128, 16), (BIT1, BIT1, 64, 32), (INT2, BIT1, 128, 64)])
 def test_read_path_on_encoded_pages(kc, vc, D, P):
     """Encode on the device, then decode attention over the destination pages:
     the read path agrees with the oracle's attention on the same bytes."""
@@ -235,6 +240,41 @@ def test_write_side_errors_are_counted_and_skipped():
     torch.cuda.synchronize()
     assert int(err.item()) == 3
     assert torch.equal(pool_t, before)
+
+
+@pytest.mark.parametrize("P", [16, 128])
+def test_encode_int2_ties_and_bit1_signs(P):
+    """INT2 quotients exactly halfway between steps go to the even code, and
+    1-bit codes follow the sign (-0 counts as positive), byte for byte with
+    the oracle on both encoder paths (register path for 16-token pages, LDS
+    path for 128)."""
+    print(f"case INT2 ties / BIT1 signs P={P}", flush=True)
+    hkv, D, n_src = 1, 64, 2
+    dst_codec = INT2 | BIT1 << 4
+    x, pool, koff, voff, codec, scale = build_pool(23, n_src, hkv, P, D, FP16, dst_codec)
+    # every group: min -1.5 and max 1.5 (offset -1.5, step 1), values on the grid and halfway
+    vals = np.array([-1.5, -1.0, -0.5, 0.0, 0.5, 1.0, 1.5, -0.0], np.float32)
+    grid = np.resize(vals, (P, D)).astype(np.float16).astype(np.float32)
+    for i in range(n_src):
+        xi = grid.copy()
+        xi[:, ::32] = -1.5
+        xi[:, 1::32] = 1.5
+        kb, _ = slay.encode_plane(xi[None, None], FP16, v_order=False)
+        vb, _ = slay.encode_plane(xi[None, None], FP16, v_order=True)
+        pool[koff[i]: koff[i] + kb.shape[1]] = kb[0]
+        pool[voff[i]: voff[i] + vb.shape[1]] = vb[0]
+    src = np.arange(n_src, dtype=np.int32)
+    dst = src + n_src
+    pool_t, koff_t, voff_t, codec_t, scale_t, src_t, dst_t = to_dev(pool, koff, voff, codec, scale, src, dst)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pkv.encode_pages(params(len(codec), hkv, P, D, pool.size), src_t, dst_t, dst_codec, pool_t, koff_t, voff_t,
+                     codec_t, scale_t, err_count=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ref, rs, rc = oracle_encode(pool, koff, voff, codec, scale, src, dst, dst_codec, hkv, P, D)
+    got = pool_t.cpu().numpy()
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
 
 
 @pytest.mark.parametrize("dst_codec", [FP8 | FP8 << 4, INT8 | INT4 << 4])
