@@ -506,8 +506,9 @@ def time_select(torch, pkv, steps, rows=48, context=262144, page=16, idx_dim=64,
 
 def time_write_side(torch, pkv, steps):
     """The write side, measured on its own: demotion of full FP16 pages
-    (pkv_encode_pages) at the 1M FP8 and 32K INT8-K/INT4-V geometries, and one
-    decode step's append (pkv_append_kv) for the 8-row batch. The source pages
+    (pkv_encode_pages) at the 1M FP8 geometry and, at the 32K geometry, to
+    INT8-K/INT4-V and to the INT2 and 1-bit tiers, and one decode step's
+    append (pkv_append_kv) for the 8-row batch. The source pages
     hold random fp16 values; every call re-encodes the same pages."""
     import numpy as np
 
@@ -515,8 +516,9 @@ def time_write_side(torch, pkv, steps):
         return (x + 255) // 256 * 256
 
     def plane(c, hkv, P, D):
-        bits = 16 if c <= 1 else (4 if c == 4 else 8)
-        return hkv * P * D * bits // 8 + (hkv * P * (D // 32) * 2 if c in (3, 4) else 0)
+        bits = {0: 16, 1: 16, 2: 8, 3: 8, 4: 4, 5: 2, 6: 1}[c]
+        groups = hkv * P * (D // 32) * 2                 # fp16 per (token, 32 dims)
+        return hkv * P * D * bits // 8 + (groups if c in (3, 4, 5, 6) else 0) + (groups if c == 5 else 0)
 
     def timed(call, n):
         call()
@@ -532,7 +534,9 @@ def time_write_side(torch, pkv, steps):
 
     res = {}
     for name, n, hkv, P, D, dst_codec in (("demote_fp16_to_fp8_1m", 16384, 2, 64, 128, 0x22),
-                                          ("demote_fp16_to_int8k_int4v_32k", 14720, 8, 16, 128, 0x43)):
+                                          ("demote_fp16_to_int8k_int4v_32k", 14720, 8, 16, 128, 0x43),
+                                          ("demote_fp16_to_int2_32k", 14720, 8, 16, 128, 0x55),
+                                          ("demote_fp16_to_bit1_32k", 14720, 8, 16, 128, 0x66)):
         sp = aligned(plane(0, hkv, P, D))
         dk, dv = aligned(plane(dst_codec & 15, hkv, P, D)), aligned(plane(dst_codec >> 4, hkv, P, D))
         base = n * 2 * sp

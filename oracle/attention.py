@@ -15,7 +15,10 @@ for every query head, with query head ``hq`` reading KV head ``hq // G``
 tokens are, in logical order, tokens 0..L-1 reached through the block table
 (FreeToken PR #499 "Design": logical -> physical translation), or in sparse
 mode the tokens t < L of the selected logical pages only (PR #499 "Why this
-works"). An empty token set gives out = 0 and lse = -inf.
+works"). A sliding window of W tokens (ARGUS "v0.5": direct attention with
+sliding-window masks) keeps only positions t >= L - W, the row's last W
+positions; W <= 0 means none. An empty token set gives out = 0 and
+lse = -inf.
 
 ``fold`` combines partial results by their log-sum-exp (PR #499 discussion,
 in-place host K/V design).
@@ -40,6 +43,14 @@ def attended_pages(w, row: int) -> list[tuple[int, int]]:
     else:
         lps = list(range(-(-L // P))) if L > 0 else []
     return [(lp, max(0, min(P, L - lp * P))) for lp in lps]
+
+
+def attended_positions(w, row: int) -> np.ndarray:
+    """Logical token positions of the row's attended tokens, in the order
+    ``gather_kv`` returns them (before any sliding window)."""
+    P = w.page_size
+    pos = [np.arange(lp * P, lp * P + valid) for lp, valid in attended_pages(w, row) if valid > 0]
+    return np.concatenate(pos) if pos else np.zeros(0, dtype=np.int64)
 
 
 def gather_kv(w, row: int, h: int) -> tuple[np.ndarray, np.ndarray]:
@@ -73,17 +84,26 @@ def _softmax_attention(K, V, q, tau):
     return out, m + np.log(l)
 
 
-def decode_attention(w, rows=None):
-    """out float64 [rows, Hq, D], lse float64 [rows, Hq]."""
+def decode_attention(w, rows=None, window=None):
+    """out float64 [rows, Hq, D], lse float64 [rows, Hq]. ``window``: the
+    sliding window in tokens (default: the workload's ``window_tokens``, if
+    any; <= 0 means none)."""
     rows = range(w.rows) if rows is None else rows
+    if window is None:
+        window = int(getattr(w, "window_tokens", 0) or 0)
     hq, hkv, D = w.num_q_heads, w.num_kv_heads, w.head_dim
     G = hq // hkv
     rows = list(rows)
     out = np.zeros((len(rows), hq, D))
     lse = np.zeros((len(rows), hq))
     for ri, r in enumerate(rows):
+        keep = None
+        if window > 0:
+            keep = attended_positions(w, r) >= int(w.seq_lens[r]) - window
         for h in range(hkv):
             K, V = gather_kv(w, r, h)
+            if keep is not None:
+                K, V = K[keep], V[keep]
             q = w.q[r, h * G:(h + 1) * G].astype(np.float64)
             o, s = _softmax_attention(K, V, q, float(w.softmax_scale))
             out[ri, h * G:(h + 1) * G] = o

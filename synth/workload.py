@@ -44,6 +44,7 @@ class Workload:
     page_scale: np.ndarray      # float32 [num_pages, Hkv, 2]
     pool: Pool
     info: dict = dataclasses.field(default_factory=dict)
+    window_tokens: int = 0      # sliding window of the decode call (0: none)
 
     @property
     def num_pages(self) -> int:

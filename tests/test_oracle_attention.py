@@ -343,3 +343,51 @@ def test_gather_sparse_uses_selected_pages_only():
             w.page_k_off[pp] = np.uint64(2**60)
     after = decode_attention(w)
     assert np.array_equal(before[0], after[0]) and np.array_equal(before[1], after[1])
+
+
+def test_sliding_window_decode_pins():
+    """Sliding-window decode (each row attends its last W positions):
+    W = 0 and W >= L leave the result unchanged; W = 1 gives the last
+    token's V and score (closed form); any W equals the chunked-prefill
+    oracle's query at T = 1 with the same window (its own masks)."""
+    from oracle.prefill import prefill_attention
+    w = small([1, 40, 300, 513], FP8, INT8, hq=8, hkv=2, dim=64, page=32, seed=4)
+    full = decode_attention(w)
+    for W in (0, 513, 10_000):
+        o, l = decode_attention(w, window=W)
+        assert np.array_equal(o, full[0]) and np.array_equal(l, full[1])
+    o1, l1 = decode_attention(w, window=1)
+    G = 4
+    for r in range(w.rows):
+        L = int(w.seq_lens[r])
+        for h in range(2):
+            K, V = gather_kv(w, r, h)
+            q = w.q[r, h * G:(h + 1) * G].astype(np.float64)
+            assert np.array_equal(o1[r, h * G:(h + 1) * G], np.broadcast_to(V[L - 1], (G, 64)))
+            assert np.allclose(l1[r, h * G:(h + 1) * G], w.softmax_scale * (q @ K[L - 1]), rtol=0, atol=1e-12)
+    q1 = w.q[:, None].astype(np.float16)
+    for W in (1, 7, 32, 33, 100, 299):
+        o, l = decode_attention(w, window=W)
+        po, pl = prefill_attention(w, q1, window=W)
+        assert np.max(np.abs(o - po[:, 0])) <= 1e-12 and np.max(np.abs(l - pl[:, 0])) <= 1e-12
+
+
+def test_sliding_window_sparse_brute_force():
+    """Sparse mode with a window: only the selected pages' tokens at
+    positions >= L - W, by direct math.fsum evaluation."""
+    w = synth.build_workload("win_sparse", rows=1, hq=1, hkv=1, dim=64, page=16, seq_lens=[100],
+                             codec_of=lambda r, lp: (FP16, FP16), seed=8,
+                             selection=np.array([[6, 1, 4]], np.int32), logical_pages=7)
+    P, L, W = 16, 100, 40                                  # positions >= 60: page 4 from token 64, page 6 to 99
+    o, l = decode_attention(w, window=W)
+    K, V = gather_kv(w, 0, 0)                               # pages 1, 4, 6 ascending: 16 + 16 + 4 tokens
+    pos = np.concatenate([np.arange(16, 32), np.arange(64, 80), np.arange(96, 100)])
+    keep = pos >= L - W
+    q = w.q[0, 0].astype(np.float64)
+    s = [w.softmax_scale * math.fsum(q * k) for k in K[keep]]
+    m = max(s)
+    e = [math.exp(x - m) for x in s]
+    den = math.fsum(e)
+    ref = np.array([math.fsum(e[i] * V[keep][i][d] for i in range(len(e))) / den for d in range(64)])
+    assert np.max(np.abs(o[0, 0] - ref)) <= 1e-12 and abs(l[0, 0] - (m + math.log(den))) <= 1e-12
+    assert keep.sum() == 20
