@@ -14,7 +14,8 @@
  * over the attended tokens t: in dense mode tokens 0 .. seq_lens[b]-1, found
  * through the row's block table (logical page -> physical page; FreeToken PR
  * #499 "Design"); in sparse mode only the tokens t < seq_lens[b] of the
- * logical pages listed in page_sel (PR #499 "What" and "Why this works").
+ * logical pages listed in page_sel (PR #499 "What" and "Why this works");
+ * with a sliding window of W tokens, only those at positions >= L_b - W.
  * The kernel walks the pages with an exact online softmax (ARGUS "Direct
  * paged attention"); long rows are split into partitions of
  * partition_tokens whose (acc, max, sum) partials are folded by log-sum-exp
@@ -90,8 +91,9 @@ extern "C" {
 
 /* 2: partitions are ranges of 16-token tiles (partition_tokens a multiple of
  *    16; 0 splits each row evenly), PKV_CODEC_MIXED_FLOAT.
- * 3: pkv_decode_attention_noalloc, pkv_noalloc_scratch_bytes, PKV_ERR_SCRATCH. */
-#define PKV_ABI_VERSION 3
+ * 3: pkv_decode_attention_noalloc, pkv_noalloc_scratch_bytes, PKV_ERR_SCRATCH.
+ * 4: pkv_params.window_tokens (sliding-window decode); PKV_INT2_G32, PKV_BIT1_G32. */
+#define PKV_ABI_VERSION 4
 
 /* Page codecs; page_codec[p] = K codec | (V codec << 4). */
 enum {
@@ -145,6 +147,12 @@ typedef struct pkv_params {
   float softmax_scale;       /* tau, finite (1/sqrt(head_dim) in the usual case)        */
   uint64_t pool_bytes;       /* size of page_pool in bytes: a plane that does not fit
                                 inside it is a device-visible error                      */
+  int32_t window_tokens;     /* decode: sliding window W >= 0 (ARGUS v0.5: direct attention
+                                with sliding-window masks): row b attends only positions
+                                >= seq_lens[b] - W, its last W; 0: none. Dense mode: the
+                                partitions cover the window's tiles only. Must be 0 for
+                                pkv_prefill_attention (which takes its window as an
+                                argument); ignored by the write side                     */
 } pkv_params;
 
 /* PKV_ABI_VERSION of the loaded library. */
@@ -161,7 +169,9 @@ const char* pkv_status_string(int status);
  * workgroups per partition index), at most one per
  * 8 tiles of the longest row and at least 1; row b's partition i then covers
  * tiles [i c, (i + 1) c), c = max(1, ceil(ceil(L_b / 16) / n)) (dense) or
- * ceil(sel_lens[b] P / 16 / n) (sparse). */
+ * ceil(sel_lens[b] P / 16 / n) (sparse). With a sliding window (dense mode)
+ * a row's tiles are counted from tile floor((L_b - W) / 16), the first one
+ * the window reaches, and there are at most ceil(W / 16) + 1 of them. */
 int pkv_num_partitions(const pkv_params* p);
 
 /* Bytes of device workspace pkv_decode_attention needs for these params:

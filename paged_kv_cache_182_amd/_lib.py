@@ -39,7 +39,7 @@ class Params(ctypes.Structure):
                 ("max_pages_per_row", ctypes.c_int32), ("max_sel_pages", ctypes.c_int32),
                 ("partition_tokens", ctypes.c_int32), ("k_codec", ctypes.c_int32),
                 ("v_codec", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-                ("pool_bytes", ctypes.c_uint64)]
+                ("pool_bytes", ctypes.c_uint64), ("window_tokens", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -89,7 +89,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_select_pages.restype = ctypes.c_int
     lib.pkv_select_pages.argtypes = [pp] + [i32] * 6 + [vp] * 9
     lib.pkv_lse_fold_into.argtypes = [i32, i32, vp, vp, vp, vp, vp]
-    if lib.pkv_abi_version() != 3:  # the allocation-free decode entry point
+    if lib.pkv_abi_version() != 4:  # window_tokens in pkv_params; INT2 and 1-bit codecs
         raise RuntimeError("libpkv ABI version mismatch")
     _lib = lib
     return lib
@@ -101,12 +101,12 @@ def status_string(status: int) -> str:
 
 def make_params(*, rows, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                 max_pages_per_row, pool_bytes, max_sel_pages=0, partition_tokens=0,
-                k_codec=CODEC_MIXED, v_codec=CODEC_MIXED, softmax_scale=None) -> Params:
+                k_codec=CODEC_MIXED, v_codec=CODEC_MIXED, softmax_scale=None, window_tokens=0) -> Params:
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(head_dim)
     return Params(rows, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                   max_pages_per_row, max_sel_pages, partition_tokens, k_codec, v_codec,
-                  softmax_scale, pool_bytes)
+                  softmax_scale, pool_bytes, window_tokens)
 
 
 def num_partitions(p: Params) -> int:

@@ -55,6 +55,8 @@ int check_params(const pkv_params* p) {
   if (p->num_pages < 0 || p->max_pages_per_row < 1 || p->max_sel_pages < 0) return PKV_ERR_INVALID_ARG;
   if (p->partition_tokens < 0 || p->partition_tokens % 16 != 0) return PKV_ERR_INVALID_ARG;
   if (!isfinite(p->softmax_scale)) return PKV_ERR_INVALID_ARG;
+  if (p->window_tokens < 0) return PKV_ERR_INVALID_ARG;
+  if (p->page_size > (1 << 20)) return PKV_ERR_UNSUPPORTED;  // in-page slot counts are 24-bit on the device
   if (!valid_codec(p->k_codec) || !valid_codec(p->v_codec)) return PKV_ERR_INVALID_ARG;
   if ((p->k_codec == PKV_CODEC_MIXED_FLOAT) != (p->v_codec == PKV_CODEC_MIXED_FLOAT)) return PKV_ERR_INVALID_ARG;
   if (p->head_dim != 64 && p->head_dim != 128) return PKV_ERR_UNSUPPORTED;
@@ -67,8 +69,16 @@ int64_t row_capacity(const pkv_params* p) {
   return p->max_sel_pages > 0 ? p->max_sel_pages : p->max_pages_per_row;
 }
 
-// 16-token tiles a row can reach at most.
-int64_t row_tiles(const pkv_params* p) { return row_capacity(p) * (p->page_size / 16); }
+// 16-token tiles a row can reach at most: with a sliding window of W tokens
+// (dense mode), the tiles that hold its W positions.
+int64_t row_tiles(const pkv_params* p) {
+  int64_t t = row_capacity(p) * (p->page_size / 16);
+  if (p->window_tokens > 0 && p->max_sel_pages == 0) {
+    const int64_t w = ((int64_t)p->window_tokens + 15) / 16 + 1;
+    if (w < t) t = w;
+  }
+  return t;
+}
 
 // Partitions per row. A positive partition_tokens fixes their length; 0 lets
 // the library split each row's tiles evenly into as many partitions as fill
@@ -175,6 +185,7 @@ int prepare(const pkv_params* p, const void* q, const uint8_t* page_pool,
   a->nparts = (int32_t)nparts;
   a->sparse = sparse ? 1 : 0;
   a->final_out = 0;
+  a->window = p->window_tokens;
   a->scale_log2 = p->softmax_scale * 1.44269504088896340736f;
   a->pool_bytes = p->pool_bytes;
   return PKV_OK;
@@ -393,6 +404,7 @@ int plan_prefill(const pkv_params* p, int32_t q_tokens, int32_t kv_begin, int32_
   int st = check_params(p);
   if (st != PKV_OK) return st;
   if (p->max_sel_pages != 0) return PKV_ERR_INVALID_ARG;  // the prefill attends the dense cache
+  if (p->window_tokens != 0) return PKV_ERR_INVALID_ARG;  // its sliding window is an argument of its own
   // the prefill kernel decodes FP16, BF16, FP8, INT8 and INT4 pages only
   if (p->k_codec > PKV_INT4_G32 || p->v_codec > PKV_INT4_G32) return PKV_ERR_UNSUPPORTED;
   if (p->partition_tokens % p->page_size != 0) return PKV_ERR_INVALID_ARG;  // prefill partitions are whole pages

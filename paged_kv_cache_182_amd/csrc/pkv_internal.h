@@ -63,6 +63,7 @@ struct DecodeArgs {
   int32_t nparts;
   int32_t sparse;
   int32_t final_out;        // 1: write out/lse (single partition); 0: write partials
+  int32_t window;           // sliding window in tokens (each row attends positions >= L - window); 0: none
   float scale_log2;         // softmax_scale * log2(e)
   uint64_t pool_bytes;      // size of the arena; planes must lie inside it
 };

@@ -105,8 +105,8 @@ struct Desc {
   uint64_t k;      // byte offset of the K plane in the pool (0 if the page is skipped)
   uint64_t v;      // byte offset of the V plane
   float sk, sv;    // FP8 scales of this KV head (1 for other codecs)
-  int32_t valid;   // attended tokens of the page (0 if skipped)
-  int32_t codec;   // K codec | V codec << 4
+  int32_t valid;   // attended tokens of the page (0 if skipped): slots [lo, valid)
+  int32_t codec;   // K codec | V codec << 4 | lo << 8, lo = leading slots before a sliding window
 };
 
 // Raw codes of one 16-token tile for one lane. Sizes per codec class; the
@@ -167,7 +167,8 @@ __host__ __device__ constexpr int max_waves_per_eu() {
 }
 
 struct TileInfo {
-  int valid;  // tokens of the tile to attend (0: skip the tile)
+  int valid;  // tokens of the tile to attend: [lo, valid) (valid 0: skip the tile)
+  int lo;     // leading tokens before a sliding window
   int kc, vc;
   float sk, sv;
 };
@@ -435,10 +436,12 @@ __device__ inline TileInfo issue_tile(Tile<D, KC, VC>& t, const Desc* desc, int 
   const int i = a.tile_shift >= 0 ? k >> a.tile_shift : k / tpp;
   const int sub = k - i * tpp;
   TileInfo ti;
-  ti.valid = dead ? 0 : min(max(uni(desc[i].valid) - 16 * sub, 0), 16);
   const int codec = uni(desc[i].codec);
+  ti.lo = min(max((codec >> 8) - 16 * sub, 0), 16);
+  ti.valid = dead ? 0 : min(max(uni(desc[i].valid) - 16 * sub, 0), 16);
+  ti.valid = ti.valid > ti.lo ? ti.valid : 0;  // wholly before the window: skip
   ti.kc = per_page(KC) ? (codec & 15) : KC;
-  ti.vc = per_page(VC) ? (codec >> 4) : VC;
+  ti.vc = per_page(VC) ? ((codec >> 4) & 15) : VC;
   ti.sk = unif(desc[i].sk);
   ti.sv = unif(desc[i].sv);
   const bool live = ti.valid > 0;
@@ -526,17 +529,21 @@ __device__ inline float row4_sum(float x) {
 // and 2,3 in odd words; an int4 word holds token j in the nibbles below.
 // 2- and 1-bit codes decode to finite values whatever their bits (their
 // scales and offsets of such tokens are zeroed instead), so they are left.
-__device__ inline void mask_v_run(uint32_t* v, int words, int bits, int nv) {
+// Tokens j of the lane's four are kept for a <= j < b (a > 0: before a
+// sliding window).
+__device__ inline void mask_v_run(uint32_t* v, int words, int bits, int a, int b) {
+  const bool k0 = a <= 0 && b > 0, k1 = a <= 1 && b > 1, k2 = a <= 2 && b > 2, k3 = a <= 3 && b > 3;
   if (bits == 8) {
-    const uint32_t m = nv >= 4 ? ~0u : (1u << (8 * nv)) - 1u;
+    const uint32_t m = (k0 ? 0x000000ffu : 0u) | (k1 ? 0x0000ff00u : 0u) | (k2 ? 0x00ff0000u : 0u) |
+                       (k3 ? 0xff000000u : 0u);
     for (int i = 0; i < words; ++i) v[i] &= m;
   } else if (bits == 16) {
-    const uint32_t m0 = nv >= 2 ? ~0u : (nv == 1 ? 0x0000ffffu : 0u);
-    const uint32_t m1 = nv >= 4 ? ~0u : (nv == 3 ? 0x0000ffffu : 0u);
+    const uint32_t m0 = (k0 ? 0x0000ffffu : 0u) | (k1 ? 0xffff0000u : 0u);
+    const uint32_t m1 = (k2 ? 0x0000ffffu : 0u) | (k3 ? 0xffff0000u : 0u);
     for (int i = 0; i < words; ++i) v[i] &= (i & 1) ? m1 : m0;
   } else if (bits == 4) {
-    const uint32_t m = (nv > 0 ? 0x00000f0fu : 0u) | (nv > 1 ? 0x0f0f0000u : 0u) |
-                       (nv > 2 ? 0x0000f0f0u : 0u) | (nv > 3 ? 0xf0f00000u : 0u);
+    const uint32_t m = (k0 ? 0x00000f0fu : 0u) | (k1 ? 0x0f0f0000u : 0u) | (k2 ? 0x0000f0f0u : 0u) |
+                       (k3 ? 0xf0f00000u : 0u);
     for (int i = 0; i < words; ++i) v[i] &= m;
   }
 }
@@ -553,16 +560,15 @@ __device__ __attribute__((always_inline)) inline void consume_tile(const Tile<D,
   using T = Tile<D, KC, VC>;
   const int kq = lane >> 4;
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
-  const bool partial = ti.valid < 16;  // wave-uniform
+  const bool partial = ti.valid < 16 || ti.lo > 0;  // wave-uniform
   const int vc = VC == C_ANY ? ti.vc : VC;
 
   uint32_t vw[T::VW];
 #pragma unroll
   for (int i = 0; i < T::VW; ++i) vw[i] = t.v[i];
   if (partial) {
-    const int nv = min(max(ti.valid - 4 * kq, 0), 4);
     constexpr int VWORDS = VC == C_ANY ? T::VW : D * bits_of(VC) / 128;
-    mask_v_run(vw, VWORDS, VC == C_ANY ? bits_of(vc) : bits_of(VC), nv);
+    mask_v_run(vw, VWORDS, VC == C_ANY ? bits_of(vc) : bits_of(VC), ti.lo - 4 * kq, ti.valid - 4 * kq);
   }
 
   // group scales (and INT2 offsets) of this lane's four tokens (4 x NC fp16
@@ -571,7 +577,8 @@ __device__ __attribute__((always_inline)) inline void consume_tile(const Tile<D,
   uint32_t kz[T::KZ ? NC * 2 : 1], vz[T::VZ ? NC * 2 : 1];
   if constexpr (T::GS) {
     const int w = lane & 31;
-    const bool live = (2 * w) / NC < ti.valid;
+    const int tok = (2 * w) / NC;
+    const bool live = tok < ti.valid && tok >= ti.lo;
     // slot words 0..31 K scales, 32..63 V scales, 64..95 V offsets, 96..127 K offsets
     const uint32_t sk = T::KS ? t.sk[0] : 0u, sv = T::VS ? t.sv[0] : 0u;
     __builtin_amdgcn_wave_barrier();
@@ -662,7 +669,7 @@ __device__ __attribute__((always_inline)) inline void consume_tile(const Tile<D,
   }
   if (partial) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s[j] = (4 * kq + j < ti.valid) ? s[j] : NEG_INF;
+    for (int j = 0; j < 4; ++j) s[j] = (4 * kq + j < ti.valid && 4 * kq + j >= ti.lo) ? s[j] : NEG_INF;
   }
 
   // online softmax over this tile's 16 tokens (lanes col, col+16, col+32, col+48)
@@ -834,10 +841,18 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>(), max_waves_per_eu<D
   // Partitions are either a fixed number of tiles (tiles_per_part) or, with
   // tiles_per_part = 0, the row's tiles split evenly into nparts, so rows of
   // different lengths give workgroups of equal work.
+  // A sliding window keeps positions >= wlo; in dense mode the partitions
+  // start at its first tile (the branch keeps calls without a window from
+  // waiting for the row length before their table reads).
   const int tpp = P / 16;
   const int ntl = a.sparse ? npg * tpp : min(L / 16 + (L % 16 != 0), npg * tpp);
-  const int tpart = a.tiles_per_part > 0 ? a.tiles_per_part : max(1, (ntl + a.nparts - 1) / a.nparts);
-  const int t0 = part * tpart;
+  int wlo = 0, lo_tile = 0;
+  if (a.window > 0) {
+    wlo = __builtin_amdgcn_readfirstlane(max(L - a.window, 0));
+    if (!a.sparse) lo_tile = min(wlo / 16, ntl);
+  }
+  const int tpart = a.tiles_per_part > 0 ? a.tiles_per_part : max(1, (ntl - lo_tile + a.nparts - 1) / a.nparts);
+  const int t0 = lo_tile + part * tpart;
   const int t1 = min(t0 + tpart, ntl);
   // table entries the partition touches inside the row: [s0, s1)
   const int s0 = t0 / tpp;
@@ -883,12 +898,15 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>(), max_waves_per_eu<D
       d.k = 0; d.v = 0; d.sk = 1.f; d.sv = 1.f; d.valid = 0; d.codec = 0;
       if (ok && live) {
         const long long rem = (long long)L - (long long)lp * P;
+        const long long before = (long long)wlo - (long long)lp * P;  // slots before the window
+        const int lo = (int)(before < 0 ? 0 : (before > P ? P : before));
         d.valid = (int)(rem < 0 ? 0 : (rem > P ? P : rem));
+        d.valid = d.valid > lo ? d.valid : 0;  // a page wholly before the window is skipped
         d.k = ko;
         d.v = vo;
         if (kc == C_FP8) d.sk = sk;
         if (vc == C_FP8) d.sv = sv;
-        d.codec = cod;
+        d.codec = cod | (lo << 8);
       } else if (live && h == 0) {
         count_error(a.err);
       }

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(pkv.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pkv_abi_version() == 3
+    assert lib.pkv_abi_version() == 4
 
 
 def test_one_hip_runtime_in_process():
@@ -259,3 +259,20 @@ def test_noalloc_rejects_requests_beyond_its_scratch_on_the_host():
                                           None, None, fake, fake, None, None)
     assert st == pkv.ERR_SCRATCH
     assert "scratch" in pkv.status_string(st)
+
+
+def test_window_partitions_on_the_host():
+    """With a sliding window the partitions cover its tiles only: at most
+    ceil(W / 16) + 1 tiles per row (dense); sparse calls are unchanged; a
+    negative window is refused, as is a window given to the prefill."""
+    p = base(partition_tokens=2048, window_tokens=8192)            # 513 tiles in 128-tile partitions
+    assert pkv.num_partitions(p) == 5
+    assert pkv.workspace_bytes(p) == 16 * 5 * 130 * 4
+    assert pkv.num_partitions(base(partition_tokens=2048, window_tokens=10 ** 7)) == 512
+    sparse = base(rows=48, page_size=16, max_pages_per_row=16384, max_sel_pages=128, partition_tokens=256,
+                  window_tokens=100)
+    assert pkv.num_partitions(sparse) == 8
+    bad = base(window_tokens=-1)
+    lib = pkv.load()
+    assert lib.pkv_num_partitions(ctypes.byref(bad)) == pkv.ERR_INVALID_ARG
+    assert lib.pkv_prefill_num_partitions(ctypes.byref(base(window_tokens=16)), 4, 0, -1) == pkv.ERR_INVALID_ARG

@@ -484,3 +484,52 @@ def test_subbyte_v_codes_exact(codec, dim):
     out, _ = run(to_device(w), params_for(w, 0))
     ref, _ = oracle.decode_attention(w)
     assert np.array_equal(out, ref.astype(np.float32).astype(np.float64))
+
+
+# ------------------------------------------------------- sliding-window decode
+@pytest.mark.parametrize("kc,vc", [(FP8, FP8), (INT8, INT4), (None, None), (INT2, BIT1)])
+def test_sliding_window_decode(kc, vc):
+    """pkv_decode_attention with a sliding window: each row attends its last
+    W positions; the partitions cover only the window's tiles (fixed,
+    sub-page and even-split partitions), the window's first page and tile
+    are masked below its start, and rows shorter than W attend everything."""
+    print(f"case sliding-window decode ({kc},{vc})", flush=True)
+    cyc = [(FP16, FP16), (FP8, FP8), (INT8, INT4), (BF16, INT8), (INT2, INT2)]
+    codec_of = (lambda r, lp: cyc[(r + lp) % len(cyc)]) if kc is None else (lambda r, lp: (kc, vc))
+    w = poison_tails(small([1, 40, 300, 1000, 4097], kc, vc, hq=16, hkv=2, dim=128, page=32, codec_of=codec_of,
+                           seed=37, q_scale=2.0))
+    for W in (1, 15, 16, 17, 100, 333, 1000, 5000):
+        w.window_tokens = W
+        ref = oracle.decode_attention(w)
+        for T in (0, 64, 16):
+            p = params_for(w, T)
+            p.window_tokens = W
+            out, lse = run(to_device(w), p)
+            compare(out, lse, *ref, f"window {W} T={T}")
+
+
+def test_sliding_window_decode_sparse_and_partials():
+    """A window in sparse mode masks the selected pages' tokens before it
+    (pages wholly before it are skipped, not counted as errors); the
+    partials of a windowed dense call fold to the windowed result."""
+    print("case sliding-window sparse + partials", flush=True)
+    w = synth.config(4, small=True)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for W in (16, 700, 2000):
+        w.window_tokens = W
+        p = params_for(w)
+        p.window_tokens = W
+        out, lse = run(to_device(w), p, err=err)
+        compare(out, lse, *oracle.decode_attention(w), f"sparse window {W}")
+    assert int(err.item()) == 0
+    wd = small([3000, 900], FP8, FP8, hq=16, hkv=2, dim=128, page=64, seed=3)
+    wd.window_tokens = 1000
+    p = params_for(wd, 256)
+    p.window_tokens = 1000
+    assert pkv.num_partitions(p) == 4                      # ceil(1000 / 16) + 1 = 64 tiles in 16-tile partitions
+    dw = to_device(wd)
+    acc, ml = pkv.decode_partials(p, *dw.args())
+    out, lse = pkv.lse_combine(acc.view(-1, 4, 128), ml.view(-1, 4, 2))
+    torch.cuda.synchronize()
+    compare(out.view(2, 16, 128).cpu().numpy().astype(np.float64), lse.view(2, 16).cpu().numpy().astype(np.float64),
+            *oracle.decode_attention(wd), "windowed partials folded")

@@ -223,3 +223,22 @@ def test_partitions_over_256_pages(kc, vc):
     w = poison_tails(small([9000, 4096, 12001], kc, vc, hq=8, hkv=2, dim=128, page=16, seed=13))
     check(w, 5, partition_tokens=8192)
     check(w, 33, 4200, -1, partition_tokens=8192)
+
+
+@pytest.mark.parametrize("window", [1, 100, 4096])
+def test_sliding_window_decode_equals_prefill_t1(window):
+    """The decode path's sliding window and the prefill path's window at
+    T = 1 are two kernels for the same result."""
+    print(f"case decode vs prefill window={window}", flush=True)
+    w = poison_tails(small([40, 300, 5000], FP8, INT8, hq=16, hkv=2, dim=128, page=16))
+    q = synth.prefill_queries(4, w.rows, 1, w.num_q_heads, w.head_dim)
+    po, pl = run_prefill(w, q, window=window)
+    w.q = np.ascontiguousarray(q[:, 0])
+    w.window_tokens = window
+    p = params_for(w, 0)
+    p.window_tokens = window
+    out, lse = pkv.decode_attention(p, *to_device(w).args())
+    torch.cuda.synchronize()
+    do, dl = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(do - po[:, 0])) <= SPLIT_OUT_TOL and np.max(np.abs(dl - pl[:, 0])) <= SPLIT_LSE_TOL
+    compare(do, dl, *oracle.decode_attention(w), f"decode window {window}")
