@@ -238,6 +238,57 @@ def time_workload(torch, pkv, w, steps, warmup, min_rot_bytes):
     return res
 
 
+def time_window_decode(torch, pkv, w, steps, warmup, window=8192, positions=64):
+    """Sliding-window decode (T = 1) over the 1M-token FP8 cache: each row
+    attends its last `window` positions. Each step moves the row's end to
+    another of `positions` spots spread over the context (a different
+    seq_lens tensor), so consecutive steps read different pages and the
+    working set of a loop (positions x the window's bytes) exceeds the
+    last-level cache."""
+    import numpy as np
+    from synth.device import to_device
+    dw = to_device(w)
+    p = params_for(pkv, w)
+    p.partition_tokens = 0
+    p.window_tokens = window
+    L = int(w.seq_lens[0])
+    ends = np.linspace(window + 4096, L, positions).astype(np.int64)
+    lens = [torch.tensor([int(e)], dtype=torch.int32, device="cuda") for e in ends]
+    base = dw.args()
+    out = torch.empty((1, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((1, w.num_q_heads), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(pkv.workspace_bytes(p), 16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        args = list(base)
+        args[7] = lens[i % positions]
+        pkv.decode_attention(p, *args, out=out, lse=lse, workspace=ws, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = []
+    for _ in range(7):
+        t0.record(stream)
+        for i in range(steps):
+            step(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        reps.append(t0.elapsed_time(t1) / steps)
+    ms = float(np.median(reps))
+    eff = window * w.num_kv_heads * (2 * w.head_dim) + 2 * w.num_kv_heads * 4 * (window // w.page_size + 1)
+    res = {"workload": f"{w.name}_window_{window}", "window_tokens": window, "partitions": pkv.num_partitions(p),
+           "ms_per_step": ms, "steps_per_s": 1e3 / ms, "effective_kv_bytes": eff, "effective_gbps": eff / ms / 1e6,
+           "rotation": f"{positions} window positions over the context"}
+    log(f"{res['workload']}: {ms * 1e3:.1f} us/step ({res['partitions']} partitions, "
+        f"{res['effective_gbps']:.0f} GB/s of the window's codes and scales)")
+    del dw
+    torch.cuda.empty_cache()
+    return res
+
+
 def read_probe(torch):
     """Measured read ceilings on this device (libpkv_probe.so, outside the
     decode library): a linear non-temporal stream over 2 GiB, and 512 MiB of
@@ -717,6 +768,7 @@ def main():
     also = {}
     probe = None
     if not args.quick:
+        also["window_decode"] = time_window_decode(torch, pkv, w5, args.steps, args.warmup)
         for cid in (3, 4):
             log(f"generating {synth.NAMES[cid]}")
             w = synth.config(cid)

@@ -130,7 +130,10 @@ typedef struct pkv_params {
   int32_t num_q_heads;       /* Hq                                                      */
   int32_t num_kv_heads;      /* Hkv; Hq % Hkv == 0, G = Hq / Hkv <= 16                   */
   int32_t head_dim;          /* D: 64 or 128                                            */
-  int32_t page_size;         /* P tokens per page: a positive multiple of 16            */
+  int32_t page_size;         /* P tokens per page: a positive multiple of 16; P above
+                                2^20, or a 16-bit plane of 4 GiB or more
+                                (Hkv * P * D * 2 bytes), is PKV_ERR_UNSUPPORTED: the
+                                kernels address a plane with 32-bit offsets      */
   int32_t num_pages;         /* physical pages described by the page tables            */
   int32_t max_pages_per_row; /* row stride of block_table (entries), >= 1               */
   int32_t max_sel_pages;     /* 0: dense mode; > 0: sparse mode, row stride of page_sel */

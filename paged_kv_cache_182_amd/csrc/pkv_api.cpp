@@ -46,6 +46,13 @@ bool valid_codec(int32_t c) {
   return c == PKV_CODEC_MIXED || c == PKV_CODEC_MIXED_FLOAT || (c >= PKV_FP16 && c <= PKV_BIT1_G32);
 }
 
+// Whether one plane of a page (largest at 16 bits per code) stays below 4 GiB:
+// the kernels address a plane with 32-bit offsets.
+bool plane_fits32(const pkv_params* p) {
+  const uint64_t d = p->head_dim > 0 ? (uint64_t)p->head_dim : 0u;
+  return (uint64_t)p->num_kv_heads * (uint64_t)p->page_size * d * 2u < (1ull << 32);
+}
+
 // Checks the plain-value part of the params. Returns PKV_OK or an error.
 int check_params(const pkv_params* p) {
   if (!p) return PKV_ERR_INVALID_ARG;
@@ -57,6 +64,7 @@ int check_params(const pkv_params* p) {
   if (!isfinite(p->softmax_scale)) return PKV_ERR_INVALID_ARG;
   if (p->window_tokens < 0) return PKV_ERR_INVALID_ARG;
   if (p->page_size > (1 << 20)) return PKV_ERR_UNSUPPORTED;  // in-page slot counts are 24-bit on the device
+  if (!plane_fits32(p)) return PKV_ERR_UNSUPPORTED;
   if (!valid_codec(p->k_codec) || !valid_codec(p->v_codec)) return PKV_ERR_INVALID_ARG;
   if ((p->k_codec == PKV_CODEC_MIXED_FLOAT) != (p->v_codec == PKV_CODEC_MIXED_FLOAT)) return PKV_ERR_INVALID_ARG;
   if (p->head_dim != 64 && p->head_dim != 128) return PKV_ERR_UNSUPPORTED;
@@ -307,6 +315,7 @@ int check_write_params(const pkv_params* p) {
   if (p->page_size <= 0 || p->page_size % 16 != 0 || p->max_pages_per_row < 1) return PKV_ERR_INVALID_ARG;
   if (p->head_dim != 64 && p->head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (p->num_rows > 65535 || p->num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
+  if (p->page_size > (1 << 20) || !plane_fits32(p)) return PKV_ERR_UNSUPPORTED;
   return PKV_OK;
 }
 

@@ -59,17 +59,19 @@ constexpr int MAX_DESC = 256;  // page descriptors staged in LDS at a time
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr float LN2 = 0.693147180559945309f;
 
-__host__ __device__ constexpr int bits_of(int c) {
-  return c <= C_BF16 ? 16 : (c == C_INT4 ? 4 : (c == C_INT2 ? 2 : (c == C_BIT1 ? 1 : 8)));
-}
+// log2 of the code width, three bits per codec (FP16 and BF16 16 bits, FP8
+// and INT8 8, INT4 4, INT2 2, BIT1 1): a shift of one constant, where a chain
+// of compares on a codec known only at run time compiles to branches
+__host__ __device__ constexpr int lg_bits(int c) { return c < 0 ? 4 : (int)((0xa6e4u >> (3 * c)) & 7u); }
+__host__ __device__ constexpr int bits_of(int c) { return 1 << lg_bits(c); }
 // codecs with one fp16 scale per (token, 32 dims): INT8, INT4, INT2, BIT1
-__host__ __device__ constexpr bool is_int(int c) { return c == C_INT8 || c == C_INT4 || c == C_INT2 || c == C_BIT1; }
+__host__ __device__ constexpr bool is_int(int c) { return (unsigned)(c - C_INT8) <= (unsigned)(C_BIT1 - C_INT8); }
 // INT2 (unsigned affine) also holds one fp16 offset per (token, 32 dims)
 __host__ __device__ constexpr bool has_zero(int c) { return c == C_INT2; }
 
 // Bytes of one plane (codes of every head, then INT group scales).
 __host__ __device__ inline uint64_t plane_bytes(int c, int hkv, int page, int d) {
-  const uint64_t codes = (uint64_t)hkv * page * d * bits_of(c) / 8;
+  const uint64_t codes = ((uint64_t)hkv * page * (d / 8)) << lg_bits(c);
   const uint64_t groups = (uint64_t)hkv * page * (d / 32) * 2;
   return codes + (is_int(c) ? groups : 0) + (has_zero(c) ? groups : 0);
 }
@@ -108,6 +110,9 @@ struct Desc {
   int32_t valid;   // attended tokens of the page (0 if skipped): slots [lo, valid)
   int32_t codec;   // K codec | V codec << 4 | lo << 8, lo = leading slots before a sliding window
 };
+static_assert(sizeof(Desc) == 32 && offsetof(Desc, v) == 8 && offsetof(Desc, sk) == 16 && offsetof(Desc, valid) == 24 &&
+                  offsetof(Desc, codec) == 28,
+              "a descriptor is read as two 16-byte words");
 
 // Raw codes of one 16-token tile for one lane. Sizes per codec class; the
 // per-page dispatch variant (C_ANY) reserves the largest.
@@ -381,45 +386,66 @@ template <int KC>
 __host__ __device__ constexpr bool k_perm() {
   return KC != C_ANY && !is_int(KC);  // C_FLT: one-scale codecs only
 }
+// log2 code width of a page's codec in a kernel built for PC: the float
+// kernel's pages hold only FP16, BF16 or FP8 (one compare instead of the
+// table lookup).
+template <int PC>
+__device__ inline int lg_page(int codec) {
+  return PC == C_FLT ? (codec == C_FP8 ? 3 : 4) : lg_bits(PC == C_ANY ? codec : PC);
+}
+// Bytes of a page's plane (fits 32 bits: the host checks plane sizes).
+template <int PC, int D>
+__device__ inline uint32_t plane_bytes_page(int codec, int hkv, int page) {
+  if constexpr (PC == C_FLT) return (uint32_t)(hkv * page * (D / 8)) << lg_page<PC>(codec);
+  else return (uint32_t)plane_bytes(PC == C_ANY ? codec : PC, hkv, page, D);
+}
 // Byte offset of head h's codes inside a plane.
 template <int D>
 __device__ inline uint32_t head_off(int codec, int h, int page) {
-  return (uint32_t)(h * page * D * bits_of(codec) / 8);
+  return (uint32_t)(h * page * (D / 8)) << lg_bits(codec);
 }
 
 // The lane's run of a plane whose codec is known only at run time: the same
 // D/32 16-byte loads for every codec, branch-free, so the compiler's wait
 // counts stay exact across pages of different codecs. Loads past the run
 // (codes of 8 bits or fewer) read through an offset beyond the plane: zeros,
-// no traffic. A run of R < 16 bytes (R = D * bits / 32) is taken from the
-// 16-byte chunk that holds it (16 / R lanes per chunk, the same cache lines)
-// and moved to the first words.
-template <int D>
+// no traffic. A run of R < 16 bytes (R = D * bits / 32) arrives inside the
+// 16-byte chunk that holds it (16 / R lanes per chunk, the same cache lines);
+// short_run() moves it to the first words when the tile is consumed (doing it
+// here would wait for the loads just issued).
+template <int D, int PC>
 __device__ inline void load_run_any(uint32_t* w, rsrc_t r, int codec, int h, int page, int sub, int lane) {
   constexpr int NL = D / 32;  // 16-byte loads of a 16-bit run
-  const int bits = bits_of(codec);
-  const uint32_t head = (uint32_t)(h * page * D * bits / 8);
-  const uint32_t base = head + (uint32_t)sub * (uint32_t)(16 * D * bits / 8);
-  const int R = D * bits / 32;
-  const int nreal = R >= 16 ? R / 16 : 1;
+  const int lg = lg_page<PC>(codec);
+  const uint32_t head = (uint32_t)(h * page * (D / 8)) << lg;
+  const uint32_t base = head + ((uint32_t)sub * (uint32_t)(2 * D) << lg);
+  const int R = (D / 32) << lg;  // bytes of the lane's run
+  const int nreal = R >= 16 ? R >> 4 : 1;
   const uint32_t lane_off = R >= 16 ? 16u * (uint32_t)lane : 16u * (uint32_t)((lane * R) >> 4);
-  u4 first;
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const u4 x = bload16<CPOL_NT>(r, i < nreal ? base + 1024u * i + lane_off : OFF_NONE);
-    if (i == 0) first = x;
     w[4 * i + 0] = x[0]; w[4 * i + 1] = x[1]; w[4 * i + 2] = x[2]; w[4 * i + 3] = x[3];
   }
-  // short runs: pick the run's words out of the loaded vector (selects on
-  // register values; an index into the tile array would move the whole tile
-  // ring to scratch memory)
+}
+
+// Move a short run (R < 16 bytes) from its place in the loaded 16-byte chunk
+// to the first words: R = 8 at word 2 (odd lanes), R = 4 at word lane % 4,
+// R = 2 in half-word lane % 8 (then spread as a 16-bit unit). Selects on
+// register values only (an index into the tile array would move the tile
+// ring to scratch memory).
+template <int D>
+__device__ inline void short_run(uint32_t* w, int codec, int lane) {
+  const int R = (D / 32) << lg_bits(codec);
+  if (R >= 16) return;
+  const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
   if (R == 8) {
     const bool odd = lane & 1;
-    w[0] = odd ? first[2] : first[0];
-    w[1] = odd ? first[3] : first[1];
-  } else if (R < 8) {
+    w[0] = odd ? w2 : w0;
+    w[1] = odd ? w3 : w1;
+  } else {
     const int q = ((lane * R) & 15) >> 2;          // word of the chunk holding the run
-    const uint32_t lo = (q & 1) ? first[1] : first[0], hi = (q & 1) ? first[3] : first[2];
+    const uint32_t lo = (q & 1) ? w1 : w0, hi = (q & 1) ? w3 : w2;
     const uint32_t x = (q & 2) ? hi : lo;
     w[0] = R == 4 ? x : spread16((lane & 1) ? x >> 16 : x & 0xffffu);
   }
@@ -436,18 +462,23 @@ __device__ inline TileInfo issue_tile(Tile<D, KC, VC>& t, const Desc* desc, int 
   const int i = a.tile_shift >= 0 ? k >> a.tile_shift : k / tpp;
   const int sub = k - i * tpp;
   TileInfo ti;
-  const int codec = uni(desc[i].codec);
+  // the descriptor as two 16-byte LDS reads issued together (one wait)
+  const u4* dp = reinterpret_cast<const u4*>(desc + i);
+  const u4 d0 = dp[0], d1 = dp[1];
+  const int codec = uni((int)d1[3]);
   ti.lo = min(max((codec >> 8) - 16 * sub, 0), 16);
-  ti.valid = dead ? 0 : min(max(uni(desc[i].valid) - 16 * sub, 0), 16);
+  ti.valid = dead ? 0 : min(max(uni((int)d1[2]) - 16 * sub, 0), 16);
   ti.valid = ti.valid > ti.lo ? ti.valid : 0;  // wholly before the window: skip
   ti.kc = per_page(KC) ? (codec & 15) : KC;
   ti.vc = per_page(VC) ? ((codec >> 4) & 15) : VC;
-  ti.sk = unif(desc[i].sk);
-  ti.sv = unif(desc[i].sv);
+  ti.sk = __builtin_bit_cast(float, uni((int)d1[0]));
+  ti.sv = __builtin_bit_cast(float, uni((int)d1[1]));
+  const uint64_t koff = ((uint64_t)(uint32_t)uni((int)d0[1]) << 32) | (uint32_t)uni((int)d0[0]);
+  const uint64_t voff = ((uint64_t)(uint32_t)uni((int)d0[3]) << 32) | (uint32_t)uni((int)d0[2]);
   const bool live = ti.valid > 0;
   const int page = a.page;
-  const rsrc_t rk = make_rsrc(a.pool + uni64(desc[i].k), live ? (uint32_t)plane_bytes(ti.kc, a.hkv, page, D) : 0u);
-  const rsrc_t rv = make_rsrc(a.pool + uni64(desc[i].v), live ? (uint32_t)plane_bytes(ti.vc, a.hkv, page, D) : 0u);
+  const rsrc_t rk = make_rsrc(a.pool + koff, live ? plane_bytes_page<KC, D>(ti.kc, a.hkv, page) : 0u);
+  const rsrc_t rv = make_rsrc(a.pool + voff, live ? plane_bytes_page<VC, D>(ti.vc, a.hkv, page) : 0u);
   // group scales first: loads complete in order and the scores need them early
   if constexpr (Tile<D, KC, VC>::GS) {
     constexpr int NW = D / 4;  // words of one tile's scales (16 tokens x D/32 fp16)
@@ -457,23 +488,23 @@ __device__ inline TileInfo issue_tile(Tile<D, KC, VC>& t, const Desc* desc, int 
     const uint32_t zgap = (uint32_t)(a.hkv * page * (D / 32) * 2);
     const int hl = lane & 31;
     if constexpr (Tile<D, KC, VC>::KS) {
-      const uint32_t base = (uint32_t)(a.hkv * page * D * bits_of(ti.kc) / 8) + blk;
+      const uint32_t base = ((uint32_t)(a.hkv * page * (D / 8)) << lg_bits(ti.kc)) + blk;
       const bool want = lane < 32 ? is_int(ti.kc) : (Tile<D, KC, VC>::KZ && has_zero(ti.kc));
       t.sk[0] = bload4(rk, want && hl < NW ? base + (lane < 32 ? 0u : zgap) + 4 * hl : OFF_NONE);
     }
     if constexpr (Tile<D, KC, VC>::VS) {
-      const uint32_t base = (uint32_t)(a.hkv * page * D * bits_of(ti.vc) / 8) + blk;
+      const uint32_t base = ((uint32_t)(a.hkv * page * (D / 8)) << lg_bits(ti.vc)) + blk;
       const bool want = lane >= 32 ? is_int(ti.vc) : (Tile<D, KC, VC>::VZ && has_zero(ti.vc));
       t.sv[0] = bload4(rv, want && hl < NW ? base + (lane >= 32 ? 0u : zgap) + 4 * hl : OFF_NONE);
     }
   }
   if constexpr (per_page(KC)) {
-    load_run_any<D>(t.k, rk, ti.kc, h, page, sub, lane);
+    load_run_any<D, KC>(t.k, rk, ti.kc, h, page, sub, lane);
   } else {
     load_run<D, bits_of(KC)>(t.k, rk, head_off<D>(KC, h, page), sub, lane);
   }
   if constexpr (per_page(VC)) {
-    load_run_any<D>(t.v, rv, ti.vc, h, page, sub, lane);
+    load_run_any<D, VC>(t.v, rv, ti.vc, h, page, sub, lane);
   } else {
     load_run<D, bits_of(VC)>(t.v, rv, head_off<D>(VC, h, page), sub, lane);
   }
@@ -794,8 +825,15 @@ __device__ __attribute__((always_inline)) inline void consume(const Tile<D, KC, 
     if (ti.kc == C_BF16 && ti.vc == C_BF16)
       return consume_as<D, C_BF16, C_BF16>(t, ti, qv, qg, qsum, scale_log2, m_run, l_run, acc, lane);
   }
-  if constexpr (KC != C_FLT)
+  if constexpr (KC == C_ANY) {
+    // pages of codes shorter than 16 bytes per lane: the runs out of their chunks
+    Tile<D, KC, VC> u = t;
+    short_run<D>(u.k, ti.kc, lane);
+    short_run<D>(u.v, ti.vc, lane);
+    consume_tile<D, KC, VC>(u, ti, qv, qg, qsum, scale_log2, m_run, l_run, acc, sc, lane);
+  } else if constexpr (KC != C_FLT) {
     consume_tile<D, KC, VC>(t, ti, qv, qg, qsum, scale_log2, m_run, l_run, acc, sc, lane);
+  }
 }
 
 template <int D, int KC, int VC>
@@ -819,71 +857,93 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>(), max_waves_per_eu<D
   const int G = a.group;
   const int P = a.page;
 
-  // ---- extent of this row and of this partition (wave-uniform values)
-  int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
-  bool bad_row = L < 0;
-  L = L < 0 ? 0 : L;
-  int npg;
-  if (a.sparse) {
-    const int n = __builtin_amdgcn_readfirstlane(a.sel_lens[b]);
-    bad_row = bad_row || n < 0 || n > a.max_sel;
-    npg = min(max(n, 0), a.max_sel);
-  } else {
-    const int n = L / P + (L % P != 0);
-    bad_row = bad_row || n > a.max_pages;
-    npg = min(n, a.max_pages);
-  }
-  npg = __builtin_amdgcn_readfirstlane(npg);
+  // ---- row length and selection length: vector buffer loads. Scalar loads
+  // complete out of order, so a scalar load of the row length would make the
+  // first use of any kernel argument wait for it too; these are counted in
+  // order and waited for only where used.
+  const uint32_t len_raw = bload4(make_rsrc(reinterpret_cast<const uint8_t*>(a.seq_lens), (uint32_t)a.rows * 4u), 4u * b);
+  uint32_t sel_raw = 0;
+  if (a.sparse)
+    sel_raw = bload4(make_rsrc(reinterpret_cast<const uint8_t*>(a.sel_lens), (uint32_t)a.rows * 4u), 4u * b);
 
-  // ---- this partition's 16-token tiles [t0, t1) of the row. A row's tiles
-  // run through its pages (dense) or its selected pages in list order
-  // (sparse), tpp per page; only tiles that can hold attended tokens count.
-  // Partitions are either a fixed number of tiles (tiles_per_part) or, with
-  // tiles_per_part = 0, the row's tiles split evenly into nparts, so rows of
-  // different lengths give workgroups of equal work.
-  // A sliding window keeps positions >= wlo; in dense mode the partitions
-  // start at its first tile (the branch keeps calls without a window from
-  // waiting for the row length before their table reads).
+  // ---- extent of this row and of this partition (wave-uniform values).
+  // A row's 16-token tiles run through its pages (dense) or its selected
+  // pages in list order (sparse), tpp per page; only tiles that can hold
+  // attended tokens count. Partitions are either a fixed number of tiles
+  // (tiles_per_part) or, with tiles_per_part = 0, the row's tiles split
+  // evenly into nparts, so rows of different lengths give workgroups of
+  // equal work. A sliding window keeps positions >= wlo; in dense mode the
+  // partitions start at its first tile.
   const int tpp = P / 16;
-  const int ntl = a.sparse ? npg * tpp : min(L / 16 + (L % 16 != 0), npg * tpp);
-  int wlo = 0, lo_tile = 0;
-  if (a.window > 0) {
-    wlo = __builtin_amdgcn_readfirstlane(max(L - a.window, 0));
-    if (!a.sparse) lo_tile = min(wlo / 16, ntl);
-  }
+  int L = 0, npg = 0, ntl = 0, wlo = 0, lo_tile = 0;
+  bool bad_row = false;
+  auto extent = [&]() {
+    L = __builtin_amdgcn_readfirstlane((int)len_raw);
+    bad_row = L < 0;
+    L = L < 0 ? 0 : L;
+    if (a.sparse) {
+      const int n = __builtin_amdgcn_readfirstlane((int)sel_raw);
+      bad_row = bad_row || n < 0 || n > a.max_sel;
+      npg = min(max(n, 0), a.max_sel);
+    } else {
+      const int n = L / P + (L % P != 0);
+      bad_row = bad_row || n > a.max_pages;
+      npg = min(n, a.max_pages);
+    }
+    npg = __builtin_amdgcn_readfirstlane(npg);
+    ntl = a.sparse ? npg * tpp : min(L / 16 + (L % 16 != 0), npg * tpp);
+    if (a.window > 0) {
+      wlo = __builtin_amdgcn_readfirstlane(max(L - a.window, 0));
+      if (!a.sparse) lo_tile = min(wlo / 16, ntl);
+    }
+  };
+  // Fixed partitions without a window do not depend on the row length: their
+  // first chunk's table reads go out before it is known (they and the length
+  // reads then cost one round together); the others wait for it first.
+  const bool early = a.tiles_per_part > 0 && a.window <= 0;
+  if (!early) extent();
   const int tpart = a.tiles_per_part > 0 ? a.tiles_per_part : max(1, (ntl - lo_tile + a.nparts - 1) / a.nparts);
   const int t0 = lo_tile + part * tpart;
-  const int t1 = min(t0 + tpart, ntl);
-  // table entries the partition touches inside the row: [s0, s1)
-  const int s0 = t0 / tpp;
-  const int s1 = t1 > t0 ? (t1 + tpp - 1) / tpp : s0;
 
   // ---- page descriptors of this partition, MAX_DESC at a time. Entries run
-  // as far as the tables go; the row length (s1) may cut them shorter. With
-  // fixed-size partitions the first chunk is gathered before the row length
-  // is known and before q is read: its table reads go out at once, and every
-  // read of a chunk is issued before any result is checked, so the gather
-  // costs two dependent rounds (three with a selection); an even split waits
-  // for the row length first.
+  // as far as the tables go; the row length may cut them shorter. Every read
+  // of a chunk is issued before any result is checked, so the gather costs
+  // two dependent rounds (three with a selection).
+  const int s0 = t0 / tpp;
   const int s_lim = min((t0 + tpart + tpp - 1) / tpp, a.sparse ? a.max_sel : a.max_pages);
-  auto stage = [&](int cbase, int chunk) {
+  struct Raw {
+    int lp, pp, cod;
+    uint64_t ko, vo;
+    float sk, sv;
+  };
+  auto stage_issue = [&](int cbase, int chunk, Raw& r) {
     if (tid < chunk) {
       const int s = cbase + tid;
-      // reads (indices clamped into their tables; results checked below)
-      const int lp = a.sparse ? a.sel[(size_t)b * a.max_sel + s] : s;
-      const bool lp_ok = (unsigned)lp < (unsigned)a.max_pages;
-      const int pp = a.bt[(size_t)b * a.max_pages + (lp_ok ? lp : 0)];
-      const bool pp_ok = lp_ok && (unsigned)pp < (unsigned)a.num_pages;
-      const int pq = pp_ok ? pp : 0;
-      const int cod = a.codec[pq];
-      const uint64_t ko = a.koff[pq];
-      const uint64_t vo = a.voff[pq];
-      float sk = 1.f, sv = 1.f;
+      // reads (indices clamped into their tables; results checked later)
+      r.lp = a.sparse ? a.sel[(size_t)b * a.max_sel + s] : s;
+      const bool lp_ok = (unsigned)r.lp < (unsigned)a.max_pages;
+      r.pp = a.bt[(size_t)b * a.max_pages + (lp_ok ? r.lp : 0)];
+      const bool pp_ok = lp_ok && (unsigned)r.pp < (unsigned)a.num_pages;
+      const int pq = pp_ok ? r.pp : 0;
+      r.cod = a.codec[pq];
+      r.ko = a.koff[pq];
+      r.vo = a.voff[pq];
+      r.sk = 1.f;
+      r.sv = 1.f;
       if (a.scale != nullptr) {
-        sk = a.scale[((size_t)pq * a.hkv + h) * 2 + 0];
-        sv = a.scale[((size_t)pq * a.hkv + h) * 2 + 1];
+        r.sk = a.scale[((size_t)pq * a.hkv + h) * 2 + 0];
+        r.sv = a.scale[((size_t)pq * a.hkv + h) * 2 + 1];
       }
-      // checks
+    }
+  };
+  // s1: the end of the row's entries (a bad entry before it is an input error)
+  auto stage_check = [&](int cbase, int chunk, int s1, const Raw& r) {
+    if (tid < chunk) {
+      const int s = cbase + tid;
+      const bool lp_ok = (unsigned)r.lp < (unsigned)a.max_pages;
+      const bool pp_ok = lp_ok && (unsigned)r.pp < (unsigned)a.num_pages;
+      const int lp = r.lp, cod = r.cod;
+      const uint64_t ko = r.ko, vo = r.vo;
       const int kc = cod & 15, vc = cod >> 4;
       bool ok = pp_ok && kc <= C_LAST && vc <= C_LAST;
       if (KC == C_FLT && !(kc == vc && kc <= C_FP8)) ok = false;  // a float page, one codec for both planes
@@ -893,7 +953,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>(), max_waves_per_eu<D
       if ((ko | vo) & 15) ok = false;
       if (ok && (ko > a.pool_bytes || a.pool_bytes - ko < plane_bytes(kc, a.hkv, P, D))) ok = false;
       if (ok && (vo > a.pool_bytes || a.pool_bytes - vo < plane_bytes(vc, a.hkv, P, D))) ok = false;
-      const bool live = s < s1;  // inside the row: a bad entry here is an input error
+      const bool live = s < s1;
       Desc d;
       d.k = 0; d.v = 0; d.sk = 1.f; d.sv = 1.f; d.valid = 0; d.codec = 0;
       if (ok && live) {
@@ -904,8 +964,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>(), max_waves_per_eu<D
         d.valid = d.valid > lo ? d.valid : 0;  // a page wholly before the window is skipped
         d.k = ko;
         d.v = vo;
-        if (kc == C_FP8) d.sk = sk;
-        if (vc == C_FP8) d.sv = sv;
+        if (kc == C_FP8) d.sk = r.sk;
+        if (vc == C_FP8) d.sv = r.sv;
         d.codec = cod | (lo << 8);
       } else if (live && h == 0) {
         count_error(a.err);
@@ -915,7 +975,16 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>(), max_waves_per_eu<D
   };
   int cbase = s0;
   int chunk = min(MAX_DESC, s_lim - cbase);
-  if (chunk > 0) stage(cbase, chunk);
+  int s1, t1;
+  {
+    Raw raw = {};
+    if (chunk > 0) stage_issue(cbase, chunk, raw);
+    if (early) extent();
+    t1 = min(t0 + tpart, ntl);
+    // table entries the partition touches inside the row: [s0, s1)
+    s1 = t1 > t0 ? (t1 + tpp - 1) / tpp : s0;
+    if (chunk > 0) stage_check(cbase, chunk, s1, raw);
+  }
 
   // ---- q of this KV head's query group (B operand of the score MFMA), in
   // the dim order of the K runs: qv for one-scale codecs (and the per-page
@@ -933,6 +1002,7 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>(), max_waves_per_eu<D
         qg[c] = col < G ? *reinterpret_cast<const h8*>(qrow + 32 * c + 8 * kq) : h8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
+
 
   // query sums over each 32-dim group, for the offsets of INT2 K pages: the
   // lane's eight dims of the grouped order, then the four rows of its column.
@@ -1004,7 +1074,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>(), max_waves_per_eu<D
     chunk = min(MAX_DESC, s_lim - cbase);
     if (chunk <= 0) break;
     lds_barrier();  // every wave is done with the previous chunk
-    stage(cbase, chunk);
+    Raw raw = {};
+    stage_issue(cbase, chunk, raw);
+    stage_check(cbase, chunk, s1, raw);
   }
 
   // reported here, not where found, so that no wait on the row length sits

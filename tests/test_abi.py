@@ -90,12 +90,26 @@ def test_partitions_and_workspace():
     ("partition_tokens", 8, -1), ("partition_tokens", -16, -1),
     ("k_codec", -2, -1),   # the float class is declared for both planes or neither
     ("num_rows", -1, -1), ("max_pages_per_row", 0, -1), ("k_codec", 9, -1),
+    ("page_size", 1 << 21, -2),   # in-page slot counts are 24-bit on the device
 ])
 def test_bad_params_rejected(field, value, status):
     p = base()
     setattr(p, field, value)
     assert pkv.load().pkv_num_partitions(ctypes.byref(p)) == status
     assert pkv.workspace_bytes(p) == 0
+
+
+def test_planes_of_4_gib_rejected():
+    # one page's 16-bit plane of Hkv * P * D * 2 bytes is addressed with 32-bit offsets
+    lib = pkv.load()
+    big = base(num_q_heads=16, num_kv_heads=16, page_size=1 << 20, num_pages=1, max_pages_per_row=1)
+    assert 16 * (1 << 20) * 128 * 2 == 1 << 32
+    assert lib.pkv_num_partitions(ctypes.byref(big)) == -2
+    below = base(num_q_heads=8, num_kv_heads=8, page_size=1 << 20, num_pages=1, max_pages_per_row=1)
+    assert lib.pkv_num_partitions(ctypes.byref(below)) > 0
+    good = [4096] * 8
+    assert lib.pkv_append_kv(ctypes.byref(wbase(num_kv_heads=16, page_size=1 << 20)), *good, 0, 0) == -2
+    assert lib.pkv_append_kv(ctypes.byref(wbase(page_size=1 << 21)), *good, 0, 0) == -2
 
 
 def call(p, **ptrs):
