@@ -42,6 +42,8 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef short s4 __attribute__((ext_vector_type(4)));
 
 enum : int { C_FP16 = 0, C_BF16 = 1, C_FP8 = 2, C_INT8 = 3, C_INT4 = 4, C_INT2 = 5, C_BIT1 = 6, C_FLT = 14, C_ANY = 15 };
 constexpr int C_LAST = C_BIT1;  // highest codec id a page may hold
@@ -241,13 +243,6 @@ __device__ inline void load_run(uint32_t* w, rsrc_t r, uint32_t head, int sub, i
 // ---------------------------------------------------------------- decode
 __device__ inline h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
 
-// two bf16 -> two fp16 (exact inside fp16 range)
-__device__ inline h2 bf16x2(uint32_t w) {
-  float lo = __builtin_bit_cast(float, w << 16);
-  float hi = __builtin_bit_cast(float, w & 0xffff0000u);
-  return h2{(_Float16)lo, (_Float16)hi};
-}
-
 // two OCP e4m3 codes (bytes 0,1 or 2,3 of w) -> two fp16 (exact)
 template <bool HI>
 __device__ inline h2 fp8x2(uint32_t w) {
@@ -292,13 +287,12 @@ __device__ inline h2 b1pair(uint32_t w, int k) {
 }
 
 // A operand of the score MFMA: dims 32c + 8kq .. +7 of the lane's token.
+// (BF16 codes do not come here: they go to the bf16 MFMA as they are.)
 template <int C, int D>
 __device__ inline h8 k_frag(const uint32_t* w, int c) {
+  static_assert(C != C_BF16, "BF16 runs feed the bf16 MFMA");
   if constexpr (C == C_FP16) {
     return __builtin_bit_cast(h8, u4{w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]});
-  } else if constexpr (C == C_BF16) {
-    h2 a = bf16x2(w[4 * c]), b = bf16x2(w[4 * c + 1]), d = bf16x2(w[4 * c + 2]), e = bf16x2(w[4 * c + 3]);
-    return h8{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
   } else if constexpr (C == C_FP8) {
     h2 a = fp8x2<false>(w[2 * c]), b = fp8x2<true>(w[2 * c]);
     h2 d = fp8x2<false>(w[2 * c + 1]), e = fp8x2<true>(w[2 * c + 1]);
@@ -324,14 +318,12 @@ __device__ inline h8 k_frag(const uint32_t* w, int c) {
   }
 }
 
-// B operand of the P.V MFMA: tokens 4kq .. +3 of dim 16n + col.
+// B operand of the P.V MFMA: tokens 4kq .. +3 of dim 16n + col (16-bit runs:
+// FP16 as they are; BF16 runs go to the bf16 MFMA, the same words).
 template <int C, int D>
 __device__ inline h4 v_frag(const uint32_t* w, int n) {
-  if constexpr (C == C_FP16) {
+  if constexpr (C == C_FP16 || C == C_BF16) {
     return __builtin_bit_cast(h4, u2{w[2 * n], w[2 * n + 1]});
-  } else if constexpr (C == C_BF16) {
-    h2 a = bf16x2(w[2 * n]), b = bf16x2(w[2 * n + 1]);
-    return h4{a[0], a[1], b[0], b[1]};
   } else if constexpr (C == C_FP8) {
     h2 a = fp8x2<false>(w[n]), b = fp8x2<true>(w[n]);
     return h4{a[0], a[1], b[0], b[1]};
@@ -354,12 +346,12 @@ __device__ inline h4 v_frag(const uint32_t* w, int n) {
   }
 }
 
-// Runtime-dispatched variants for pages of mixed codecs.
+// Runtime-dispatched variants for pages of mixed codecs (BF16 runs are
+// taken before: they feed the bf16 MFMA).
 template <int D>
 __device__ inline h8 k_frag_any(const uint32_t* w, int c, int codec) {
   switch (codec) {
     case C_FP16: return k_frag<C_FP16, D>(w, c);
-    case C_BF16: return k_frag<C_BF16, D>(w, c);
     case C_FP8: return k_frag<C_FP8, D>(w, c);
     case C_INT8: return k_frag<C_INT8, D>(w, c);
     case C_INT4: return k_frag<C_INT4, D>(w, c);
@@ -371,7 +363,6 @@ template <int D>
 __device__ inline h4 v_frag_any(const uint32_t* w, int n, int codec) {
   switch (codec) {
     case C_FP16: return v_frag<C_FP16, D>(w, n);
-    case C_BF16: return v_frag<C_BF16, D>(w, n);
     case C_FP8: return v_frag<C_FP8, D>(w, n);
     case C_INT8: return v_frag<C_INT8, D>(w, n);
     case C_INT4: return v_frag<C_INT4, D>(w, n);
@@ -517,6 +508,42 @@ __device__ inline f4 mfma32(h8 a, h8 b, f4 c) {
 __device__ inline f4 mfma16(h4 a, h4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
+// The bf16 forms, for BF16 pages: their codes go in as they are, so values
+// of bf16's whole range (beyond fp16's 65504, below its 2^-24) stay exact.
+__device__ inline f4 mfma32_bf(u4 a, u4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, a), __builtin_bit_cast(bf8, b), c, 0, 0, 0);
+}
+__device__ inline f4 mfma16_bf(u2 a, u2 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), c, 0, 0, 0);
+}
+// Eight fp16 query values as bf16 high and low parts, x = hi + lo exactly:
+// hi keeps the top 8 of x's 11 significant bits (truncation), the rest, at
+// most 3 bits, is exact in bf16 (whose exponent range holds fp16's
+// subnormals); each products of a bf16 code with hi and with lo is exact.
+__device__ inline void bf_split8(h8 x, u4& hi, u4& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = (float)x[2 * i], b = (float)x[2 * i + 1];
+    const uint32_t ha = __builtin_bit_cast(uint32_t, a) & 0xffff0000u, hb = __builtin_bit_cast(uint32_t, b) & 0xffff0000u;
+    const uint32_t la = __builtin_bit_cast(uint32_t, a - __builtin_bit_cast(float, ha));
+    const uint32_t lb = __builtin_bit_cast(uint32_t, b - __builtin_bit_cast(float, hb));
+    hi[i] = __builtin_amdgcn_perm(hb, ha, 0x07060302u);
+    lo[i] = __builtin_amdgcn_perm(lb, la, 0x07060302u);
+  }
+}
+// Four fp32 softmax weights as bf16 high (truncated) and low (the remainder
+// rounded to nearest) parts: 16 significant bits, more than the fp16 weights
+// of the other one-scale codecs.
+__device__ inline void bf_split4(const float* p, u2& hi, u2& lo) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float a = p[2 * i], b = p[2 * i + 1];
+    const uint32_t ha = __builtin_bit_cast(uint32_t, a) & 0xffff0000u, hb = __builtin_bit_cast(uint32_t, b) & 0xffff0000u;
+    const __bf16 la = (__bf16)(a - __builtin_bit_cast(float, ha)), lb = (__bf16)(b - __builtin_bit_cast(float, hb));
+    hi[i] = __builtin_amdgcn_perm(hb, ha, 0x07060302u);
+    lo[i] = (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16);
+  }
+}
 
 // Max and sum over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows
 // that hold one column), with the row-swapping permutes of gfx950: swapping
@@ -585,7 +612,7 @@ __device__ inline void mask_v_run(uint32_t* v, int words, int bits, int a, int b
 // query head over dims 32c .. 32c + 31 (for INT2 K offsets).
 template <int D, int KC, int VC>
 __device__ __attribute__((always_inline)) inline void consume_tile(const Tile<D, KC, VC>& t, const TileInfo& ti, const h8* qv,
-                                    const h8* qg, const float* qsum, float scale_log2, float& m_run,
+                                    const h8* qg, const u4* qb, const float* qsum, float scale_log2, float& m_run,
                                     float& l_run, f4* acc, uint32_t* sc, int lane) {
   constexpr int NC = D / 32, NB = D / 16;
   using T = Tile<D, KC, VC>;
@@ -658,10 +685,20 @@ __device__ __attribute__((always_inline)) inline void consume_tile(const Tile<D,
   if (KC == C_ANY || is_int(KC)) {
     // one accumulator per 32-dim group, scaled per (token, group)
     f4 scg[NC];
+    if (KC == C_ANY && ti.kc == C_BF16) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      h8 kf = KC == C_ANY ? k_frag_any<D>(t.k, c, ti.kc) : k_frag<KC == C_ANY ? 0 : KC, D>(t.k, c);
-      scg[c] = mfma32(kf, (KC == C_ANY && kgrouped) ? qg[c] : qv[c], zero);
+      for (int c = 0; c < NC; ++c) {
+        u4 qh, ql;
+        bf_split8(qv[c], qh, ql);
+        const u4 kr = {t.k[4 * c], t.k[4 * c + 1], t.k[4 * c + 2], t.k[4 * c + 3]};
+        scg[c] = mfma32_bf(kr, ql, mfma32_bf(kr, qh, zero));
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        h8 kf = KC == C_ANY ? k_frag_any<D>(t.k, c, ti.kc) : k_frag<is_int(KC) ? KC : C_FP16, D>(t.k, c);
+        scg[c] = mfma32(kf, (KC == C_ANY && kgrouped) ? qg[c] : qv[c], zero);
+      }
     }
     if (kgrouped) {
       // the per-page kernel reads scales and offsets from the LDS slot where used (registers are short there)
@@ -690,6 +727,24 @@ __device__ __attribute__((always_inline)) inline void consume_tile(const Tile<D,
         s[j] = x * f;
       }
     }
+  } else if constexpr (KC == C_BF16) {
+    // the codes against the query's bf16 high and low parts
+    f4 acc_s = zero;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u4 qh, ql;
+      if (qb) {
+        qh = qb[c];
+        ql = qb[NC + c];
+      } else {
+        bf_split8(qv[c], qh, ql);
+      }
+      const u4 kr = {t.k[4 * c], t.k[4 * c + 1], t.k[4 * c + 2], t.k[4 * c + 3]};
+      acc_s = mfma32_bf(kr, ql, mfma32_bf(kr, qh, acc_s));
+    }
+    const float f = scale_log2 * ti.sk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[j] = acc_s[j] * f;
   } else {
     f4 acc_s = zero;
 #pragma unroll
@@ -773,6 +828,15 @@ __device__ __attribute__((always_inline)) inline void consume_tile(const Tile<D,
       for (int j = 0; j < 4; ++j) pa[g][j] = (_Float16)__builtin_fmaf(p[j], (float)v16[j * NC + g], 0.0f);
 #pragma unroll
     for (int n = 0; n < NB; ++n) acc[n] = mfma16(pa[n / 2], vfrag(n), acc[n]);
+  } else if (vc == C_BF16) {
+    // the codes against the weights' bf16 high and low parts
+    u2 ph, pl;
+    bf_split4(p, ph, pl);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const u2 vr = {vw[2 * n], vw[2 * n + 1]};
+      acc[n] = mfma16_bf(pl, vr, mfma16_bf(ph, vr, acc[n]));
+    }
   } else if (vc == C_FP8) {
     h4 hi, lo;
 #pragma unroll
@@ -805,7 +869,7 @@ __device__ __attribute__((always_inline)) inline void consume_as(const Tile<D, K
   for (int i = 0; i < Tile<D, K2, V2>::KW; ++i) u.k[i] = t.k[i];
 #pragma unroll
   for (int i = 0; i < Tile<D, K2, V2>::VW; ++i) u.v[i] = t.v[i];
-  consume_tile<D, K2, V2>(u, ti, qv, qg, qsum, scale_log2, m_run, l_run, acc, nullptr, lane);
+  consume_tile<D, K2, V2>(u, ti, qv, qg, nullptr, qsum, scale_log2, m_run, l_run, acc, nullptr, lane);
 }
 
 // Consume one tile. With codecs known only at run time, pages of the common
@@ -815,14 +879,16 @@ __device__ __attribute__((always_inline)) inline void consume_as(const Tile<D, K
 // gather skipped and counted them).
 template <int D, int KC, int VC>
 __device__ __attribute__((always_inline)) inline void consume(const Tile<D, KC, VC>& t, const TileInfo& ti, const h8* qv, const h8* qg,
-                               const float* qsum, float scale_log2, float& m_run, float& l_run, f4* acc,
-                               uint32_t* sc, int lane) {
+                               const u4* qb, const float* qsum, float scale_log2, float& m_run, float& l_run,
+                               f4* acc, uint32_t* sc, int lane) {
   if constexpr ((KC == C_ANY && VC == C_ANY) || (KC == C_FLT && VC == C_FLT)) {
     if (ti.kc == C_FP8 && ti.vc == C_FP8)
       return consume_as<D, C_FP8, C_FP8>(t, ti, qv, qg, qsum, scale_log2, m_run, l_run, acc, lane);
     if (ti.kc == C_FP16 && ti.vc == C_FP16)
       return consume_as<D, C_FP16, C_FP16>(t, ti, qv, qg, qsum, scale_log2, m_run, l_run, acc, lane);
-    if (ti.kc == C_BF16 && ti.vc == C_BF16)
+    // (BF16 pages of the any-codec kernel take its generic path, which feeds
+    // BF16 planes to the bf16 MFMA: one copy of that code fewer)
+    if (KC == C_FLT && ti.kc == C_BF16 && ti.vc == C_BF16)
       return consume_as<D, C_BF16, C_BF16>(t, ti, qv, qg, qsum, scale_log2, m_run, l_run, acc, lane);
   }
   if constexpr (KC == C_ANY) {
@@ -830,9 +896,9 @@ __device__ __attribute__((always_inline)) inline void consume(const Tile<D, KC, 
     Tile<D, KC, VC> u = t;
     short_run<D>(u.k, ti.kc, lane);
     short_run<D>(u.v, ti.vc, lane);
-    consume_tile<D, KC, VC>(u, ti, qv, qg, qsum, scale_log2, m_run, l_run, acc, sc, lane);
+    consume_tile<D, KC, VC>(u, ti, qv, qg, nullptr, qsum, scale_log2, m_run, l_run, acc, sc, lane);
   } else if constexpr (KC != C_FLT) {
-    consume_tile<D, KC, VC>(t, ti, qv, qg, qsum, scale_log2, m_run, l_run, acc, sc, lane);
+    consume_tile<D, KC, VC>(t, ti, qv, qg, qb, qsum, scale_log2, m_run, l_run, acc, sc, lane);
   }
 }
 
@@ -1024,6 +1090,14 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>(), max_waves_per_eu<D
   }
   const float* const qsum = KC == C_ANY ? qsum_lds + (wave * 16 + col) * NC : qsum_reg;
 
+  // the BF16 kernel's query as bf16 high and low parts, once (the per-page
+  // kernels split it for their BF16 pages as they come)
+  u4 qb[KC == C_BF16 ? 2 * NC : 1];
+  if constexpr (KC == C_BF16) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) bf_split8(qv[c], qb[c], qb[NC + c]);
+  }
+
   float m_run = NEG_INF, l_run = 0.f;
   f4 acc[NB];
 #pragma unroll
@@ -1061,7 +1135,8 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>(), max_waves_per_eu<D
           // past the end: same loads through a zero-size resource (no traffic)
           inf[nx] = issue_tile<D, KC, VC>(t[nx], desc, min(kn, klast), tpp, a, h, lane, kn > klast);
           if (it + s < nmine && inf[s].valid > 0)
-            consume<D, KC, VC>(t[s], inf[s], qv, qg, qsum, a.scale_log2, m_run, l_run, acc, sc, lane);
+            consume<D, KC, VC>(t[s], inf[s], qv, qg, KC == C_BF16 ? qb : nullptr, qsum, a.scale_log2, m_run, l_run,
+                               acc, sc, lane);
         }
       }
     }

@@ -276,6 +276,21 @@ __device__ inline u4 convert(u4 raw, uint32_t off, int codec) {
   else return to_h8_c<C>(select_bytes(raw, off, bits_of(C)));
 }
 
+// Whether the fp16 image words of eight bf16 codes (a 16-bit run: the raw
+// words themselves) hold their values unchanged: a value past fp16's 65504,
+// or finer than its subnormal step, does not come back.
+__device__ inline bool bf16_kept(u4 codes, u4 img) {
+  bool ok = true;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const h2 x = as_h2(img[k]);
+    const uint32_t back = (__builtin_bit_cast(uint32_t, (float)x[0]) >> 16) |
+                          (__builtin_bit_cast(uint32_t, (float)x[1]) & 0xffff0000u);
+    ok = ok && back == codes[k];
+  }
+  return ok;
+}
+
 // Zero the V values of tokens past the row (their bytes may be anything): run
 // element e = 8c + i of lane L holds token 4(L/16) + i%4; word k holds
 // elements 2k and 2k+1.
@@ -314,7 +329,7 @@ __device__ inline void stage_scales(const Raw<D>& raw, const TileMeta& m, float*
 // holds the same jobs of both tiles, so it writes the interleaved V operand.
 template <int D, int KC, int VC>
 __device__ inline void produce_pair(const Raw<D>& ra, const Raw<D>& rb, const TileMeta& ma, const TileMeta& mb,
-                                    PairStage<D>& st, int wave, int lane) {
+                                    PairStage<D>& st, int wave, int lane, bool& lost) {
   constexpr int NC = D / 32;
 #pragma unroll
   for (int q = 0; q < Raw<D>::JOBS; ++q) {
@@ -324,11 +339,22 @@ __device__ inline void produce_pair(const Raw<D>& ra, const Raw<D>& rb, const Ti
     if (is_v) {
       const u4 xa = mask_v_tail(convert<VC>(ra.x[q], ra.off[q], ma.vc), ma.valid, lane);
       const u4 xb = mask_v_tail(convert<VC>(rb.x[q], rb.off[q], mb.vc), mb.valid, lane);
+      if constexpr (VC == C_BF16 || VC == C_ANY) {
+        // values of tokens inside the row (the tails are zero on both sides)
+        if ((VC == C_BF16 || ma.vc == C_BF16) && !bf16_kept(mask_v_tail(ra.x[q], ma.valid, lane), xa)) lost = true;
+        if ((VC == C_BF16 || mb.vc == C_BF16) && !bf16_kept(mask_v_tail(rb.x[q], mb.valid, lane), xb)) lost = true;
+      }
       st.v[2 * c][lane] = u4{xa[0], xa[1], xb[0], xb[1]};
       st.v[2 * c + 1][lane] = u4{xa[2], xa[3], xb[2], xb[3]};
     } else {
-      st.k[0][64 * c + lane] = convert<KC>(ra.x[q], ra.off[q], ma.kc);
-      st.k[1][64 * c + lane] = convert<KC>(rb.x[q], rb.off[q], mb.kc);
+      const u4 ka = convert<KC>(ra.x[q], ra.off[q], ma.kc), kb = convert<KC>(rb.x[q], rb.off[q], mb.kc);
+      st.k[0][64 * c + lane] = ka;
+      st.k[1][64 * c + lane] = kb;
+      if constexpr (KC == C_BF16 || KC == C_ANY) {
+        // the lane's token (lane % 16), when it lies inside the row
+        if ((KC == C_BF16 || ma.kc == C_BF16) && (lane & 15) < ma.valid && !bf16_kept(ra.x[q], ka)) lost = true;
+        if ((KC == C_BF16 || mb.kc == C_BF16) && (lane & 15) < mb.valid && !bf16_kept(rb.x[q], kb)) lost = true;
+      }
     }
   }
   if constexpr (KC == C_ANY || VC == C_ANY || is_int(KC) || is_int(VC)) {
@@ -587,7 +613,9 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
         const TileMeta mA = mt[2 * s], mB = mt[2 * s + 1];
         // unconditional: a dead tile converts zeros that are never read, and the
         // ring registers are always consumed before they are loaded again
-        produce_pair<D, KC, VC>(raw[2 * s], raw[2 * s + 1], mA, mB, st, wave, lane);
+        bool lost = false;
+        produce_pair<D, KC, VC>(raw[2 * s], raw[2 * s + 1], mA, mB, st, wave, lane, lost);
+        if (lost && reporter) ++nerr;  // a BF16 value outside fp16's range
         mt[2 * s] = meta(i + 2 * PAIR_RING);
         issue<D>(raw[2 * s], mt[2 * s], a, h, wave, lane);
         mt[2 * s + 1] = meta(i + 2 * PAIR_RING + 1);

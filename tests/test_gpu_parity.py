@@ -533,3 +533,95 @@ def test_sliding_window_decode_sparse_and_partials():
     torch.cuda.synchronize()
     compare(out.view(2, 16, 128).cpu().numpy().astype(np.float64), lse.view(2, 16).cpu().numpy().astype(np.float64),
             *oracle.decode_attention(wd), "windowed partials folded")
+
+
+# ------------------------------------------------ BF16 over its whole range
+def rewrite_bf16(w, make):
+    """Replace the values of every BF16 plane with ``make(row, lp, is_v)``
+    (float32 [Hkv, P, D]), encoded as the layout prescribes; other planes
+    keep their bytes."""
+    from synth.layout import encode_plane
+    arr = w.pool.as_array()
+    P, D, hkv = w.page_size, w.head_dim, w.num_kv_heads
+    for r in range(w.rows):
+        for lp in range(-(-int(w.seq_lens[r]) // P)):
+            pp = int(w.block_table[r, lp])
+            code = int(w.page_codec[pp])
+            for is_v, codec, off in ((False, code & 15, int(w.page_k_off[pp])), (True, code >> 4, int(w.page_v_off[pp]))):
+                if codec != BF16:
+                    continue
+                x = make(r, lp, is_v).astype(np.float32).reshape(1, hkv, P, D)
+                b, _ = encode_plane(x, BF16, v_order=is_v)
+                arr[off:off + b.shape[1]] = b[0]
+
+
+def vmax_per_row(w):
+    """Largest |V| each (row, query head) attends, from the decoded pages."""
+    from oracle.attention import gather_kv
+    G = w.num_q_heads // w.num_kv_heads
+    m = np.zeros((w.rows, w.num_q_heads))
+    for r in range(w.rows):
+        for hk in range(w.num_kv_heads):
+            _, v = gather_kv(w, r, hk)
+            if v.size:
+                m[r, hk * G:(hk + 1) * G] = np.max(np.abs(v))
+    return m
+
+
+def test_bf16_beyond_fp16_range():
+    """BF16 codes go to the bf16 MFMA as they are: values past fp16's 65504
+    and below its 2^-24 stay exact. Rows: N(0,1) with 5% outliers x 1e5 (q x
+    1e-4, scores of order one); K and V near 1e-30; K near 1e6 against q
+    near 1e-6 (fp16 subnormals; scores again of order one). Bound on out: the weights keep 16
+    significant bits (2^-16 relative) and every product is exact, so the
+    error is below 2^-16 of the largest |V| a row attends plus fp32 rounding:
+    3e-5 x that maximum, and 1e-3 absolute on top for rows of values near
+    one. LSE: scores of order one, 1e-4 as everywhere. Each page class runs:
+    the BF16 kernel, the float per-page kernel and the any-codec kernel."""
+    print("case bf16 full range", flush=True)
+    w = small([700, 333, 1024, 17], BF16, BF16, hq=8, hkv=2, dim=128, page=64, seed=21)
+    rng = np.random.default_rng(8)
+
+    def make(r, lp, is_v):
+        x = rng.standard_normal((w.num_kv_heads, w.page_size, w.head_dim)).astype(np.float32)
+        if r == 0:
+            big = rng.random(x.shape) < 0.05
+            return np.where(big, x * 1e5, x)
+        if r == 1:
+            return x * 1e-30
+        if r == 2:
+            return x * 1e6 if not is_v else x
+        return x * 3e4
+    rewrite_bf16(w, make)
+    qs = np.array([1e-4, 1.0, 1e-6, 1e-4], dtype=np.float32)
+    w.q = (w.q.astype(np.float32) * qs[:, None, None]).astype(np.float16)
+    assert np.all(np.isfinite(w.q.astype(np.float32))) and np.count_nonzero(w.q[2]) > w.q[2].size // 2
+    ref_out, ref_lse = oracle.decode_attention(w)
+    assert np.all(np.isfinite(ref_out)) and np.all(np.isfinite(ref_lse))
+    tol = 3e-5 * vmax_per_row(w)[:, :, None] + np.where(np.arange(w.rows) == 1, 0.0, 1e-3)[:, None, None]
+    dw = to_device(w)
+    for kc in (BF16, pkv.CODEC_MIXED_FLOAT, pkv.CODEC_MIXED):
+        o, l = run(dw, params_for(w, 256, k_codec=kc, v_codec=kc))
+        err = np.abs(o - ref_out)
+        print(f"bf16 range kernel {kc}: out err / tol max {float(np.max(err / tol)):.3f}, "
+              f"lse max-abs {float(np.max(np.abs(l - ref_lse))):.3e}", flush=True)
+        assert np.all(np.isfinite(o)) and np.all(err <= tol), f"kernel {kc}"
+        assert float(np.max(np.abs(l - ref_lse))) <= 1e-4
+        # row 1 (values near 1e-30) is not flushed: its outputs match to 1e-4 relative
+        assert np.max(np.abs(o[1] - ref_out[1])) <= 1e-4 * np.max(np.abs(ref_out[1]))
+
+
+def test_bf16_planes_beside_other_codecs():
+    """The any-codec kernel with BF16 on one plane only: K BF16 / V FP8 and
+    K INT8 / V BF16 pages, values past fp16's range on the BF16 planes."""
+    print("case bf16 mixed pairs", flush=True)
+    w = small([900, 400], None, None, hq=16, hkv=2, dim=128, page=16, seed=5,
+              codec_of=lambda r, lp: (BF16, FP8) if (r + lp) % 2 else (INT8, BF16))
+    rng = np.random.default_rng(9)
+    rewrite_bf16(w, lambda r, lp, is_v: rng.standard_normal((2, 16, 128)).astype(np.float32) * (1e5 if is_v else 2e5))
+    w.q = (w.q.astype(np.float32) * 1e-5).astype(np.float16)
+    ref_out, ref_lse = oracle.decode_attention(w)
+    o, l = run(to_device(w), params_for(w, 128))
+    tol = 3e-5 * vmax_per_row(w)[:, :, None] + 1e-3
+    assert np.all(np.isfinite(o)) and np.all(np.abs(o - ref_out) <= tol)
+    assert float(np.max(np.abs(l - ref_lse))) <= 1e-4

@@ -242,3 +242,25 @@ def test_sliding_window_decode_equals_prefill_t1(window):
     do, dl = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
     assert np.max(np.abs(do - po[:, 0])) <= SPLIT_OUT_TOL and np.max(np.abs(dl - pl[:, 0])) <= SPLIT_LSE_TOL
     compare(do, dl, *oracle.decode_attention(w), f"decode window {window}")
+
+
+def test_bf16_beyond_fp16_range_is_counted():
+    """The prefill kernel stages BF16 codes as fp16 images: a value that image
+    cannot hold (here outliers x 1e6, past 65504) counts as a device-visible
+    problem; the same pages without the outliers count none (checked in
+    every BF16 case above, tails poisoned or not)."""
+    print("case prefill bf16 range", flush=True)
+    q = synth.prefill_queries(3, 2, 4, 8, 128, 1.0)
+    for kc, vc in ((BF16, BF16), (BF16, FP8), (INT8, BF16)):
+        w = small([300, 200], kc, vc, hq=8, hkv=2, dim=128, page=16, seed=4, outlier_frac=0.01, outlier_mult=1e6)
+        dw = to_device(w)
+        for pk in ({}, {"k_codec": pkv.CODEC_MIXED, "v_codec": pkv.CODEC_MIXED}):
+            p = params_for(w, 0, **pk)
+            err = torch.zeros(1, dtype=torch.int32, device="cuda")
+            pkv.prefill_attention(p, torch.from_numpy(q).cuda(), dw.pool, dw.page_k_off, dw.page_v_off, dw.page_codec,
+                                  dw.page_scale, dw.block_table, dw.seq_lens, err_count=err)
+            torch.cuda.synchronize()
+            print(f"prefill bf16 range {kc}/{vc} {pk}: {int(err.item())} counted", flush=True)
+            assert int(err.item()) > 0
+        w0 = small([300, 200], kc, vc, hq=8, hkv=2, dim=128, page=16, seed=4)
+        run_prefill(w0, q, expect_err=0)
