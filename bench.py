@@ -124,6 +124,32 @@ def total_bytes(w, nparts, eff):
     return int(eff + tables + io + partials)
 
 
+SETTLE_MS = 50.0
+
+
+def settle_device(torch, ms=SETTLE_MS):
+    """Keep the device busy with plain 256 MiB copies for about `ms` before any
+    timing. Under a sudden load the MI355X runs a transient of a few
+    milliseconds (measured: with 5 warm-up steps the timed 1M blocks swing
+    from 96 to 105 us, with 100 they hold at 94.5 us); this passes it without
+    touching the workload, its steps or their count. Not a decode step: it
+    reads and writes a scratch buffer only."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    spent, n = 0.0, 0
+    while spent < ms:
+        t0.record()
+        for _ in range(8):
+            dst.copy_(src)
+        t1.record()
+        torch.cuda.synchronize()
+        spent += t0.elapsed_time(t1)
+        n += 8
+    del src, dst
+    log(f"device settled: {n} copies of {COPY_BYTES >> 20} MiB in {spent:.0f} ms")
+
+
 def time_workload(torch, pkv, w, steps, warmup, min_rot_bytes):
     import numpy as np
     from synth import effective_kv_bytes_formula
@@ -155,6 +181,7 @@ def time_workload(torch, pkv, w, steps, warmup, min_rot_bytes):
     assert int(err.item()) == 0, "device-visible input errors"
     assert bool(torch.isfinite(out).all()), "non-finite output"
 
+    settle_device(torch)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
