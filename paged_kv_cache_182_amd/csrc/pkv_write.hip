@@ -478,6 +478,15 @@ __device__ inline float recip_fp16_scale(float s) {
   return __builtin_fmaf(r0, __builtin_fmaf(-s, r0, 1.0f), r0);
 }
 
+// INT2 code u = clip(rint(RN((x - z) / s)), 0, 3) with the division as
+// recip_div by r = RN(1 / s): for an fp16 step s the corrected quotient is
+// RN(d / s) for every fp32 d, which tests/division/check_affine2_div.c checks
+// for every step over every dividend near the rounding boundaries.
+__device__ inline uint32_t affine2_code_r(float x, float z, float st, float r) {
+  const float q = __builtin_rintf(recip_div(x - z, st, r));
+  return (uint32_t)(int)fminf(fmaxf(q, 0.0f), 3.0f);
+}
+
 // ------------------------------------------------------ encode, register path
 // Pages of up to four tiles (P <= 64): one wave per unit (page pair, KV head,
 // plane), units dealt round-robin over the waves of the grid. The wave holds
@@ -505,21 +514,130 @@ __device__ inline float row16_max(float x) {
   x = fmaxf(x, dpp_f(x, 0x141));
   return fmaxf(x, dpp_f(x, 0x140));
 }
-// max over lanes l, l^16, l^32, l^48
-__device__ inline float rows4_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+
+// ---- many reductions at once over the 16 lanes of a row (reduce-scatter)
+// A lane holds one value per combo. A step pairs lanes whose index differs in
+// one bit b (the row mirror pairs l and 15 - l, the half-row mirror l and
+// 7 - l inside each 8 lanes, the quad permutes l ^ 2 and l ^ 1) and each lane
+// keeps, combined with its partner's copy, the half of its combos whose bit b
+// equals its own: N combos over 16 lanes take N - 1 exchanges instead of
+// 4 N, and lane l ends with combo l.
+template <int CTRL>
+__device__ inline uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
 }
-__device__ inline float row16_min(float x) { return -row16_max(-x); }
-__device__ inline float rows4_min(float x) { return -rows4_max(-x); }
-// exact float64 sums (of 16-bit magnitudes) over the same lane sets
-__device__ inline double row16_sum(double x) {
-  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o);
+template <int CTRL>
+__device__ inline double dpp_d(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint64_t lo = dpp_u<CTRL>((uint32_t)u), hi = dpp_u<CTRL>((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, lo | (hi << 32));
+}
+template <int CTRL>
+__device__ inline uint32_t dpp_any(uint32_t x) { return dpp_u<CTRL>(x); }
+template <int CTRL>
+__device__ inline double dpp_any(double x) { return dpp_d<CTRL>(x); }
+
+// one step on v[0 .. N): v[k] for k < N / 2 becomes op(kept, partner's copy)
+// of combo k + N/2 (keep_hi) or k
+template <int CTRL, int N, class T, class Op>
+__device__ inline void halve(T* v, bool keep_hi, Op op) {
+#pragma unroll
+  for (int k = 0; k < N / 2; ++k) {
+    const T lo = v[k], hi = v[k + N / 2];
+    const T keep = keep_hi ? hi : lo, send = keep_hi ? lo : hi;
+    v[k] = op(keep, dpp_any<CTRL>(send));
+  }
+}
+// N = 16 or 8 combos (index = the lane that keeps it); returns combo l16's
+// reduction over the row (lanes l16 >= N hold a copy of combo l16 % N's).
+template <int N, class T, class Op>
+__device__ inline T row16_scatter(T (&v)[N], int l16, Op op) {
+  static_assert(N == 8 || N == 16, "8 or 16 combos");
+  if constexpr (N == 16) {
+    halve<0x140, 16>(v, (l16 & 8) != 0, op);  // row mirror: partners differ in bit 3
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = op(v[k], dpp_any<0x140>(v[k]));  // both halves of the row
+  }
+  halve<0x141, 8>(v, (l16 & 4) != 0, op);  // half-row mirror: bit 2 (bit 3 kept)
+  halve<0x4E, 4>(v, (l16 & 2) != 0, op);   // quad [2,3,0,1]: bit 1
+  halve<0xB1, 2>(v, (l16 & 1) != 0, op);   // quad [1,0,3,2]: bit 0
+  return v[0];
+}
+
+// The same for combos held two to a 32-bit word (combo 2w in the low half of
+// word w, 2w + 1 in the high half), combined by a packed operation: returns
+// the 16-bit reduction of combo l16 (N = 16 or 8 combos).
+template <int N, class Op>
+__device__ inline uint32_t row16_scatter_pairs(uint32_t (&w)[N / 2], int l16, Op op) {
+  static_assert(N == 8 || N == 16, "8 or 16 combos");
+  if constexpr (N == 16) {
+    halve<0x140, 8>(w, (l16 & 8) != 0, op);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = op(w[k], dpp_u<0x140>(w[k]));
+  }
+  halve<0x141, 4>(w, (l16 & 4) != 0, op);
+  halve<0x4E, 2>(w, (l16 & 2) != 0, op);
+  const uint32_t r = op(w[0], dpp_u<0xB1>(w[0]));  // both halves over the whole row
+  return (l16 & 1) ? r >> 16 : r & 0xffffu;
+}
+
+// Order-preserving signed 16-bit key of a 16-bit float's bits (FP16 or BF16:
+// sign and magnitude): larger values give larger keys; and back.
+__device__ inline uint32_t key16(uint32_t u) { return (u & 0x8000u) ? (u ^ 0x7FFFu) : u; }
+__device__ inline uint32_t unkey16(uint32_t k) { k &= 0xFFFFu; return (k & 0x8000u) ? (k ^ 0x7FFFu) : k; }
+template <bool BF>
+__device__ inline float bits16_to_float(uint32_t u) {
+  if constexpr (BF) return __builtin_bit_cast(float, u << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)u);
+}
+__device__ inline uint32_t pk_max_i16(uint32_t a, uint32_t b) {
+  typedef short s2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s2, a), __builtin_bit_cast(s2, b)));
+}
+// bits of element i (0..7) of a 16-byte chunk of 16-bit codes
+__device__ inline uint32_t chunk_bits(const u4& x, int i) {
+  const uint32_t w = x[i >> 1];
+  return (i & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// max (and exact float64 sums of 16-bit magnitudes) over lanes l, l^16, l^32,
+// l^48 by the row swaps of gfx950 (no LDS)
+template <int ROWS>
+__device__ inline void swap_rows_u(uint32_t x, uint32_t& a, uint32_t& b) {
+  if constexpr (ROWS == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    a = r[0]; b = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    a = r[0]; b = r[1];
+  }
+  asm volatile("" : "+v"(a), "+v"(b));
+}
+__device__ inline float rows4_max_sw(float x) {
+  uint32_t a, b;
+  swap_rows_u<16>(__builtin_bit_cast(uint32_t, x), a, b);
+  x = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  swap_rows_u<32>(__builtin_bit_cast(uint32_t, x), a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ inline double rows4_sum_sw(double x) {
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    uint32_t la, lb, ha, hb;
+    if (r == 0) {
+      swap_rows_u<16>((uint32_t)u, la, lb);
+      swap_rows_u<16>((uint32_t)(u >> 32), ha, hb);
+    } else {
+      swap_rows_u<32>((uint32_t)u, la, lb);
+      swap_rows_u<32>((uint32_t)(u >> 32), ha, hb);
+    }
+    x = __builtin_bit_cast(double, (uint64_t)la | ((uint64_t)ha << 32)) +
+        __builtin_bit_cast(double, (uint64_t)lb | ((uint64_t)hb << 32));
+  }
   return x;
-}
-__device__ inline double rows4_sum(double x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
 }
 
 // element i (0..7) of a 16-byte chunk of 16-bit codes (BF16 or FP16), as float
@@ -600,7 +718,7 @@ __device__ inline void store_run(const u4* x, const float (*s2)[D / 32], const f
       } else if constexpr (DC == W_BF16) {
         code = f_to_bf16(v);
       } else if constexpr (DC == W_INT2) {
-        code = affine2_code(v, z2[e & 3][e >> 3], s2[e & 3][e >> 3]);
+        code = affine2_code_r(v, z2[e & 3][e >> 3], s2[e & 3][e >> 3], r2[e & 3][e >> 3]);
       } else if constexpr (DC == W_BIT1) {
         code = v < 0.f ? 1u : 0u;
       } else {
@@ -690,7 +808,7 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
             for (int c = 0; c < NC; ++c)
 #pragma unroll
               for (int k = 0; k < 8; ++k) m = fmaxf(m, __builtin_fabsf(chunk_elem<BF>(cur.x[t][c], k)));
-          m = rows4_max(row16_max(m));
+          m = rows4_max_sw(row16_max(m));
           s8 = m == 0.f ? 1.f : __fdiv_rn(m, 448.0f);
         }
         const float r8 = __fdiv_rn(1.0f, s8);
@@ -721,25 +839,36 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
             if (is_v) {
               // group g of token 4kq + j: elements 8g + j and 8g + 4 + j on the 16 lanes of row kq;
               // lane l16 < 4 NC of each row keeps combo (j, g) = (l16 / NC, l16 % NC)
+              // all 4 NC combos reduced together over the row (reduce-scatter)
+              constexpr int NCB = 4 * NC;
               float mine_s = 1.f, mine_z = 0.f;
+              if (aff) {
+                // max and min at once: keys of x (low half) and of -x (high half)
+                uint32_t kw[NCB];
 #pragma unroll
-              for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int g = 0; g < NC; ++g) {
-                  const float e0 = chunk_elem<BF>(x[g], j), e1 = chunk_elem<BF>(x[g], 4 + j);
-                  float sv = 1.f, zv = 0.f;
-                  if (aff) {
-                    affine2_params(row16_min(fminf(e0, e1)), row16_max(fmaxf(e0, e1)), zv, sv);
-                  } else {
-                    sv = sign1_scale(row16_sum((double)__builtin_fabsf(e0) + (double)__builtin_fabsf(e1)));
+                  for (int g = 0; g < NC; ++g) {
+                    const uint32_t u0 = chunk_bits(x[g], j), u1 = chunk_bits(x[g], 4 + j);
+                    kw[j * NC + g] = pk_max_i16(key16(u0) | (key16(u0 ^ 0x8000u) << 16),
+                                                key16(u1) | (key16(u1 ^ 0x8000u) << 16));
                   }
-                  const bool me = l16 == j * NC + g;
-                  mine_s = me ? sv : mine_s;
-                  mine_z = me ? zv : mine_z;
-                }
+                const uint32_t r = row16_scatter<NCB>(kw, l16, pk_max_i16);
+                affine2_params(-bits16_to_float<BF>(unkey16(r >> 16)), bits16_to_float<BF>(unkey16(r)), mine_z, mine_s);
+              } else {
+                double sm[NCB];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                  for (int g = 0; g < NC; ++g)
+                    sm[j * NC + g] = (double)__builtin_fabsf(chunk_elem<BF>(x[g], j)) +
+                                     (double)__builtin_fabsf(chunk_elem<BF>(x[g], 4 + j));
+                mine_s = sign1_scale(row16_scatter<NCB>(sm, l16, [](double a, double b) { return a + b; }));
+              }
               if (l16 < 4 * NC) {
                 sx[wv][kq][l16] = mine_s;
                 zx[wv][kq][l16] = mine_z;
+                if (aff) rx[wv][kq][l16] = recip_fp16_scale(mine_s);
                 const int j = l16 / NC, g = l16 % NC;
                 const size_t at = sc_base + ((size_t)(4 * kq + j) * NC + g) * 2;
                 *reinterpret_cast<_Float16*>(a.pool + dof + at) = (_Float16)mine_s;
@@ -753,6 +882,7 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
                 for (int g = 0; g < NC; ++g) {
                   s2[j][g] = sx[wv][kq][j * NC + g];
                   z2[j][g] = zx[wv][kq][j * NC + g];
+                  if (aff) r2[j][g] = rx[wv][kq][j * NC + g];
                 }
               __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
               __builtin_amdgcn_wave_barrier();
@@ -768,17 +898,19 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
                     lo = fminf(lo, chunk_elem<BF>(x[c], k));
                     hi = fmaxf(hi, chunk_elem<BF>(x[c], k));
                   }
-                  affine2_params(rows4_min(lo), rows4_max(hi), zv, sv);
+                  affine2_params(-rows4_max_sw(-lo), rows4_max_sw(hi), zv, sv);
                 } else {
                   double m = 0.0;
 #pragma unroll
                   for (int k = 0; k < 8; ++k) m += (double)__builtin_fabsf(chunk_elem<BF>(x[c], k));
-                  sv = sign1_scale(rows4_sum(m));
+                  sv = sign1_scale(rows4_sum_sw(m));
                 }
+                const float rv = aff ? recip_fp16_scale(sv) : 1.f;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                   s2[j][c] = sv;
                   z2[j][c] = zv;
+                  r2[j][c] = rv;
                 }
                 if (kq == (c & 3) && (NC == 4 || kq < NC)) {
                   const size_t at = sc_base + ((size_t)l16 * NC + c) * 2;
@@ -799,15 +931,18 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
             if (is_v) {
               // group g of token 4kq + j: elements 8g + j and 8g + 4 + j on the 16 lanes of row kq;
               // lane l16 < 4 NC of each row computes combo (j, g) = (l16 / NC, l16 % NC)
-              float mine = 0.f;
+              // magnitudes' bits (order-preserving), two combos to a word, all
+              // reduced together over the row
+              constexpr int NCB = 4 * NC;
+              uint32_t kw[NCB / 2];
 #pragma unroll
-              for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int g = 0; g < NC; ++g) {
-                  const float mg = row16_max(fmaxf(__builtin_fabsf(chunk_elem<BF>(x[g], j)),
-                                                   __builtin_fabsf(chunk_elem<BF>(x[g], 4 + j))));
-                  mine = (l16 == j * NC + g) ? mg : mine;
-                }
+              for (int cb = 0; cb < NCB; ++cb) {
+                const int j = cb / NC, g = cb % NC;
+                const uint32_t a0 = chunk_bits(x[g], j) & 0x7FFFu, a1 = chunk_bits(x[g], 4 + j) & 0x7FFFu;
+                const uint32_t m = a0 > a1 ? a0 : a1;
+                kw[cb >> 1] = (cb & 1) ? (kw[cb >> 1] | (m << 16)) : m;
+              }
+              const float mine = bits16_to_float<BF>(row16_scatter_pairs<NCB>(kw, l16, pk_max_i16));
               if (l16 < 4 * NC) {
                 const _Float16 s16 = scale_of(mine);
                 sx[wv][kq][l16] = (float)s16;
@@ -833,7 +968,7 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
                 float m = 0.f;
 #pragma unroll
                 for (int k = 0; k < 8; ++k) m = fmaxf(m, __builtin_fabsf(chunk_elem<BF>(x[c], k)));
-                m = rows4_max(m);
+                m = rows4_max_sw(m);
                 const _Float16 s16 = scale_of(m);
                 const float sf = (float)s16, rf = recip_fp16_scale(sf);
 #pragma unroll
