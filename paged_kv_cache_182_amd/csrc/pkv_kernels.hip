@@ -1140,11 +1140,12 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>(), max_waves_per_eu<D
         }
       }
     }
-    // Drain the ring's discarded loads (zero-size reads, no traffic): with
-    // nothing in flight across the loop edge, the wait counts at the top of
-    // the loop only cover q, not the tile registers.
-    __builtin_amdgcn_s_waitcnt(VMCNT0);
     if (cbase + chunk >= s1) break;  // the row ends inside this chunk
+    // Before the next chunk, drain the ring's discarded loads (zero-size
+    // reads, no traffic): with nothing in flight across the loop edge, the
+    // wait counts at the top of the loop only cover q, not the tile
+    // registers. After the last chunk nothing waits for them here.
+    __builtin_amdgcn_s_waitcnt(VMCNT0);
     cbase += MAX_DESC;
     chunk = min(MAX_DESC, s_lim - cbase);
     if (chunk <= 0) break;
@@ -1174,22 +1175,31 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>(), max_waves_per_eu<D
     for (int j = 0; j < 4; ++j) red_acc[(wave * 16 + 4 * kq + j) * D + 16 * n + col] = acc[n][j];
   lds_barrier();
 
-  for (int idx = tid; idx < G * D; idx += THREADS) {
+  // at most 16 * D / THREADS outputs per thread (G <= 16), unrolled so that
+  // the LDS reads of all of them go out together
+#pragma unroll
+  for (int it = 0; it < 16 * D / THREADS; ++it) {
+    const int idx = tid + it * THREADS;
+    if (idx >= G * D) break;
     const int g = idx / D, d = idx - g * D;
+    // every wave's (m, l, acc) read at once (one LDS round, no branches); a
+    // wave with nothing attended (m = -inf, l = 0, acc = 0) weighs 0
+    float mw[WAVES], lw[WAVES], aw[WAVES];
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      mw[w] = red_m[w * 16 + g];
+      lw[w] = red_l[w * 16 + g];
+      aw[w] = red_acc[(w * 16 + g) * D + d];
+    }
     float M = NEG_INF;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, red_m[w * 16 + g]);
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mw[w]);
     float Ls = 0.f, A = 0.f;
-    if (M != NEG_INF) {
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) {
-        const float mw = red_m[w * 16 + g];
-        if (mw != NEG_INF) {
-          const float e = __builtin_amdgcn_exp2f(mw - M);
-          Ls += e * red_l[w * 16 + g];
-          A += e * red_acc[(w * 16 + g) * D + d];
-        }
-      }
+    for (int w = 0; w < WAVES; ++w) {
+      const float e = mw[w] != NEG_INF ? __builtin_amdgcn_exp2f(mw[w] - M) : 0.f;
+      Ls += e * lw[w];
+      A += e * aw[w];
     }
     const size_t row = (size_t)b * a.hq + (size_t)h * G + g;
     if (a.final_out) {
