@@ -467,7 +467,9 @@ int pkv_select_capacity(int32_t page_size, int32_t block_tokens, int32_t block_t
  *   q_idx         fp16 [B][idx_dim], idx_dim a positive multiple of 8 (<= 4096).
  *   slab          fp16 [B][max_blocks][idx_dim], 16-byte aligned; a row with
  *                 more than max_blocks blocks is cut to max_blocks and counted
- *                 in *err_count.
+ *                 in *err_count. A row of the slab, (max_blocks + 64) * idx_dim
+ *                 * 2 bytes, must stay below 4 GiB - 64 KiB (PKV_ERR_UNSUPPORTED
+ *                 otherwise).
  *   block_scores  fp32 [B][max_blocks]: written with the scores of the row's
  *                 blocks (the scratch the selection reads).
  *   page_sel      int32 [B][max_sel_pages], sel_lens int32 [B] (written).

@@ -580,6 +580,8 @@ int pkv_select_pages(const pkv_params* p, int32_t block_tokens, int32_t block_to
       idx_dim % 8 != 0 || max_blocks < 0)
     return PKV_ERR_INVALID_ARG;
   if (idx_dim > 4096 || p->max_pages_per_row > kSelectMaxPages || p->num_rows > 65535) return PKV_ERR_UNSUPPORTED;
+  // a row of the slab is read through one 32-bit buffer range (with a chunk of 64 blocks to spare)
+  if (((int64_t)max_blocks + 64) * idx_dim * 2 > (int64_t(1) << 32) - (int64_t(1) << 16)) return PKV_ERR_UNSUPPORTED;
   if (p->num_rows == 0) return PKV_OK;
   if (!q_idx || !seq_lens || !page_sel || !sel_lens || (max_blocks > 0 && (!slab || !block_scores)))
     return PKV_ERR_INVALID_ARG;
@@ -606,6 +608,7 @@ int pkv_select_pages(const pkv_params* p, int32_t block_tokens, int32_t block_to
   a.recent_pages = recent_pages;
   a.idx_dim = idx_dim;
   a.max_blocks = max_blocks;
+  a.cus = compute_units();
   return pkv::launch_select(a, stream) == 0 ? PKV_OK : PKV_ERR_HIP;
 }
 

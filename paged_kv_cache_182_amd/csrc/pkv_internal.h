@@ -143,6 +143,7 @@ struct SelectArgs {
   int32_t* err;             // device counter or nullptr
   int32_t rows, page, max_pages, max_sel;
   int32_t block_tokens, block_topk, sink_pages, recent_pages, idx_dim, max_blocks;
+  int32_t cus;  // compute units of the device (sizes the score grid)
 };
 
 int launch_select(const SelectArgs& a, void* stream);

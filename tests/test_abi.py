@@ -257,6 +257,9 @@ def test_select_capacity_and_host_checks():
                                   num_pages=1, max_pages_per_row=1 << 20, pool_bytes=0, max_sel_pages=8)) == -2
     assert sel(pp=pkv.make_params(rows=0, num_q_heads=1, num_kv_heads=1, head_dim=128, page_size=16,
                                   num_pages=1, max_pages_per_row=64, pool_bytes=0, max_sel_pages=8), q=0) == 0
+    # a slab row is read through one 32-bit buffer range: (max_blocks + 64) * idx_dim * 2 < 4 GiB - 64 KiB
+    assert sel(dim=4096, mb=(1 << 19) - 64) == -2               # 4 GiB exactly: refused
+    assert sel(dim=8, mb=(1 << 28)) == -2
 
 
 def test_noalloc_rejects_requests_beyond_its_scratch_on_the_host():

@@ -31,7 +31,7 @@ def run_select(lens, P, BT, k, sink, recent, idx_dim, max_sel, max_pages, q, sla
     return sel.cpu().numpy(), n.cpu().numpy(), sc.cpu().numpy(), int(dropped.item())
 
 
-def check(lens, P, BT, k, sink, recent, idx_dim, max_sel, seed, ties=False, nan=False):
+def check(lens, P, BT, k, sink, recent, idx_dim, max_sel, seed, ties=False, nan=False, nan_frac=0.05):
     rng = np.random.default_rng(seed)
     max_pages = max(-(-max(lens) // P), 1)
     max_blocks = max(-(-max(lens) // BT), 1)
@@ -43,7 +43,7 @@ def check(lens, P, BT, k, sink, recent, idx_dim, max_sel, seed, ties=False, nan=
         q = rng.standard_normal((rows, idx_dim)).astype(np.float16)
         slab = (rng.standard_normal((rows, max_blocks, idx_dim)) * 2).astype(np.float16)
     if nan:
-        slab[rng.random((rows, max_blocks)) < 0.05, 3] = np.nan
+        slab[rng.random((rows, max_blocks)) < nan_frac, 3] = np.nan
     sel, n, sc, dropped = run_select(lens, P, BT, k, sink, recent, idx_dim, max_sel, max_pages, q, slab)
     total_drop = 0
     for r, L in enumerate(lens):
@@ -64,7 +64,7 @@ def test_selection_matches_oracle(P, BT):
         check(lens, P, BT, k, 1, 2, 64, 400, seed=P + BT + k)
 
 
-@pytest.mark.parametrize("idx_dim", [8, 64, 128])
+@pytest.mark.parametrize("idx_dim", [8, 64, 128, 136])
 def test_ties_and_nan_scores(idx_dim):
     lens = [4000, 333, 16384]
     check(lens, 16, 16, 50, 0, 1, idx_dim, 200, seed=idx_dim, ties=True)
@@ -86,6 +86,23 @@ def test_large_rows_radix_select():
     lens = [262144, 262144 - 5, 131072]
     check(lens, 16, 16, 127, 0, 1, 64, pkv.select_capacity(16, 16, 127, 0, 1), seed=11)
     check(lens, 16, 16, 127, 0, 1, 64, 128, seed=12, ties=True)
+
+
+def test_select_search_paths():
+    """Each way the k-th best key is found: per-wave candidates with one wave
+    searching them (16,384 blocks, k 127), the same with 32 keys per thread
+    (20,000 blocks), the search over every key when the candidates overflow
+    (k 300 on 16,384 blocks: at least 300 from each of 16 waves), keys re-read
+    from memory per step (40,000 blocks), and a row whose k-th key is a NaN
+    score (the lowest key)."""
+    print("case 16,384 / 20,000 / 40,000 blocks", flush=True)
+    cap = pkv.select_capacity(16, 16, 127, 0, 1)
+    check([262144, 20000 * 16 - 3, 40000 * 16], 16, 16, 127, 0, 1, 64, cap, seed=31)
+    check([262144, 20000 * 16, 40000 * 16 - 9], 16, 16, 127, 0, 1, 64, cap, seed=32, ties=True)
+    print("case candidate overflow", flush=True)
+    check([262144, 262144 - 100], 16, 16, 300, 0, 1, 64, pkv.select_capacity(16, 16, 300, 0, 1), seed=33)
+    print("case k-th key a NaN", flush=True)
+    check([16 * 1000, 16 * 5000], 16, 16, 700, 0, 0, 64, 1000, seed=34, nan=True, nan_frac=0.5)
 
 
 @pytest.mark.parametrize("idx_dim", [64, 128])
