@@ -41,7 +41,6 @@
  *                 fp16 step s per (token, 32 dims).
  *   PKV_BIT1_G32  the 1-bit tier: sign codes (bit 1 = negative) times one
  *                 fp16 scale per (token, 32 dims).
- * The chunked prefill (pkv_prefill_attention) reads the first five only.
  *
  * In-page layout (this library's definition). page_k_off[p] / page_v_off[p]
  * are byte offsets from page_pool to the K and V planes of physical page p;
@@ -391,12 +390,10 @@ int pkv_encode_pages(const pkv_params* p, int32_t n, const int32_t* src_pages, c
  * FP8 page scales must be finite and nonzero here (the encoder's always
  * are): the kernel keeps its V sums in units of the current page's V scale.
  *
- * Dense mode only: max_sel_pages must be 0. Codecs (FP16, BF16, FP8, INT8
- * and INT4: a declared INT2 or BIT1 codec returns PKV_ERR_UNSUPPORTED, and
- * such a page met under PKV_CODEC_MIXED is a device-visible error), the page
- * tables, the device-visible error counting and the threading rules are
- * those of pkv_decode_attention (each bad page is counted once per partition
- * and row).
+ * Dense mode only: max_sel_pages must be 0. Codecs (all seven; BF16 as
+ * described with the codecs), the page tables, the device-visible error
+ * counting and the threading rules are those of pkv_decode_attention (each
+ * bad page is counted once per partition and row).
  */
 
 /* Partitions of the key range for this call (>= 1), or a negative status. */

@@ -414,8 +414,6 @@ int plan_prefill(const pkv_params* p, int32_t q_tokens, int32_t kv_begin, int32_
   if (st != PKV_OK) return st;
   if (p->max_sel_pages != 0) return PKV_ERR_INVALID_ARG;  // the prefill attends the dense cache
   if (p->window_tokens != 0) return PKV_ERR_INVALID_ARG;  // its sliding window is an argument of its own
-  // the prefill kernel decodes FP16, BF16, FP8, INT8 and INT4 pages only
-  if (p->k_codec > PKV_INT4_G32 || p->v_codec > PKV_INT4_G32) return PKV_ERR_UNSUPPORTED;
   if (p->partition_tokens % p->page_size != 0) return PKV_ERR_INVALID_ARG;  // prefill partitions are whole pages
   if (q_tokens < 0 || kv_begin < 0 || (kv_end >= 0 && kv_end < kv_begin)) return PKV_ERR_INVALID_ARG;
   const int64_t cap = (int64_t)p->max_pages_per_row * p->page_size;

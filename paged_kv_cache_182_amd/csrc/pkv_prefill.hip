@@ -49,7 +49,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-enum : int { C_FP16 = 0, C_BF16 = 1, C_FP8 = 2, C_INT8 = 3, C_INT4 = 4, C_ANY = 15 };
+enum : int { C_FP16 = 0, C_BF16 = 1, C_FP8 = 2, C_INT8 = 3, C_INT4 = 4, C_INT2 = 5, C_BIT1 = 6, C_ANY = 15 };
 
 constexpr int WAVES = 4;
 constexpr int THREADS = 64 * WAVES;
@@ -59,12 +59,18 @@ constexpr int PAIR_RING = 1;              // tile pairs of codes in flight per t
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr float LN2 = 0.693147180559945309f;
 
-__host__ __device__ constexpr int bits_of(int c) { return c <= C_BF16 ? 16 : (c == C_INT4 ? 4 : 8); }
-__host__ __device__ constexpr bool is_int(int c) { return c == C_INT8 || c == C_INT4; }
+// code width: FP16 and BF16 16 bits, FP8 and INT8 8, INT4 4, INT2 2, BIT1 1
+// (log2 of it, three bits per codec, in one constant)
+__host__ __device__ constexpr int bits_of(int c) { return 1 << ((0xa6e4u >> (3 * c)) & 7u); }
+// one fp16 scale per (token, 32 dims): INT8, INT4, INT2, BIT1
+__host__ __device__ constexpr bool is_int(int c) { return c >= C_INT8 && c <= C_BIT1; }
+// INT2 (unsigned affine) also holds one fp16 offset per (token, 32 dims)
+__host__ __device__ constexpr bool has_zero(int c) { return c == C_INT2; }
 
 __device__ inline uint64_t plane_bytes(int c, int hkv, int page, int d) {
   const uint64_t codes = (uint64_t)hkv * page * d * bits_of(c) / 8;
-  return codes + (is_int(c) ? (uint64_t)hkv * page * (d / 32) * 2 : 0);
+  const uint64_t groups = (uint64_t)hkv * page * (d / 32) * 2;
+  return codes + (is_int(c) ? groups : 0) + (has_zero(c) ? groups : 0);
 }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -119,6 +125,35 @@ __device__ inline u4 int4x8_to_h8(uint32_t w) {
   const h2 o3 = __builtin_elementwise_fma(as_h2((u8 & 0x00f000f0u) ^ 0x64806480u), s16, -off16);
   return u4{__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1), __builtin_bit_cast(uint32_t, o2),
             __builtin_bit_cast(uint32_t, o3)};
+}
+
+// Run words of the sub-byte codecs hold 16 (INT2) or 32 (BIT1) elements, the
+// even ones in the low half-word and the odd ones in the high half-word, each
+// half in element order; a BIT1 run of head_dim 64 is a 16-bit unit (even
+// elements in its low byte), spread here to the two half-words.
+__device__ inline uint32_t spread16(uint32_t u) { return (u & 0xffu) | ((u & 0xff00u) << 8); }
+// two unsigned 2-bit codes at bits s, s+1 and 16+s, 17+s -> fp16 pair (exact)
+__device__ inline uint32_t u2pair(uint32_t w, int s) {
+  const h2 off = {(_Float16)1024.0f, (_Float16)1024.0f};
+  return __builtin_bit_cast(uint32_t, as_h2(((w >> s) & 0x00030003u) | 0x64006400u) - off);
+}
+// two sign codes at bits k and 16+k -> fp16 pair of +-1 (bit set: -1)
+__device__ inline uint32_t b1pair(uint32_t w, int k) { return ((w << (15 - k)) & 0x80008000u) | 0x3C003C00u; }
+// elements 8c .. 8c+7 of a run (job c) from the run word holding them
+__device__ inline u4 int2x8_to_h8(uint32_t w, int c) {
+  const int s0 = 8 * (c & 1);
+  return u4{u2pair(w, s0), u2pair(w, s0 + 2), u2pair(w, s0 + 4), u2pair(w, s0 + 6)};
+}
+__device__ inline u4 bit1x8_to_h8(uint32_t w, int c) {
+  return u4{b1pair(w, 4 * c), b1pair(w, 4 * c + 1), b1pair(w, 4 * c + 2), b1pair(w, 4 * c + 3)};
+}
+// the run word of a sub-byte job from its aligned 16-byte chunk
+template <int D>
+__device__ inline uint32_t sub_word(u4 x, uint32_t off, int bits) {
+  const uint32_t k = (off >> 2) & 3;
+  const uint32_t w = k == 0 ? x[0] : (k == 1 ? x[1] : (k == 2 ? x[2] : x[3]));
+  if (D == 64 && bits == 1) return spread16(((off >> 1) & 1) ? w >> 16 : w & 0xffffu);
+  return w;
 }
 
 // Eight consecutive run elements, raw (16, 8 or 4 bytes in the low words) ->
@@ -232,14 +267,17 @@ __device__ inline void issue(Raw<D>& raw, const TileMeta& m, const PrefillArgs& 
   const rsrc_t rk = make_rsrc(a.pool + m.koff, live ? (uint32_t)plane_bytes(m.kc, a.hkv, P, D) : 0u);
   const rsrc_t rv = make_rsrc(a.pool + m.voff, live ? (uint32_t)plane_bytes(m.vc, a.hkv, P, D) : 0u);
   const int sub = m.sub;
-  // INT group scales of the tile, 16 tokens x NC fp16 per plane: lanes
-  // 0 .. 2NC-1 of wave 0 (K) and of wave 1 (V), 16 bytes each
+  // INT group scales of the tile, 16 tokens x NC fp16 per plane, 16 bytes
+  // per lane in lanes 0 .. 2NC-1: K scales in wave 0, V scales in wave 1, and
+  // the INT2 offsets (laid out as the scales, after every head's scales) of
+  // K in wave 2 and of V in wave 3
   {
-    const bool sv = wave == 1;
+    const bool sv = (wave & 1) != 0;
     const int codec = sv ? m.vc : m.kc;
-    const uint32_t base = (uint32_t)((uint64_t)a.hkv * P * D * bits_of(codec) / 8) +
+    const uint32_t zgap = wave >= 2 ? (uint32_t)(a.hkv * P * NC * 2) : 0u;
+    const uint32_t base = (uint32_t)((uint64_t)a.hkv * P * D * bits_of(codec) / 8) + zgap +
                           (uint32_t)((h * P + 16 * sub) * NC * 2) + 16 * lane;
-    const bool want = wave < 2 && lane < 2 * NC && is_int(codec);
+    const bool want = lane < 2 * NC && (wave < 2 ? is_int(codec) : has_zero(codec));
     raw.sc = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(sv ? rv : rk, (int)(want ? base : OFF_NONE),
                                                                            0, 0));
   }
@@ -268,12 +306,24 @@ struct PairStage {
   u4 v[D / 16][64];
   float ks[2][SCL];
   float vs[2][SCL];
+  float kz[2][SCL];  // INT2 offsets (0 for the other codecs)
+  float vz[2][SCL];
 };
 
-template <int C>
-__device__ inline u4 convert(u4 raw, uint32_t off, int codec) {
-  if constexpr (C == C_ANY) return to_h8(select_bytes(raw, off, bits_of(codec)), codec);
-  else return to_h8_c<C>(select_bytes(raw, off, bits_of(C)));
+// Job c's eight elements (c: its 8-element chunk of the run) as fp16.
+template <int C, int D>
+__device__ inline u4 convert(u4 raw, uint32_t off, int codec, int c) {
+  if constexpr (C == C_INT2) {
+    return int2x8_to_h8(sub_word<D>(raw, off, 2), c);
+  } else if constexpr (C == C_BIT1) {
+    return bit1x8_to_h8(sub_word<D>(raw, off, 1), c);
+  } else if constexpr (C == C_ANY) {
+    if (codec == C_INT2) return int2x8_to_h8(sub_word<D>(raw, off, 2), c);
+    if (codec == C_BIT1) return bit1x8_to_h8(sub_word<D>(raw, off, 1), c);
+    return to_h8(select_bytes(raw, off, bits_of(codec)), codec);
+  } else {
+    return to_h8_c<C>(select_bytes(raw, off, bits_of(C)));
+  }
 }
 
 // Whether the fp16 image words of eight bf16 codes (a 16-bit run: the raw
@@ -303,23 +353,25 @@ __device__ inline u4 mask_v_tail(u4 x, int valid, int lane) {
 }
 
 // INT group scales of one tile into LDS: lanes 0 .. 2NC-1 of wave 0 (K) and
-// of wave 1 (V); zero past the row, 1 for the other codecs.
+// of wave 1 (V), zero past the row and 1 for the other codecs; INT2 offsets
+// from waves 2 (K) and 3 (V), zero past the row and for the other codecs.
 template <int D>
-__device__ inline void stage_scales(const Raw<D>& raw, const TileMeta& m, float* ks, float* vs, int wave,
-                                    int lane) {
+__device__ inline void stage_scales(const Raw<D>& raw, const TileMeta& m, float* ks, float* vs, float* kz,
+                                    float* vz, int wave, int lane) {
   constexpr int NC = D / 32;
-  if (wave < 2 && lane < 2 * NC) {
-    const bool sv = wave == 1;
+  if (lane < 2 * NC) {
+    const bool sv = (wave & 1) != 0, zero = wave >= 2;
     const int codec = sv ? m.vc : m.kc;
+    const bool has = zero ? has_zero(codec) : is_int(codec);
     float f[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t w = raw.sc[e >> 1];
       const uint16_t hbits = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
       const int tok = (8 * lane + e) / NC;
-      f[e] = !is_int(codec) ? 1.0f : (tok < m.valid ? (float)__builtin_bit_cast(_Float16, hbits) : 0.0f);
+      f[e] = !has ? (zero ? 0.0f : 1.0f) : (tok < m.valid ? (float)__builtin_bit_cast(_Float16, hbits) : 0.0f);
     }
-    float* dst = (sv ? vs : ks) + 8 * lane;
+    float* dst = (zero ? (sv ? vz : kz) : (sv ? vs : ks)) + 8 * lane;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dst[e] = f[e];
   }
@@ -337,8 +389,8 @@ __device__ inline void produce_pair(const Raw<D>& ra, const Raw<D>& rb, const Ti
     const bool is_v = wj >= NC;
     const int c = is_v ? wj - NC : wj;
     if (is_v) {
-      const u4 xa = mask_v_tail(convert<VC>(ra.x[q], ra.off[q], ma.vc), ma.valid, lane);
-      const u4 xb = mask_v_tail(convert<VC>(rb.x[q], rb.off[q], mb.vc), mb.valid, lane);
+      const u4 xa = mask_v_tail(convert<VC, D>(ra.x[q], ra.off[q], ma.vc, c), ma.valid, lane);
+      const u4 xb = mask_v_tail(convert<VC, D>(rb.x[q], rb.off[q], mb.vc, c), mb.valid, lane);
       if constexpr (VC == C_BF16 || VC == C_ANY) {
         // values of tokens inside the row (the tails are zero on both sides)
         if ((VC == C_BF16 || ma.vc == C_BF16) && !bf16_kept(mask_v_tail(ra.x[q], ma.valid, lane), xa)) lost = true;
@@ -347,7 +399,7 @@ __device__ inline void produce_pair(const Raw<D>& ra, const Raw<D>& rb, const Ti
       st.v[2 * c][lane] = u4{xa[0], xa[1], xb[0], xb[1]};
       st.v[2 * c + 1][lane] = u4{xa[2], xa[3], xb[2], xb[3]};
     } else {
-      const u4 ka = convert<KC>(ra.x[q], ra.off[q], ma.kc), kb = convert<KC>(rb.x[q], rb.off[q], mb.kc);
+      const u4 ka = convert<KC, D>(ra.x[q], ra.off[q], ma.kc, c), kb = convert<KC, D>(rb.x[q], rb.off[q], mb.kc, c);
       st.k[0][64 * c + lane] = ka;
       st.k[1][64 * c + lane] = kb;
       if constexpr (KC == C_BF16 || KC == C_ANY) {
@@ -358,8 +410,8 @@ __device__ inline void produce_pair(const Raw<D>& ra, const Raw<D>& rb, const Ti
     }
   }
   if constexpr (KC == C_ANY || VC == C_ANY || is_int(KC) || is_int(VC)) {
-    stage_scales<D>(ra, ma, st.ks[0], st.vs[0], wave, lane);
-    stage_scales<D>(rb, mb, st.ks[1], st.vs[1], wave, lane);
+    stage_scales<D>(ra, ma, st.ks[0], st.vs[0], st.kz[0], st.vz[0], wave, lane);
+    stage_scales<D>(rb, mb, st.ks[1], st.vs[1], st.kz[1], st.vz[1], wave, lane);
   }
 }
 
@@ -398,10 +450,13 @@ __device__ inline float row4_sum(float x) {
 
 // Raw scores of one staged tile for the wave's NBC column blocks (lane l:
 // tokens 4(l/16) + j of column l % 16), before the K scale. INT K: one
-// accumulator per 32-dim group, weighted by the token's fp16 group scale.
+// accumulator per 32-dim group, weighted by the token's fp16 group scale;
+// INT2 K adds each group's offset times the column's query sum over the
+// group (qsum), the offset's share of the dot product.
 template <int D>
-__device__ inline void tile_scores(const u4* kimg, const float* ks, bool kint, const h8 (&qf)[NBC][D / 32],
-                                   int lane, f4 (&s)[NBC]) {
+__device__ inline void tile_scores(const u4* kimg, const float* ks, const float* kz, bool kint, bool kzero,
+                                   const h8 (&qf)[NBC][D / 32], const float (&qsum)[NBC][D / 32], int lane,
+                                   f4 (&s)[NBC]) {
   constexpr int NC = D / 32;
   const int kq = lane >> 4;
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -424,6 +479,10 @@ __device__ inline void tile_scores(const u4* kimg, const float* ks, bool kint, c
         float x = 0.f;
 #pragma unroll
         for (int c = 0; c < NC; ++c) x += ksc[j][c] * sg[c][j];
+        if (kzero) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c) x += kz[(4 * kq + j) * NC + c] * qsum[cb][c];
+        }
         s[cb][j] = x;
       }
     }
@@ -513,6 +572,23 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
       qf[cb][c2] = real ? *reinterpret_cast<const h8*>(qrow + 32 * c2 + 8 * kq) : h8{0, 0, 0, 0, 0, 0, 0, 0};
   }
 
+  // INT2 K: the column's query summed over each 32-dim group (fp32)
+  constexpr bool KZ = KC == C_ANY || has_zero(KC);
+  constexpr bool VZ = VC == C_ANY || has_zero(VC);
+  float qsum[NBC][NC];
+#pragma unroll
+  for (int cb = 0; cb < NBC; ++cb)
+#pragma unroll
+    for (int c2 = 0; c2 < NC; ++c2) {
+      float x = 0.f;
+      if constexpr (KZ) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x += (float)qf[cb][c2][e];
+        x = row4_sum(x);
+      }
+      qsum[cb][c2] = x;
+    }
+
   float m_run[NBC], l_run[NBC];
   // acc holds the P.V sums divided by sv_cur, the FP8 V scale of the page
   // last attended: a page with another scale rescales acc once, so FP8 V
@@ -549,7 +625,7 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
       const int cod = a.codec[pq];
       const int kc = cod & 15, vc = cod >> 4;
       const uint64_t ko = a.koff[pq], vo = a.voff[pq];
-      ok = ok && kc <= C_INT4 && vc <= C_INT4 && (KC == C_ANY || kc == KC) && (VC == C_ANY || vc == VC);
+      ok = ok && kc <= C_BIT1 && vc <= C_BIT1 && (KC == C_ANY || kc == KC) && (VC == C_ANY || vc == VC);
       ok = ok && (a.k_codec < 0 || kc == a.k_codec) && (a.v_codec < 0 || vc == a.v_codec);
       ok = ok && !((kc == C_FP8 || vc == C_FP8) && a.scale == nullptr) && ((ko | vo) & 15) == 0;
       ok = ok && ko <= a.pool_bytes && a.pool_bytes - ko >= plane_bytes(kc, a.hkv, P, D);
@@ -631,8 +707,8 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
         const int kcA = KC == C_ANY ? mA.kc : KC, kcB = KC == C_ANY ? mB.kc : KC;
         const int vcA = VC == C_ANY ? mA.vc : VC, vcB = VC == C_ANY ? mB.vc : VC;
         f4 sA[NBC], sB[NBC];
-        tile_scores<D>(st.k[0], st.ks[0], is_int(kcA), qf, lane, sA);
-        tile_scores<D>(st.k[1], st.ks[1], is_int(kcB), qf, lane, sB);
+        tile_scores<D>(st.k[0], st.ks[0], st.kz[0], is_int(kcA), KZ && has_zero(kcA), qf, qsum, lane, sA);
+        tile_scores<D>(st.k[1], st.ks[1], st.kz[1], is_int(kcB), KZ && has_zero(kcB), qf, qsum, lane, sB);
         // scores in log2 units are raw * f: f > 0 goes into the max and the exp
         const float fA = is_int(kcA) ? a.scale_log2 : a.scale_log2 * mA.sk;
         const float fB = is_int(kcB) ? a.scale_log2 : a.scale_log2 * mB.sk;
@@ -655,11 +731,18 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
         const float r_split = svA / svB;
 
         const bool vint = is_int(vcA) || is_int(vcB);
+        // INT2 V (a pair holding one): its value z + s*u is the sum of an offset
+        // term and a step term, each of which can far exceed the value, so both
+        // go to the MFMA with their weights split in fp16 high and low parts
+        // (22 bits): p*s with the codes u, and p with the offsets z
+        const bool vzero = VZ && (has_zero(vcA) || has_zero(vcB));
 
         // ---- online softmax of both column blocks; pa holds the P operand
         // (INT V: the weights times the token's fp16 group scale, one operand
         // per group; the staged scales are 1 for other codecs)
         h8 pa[NBC][NC];
+        h8 pl[VZ ? NBC : 1][VZ ? NC : 1];  // INT2 V: low parts of pa
+        h8 ph[VZ ? NBC : 1], pq[VZ ? NBC : 1];  // INT2 V: the plain weights, high and low
 #pragma unroll
         for (int cb = 0; cb < NBC; ++cb) {
           float s8[8];
@@ -699,7 +782,29 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
             p[4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s8[4 + j], fB, -mu));
           }
           l_run[cb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-          if (vint) {
+          bool done = false;
+          if constexpr (VZ) {
+            if (vzero) {
+#pragma unroll
+              for (int g = 0; g < NC; ++g)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                  const float wv = p[j] * st.vs[j >> 2][(4 * kq + (j & 3)) * NC + g];
+                  const _Float16 hi = (_Float16)wv;
+                  pa[cb][g][j] = hi;
+                  pl[cb][g][j] = (_Float16)(wv - (float)hi);
+                }
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const _Float16 hi = (_Float16)p[j];
+                ph[cb][j] = hi;
+                pq[cb][j] = (_Float16)(p[j] - (float)hi);
+              }
+              done = true;
+            }
+          }
+          if (done) {
+          } else if (vint) {
 #pragma unroll
             for (int g = 0; g < NC; ++g)
 #pragma unroll
@@ -713,39 +818,48 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
           }
         }
 
-        // ---- P.V, dims 16n .. 16n+15 at a time
+        // ---- P.V, dims 16n .. 16n+15 at a time. INT2 V: the offsets of the
+        // lane's eight tokens (the same for the 16 dims of a block) as B.
         auto vfrag = [&](int n) { return __builtin_bit_cast(h8, st.v[n][lane]); };
-        if (!split) {
+        h8 zf[VZ ? NC : 1];
+        if constexpr (VZ) {
+          if (vzero) {
 #pragma unroll
-          for (int n = 0; n < NB; ++n) {
-            const h8 vf = vfrag(n);
+            for (int g = 0; g < NC; ++g)
 #pragma unroll
-            for (int cb = 0; cb < NBC; ++cb) acc[cb][n] = mfma32(pa[cb][vint ? n / 2 : 0], vf, acc[cb][n]);
+              for (int j = 0; j < 8; ++j) zf[g][j] = (_Float16)st.vz[j >> 2][(4 * kq + (j & 3)) * NC + g];
           }
-        } else {
-          const _Float16 z = 0;
+        }
+        // one pass over the dims with the weights of the tokens picked by keep
+        // (both tiles, or one of them when the pair is split)
+        auto pv = [&](auto keep) {
 #pragma unroll
           for (int n = 0; n < NB; ++n) {
             const h8 vf = vfrag(n);
+            const int g = vint ? n / 2 : 0;
 #pragma unroll
             for (int cb = 0; cb < NBC; ++cb) {
-              const h8 w = pa[cb][vint ? n / 2 : 0];
-              acc[cb][n] = mfma32(h8{w[0], w[1], w[2], w[3], z, z, z, z}, vf, acc[cb][n]);
+              acc[cb][n] = mfma32(keep(pa[cb][g]), vf, acc[cb][n]);
+              if constexpr (VZ) {
+                if (vzero) {
+                  acc[cb][n] = mfma32(keep(pl[cb][g]), vf, acc[cb][n]);
+                  acc[cb][n] = mfma32(keep(ph[cb]), zf[n / 2], acc[cb][n]);
+                  acc[cb][n] = mfma32(keep(pq[cb]), zf[n / 2], acc[cb][n]);
+                }
+              }
             }
           }
+        };
+        if (!split) {
+          pv([](h8 w) { return w; });
+        } else {
+          const _Float16 z = 0;
+          pv([z](h8 w) { return h8{w[0], w[1], w[2], w[3], z, z, z, z}; });
 #pragma unroll
           for (int cb = 0; cb < NBC; ++cb)
 #pragma unroll
             for (int n = 0; n < NB; ++n) acc[cb][n] *= r_split;
-#pragma unroll
-          for (int n = 0; n < NB; ++n) {
-            const h8 vf = vfrag(n);
-#pragma unroll
-            for (int cb = 0; cb < NBC; ++cb) {
-              const h8 w = pa[cb][vint ? n / 2 : 0];
-              acc[cb][n] = mfma32(h8{z, z, z, z, w[4], w[5], w[6], w[7]}, vf, acc[cb][n]);
-            }
-          }
+          pv([z](h8 w) { return h8{z, z, z, z, w[4], w[5], w[6], w[7]}; });
         }
         if (split) sv_cur = svB;
       }

@@ -14,7 +14,7 @@ import oracle
 import paged_kv_cache_182_amd as pkv
 import synth
 from synth.device import to_device
-from synth.layout import BF16, FP8, FP16, INT4, INT8
+from synth.layout import BF16, BIT1, FP8, FP16, INT2, INT4, INT8
 from gpu_util import compare, params_for, poison_tails
 
 pytestmark = pytest.mark.gpu
@@ -28,7 +28,8 @@ pytestmark = pytest.mark.gpu
 SPLIT_OUT_TOL = 5e-4
 SPLIT_LSE_TOL = 2e-5
 
-PAIRS = [(FP16, FP16), (BF16, BF16), (FP8, FP8), (INT8, INT4), (INT4, INT8), (FP8, FP16), (FP16, INT8)]
+PAIRS = [(FP16, FP16), (BF16, BF16), (FP8, FP8), (INT8, INT4), (INT4, INT8), (FP8, FP16), (FP16, INT8),
+         (INT2, INT2), (BIT1, BIT1), (INT2, BIT1), (BIT1, INT2), (FP8, INT2), (INT2, FP16)]
 
 
 def small(seq_lens, kc, vc, hq, hkv, dim, page, seed=7, **kw):
@@ -100,7 +101,8 @@ def test_chunk_longer_than_row_and_empty_rows():
 
 
 def test_mixed_codecs_per_page():
-    pairs = [(FP16, FP16), (FP8, FP8), (INT8, INT4), (BF16, FP8), (INT4, INT8)]
+    pairs = [(FP16, FP16), (FP8, FP8), (INT8, INT4), (BF16, FP8), (INT4, INT8), (INT2, INT2), (BIT1, INT2),
+             (INT2, BIT1)]
     rng = np.random.default_rng(4)
     pick = {}
 
@@ -264,3 +266,68 @@ def test_bf16_beyond_fp16_range_is_counted():
             assert int(err.item()) > 0
         w0 = small([300, 200], kc, vc, hq=8, hkv=2, dim=128, page=16, seed=4)
         run_prefill(w0, q, expect_err=0)
+
+
+@pytest.mark.parametrize("dim", [64, 128])
+def test_tier_cascade_rows(dim):
+    """A row whose pages sit in every tier of the cascade, newest FP16 to
+    oldest 1-bit, under the per-page codec kernel at whole-page and
+    library-chosen partitions."""
+    print(f"case tier cascade dim={dim}", flush=True)
+    tiers = [BIT1, INT2, INT4, INT8, FP8, FP16]          # logical page 0 is the oldest
+
+    def codec_of(r, lp):
+        c = tiers[min(lp * len(tiers) // 12, len(tiers) - 1)]
+        return (c, c)
+    w = poison_tails(small([12 * 64 - 5, 700, 64], 0, 0, hq=16, hkv=2, dim=dim, page=64, codec_of=codec_of,
+                           seed=19, q_scale=2.0))
+    for pt in (128, 0):
+        check(w, 24, partition_tokens=pt, k_codec=pkv.CODEC_MIXED, v_codec=pkv.CODEC_MIXED,
+              what=f"tier cascade dim={dim} pt={pt}")
+
+
+@pytest.mark.parametrize("codec", [INT2, BIT1])
+@pytest.mark.parametrize("dim", [64, 128])
+def test_subbyte_v_codes_exact(codec, dim):
+    """One key per row and a zero query: each query's out is that key's V
+    exactly. Every 2-bit code (INT2: offset + step * u) or both signs (BIT1),
+    with fp16 steps and offsets whose sums are exact in fp32."""
+    print(f"case sub-byte V codes {codec} dim={dim}", flush=True)
+    from oracle.layout import code_bits
+    rows = 4
+    w = small([1] * rows, FP16, codec, hq=2, hkv=1, dim=dim, page=16, seed=5)
+    arr = w.pool.as_array()
+    bpos, shift = code_bits(16, dim, codec, True)
+    rng = np.random.default_rng(9)
+    G = dim // 32
+    for r in range(rows):
+        pp = int(w.block_table[r, 0])
+        off = int(w.page_v_off[pp])
+        head_bytes = 16 * dim * (2 if codec == INT2 else 1) // 8
+        arr[off:off + head_bytes] = 0
+        codes = rng.integers(0, 4 if codec == INT2 else 2, size=dim)
+        np.bitwise_or.at(arr, off + bpos[0], (codes << shift[0]).astype(np.uint8))
+        sc = off + head_bytes
+        steps = np.float16(rng.choice([0.25, 0.5, 1.5, 3.0], size=G))
+        arr[sc:sc + 2 * G] = np.frombuffer(steps.tobytes(), np.uint8)
+        if codec == INT2:
+            zo = sc + 16 * G * 2
+            offs = np.float16(rng.choice([-2.0, -0.75, 0.125, 1.0], size=G))
+            arr[zo:zo + 2 * G] = np.frombuffer(offs.tobytes(), np.uint8)
+    q = np.zeros((rows, 1, w.num_q_heads, dim), dtype=np.float16)
+    out, _ = run_prefill(w, q)
+    ref, _ = oracle.prefill_attention(w, q)
+    assert np.array_equal(out, ref.astype(np.float32).astype(np.float64))
+
+
+@pytest.mark.parametrize("dim", [64, 128])
+def test_int2_large_values(dim):
+    """INT2 K and V pages of N(0, 16^2) values: a group's offset and step
+    terms (about 40 and up to 80) far exceed the weighted values they sum to,
+    so each must reach the MFMA with 22-bit weights (fp16 high and low parts)
+    to stay within the 1e-3 bar; the per-page kernel and the declared pair."""
+    print(f"case INT2 large values dim={dim}", flush=True)
+    w = poison_tails(small([300, 513, 64], INT2, INT2, hq=8, hkv=2, dim=dim, page=32, seed=23,
+                           outlier_frac=1.0, outlier_mult=16.0))
+    check(w, 24, partition_tokens=64)
+    check(w, 24, partition_tokens=0, k_codec=pkv.CODEC_MIXED, v_codec=pkv.CODEC_MIXED)
