@@ -467,6 +467,14 @@ __device__ inline float recip_div(float x, float s, float r) {
   const float q0 = __fmul_rn(x, r);
   return __builtin_fmaf(-__builtin_fmaf(q0, s, -x), r, q0);
 }
+// The same quotient with q0 taken as fma(x, r, 0): equal to RN(x * r) but for
+// the sign of a zero product, which leaves q zero alike. Written so, the
+// product reads an fp16 x straight from its half of the source word (a mixed-
+// precision fma), with no conversion of its own.
+__device__ inline float recip_div0(float x, float s, float r) {
+  const float q0 = __builtin_fmaf(x, r, 0.0f);
+  return __builtin_fmaf(-__builtin_fmaf(q0, s, -x), r, q0);
+}
 
 // RN(1 / s) for a stored fp16 group scale s (as float, in [2^-24, 65504]):
 // the hardware reciprocal estimate and one Newton step. Exact for every such s
@@ -699,14 +707,45 @@ __device__ inline void store_run(const u4* x, const float (*s2)[D / 32], const f
 #pragma unroll
     for (int e = 0; e < E; e += 2) {
       const float v0 = chunk_elem<BF>(x[e >> 3], e & 7), v1 = chunk_elem<BF>(x[e >> 3], (e + 1) & 7);
-      const float q0 = fast8 ? recip_div(v0, s8, r8) : __fdiv_rn(v0, s8);
-      const float q1 = fast8 ? recip_div(v1, s8, r8) : __fdiv_rn(v1, s8);
+      const float q0 = fast8 ? recip_div0(v0, s8, r8) : __fdiv_rn(v0, s8);
+      const float q1 = fast8 ? recip_div0(v1, s8, r8) : __fdiv_rn(v1, s8);
       const float y0 = fminf(fmaxf(q0, -448.0f), 448.0f);
       const float y1 = fminf(fmaxf(q1, -448.0f), 448.0f);
       if ((e >> 1) & 1)
         word[e >> 2] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, (int)word[e >> 2], true);
       else
         word[e >> 2] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, (int)word[e >> 2], false);
+    }
+  } else if constexpr (DC == W_INT8 || DC == W_INT4) {
+    // code = clip(rint(x / s), +-qmax): the quotient clamped (a median of
+    // three, exact: the bounds are integers), then 1.5 * 2^23 added, which
+    // rounds it to the nearest integer with ties to even (as rint) and leaves
+    // that integer's two's complement in the low bits of the sum
+    constexpr float MAGIC = 12582912.0f;
+    uint32_t cw[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float v = chunk_elem<BF>(x[e >> 3], e & 7);
+      const float q = __builtin_amdgcn_fmed3f(recip_div0(v, s2[e & 3][e >> 3], r2[e & 3][e >> 3]), -QMAX, QMAX);
+      cw[e] = __builtin_bit_cast(uint32_t, q + MAGIC);
+    }
+    if constexpr (DC == W_INT8) {
+      // bytes in element order: elements 4k .. 4k+3 in word k
+#pragma unroll
+      for (int k = 0; k < NWD; ++k) {
+        const uint32_t lo = __builtin_amdgcn_perm(cw[4 * k + 1], cw[4 * k], 0x0C0C0400u);
+        const uint32_t hi = __builtin_amdgcn_perm(cw[4 * k + 3], cw[4 * k + 2], 0x04000C0Cu);
+        word[k] = lo | hi;
+      }
+    } else {
+      // eight codes per word: element 2m at bits 4m, element 2m + 1 at 16 + 4m
+#pragma unroll
+      for (int k = 0; k < NWD; ++k)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t pr = __builtin_amdgcn_perm(cw[8 * k + 2 * m + 1], cw[8 * k + 2 * m], 0x0C040C00u) & 0x000F000Fu;
+          word[k] |= pr << (4 * m);
+        }
     }
   } else {
 #pragma unroll
@@ -719,11 +758,9 @@ __device__ inline void store_run(const u4* x, const float (*s2)[D / 32], const f
         code = f_to_bf16(v);
       } else if constexpr (DC == W_INT2) {
         code = affine2_code_r(v, z2[e & 3][e >> 3], s2[e & 3][e >> 3], r2[e & 3][e >> 3]);
-      } else if constexpr (DC == W_BIT1) {
-        code = v < 0.f ? 1u : 0u;
       } else {
-        const float q = __builtin_rintf(recip_div(v, s2[e & 3][e >> 3], r2[e & 3][e >> 3]));
-        code = (uint32_t)(int)fminf(fmaxf(q, -QMAX), QMAX);
+        static_assert(DC == W_BIT1, "INT8 and INT4 codes are made above");
+        code = v < 0.f ? 1u : 0u;
       }
       put_code<BITS, E>(word, e, code);
     }
