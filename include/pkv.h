@@ -26,12 +26,10 @@
  * "v0.5": FP16/BF16 and Q8/Q4 group pages; PR #499 update: FP8 e4m3 codes +
  * fp32 scales):
  *   PKV_FP16      IEEE binary16.
- *   PKV_BF16      bfloat16. Decode feeds the codes to the bf16 matrix
- *                 instructions as they are, against the query and the softmax
- *                 weights split into bf16 high and low parts: bf16's whole
- *                 range is exact. The prefill stages them as fp16: a value
- *                 that fp16 cannot hold (|x| > 65504, or finer than fp16's
- *                 subnormal step) is counted in err_count.
+ *   PKV_BF16      bfloat16. Decode and the chunked prefill feed the codes
+ *                 to the bf16 matrix instructions as they are, against the
+ *                 query and the softmax weights split into bf16 high and low
+ *                 parts: bf16's whole range is exact.
  *   PKV_FP8_E4M3  OCP E4M3FN codes times page_scale[page][h][K|V] (fp32).
  *   PKV_INT8_G32  int8 codes times one fp16 scale per (token, 32 dims).
  *   PKV_INT4_G32  int4 codes times one fp16 scale per (token, 32 dims).

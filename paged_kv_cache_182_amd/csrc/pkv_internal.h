@@ -33,12 +33,14 @@ constexpr int decode_waves_per_simd(int head_dim, int k_codec, int v_codec) {
 }
 
 // Waves per SIMD of the prefill kernel for (head_dim, K codec, V codec) as
-// compiled (its register count decides): three / two at head_dim 64 and two /
-// one at 128, the second figure for the group-scale and per-page dispatch
-// variants. Sizes the library-chosen prefill partition count.
+// compiled (its register count decides): at head_dim 64 three for a 16-bit
+// or FP8 pair, two for the group-scale pairs, one for the per-page dispatch
+// variant; at 128 two for a 16-bit or FP8 pair, one otherwise. Sizes the
+// library-chosen prefill partition count.
 constexpr int prefill_waves_per_simd(int head_dim, int k_codec, int v_codec) {
   const bool fp_pair = k_codec >= 0 && k_codec <= 2 && k_codec == v_codec;
-  return head_dim == 64 ? (fp_pair ? 3 : 2) : (fp_pair ? 2 : 1);
+  const bool per_page = k_codec < 0 || v_codec < 0;  // the per-page dispatch kernel: one wave per SIMD
+  return head_dim == 64 ? (fp_pair ? 3 : (per_page ? 1 : 2)) : (fp_pair ? 2 : 1);
 }
 
 // Everything one decode launch needs, resolved on the host.

@@ -48,6 +48,7 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 
 enum : int { C_FP16 = 0, C_BF16 = 1, C_FP8 = 2, C_INT8 = 3, C_INT4 = 4, C_INT2 = 5, C_BIT1 = 6, C_ANY = 15 };
 
@@ -91,10 +92,47 @@ __device__ inline void lds_barrier() {
 // ---------------------------------------------------------------- codes -> fp16
 __device__ inline h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
 
-__device__ inline uint32_t bf16x2_to_h2(uint32_t w) {
-  const float lo = __builtin_bit_cast(float, w << 16);
-  const float hi = __builtin_bit_cast(float, w & 0xffff0000u);
-  return __builtin_bit_cast(uint32_t, h2{(_Float16)lo, (_Float16)hi});
+// bf16 operands. The codes of a BF16 page are not converted: they go to the
+// bf16 MFMA as they are, against the query and the softmax weights split in
+// bf16 high and low parts, so every product is exact and bf16's whole range
+// is kept (ARGUS v0.5: FP16/BF16 direct attention).
+__device__ inline f4 mfma32_bf(u4 a, u4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, a), __builtin_bit_cast(bf8, b), c, 0, 0, 0);
+}
+// Eight fp16 query values as bf16: the high parts (the top 8 of the 11
+// significant bits, by truncation) and the low parts (the remaining 3 bits,
+// exact in bf16, whose exponent range holds fp16's subnormals).
+__device__ inline u4 bf_hi8(h8 x) {
+  u4 hi;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = __builtin_bit_cast(uint32_t, (float)x[2 * i]), b = __builtin_bit_cast(uint32_t, (float)x[2 * i + 1]);
+    hi[i] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+  }
+  return hi;
+}
+__device__ inline u4 bf_lo8(h8 x) {
+  u4 lo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = (float)x[2 * i], b = (float)x[2 * i + 1];
+    const float ra = a - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) & 0xffff0000u);
+    const float rb = b - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, b) & 0xffff0000u);
+    lo[i] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, rb), __builtin_bit_cast(uint32_t, ra), 0x07060302u);
+  }
+  return lo;
+}
+// Eight fp32 softmax weights as bf16 high (truncated) and low (the remainder,
+// rounded to nearest) parts: 16 significant bits.
+__device__ inline void bf_split_w8(const float* p, u4& hi, u4& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = p[2 * i], b = p[2 * i + 1];
+    const uint32_t ha = __builtin_bit_cast(uint32_t, a) & 0xffff0000u, hb = __builtin_bit_cast(uint32_t, b) & 0xffff0000u;
+    const __bf16 la = (__bf16)(a - __builtin_bit_cast(float, ha)), lb = (__bf16)(b - __builtin_bit_cast(float, hb));
+    hi[i] = __builtin_amdgcn_perm(hb, ha, 0x07060302u);
+    lo[i] = (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16);
+  }
 }
 
 template <bool HI>
@@ -163,7 +201,7 @@ __device__ inline u4 to_h8_c(u4 r) {
   if constexpr (C == C_FP16) {
     return r;
   } else if constexpr (C == C_BF16) {
-    return u4{bf16x2_to_h2(r[0]), bf16x2_to_h2(r[1]), bf16x2_to_h2(r[2]), bf16x2_to_h2(r[3])};
+    return r;  // kept as bf16 codes: they feed the bf16 MFMA
   } else if constexpr (C == C_FP8) {
     return u4{fp8x2_to_h2<false>(r[0]), fp8x2_to_h2<true>(r[0]), fp8x2_to_h2<false>(r[1]), fp8x2_to_h2<true>(r[1])};
   } else if constexpr (C == C_INT8) {
@@ -176,7 +214,7 @@ __device__ inline u4 to_h8_c(u4 r) {
 __device__ inline u4 to_h8(u4 r, int codec) {
   switch (codec) {
     case C_FP16: return r;
-    case C_BF16: return u4{bf16x2_to_h2(r[0]), bf16x2_to_h2(r[1]), bf16x2_to_h2(r[2]), bf16x2_to_h2(r[3])};
+    case C_BF16: return r;  // kept as bf16 codes
     case C_FP8:
       return u4{fp8x2_to_h2<false>(r[0]), fp8x2_to_h2<true>(r[0]), fp8x2_to_h2<false>(r[1]),
                 fp8x2_to_h2<true>(r[1])};
@@ -326,21 +364,6 @@ __device__ inline u4 convert(u4 raw, uint32_t off, int codec, int c) {
   }
 }
 
-// Whether the fp16 image words of eight bf16 codes (a 16-bit run: the raw
-// words themselves) hold their values unchanged: a value past fp16's 65504,
-// or finer than its subnormal step, does not come back.
-__device__ inline bool bf16_kept(u4 codes, u4 img) {
-  bool ok = true;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const h2 x = as_h2(img[k]);
-    const uint32_t back = (__builtin_bit_cast(uint32_t, (float)x[0]) >> 16) |
-                          (__builtin_bit_cast(uint32_t, (float)x[1]) & 0xffff0000u);
-    ok = ok && back == codes[k];
-  }
-  return ok;
-}
-
 // Zero the V values of tokens past the row (their bytes may be anything): run
 // element e = 8c + i of lane L holds token 4(L/16) + i%4; word k holds
 // elements 2k and 2k+1.
@@ -381,7 +404,7 @@ __device__ inline void stage_scales(const Raw<D>& raw, const TileMeta& m, float*
 // holds the same jobs of both tiles, so it writes the interleaved V operand.
 template <int D, int KC, int VC>
 __device__ inline void produce_pair(const Raw<D>& ra, const Raw<D>& rb, const TileMeta& ma, const TileMeta& mb,
-                                    PairStage<D>& st, int wave, int lane, bool& lost) {
+                                    PairStage<D>& st, int wave, int lane) {
   constexpr int NC = D / 32;
 #pragma unroll
   for (int q = 0; q < Raw<D>::JOBS; ++q) {
@@ -391,22 +414,12 @@ __device__ inline void produce_pair(const Raw<D>& ra, const Raw<D>& rb, const Ti
     if (is_v) {
       const u4 xa = mask_v_tail(convert<VC, D>(ra.x[q], ra.off[q], ma.vc, c), ma.valid, lane);
       const u4 xb = mask_v_tail(convert<VC, D>(rb.x[q], rb.off[q], mb.vc, c), mb.valid, lane);
-      if constexpr (VC == C_BF16 || VC == C_ANY) {
-        // values of tokens inside the row (the tails are zero on both sides)
-        if ((VC == C_BF16 || ma.vc == C_BF16) && !bf16_kept(mask_v_tail(ra.x[q], ma.valid, lane), xa)) lost = true;
-        if ((VC == C_BF16 || mb.vc == C_BF16) && !bf16_kept(mask_v_tail(rb.x[q], mb.valid, lane), xb)) lost = true;
-      }
       st.v[2 * c][lane] = u4{xa[0], xa[1], xb[0], xb[1]};
       st.v[2 * c + 1][lane] = u4{xa[2], xa[3], xb[2], xb[3]};
     } else {
       const u4 ka = convert<KC, D>(ra.x[q], ra.off[q], ma.kc, c), kb = convert<KC, D>(rb.x[q], rb.off[q], mb.kc, c);
       st.k[0][64 * c + lane] = ka;
       st.k[1][64 * c + lane] = kb;
-      if constexpr (KC == C_BF16 || KC == C_ANY) {
-        // the lane's token (lane % 16), when it lies inside the row
-        if ((KC == C_BF16 || ma.kc == C_BF16) && (lane & 15) < ma.valid && !bf16_kept(ra.x[q], ka)) lost = true;
-        if ((KC == C_BF16 || mb.kc == C_BF16) && (lane & 15) < mb.valid && !bf16_kept(rb.x[q], kb)) lost = true;
-      }
     }
   }
   if constexpr (KC == C_ANY || VC == C_ANY || is_int(KC) || is_int(VC)) {
@@ -453,16 +466,33 @@ __device__ inline float row4_sum(float x) {
 // accumulator per 32-dim group, weighted by the token's fp16 group scale;
 // INT2 K adds each group's offset times the column's query sum over the
 // group (qsum), the offset's share of the dot product.
-template <int D>
-__device__ inline void tile_scores(const u4* kimg, const float* ks, const float* kz, bool kint, bool kzero,
-                                   const h8 (&qf)[NBC][D / 32], const float (&qsum)[NBC][D / 32], int lane,
-                                   f4 (&s)[NBC]) {
+// BF16 K (kbf): the codes against the query's bf16 high parts (qhi: qf holds
+// them in the BF16 kernel; split from the fp16 query here otherwise) and low
+// parts (the wave's LDS copy qlo, [block][chunk][lane]).
+template <int D, bool QHI>
+__device__ inline void tile_scores(const u4* kimg, const float* ks, const float* kz, bool kint, bool kzero, bool kbf,
+                                   const h8 (&qf)[NBC][D / 32], const float (&qsum)[NBC][D / 32], const u4* qlo,
+                                   int lane, f4 (&s)[NBC]) {
   constexpr int NC = D / 32;
   const int kq = lane >> 4;
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
   h8 kf[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) kf[c] = __builtin_bit_cast(h8, kimg[64 * c + lane]);
+  if (kbf) {
+#pragma unroll
+    for (int cb = 0; cb < NBC; ++cb) {
+      f4 sa = zero;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u4 kr = __builtin_bit_cast(u4, kf[c]);
+        const u4 qh = QHI ? __builtin_bit_cast(u4, qf[cb][c]) : bf_hi8(qf[cb][c]);
+        sa = mfma32_bf(kr, qlo[(cb * NC + c) * 64 + lane], mfma32_bf(kr, qh, sa));
+      }
+      s[cb] = sa;
+    }
+    return;
+  }
   if (kint) {
     float ksc[4][NC];
 #pragma unroll
@@ -499,16 +529,20 @@ __device__ inline void tile_scores(const u4* kimg, const float* ks, const float*
 
 // ---------------------------------------------------------------- kernel
 // Waves per SIMD asked of the compiler: two where the pair's registers fit in
-// half the file, one for the group-scale and per-page dispatch variants.
+// half the file, one for the group-scale variants at head_dim 128 and for the
+// per-page dispatch variant (at head_dim 64 it spilled at two).
 template <int D, int KC, int VC>
 __host__ __device__ constexpr int prefill_waves() {
-  return (D == 128 && (is_int(KC) || is_int(VC) || KC == C_ANY || VC == C_ANY)) ? 1 : 2;
+  return (KC == C_ANY || VC == C_ANY || (D == 128 && (is_int(KC) || is_int(VC)))) ? 1 : 2;
 }
 
 template <int D, int KC, int VC>
 __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(prefill_waves<D, KC, VC>()))) prefill_kernel(const PrefillArgs a) {
   constexpr int NC = D / 32, NB = D / 16;
   __shared__ PairStage<D> stage[2];
+  // BF16 K: the query's bf16 low parts, one copy per wave ([block][chunk][lane])
+  constexpr bool KB = KC == C_BF16 || KC == C_ANY;
+  __shared__ u4 qlo_lds[KB ? WAVES * NBC * NC * 64 : 1];
   __shared__ PDesc desc[MAX_DESC];
 
   // block -> (partition, column group): the column groups of one partition
@@ -570,6 +604,21 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
 #pragma unroll
     for (int c2 = 0; c2 < NC; ++c2)
       qf[cb][c2] = real ? *reinterpret_cast<const h8*>(qrow + 32 * c2 + 8 * kq) : h8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  // BF16 K: the low parts go to the wave's LDS copy (written and read by the
+  // wave alone); the BF16 kernel keeps the high parts in qf's registers, the
+  // per-page kernel splits them from the fp16 query for its BF16 tiles
+  const u4* qlo = KB ? qlo_lds + wave * NBC * NC * 64 : nullptr;
+  if constexpr (KB) {
+#pragma unroll
+    for (int cb = 0; cb < NBC; ++cb)
+#pragma unroll
+      for (int c2 = 0; c2 < NC; ++c2) {
+        qlo_lds[((wave * NBC + cb) * NC + c2) * 64 + lane] = bf_lo8(qf[cb][c2]);
+        if constexpr (KC == C_BF16) qf[cb][c2] = __builtin_bit_cast(h8, bf_hi8(qf[cb][c2]));
+      }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
   }
 
   // INT2 K: the column's query summed over each 32-dim group (fp32)
@@ -689,9 +738,7 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
         const TileMeta mA = mt[2 * s], mB = mt[2 * s + 1];
         // unconditional: a dead tile converts zeros that are never read, and the
         // ring registers are always consumed before they are loaded again
-        bool lost = false;
-        produce_pair<D, KC, VC>(raw[2 * s], raw[2 * s + 1], mA, mB, st, wave, lane, lost);
-        if (lost && reporter) ++nerr;  // a BF16 value outside fp16's range
+        produce_pair<D, KC, VC>(raw[2 * s], raw[2 * s + 1], mA, mB, st, wave, lane);
         mt[2 * s] = meta(i + 2 * PAIR_RING);
         issue<D>(raw[2 * s], mt[2 * s], a, h, wave, lane);
         mt[2 * s + 1] = meta(i + 2 * PAIR_RING + 1);
@@ -707,8 +754,10 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
         const int kcA = KC == C_ANY ? mA.kc : KC, kcB = KC == C_ANY ? mB.kc : KC;
         const int vcA = VC == C_ANY ? mA.vc : VC, vcB = VC == C_ANY ? mB.vc : VC;
         f4 sA[NBC], sB[NBC];
-        tile_scores<D>(st.k[0], st.ks[0], st.kz[0], is_int(kcA), KZ && has_zero(kcA), qf, qsum, lane, sA);
-        tile_scores<D>(st.k[1], st.ks[1], st.kz[1], is_int(kcB), KZ && has_zero(kcB), qf, qsum, lane, sB);
+        tile_scores<D, KC == C_BF16>(st.k[0], st.ks[0], st.kz[0], is_int(kcA), KZ && has_zero(kcA), KB && kcA == C_BF16,
+                                     qf, qsum, qlo, lane, sA);
+        tile_scores<D, KC == C_BF16>(st.k[1], st.ks[1], st.kz[1], is_int(kcB), KZ && has_zero(kcB), KB && kcB == C_BF16,
+                                     qf, qsum, qlo, lane, sB);
         // scores in log2 units are raw * f: f > 0 goes into the max and the exp
         const float fA = is_int(kcA) ? a.scale_log2 : a.scale_log2 * mA.sk;
         const float fB = is_int(kcB) ? a.scale_log2 : a.scale_log2 * mB.sk;
@@ -719,7 +768,11 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
         // across pages) split the P.V in two, with a rescale between the halves
         const float svB = offB ? mA.sv : mB.sv;
         const float svA = offA ? svB : mA.sv;
-        const bool split = svA != svB;
+        // BF16 V tiles go to the bf16 MFMA: a pair with one of them and one tile
+        // of another codec is split in two halves as well
+        constexpr bool VB = VC == C_BF16 || VC == C_ANY;
+        const bool vbfA = VB && vcA == C_BF16, vbfB = VB && vcB == C_BF16;
+        const bool split = svA != svB || vbfA != vbfB;
         if (svA != sv_cur) {
           const float r = sv_cur / svA;
 #pragma unroll
@@ -743,6 +796,7 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
         h8 pa[NBC][NC];
         h8 pl[VZ ? NBC : 1][VZ ? NC : 1];  // INT2 V: low parts of pa
         h8 ph[VZ ? NBC : 1], pq[VZ ? NBC : 1];  // INT2 V: the plain weights, high and low
+        u4 pbh[VB ? NBC : 1], pbl[VB ? NBC : 1];  // BF16 V: the weights in bf16, high and low
 #pragma unroll
         for (int cb = 0; cb < NBC; ++cb) {
           float s8[8];
@@ -782,6 +836,9 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
             p[4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s8[4 + j], fB, -mu));
           }
           l_run[cb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+          if constexpr (VB) {
+            if (vbfA || vbfB) bf_split_w8(p, pbh[cb], pbl[cb]);
+          }
           bool done = false;
           if constexpr (VZ) {
             if (vzero) {
@@ -832,7 +889,19 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
         }
         // one pass over the dims with the weights of the tokens picked by keep
         // (both tiles, or one of them when the pair is split)
-        auto pv = [&](auto keep) {
+        auto pv = [&](auto keep, auto keepu, bool bfh) {
+          if constexpr (VB) {
+            if (bfh) {
+#pragma unroll
+              for (int n = 0; n < NB; ++n) {
+                const u4 vr = st.v[n][lane];
+#pragma unroll
+                for (int cb = 0; cb < NBC; ++cb)
+                  acc[cb][n] = mfma32_bf(keepu(pbl[cb]), vr, mfma32_bf(keepu(pbh[cb]), vr, acc[cb][n]));
+              }
+              return;
+            }
+          }
 #pragma unroll
           for (int n = 0; n < NB; ++n) {
             const h8 vf = vfrag(n);
@@ -851,15 +920,17 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
           }
         };
         if (!split) {
-          pv([](h8 w) { return w; });
+          pv([](h8 w) { return w; }, [](u4 w) { return w; }, vbfA);
         } else {
           const _Float16 z = 0;
-          pv([z](h8 w) { return h8{w[0], w[1], w[2], w[3], z, z, z, z}; });
+          pv([z](h8 w) { return h8{w[0], w[1], w[2], w[3], z, z, z, z}; }, [](u4 w) { return u4{w[0], w[1], 0u, 0u}; },
+             vbfA);
 #pragma unroll
           for (int cb = 0; cb < NBC; ++cb)
 #pragma unroll
             for (int n = 0; n < NB; ++n) acc[cb][n] *= r_split;
-          pv([z](h8 w) { return h8{z, z, z, z, w[4], w[5], w[6], w[7]}; });
+          pv([z](h8 w) { return h8{z, z, z, z, w[4], w[5], w[6], w[7]}; }, [](u4 w) { return u4{0u, 0u, w[2], w[3]}; },
+             vbfB);
         }
         if (split) sv_cur = svB;
       }

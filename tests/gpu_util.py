@@ -99,3 +99,22 @@ def poison_tails(w):
                         s1 = base + (h * P + P) * (D // 32) * 2
                         arr[s0:s1] = 0x7C                         # fp16 0x7C7C: NaN
     return w
+
+
+def rewrite_bf16(w, make):
+    """Replace the values of every BF16 plane with ``make(row, lp, is_v)``
+    (float32 [Hkv, P, D]), encoded as the layout prescribes; other planes
+    keep their bytes."""
+    from synth.layout import BF16, encode_plane
+    arr = w.pool.as_array()
+    P, D, hkv = w.page_size, w.head_dim, w.num_kv_heads
+    for r in range(w.rows):
+        for lp in range(-(-int(w.seq_lens[r]) // P)):
+            pp = int(w.block_table[r, lp])
+            code = int(w.page_codec[pp])
+            for is_v, codec, off in ((False, code & 15, int(w.page_k_off[pp])), (True, code >> 4, int(w.page_v_off[pp]))):
+                if codec != BF16:
+                    continue
+                x = make(r, lp, is_v).astype(np.float32).reshape(1, hkv, P, D)
+                b, _ = encode_plane(x, BF16, v_order=is_v)
+                arr[off:off + b.shape[1]] = b[0]

@@ -12,7 +12,7 @@ import paged_kv_cache_182_amd as pkv
 import synth
 from synth.device import to_device
 from synth.layout import BF16, BIT1, FP8, FP16, INT2, INT4, INT8
-from gpu_util import compare, params_for, poison_tails, run
+from gpu_util import rewrite_bf16, compare, params_for, poison_tails, run
 
 pytestmark = pytest.mark.gpu
 
@@ -536,25 +536,6 @@ def test_sliding_window_decode_sparse_and_partials():
 
 
 # ------------------------------------------------ BF16 over its whole range
-def rewrite_bf16(w, make):
-    """Replace the values of every BF16 plane with ``make(row, lp, is_v)``
-    (float32 [Hkv, P, D]), encoded as the layout prescribes; other planes
-    keep their bytes."""
-    from synth.layout import encode_plane
-    arr = w.pool.as_array()
-    P, D, hkv = w.page_size, w.head_dim, w.num_kv_heads
-    for r in range(w.rows):
-        for lp in range(-(-int(w.seq_lens[r]) // P)):
-            pp = int(w.block_table[r, lp])
-            code = int(w.page_codec[pp])
-            for is_v, codec, off in ((False, code & 15, int(w.page_k_off[pp])), (True, code >> 4, int(w.page_v_off[pp]))):
-                if codec != BF16:
-                    continue
-                x = make(r, lp, is_v).astype(np.float32).reshape(1, hkv, P, D)
-                b, _ = encode_plane(x, BF16, v_order=is_v)
-                arr[off:off + b.shape[1]] = b[0]
-
-
 def vmax_per_row(w):
     """Largest |V| each (row, query head) attends, from the decoded pages."""
     from oracle.attention import gather_kv
