@@ -342,6 +342,9 @@ int pkv_append_kv(const pkv_params* p, const void* k_new, const void* v_new, uin
  *                        the sum taken in float64 (exact for 16-bit sources),
  *                        capped at 65504; bit = x < 0.
  *                   BF16/FP16: the value, rounded to nearest even.
+ *                 Source values are expected finite (infinities saturate
+ *                 the INT codes); the codes of a block or group holding a
+ *                 NaN are unspecified.
  *   page_codec    page_codec[dst] is set to dst_codec.
  *   page_scale    [num_pages][Hkv][2]; page_scale[dst][h] is set to the FP8
  *                 scales (1 for a plane in another codec). May be NULL only

@@ -490,9 +490,14 @@ __device__ inline float recip_fp16_scale(float s) {
 // recip_div by r = RN(1 / s): for an fp16 step s the corrected quotient is
 // RN(d / s) for every fp32 d, which tests/division/check_affine2_div.c checks
 // for every step over every dividend near the rounding boundaries.
+// Computed as for the INT codes: the quotient clamped to [0, 3] by a median of
+// three, then 1.5 * 2^23 added (rounds to the nearest integer, ties to even,
+// and leaves it in the low bits); d = x - z as fma(x, 1, -z), the same value,
+// so an fp16 x is read from its half of the source word.
 __device__ inline uint32_t affine2_code_r(float x, float z, float st, float r) {
-  const float q = __builtin_rintf(recip_div(x - z, st, r));
-  return (uint32_t)(int)fminf(fmaxf(q, 0.0f), 3.0f);
+  const float d = __builtin_fmaf(x, 1.0f, -z);
+  const float q = __builtin_amdgcn_fmed3f(recip_div0(d, st, r), 0.0f, 3.0f);
+  return __builtin_bit_cast(uint32_t, q + 12582912.0f) & 3u;
 }
 
 // ------------------------------------------------------ encode, register path
