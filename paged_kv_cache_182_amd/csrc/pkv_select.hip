@@ -11,12 +11,15 @@
 //    rounding and the result is reproducible bit for bit). A wave streams 64
 //    blocks at a time through a private LDS slot, loaded coalesced.
 //  * select_kernel: one 1024-thread workgroup per row. The key of the k-th
-//    best score is found exactly, one bit at a time from the top: a bit is
-//    kept when at least k keys reach the candidate (counts by wave ballots
-//    over keys held in registers, summed across the waves through LDS).
-//    Blocks above it are taken, and of those equal to it the lowest block
-//    indices (ranked by workgroup prefix counts, only when more keys equal
-//    it than are needed). The pages of the chosen blocks, and the forced
+//    best score is found exactly. First a lower bound of it from the waves'
+//    lane maxima keeps only the keys that can reach it (usually a few
+//    hundred) as candidates in LDS; one wave then finds the key one bit at a
+//    time from the top, a bit kept when at least k candidates reach it
+//    (per-lane counts summed by DPP). Short rows, large k and candidate sets
+//    over the cap take the same bit search over all the row's keys (wave
+//    ballots summed across the waves through LDS). Blocks above the key are
+//    taken, and of those equal to it the lowest block indices (ranked by
+//    workgroup prefix counts, only when more keys equal it than are needed). The pages of the chosen blocks, and the forced
 //    first and last pages, are marked in an LDS bitmap, which a popcount
 //    prefix scan turns into the ascending page list.
 
