@@ -1298,10 +1298,12 @@ __global__ void __launch_bounds__(64) combine_kernel(int nparts, int D, int vec,
   }
 }
 
-// Fold for few parts per row: one thread per (row, dim), every part's loads
-// issued before they are used, parts summed in ascending order.
+// Fold for few parts per row: one thread per (row, dim), the loads of BATCH
+// parts issued before they are used (up to 32 parts in one round), parts
+// summed in ascending order (the batch changes no result).
 constexpr int FOLD_SMALL_MAX = 64;
 
+template <int BATCH>
 __global__ void __launch_bounds__(256) combine_small_kernel(int rows, int nparts, int D,
                                                             const float* __restrict__ part_acc,
                                                             const float* __restrict__ part_ml,
@@ -1313,17 +1315,17 @@ __global__ void __launch_bounds__(256) combine_small_kernel(int rows, int nparts
   const float* ml = part_ml + row * nparts * 2;
   const float* acc = part_acc + row * nparts * D + d;
   float M = NEG_INF, L = 0.f, A = 0.f;
-  for (int p0 = 0; p0 < nparts; p0 += 8) {
-    float m[8], l[8], x[8];
+  for (int p0 = 0; p0 < nparts; p0 += BATCH) {
+    float m[BATCH], l[BATCH], x[BATCH];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < BATCH; ++u) {
       const int p = p0 + u;
       m[u] = p < nparts ? ml[2 * p] : NEG_INF;
       l[u] = p < nparts ? ml[2 * p + 1] : 0.f;
       x[u] = p < nparts ? acc[(long long)p * D] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < BATCH; ++u) {
       if (live_part(m[u], l[u])) {
         // running log-sum-exp over the parts seen so far
         if (m[u] > M) {
@@ -1412,8 +1414,16 @@ int launch_combine(int rows, int nparts, int head_dim, const float* part_acc, co
   // chip; few rows with many parts go to one wave per (row, 4 dims)
   if (nparts <= 8 || (nparts <= FOLD_SMALL_MAX && (long long)rows * head_dim >= 16384)) {
     const long long threads = (long long)rows * head_dim;
-    hipLaunchKernelGGL(combine_small_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, rows,
-                       nparts, head_dim, part_acc, part_ml, out, lse);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (nparts <= 8)
+      hipLaunchKernelGGL(combine_small_kernel<8>, grid, dim3(256), 0, s, rows, nparts, head_dim, part_acc, part_ml,
+                         out, lse);
+    else if (nparts <= 16)
+      hipLaunchKernelGGL(combine_small_kernel<16>, grid, dim3(256), 0, s, rows, nparts, head_dim, part_acc, part_ml,
+                         out, lse);
+    else
+      hipLaunchKernelGGL(combine_small_kernel<32>, grid, dim3(256), 0, s, rows, nparts, head_dim, part_acc, part_ml,
+                         out, lse);
   } else {
     const int vec = (head_dim % 4 == 0) && (reinterpret_cast<uintptr_t>(part_acc) % 16 == 0);
     hipLaunchKernelGGL(combine_kernel, dim3(rows, (head_dim + 3) / 4), dim3(64), 0, s, nparts, head_dim, vec,
