@@ -388,8 +388,11 @@ int pkv_encode_pages(const pkv_params* p, int32_t n, const int32_t* src_pages, c
  * kv_begin = (the smallest first-query position) - W + 1 lets the partitions
  * cover only the keys in play.
  *
- * FP8 page scales must be finite and nonzero here (the encoder's always
- * are): the kernel keeps its V sums in units of the current page's V scale.
+ * FP8 page scales must be finite here. The V page scale s enters the
+ * softmax in the log domain (log2|s| added to the page's scores, 1/|s| on the
+ * weights' sum, its sign on the weights): |s| below 2^-40 is taken as 2^-40
+ * (a V value moves by less than 4.1e-10) and |s| above 2^40 is outside the
+ * supported domain (the encoder's scales lie in [2^-33, 147]).
  *
  * Dense mode only: max_sel_pages must be 0. Codecs (all seven; BF16 as
  * described with the codecs), the page tables, the device-visible error

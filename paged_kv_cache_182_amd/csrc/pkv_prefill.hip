@@ -30,9 +30,11 @@
 // Codes convert to fp16 exactly, and scales stay in fp32: FP8 K scales
 // multiply the scores, INT K group scales weight one score accumulator per
 // group, INT V group scales multiply the weights per group (fp16 scales, so a
-// weight of 1 stays exact), and the FP8 V page scale multiplies the output:
-// the accumulator is kept in units of the current page's scale and rescaled
-// when a page with another scale comes.
+// weight of 1 stays exact), and the FP8 V page scale s enters the softmax in
+// the log domain: log2|s| is added to the tile's scores (the weights then
+// carry it; the largest weight stays exactly 1), the weights' sum takes 1/|s|
+// and the sign of s flips the tile's weights. So no accumulator is rescaled
+// when the page scale changes.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -230,7 +232,8 @@ __device__ inline u4 to_h8(u4 r, int codec) {
 // Per-tile values every thread holds alike (wave-uniform, so scalar).
 struct TileMeta {
   uint64_t koff, voff;  // plane offsets of the page (0 when dead)
-  float sk, sv;         // FP8 scales of this KV head (1 otherwise)
+  float sk;             // FP8 K scale of this KV head (1 otherwise)
+  float sv;             // FP8 V scale as fp8_v_scale_word (64: none)
   int valid;            // tokens of the tile inside the row (0: dead tile)
   int kc, vc;
   int j0;               // position of the tile's first token
@@ -238,9 +241,20 @@ struct TileMeta {
 };
 
 // Page descriptor staged in LDS (32 bytes).
+// The FP8 V page scale s as 64 + log2|s|, log2|s| clamped to [-40, 40], with
+// the sign of s (64: no scale). Below 2^-40 a V value |code s| <= 448 |s|
+// moves by less than 4.1e-10; scales above 2^40 are outside the supported
+// domain (the encoder's lie in [2^-33, 147]). The clamp keeps every weight
+// that matters next to the largest a normal fp32 number.
+__device__ inline float fp8_v_scale_word(float s) {
+  const float l = fminf(fmaxf(__builtin_amdgcn_logf(fabsf(s)), -40.f), 40.f);  // log2; -inf for 0 clamps
+  return __builtin_copysignf(64.f + l, s);
+}
+
 struct PDesc {
   uint64_t k, v;   // plane offsets (0 if the page is skipped)
-  float sk, sv;    // FP8 scales of this KV head (1 otherwise)
+  float sk;        // FP8 K scale of this KV head (1 otherwise)
+  float sv;        // FP8 V scale as fp8_v_scale_word (64: none)
   int32_t valid;   // tokens of the page inside the row (0: skipped)
   int32_t codec;   // K codec | V codec << 4
 };
@@ -638,12 +652,9 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
       qsum[cb][c2] = x;
     }
 
+  // m_run: the running max of the scores plus log2|s| of FP8 V pages, the
+  // reference of l_run (the weights' sum without s) and acc (the P.V sums)
   float m_run[NBC], l_run[NBC];
-  // acc holds the P.V sums divided by sv_cur, the FP8 V scale of the page
-  // last attended: a page with another scale rescales acc once, so FP8 V
-  // weights go to the MFMA as plain fp16(p) (exact at p = 1), as for 16-bit
-  // pages, and the V codes stay exact fp16 values
-  float sv_cur = 1.f;
   f4 acc[NBC][NB];
 #pragma unroll
   for (int cb = 0; cb < NBC; ++cb) {
@@ -683,7 +694,7 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
       d.k = ok ? ko : 0;
       d.v = ok ? vo : 0;
       d.sk = ok && kc == C_FP8 ? a.scale[((size_t)pq * a.hkv + h) * 2 + 0] : 1.f;
-      d.sv = ok && vc == C_FP8 ? a.scale[((size_t)pq * a.hkv + h) * 2 + 1] : 1.f;
+      d.sv = ok && vc == C_FP8 ? fp8_v_scale_word(a.scale[((size_t)pq * a.hkv + h) * 2 + 1]) : 64.f;
       d.valid = ok ? min(P, L - lp * P) : 0;
       d.codec = ok ? cod : 0;
       if (!ok) ++nerr;
@@ -698,7 +709,7 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
     auto meta = [&](int i) {
       TileMeta m;
       m.j0 = c0 + 16 * i;
-      m.koff = 0; m.voff = 0; m.sk = 1.f; m.sv = 1.f; m.valid = 0; m.sub = 0;
+      m.koff = 0; m.voff = 0; m.sk = 1.f; m.sv = 64.f; m.valid = 0; m.sub = 0;
       m.kc = KC == C_ANY ? 0 : KC;
       m.vc = VC == C_ANY ? 0 : VC;
       if (i >= nt) return m;
@@ -763,25 +774,17 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
         const float fB = is_int(kcB) ? a.scale_log2 : a.scale_log2 * mB.sk;
         const bool masked = offA || offB || mA.j0 < w_lo_max || mB.j0 + 16 > w_hi_min;
 
-        // ---- FP8 V scales: acc is kept in units of sv_cur. A tile that attends
-        // nothing takes its partner's scale; two different scales (a pair
-        // across pages) split the P.V in two, with a rescale between the halves
-        const float svB = offB ? mA.sv : mB.sv;
-        const float svA = offA ? svB : mA.sv;
+        // ---- FP8 V scales in the log domain (log2|s| = 0, 1/|s| = 1 for the
+        // other codecs and for dead tiles)
+        const float lsvA = fabsf(mA.sv) - 64.f, lsvB = fabsf(mB.sv) - 64.f;
+        const float isvA = lsvA == 0.f ? 1.f : __builtin_amdgcn_exp2f(-lsvA);
+        const float isvB = lsvB == 0.f ? 1.f : __builtin_amdgcn_exp2f(-lsvB);
+        const bool negA = mA.sv < 0.f, negB = mB.sv < 0.f;
         // BF16 V tiles go to the bf16 MFMA: a pair with one of them and one tile
-        // of another codec is split in two halves as well
+        // of another codec is split in two halves
         constexpr bool VB = VC == C_BF16 || VC == C_ANY;
         const bool vbfA = VB && vcA == C_BF16, vbfB = VB && vcB == C_BF16;
-        const bool split = svA != svB || vbfA != vbfB;
-        if (svA != sv_cur) {
-          const float r = sv_cur / svA;
-#pragma unroll
-          for (int cb = 0; cb < NBC; ++cb)
-#pragma unroll
-            for (int n = 0; n < NB; ++n) acc[cb][n] *= r;
-          sv_cur = svA;
-        }
-        const float r_split = svA / svB;
+        const bool split = vbfA != vbfB;
 
         const bool vint = is_int(vcA) || is_int(vcB);
         // INT2 V (a pair holding one): its value z + s*u is the sum of an offset
@@ -813,8 +816,8 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
               s8[4 + j] = (mB.valid > 0 && pb_ >= lo_col[cb] && pb_ < hi_col[cb]) ? s8[4 + j] : NEG_INF;
             }
           }
-          const float mxa = fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])) * fA;
-          const float mxb = fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])) * fB;
+          const float mxa = __builtin_fmaf(fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])), fA, lsvA);
+          const float mxb = __builtin_fmaf(fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])), fB, lsvB);
           const float mx = row4_max(fmaxf(mxa, mxb));
           const float m_new = fmaxf(m_run[cb], mx);
           if (__any(m_new > m_run[cb])) {
@@ -830,12 +833,22 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
           }
           const float mu = m_run[cb] == NEG_INF ? 0.f : m_run[cb];
           float p[8];
+          const float oA = lsvA - mu, oB = lsvB - mu;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s8[j], fA, -mu));
-            p[4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s8[4 + j], fB, -mu));
+            p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s8[j], fA, oA));
+            p[4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s8[4 + j], fB, oB));
           }
-          l_run[cb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+          l_run[cb] += __builtin_fmaf((p[0] + p[1]) + (p[2] + p[3]), isvA, ((p[4] + p[5]) + (p[6] + p[7])) * isvB);
+          // a negative FP8 V scale flips its tile's weights
+          if (negA) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[j] = -p[j];
+          }
+          if (negB) {
+#pragma unroll
+            for (int j = 4; j < 8; ++j) p[j] = -p[j];
+          }
           if constexpr (VB) {
             if (vbfA || vbfB) bf_split_w8(p, pbh[cb], pbl[cb]);
           }
@@ -925,14 +938,9 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
           const _Float16 z = 0;
           pv([z](h8 w) { return h8{w[0], w[1], w[2], w[3], z, z, z, z}; }, [](u4 w) { return u4{w[0], w[1], 0u, 0u}; },
              vbfA);
-#pragma unroll
-          for (int cb = 0; cb < NBC; ++cb)
-#pragma unroll
-            for (int n = 0; n < NB; ++n) acc[cb][n] *= r_split;
           pv([z](h8 w) { return h8{z, z, z, z, w[4], w[5], w[6], w[7]}; }, [](u4 w) { return u4{0u, 0u, w[2], w[3]}; },
              vbfB);
         }
-        if (split) sv_cur = svB;
       }
     }
   }
@@ -967,11 +975,11 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
       const size_t r = ((size_t)b * T + t) * a.hq + (size_t)h * G + g;
       if (a.final_out) {
 #pragma unroll
-        for (int n = 0; n < NB; ++n) a.out[r * D + 16 * n + col] = lj > 0.f ? acc[cb][n][j] * sv_cur / lj : 0.f;
+        for (int n = 0; n < NB; ++n) a.out[r * D + 16 * n + col] = lj > 0.f ? acc[cb][n][j] / lj : 0.f;
       } else {
         float* dst = a.part_acc + (r * a.nparts + part) * D;
 #pragma unroll
-        for (int n = 0; n < NB; ++n) dst[16 * n + col] = acc[cb][n][j] * sv_cur;
+        for (int n = 0; n < NB; ++n) dst[16 * n + col] = acc[cb][n][j];
       }
     }
   }

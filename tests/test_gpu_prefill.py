@@ -15,7 +15,7 @@ import paged_kv_cache_182_amd as pkv
 import synth
 from synth.device import to_device
 from synth.layout import BF16, BIT1, FP8, FP16, INT2, INT4, INT8
-from gpu_util import compare, params_for, poison_tails, rewrite_bf16
+from gpu_util import compare, params_for, poison_tails, rewrite_bf16, run
 
 pytestmark = pytest.mark.gpu
 
@@ -389,3 +389,24 @@ def test_int2_large_values(dim):
                            outlier_frac=1.0, outlier_mult=16.0))
     check(w, 24, partition_tokens=64)
     check(w, 24, partition_tokens=0, k_codec=pkv.CODEC_MIXED, v_codec=pkv.CODEC_MIXED)
+
+
+@pytest.mark.parametrize("dim", [64, 128])
+def test_fp8_v_scales_sign_zero_and_tiny(dim):
+    """FP8 V page scales enter the softmax in the log domain: 16-token pages
+    (every pair of tiles spans two pages) with scales of both signs, a zero
+    scale (its codes decode to zero whatever they hold) and one of 2^-50
+    (taken as 2^-40: its values move by less than 4.1e-10), through the
+    prefill and, the same pages, the decode kernel, against the oracle."""
+    print(f"case fp8 v scales dim={dim}", flush=True)
+    w = small([700, 64, 1500, 33], FP8, FP8, hq=16, hkv=2, dim=dim, page=16)
+    rng = np.random.default_rng(dim)
+    sc = w.page_scale.copy()
+    sc[:, :, 1] *= rng.choice([-1.0, 1.0], size=sc.shape[:2]) * rng.uniform(0.5, 2.0, size=sc.shape[:2])
+    sc[w.block_table[0, 3], :, 1] = 0.0
+    sc[w.block_table[2, 10], :, 1] = 2.0 ** -50
+    w.page_scale[...] = sc.astype(w.page_scale.dtype)
+    check(w, 24, partition_tokens=0, q_scale=2.0)
+    check(w, 5, partition_tokens=64)
+    out, lse = run(to_device(w), params_for(w, 0))
+    compare(out, lse, *oracle.decode_attention(w), f"decode {w.name}")
