@@ -13,7 +13,7 @@
 //
 // Work unit: one workgroup of four waves owns (partition, KV head, row, group
 // of 128 query columns), a column being one (query token, query head of the
-// KV head's group) pair; each wave owns 32 columns. The partition's 16-token
+// KV head's group) pair; each wave owns 16 NBC (32) columns. The partition's 16-token
 // tiles go two at a time: each pair is converted once, by the whole
 // workgroup, from its page codes into an fp16 image in LDS (double-buffered,
 // one barrier per pair); each wave then reads the image as MFMA operands:
@@ -596,8 +596,8 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(pr
   auto lo_of = [&](int t) { return a.window > 0 ? max(p_lo, L - T + t + 1 - a.window) : p_lo; };
   const int wg_lo = lo_of(c_first / G);
   // this wave's columns
-  const int w_first = c_first + 32 * wave;
-  const int w_last = min(w_first + 32, ncols) - 1;
+  const int w_first = c_first + 16 * NBC * wave;
+  const int w_last = min(w_first + 16 * NBC, ncols) - 1;
   const bool wave_live = w_first < ncols;
   const int w_hi_min = hi_of(w_first / G);
   const int w_hi_max = wave_live ? hi_of(w_last / G) : p_lo;
