@@ -32,15 +32,21 @@ constexpr int decode_waves_per_simd(int head_dim, int k_codec, int v_codec) {
   return (k_codec == 2 && v_codec == 2) ? 4 : 3;
 }
 
-// Waves per SIMD of the prefill kernel for (head_dim, K codec, V codec) as
-// compiled (its register count decides): at head_dim 64 three for a 16-bit
-// or FP8 pair, two for the group-scale pairs, one for the per-page dispatch
-// variant; at 128 two for a 16-bit or FP8 pair, one otherwise. Sizes the
-// library-chosen prefill partition count.
+// Pairs launch_prefill instantiates (FP16, BF16 and FP8 with themselves,
+// INT8-K with INT4-V); every other pair runs the per-page kernel.
+constexpr bool prefill_pair_kernel(int k_codec, int v_codec) {
+  return (k_codec == v_codec && k_codec >= 0 && k_codec <= 2) || (k_codec == 3 && v_codec == 4);
+}
+// Waves per SIMD of the prefill kernel for (head_dim, K codec, V codec): the
+// occupancy asked of the compiler (as its minimum) and the one the
+// library-chosen prefill partition count is sized for. At head_dim 64 four
+// for FP16 and FP8 (128 VGPRs), three for BF16 (125: its query's bf16
+// parts), two for INT8/INT4 (at three it spills); at 128 two for the 16-bit
+// and FP8 pairs, one for INT8/INT4; one for the per-page kernel.
 constexpr int prefill_waves_per_simd(int head_dim, int k_codec, int v_codec) {
-  const bool fp_pair = k_codec >= 0 && k_codec <= 2 && k_codec == v_codec;
-  const bool per_page = k_codec < 0 || v_codec < 0;  // the per-page dispatch kernel: one wave per SIMD
-  return head_dim == 64 ? (fp_pair ? 3 : (per_page ? 1 : 2)) : (fp_pair ? 2 : 1);
+  if (!prefill_pair_kernel(k_codec, v_codec)) return 1;
+  if (head_dim == 64) return k_codec == 0 || k_codec == 2 ? 4 : (k_codec == 1 ? 3 : 2);
+  return k_codec <= 2 ? 2 : 1;
 }
 
 // Everything one decode launch needs, resolved on the host.

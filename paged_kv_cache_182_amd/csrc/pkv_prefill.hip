@@ -542,12 +542,12 @@ __device__ inline void tile_scores(const u4* kimg, const float* ks, const float*
 }
 
 // ---------------------------------------------------------------- kernel
-// Waves per SIMD asked of the compiler: two where the pair's registers fit in
-// half the file, one for the group-scale variants at head_dim 128 and for the
-// per-page dispatch variant (at head_dim 64 it spilled at two).
+// Waves per SIMD asked of the compiler (its minimum occupancy), as the host
+// sizes the partitions: see prefill_waves_per_simd (the per-page dispatch
+// variant, one, spilled at two at head_dim 64).
 template <int D, int KC, int VC>
 __host__ __device__ constexpr int prefill_waves() {
-  return (KC == C_ANY || VC == C_ANY || (D == 128 && (is_int(KC) || is_int(VC)))) ? 1 : 2;
+  return prefill_waves_per_simd(D, KC == C_ANY ? -1 : KC, VC == C_ANY ? -1 : VC);
 }
 
 template <int D, int KC, int VC>
