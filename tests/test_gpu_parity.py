@@ -100,6 +100,21 @@ def test_empty_rows_and_partitions():
     check(ws)
 
 
+def test_many_short_rows():
+    """1,500 rows of 0 to 200 tokens (a decode batch of short sequences): rows x
+    KV heads far above one round of resident workgroups, so the library picks
+    one partition per row and writes out/lse directly; and 64-token
+    partitions, folded."""
+    print("case many short rows", flush=True)
+    rng = np.random.default_rng(11)
+    lens = rng.integers(0, 201, 1500).tolist()
+    lens[:3] = [0, 1, 200]
+    w = small(lens, FP8, FP8, hq=8, hkv=2, dim=64, page=16)
+    assert pkv.num_partitions(params_for(w, 0)) == 1
+    check(w, partition_tokens=0)
+    check(w, partition_tokens=64)
+
+
 # ------------------------------------------------ partitions finer than a page, even splits
 @pytest.mark.parametrize("kc,vc,page", [(FP8, FP8, 64), (INT8, INT4, 64), (FP16, FP16, 1024), (None, None, 1024)])
 def test_sub_page_partitions(kc, vc, page):
