@@ -200,6 +200,16 @@ def test_prefill_partitions_and_workspace():
     n = pkv.prefill_num_partitions(auto, 64)
     assert n == 512 // 8
     assert pkv.prefill_num_partitions(auto, 64, 5, 5) == 1   # empty window
+    # the same count per kernel as it runs (its waves per SIMD): 256 compute
+    # units x waves over 8 workgroups per partition index; pairs without a
+    # kernel of their own run the one-wave per-page kernel
+    waves = {(64, pkv.FP16, pkv.FP16): 4, (64, pkv.FP8_E4M3, pkv.FP8_E4M3): 4, (64, pkv.BF16, pkv.BF16): 3,
+             (64, pkv.INT8_G32, pkv.INT4_G32): 2, (64, pkv.FP8_E4M3, pkv.FP16): 1,
+             (128, pkv.FP16, pkv.FP16): 2, (128, pkv.BF16, pkv.BF16): 2, (128, pkv.INT8_G32, pkv.INT4_G32): 1,
+             (128, pkv.FP8_E4M3, pkv.FP16): 1, (128, pkv.INT4_G32, pkv.INT8_G32): 1}
+    for (d, kc, vc), wv in waves.items():
+        q = base(partition_tokens=0, head_dim=d, k_codec=kc, v_codec=vc)
+        assert pkv.prefill_num_partitions(q, 64) == 256 * wv // 8, (d, kc, vc)
 
 
 def test_prefill_host_checks():
