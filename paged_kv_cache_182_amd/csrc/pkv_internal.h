@@ -27,8 +27,9 @@ constexpr int decode_waves_per_simd(int head_dim, int k_codec, int v_codec) {
   if (k_codec == -2 && v_codec == -2) return head_dim == 64 ? 4 : 2;  // float pages only
   if (!decode_pair_kernel(k_codec, v_codec)) return head_dim == 64 ? 3 : 2;
   const bool one_scale = k_codec <= 2 && v_codec <= 2;
-  // BF16 at head_dim 64 keeps its query's bf16 parts in registers: five waves
-  if (head_dim == 64) return one_scale ? (k_codec == 1 ? 5 : 6) : 4;
+  // BF16 at head_dim 64 keeps its query's bf16 parts in registers: five
+  // waves; INT8 with itself (95 VGPRs) five, the other group-scale pairs four
+  if (head_dim == 64) return one_scale ? (k_codec == 1 ? 5 : 6) : (k_codec == 3 && v_codec == 3 ? 5 : 4);
   return (k_codec == 2 && v_codec == 2) ? 4 : 3;
 }
 
