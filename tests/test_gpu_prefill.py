@@ -408,5 +408,9 @@ def test_fp8_v_scales_sign_zero_and_tiny(dim):
     w.page_scale[...] = sc.astype(w.page_scale.dtype)
     check(w, 24, partition_tokens=0, q_scale=2.0)
     check(w, 5, partition_tokens=64)
-    out, lse = run(to_device(w), params_for(w, 0))
-    compare(out, lse, *oracle.decode_attention(w), f"decode {w.name}")
+    # the same pages declared per page: the per-page (any codec) kernels
+    mixed = dict(k_codec=pkv.CODEC_MIXED, v_codec=pkv.CODEC_MIXED)
+    check(w, 24, partition_tokens=0, q_scale=2.0, **mixed)
+    for pk in ({}, mixed):
+        out, lse = run(to_device(w), params_for(w, 0, **pk))
+        compare(out, lse, *oracle.decode_attention(w), f"decode {w.name} {pk}")
