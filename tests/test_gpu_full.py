@@ -48,3 +48,38 @@ def test_full_config(cid):
         return
     ref_o, ref_l = oracle.decode_attention(w)
     compare(out, lse, ref_o, ref_l, f"config {cid}")
+
+
+def test_full_prefill_chunk_1m():
+    """The chunked prefill at the size the benchmark times: a 64-token chunk
+    (q = fp16(3.6 z)) over the 1M-token FP8 cache with library-chosen
+    partitions. Every output is finite and run-to-run identical; the first and
+    last query tokens of both KV heads are compared with the oracle over their
+    causal keys (all the cache before them)."""
+    print("case full prefill chunk 64 over 1M", flush=True)
+    from oracle.attention import _softmax_attention, gather_kv
+    w = synth.config(5)
+    dw = to_device(w)
+    p = params_for(w, 0)
+    T, G = 64, w.num_q_heads // w.num_kv_heads
+    q = synth.prefill_queries(11, 1, T, w.num_q_heads, w.head_dim, 3.6)
+    qd = torch.from_numpy(q).cuda()
+    args = (qd, dw.pool, dw.page_k_off, dw.page_v_off, dw.page_codec, dw.page_scale, dw.block_table, dw.seq_lens)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, lse = pkv.prefill_attention(p, *args, err_count=err)
+    out2, lse2 = pkv.prefill_attention(p, *args)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    out, lse = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    assert np.array_equal(out, out2.cpu().numpy()) and np.array_equal(lse, lse2.cpu().numpy())
+    L = int(w.seq_lens[0])
+    for h in range(w.num_kv_heads):
+        K, V = gather_kv(w, 0, h)
+        for t in (0, T - 1):
+            n = L - T + t + 1  # keys at positions 0 .. L - T + t
+            qh = q[0, t, h * G:(h + 1) * G].astype(np.float64)
+            ref_o, ref_l = _softmax_attention(K[:n], V[:n], qh, w.softmax_scale)
+            compare(out[0, t, h * G:(h + 1) * G], lse[0, t, h * G:(h + 1) * G], ref_o, ref_l,
+                    f"prefill 1M query token {t} KV head {h}")
+        del K, V
