@@ -83,3 +83,38 @@ def test_full_prefill_chunk_1m():
             compare(out[0, t, h * G:(h + 1) * G], lse[0, t, h * G:(h + 1) * G], ref_o, ref_l,
                     f"prefill 1M query token {t} KV head {h}")
         del K, V
+
+
+def test_full_window_decode_1m():
+    """Sliding-window decode as the benchmark times it: the 1M-token FP8 row
+    with a window of 8,192 positions, library-chosen partitions, the row's
+    end at three of the benchmark's spots (the first, one inside a page, the
+    last); every query head against the oracle over the window's keys."""
+    print("case full window decode 1M", flush=True)
+    from oracle.attention import _softmax_attention, gather_kv
+    w = synth.config(5)
+    dw = to_device(w)
+    p = params_for(w, 0)
+    W = 8192
+    p.window_tokens = W
+    G = w.num_q_heads // w.num_kv_heads
+    L = int(w.seq_lens[0])
+    ends = np.linspace(W + 4096, L, 64).astype(np.int64)
+    picks = [int(ends[0]), int(ends[17]), int(ends[-1])]
+    assert picks[1] % w.page_size != 0
+    base = list(dw.args())
+    res = {}
+    for e in picks:
+        base[7] = torch.tensor([e], dtype=torch.int32, device="cuda")
+        out, lse = pkv.decode_attention(p, *base)
+        torch.cuda.synchronize()
+        res[e] = (out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))
+    for h in range(w.num_kv_heads):
+        K, V = gather_kv(w, 0, h)
+        qh = w.q[0, h * G:(h + 1) * G].astype(np.float64)
+        for e in picks:
+            ref_o, ref_l = _softmax_attention(K[e - W:e], V[e - W:e], qh, w.softmax_scale)
+            out, lse = res[e]
+            compare(out[0, h * G:(h + 1) * G], lse[0, h * G:(h + 1) * G], ref_o, ref_l,
+                    f"window {W} ending at {e}, KV head {h}")
+        del K, V
