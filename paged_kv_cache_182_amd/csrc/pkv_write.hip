@@ -51,6 +51,7 @@ __device__ inline bool w16(int c) { return c == W_FP16 || c == W_BF16; }
 __host__ __device__ constexpr bool wint(int c) { return c == W_INT8 || c == W_INT4; }
 // codecs with one fp16 scale per (token, 32 dims), in the grouped K order
 __host__ __device__ constexpr bool wgrp(int c) { return wint(c) || c == W_INT2 || c == W_BIT1; }
+__host__ __device__ constexpr bool wsub(int c) { return c == W_INT2 || c == W_BIT1; }
 
 __device__ inline uint64_t wplane_bytes(int c, int hkv, int page, int d) {
   const uint64_t codes = (uint64_t)hkv * page * d * wbits(c) / 8;
@@ -694,13 +695,14 @@ __device__ inline void load_unit(UnitSrc<D, NT>& u, const uint8_t* sp, bool grou
 }
 
 // Encode one tile's destination run from the lane's eight-element source
-// chunks x[c] (elements 8c .. 8c+7 of the run) and write it. INT scales come
-// as s2[j][g] with their reciprocals r2: element e uses entry (e % 4, e / 8)
-// (for V runs: token 4(lane/16) + e % 4, group e / 8; grouped K runs fill
-// every j of group g alike).
-template <int D, int DC, bool BF>
-__device__ inline void store_run(const u4* x, const float (*s2)[D / 32], const float (*r2)[D / 32],
-                                 const float (*z2)[D / 32], float s8, float r8, bool fast8, uint8_t* td, int lane) {
+// chunks x[c] (elements 8c .. 8c+7 of the run) and write it. Group
+// parameters (INT scale s, its reciprocal r, INT2 offset z) come per chunk:
+// gp(g, s, r, z) fills entry j = 0..3 for chunk g, and element 8g + k uses
+// entry k % 4 (for V runs: token 4(lane/16) + k % 4, group g; grouped K runs
+// fill every j alike). They are fetched when the chunk is encoded, so a V
+// run's 16 groups need not stay in registers across the tile.
+template <int D, int DC, bool BF, class GP>
+__device__ inline void store_run(const u4* x, GP&& gp, float s8, float r8, bool fast8, uint8_t* td, int lane) {
   constexpr int BITS = wbits(DC);
   constexpr int E = D / 4, RD = D * BITS / 32;
   constexpr int NWD = RD < 4 ? 1 : RD / 4;
@@ -727,30 +729,41 @@ __device__ inline void store_run(const u4* x, const float (*s2)[D / 32], const f
     // rounds it to the nearest integer with ties to even (as rint) and leaves
     // that integer's two's complement in the low bits of the sum
     constexpr float MAGIC = 12582912.0f;
-    uint32_t cw[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float v = chunk_elem<BF>(x[e >> 3], e & 7);
-      const float q = __builtin_amdgcn_fmed3f(recip_div0(v, s2[e & 3][e >> 3], r2[e & 3][e >> 3]), -QMAX, QMAX);
-      cw[e] = __builtin_bit_cast(uint32_t, q + MAGIC);
-    }
-    if constexpr (DC == W_INT8) {
-      // bytes in element order: elements 4k .. 4k+3 in word k
+    for (int g = 0; g < E / 8; ++g) {
+      float s[4], r[4], z[4];
+      gp(g, s, r, z);
+      uint32_t cw[8];
 #pragma unroll
-      for (int k = 0; k < NWD; ++k) {
-        const uint32_t lo = __builtin_amdgcn_perm(cw[4 * k + 1], cw[4 * k], 0x0C0C0400u);
-        const uint32_t hi = __builtin_amdgcn_perm(cw[4 * k + 3], cw[4 * k + 2], 0x04000C0Cu);
-        word[k] = lo | hi;
+      for (int k = 0; k < 8; ++k) {
+        const float q = __builtin_amdgcn_fmed3f(recip_div0(chunk_elem<BF>(x[g], k), s[k & 3], r[k & 3]), -QMAX, QMAX);
+        cw[k] = __builtin_bit_cast(uint32_t, q + MAGIC);
       }
-    } else {
-      // eight codes per word: element 2m at bits 4m, element 2m + 1 at 16 + 4m
+      if constexpr (DC == W_INT8) {
+        // bytes in element order: elements 4k .. 4k+3 in word k
 #pragma unroll
-      for (int k = 0; k < NWD; ++k)
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t lo = __builtin_amdgcn_perm(cw[4 * h + 1], cw[4 * h], 0x0C0C0400u);
+          const uint32_t hi = __builtin_amdgcn_perm(cw[4 * h + 3], cw[4 * h + 2], 0x04000C0Cu);
+          word[2 * g + h] = lo | hi;
+        }
+      } else {
+        // eight codes per word: element 2m at bits 4m, element 2m + 1 at 16 + 4m
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const uint32_t pr = __builtin_amdgcn_perm(cw[8 * k + 2 * m + 1], cw[8 * k + 2 * m], 0x0C040C00u) & 0x000F000Fu;
-          word[k] |= pr << (4 * m);
+          const uint32_t pr = __builtin_amdgcn_perm(cw[2 * m + 1], cw[2 * m], 0x0C040C00u) & 0x000F000Fu;
+          word[g] |= pr << (4 * m);
         }
+      }
+    }
+  } else if constexpr (DC == W_INT2) {
+#pragma unroll
+    for (int g = 0; g < E / 8; ++g) {
+      float s[4], r[4], z[4];
+      gp(g, s, r, z);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        put_code<BITS, E>(word, 8 * g + k, affine2_code_r(chunk_elem<BF>(x[g], k), z[k & 3], s[k & 3], r[k & 3]));
     }
   } else {
 #pragma unroll
@@ -761,10 +774,8 @@ __device__ inline void store_run(const u4* x, const float (*s2)[D / 32], const f
         code = __builtin_bit_cast(uint16_t, (_Float16)v);
       } else if constexpr (DC == W_BF16) {
         code = f_to_bf16(v);
-      } else if constexpr (DC == W_INT2) {
-        code = affine2_code_r(v, z2[e & 3][e >> 3], s2[e & 3][e >> 3], r2[e & 3][e >> 3]);
       } else {
-        static_assert(DC == W_BIT1, "INT8 and INT4 codes are made above");
+        static_assert(DC == W_BIT1, "INT8, INT4 and INT2 codes are made above");
         code = v < 0.f ? 1u : 0u;
       }
       put_code<BITS, E>(word, e, code);
@@ -774,18 +785,35 @@ __device__ inline void store_run(const u4* x, const float (*s2)[D / 32], const f
 }
 
 // DK: the destination codec pair (K low nibble, V high nibble) the kernel is
-// specialised for (FP8/FP8), else -1 (any pair of FP16, BF16, FP8, INT8 and
-// INT4, chosen per plane at run time) or -2 (any pair with an INT2 or BIT1
-// plane: their reductions and packing are built only here, so the other
-// kernels keep their registers). A call has one destination pair. (An
-// INT8/INT4 specialisation held as many registers as the generic kernel and
-// is not built.)
+// specialised for (FP8/FP8, INT2/INT2, BIT1/BIT1), else -1 (any pair of FP16,
+// BF16, FP8, INT8 and INT4, chosen per plane at run time) or -2 (any other
+// pair with an INT2 or BIT1 plane: their reductions and packing are built only
+// here and in the two sub-byte specialisations, so the other kernels keep
+// their registers). A call has one destination pair. (An INT8/INT4
+// specialisation held as many registers as the generic kernel and is not
+// built.)
+// Waves per SIMD the register kernels are compiled for, where a unit holds at
+// most 128 x 16 source elements (measured on demotions of 14,720 16-token
+// pages at head_dim 128: the generic kernel at four waves 300-309 us against
+// 344-352 at three, INT2/INT2 at four 347-365 us against 364-369 at three,
+// BIT1/BIT1 at three, its fp64 sums spilling at four). Larger units keep the
+// compiler's choice.
 template <int D, int NT, int DK>
-__global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int nunits) {
+__host__ __device__ constexpr int enc_waves() {
+  if (D * NT > 128) return 1;
+  if (DK == -1 || DK == (W_INT2 | W_INT2 << 4)) return 4;
+  if (DK == (W_BIT1 | W_BIT1 << 4)) return 3;
+  return 1;
+}
+template <int D, int NT, int DK>
+__global__ void __launch_bounds__(64 * EW) __attribute__((amdgpu_waves_per_eu(enc_waves<D, NT, DK>()))) encode_reg_kernel(EncodeArgs a, int nunits) {
   constexpr int NC = D / 32;
-  __shared__ float sx[EW][4][16];  // per wave: INT V scales of its tile, [row][combo]
-  __shared__ float rx[EW][4][16];  // and their reciprocals RN(1 / s)
-  __shared__ float zx[EW][4][16];  // INT2 V offsets
+  constexpr bool SUBK = DK == -2 || (DK >= 0 && (wsub(DK & 15) || wsub(DK >> 4)));  // builds the INT2/BIT1 paths
+  // per wave, the group parameters of its V tile: [row][4 g + j] for group g
+  // of the row's token j (chunk-major: one 16-byte read gives a chunk's four)
+  __shared__ float sx[EW][4][16];  // INT scales
+  __shared__ float rx[EW][4][16];  // their reciprocals RN(1 / s)
+  __shared__ float zx[EW][4][16];  // INT2 offsets
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int gw = blockIdx.x * EW + wv, nw = gridDim.x * EW;
@@ -801,7 +829,10 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
   // in registers (the FP8 kernel, free of the INT scale state, holds two
   // 64-token units at head_dim 128 in 224 VGPRs); larger units are loaded at
   // the start of their turn and other waves hide the latency
-  constexpr bool PREFETCH = NT * NC <= (DK == (W_FP8 | W_FP8 << 4) ? 16 : 8);
+  // (INT2/INT2 one-tile units at head_dim 128 go without it: they fit four
+  // waves per SIMD only so, and other waves hide the load)
+  constexpr bool PREFETCH = !(DK == (W_INT2 | W_INT2 << 4) && D == 128 && NT == 1) &&
+                            NT * NC <= (DK == (W_FP8 | W_FP8 << 4) ? 16 : 8);
   UnitSrc<D, NT> cur, nxt;
   int u = gw;
   bool have = false;
@@ -873,7 +904,7 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
           for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int g = 0; g < NC; ++g) s2[j][g] = r2[j][g] = 1.f, z2[j][g] = 0.f;
-          if (DK == -2 && wgrp(dcodec) && !wint(dcodec)) {
+          if (SUBK && wsub(dcodec)) {
             // INT2 (offset and step per group) and BIT1 (mean magnitude per group)
             const size_t sc_base = (size_t)hkv * P * D * dbits / 8 + ((size_t)h * P + 16 * t) * NC * 2;
             const size_t zgap = (size_t)hkv * P * NC * 2;
@@ -908,26 +939,16 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
                 mine_s = sign1_scale(row16_scatter<NCB>(sm, l16, [](double a, double b) { return a + b; }));
               }
               if (l16 < 4 * NC) {
-                sx[wv][kq][l16] = mine_s;
-                zx[wv][kq][l16] = mine_z;
-                if (aff) rx[wv][kq][l16] = recip_fp16_scale(mine_s);
                 const int j = l16 / NC, g = l16 % NC;
+                sx[wv][kq][4 * g + j] = mine_s;
+                zx[wv][kq][4 * g + j] = mine_z;
+                if (aff) rx[wv][kq][4 * g + j] = recip_fp16_scale(mine_s);
                 const size_t at = sc_base + ((size_t)(4 * kq + j) * NC + g) * 2;
                 *reinterpret_cast<_Float16*>(a.pool + dof + at) = (_Float16)mine_s;
                 if (aff) *reinterpret_cast<_Float16*>(a.pool + dof + at + zgap) = (_Float16)mine_z;
               }
               __builtin_amdgcn_wave_barrier();
               __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int g = 0; g < NC; ++g) {
-                  s2[j][g] = sx[wv][kq][j * NC + g];
-                  z2[j][g] = zx[wv][kq][j * NC + g];
-                  if (aff) r2[j][g] = rx[wv][kq][j * NC + g];
-                }
-              __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-              __builtin_amdgcn_wave_barrier();
             } else {
               // grouped K: chunk c is group c of token lane%16, spread over the 4 rows
 #pragma unroll
@@ -987,22 +1008,13 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
               const float mine = bits16_to_float<BF>(row16_scatter_pairs<NCB>(kw, l16, pk_max_i16));
               if (l16 < 4 * NC) {
                 const _Float16 s16 = scale_of(mine);
-                sx[wv][kq][l16] = (float)s16;
-                rx[wv][kq][l16] = recip_fp16_scale((float)s16);
                 const int j = l16 / NC, g = l16 % NC;
+                sx[wv][kq][4 * g + j] = (float)s16;
+                rx[wv][kq][4 * g + j] = recip_fp16_scale((float)s16);
                 *reinterpret_cast<_Float16*>(a.pool + dof + sc_base + ((size_t)(4 * kq + j) * NC + g) * 2) = s16;
               }
               __builtin_amdgcn_wave_barrier();
               __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int g = 0; g < NC; ++g) {
-                  s2[j][g] = sx[wv][kq][j * NC + g];
-                  r2[j][g] = rx[wv][kq][j * NC + g];
-                }
-              __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-              __builtin_amdgcn_wave_barrier();
             } else {
               // grouped K: chunk c is group c of token lane%16, spread over the 4 rows
 #pragma unroll
@@ -1024,21 +1036,40 @@ __global__ void __launch_bounds__(64 * EW) encode_reg_kernel(EncodeArgs a, int n
             }
           }
           uint8_t* td = dp + (size_t)t * 16 * D * dbits / 8;
-          const bool sub = DK == -2 && (dcodec == W_INT2 || dcodec == W_BIT1);
+          // group parameters of chunk g: a V tile's from its wave's LDS rows,
+          // a grouped K tile's from the lane's registers
+          auto gp = [&](int g, float (&gs)[4], float (&gr)[4], float (&gz)[4]) {
+            if (is_v) {
+              const float4 vs = *reinterpret_cast<const float4*>(&sx[wv][kq][4 * g]);
+              const float4 vr = *reinterpret_cast<const float4*>(&rx[wv][kq][4 * g]);
+              const float4 vz = *reinterpret_cast<const float4*>(&zx[wv][kq][4 * g]);
+              gs[0] = vs.x; gs[1] = vs.y; gs[2] = vs.z; gs[3] = vs.w;
+              gr[0] = vr.x; gr[1] = vr.y; gr[2] = vr.z; gr[3] = vr.w;
+              gz[0] = vz.x; gz[1] = vz.y; gz[2] = vz.z; gz[3] = vz.w;
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) gs[j] = s2[j][g], gr[j] = r2[j][g], gz[j] = z2[j][g];
+            }
+          };
+          const bool sub = SUBK && wsub(dcodec);
           if (sub) {
-            if constexpr (DK == -2) {
-              if (dcodec == W_INT2) store_run<D, W_INT2, BF>(x, s2, r2, z2, s8, r8, fast8, td, lane);
-              else store_run<D, W_BIT1, BF>(x, s2, r2, z2, s8, r8, fast8, td, lane);
+            if constexpr (SUBK) {
+              if (dcodec == W_INT2) store_run<D, W_INT2, BF>(x, gp, s8, r8, fast8, td, lane);
+              else store_run<D, W_BIT1, BF>(x, gp, s8, r8, fast8, td, lane);
             }
           } else {
             switch (dcodec) {
-              case W_FP16: store_run<D, W_FP16, BF>(x, s2, r2, z2, s8, r8, fast8, td, lane); break;
-              case W_BF16: store_run<D, W_BF16, BF>(x, s2, r2, z2, s8, r8, fast8, td, lane); break;
-              case W_FP8: store_run<D, W_FP8, BF>(x, s2, r2, z2, s8, r8, fast8, td, lane); break;
-              case W_INT8: store_run<D, W_INT8, BF>(x, s2, r2, z2, s8, r8, fast8, td, lane); break;
-              default: store_run<D, W_INT4, BF>(x, s2, r2, z2, s8, r8, fast8, td, lane); break;
+              case W_FP16: store_run<D, W_FP16, BF>(x, gp, s8, r8, fast8, td, lane); break;
+              case W_BF16: store_run<D, W_BF16, BF>(x, gp, s8, r8, fast8, td, lane); break;
+              case W_FP8: store_run<D, W_FP8, BF>(x, gp, s8, r8, fast8, td, lane); break;
+              case W_INT8: store_run<D, W_INT8, BF>(x, gp, s8, r8, fast8, td, lane); break;
+              default: store_run<D, W_INT4, BF>(x, gp, s8, r8, fast8, td, lane); break;
             }
           }
+          // the V parameters are read above before the next tile or unit
+          // writes its own (same wave, in order; the fence orders the compiler)
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+          __builtin_amdgcn_wave_barrier();
         }
       };
       if (scodec == W_BF16) work(std::integral_constant<bool, true>{});
@@ -1093,8 +1124,17 @@ void launch_encode_reg(const EncodeArgs& a, hipStream_t s) {
   if (fp8) {
     hipLaunchKernelGGL((encode_reg_kernel<D, NT, W_FP8 | W_FP8 << 4>), dim3(wgs), dim3(64 * EW), 0, s, a, nunits);
   } else if (sub_byte_dst(a.dst_codec)) {
-    if constexpr (sub_reg_path(D, NT))
-      hipLaunchKernelGGL((encode_reg_kernel<D, NT, -2>), dim3(wgs), dim3(64 * EW), 0, s, a, nunits);
+    // the uniform INT2 and BIT1 pairs compile their own path alone (fewer
+    // registers, more waves per SIMD than the kernel for any sub-byte pair)
+    constexpr int I2 = W_INT2 | W_INT2 << 4, B1 = W_BIT1 | W_BIT1 << 4;
+    if constexpr (sub_reg_path(D, NT)) {
+      if (a.dst_codec == I2)
+        hipLaunchKernelGGL((encode_reg_kernel<D, NT, I2>), dim3(wgs), dim3(64 * EW), 0, s, a, nunits);
+      else if (a.dst_codec == B1)
+        hipLaunchKernelGGL((encode_reg_kernel<D, NT, B1>), dim3(wgs), dim3(64 * EW), 0, s, a, nunits);
+      else
+        hipLaunchKernelGGL((encode_reg_kernel<D, NT, -2>), dim3(wgs), dim3(64 * EW), 0, s, a, nunits);
+    }
   } else {
     hipLaunchKernelGGL((encode_reg_kernel<D, NT, -1>), dim3(wgs), dim3(64 * EW), 0, s, a, nunits);
   }

@@ -89,6 +89,8 @@ CASES = [  # (K codec, V codec, head_dim, page)
     # staged path (longer units)
     (INT2, INT2, 128, 16), (BIT1, BIT1, 128, 32), (INT2, BIT1, 64, 64), (BIT1, INT8, 64, 16),
     (INT8, INT2, 128, 64), (BIT1, BIT1, 128, 128), (INT2, FP8, 64, 256),
+    # the uniform INT2 and 1-bit pairs' own kernels: one-tile units at head_dim 128, head_dim 64 units
+    (BIT1, BIT1, 128, 16), (INT2, INT2, 64, 48), (BIT1, BIT1, 64, 16),
 ]
 
 
@@ -115,7 +117,7 @@ def test_encode_bytes_match_oracle(kc, vc, D, P, src_codec):
     assert np.array_equal(scale_t.cpu().numpy(), rs)
 
 
-@pytest.mark.parametrize("kc,vc,P", [(FP8, FP8, 64), (INT8, INT4, 16)])
+@pytest.mark.parametrize("kc,vc,P", [(FP8, FP8, 64), (INT8, INT4, 16), (INT2, INT2, 16), (BIT1, BIT1, 16)])
 def test_encode_many_units_sampled(kc, vc, P):
     """More (page, head, plane) units than the launch has waves (4,096
     workgroups x 4 waves), so waves loop and encode a prefetched second unit:
