@@ -1217,8 +1217,10 @@ __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, KC, VC>(), max_waves_per_eu<D
 }
 
 // ---------------------------------------------------------------- fold
-// Grid (row, 4-dim group), one wave each: spread over the whole chip, one
-// round of loads, no LDS. Lane l keeps a running log-sum-exp over the parts
+// Fold for many parts where the wide fold below does not apply (head_dim not
+// a multiple of 32, partials not 16-byte (acc) or 8-byte (m, l) aligned, more
+// than 512 parts). Grid (row, 4-dim group), one wave each: spread over the
+// whole chip, one round of loads, no LDS. Lane l keeps a running log-sum-exp over the parts
 // p = l + 64k (every load of a batch in flight together); the 64 lanes then
 // merge by a fixed butterfly (lane distance 32, 16, ..., 1), so results are
 // run-to-run identical.
@@ -1295,6 +1297,84 @@ __global__ void __launch_bounds__(64) combine_kernel(int nparts, int D, int vec,
     for (int j = 0; j < 4; ++j)
       if (d0 + j < D) o[j] = any ? A[j] / L : 0.f;
     if (blockIdx.y == 0) lse[row] = any ? M + logf(L) : NEG_INF;
+  }
+}
+
+// Fold for many parts (up to 32 KP per row) of rows whose head_dim is a
+// multiple of 32: a workgroup of 256 threads per (row, 32 dims). Thread t
+// takes dims 4 (t % 8) .. +3 of the slice for parts t / 8 + 32 k, so
+// the eight threads of a part read its whole 128-byte line and every load
+// instruction reads eight full lines (a wave per 4 dims would touch 64 lines
+// per load and fetch each line eight times). All of a thread's loads are in
+// flight together. The row's maximum M is taken first (exact in any order),
+// then each live part enters with weight exp(m_p - M), with no chain of
+// rescales; the part-slices' sums are added in LDS in ascending order, so
+// results are run-to-run identical. part_ml is 8-byte aligned: (m, l) load
+// as one pair. (512 threads, half the parts per thread, measured no faster
+// on 512 parts.)
+template <int KP>
+__global__ void __launch_bounds__(256) combine_wide_kernel(int nparts, int D, const float* __restrict__ part_acc,
+                                                          const float* __restrict__ part_ml,
+                                                          float* __restrict__ out, float* __restrict__ lse) {
+  constexpr int SL = 32, NW = 4;  // part-slices, waves
+  __shared__ float wmax[NW];
+  __shared__ float sl[SL][8];
+  __shared__ f4 sa[SL][8];
+  const int t = threadIdx.x, q = t & 7, sl_i = t >> 3;
+  const int row = blockIdx.x, d0 = 32 * blockIdx.y + 4 * q;
+  const float* ml = part_ml + (size_t)row * nparts * 2;
+  const float* acc = part_acc + (size_t)row * nparts * D + d0;
+  float m[KP], l[KP];
+  f4 x[KP];
+#pragma unroll
+  for (int u = 0; u < KP; ++u) {
+    const int p = sl_i + SL * u;
+    const bool in = p < nparts;
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 v = in ? *reinterpret_cast<const f2*>(ml + 2 * (size_t)p) : f2{NEG_INF, 0.f};
+    m[u] = v[0];
+    l[u] = v[1];
+    x[u] = in ? *reinterpret_cast<const f4*>(acc + (size_t)p * D) : f4{0.f, 0.f, 0.f, 0.f};
+  }
+  float mx = NEG_INF;
+#pragma unroll
+  for (int u = 0; u < KP; ++u)
+    if (live_part(m[u], l[u])) mx = fmaxf(mx, m[u]);
+  mx = fmaxf(mx, dpp_f<0xB1>(mx));   // quad_perm [1,0,3,2]
+  mx = fmaxf(mx, dpp_f<0x4E>(mx));   // quad_perm [2,3,0,1]
+  mx = fmaxf(mx, dpp_f<0x141>(mx));  // row_half_mirror
+  mx = fmaxf(mx, dpp_f<0x140>(mx));  // row_mirror
+  mx = row4_max(mx);
+  if ((t & 63) == 0) wmax[t >> 6] = mx;
+  __syncthreads();
+  float M = wmax[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) M = fmaxf(M, wmax[k]);
+  float L = 0.f;
+  f4 A = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < KP; ++u) {
+    if (live_part(m[u], l[u])) {  // an empty part's acc is never used
+      const float w = __expf(m[u] - M);
+      L = fmaf(w, l[u], L);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) A[j] = fmaf(w, x[u][j], A[j]);
+    }
+  }
+  sl[sl_i][q] = L;
+  sa[sl_i][q] = A;
+  __syncthreads();
+  if (t < 32) {  // thread (q, j): dim 4 q + j of the slice
+    const int qq = t & 7, j = t >> 3;
+    float Ls = 0.f, As = 0.f;
+#pragma unroll 8
+    for (int k = 0; k < SL; ++k) {
+      Ls += sl[k][qq];
+      As += sa[k][qq][j];
+    }
+    const bool any = Ls > 0.f;
+    out[(size_t)row * D + 32 * blockIdx.y + 4 * qq + j] = any ? As / Ls : 0.f;
+    if (blockIdx.y == 0 && t == 0) lse[row] = any ? M + logf(Ls) : NEG_INF;
   }
 }
 
@@ -1424,6 +1504,16 @@ int launch_combine(int rows, int nparts, int head_dim, const float* part_acc, co
     else
       hipLaunchKernelGGL(combine_small_kernel<32>, grid, dim3(256), 0, s, rows, nparts, head_dim, part_acc, part_ml,
                          out, lse);
+  } else if (head_dim % 32 == 0 && reinterpret_cast<uintptr_t>(part_acc) % 16 == 0 &&
+             reinterpret_cast<uintptr_t>(part_ml) % 8 == 0 && nparts <= 512) {
+    // many parts, whole 128-byte lines per load: a workgroup per (row, 32 dims)
+    const dim3 grid(rows, head_dim / 32);
+    if (nparts <= 128)
+      hipLaunchKernelGGL(combine_wide_kernel<4>, grid, dim3(256), 0, s, nparts, head_dim, part_acc, part_ml, out, lse);
+    else if (nparts <= 256)
+      hipLaunchKernelGGL(combine_wide_kernel<8>, grid, dim3(256), 0, s, nparts, head_dim, part_acc, part_ml, out, lse);
+    else
+      hipLaunchKernelGGL(combine_wide_kernel<16>, grid, dim3(256), 0, s, nparts, head_dim, part_acc, part_ml, out, lse);
   } else {
     const int vec = (head_dim % 4 == 0) && (reinterpret_cast<uintptr_t>(part_acc) % 16 == 0);
     hipLaunchKernelGGL(combine_kernel, dim3(rows, (head_dim + 3) / 4), dim3(64), 0, s, nparts, head_dim, vec,

@@ -362,9 +362,15 @@ def check_partials(w, T, bounds_of):
     (3, 130, 30, 0),      # many parts, head_dim not a multiple of 4
     (4, 200, 128, 1),     # part_acc only 4-byte aligned (one float into its buffer)
     (2, 1000, 64, 3),
+    # the wide fold (head_dim a multiple of 32, up to 512 parts): each part
+    # count per thread, part counts just past a slice boundary, head_dim 96
+    (16, 65, 128, 0), (3, 256, 64, 0), (5, 257, 96, 0), (14, 128, 64, 0), (2, 12, 32, 0),
+    (6, 300, 128, -1),    # part_ml only 4-byte aligned (part_acc aligned): the per-4-dims fold
 ])
 def test_lse_combine_matches_oracle_fold(rows, parts, dim, shift):
     print(f"case fold {rows} {parts} {dim} shift {shift}", flush=True)
+    ml_shift = 1 if shift < 0 else 0
+    shift = max(shift, 0)
     rng = np.random.default_rng(rows * 1000 + parts)
     m = (3 * rng.standard_normal((rows, parts))).astype(np.float32)
     l = rng.uniform(0.5, 50, (rows, parts)).astype(np.float32)
@@ -382,7 +388,10 @@ def test_lse_combine_matches_oracle_fold(rows, parts, dim, shift):
     buf = torch.zeros(acc.size + shift, dtype=torch.float32, device="cuda")
     acc_t = buf[shift:].view(rows, parts, dim)
     acc_t.copy_(torch.from_numpy(acc))
-    out, lse = pkv.lse_combine(acc_t, torch.from_numpy(ml).cuda())
+    ml_buf = torch.zeros(ml.size + ml_shift, dtype=torch.float32, device="cuda")
+    ml_t = ml_buf[ml_shift:].view(rows, parts, 2)
+    ml_t.copy_(torch.from_numpy(ml))
+    out, lse = pkv.lse_combine(acc_t, ml_t)
     torch.cuda.synchronize()
     ref_out, ref_lse = oracle.fold(acc.astype(np.float64), m.astype(np.float64), l.astype(np.float64))
     out, lse = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
