@@ -796,13 +796,12 @@ __device__ inline void store_run(const u4* x, GP&& gp, float s8, float r8, bool 
 // most 128 x 16 source elements (measured on demotions of 14,720 16-token
 // pages at head_dim 128: the generic kernel at four waves 300-309 us against
 // 344-352 at three, INT2/INT2 at four 347-365 us against 364-369 at three,
-// BIT1/BIT1 at three, its fp64 sums spilling at four). Larger units keep the
-// compiler's choice.
+// BIT1/BIT1 at four 275-284 us against 298-309 at three). Larger units keep
+// the compiler's choice.
 template <int D, int NT, int DK>
 __host__ __device__ constexpr int enc_waves() {
   if (D * NT > 128) return 1;
-  if (DK == -1 || DK == (W_INT2 | W_INT2 << 4)) return 4;
-  if (DK == (W_BIT1 | W_BIT1 << 4)) return 3;
+  if (DK == -1 || DK == (W_INT2 | W_INT2 << 4) || DK == (W_BIT1 | W_BIT1 << 4)) return 4;
   return 1;
 }
 template <int D, int NT, int DK>
@@ -829,9 +828,11 @@ __global__ void __launch_bounds__(64 * EW) __attribute__((amdgpu_waves_per_eu(en
   // in registers (the FP8 kernel, free of the INT scale state, holds two
   // 64-token units at head_dim 128 in 224 VGPRs); larger units are loaded at
   // the start of their turn and other waves hide the latency
-  // (INT2/INT2 one-tile units at head_dim 128 go without it: they fit four
-  // waves per SIMD only so, and other waves hide the load)
-  constexpr bool PREFETCH = !(DK == (W_INT2 | W_INT2 << 4) && D == 128 && NT == 1) &&
+  // (INT2/INT2 and BIT1/BIT1 one-tile units at head_dim 128 go without it:
+  // they fit four waves per SIMD without spills only so, and other waves
+  // hide the load)
+  constexpr bool SUB_PAIR = DK == (W_INT2 | W_INT2 << 4) || DK == (W_BIT1 | W_BIT1 << 4);
+  constexpr bool PREFETCH = !(SUB_PAIR && D == 128 && NT == 1) &&
                             NT * NC <= (DK == (W_FP8 | W_FP8 << 4) ? 16 : 8);
   UnitSrc<D, NT> cur, nxt;
   int u = gw;
@@ -929,14 +930,24 @@ __global__ void __launch_bounds__(64 * EW) __attribute__((amdgpu_waves_per_eu(en
                 const uint32_t r = row16_scatter<NCB>(kw, l16, pk_max_i16);
                 affine2_params(-bits16_to_float<BF>(unkey16(r >> 16)), bits16_to_float<BF>(unkey16(r)), mine_z, mine_s);
               } else {
-                double sm[NCB];
+                // fp64 sums of the pairs, reduced eight combos at a time (tokens
+                // 4kq, 4kq + 1, then 4kq + 2, 4kq + 3 at head_dim 128): the
+                // same lane pairs in the same order as one 16-combo reduction,
+                // with half the sums live
+                auto add = [](double a, double b) { return a + b; };
+                double r[NCB / 8];
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int h = 0; h < NCB / 8; ++h) {
+                  double sm[8];
 #pragma unroll
-                  for (int g = 0; g < NC; ++g)
-                    sm[j * NC + g] = (double)__builtin_fabsf(chunk_elem<BF>(x[g], j)) +
-                                     (double)__builtin_fabsf(chunk_elem<BF>(x[g], 4 + j));
-                mine_s = sign1_scale(row16_scatter<NCB>(sm, l16, [](double a, double b) { return a + b; }));
+                  for (int c = 0; c < 8; ++c) {
+                    const int j = (8 * h + c) / NC, g = (8 * h + c) % NC;
+                    sm[c] = (double)__builtin_fabsf(chunk_elem<BF>(x[g], j)) +
+                            (double)__builtin_fabsf(chunk_elem<BF>(x[g], 4 + j));
+                  }
+                  r[h] = row16_scatter<8>(sm, l16, add);
+                }
+                mine_s = sign1_scale(NCB == 16 && (l16 & 8) ? r[NCB / 8 - 1] : r[0]);
               }
               if (l16 < 4 * NC) {
                 const int j = l16 / NC, g = l16 % NC;
