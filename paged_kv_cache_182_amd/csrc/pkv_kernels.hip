@@ -1303,9 +1303,10 @@ __global__ void __launch_bounds__(64) combine_kernel(int nparts, int D, int vec,
 // Fold for many parts (up to 32 KP per row) of rows whose head_dim is a
 // multiple of 32: a workgroup of 256 threads per (row, 32 dims). Thread t
 // takes dims 4 (t % 8) .. +3 of the slice for parts t / 8 + 32 k, so
-// the eight threads of a part read its whole 128-byte line and every load
-// instruction reads eight full lines (a wave per 4 dims would touch 64 lines
-// per load and fetch each line eight times). All of a thread's loads are in
+// the eight threads of a part read its 128 contiguous bytes and every load
+// instruction reads eight such spans, whole cache lines when part_acc is
+// 128-byte aligned as the library's workspace is (a wave per 4 dims touches
+// 64 lines per load and fetches each line eight times). All of a thread's loads are in
 // flight together. The row's maximum M is taken first (exact in any order),
 // then each live part enters with weight exp(m_p - M), with no chain of
 // rescales; the part-slices' sums are added in LDS in ascending order, so
