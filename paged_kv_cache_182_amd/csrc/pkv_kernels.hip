@@ -1381,43 +1381,75 @@ __global__ void __launch_bounds__(256) combine_wide_kernel(int nparts, int D, co
 
 // Fold for few parts per row: one thread per (row, dim), the loads of BATCH
 // parts issued before they are used (up to 32 parts in one round), parts
-// summed in ascending order (the batch changes no result).
+// summed in ascending order. With every part in one batch the row's maximum
+// comes first (as in the wide fold); more parts take a running log-sum-exp.
 constexpr int FOLD_SMALL_MAX = 64;
 
 template <int BATCH>
-__global__ void __launch_bounds__(256) combine_small_kernel(int rows, int nparts, int D,
+__global__ void __launch_bounds__(256) combine_small_kernel(int rows, int nparts, int D, int ml2,
                                                             const float* __restrict__ part_acc,
                                                             const float* __restrict__ part_ml,
                                                             float* __restrict__ out, float* __restrict__ lse) {
-  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long row = gid / D;
-  const int d = (int)(gid - row * D);
-  if (row >= rows) return;
+  // grid (row groups of 4, dim groups of 64): thread (row, dim) without a division
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int d = (int)blockIdx.y * 64 + (int)(threadIdx.x & 63);
+  if (row >= rows || d >= D) return;
   const float* ml = part_ml + row * nparts * 2;
   const float* acc = part_acc + row * nparts * D + d;
   float M = NEG_INF, L = 0.f, A = 0.f;
-  for (int p0 = 0; p0 < nparts; p0 += BATCH) {
+  if (nparts <= BATCH) {
+    // every part in one round of loads: the maximum first, then each live
+    // part with weight exp(m_p - M) in ascending order (no rescale chain)
     float m[BATCH], l[BATCH], x[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      const int p = p0 + u;
-      m[u] = p < nparts ? ml[2 * p] : NEG_INF;
-      l[u] = p < nparts ? ml[2 * p + 1] : 0.f;
-      x[u] = p < nparts ? acc[(long long)p * D] : 0.f;
+      const bool in = u < nparts;
+      if (ml2) {  // part_ml 8-byte aligned: (m, l) as one pair
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        const f2 v = in ? *reinterpret_cast<const f2*>(ml + 2 * u) : f2{NEG_INF, 0.f};
+        m[u] = v[0];
+        l[u] = v[1];
+      } else {
+        m[u] = in ? ml[2 * u] : NEG_INF;
+        l[u] = in ? ml[2 * u + 1] : 0.f;
+      }
+      x[u] = in ? acc[(long long)u * D] : 0.f;
     }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u)
+      if (live_part(m[u], l[u])) M = fmaxf(M, m[u]);
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       if (live_part(m[u], l[u])) {
-        // running log-sum-exp over the parts seen so far
-        if (m[u] > M) {
-          const float c = M == NEG_INF ? 0.f : __expf(M - m[u]);
-          L *= c;
-          A *= c;
-          M = m[u];
-        }
         const float w = __expf(m[u] - M);
-        L += w * l[u];
-        A += w * x[u];
+        L = fmaf(w, l[u], L);
+        A = fmaf(w, x[u], A);
+      }
+    }
+  } else {
+    for (int p0 = 0; p0 < nparts; p0 += BATCH) {
+      float m[BATCH], l[BATCH], x[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int p = p0 + u;
+        m[u] = p < nparts ? ml[2 * p] : NEG_INF;
+        l[u] = p < nparts ? ml[2 * p + 1] : 0.f;
+        x[u] = p < nparts ? acc[(long long)p * D] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        if (live_part(m[u], l[u])) {
+          // running log-sum-exp over the parts seen so far
+          if (m[u] > M) {
+            const float c = M == NEG_INF ? 0.f : __expf(M - m[u]);
+            L *= c;
+            A *= c;
+            M = m[u];
+          }
+          const float w = __expf(m[u] - M);
+          L += w * l[u];
+          A += w * x[u];
+        }
       }
     }
   }
@@ -1493,20 +1525,26 @@ int launch_combine(int rows, int nparts, int head_dim, const float* part_acc, co
   // one thread per (row, dim) walks the parts eight at a time: right when
   // that is one round of loads, or when there are threads enough to fill the
   // chip; few rows with many parts go to one wave per (row, 4 dims)
-  if (nparts <= 8 || (nparts <= FOLD_SMALL_MAX && (long long)rows * head_dim >= 16384)) {
-    const long long threads = (long long)rows * head_dim;
-    const dim3 grid((unsigned)((threads + 255) / 256));
+  const bool wide_ok = head_dim % 32 == 0 && reinterpret_cast<uintptr_t>(part_acc) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(part_ml) % 8 == 0 && nparts <= 512;
+  // (17 to 64 parts go to the wide fold where it applies: 336 rows x 21
+  // parts at head_dim 64 took 3.9 us there against 5.2 us here; up to 16
+  // parts this one is faster, 256 rows x 12 parts 3.6 against 3.9 us)
+  const bool small = (nparts <= 8 || (nparts <= FOLD_SMALL_MAX && (long long)rows * head_dim >= 16384)) &&
+                     !(wide_ok && nparts > 16);
+  if (small) {
+    const dim3 grid((unsigned)((rows + 3) / 4), (unsigned)((head_dim + 63) / 64));
+    const int ml2 = reinterpret_cast<uintptr_t>(part_ml) % 8 == 0;
     if (nparts <= 8)
-      hipLaunchKernelGGL(combine_small_kernel<8>, grid, dim3(256), 0, s, rows, nparts, head_dim, part_acc, part_ml,
-                         out, lse);
+      hipLaunchKernelGGL(combine_small_kernel<8>, grid, dim3(256), 0, s, rows, nparts, head_dim, ml2, part_acc,
+                         part_ml, out, lse);
     else if (nparts <= 16)
-      hipLaunchKernelGGL(combine_small_kernel<16>, grid, dim3(256), 0, s, rows, nparts, head_dim, part_acc, part_ml,
-                         out, lse);
+      hipLaunchKernelGGL(combine_small_kernel<16>, grid, dim3(256), 0, s, rows, nparts, head_dim, ml2, part_acc,
+                         part_ml, out, lse);
     else
-      hipLaunchKernelGGL(combine_small_kernel<32>, grid, dim3(256), 0, s, rows, nparts, head_dim, part_acc, part_ml,
-                         out, lse);
-  } else if (head_dim % 32 == 0 && reinterpret_cast<uintptr_t>(part_acc) % 16 == 0 &&
-             reinterpret_cast<uintptr_t>(part_ml) % 8 == 0 && nparts <= 512) {
+      hipLaunchKernelGGL(combine_small_kernel<32>, grid, dim3(256), 0, s, rows, nparts, head_dim, ml2, part_acc,
+                         part_ml, out, lse);
+  } else if (wide_ok) {
     // many parts, whole 128-byte lines per load: a workgroup per (row, 32 dims)
     const dim3 grid(rows, head_dim / 32);
     if (nparts <= 128)

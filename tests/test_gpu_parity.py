@@ -366,6 +366,10 @@ def check_partials(w, T, bounds_of):
     # count per thread, part counts just past a slice boundary, head_dim 96
     (16, 65, 128, 0), (3, 256, 64, 0), (5, 257, 96, 0), (14, 128, 64, 0), (2, 12, 32, 0),
     (6, 300, 128, -1),    # part_ml only 4-byte aligned (part_acc aligned): the per-4-dims fold
+    # the per-(row, dim) fold: every part in one batch (maximum first), (m, l)
+    # as pairs and as single floats; more parts than a batch (running
+    # log-sum-exp); 17-64 parts with head_dim a multiple of 32 (wide fold)
+    (130, 12, 128, 0), (130, 12, 128, -1), (600, 20, 30, 0), (600, 40, 30, 0), (336, 21, 64, 0),
 ])
 def test_lse_combine_matches_oracle_fold(rows, parts, dim, shift):
     print(f"case fold {rows} {parts} {dim} shift {shift}", flush=True)
